@@ -1,0 +1,153 @@
+"""Oracle number formats (TEST INFRASTRUCTURE ONLY).
+
+The pages name the formats (INT4/UINT4, MXFP4 = E2M1 elements with E8M0
+block scales, FP8 E4M3, BF16) in "Announcing Humming: Fast, Flexible Kernels
+for Quantized Inference", sections "Background" and "WnA16"; they never give
+bit layouts.  The readings below are the OCP definitions:
+
+* INT4: two's complement nibble, values -8..7.  UINT4: 0..15.
+* E2M1 (OCP MX v1.0): sign, 2 exponent bits (bias 1), 1 mantissa bit;
+  magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; no Inf/NaN.
+* E4M3 "FN" (OCP FP8): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+  exponent field 0 is subnormal with quantum 2^-9; codes 0x7F/0xFF are NaN;
+  no Inf; largest finite 448.
+* E8M0 (OCP MX v1.0): 2^(c-127); c = 255 is NaN.
+* BF16: the upper 16 bits of an IEEE float32.
+
+Encoders round to nearest, ties to even, and saturate (E4M3) where noted.
+All values are returned as float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def decode_int4(c):
+    c = np.asarray(c, dtype=np.int64) & 0xF
+    return np.where(c >= 8, c - 16, c).astype(np.float64)
+
+
+def decode_uint4(c):
+    return (np.asarray(c, dtype=np.int64) & 0xF).astype(np.float64)
+
+
+def decode_e2m1(c):
+    c = np.asarray(c, dtype=np.int64) & 0xF
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+def decode_e4m3(c):
+    c = np.asarray(c, dtype=np.int64) & 0xFF
+    s = (c >> 7) & 1
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+def decode_e8m0(c):
+    c = np.asarray(c, dtype=np.int64) & 0xFF
+    v = np.ldexp(1.0, c - 127)
+    return np.where(c == 255, np.nan, v).astype(np.float64)
+
+
+def decode_bf16(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode_f32(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _rne(x):
+    # NumPy's round() is round-half-to-even.
+    return np.round(x)
+
+
+def encode_bf16(x):
+    """float64 values -> bf16 bit patterns, one RNE rounding of the exact
+    value (8 significant bits, subnormal quantum 2^-133)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                      # a = f * 2^e, f in [0.5, 1)
+    e = np.where(a == 0, -200, e)
+    q_exp = np.maximum(e - 8, -133)          # quantum exponent
+    r = np.ldexp(_rne(np.ldexp(a, -q_exp)), q_exp)
+    r = np.where(r > 3.3895313892515355e38, np.inf, r)
+    r = np.where(np.isnan(a), np.nan, r)
+    r = np.copysign(r, x)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def round_e4m3(v):
+    """float64 -> nearest E4M3 value (RNE), saturated to +-448, signed zero
+    kept.  Returns float64 values that are exactly representable."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                      # a in [2^(e-1), 2^e)
+    e = np.where(a == 0, -200, e)
+    q_exp = np.maximum(e - 4, -9)            # 3 mantissa bits, subnormal 2^-9
+    r = np.ldexp(_rne(np.ldexp(a, -q_exp)), q_exp)
+    r = np.minimum(r, E4M3_MAX)
+    return np.copysign(r, v)
+
+
+def encode_e4m3(v):
+    """float64 -> E4M3 code (uint8), RNE with saturation to +-448."""
+    r = round_e4m3(v)
+    sign = np.signbit(r).astype(np.int64)
+    a = np.abs(r)
+    _, e = np.frexp(a)
+    ub = e - 1                               # unbiased exponent of a normal
+    normal = a >= 2.0 ** -6
+    exp_field = np.where(normal, ub + 7, 0)
+    man = np.where(normal, np.ldexp(a, -ub) * 8.0 - 8.0, np.ldexp(a, 9))
+    man = np.where(a == 0, 0, man)
+    exp_field = np.where(a == 0, 0, exp_field)
+    code = (sign << 7) | (exp_field.astype(np.int64) << 3) | man.astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def floor_log2(a):
+    """Exact floor(log2 a) for finite a > 0, read from the exponent field."""
+    _, e = np.frexp(np.asarray(a, dtype=np.float64))
+    return e - 1
+
+
+def decode_scale(scales, dtype: str):
+    if dtype == "bf16":
+        return decode_bf16(scales)
+    if dtype == "f32":
+        return decode_f32(scales)
+    if dtype == "e8m0":
+        return decode_e8m0(scales)
+    raise ValueError(f"unknown scale dtype {dtype}")
+
+
+def unpack_nibbles(packed):
+    """uint8 [..., K/2] -> uint8 [..., K]; even k from the low nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def decode_weight_codes(codes, weight_dtype: str):
+    """Canonical code array -> float64 element values v(q)."""
+    if weight_dtype in ("int4", "uint4", "e2m1"):
+        q = unpack_nibbles(codes)
+        return {"int4": decode_int4, "uint4": decode_uint4,
+                "e2m1": decode_e2m1}[weight_dtype](q)
+    if weight_dtype == "e4m3":
+        return decode_e4m3(codes)
+    raise ValueError(f"unknown weight dtype {weight_dtype}")

@@ -1,0 +1,134 @@
+"""Oracle MoE layer (TEST INFRASTRUCTURE ONLY).
+
+What the pages fix: an MoE layer runs a fused Gateup GEMM and a Down GEMM per
+expert ("Announcing Humming: Fast, Flexible Kernels for Quantized Inference",
+section "Performance": the MoE figure sums the Gateup and Down GEMM
+latencies); tokens are routed by ``topk_ids`` / ``topk_weights``, grouped by
+expert (``moe_align_block_size``, ``moe_permute_prepare``) and the expert
+outputs are combined by a top-k weighted sum (``moe_fused_mul_sum``,
+``moe_unpermute``) -- sections "Implementation breakdown" and "Key source
+snippets" of the prhub.com.cn summary of SGLang PR #23754.
+
+Readings where the pages are silent:
+
+* activation between the GEMMs: a = silu(h[:I]) * h[I:], silu(g) = g/(1+e^-g),
+  gate = first I rows of the fused weight, up = last I rows; no clamp and a
+  routed scaling factor of 1.
+* precision at the stage boundary follows the activation format: bf16 (RNE)
+  for W4A16, MXFP8 of the float value for W4A8; the token activations are
+  MXFP8-quantized for W4A8.
+* align: flat index f = t*topk + j; experts' segments in expert order, each
+  padded to a multiple of block_m; inside a segment ascending f (stable);
+  padding slots hold the sentinel T*topk.
+* reduce: out[t] = sum_j w[t,j] * y[t*topk + j], then bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import decode_bf16, encode_bf16
+from .gemm import WeightDesc, dequant_weight
+from .quant import dequant_mxfp8, quant_mxfp8
+
+
+def align_capacity(num_tokens: int, topk: int, num_experts: int, block_m: int) -> int:
+    """Upper bound of the padded sorted-id buffer length."""
+    return num_tokens * topk + num_experts * (block_m - 1)
+
+
+def align(ids, num_experts: int, block_m: int):
+    """ids int [T, topk] -> (sorted int32 [capacity], offsets int32 [E+1],
+    counts int32 [E]).  Entries past offsets[E] also hold the sentinel."""
+    ids = np.asarray(ids, dtype=np.int64)
+    t, k = ids.shape
+    flat = ids.reshape(-1)
+    sentinel = t * k
+    counts = np.bincount(flat, minlength=num_experts)[:num_experts].astype(np.int64)
+    padded = -(-counts // block_m) * block_m
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    cap = align_capacity(t, k, num_experts, block_m)
+    out = np.full(cap, sentinel, dtype=np.int64)
+    order = np.argsort(flat, kind="stable")     # by expert, ties by ascending f
+    start = 0
+    for e in range(num_experts):
+        c = int(counts[e])
+        out[offsets[e]:offsets[e] + c] = order[start:start + c]
+        start += c
+    return out.astype(np.int32), offsets.astype(np.int32), counts.astype(np.int32)
+
+
+def silu(g):
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(h, inter: int):
+    return silu(h[:, :inter]) * h[:, inter:2 * inter]
+
+
+def round_bf16(a):
+    return decode_bf16(encode_bf16(a))
+
+
+def qdq_mxfp8(a):
+    q, e = quant_mxfp8(a)
+    return dequant_mxfp8(q, e)
+
+
+def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
+                x_bits, ids, weights, act_fmt: str, experts=None,
+                return_y: bool = False):
+    """Full MoE layer in float64.  Returns out (float64 [T, H]) before the
+    final bf16 rounding, and optionally y (float64 [T*topk, H]) indexed by
+    flat routing index.
+
+    ``w13`` / ``w2``: dicts with canonical ``codes``, ``scales`` and optional
+    ``zeros`` / ``global_scale``.  ``act_fmt``: "bf16" (W4A16) or "mxfp8"
+    (W4A8).  ``experts``: restrict to these experts (bounded samples).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    wts = np.asarray(weights, dtype=np.float32).astype(np.float64)
+    t, k = ids.shape
+    hdim = desc13.k
+    inter = desc2.k
+    assert desc13.n == 2 * inter and desc2.n == hdim
+    x = decode_bf16(x_bits)
+    if act_fmt == "mxfp8":
+        a_in = qdq_mxfp8(x)
+    elif act_fmt == "bf16":
+        a_in = x
+    else:
+        raise ValueError(act_fmt)
+    out = np.zeros((t, hdim), dtype=np.float64)
+    y_all = np.zeros((t * k, hdim), dtype=np.float64) if return_y else None
+    flat = ids.reshape(-1)
+    ex = range(desc13.num_experts) if experts is None else experts
+    for e in ex:
+        f = np.nonzero(flat == e)[0]
+        if f.size == 0:
+            continue
+        tok = f // k
+        w_gu = dequant_weight(desc13, w13["codes"], w13["scales"], w13.get("zeros"),
+                              w13.get("global_scale"), experts=[e])[0]
+        h = a_in[tok] @ w_gu.T
+        del w_gu
+        a = swiglu(h, inter)
+        a = round_bf16(a) if act_fmt == "bf16" else qdq_mxfp8(a)
+        w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
+                              w2.get("global_scale"), experts=[e])[0]
+        y = a @ w_dn.T
+        del w_dn
+        if return_y:
+            y_all[f] = y
+        np.add.at(out, tok, wts.reshape(-1)[f][:, None] * y)
+    return (out, y_all) if return_y else out
+
+
+def reduce(y, weights, topk: int):
+    """out[t] = sum_j w[t,j] * y[t*topk + j] (float64), y float64 [T*topk, H]."""
+    y = np.asarray(y, dtype=np.float64)
+    w = np.asarray(weights, dtype=np.float32).astype(np.float64)
+    t = w.shape[0]
+    return (y.reshape(t, topk, -1) * w[:, :, None]).sum(axis=1)

@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws random numbers and lays them out in the canonical
+("standard format") host layout that both the CPU oracle and the GPU library
+consume.  It holds none of the method's arithmetic: no dequantization, no
+GEMM, no activation quantizer, no routing sort.  Where an input has to be
+rounded to a storage type (bf16 activations, FP8 weights of the W8A8 case)
+the rounding is done by PyTorch's own dtype conversion, which is a library
+routine and not part of what is being tested.
+
+Canonical host layout (every array is a NumPy array on the host):
+
+* 4-bit codes: ``uint8 [E][N][K/2]``, two codes per byte, the even k in the
+  low nibble.  8-bit codes: ``uint8 [E][N][K]``.
+* scales: ``[E][N][K/G]``; bf16 as ``uint16`` bit patterns, f32 as
+  ``float32``, E8M0 as ``uint8`` exponent codes.
+* zero points: ``uint8 [E][N][K/G]`` holding uint4 values (0..15).
+* second-level (global) scale: ``float32 [E]``.
+* bf16 activations: ``uint16 [M][K]`` bit patterns.
+
+The weight formats, scale granularities and zero points follow the
+quantization description of "Announcing Humming: Fast, Flexible Kernels for
+Quantized Inference", section "Unified quantization representation"; the
+workload shapes and value distributions are those of the dense W4A16, dense
+W8A8 and MoE W4A16 / W4A8 workloads measured in that post's "Performance"
+section, with the sizes fixed here.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rng", "seed_for", "bf16_bits", "bf16_normal", "pack_nibbles",
+    "dense_w4a16", "dense_w8a8", "moe_weights_mxfp4", "routing",
+    "DENSE_SWEEP_M", "FP8_SWEEP_M", "MOE_W4A16_T", "MOE_W4A8_T",
+]
+
+DENSE_SWEEP_M = (1, 4, 16, 64, 256, 1024, 4096)
+FP8_SWEEP_M = (1, 16, 128, 1024, 4096)
+MOE_W4A16_T = (1, 16, 64, 512, 4096)
+MOE_W4A8_T = (1, 64, 1024, 8192)
+
+
+def seed_for(config: int, index: int = 0) -> int:
+    """Seed convention: 1000 * workload number + sweep index."""
+    return 1000 * int(config) + int(index)
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> bf16 bit patterns (uint16), rounded by torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_normal(g: np.random.Generator, shape) -> np.ndarray:
+    """bf16 ~ N(0,1): float32 normal draws rounded to bf16."""
+    return bf16_bits(g.standard_normal(shape, dtype=np.float32))
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """uint8 codes (0..15) [..., K] -> uint8 [..., K/2], even k in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def _uniform_bf16(g, lo, hi, shape):
+    return bf16_bits(g.uniform(lo, hi, size=shape).astype(np.float32))
+
+
+def dense_w4a16(seed: int, m: int, n: int, k: int, group: int = 128,
+                asym: bool = False, num_experts: int = 1,
+                scale_lo: float = 0.005, scale_hi: float = 0.02,
+                zero_lo: int = 6, zero_hi: int = 9):
+    """Group-quantized 4-bit weights with bf16 scales and bf16 activations.
+
+    ``asym=False``: signed INT4 codes uniform in [-8, 7] (two's complement
+    nibbles), no zero point.  ``asym=True``: UINT4 codes uniform in [0, 15]
+    with uint4 zero points uniform in [zero_lo, zero_hi] per group.
+    """
+    g = rng(seed)
+    e = num_experts
+    kg = k // group
+    if asym:
+        codes = g.integers(0, 16, size=(e, n, k), dtype=np.int64)
+        zeros = g.integers(zero_lo, zero_hi + 1, size=(e, n, kg)).astype(np.uint8)
+    else:
+        v = g.integers(-8, 8, size=(e, n, k), dtype=np.int64)
+        codes = v & 0xF
+        zeros = None
+    scales = _uniform_bf16(g, scale_lo, scale_hi, (e, n, kg))
+    x = bf16_normal(g, (m, k))
+    return {
+        "codes": pack_nibbles(codes.astype(np.uint8)),
+        "scales": scales,
+        "zeros": zeros,
+        "x": x,
+        "m": m, "n": n, "k": k, "group": group, "num_experts": e,
+        "weight_dtype": "uint4" if asym else "int4",
+    }
+
+
+def dense_w8a8(seed: int, m: int, n: int, k: int, w_std: float = 0.05):
+    """FP8 E4M3 weights with one fp32 scale per output channel.
+
+    Weights are drawn as N(0,1) * w_std in float32, the per-channel scale is
+    amax_n / 448 in float32 and the codes are torch's float8_e4m3fn
+    conversion of w / scale (clamped to the finite range first).
+    Activations are bf16 ~ N(0,1); they are quantized per token on the GPU.
+    """
+    import torch
+    g = rng(seed)
+    w = (g.standard_normal((n, k), dtype=np.float32) * np.float32(w_std)).astype(np.float32)
+    amax = np.abs(w).max(axis=1).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    r = np.clip(w / s[:, None], -448.0, 448.0).astype(np.float32)
+    codes = torch.from_numpy(r).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    x = bf16_normal(g, (m, k))
+    return {
+        "codes": codes.reshape(1, n, k), "scales": s.reshape(1, n, 1),
+        "zeros": None, "x": x, "m": m, "n": n, "k": k, "group": k,
+        "num_experts": 1, "weight_dtype": "e4m3",
+    }
+
+
+def moe_weights_mxfp4(seed: int, num_experts: int, n: int, k: int,
+                      exp_lo: int = -8, exp_hi: int = -4):
+    """MXFP4 weights: E2M1 codes uniform over all 16 codes, one E8M0 scale per
+    32 along K with unbiased exponent uniform in [exp_lo, exp_hi]."""
+    g = rng(seed)
+    codes = g.integers(0, 16, size=(num_experts, n, k), dtype=np.int64).astype(np.uint8)
+    sc = g.integers(127 + exp_lo, 127 + exp_hi + 1,
+                    size=(num_experts, n, k // 32)).astype(np.uint8)
+    return {"codes": pack_nibbles(codes), "scales": sc, "zeros": None,
+            "n": n, "k": k, "group": 32, "num_experts": num_experts,
+            "weight_dtype": "e2m1"}
+
+
+def routing(seed: int, t: int, num_experts: int, topk: int,
+            zipf_s: float | None = None):
+    """Router inputs: logits ~ N(0,1) (+ per-expert bias), softmax in fp64,
+    top-k by probability (ties to the lower expert id), weights renormalised
+    over the selected experts and stored as float32.
+
+    With ``zipf_s`` the bias of expert e is ``-zipf_s * ln(r_e)`` where r is a
+    seeded permutation of 1..E: the Zipf(s) log-weights that skew the load.
+    Returns ``(ids int32 [T, topk], weights float32 [T, topk])``.
+    """
+    g = rng(seed)
+    logits = g.standard_normal((t, num_experts), dtype=np.float32).astype(np.float64)
+    if zipf_s is not None:
+        r = g.permutation(num_experts) + 1
+        logits = logits + (-float(zipf_s) * np.log(r.astype(np.float64)))[None, :]
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    # stable sort on (-p, expert id): descending probability, ties -> lower id
+    order = np.argsort(-p, axis=1, kind="stable")[:, :topk]
+    pt = np.take_along_axis(p, order, axis=1)
+    w = (pt / pt.sum(axis=1, keepdims=True)).astype(np.float32)
+    return order.astype(np.int32), w

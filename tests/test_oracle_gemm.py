@@ -1,0 +1,170 @@
+"""Pins of the oracle's dequantization and dense layer: a pure-Python
+Fraction triple loop with scalar decoders of its own, and the invariants the
+description implies (G = K equals per-channel, q == z gives zero output,
+exact-integer cases equal to the bit)."""
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import gemm as G
+from oracle.formats import decode_bf16
+from synth import bf16_bits, pack_nibbles
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def s_int4(c):
+    return c - 16 if c >= 8 else c
+
+
+def s_e2m1(c):
+    v = E2M1[c & 7]
+    return -v if c & 8 else v
+
+
+def s_e4m3(c):
+    return float(torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).float()[0])
+
+
+def s_bf16(b):
+    return struct.unpack("<f", struct.pack("<I", int(b) << 16))[0]
+
+
+def s_scale(v, dtype):
+    if dtype == "bf16":
+        return Fraction(s_bf16(v))
+    if dtype == "f32":
+        return Fraction(float(np.float32(v)))
+    return Fraction(2) ** (int(v) - 127)
+
+
+def brute_linear(desc, a_vals, codes_unpacked, scales, zeros, gscale):
+    """C[m][n] with exact rationals, one scalar at a time."""
+    dec = {"int4": s_int4, "uint4": lambda c: c, "e2m1": s_e2m1, "e4m3": s_e4m3}[desc.weight_dtype]
+    m, k = len(a_vals), desc.k
+    out = []
+    for i in range(m):
+        row = []
+        for n in range(desc.n):
+            acc = Fraction(0)
+            for kk in range(k):
+                if desc.scale_gran == "group":
+                    gi, ni = kk // desc.group_size, n
+                elif desc.scale_gran == "channel":
+                    gi, ni = 0, n
+                else:
+                    gi, ni = 0, 0
+                v = Fraction(dec(int(codes_unpacked[n][kk])))
+                if desc.has_zero:
+                    v -= int(zeros[ni][gi])
+                w = v * s_scale(scales[ni][gi], desc.scale_dtype)
+                if desc.has_global:
+                    w *= Fraction(float(np.float32(gscale)))
+                acc += Fraction(float(a_vals[i][kk])) * w
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+CASES = [
+    ("int4", "group", 16, "bf16", False, False),
+    ("uint4", "group", 16, "bf16", True, False),
+    ("uint4", "channel", 0, "f32", True, True),
+    ("int4", "tensor", 0, "f32", False, True),
+    ("e2m1", "group", 32, "e8m0", False, False),
+    ("e2m1", "group", 16, "bf16", False, True),
+    ("e4m3", "channel", 0, "f32", False, False),
+]
+
+
+@pytest.mark.parametrize("wd,gran,gs,sd,zp,gl", CASES)
+def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
+    g = np.random.default_rng(hash((wd, gran, gs, sd)) & 0xFFFF)
+    m, n, k = 3, 5, 64
+    desc = G.WeightDesc(wd, gran, gs, sd, zp, gl, 1, n, k)
+    ng = desc.groups()
+    sn = 1 if gran == "tensor" else n
+    if wd == "e4m3":
+        cu = g.integers(0, 256, size=(n, k))
+        cu = np.where((cu & 0x7F) == 0x7F, 0x7E, cu).astype(np.uint8)
+        codes = cu[None]
+    else:
+        cu = g.integers(0, 16, size=(n, k)).astype(np.uint8)
+        codes = pack_nibbles(cu)[None]
+    if sd == "bf16":
+        sc = bf16_bits(g.uniform(0.005, 0.02, size=(sn, ng)).astype(np.float32))
+    elif sd == "f32":
+        sc = g.uniform(0.01, 0.1, size=(sn, ng)).astype(np.float32)
+    else:
+        sc = g.integers(119, 124, size=(sn, ng)).astype(np.uint8)
+    zeros = g.integers(0, 16, size=(sn, ng)).astype(np.uint8) if zp else None
+    gsc = np.array([0.75], np.float32)
+    a_bits = bf16_bits(g.standard_normal((m, k)).astype(np.float32))
+    a = decode_bf16(a_bits)
+    got = G.linear(desc, a, codes, sc[None], None if zeros is None else zeros[None], gsc)
+    ref = brute_linear(desc, a.tolist(), cu, sc, zeros, gsc[0])
+    for i in range(m):
+        for j in range(n):
+            r = float(ref[i][j])
+            assert abs(got[i, j] - r) <= 1e-12 * max(1.0, abs(r)), (i, j, got[i, j], r)
+
+
+def test_exact_integer_case_is_exact():
+    # Integer activations and power-of-two scales: every product and partial
+    # sum is exactly representable, so the fp64 result equals the rational one.
+    g = np.random.default_rng(20)
+    m, n, k = 4, 6, 128
+    desc = G.WeightDesc("uint4", "group", 32, "bf16", True, False, 1, n, k)
+    cu = g.integers(0, 16, size=(n, k)).astype(np.uint8)
+    sc = bf16_bits(np.full((n, 4), 2.0 ** -4, np.float32))
+    z = g.integers(0, 16, size=(n, 4)).astype(np.uint8)
+    a = g.integers(-8, 9, size=(m, k)).astype(np.float64)
+    got = G.linear(desc, a, pack_nibbles(cu)[None], sc[None], z[None])
+    ref = brute_linear(desc, a.tolist(), cu, sc, z, None)
+    assert all(got[i, j] == ref[i][j] for i in range(m) for j in range(n))
+
+
+def test_group_equals_k_is_channel():
+    g = np.random.default_rng(21)
+    n, k = 8, 256
+    cu = pack_nibbles(g.integers(0, 16, size=(1, n, k)).astype(np.uint8))
+    sc = bf16_bits(g.uniform(0.005, 0.02, size=(1, n, 1)).astype(np.float32))
+    z = g.integers(0, 16, size=(1, n, 1)).astype(np.uint8)
+    a = decode_bf16(bf16_bits(g.standard_normal((5, k)).astype(np.float32)))
+    d_g = G.WeightDesc("uint4", "group", k, "bf16", True, False, 1, n, k)
+    d_c = G.WeightDesc("uint4", "channel", 0, "bf16", True, False, 1, n, k)
+    assert np.array_equal(G.linear(d_g, a, cu, sc, z), G.linear(d_c, a, cu, sc, z))
+
+
+def test_codes_equal_zero_point_give_zero():
+    g = np.random.default_rng(22)
+    n, k, gs = 8, 256, 128
+    z = g.integers(0, 16, size=(1, n, k // gs)).astype(np.uint8)
+    cu = np.repeat(z, gs, axis=2)
+    sc = bf16_bits(g.uniform(0.005, 0.02, size=(1, n, k // gs)).astype(np.float32))
+    a = decode_bf16(bf16_bits(g.standard_normal((3, k)).astype(np.float32)))
+    d = G.WeightDesc("uint4", "group", gs, "bf16", True, False, 1, n, k)
+    out = G.linear(d, a, pack_nibbles(cu), sc, z)
+    assert np.all(out == 0)
+    # symmetric all-zero codes
+    d2 = G.WeightDesc("int4", "group", gs, "bf16", False, False, 1, n, k)
+    out2 = G.linear(d2, a, np.zeros((1, n, k // 2), np.uint8), sc)
+    assert np.all(out2 == 0)
+
+
+def test_dequant_weight_per_expert_selection():
+    g = np.random.default_rng(23)
+    e, n, k = 3, 4, 64
+    d = G.WeightDesc("e2m1", "group", 32, "e8m0", False, False, e, n, k)
+    codes = pack_nibbles(g.integers(0, 16, size=(e, n, k)).astype(np.uint8))
+    sc = g.integers(119, 124, size=(e, n, 2)).astype(np.uint8)
+    full = G.dequant_weight(d, codes, sc)
+    for i in range(e):
+        assert np.array_equal(G.dequant_weight(d, codes, sc, experts=[i])[0], full[i])
+        # one element by hand
+        c = int(codes[i, 1, 3] >> 4)            # k = 7 -> high nibble of byte 3
+        assert full[i, 1, 7] == s_e2m1(c) * math.ldexp(1.0, int(sc[i, 1, 0]) - 127)

@@ -1,0 +1,113 @@
+"""Pins of the oracle's MoE pieces: align against Python's sorted(), the
+reduce against its special cases, and the layer against a loop of dense
+layers and the E=1 / top-1 / w=1 reduction to dense -> SwiGLU -> dense."""
+import numpy as np
+import pytest
+
+from oracle import gemm as G
+from oracle import moe as M
+from oracle.formats import decode_bf16, encode_bf16
+from synth import bf16_bits, moe_weights_mxfp4, routing
+
+
+@pytest.mark.parametrize("t,k,e,bm", [(1, 8, 128, 16), (37, 8, 16, 4), (64, 2, 8, 1), (5, 3, 40, 64)])
+def test_align_vs_sorted(t, k, e, bm):
+    g = np.random.default_rng(t * 131 + e)
+    ids = g.integers(0, e, size=(t, k)).astype(np.int32)
+    srt, off, cnt = M.align(ids, e, bm)
+    flat = ids.reshape(-1).tolist()
+    order = sorted(range(t * k), key=lambda f: (flat[f], f))
+    assert cnt.sum() == t * k
+    assert off[0] == 0 and np.all(np.diff(off) >= 0) and np.all(off % bm == 0)
+    pos = 0
+    for ex in range(e):
+        seg = srt[off[ex]:off[ex + 1]]
+        real = [f for f in seg if f != t * k]
+        assert real == order[pos:pos + cnt[ex]]
+        assert all(f == t * k for f in seg[cnt[ex]:])
+        assert len(seg) == -(-cnt[ex] // bm) * bm
+        pos += cnt[ex]
+    assert np.all(srt[off[e]:] == t * k)
+    assert len(srt) == M.align_capacity(t, k, e, bm)
+
+
+def test_align_block1_is_permutation():
+    g = np.random.default_rng(5)
+    ids = g.integers(0, 10, size=(50, 4))
+    srt, off, cnt = M.align(ids, 10, 1)
+    assert sorted(srt.tolist()) == list(range(200))
+    assert np.array_equal(off[1:], np.cumsum(cnt))
+
+
+def test_reduce_special_cases():
+    g = np.random.default_rng(6)
+    y = g.standard_normal((10, 7))
+    out = M.reduce(y, np.ones((10, 1), np.float32), 1)
+    assert np.array_equal(out, y)
+    w = np.array([[0.25, 0.5, 0.25]], np.float32)
+    yy = np.repeat(g.standard_normal((1, 7)), 3, axis=0)
+    assert np.allclose(M.reduce(yy, w, 3), yy[:1], rtol=0, atol=1e-15)
+
+
+def _small_layer(seed, e, hdim, inter):
+    w13 = moe_weights_mxfp4(seed, e, 2 * inter, hdim)
+    w2 = moe_weights_mxfp4(seed + 1, e, hdim, inter)
+    d13 = G.WeightDesc("e2m1", "group", 32, "e8m0", False, False, e, 2 * inter, hdim)
+    d2 = G.WeightDesc("e2m1", "group", 32, "e8m0", False, False, e, hdim, inter)
+    return d13, w13, d2, w2
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_moe_equals_loop_of_dense(act):
+    e, hdim, inter, t, k = 6, 64, 32, 9, 3
+    d13, w13, d2, w2 = _small_layer(30, e, hdim, inter)
+    g = np.random.default_rng(31)
+    x = bf16_bits(g.standard_normal((t, hdim)).astype(np.float32))
+    ids, wts = routing(32, t, e, k)
+    out = M.moe_forward(d13, w13, d2, w2, x, ids, wts, act)
+    a_in = decode_bf16(x) if act == "bf16" else M.qdq_mxfp8(decode_bf16(x))
+    ref = np.zeros_like(out)
+    for tt in range(t):
+        for j in range(k):
+            ex = int(ids[tt, j])
+            h = G.linear(d13, a_in[tt:tt + 1], w13["codes"], w13["scales"], expert=ex)
+            a = M.silu(h[:, :inter]) * h[:, inter:]
+            a = decode_bf16(encode_bf16(a)) if act == "bf16" else M.qdq_mxfp8(a)
+            y = G.linear(d2, a, w2["codes"], w2["scales"], expert=ex)
+            ref[tt] += float(wts[tt, j]) * y[0]
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_moe_single_expert_top1_is_dense_swiglu_dense():
+    hdim, inter, t = 64, 32, 5
+    d13, w13, d2, w2 = _small_layer(40, 1, hdim, inter)
+    g = np.random.default_rng(41)
+    x = bf16_bits(g.standard_normal((t, hdim)).astype(np.float32))
+    ids = np.zeros((t, 1), np.int32)
+    wts = np.ones((t, 1), np.float32)
+    out = M.moe_forward(d13, w13, d2, w2, x, ids, wts, "bf16")
+    w_gu = G.dequant_weight(d13, w13["codes"], w13["scales"])[0]
+    w_dn = G.dequant_weight(d2, w2["codes"], w2["scales"])[0]
+    h = decode_bf16(x) @ w_gu.T
+    gate, up = h[:, :inter], h[:, inter:]
+    a = gate * (1.0 / (1.0 + np.exp(-gate))) * up
+    a = decode_bf16(encode_bf16(a))
+    assert np.allclose(out, a @ w_dn.T, rtol=1e-13, atol=0)
+
+
+def test_silu_closed_form_points():
+    assert M.silu(0.0) == 0.0
+    assert abs(M.silu(1.0) - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16
+    assert M.silu(-1000.0) == 0.0
+    assert M.silu(1000.0) == 1000.0
+
+
+def test_routing_generator_properties():
+    ids, w = routing(7, 100, 128, 8)
+    assert ids.shape == (100, 8) and w.dtype == np.float32
+    assert all(len(set(r)) == 8 for r in ids.tolist())
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 1e-7)
+    ids_z, _ = routing(8, 4096, 128, 8, zipf_s=1.1)
+    cnt = np.bincount(ids_z.reshape(-1), minlength=128)
+    assert cnt.max() > 5 * np.median(cnt)
