@@ -1,0 +1,239 @@
+/*
+ * hum.h -- C ABI of the MI355X (gfx950) quantized GEMM library.
+ *
+ * One quantization description (weight format, scale granularity, scale
+ * dtype, zero point, second-level scale, activation format) drives weight
+ * preparation and the dense / MoE GEMMs.  The description follows "Announcing
+ * Humming: Fast, Flexible Kernels for Quantized Inference", section "Unified
+ * quantization representation"; the preparation step (validate, pad, repack
+ * into the kernel layout) follows section "Per-workload tuning and JIT
+ * compilation" of the same post.
+ *
+ * Conventions for every entry point:
+ *  - Memory: every pointer argument that names tensor data is a DEVICE
+ *    pointer owned by the caller (the library allocates nothing).  Host
+ *    pointers are only the descriptor / config structs.
+ *  - Streams: work is enqueued on `stream` (a hipStream_t passed as void*;
+ *    NULL means the default stream) and is ordered with the caller's other
+ *    work on that stream.  No entry point synchronizes the device.
+ *  - Errors: argument / shape / format errors return a non-zero hum_status
+ *    before anything is launched; hum_last_error() then describes the
+ *    problem (thread-local string).  A failed launch returns HUM_ERR_HIP.
+ *  - Layout: row-major, K contiguous.  4-bit codes are packed two per byte,
+ *    the even k in the low nibble.
+ *  - Limits: K must be a multiple of 128; N is arbitrary.  Integer (INT4 /
+ *    UINT4) group sizes must be multiples of 128; MXFP4 uses group 32 with
+ *    E8M0 scales.
+ */
+#ifndef HUM_H_
+#define HUM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hum_status {
+  HUM_OK = 0,
+  HUM_ERR_INVALID_ARG = 1,  /* NULL pointer, bad size, inconsistent shapes */
+  HUM_ERR_UNSUPPORTED = 2,  /* valid description this library does not run */
+  HUM_ERR_WORKSPACE = 3,    /* buffer smaller than the matching *_bytes() query */
+  HUM_ERR_HIP = 4           /* a HIP launch / runtime call failed */
+} hum_status;
+
+typedef enum hum_dtype {
+  HUM_BF16 = 0,
+  HUM_F32 = 1,
+  HUM_INT4 = 2,   /* signed two's-complement nibble, -8..7 */
+  HUM_UINT4 = 3,  /* unsigned nibble 0..15, optional zero point */
+  HUM_E2M1 = 4,   /* FP4 (MXFP4 element) */
+  HUM_E4M3 = 5,   /* FP8 E4M3 "FN": max 448, NaN = 0x7F/0xFF, no Inf */
+  HUM_E8M0 = 6    /* power-of-two scale 2^(c-127) */
+} hum_dtype;
+
+typedef enum hum_scale_gran {
+  HUM_SCALE_TENSOR = 0,   /* one scale per expert          : scales [E][1][1] */
+  HUM_SCALE_CHANNEL = 1,  /* one scale per output channel  : scales [E][N][1] */
+  HUM_SCALE_GROUP = 2     /* one scale per group along K   : scales [E][N][K/G] */
+} hum_scale_gran;
+
+typedef enum hum_act_fmt {
+  HUM_ACT_BF16 = 0,       /* bf16 activations as given (WnA16) */
+  HUM_ACT_FP8_TOKEN = 1,  /* E4M3 codes + one f32 scale per row (W8A8) */
+  HUM_ACT_MXFP8 = 2       /* E4M3 codes + one E8M0 scale per 32 along K (W4A8) */
+} hum_act_fmt;
+
+/* The quantization description of one weight tensor [E][N][K]. */
+typedef struct hum_weight_desc {
+  int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_E2M1 | HUM_E4M3 */
+  int32_t scale_gran;        /* hum_scale_gran */
+  int32_t group_size;        /* K elements per group (HUM_SCALE_GROUP only) */
+  int32_t scale_dtype;       /* HUM_BF16 | HUM_F32 | HUM_E8M0 */
+  int32_t has_zero_point;    /* 0/1; UINT4 only; zeros u8 [E][N][K/G] (0..15) */
+  int32_t has_global_scale;  /* 0/1; second-level f32 scale per expert, [E] */
+  int32_t act_fmt;           /* hum_act_fmt the layer runs with */
+  int32_t num_experts;       /* E >= 1 (dense layers use 1) */
+  int64_t n;                 /* output channels per expert */
+  int64_t k;                 /* reduction length */
+} hum_weight_desc;
+
+/* Tile / split-K configuration (output of the selector, or forced). */
+typedef struct hum_tile_config {
+  int32_t wave_m;    /* 16-row MFMA sub-tiles per wave (rows per WG = 16*wave_m) */
+  int32_t wave_n;    /* 16-column sub-tiles per wave */
+  int32_t waves_n;   /* waves of a workgroup side by side along N */
+  int32_t waves_k;   /* waves of a workgroup splitting K (in-WG split-K) */
+  int32_t split_k;   /* workgroups splitting K (cross-WG split-K, fp32 partials) */
+  int32_t block_m;   /* MoE: rows per expert block (multiple of 16*wave_m) */
+} hum_tile_config;
+
+/* ---- weight preparation ------------------------------------------------ */
+
+/* Bytes of the packed (kernel-layout) buffer for `desc`; 0 if the
+ * description is invalid or unsupported (see hum_last_error()). */
+size_t hum_packed_weight_bytes(const hum_weight_desc* desc);
+
+/* Canonical ("standard format") tensors -> packed kernel layout.
+ *   codes  : u8 [E][N][K/2] (4-bit) or [E][N][K] (E4M3)
+ *   scales : [E][N'][K/G'] in scale_dtype (N' = 1 for TENSOR, G' per gran)
+ *   zeros  : u8 [E][N'][K/G'] or NULL when has_zero_point == 0
+ *   global_scale : f32 [E] or NULL when has_global_scale == 0
+ *   packed : device buffer of at least hum_packed_weight_bytes(desc)
+ * Pads N to a multiple of 16 with codes that decode to zero and converts
+ * group size K (and per-tensor scales) to the per-channel form. */
+hum_status hum_prepare_weight(const hum_weight_desc* desc, const void* codes,
+                              const void* scales, const void* zeros,
+                              const float* global_scale, void* packed,
+                              size_t packed_bytes, void* stream);
+
+/* Test export: packed -> f32 [E][N][K] of (v(q) - z) * S, excluding the
+ * second-level scale.  Exact for every supported format. */
+hum_status hum_dequant_weight(const hum_weight_desc* desc, const void* packed,
+                              float* out, void* stream);
+
+/* ---- activation quantizer ---------------------------------------------- */
+
+/* bf16 x [m][k] (row stride ld_x elements) -> E4M3 codes q [m][k] plus
+ *   HUM_ACT_FP8_TOKEN : scales f32 [m], s = amax/448 (1 for a zero row),
+ *                       q = E4M3_RNE_SAT(x / s) with an IEEE f32 division;
+ *   HUM_ACT_MXFP8     : scales u8 [m][k/32], E = clamp(floor(log2 amax) - 8
+ *                       + 127, 0, 254) (127 for a zero block),
+ *                       q = E4M3_RNE_SAT(x / 2^(E-127)).
+ * The formats are those named in the "End-to-end inference performance"
+ * ("tokenwise FP8") and "Choosing the activation type" (MXFP8) sections of
+ * the Humming announcement; the scale rules are the OCP ones.
+ * k must be a multiple of 32 for MXFP8. */
+hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf16,
+                         int64_t ld_x, void* q, void* scales, void* stream);
+
+/* ---- dense layer --------------------------------------------------------- */
+
+/* Workspace bytes hum_linear needs for m rows (quantized activations,
+ * row sums, split-K partials and counters). */
+size_t hum_linear_workspace_bytes(const hum_weight_desc* desc, int64_t m);
+
+/* C[m][n] = A[m][:] . W[n][:] (+ bias[n]) -> bf16, fp32 accumulation
+ * ("WnA16" and "W8A8 / W4A8 / W4A4" sections of the Humming announcement).
+ *   a        : bf16 [m][k]; or, when act_fmt != BF16 and a_scales != NULL,
+ *              already-quantized E4M3 codes [m][k] with their scales
+ *              (f32 [m] for FP8_TOKEN, u8 [m][k/32] for MXFP8)
+ *   bias     : bf16 [n] or NULL
+ *   out      : bf16 [m][n] (row stride n)
+ *   workspace: device buffer of hum_linear_workspace_bytes(desc, m) bytes.
+ *              Its first 256 KiB are split-K tickets: they must be zero
+ *              before the first call (hum_prepare_workspace() zeroes a
+ *              buffer) and every call leaves them zero again, so one buffer
+ *              serves any sequence of hum_linear / hum_moe_gemm calls that
+ *              are ordered on one stream.  Calls that overlap in time must
+ *              use different workspaces.
+ * Only num_experts == 1 descriptions are dense layers. */
+hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m,
+                      const void* a, const void* a_scales, const void* bias,
+                      void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* hum_linear with an explicit tile configuration (NULL = selector). */
+hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m,
+                         const void* a, const void* a_scales, const void* bias,
+                         void* out, void* workspace, size_t ws_bytes,
+                         const hum_tile_config* cfg, void* stream);
+
+/* Workspace bytes hum_linear_ex needs with configuration `cfg`
+ * (NULL = the selector's choice). */
+size_t hum_linear_workspace_bytes_ex(const hum_weight_desc* desc, int64_t m,
+                                     const hum_tile_config* cfg);
+
+/* Zero a workspace before its first use (enqueued on `stream`). */
+hum_status hum_prepare_workspace(void* workspace, size_t ws_bytes, void* stream);
+
+/* Selector: the tile / split-K configuration hum_linear would use for m
+ * rows (pure host function of the description, m and the device).  Device
+ * heuristics per M range follow "Device-parameter tuning" in the Humming
+ * announcement. */
+hum_status hum_select_config(const hum_weight_desc* desc, int64_t m,
+                             hum_tile_config* cfg_out);
+
+/* ---- MoE layer ----------------------------------------------------------- */
+
+/* Workspace bytes hum_moe_gemm needs for T tokens routed to topk experts. */
+size_t hum_moe_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2,
+                               int64_t num_tokens, int32_t topk);
+
+/* Full MoE expert layer ("indexed" grouping: rows gathered through the
+ * sorted routing ids; SGLang PR #23754 summary, "Key source snippets"):
+ *   align (sort token slots by expert) -> gate_up grouped GEMM with a fused
+ *   SwiGLU (a = silu(h[:I]) * h[I:], requantized to MXFP8 for W4A8) -> down
+ *   grouped GEMM -> top-k weighted reduce.
+ *   w13 : [E][2I][H] description + packed buffer; w2 : [E][H][I]
+ *   x   : bf16 [T][H]; topk_ids i32 [T][topk]; topk_weights f32 [T][topk]
+ *   out : bf16 [T][H]
+ * topk_ids must lie in [0, E).  At most 512 experts.
+ * No device->host synchronization: grids are sized from T, topk and E. */
+hum_status hum_moe_gemm(const hum_weight_desc* w13, const void* packed_w13,
+                        const hum_weight_desc* w2, const void* packed_w2,
+                        int64_t num_tokens, int32_t topk, const void* x_bf16,
+                        const int32_t* topk_ids, const float* topk_weights,
+                        void* out_bf16, void* workspace, size_t ws_bytes, void* stream);
+
+/* hum_moe_gemm with an explicit configuration (NULL = selector); the gate_up
+ * and down GEMMs share cfg's tile shape and block_m = 16 * cfg->wave_m
+ * (wave_n must be a multiple of 4 for the MXFP8 SwiGLU epilogue). */
+hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13,
+                           const hum_weight_desc* w2, const void* packed_w2,
+                           int64_t num_tokens, int32_t topk, const void* x_bf16,
+                           const int32_t* topk_ids, const float* topk_weights,
+                           void* out_bf16, void* workspace, size_t ws_bytes,
+                           const hum_tile_config* cfg, void* stream);
+
+/* Workspace bytes hum_moe_gemm_ex needs with configuration `cfg`. */
+size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_desc* w2,
+                                  int64_t num_tokens, int32_t topk,
+                                  const hum_tile_config* cfg);
+
+/* Stage export: sort the flat routing slots f = t*topk + j by expert.
+ *   sorted  : i32 [T*topk + E*(block_m-1)]; segment of expert e starts at
+ *             offsets[e], holds its slots in ascending f, is padded to a
+ *             multiple of block_m with the sentinel T*topk (as is the tail)
+ *   offsets : i32 [E+1]; counts : i32 [E]
+ * ("moe_align_block_size" / "moe_permute_prepare" in the SGLang PR #23754
+ * summary, "Implementation breakdown" and "Review highlights"). */
+hum_status hum_moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t topk,
+                         int32_t num_experts, int32_t block_m, int32_t* sorted,
+                         int32_t* offsets, int32_t* counts, void* stream);
+
+/* Stage export: out[t] = bf16(sum_j w[t][j] * y[t*topk + j]) with y bf16
+ * [T*topk][h] indexed by flat slot, fp32 sum in fixed j order
+ * ("moe_fused_mul_sum" in the SGLang PR #23754 summary). */
+hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights,
+                          int64_t num_tokens, int32_t topk, int64_t h,
+                          void* out_bf16, void* stream);
+
+/* Thread-local description of the last error (empty string if none). */
+const char* hum_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HUM_H_ */

@@ -1,0 +1,337 @@
+"""Python binding of libhum (MI355X / gfx950 quantized GEMM).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libhum.so``; PyTorch provides device memory and the current
+stream.  The names mirror the C ABI in ``include/hum.h``.  If the library is
+not built, every entry point raises -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+__all__ = [
+    "HumError", "WeightDesc", "TileConfig", "lib_path", "load_library",
+    "BF16", "F32", "INT4", "UINT4", "E2M1", "E4M3", "E8M0",
+    "SCALE_TENSOR", "SCALE_CHANNEL", "SCALE_GROUP",
+    "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8",
+    "packed_weight_bytes", "prepare_weight", "dequant_weight", "quant_act",
+    "select_config", "linear_workspace_bytes", "linear", "moe_workspace_bytes",
+    "moe_gemm", "moe_align", "moe_reduce", "Workspace", "header_functions",
+]
+
+BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0 = range(7)
+SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP = range(3)
+ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8 = range(3)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_HERE), "include", "hum.h")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libhum.so")
+
+
+class HumError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hum status {status}: {msg}")
+        self.status = status
+
+
+class WeightDesc(ctypes.Structure):
+    _fields_ = [
+        ("weight_dtype", ctypes.c_int32), ("scale_gran", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("scale_dtype", ctypes.c_int32),
+        ("has_zero_point", ctypes.c_int32), ("has_global_scale", ctypes.c_int32),
+        ("act_fmt", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+    ]
+
+    def __repr__(self):
+        return ("WeightDesc(" + ", ".join(f"{f}={getattr(self, f)}" for f, _ in self._fields_) + ")")
+
+
+class TileConfig(ctypes.Structure):
+    _fields_ = [
+        ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32), ("waves_n", ctypes.c_int32),
+        ("waves_k", ctypes.c_int32), ("split_k", ctypes.c_int32), ("block_m", ctypes.c_int32),
+    ]
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f, _ in self._fields_)
+
+    def __repr__(self):
+        return "TileConfig(" + ", ".join(f"{f}={getattr(self, f)}" for f, _ in self._fields_) + ")"
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_DP = ctypes.POINTER(WeightDesc)
+_CP = ctypes.POINTER(TileConfig)
+
+_SIGS = {
+    "hum_last_error": (ctypes.c_char_p, []),
+    "hum_packed_weight_bytes": (_SZ, [_DP]),
+    "hum_prepare_weight": (_I32, [_DP, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hum_dequant_weight": (_I32, [_DP, _P, _P, _P]),
+    "hum_quant_act": (_I32, [_I32, _I64, _I64, _P, _I64, _P, _P, _P]),
+    "hum_linear_workspace_bytes": (_SZ, [_DP, _I64]),
+    "hum_linear_workspace_bytes_ex": (_SZ, [_DP, _I64, _CP]),
+    "hum_linear": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hum_linear_ex": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
+    "hum_prepare_workspace": (_I32, [_P, _SZ, _P]),
+    "hum_select_config": (_I32, [_DP, _I64, _CP]),
+    "hum_moe_workspace_bytes": (_SZ, [_DP, _DP, _I64, _I32]),
+    "hum_moe_workspace_bytes_ex": (_SZ, [_DP, _DP, _I64, _I32, _CP]),
+    "hum_moe_gemm": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "hum_moe_gemm_ex": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
+    "hum_moe_align": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "hum_moe_reduce": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/hum.h declares."""
+    txt = open(_HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(hum_\w+)\s*\(", txt)))
+
+
+def load_library():
+    """Load libhum.so (raises if it is missing: the library has no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                           "(quantized_gemm_packed_amd.build.build_library())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise HumError(status, load_library().hum_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3}
+_GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP}
+_SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0}
+_AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8}
+
+
+def make_desc(weight_dtype, scale_gran, group_size, scale_dtype, n, k, num_experts=1,
+              has_zero=False, has_global=False, act_fmt="bf16") -> WeightDesc:
+    """Build a WeightDesc from names ("int4", "group", "bf16", ...)."""
+    d = WeightDesc()
+    d.weight_dtype = _DT.get(weight_dtype, weight_dtype)
+    d.scale_gran = _GR.get(scale_gran, scale_gran)
+    d.group_size = int(group_size)
+    d.scale_dtype = _SD.get(scale_dtype, scale_dtype)
+    d.has_zero_point = int(bool(has_zero))
+    d.has_global_scale = int(bool(has_global))
+    d.act_fmt = _AF.get(act_fmt, act_fmt)
+    d.num_experts = int(num_experts)
+    d.n = int(n)
+    d.k = int(k)
+    return d
+
+
+__all__.append("make_desc")
+
+
+def packed_weight_bytes(desc: WeightDesc) -> int:
+    b = load_library().hum_packed_weight_bytes(ctypes.byref(desc))
+    if b == 0:
+        raise HumError(2, load_library().hum_last_error().decode())
+    return b
+
+
+def prepare_weight(desc: WeightDesc, codes, scales, zeros=None, global_scale=None, packed=None):
+    """Canonical device tensors -> packed uint8 device tensor."""
+    import torch
+    for t, nm in ((codes, "codes"), (scales, "scales"), (zeros, "zeros"), (global_scale, "global_scale")):
+        _gpu(t, nm)
+    nb = packed_weight_bytes(desc)
+    if packed is None:
+        packed = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    _check(load_library().hum_prepare_weight(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                             _ptr(global_scale), _ptr(packed), packed.numel(),
+                                             _stream(codes.device)))
+    return packed
+
+
+def dequant_weight(desc: WeightDesc, packed):
+    import torch
+    _gpu(packed, "packed")
+    out = torch.empty((desc.num_experts, desc.n, desc.k), dtype=torch.float32, device=packed.device)
+    _check(load_library().hum_dequant_weight(ctypes.byref(desc), _ptr(packed), _ptr(out), _stream(packed.device)))
+    return out
+
+
+def quant_act(act_fmt, x):
+    """bf16 x [m, k] -> (E4M3 codes uint8 [m, k], scales)."""
+    import torch
+    _gpu(x, "x")
+    fmt = _AF.get(act_fmt, act_fmt)
+    m, k = x.shape
+    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if fmt == ACT_FP8_TOKEN:
+        s = torch.empty((m,), dtype=torch.float32, device=x.device)
+    else:
+        s = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _check(load_library().hum_quant_act(fmt, m, k, _ptr(x), k, _ptr(q), _ptr(s), _stream(x.device)))
+    return q, s
+
+
+def select_config(desc: WeightDesc, m: int) -> TileConfig:
+    c = TileConfig()
+    _check(load_library().hum_select_config(ctypes.byref(desc), int(m), ctypes.byref(c)))
+    return c
+
+
+def linear_workspace_bytes(desc: WeightDesc, m: int, cfg: TileConfig | None = None) -> int:
+    lib = load_library()
+    if cfg is None:
+        return lib.hum_linear_workspace_bytes(ctypes.byref(desc), int(m))
+    return lib.hum_linear_workspace_bytes_ex(ctypes.byref(desc), int(m), ctypes.byref(cfg))
+
+
+class Workspace:
+    """A zero-initialised device buffer that grows on demand.  The library
+    leaves its split-K counters zero after every call, so one buffer serves
+    any sequence of calls on one stream."""
+
+    def __init__(self, device):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        import torch
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_WS: dict = {}
+
+
+def _workspace(device):
+    import torch
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    if key not in _WS:
+        _WS[key] = Workspace(torch.device("cuda", key))
+    return _WS[key]
+
+
+def linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, cfg: TileConfig | None = None,
+           workspace=None):
+    """bf16 out [m, n] = A @ W^T (+ bias)."""
+    import torch
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias")):
+        _gpu(t, nm)
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, desc.n), dtype=torch.bfloat16, device=a.device)
+    need = linear_workspace_bytes(desc, m, cfg)
+    ws = workspace if workspace is not None else _workspace(a.device).get(need)
+    wsb = 0 if ws is None else ws.numel()
+    lib = load_library()
+    _check(lib.hum_linear_ex(ctypes.byref(desc), _ptr(packed), m, _ptr(a), _ptr(a_scales), _ptr(bias), _ptr(out),
+                             _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg), _stream(a.device)))
+    return out
+
+
+def moe_workspace_bytes(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, cfg: TileConfig | None = None) -> int:
+    lib = load_library()
+    if cfg is None:
+        return lib.hum_moe_workspace_bytes(ctypes.byref(w13), ctypes.byref(w2), int(t), int(topk))
+    return lib.hum_moe_workspace_bytes_ex(ctypes.byref(w13), ctypes.byref(w2), int(t), int(topk), ctypes.byref(cfg))
+
+
+def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids, topk_weights, out=None,
+             cfg: TileConfig | None = None, workspace=None):
+    """bf16 out [T, H] of the MoE expert layer."""
+    import torch
+    for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"), (topk_ids, "topk_ids"),
+                  (topk_weights, "topk_weights")):
+        _gpu(t, nm)
+    t_count, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((t_count, w13.k), dtype=torch.bfloat16, device=x.device)
+    need = moe_workspace_bytes(w13, w2, t_count, topk, cfg)
+    if need == 0 and t_count > 0:
+        raise HumError(2, load_library().hum_last_error().decode())
+    ws = workspace if workspace is not None else _workspace(x.device).get(need)
+    wsb = 0 if ws is None else ws.numel()
+    _check(load_library().hum_moe_gemm_ex(ctypes.byref(w13), _ptr(packed_w13), ctypes.byref(w2), _ptr(packed_w2),
+                                          t_count, topk, _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
+                                          _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg),
+                                          _stream(x.device)))
+    return out
+
+
+def moe_align(topk_ids, num_experts: int, block_m: int):
+    """-> (sorted int32 [T*topk + E*(block_m-1)], offsets int32 [E+1], counts int32 [E])."""
+    import torch
+    _gpu(topk_ids, "topk_ids")
+    t, k = topk_ids.shape
+    cap = t * k + num_experts * (block_m - 1)
+    dev = topk_ids.device
+    srt = torch.empty(cap, dtype=torch.int32, device=dev)
+    off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    cnt = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    _check(load_library().hum_moe_align(_ptr(topk_ids), t, k, num_experts, block_m, _ptr(srt), _ptr(off), _ptr(cnt),
+                                        _stream(dev)))
+    return srt, off, cnt
+
+
+def moe_reduce(y, topk_weights):
+    """y bf16 [T*topk, H], w f32 [T, topk] -> bf16 [T, H]."""
+    import torch
+    _gpu(y, "y")
+    _gpu(topk_weights, "topk_weights")
+    t, k = topk_weights.shape
+    h = y.shape[1]
+    out = torch.empty((t, h), dtype=torch.bfloat16, device=y.device)
+    _check(load_library().hum_moe_reduce(_ptr(y), _ptr(topk_weights), t, k, h, _ptr(out), _stream(y.device)))
+    return out
+
+
+@dataclass
+class _Version:
+    arch: str = "gfx950"
+
+
+version = _Version()

@@ -1,0 +1,287 @@
+// Activation quantizers, MoE routing align and the top-k weighted reduce.
+//
+// * Activation formats: "tokenwise FP8" (Announcing Humming, section
+//   "End-to-end inference performance") and MXFP8 (section "Choosing the
+//   activation type"); scale rules are the OCP ones (see hum.h).
+// * Align = "moe_align_block_size" / "moe_permute_prepare" and reduce =
+//   "moe_fused_mul_sum" of the SGLang PR #23754 summary ("Implementation
+//   breakdown", "Review highlights").  Both are written for gfx950 here: one
+//   workgroup sorts by expert with wave ballots (stable, no atomics on the
+//   output order), and the reduce streams 16-byte rows.
+#include "dev_common.h"
+#include "hum_internal.h"
+
+namespace hum {
+
+static inline unsigned cdiv_u(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------------------
+// Per-token FP8: one workgroup per row.
+
+__global__ __launch_bounds__(256) void quant_fp8_token_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                              int64_t k, uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * ldx;
+  const int tid = threadIdx.x;
+  __shared__ float red[4];
+  float amax = 0.0f;
+  for (int64_t c = (int64_t)tid * 8; c < k; c += 256 * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[i] & 0xFFFF)));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(v[i] >> 16)));
+    }
+  }
+  amax = row16_max(amax);
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE f32 division
+  if (tid == 0) s[row] = sc;
+  uint8_t* qr = q + row * k;
+  for (int64_t c = (int64_t)tid * 8; c < k; c += 256 * 8) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xr + c);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_bits_to_f32(v[i] & 0xFFFF) / sc;
+      const float b = bf16_bits_to_f32(v[i] >> 16) / sc;
+      const uint32_t p = f32x2_to_e4m3x2(a, b);
+      if (i < 2) w0 |= p << (16 * i);
+      else w1 |= p << (16 * (i - 2));
+    }
+    uint2 o;
+    o.x = w0;
+    o.y = w1;
+    *reinterpret_cast<uint2*>(qr + c) = o;
+  }
+}
+
+hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
+                                  float* s, void* stream) {
+  if (m == 0) return HUM_OK;
+  quant_fp8_token_kernel<<<(unsigned)m, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), ldx, k, static_cast<uint8_t*>(q), s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_fp8_token launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8: each thread quantizes 8 elements; a DPP quad owns one 32-block.
+
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ s) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;  // chunks per row
+  const bool valid = id < m * cpr;
+  const int64_t row = valid ? id / cpr : 0;
+  const int64_t c8 = valid ? id % cpr : 0;
+  u32x4_t v = {0, 0, 0, 0};
+  if (valid) v = *reinterpret_cast<const u32x4_t*>(x + row * ldx + c8 * 8);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFF);
+    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+  amax = quad_max(amax);  // the 4 chunks of one 32-block are one DPP quad
+  const int e = mx_scale_code(amax);
+  const float inv = mx_inv_scale(e);
+  if (!valid) return;
+  uint2 o;
+  o.x = f32x2_to_e4m3x2(f[0] * inv, f[1] * inv) | (f32x2_to_e4m3x2(f[2] * inv, f[3] * inv) << 16);
+  o.y = f32x2_to_e4m3x2(f[4] * inv, f[5] * inv) | (f32x2_to_e4m3x2(f[6] * inv, f[7] * inv) << 16);
+  *reinterpret_cast<uint2*>(q + row * k + c8 * 8) = o;
+  if ((c8 & 3) == 0) s[row * (k / 32) + c8 / 4] = (uint8_t)e;
+}
+
+hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
+                              uint8_t* s, void* stream) {
+  if (m == 0) return HUM_OK;
+  const int64_t chunks = m * (k / 8);
+  quant_mxfp8_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp8 launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fill kernel (used instead of hipMemsetAsync so the path stays capturable).
+
+__global__ void zero_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hum_status launch_zero(void* p, size_t bytes, void* stream) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words == 0) return HUM_OK;
+  int64_t g = (words + 255) / 256;
+  if (g > 4096) g = 4096;
+  zero_kernel<<<(unsigned)g, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<uint32_t*>(p), words);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "zero launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Align: stable counting sort of the flat slots f = t*topk + j by expert,
+// segments padded to block_m, plus the block -> expert map of the GEMMs.
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+constexpr int kMaxExperts = 512;
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                              int32_t num_experts, int32_t block_m,
+                                                              int32_t* __restrict__ sorted, int64_t cap,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ block_expert,
+                                                              int64_t nblocks) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts + 1];
+  __shared__ int32_t running[kMaxExperts];
+  __shared__ int32_t wcnt[kAlignWaves][kMaxExperts];  // per-wave counts of one chunk
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int32_t E = num_experts;
+  const int32_t sentinel = (int32_t)n;
+  for (int64_t i = tid; i < cap; i += kAlignThreads) sorted[i] = sentinel;
+  for (int e = tid; e < E; e += kAlignThreads) {
+    cnt[e] = 0;
+    running[e] = 0;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += kAlignThreads) {
+    const int32_t e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    off[0] = 0;
+    for (int e = 0; e < E; ++e) {
+      acc += (cnt[e] + block_m - 1) / block_m * block_m;
+      off[e + 1] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kAlignThreads) offsets[e] = off[e];
+  for (int e = tid; e < E; e += kAlignThreads) counts[e] = cnt[e];
+  for (int64_t b = tid; b < nblocks; b += kAlignThreads) {
+    const int64_t pos = b * block_m;
+    int32_t ex = -1;
+    if (pos < off[E]) {
+      int lo = 0, hi = E - 1;  // largest e with off[e] <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= pos) lo = mid;
+        else hi = mid - 1;
+      }
+      ex = lo;
+    }
+    block_expert[b] = ex;
+  }
+  // Stable scatter, 1024 slots per chunk.  Lanes of a wave holding the same
+  // expert are found with one ballot per id bit; per-wave counts go through
+  // an LDS table so that a slot's position is
+  //   segment start + earlier chunks + earlier waves + earlier lanes.
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = 0; base < n; base += kAlignThreads) {
+    const int64_t i = base + tid;
+    int32_t e = (i < n) ? ids[i] : -1;
+    if (e < 0 || e >= E) e = -1;
+    const uint32_t key = (uint32_t)(e + 1);
+    uint64_t same = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1u;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank_w = __popcll(same & lt_mask);
+    const bool leader = (same & lt_mask) == 0;
+    for (int idx = tid; idx < kAlignWaves * E; idx += kAlignThreads) wcnt[idx / E][idx % E] = 0;
+    __syncthreads();
+    if (leader && e >= 0) wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (e >= 0) {
+      int32_t prefix = 0;
+      for (int w = 0; w < wave; ++w) prefix += wcnt[w][e];
+      sorted[off[e] + running[e] + prefix + rank_w] = (int32_t)i;
+    }
+    __syncthreads();
+    for (int ex = tid; ex < E; ex += kAlignThreads) {
+      int32_t tot = 0;
+      for (int w = 0; w < kAlignWaves; ++w) tot += wcnt[w][ex];
+      running[ex] += tot;
+    }
+    __syncthreads();
+  }
+}
+
+hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e, int32_t block_m,
+                        int32_t* sorted, int32_t* offsets, int32_t* counts, int32_t* block_expert,
+                        int64_t nblocks, void* stream) {
+  if (e > kMaxExperts) return set_error(HUM_ERR_UNSUPPORTED, "align: at most %d experts", kMaxExperts);
+  const int64_t n = t * topk;
+  const int64_t cap = n + (int64_t)e * (block_m - 1);
+  align_kernel<<<1, kAlignThreads, 0, static_cast<hipStream_t>(stream)>>>(ids, n, e, block_m, sorted, cap,
+                                                                          offsets, counts, block_expert, nblocks);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "align launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Reduce: out[t][:] = bf16(sum_j w[t][j] * y[t*topk + j][:]), fp32, j order.
+
+__global__ __launch_bounds__(256) void moe_reduce_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
+                                                         int64_t t_count, int32_t topk, int64_t h,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t cpr = h / 8;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= t_count * cpr) return;
+  const int64_t t = id / cpr, c8 = id % cpr;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < topk; ++j) {
+    const float wj = w[t * topk + j];
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + (t * topk + j) * h + c8 * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += wj * bf16_bits_to_f32(v[i] & 0xFFFF);
+      acc[2 * i + 1] += wj * bf16_bits_to_f32(v[i] >> 16);
+    }
+  }
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_bits(acc[2 * i]) | (f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<u32x4_t*>(out + t * h + c8 * 8) = o;
+}
+
+hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t topk, int64_t h,
+                             void* out, void* stream) {
+  if (t == 0) return HUM_OK;
+  moe_reduce_kernel<<<cdiv_u(t * (h / 8), 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(y), w, t, topk, h, static_cast<uint16_t*>(out));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "moe_reduce launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+}  // namespace hum

@@ -1,0 +1,577 @@
+// C ABI entry points: description checks, packed layout, the tile / split-K
+// selector, workspace carving and dispatch.  Host code only.
+//
+// The selector follows the idea of "Device-parameter tuning" in "Announcing
+// Humming: Fast, Flexible Kernels for Quantized Inference": the shape, the
+// format and the device's resources (here: 256 CUs, 160 KB LDS, wave64)
+// choose a tile and split per M range, at run time, with no compilation.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "hum_internal.h"
+
+namespace hum {
+
+static thread_local char g_err[512];
+
+hum_status set_error(hum_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// Every workspace starts with the same ticket area for cross-workgroup
+// split-K.  The last workgroup of each tile resets its ticket, so the area is
+// zero after every call whatever layout the rest of the buffer had.
+static const int64_t kMaxTickets = 65536;
+static const int64_t kTicketBytes = kMaxTickets * 4;
+
+hum_status check_desc(const hum_weight_desc* d) {
+  if (!d) return set_error(HUM_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_experts < 1) return set_error(HUM_ERR_INVALID_ARG, "num_experts must be >= 1");
+  if (d->n < 1) return set_error(HUM_ERR_INVALID_ARG, "n must be >= 1");
+  if (d->k < 128 || d->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "k must be a positive multiple of 128 (got %lld)", (long long)d->k);
+  if (d->n > (int64_t)1 << 30 || d->k > (int64_t)1 << 30) return set_error(HUM_ERR_UNSUPPORTED, "n/k too large");
+  if (d->has_zero_point != 0 && d->has_zero_point != 1) return set_error(HUM_ERR_INVALID_ARG, "has_zero_point must be 0/1");
+  if (d->has_global_scale != 0 && d->has_global_scale != 1) return set_error(HUM_ERR_INVALID_ARG, "has_global_scale must be 0/1");
+  if (d->scale_gran < HUM_SCALE_TENSOR || d->scale_gran > HUM_SCALE_GROUP) return set_error(HUM_ERR_INVALID_ARG, "bad scale_gran");
+  if (d->scale_gran == HUM_SCALE_GROUP) {
+    if (d->group_size <= 0 || d->k % d->group_size) return set_error(HUM_ERR_INVALID_ARG, "group_size must divide k");
+  }
+  switch (d->weight_dtype) {
+    case HUM_INT4:
+    case HUM_UINT4:
+      if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "integer weights run with bf16 activations");
+      if (d->scale_dtype != HUM_BF16 && d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "integer weights take bf16 or f32 scales");
+      if (d->scale_gran == HUM_SCALE_GROUP && d->group_size % 128) return set_error(HUM_ERR_UNSUPPORTED, "integer group_size must be a multiple of 128");
+      if (d->has_zero_point && d->weight_dtype != HUM_UINT4) return set_error(HUM_ERR_UNSUPPORTED, "zero points need UINT4 codes");
+      return HUM_OK;
+    case HUM_E2M1:
+      if (d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32 || d->scale_dtype != HUM_E8M0)
+        return set_error(HUM_ERR_UNSUPPORTED, "E2M1 weights need E8M0 scales per 32 along K (MXFP4)");
+      if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E2M1 takes no zero point");
+      if (d->act_fmt != HUM_ACT_BF16 && d->act_fmt != HUM_ACT_MXFP8) return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 runs with bf16 or MXFP8 activations");
+      return HUM_OK;
+    case HUM_E4M3:
+      if (d->scale_gran == HUM_SCALE_GROUP) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take per-channel or per-tensor scales");
+      if (d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take f32 scales");
+      if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 takes no zero point");
+      if (d->act_fmt != HUM_ACT_FP8_TOKEN) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights run with per-token FP8 activations");
+      return HUM_OK;
+    default:
+      return set_error(HUM_ERR_UNSUPPORTED, "unsupported weight dtype %d", d->weight_dtype);
+  }
+}
+
+int fmt_of(const hum_weight_desc* d) {
+  if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
+  if (d->weight_dtype == HUM_E4M3) return F_FP8;
+  return d->act_fmt == HUM_ACT_MXFP8 ? F_MXFP4_MXFP8 : F_MXFP4_BF16;
+}
+
+hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
+  hum_status st = check_desc(d);
+  if (st != HUM_OK) return st;
+  *L = Layout();
+  L->nt = cdiv(d->n, kNSub);
+  L->kb = d->k / kKBlk;
+  L->kb4 = cdiv(L->kb, 4);
+  const int f = fmt_of(d);
+  L->code_bytes = (f == F_FP8) ? 32 : 16;
+  L->codes_per_expert = L->nt * L->kb * 64 * L->code_bytes;
+  if (f == F_INT) {
+    const bool grp = d->scale_gran == HUM_SCALE_GROUP && d->group_size < d->k;
+    L->ng = grp ? d->k / d->group_size : 1;
+    L->kb_per_group = grp ? d->group_size / kKBlk : (int)L->kb;
+    L->scale_f32 = d->scale_dtype == HUM_F32;
+    L->scales_per_expert = align256(L->nt * L->ng * 16 * (L->scale_f32 ? 4 : 2));
+    L->zeros_per_expert = d->has_zero_point ? align256(L->nt * L->ng * 8) : 0;
+  } else if (f == F_FP8) {
+    L->ng = 1;
+    L->scales_per_expert = align256(L->nt * 16 * 4);
+  } else {
+    L->ng = L->kb * 4;
+    L->scales_per_expert = L->nt * L->kb4 * 64 * 4;
+  }
+  const int64_t E = d->num_experts;
+  L->codes_off = 0;
+  L->scales_off = align256(E * L->codes_per_expert);
+  L->zeros_off = align256(L->scales_off + E * L->scales_per_expert);
+  L->gscale_off = align256(L->zeros_off + E * L->zeros_per_expert);
+  L->total = align256(L->gscale_off + E * 4);
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Selector.
+
+static const int kCUs = 256;
+
+static bool cfg_valid_dense(const hum_weight_desc* d, const hum_tile_config& c) {
+  KernelKey k{fmt_of(d), c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
+  return gemm_instance_exists(k) && c.split_k >= 1;
+}
+
+// Split so that the grid reaches `target` workgroups, keeping at least one
+// stage of K-blocks per split.
+static int pick_split(int64_t tiles, int64_t kb, int waves_k, int64_t target) {
+  int64_t s = 1;
+  while (tiles * s < target && kb / (waves_k * (s * 2)) >= 1 && s < 16) s *= 2;
+  return (int)s;
+}
+
+static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
+  hum_tile_config c{};
+  const int64_t nt = cdiv(d->n, kNSub);
+  const int64_t kb = d->k / kKBlk;
+  if (m <= 16) {
+    c.wave_m = 1; c.wave_n = 1; c.waves_n = 1; c.waves_k = 4;
+  } else if (m <= 32) {
+    c.wave_m = 2; c.wave_n = 2; c.waves_n = 2; c.waves_k = 2;
+  } else if (m <= 64) {
+    c.wave_m = 4; c.wave_n = 2; c.waves_n = 2; c.waves_k = 2;
+  } else if (m <= 128) {
+    c.wave_m = 4; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+  } else {
+    c.wave_m = 8; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+  }
+  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
+  const int64_t n_tiles = cdiv(nt, (int64_t)c.wave_n * c.waves_n);
+  c.split_k = (m_tiles * n_tiles > kMaxTickets) ? 1 : pick_split(m_tiles * n_tiles, kb, c.waves_k, 2 * kCUs);
+  c.block_m = 16 * c.wave_m;
+  return c;
+}
+
+static hum_tile_config select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
+  hum_tile_config c{};
+  const double rows = (double)t * topk / w13->num_experts;
+  if (rows <= 16) {
+    c.wave_m = 1; c.wave_n = 4; c.waves_n = 1; c.waves_k = 4;
+  } else if (rows <= 48) {
+    c.wave_m = 2; c.wave_n = 4; c.waves_n = 2; c.waves_k = 2;
+  } else if (rows <= 160) {
+    c.wave_m = 4; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+  } else {
+    c.wave_m = 8; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+  }
+  c.split_k = 1;
+  c.block_m = 16 * c.wave_m;
+  return c;
+}
+
+static void log_cfg(const char* what, const hum_tile_config& c, int64_t m) {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("HUM_LOG");
+    on = e && e[0] == '1';
+  }
+  if (on)
+    fprintf(stderr, "[hum] %s m=%lld wave_m=%d wave_n=%d waves_n=%d waves_k=%d split_k=%d block_m=%d\n", what,
+            (long long)m, c.wave_m, c.wave_n, c.waves_n, c.waves_k, c.split_k, c.block_m);
+}
+
+// ---------------------------------------------------------------------------
+// Dense workspace: [counters][partials][quantized activations][scales].
+
+struct DenseWs {
+  int64_t counters = 0, partials = 0, aq = 0, as = 0, total = 0;
+};
+
+static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_config& c, bool quant_a) {
+  DenseWs w;
+  const int64_t nt = cdiv(d->n, kNSub);
+  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
+  const int64_t n_tiles = cdiv(nt, (int64_t)c.wave_n * c.waves_n);
+  const int64_t tiles = m_tiles * n_tiles;
+  int64_t off = 0;
+  w.counters = off;
+  off = kTicketBytes;
+  w.partials = off;
+  off = align256(off + (c.split_k > 1 ? tiles * c.split_k * c.waves_n * (int64_t)c.wave_m * c.wave_n * 256 * 4 : 0));
+  w.aq = off;
+  if (quant_a) {
+    off = align256(off + m * d->k);
+    w.as = off;
+    off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 ? m * (d->k / 32) : m * 4));
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace hum
+
+using namespace hum;
+
+extern "C" {
+
+const char* hum_last_error(void) { return g_err; }
+
+size_t hum_packed_weight_bytes(const hum_weight_desc* desc) {
+  clear_error();
+  Layout L;
+  if (compute_layout(desc, &L) != HUM_OK) return 0;
+  return (size_t)L.total;
+}
+
+hum_status hum_prepare_weight(const hum_weight_desc* desc, const void* codes, const void* scales,
+                              const void* zeros, const float* global_scale, void* packed,
+                              size_t packed_bytes, void* stream) {
+  clear_error();
+  Layout L;
+  hum_status st = compute_layout(desc, &L);
+  if (st != HUM_OK) return st;
+  if (!codes || !scales || !packed) return set_error(HUM_ERR_INVALID_ARG, "codes, scales and packed must be non-NULL");
+  if (desc->has_zero_point && !zeros) return set_error(HUM_ERR_INVALID_ARG, "zeros is NULL but has_zero_point = 1");
+  if (desc->has_global_scale && !global_scale) return set_error(HUM_ERR_INVALID_ARG, "global_scale is NULL but has_global_scale = 1");
+  if (packed_bytes < (size_t)L.total) return set_error(HUM_ERR_WORKSPACE, "packed buffer too small (%zu < %lld)", packed_bytes, (long long)L.total);
+  return launch_repack(desc, L, codes, scales, zeros, global_scale, packed, stream);
+}
+
+hum_status hum_dequant_weight(const hum_weight_desc* desc, const void* packed, float* out, void* stream) {
+  clear_error();
+  Layout L;
+  hum_status st = compute_layout(desc, &L);
+  if (st != HUM_OK) return st;
+  if (!packed || !out) return set_error(HUM_ERR_INVALID_ARG, "packed and out must be non-NULL");
+  return launch_dequant(desc, L, packed, out, stream);
+}
+
+hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf16, int64_t ld_x, void* q,
+                         void* scales, void* stream) {
+  clear_error();
+  if (m < 0 || k <= 0 || ld_x < k) return set_error(HUM_ERR_INVALID_ARG, "bad m/k/ld_x");
+  if (m > 0 && (!x_bf16 || !q || !scales)) return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  if (k % 8 || ld_x % 8) return set_error(HUM_ERR_UNSUPPORTED, "k and ld_x must be multiples of 8");
+  if (act_fmt == HUM_ACT_FP8_TOKEN) return launch_quant_fp8_token(m, k, x_bf16, ld_x, q, static_cast<float*>(scales), stream);
+  if (act_fmt == HUM_ACT_MXFP8) {
+    if (k % 32) return set_error(HUM_ERR_UNSUPPORTED, "MXFP8 needs k % 32 == 0");
+    return launch_quant_mxfp8(m, k, x_bf16, ld_x, q, static_cast<uint8_t*>(scales), stream);
+  }
+  return set_error(HUM_ERR_INVALID_ARG, "act_fmt must be FP8_TOKEN or MXFP8");
+}
+
+hum_status hum_select_config(const hum_weight_desc* desc, int64_t m, hum_tile_config* cfg_out) {
+  clear_error();
+  hum_status st = check_desc(desc);
+  if (st != HUM_OK) return st;
+  if (!cfg_out || m < 0) return set_error(HUM_ERR_INVALID_ARG, "bad arguments");
+  *cfg_out = select_dense(desc, m < 1 ? 1 : m);
+  return HUM_OK;
+}
+
+size_t hum_linear_workspace_bytes_ex(const hum_weight_desc* desc, int64_t m, const hum_tile_config* cfg) {
+  clear_error();
+  if (check_desc(desc) != HUM_OK || m < 0) return 0;
+  const hum_tile_config c = cfg ? *cfg : select_dense(desc, m < 1 ? 1 : m);
+  return (size_t)dense_ws(desc, m < 1 ? 1 : m, c, desc->act_fmt != HUM_ACT_BF16).total;
+}
+
+size_t hum_linear_workspace_bytes(const hum_weight_desc* desc, int64_t m) {
+  return hum_linear_workspace_bytes_ex(desc, m, nullptr);
+}
+
+hum_status hum_prepare_workspace(void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (ws_bytes == 0) return HUM_OK;
+  if (!workspace) return set_error(HUM_ERR_INVALID_ARG, "workspace is NULL");
+  return launch_zero(workspace, ws_bytes, stream);
+}
+
+static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const Layout& L, const void* packed) {
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  p.codes = pk + L.codes_off;
+  p.wscale = pk + L.scales_off;
+  p.wzero = d->has_zero_point ? pk + L.zeros_off : nullptr;
+  p.gscale = reinterpret_cast<const float*>(pk + L.gscale_off);
+  p.codes_per_expert = L.codes_per_expert;
+  p.scales_per_expert = L.scales_per_expert;
+  p.zeros_per_expert = L.zeros_per_expert;
+  p.nt_count = (int)L.nt;
+  p.kb_count = (int)L.kb;
+  p.ng = (int)L.ng;
+  p.kb_per_group = L.kb_per_group;
+  p.kb4 = (int)L.kb4;
+  p.scale_f32 = L.scale_f32;
+  p.int_offset = (d->weight_dtype == HUM_INT4) ? 136 : 128;
+  p.has_zero = d->has_zero_point;
+  p.n = d->n;
+  p.swiglu_nt_off = 0;
+}
+
+static bool cfg_sane(const hum_tile_config& c) {
+  return c.wave_m >= 1 && c.wave_n >= 1 && c.waves_n >= 1 && c.waves_k >= 1 && c.waves_n * c.waves_k == 4 &&
+         c.split_k >= 1 && c.split_k <= 64;
+}
+
+hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a,
+                         const void* a_scales, const void* bias, void* out, void* workspace, size_t ws_bytes,
+                         const hum_tile_config* cfg, void* stream) {
+  clear_error();
+  Layout L;
+  hum_status st = compute_layout(desc, &L);
+  if (st != HUM_OK) return st;
+  if (desc->num_experts != 1) return set_error(HUM_ERR_INVALID_ARG, "hum_linear takes a dense (num_experts == 1) description");
+  if (m < 0) return set_error(HUM_ERR_INVALID_ARG, "m < 0");
+  if (m == 0) return HUM_OK;
+  if (!packed || !a || !out) return set_error(HUM_ERR_INVALID_ARG, "packed, a and out must be non-NULL");
+  hum_tile_config c = cfg ? *cfg : select_dense(desc, m);
+  if (!cfg_sane(c) || !cfg_valid_dense(desc, c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  const DenseWs w = dense_ws(desc, m, c, quant_a);
+  if (c.split_k > 1 && cdiv(m, 16 * c.wave_m) * cdiv(L.nt, (int64_t)c.wave_n * c.waves_n) > kMaxTickets)
+    return set_error(HUM_ERR_UNSUPPORTED, "split-K needs at most %lld output tiles", (long long)kMaxTickets);
+  if (w.total > 0 && (!workspace || ws_bytes < (size_t)w.total))
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
+  log_cfg("linear", c, m);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const void* a_use = a;
+  const void* as_use = a_scales;
+  if (quant_a) {
+    st = hum_quant_act(desc->act_fmt, m, desc->k, a, desc->k, ws + w.aq, ws + w.as, stream);
+    if (st != HUM_OK) return st;
+    a_use = ws + w.aq;
+    as_use = ws + w.as;
+  }
+  GemmParams p{};
+  fill_weight_params(p, desc, L, packed);
+  p.a = a_use;
+  p.lda = desc->k;
+  p.a_scale = as_use;
+  p.a_scale_ld = desc->k / 32;
+  p.m = m;
+  p.sorted = nullptr;
+  p.block_expert = nullptr;
+  p.topk = 1;
+  p.sentinel = 0;
+  p.out = out;
+  p.ldo = desc->n;
+  p.out_scale = nullptr;
+  p.bias = static_cast<const uint16_t*>(bias);
+  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
+  p.n_tiles = (int)cdiv(L.nt, (int64_t)c.wave_n * c.waves_n);
+  p.split_k = c.split_k;
+  p.kb_per_split = (int)cdiv(cdiv(L.kb, c.split_k), c.waves_k) * c.waves_k;
+  p.partials = reinterpret_cast<float*>(ws + w.partials);
+  p.counters = reinterpret_cast<int32_t*>(ws + w.counters);
+  KernelKey key{fmt_of(desc), c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
+  return launch_gemm(key, p, m_tiles, stream);
+}
+
+hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a, const void* a_scales,
+                      const void* bias, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// MoE.
+
+struct MoeWs {
+  int64_t counters = 0, partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0;
+  int64_t xq = 0, xs = 0, inter = 0, inter_s = 0, y = 0, total = 0;
+  int64_t cap = 0, nblocks = 0, tiles = 0;
+};
+
+static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
+                    const hum_tile_config& c) {
+  MoeWs w;
+  const int64_t E = w13->num_experts;
+  const int64_t bm = 16 * c.wave_m;
+  const int64_t inter = w2->k;
+  const int64_t h = w13->k;
+  w.cap = t * topk + E * (bm - 1);
+  w.nblocks = cdiv(w.cap, bm);
+  const int64_t nt_i = cdiv(inter, kNSub), nt_h = cdiv(h, kNSub);
+  const int64_t tiles_up = w.nblocks * cdiv(nt_i, (int64_t)(c.wave_n / 2) * c.waves_n);
+  const int64_t tiles_dn = w.nblocks * cdiv(nt_h, (int64_t)c.wave_n * c.waves_n);
+  w.tiles = tiles_up > tiles_dn ? tiles_up : tiles_dn;
+  const bool mx = w13->act_fmt == HUM_ACT_MXFP8;
+  int64_t off = 0;
+  w.counters = off;
+  off = kTicketBytes;
+  w.partials = off;
+  off = align256(off + (c.split_k > 1 ? w.tiles * c.split_k * c.waves_n * (int64_t)c.wave_m * c.wave_n * 256 * 4 : 0));
+  w.sorted = off;
+  off = align256(off + w.cap * 4);
+  w.offsets = off;
+  off = align256(off + (E + 1) * 4);
+  w.counts = off;
+  off = align256(off + E * 4);
+  w.bexp = off;
+  off = align256(off + w.nblocks * 4);
+  w.xq = off;
+  if (mx) {
+    off = align256(off + t * h);
+    w.xs = off;
+    off = align256(off + t * (h / 32));
+  }
+  w.inter = off;
+  off = align256(off + w.cap * inter * (mx ? 1 : 2));
+  w.inter_s = off;
+  if (mx) off = align256(off + w.cap * (inter / 32));
+  w.y = off;
+  off = align256(off + t * topk * h * 2);
+  w.total = off;
+  return w;
+}
+
+static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk) {
+  hum_status st = check_desc(w13);
+  if (st != HUM_OK) return st;
+  st = check_desc(w2);
+  if (st != HUM_OK) return st;
+  if (w13->num_experts != w2->num_experts) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 expert counts differ");
+  if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1)
+    return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs MXFP4 (E2M1 + E8M0) expert weights");
+  if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
+  if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");
+  if (w2->n != w13->k) return set_error(HUM_ERR_INVALID_ARG, "w2 n must equal the hidden size (w13 k)");
+  if (w2->k % 64) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 64");
+  if (w13->k % 8) return set_error(HUM_ERR_UNSUPPORTED, "hidden size must be a multiple of 8");
+  if (t < 0 || topk < 1 || topk > 64) return set_error(HUM_ERR_INVALID_ARG, "bad num_tokens / topk");
+  if (w13->num_experts > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
+  if ((t * topk + (int64_t)w13->num_experts * 127) >= ((int64_t)1 << 31)) return set_error(HUM_ERR_UNSUPPORTED, "too many tokens");
+  return HUM_OK;
+}
+
+size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
+                                  const hum_tile_config* cfg) {
+  clear_error();
+  if (check_moe(w13, w2, t, topk) != HUM_OK) return 0;
+  const hum_tile_config c = cfg ? *cfg : select_moe(w13, t, topk);
+  return (size_t)moe_ws(w13, w2, t, topk, c).total;
+}
+
+size_t hum_moe_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk) {
+  return hum_moe_workspace_bytes_ex(w13, w2, t, topk, nullptr);
+}
+
+hum_status hum_moe_align(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t e, int32_t block_m,
+                         int32_t* sorted, int32_t* offsets, int32_t* counts, void* stream) {
+  clear_error();
+  if (t < 0 || topk < 1 || e < 1 || block_m < 1) return set_error(HUM_ERR_INVALID_ARG, "bad sizes");
+  if (!sorted || !offsets || !counts || (t > 0 && !topk_ids)) return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  if (e > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
+  // The block -> expert map the GEMMs use is internal; this export skips it.
+  return launch_align(topk_ids, t, topk, e, block_m, sorted, offsets, counts, nullptr, 0, stream);
+}
+
+hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights, int64_t t, int32_t topk, int64_t h,
+                          void* out_bf16, void* stream) {
+  clear_error();
+  if (t < 0 || topk < 1 || h < 8 || h % 8) return set_error(HUM_ERR_INVALID_ARG, "bad sizes (h must be a multiple of 8)");
+  if (t > 0 && (!y_bf16 || !topk_weights || !out_bf16)) return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  return launch_moe_reduce(y_bf16, topk_weights, t, topk, h, out_bf16, stream);
+}
+
+hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                           const void* packed_w2, int64_t t, int32_t topk, const void* x_bf16,
+                           const int32_t* topk_ids, const float* topk_weights, void* out_bf16, void* workspace,
+                           size_t ws_bytes, const hum_tile_config* cfg, void* stream) {
+  clear_error();
+  hum_status st = check_moe(w13, w2, t, topk);
+  if (st != HUM_OK) return st;
+  if (t == 0) return HUM_OK;
+  if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
+    return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  const hum_tile_config c = cfg ? *cfg : select_moe(w13, t, topk);
+  if (!cfg_sane(c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  const int f = fmt_of(w13);
+  const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
+  KernelKey kup{f, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_GATHER, epi_up};
+  KernelKey kdn{f, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_SCATTER};
+  if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  const MoeWs w = moe_ws(w13, w2, t, topk, c);
+  if (c.split_k > 1 && w.tiles > kMaxTickets)
+    return set_error(HUM_ERR_UNSUPPORTED, "split-K needs at most %lld output tiles", (long long)kMaxTickets);
+  if (!workspace || ws_bytes < (size_t)w.total)
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
+  log_cfg("moe", c, t);
+  Layout L13, L2;
+  compute_layout(w13, &L13);
+  compute_layout(w2, &L2);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t E = w13->num_experts, h = w13->k, inter = w2->k;
+  const int32_t bm = 16 * c.wave_m;
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
+  st = launch_align(topk_ids, t, topk, (int32_t)E, bm, sorted, reinterpret_cast<int32_t*>(ws + w.offsets),
+                    reinterpret_cast<int32_t*>(ws + w.counts), bexp, w.nblocks, stream);
+  if (st != HUM_OK) return st;
+  const bool mx = f == F_MXFP4_MXFP8;
+  const void* x_use = x_bf16;
+  if (mx) {
+    st = launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
+    if (st != HUM_OK) return st;
+    x_use = ws + w.xq;
+  }
+  // gate_up (+ SwiGLU)
+  GemmParams p{};
+  fill_weight_params(p, w13, L13, packed_w13);
+  p.n = inter;
+  p.swiglu_nt_off = (int)(inter / kNSub);
+  p.a = x_use;
+  p.lda = h;
+  p.a_scale = mx ? ws + w.xs : nullptr;
+  p.a_scale_ld = h / 32;
+  p.m = w.cap;
+  p.sorted = sorted;
+  p.block_expert = bexp;
+  p.topk = topk;
+  p.sentinel = (int)(t * topk);
+  p.out = ws + w.inter;
+  p.ldo = inter;
+  p.out_scale = mx ? ws + w.inter_s : nullptr;
+  p.bias = nullptr;
+  p.n_tiles = (int)cdiv(cdiv(inter, kNSub), (int64_t)(c.wave_n / 2) * c.waves_n);
+  p.split_k = c.split_k;
+  p.kb_per_split = (int)cdiv(cdiv(L13.kb, c.split_k), c.waves_k) * c.waves_k;
+  p.partials = reinterpret_cast<float*>(ws + w.partials);
+  p.counters = reinterpret_cast<int32_t*>(ws + w.counters);
+  st = launch_gemm(kup, p, w.nblocks, stream);
+  if (st != HUM_OK) return st;
+  // down (rows scattered back to flat slots)
+  GemmParams q{};
+  fill_weight_params(q, w2, L2, packed_w2);
+  q.a = ws + w.inter;
+  q.lda = inter;
+  q.a_scale = mx ? ws + w.inter_s : nullptr;
+  q.a_scale_ld = inter / 32;
+  q.m = w.cap;
+  q.sorted = sorted;
+  q.block_expert = bexp;
+  q.topk = topk;
+  q.sentinel = (int)(t * topk);
+  q.out = ws + w.y;
+  q.ldo = h;
+  q.out_scale = nullptr;
+  q.bias = nullptr;
+  q.n_tiles = (int)cdiv(L2.nt, (int64_t)c.wave_n * c.waves_n);
+  q.split_k = c.split_k;
+  q.kb_per_split = (int)cdiv(cdiv(L2.kb, c.split_k), c.waves_k) * c.waves_k;
+  q.partials = reinterpret_cast<float*>(ws + w.partials);
+  q.counters = reinterpret_cast<int32_t*>(ws + w.counters);
+  st = launch_gemm(kdn, q, w.nblocks, stream);
+  if (st != HUM_OK) return st;
+  return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
+}
+
+hum_status hum_moe_gemm(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                        const void* packed_w2, int64_t t, int32_t topk, const void* x_bf16,
+                        const int32_t* topk_ids, const float* topk_weights, void* out_bf16, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  return hum_moe_gemm_ex(w13, packed_w13, w2, packed_w2, t, topk, x_bf16, topk_ids, topk_weights, out_bf16,
+                         workspace, ws_bytes, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace hum {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E8M0 code -> float 2^(c-127); 255 -> NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  if (c == 0) return __uint_as_float(0x00400000u);  // 2^-127 (subnormal)
+  if (c == 255) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float(c << 23);
+}
+
+// Two floats -> two E4M3 codes (RNE, saturated to +-448, signed zero kept).
+// The hardware conversion rounds to nearest even; the clamp makes it
+// saturate instead of producing NaN above 448.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Sum / max over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane
+// of the row receives the result.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));  // row_ror:1
+  return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false)));
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max over the 4 lanes of a DPP quad.
+__device__ __forceinline__ float quad_max(float v) {
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad_perm 1,0,3,2
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad_perm 2,3,0,1
+  return v;
+}
+
+// floor(log2(a)) for a finite float a > 0, from the exponent field.
+__device__ __forceinline__ int floor_log2_f32(float a) {
+  uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF);
+  if (e == 0) return 31 - __builtin_clz(u & 0x007FFFFFu) - 149;  // subnormal
+  return e - 127;
+}
+
+// MX scale exponent code for a block whose absolute maximum is `amax`.
+__device__ __forceinline__ int mx_scale_code(float amax) {
+  if (!(amax > 0.0f)) return 127;
+  int e = floor_log2_f32(amax) - 8 + 127;
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
+// 2^(127 - e) as an exact float for e in [0, 254] (the reciprocal of the
+// MX block scale 2^(e-127)).
+__device__ __forceinline__ float mx_inv_scale(int e) {
+  int p = 127 - e;  // -127 .. 127
+  if (p >= -126) return __uint_as_float((uint32_t)(p + 127) << 23);
+  return __uint_as_float(0x00400000u);  // 2^-127
+}
+
+}  // namespace hum

@@ -1,0 +1,125 @@
+// Internal declarations shared by the library's translation units.
+//
+// Packed weight layout (what hum_prepare_weight produces), per expert e:
+//
+//   codes : [NT][KB][64 lanes][B bytes]   NT = ceil(N/16), KB = K/128
+//           B = 16 for 4-bit formats, 32 for E4M3.  Lane l = c + 16*lg
+//           (c = column within the 16-column sub-tile, lg = 0..3) holds
+//             4-bit : k = 128*kb + 32*lg + (0..31)            (32 codes)
+//             E4M3  : k = 128*kb + 16*lg + (0..15) then
+//                     k = 128*kb + 64 + 16*lg + (0..15)     (32 codes)
+//           which is the operand order of the gfx950 MFMA instructions the
+//           GEMM issues (16x16x32 bf16 per 8-k step, 16x16x128 f8f6f4).
+//           INT4 / UINT4 nibbles of one 8-k step sit in one dword in the
+//           order k0,k2,k4,k6 at bits 0,4,8,12 and k1,k3,k5,k7 at bits
+//           16,20,24,28, so that (w >> 4j) & 0x000F000F | 0x43004300 is the
+//           bf16 pair (128 + u_{2j}, 128 + u_{2j+1}).  INT4 is stored
+//           offset by 8 (u = v + 8).  E2M1 keeps the canonical order (even
+//           k in the low nibble).
+//   meta  : INT4/UINT4 : scales [NT][NG][16] (bf16 or f32), zeros
+//                        [NT][NG][8 bytes] (16 nibbles, column c at nibble c)
+//           E2M1/E8M0  : scales [NT][KB4][64 lanes][4 bytes], byte i of the
+//                        dword of lane l is the E8M0 code of column c and
+//                        32-block lg of K-block 4*kb4 + i
+//           E4M3       : scales f32 [NT*16]
+//   global scale : f32 [E] (1.0 when absent)
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/hum.h"
+
+namespace hum {
+
+constexpr int kNSub = 16;     // columns per sub-tile
+constexpr int kKBlk = 128;    // K per packed block
+
+struct Layout {
+  int64_t nt = 0, kb = 0, ng = 0, kb4 = 0;
+  int64_t codes_per_expert = 0;   // bytes
+  int64_t scales_per_expert = 0;  // bytes
+  int64_t zeros_per_expert = 0;   // bytes
+  int64_t codes_off = 0, scales_off = 0, zeros_off = 0, gscale_off = 0, total = 0;
+  int code_bytes = 16;            // per lane per (nt, kb)
+  int kb_per_group = 1;           // INT formats
+  int scale_f32 = 0;              // INT formats: 1 = f32 scales, 0 = bf16
+};
+
+enum Fmt : int { F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3 };
+
+// Validates the description; on failure sets the thread-local error and
+// returns a non-OK status.
+hum_status check_desc(const hum_weight_desc* d);
+hum_status compute_layout(const hum_weight_desc* d, Layout* L);
+int fmt_of(const hum_weight_desc* d);
+
+hum_status set_error(hum_status s, const char* fmt, ...);
+void clear_error();
+
+// ---- launchers (return HUM_ERR_HIP on a launch failure) -----------------
+hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* codes,
+                         const void* scales, const void* zeros, const float* gscale,
+                         void* packed, void* stream);
+hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void* packed,
+                          float* out, void* stream);
+hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t ldx,
+                                  void* q, float* s, void* stream);
+hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
+                              uint8_t* s, void* stream);
+hum_status launch_zero(void* p, size_t bytes, void* stream);
+hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
+                        int32_t block_m, int32_t* sorted, int32_t* offsets, int32_t* counts,
+                        int32_t* block_expert, int64_t nblocks, void* stream);
+hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t topk,
+                             int64_t h, void* out, void* stream);
+
+// GEMM epilogues / A-row modes
+enum Epi : int { EPI_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_SWIGLU_MXFP8 = 2, EPI_SCATTER = 3 };
+enum AMode : int { A_DIRECT = 0, A_GATHER = 1 };
+
+struct GemmParams {
+  // weights
+  const uint8_t* codes;
+  const uint8_t* wscale;
+  const uint8_t* wzero;
+  const float* gscale;
+  int64_t codes_per_expert, scales_per_expert, zeros_per_expert;
+  int nt_count, kb_count, ng, kb_per_group, kb4;
+  int scale_f32, int_offset, has_zero;
+  int64_t n;          // valid output columns (I for the SwiGLU epilogues)
+  int swiglu_nt_off;  // up sub-tile offset (I / 16) for SwiGLU
+  // activations
+  const void* a;
+  int64_t lda;        // elements (bytes for fp8)
+  const void* a_scale;
+  int64_t a_scale_ld; // MXFP8: scale bytes per row
+  int64_t m;          // rows (dense) / padded sorted length (MoE)
+  // MoE
+  const int32_t* sorted;
+  const int32_t* block_expert;
+  int topk;
+  int sentinel;
+  // outputs
+  void* out;
+  int64_t ldo;        // elements
+  void* out_scale;    // MXFP8 epilogue scales, [rows][ldo/32]
+  const uint16_t* bias;
+  float* partials;
+  int32_t* counters;
+  int split_k;
+  int kb_per_split;
+  int n_tiles;
+};
+
+struct KernelKey {
+  int fmt, wm, wn, waves_n, waves_k, amode, epi;
+};
+
+// Launches the GEMM kernel instance matching `key` (HUM_ERR_UNSUPPORTED if
+// no such instance is compiled).  Grid = m_tiles * n_tiles * split_k.
+hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles,
+                       void* stream);
+bool gemm_instance_exists(const KernelKey& key);
+
+}  // namespace hum

@@ -31,7 +31,7 @@ import numpy as np
 
 __all__ = [
     "rng", "seed_for", "bf16_bits", "bf16_normal", "pack_nibbles",
-    "dense_w4a16", "dense_w8a8", "moe_weights_mxfp4", "routing",
+    "dense_w4a16", "dense_w8a8", "moe_weights_mxfp4", "routing", "quant_weights",
     "DENSE_SWEEP_M", "FP8_SWEEP_M", "MOE_W4A16_T", "MOE_W4A8_T",
 ]
 
@@ -87,22 +87,55 @@ def dense_w4a16(seed: int, m: int, n: int, k: int, group: int = 128,
     e = num_experts
     kg = k // group
     if asym:
-        codes = g.integers(0, 16, size=(e, n, k), dtype=np.int64)
-        zeros = g.integers(zero_lo, zero_hi + 1, size=(e, n, kg)).astype(np.uint8)
+        codes = g.integers(0, 16, size=(e, n, k), dtype=np.uint8)
+        zeros = g.integers(zero_lo, zero_hi + 1, size=(e, n, kg), dtype=np.uint8)
     else:
-        v = g.integers(-8, 8, size=(e, n, k), dtype=np.int64)
-        codes = v & 0xF
+        v = g.integers(-8, 8, size=(e, n, k), dtype=np.int8)
+        codes = (v & 0xF).astype(np.uint8)
         zeros = None
     scales = _uniform_bf16(g, scale_lo, scale_hi, (e, n, kg))
     x = bf16_normal(g, (m, k))
     return {
-        "codes": pack_nibbles(codes.astype(np.uint8)),
+        "codes": pack_nibbles(codes),
         "scales": scales,
         "zeros": zeros,
         "x": x,
         "m": m, "n": n, "k": k, "group": group, "num_experts": e,
         "weight_dtype": "uint4" if asym else "int4",
     }
+
+
+def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
+                  scale_dtype: str, num_experts: int, n: int, k: int,
+                  zero: bool = False, global_scale: bool = False,
+                  scale_lo: float = 0.005, scale_hi: float = 0.02,
+                  e8m0_lo: int = 119, e8m0_hi: int = 123):
+    """Random canonical weights of any supported description: codes uniform
+    over the format's codes (E4M3 without its NaN codes), scales uniform in
+    [scale_lo, scale_hi] (bf16 / f32) or E8M0 codes in [e8m0_lo, e8m0_hi],
+    zero points uniform in [0, 15], global scales uniform in [0.5, 2]."""
+    g = rng(seed)
+    e = num_experts
+    if scale_gran == "group":
+        sn, sg = n, k // group
+    elif scale_gran == "channel":
+        sn, sg = n, 1
+    else:
+        sn, sg = 1, 1
+    if weight_dtype == "e4m3":
+        c = g.integers(0, 256, size=(e, n, k), dtype=np.uint8)
+        codes = np.where((c & 0x7F) == 0x7F, c & 0xFE, c).astype(np.uint8)
+    else:
+        codes = pack_nibbles(g.integers(0, 16, size=(e, n, k), dtype=np.uint8))
+    if scale_dtype == "bf16":
+        scales = _uniform_bf16(g, scale_lo, scale_hi, (e, sn, sg))
+    elif scale_dtype == "f32":
+        scales = g.uniform(scale_lo, scale_hi, size=(e, sn, sg)).astype(np.float32)
+    else:
+        scales = g.integers(e8m0_lo, e8m0_hi + 1, size=(e, sn, sg), dtype=np.uint8)
+    zeros = g.integers(0, 16, size=(e, sn, sg), dtype=np.uint8) if zero else None
+    gsc = g.uniform(0.5, 2.0, size=e).astype(np.float32) if global_scale else None
+    return {"codes": codes, "scales": scales, "zeros": zeros, "global_scale": gsc}
 
 
 def dense_w8a8(seed: int, m: int, n: int, k: int, w_std: float = 0.05):
@@ -133,10 +166,13 @@ def moe_weights_mxfp4(seed: int, num_experts: int, n: int, k: int,
     """MXFP4 weights: E2M1 codes uniform over all 16 codes, one E8M0 scale per
     32 along K with unbiased exponent uniform in [exp_lo, exp_hi]."""
     g = rng(seed)
-    codes = g.integers(0, 16, size=(num_experts, n, k), dtype=np.int64).astype(np.uint8)
+    codes = np.empty((num_experts, n, k // 2), dtype=np.uint8)
+    for e in range(num_experts):  # one expert at a time bounds host memory
+        c = g.integers(0, 16, size=(n, k), dtype=np.uint8)
+        codes[e] = pack_nibbles(c)
     sc = g.integers(127 + exp_lo, 127 + exp_hi + 1,
-                    size=(num_experts, n, k // 32)).astype(np.uint8)
-    return {"codes": pack_nibbles(codes), "scales": sc, "zeros": None,
+                    size=(num_experts, n, k // 32), dtype=np.uint8)
+    return {"codes": codes, "scales": sc, "zeros": None,
             "n": n, "k": k, "group": 32, "num_experts": num_experts,
             "weight_dtype": "e2m1"}
 

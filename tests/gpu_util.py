@@ -1,0 +1,76 @@
+"""Helpers shared by the GPU parity tests: host <-> device marshalling of the
+canonical tensors, descriptor pairs (library + oracle) and the tolerance
+check.  Tolerance (relative Frobenius <= 5e-3, max |diff| <= 1e-2 * max
+|oracle|) is the one fixed for bf16-output GEMMs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import quantized_gemm_packed_amd as hum
+
+DEV = "cuda"
+REL_FRO = 5e-3
+MAX_REL = 1e-2
+
+
+def dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    t = torch.from_numpy(a).to(DEV)
+    return t if dtype is None else t.to(dtype)
+
+
+def dev_scales(sc, scale_dtype):
+    if scale_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(sc).view(np.int16)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(sc)).to(DEV)
+
+
+def f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bf16_bits_of(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def descs(wd, gran, gs, sd, e, n, k, zero=False, glob=False, act="bf16"):
+    hd = hum.make_desc(wd, gran, gs, sd, n, k, num_experts=e, has_zero=zero, has_global=glob, act_fmt=act)
+    od = oracle.gemm.WeightDesc(wd, gran, gs, sd, zero, glob, e, n, k)
+    return hd, od
+
+
+def prepare(hd, w, sd):
+    return hum.prepare_weight(hd, dev(w["codes"]), dev_scales(w["scales"], sd),
+                              None if w.get("zeros") is None else dev(w["zeros"]),
+                              None if w.get("global_scale") is None else dev(w["global_scale"]))
+
+
+def tol_stats(gpu, ref):
+    g = f64(gpu) if isinstance(gpu, torch.Tensor) else gpu
+    ref = np.asarray(ref, np.float64)
+    nrm = np.linalg.norm(ref)
+    rel = np.linalg.norm(g - ref) / nrm if nrm > 0 else np.linalg.norm(g)
+    am = np.abs(ref).max() if ref.size else 0.0
+    mx = np.abs(g - ref).max() / am if am > 0 else (np.abs(g).max() if g.size else 0.0)
+    return rel, mx
+
+
+def assert_tol(gpu, ref, what=""):
+    rel, mx = tol_stats(gpu, ref)
+    assert rel <= REL_FRO and mx <= MAX_REL, f"{what}: relFro={rel:.3e} maxrel={mx:.3e}"
+    return rel, mx
+
+
+def assert_bf16_exact(gpu, ref, what=""):
+    """GPU bf16 output equals bf16(oracle) bit for bit (+0 / -0 both accepted)."""
+    got = bf16_bits_of(gpu)
+    exp = oracle.formats.encode_bf16(ref)
+    same = (got == exp) | ((got & 0x7FFF) == 0) & ((exp & 0x7FFF) == 0)
+    if not same.all():
+        idx = np.argwhere(~same)[:5]
+        raise AssertionError(f"{what}: {int((~same).sum())} mismatches, first {idx.tolist()}: "
+                             f"got {[hex(int(got[tuple(i)])) for i in idx]} exp {[hex(int(exp[tuple(i)])) for i in idx]}")

@@ -1,0 +1,96 @@
+"""CPU checks of the C ABI library: it loads, exports every function
+include/hum.h declares, and its host-side validation / sizing / selector
+paths answer without touching a GPU."""
+import ctypes
+
+import pytest
+
+import quantized_gemm_packed_amd as hum
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hum.load_library()
+
+
+def test_exports_every_header_function(lib):
+    names = hum.header_functions()
+    assert len(names) >= 15
+    raw = ctypes.CDLL(hum.lib_path())
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, missing
+    assert set(names) <= set(hum._SIGS), set(names) - set(hum._SIGS)
+
+
+def test_packed_size_dense_int4(lib):
+    d = hum.make_desc("uint4", "group", 128, "bf16", 8192, 8192, has_zero=True)
+    nb = hum.packed_weight_bytes(d)
+    codes = 8192 * 8192 // 2
+    scales = 8192 * 64 * 2
+    zeros = 8192 * 64 // 2
+    assert codes + scales + zeros <= nb <= codes + scales + zeros + 4096
+
+
+def test_packed_size_ragged_n_pads_to_16(lib):
+    d = hum.make_desc("int4", "group", 128, "bf16", 40, 256)
+    assert hum.packed_weight_bytes(d) >= 48 * 256 // 2
+
+
+@pytest.mark.parametrize("bad", [
+    dict(weight_dtype="int4", scale_gran="group", group_size=64, scale_dtype="bf16"),   # G % 128
+    dict(weight_dtype="int4", scale_gran="group", group_size=128, scale_dtype="bf16", has_zero=True),
+    dict(weight_dtype="e2m1", scale_gran="group", group_size=128, scale_dtype="e8m0"),
+    dict(weight_dtype="e4m3", scale_gran="channel", group_size=0, scale_dtype="f32", act_fmt="bf16"),
+    dict(weight_dtype="e4m3", scale_gran="group", group_size=128, scale_dtype="f32", act_fmt="fp8_token"),
+])
+def test_unsupported_descriptions_rejected(lib, bad):
+    kw = dict(n=256, k=1024)
+    kw.update(bad)
+    d = hum.make_desc(kw.pop("weight_dtype"), kw.pop("scale_gran"), kw.pop("group_size"), kw.pop("scale_dtype"),
+                      **kw)
+    assert lib.hum_packed_weight_bytes(ctypes.byref(d)) == 0
+    assert lib.hum_last_error()
+
+
+def test_k_not_multiple_of_128_rejected(lib):
+    d = hum.make_desc("int4", "channel", 0, "bf16", 64, 200)
+    assert lib.hum_packed_weight_bytes(ctypes.byref(d)) == 0
+    assert b"multiple of 128" in lib.hum_last_error()
+
+
+def test_null_pointers_rejected_before_launch(lib):
+    d = hum.make_desc("int4", "group", 128, "bf16", 64, 256)
+    st = lib.hum_prepare_weight(ctypes.byref(d), None, None, None, None, None, 0, None)
+    assert st == 1
+    st = lib.hum_linear(ctypes.byref(d), None, 4, None, None, None, None, None, 0, None)
+    assert st == 1
+
+
+def test_small_packed_buffer_is_workspace_error(lib):
+    d = hum.make_desc("int4", "group", 128, "bf16", 64, 256)
+    st = lib.hum_prepare_weight(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None,
+                                ctypes.c_void_p(16), 10, None)
+    assert st == 3
+
+
+def test_selector_is_deterministic_and_covers_m_range(lib):
+    d = hum.make_desc("uint4", "group", 128, "bf16", 8192, 8192, has_zero=True)
+    seen = set()
+    for m in (1, 4, 16, 64, 256, 1024, 4096):
+        c1 = hum.select_config(d, m).as_tuple()
+        c2 = hum.select_config(d, m).as_tuple()
+        assert c1 == c2
+        wave_m, wave_n, waves_n, waves_k, split_k, block_m = c1
+        assert waves_n * waves_k == 4 and split_k >= 1
+        assert 16 * wave_m >= min(m, 128)
+        seen.add(c1)
+    assert len(seen) >= 3
+
+
+def test_workspace_sizes(lib):
+    d = hum.make_desc("e4m3", "channel", 0, "f32", 7168, 2048, act_fmt="fp8_token")
+    assert hum.linear_workspace_bytes(d, 128) >= 128 * 2048 + 128 * 4
+    w13 = hum.make_desc("e2m1", "group", 32, "e8m0", 2048, 4096, num_experts=128)
+    w2 = hum.make_desc("e2m1", "group", 32, "e8m0", 4096, 1024, num_experts=128)
+    nb = hum.moe_workspace_bytes(w13, w2, 64, 8)
+    assert nb >= 64 * 8 * 4096 * 2

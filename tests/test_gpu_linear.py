@@ -1,0 +1,203 @@
+"""GPU: dense quantized GEMM (hum_linear) against the oracle.
+
+* exact-integer cases (integer activations, power-of-two scales, integer
+  zero points) must match bf16(oracle) bit for bit for every compiled tile
+  configuration and split-K factor;
+* random cases must meet the bf16-output tolerance;
+* edge cases: M = 1, ragged N (not a multiple of any tile), bias, global
+  scale, G = K, repeat-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_packed_amd as hum
+import synth
+from gpu_util import assert_bf16_exact, assert_tol, descs, dev, prepare
+
+pytestmark = pytest.mark.gpu
+
+DENSE_TILES = [(1, 1, 1, 4), (1, 2, 2, 2), (1, 4, 4, 1), (2, 2, 2, 2), (4, 2, 2, 2), (4, 4, 4, 1), (8, 4, 4, 1)]
+
+
+def cfg(t, split):
+    c = hum.TileConfig()
+    c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.split_k = split
+    c.block_m = 16 * t[0]
+    return c
+
+
+def _int_exact_case(seed, wd, m, n, k, gs, zero):
+    g = synth.rng(seed)
+    w = synth.quant_weights(seed, wd, "group", gs, "bf16", 1, n, k, zero=zero)
+    ng = k // gs
+    w["scales"] = synth.bf16_bits(np.ldexp(1.0, g.integers(-5, -2, size=(1, n, ng))).astype(np.float32))
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    return w, xb
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("split", [1, 2, 4])
+def test_int_exact_every_tile(tile, split):
+    m, n, k, gs = 37, 640, 1024, 128
+    w, xb = _int_exact_case(31, "uint4", m, n, k, gs, True)
+    hd, od = descs("uint4", "group", gs, "bf16", 1, n, k, zero=True)
+    print(f"case uint4 exact tile={tile} split={split}", flush=True)
+    packed = prepare(hd, w, "bf16")
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w["zeros"])
+    assert_bf16_exact(out, ref, f"tile={tile} split={split}")
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_int4_sym_exact_every_tile(tile):
+    m, n, k, gs = 5, 200, 512, 256
+    w, xb = _int_exact_case(32, "int4", m, n, k, gs, False)
+    hd, od = descs("int4", "group", gs, "bf16", 1, n, k)
+    packed = prepare(hd, w, "bf16")
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_mxfp4_bf16_exact_every_tile(tile):
+    m, n, k = 9, 96, 512
+    g = synth.rng(33)
+    w = synth.quant_weights(33, "e2m1", "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k)
+    packed = prepare(hd, w, "e8m0")
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 1))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+def test_workload_dense_int4_sym_g128_tiny():
+    """Dense W4A16 INT4 symmetric G128, M=16 N=512 K=1024 (selector config)."""
+    case = synth.dense_w4a16(synth.seed_for(1), 16, 512, 1024, group=128)
+    hd, od = descs("int4", "group", 128, "bf16", 1, 512, 1024)
+    packed = prepare(hd, case, "bf16")
+    out = hum.linear(hd, packed, dev(case["x"]))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(case["x"]), case["codes"], case["scales"])
+    assert_tol(out, ref, "cfg1")
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 33, 64, 130, 300])
+def test_uint4_zp_random_vs_oracle(m):
+    n, k = 640, 2048
+    case = synth.dense_w4a16(synth.seed_for(2, m), m, n, k, group=128, asym=True)
+    hd, od = descs("uint4", "group", 128, "bf16", 1, n, k, zero=True)
+    packed = prepare(hd, case, "bf16")
+    out = hum.linear(hd, packed, dev(case["x"]))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(case["x"]), case["codes"], case["scales"], case["zeros"])
+    assert_tol(out, ref, f"m={m}")
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_fp8_w8a8_every_tile(tile):
+    m, n, k = 21, 320, 1024
+    case = synth.dense_w8a8(synth.seed_for(3, 7), m, n, k)
+    hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+    packed = prepare(hd, case, "f32")
+    out = hum.linear(hd, packed, dev(case["x"]), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_per_token(oracle.formats.decode_bf16(case["x"]).astype(np.float32))
+    a = oracle.quant.dequant_fp8_per_token(q, s)
+    ref = oracle.gemm.linear(od, a, case["codes"], case["scales"])
+    assert_tol(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 128, 257])
+def test_fp8_w8a8_selector_vs_oracle(m):
+    n, k = 7168 // 8, 2048
+    case = synth.dense_w8a8(synth.seed_for(3, m), m, n, k)
+    hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+    packed = prepare(hd, case, "f32")
+    out = hum.linear(hd, packed, dev(case["x"]))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_per_token(oracle.formats.decode_bf16(case["x"]).astype(np.float32))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_fp8_per_token(q, s), case["codes"], case["scales"])
+    assert_tol(out, ref, f"m={m}")
+
+
+def test_fp8_prequantized_activations_match_internal_quant():
+    m, n, k = 33, 256, 1024
+    case = synth.dense_w8a8(91, m, n, k)
+    hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+    packed = prepare(hd, case, "f32")
+    x = dev(case["x"])
+    q, s = hum.quant_act("fp8_token", x)
+    o1 = hum.linear(hd, packed, x)
+    o2 = hum.linear(hd, packed, q, a_scales=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_bias_and_global_scale():
+    m, n, k = 12, 100, 768
+    w = synth.quant_weights(41, "uint4", "group", 256, "f32", 1, n, k, zero=True, global_scale=True,
+                            scale_lo=0.01, scale_hi=0.05)
+    g = synth.rng(42)
+    xb = synth.bf16_normal(g, (m, k))
+    bias = synth.bf16_normal(g, (n,))
+    hd, od = descs("uint4", "group", 256, "f32", 1, n, k, zero=True, glob=True)
+    packed = prepare(hd, w, "f32")
+    out = hum.linear(hd, packed, dev(xb), bias=dev(bias))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w["zeros"],
+                             w["global_scale"], bias_bits=bias)
+    assert_tol(out, ref, "bias+global")
+
+
+def test_channel_and_tensor_scales():
+    m, n, k = 8, 64, 512
+    for gran in ("channel", "tensor"):
+        w = synth.quant_weights(43, "int4", gran, 0, "f32", 1, n, k)
+        xb = synth.bf16_normal(synth.rng(44), (m, k))
+        hd, od = descs("int4", gran, 0, "f32", 1, n, k)
+        out = hum.linear(hd, prepare(hd, w, "f32"), dev(xb))
+        torch.cuda.synchronize()
+        ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+        assert_tol(out, ref, gran)
+
+
+def test_zero_codes_equal_zero_point_give_zero():
+    """q == z everywhere -> exactly zero output (integer activations keep
+    every fp32 partial sum exact, so the offset correction cancels exactly);
+    with real-valued activations the residue stays at fp32 rounding level."""
+    m, n, k = 4, 48, 256
+    w = synth.quant_weights(45, "uint4", "group", 128, "bf16", 1, n, k, zero=True)
+    w["codes"] = synth.pack_nibbles(np.repeat(w["zeros"], 128, axis=2))
+    hd, _ = descs("uint4", "group", 128, "bf16", 1, n, k, zero=True)
+    packed = prepare(hd, w, "bf16")
+    xi = synth.bf16_bits(synth.rng(46).integers(-8, 9, size=(m, k)).astype(np.float32))
+    out = hum.linear(hd, packed, dev(xi))
+    xr = synth.bf16_normal(synth.rng(46), (m, k))
+    out_r = hum.linear(hd, packed, dev(xr))
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0)
+    # bound: fp32 rounding of the two K-block sums, |sum a*(128+z)| * s * 2^-20
+    a = np.abs(oracle.formats.decode_bf16(xr)).sum(axis=1)
+    bound = a * 143 * 0.02 * 2.0 ** -20
+    assert np.all(np.abs(out_r.float().cpu().numpy()) <= bound[:, None])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    m, n, k = 3, 2048, 4096
+    case = synth.dense_w4a16(47, m, n, k, group=128, asym=True)
+    hd, _ = descs("uint4", "group", 128, "bf16", 1, n, k, zero=True)
+    packed = prepare(hd, case, "bf16")
+    x = dev(case["x"])
+    c = hum.select_config(hd, m)
+    assert c.split_k > 1
+    o1 = hum.linear(hd, packed, x).clone()
+    o2 = hum.linear(hd, packed, x)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

@@ -1,0 +1,129 @@
+"""GPU: MoE pieces against the oracle -- align (bit exact), weighted reduce,
+and the full layer (hum_moe_gemm) for MXFP4 W4A16 and W4A8 on every compiled
+tile shape, with skewed / empty / single-expert routings."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_packed_amd as hum
+import synth
+from gpu_util import assert_tol, descs, dev, prepare
+
+pytestmark = pytest.mark.gpu
+
+MOE_TILES = [(1, 4, 1, 4), (1, 4, 2, 2), (2, 4, 2, 2), (4, 4, 4, 1), (8, 4, 4, 1)]
+
+
+def cfg(t, split=1):
+    c = hum.TileConfig()
+    c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.split_k = split
+    c.block_m = 16 * t[0]
+    return c
+
+
+@pytest.mark.parametrize("t,k,e,bm,zipf", [(1, 8, 128, 16, None), (37, 8, 16, 32, None), (300, 4, 64, 64, None),
+                                           (4096, 8, 128, 128, 1.1), (8192, 8, 128, 16, 1.1), (5, 3, 7, 1, None)])
+def test_align_bit_exact(t, k, e, bm, zipf):
+    ids, _ = synth.routing(500 + t, t, e, k, zipf_s=zipf)
+    print(f"case align t={t} k={k} e={e} bm={bm}", flush=True)
+    srt, off, cnt = hum.moe_align(dev(ids), e, bm)
+    torch.cuda.synchronize()
+    rs, ro, rc = oracle.moe.align(ids, e, bm)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(off.cpu().numpy(), ro)
+    assert np.array_equal(srt.cpu().numpy(), rs)
+
+
+def test_align_all_to_one_expert():
+    t, k, e = 300, 2, 16
+    ids = np.full((t, k), 5, np.int32)
+    ids[:, 1] = 9
+    srt, off, cnt = hum.moe_align(dev(ids), e, 64)
+    torch.cuda.synchronize()
+    rs, ro, rc = oracle.moe.align(ids, e, 64)
+    assert np.array_equal(srt.cpu().numpy(), rs) and np.array_equal(off.cpu().numpy(), ro)
+
+
+@pytest.mark.parametrize("t,k,h", [(1, 8, 4096), (33, 8, 256), (7, 1, 64)])
+def test_reduce_vs_oracle(t, k, h):
+    g = synth.rng(600 + t)
+    y = synth.bf16_normal(g, (t * k, h))
+    _, w = synth.routing(601 + t, t, 16, k)
+    out = hum.moe_reduce(dev(y), dev(w))
+    torch.cuda.synchronize()
+    ref = oracle.moe.reduce(oracle.formats.decode_bf16(y), w, k)
+    got = out.float().cpu().numpy().astype(np.float64)
+    # one bf16 rounding of an fp32 sum: within 2^-8 relative per element
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+def _layer(seed, e, h, inter, act):
+    w13 = synth.moe_weights_mxfp4(seed, e, 2 * inter, h)
+    w2 = synth.moe_weights_mxfp4(seed + 1, e, h, inter)
+    d13, o13 = descs("e2m1", "group", 32, "e8m0", e, 2 * inter, h, act=act)
+    d2, o2 = descs("e2m1", "group", 32, "e8m0", e, h, inter, act=act)
+    return w13, w2, d13, o13, d2, o2, prepare(d13, w13, "e8m0"), prepare(d2, w2, "e8m0")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("t", [1, 9, 70])
+def test_moe_layer_every_tile(act, tile, t):
+    e, h, inter, k = 8, 256, 128, 2
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(700, e, h, inter, act)
+    ids, wts = synth.routing(701 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(702 + t), (t, h))
+    print(f"case moe act={act} tile={tile} t={t}", flush=True)
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg(tile))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"act={act} tile={tile} t={t}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_moe_split_k(act):
+    e, h, inter, k, t = 4, 512, 256, 2, 3
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(710, e, h, inter, act)
+    ids, wts = synth.routing(711, t, e, k)
+    xb = synth.bf16_normal(synth.rng(712), (t, h))
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg((1, 4, 1, 4), split=2))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"split act={act}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_moe_skewed_and_empty_experts(act):
+    e, h, inter, k, t = 16, 256, 128, 4, 200
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(720, e, h, inter, act)
+    ids, wts = synth.routing(721, t, e, k, zipf_s=1.5)
+    ids[:, 0] = 3                                  # one expert gets every token
+    ids = np.where(ids == 7, 8, ids).astype(np.int32)   # expert 7 gets none
+    ids[:, 1] = np.where(ids[:, 1] == 3, 11, ids[:, 1])
+    xb = synth.bf16_normal(synth.rng(722), (t, h))
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"skewed act={act}")
+
+
+def test_moe_single_expert_equals_dense_chain():
+    """E = 1, top-1, w = 1: the layer is dense gate_up -> SwiGLU -> dense down."""
+    h, inter, t = 256, 128, 11
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(730, 1, h, inter, "bf16")
+    ids = np.zeros((t, 1), np.int32)
+    wts = np.ones((t, 1), np.float32)
+    xb = synth.bf16_normal(synth.rng(731), (t, h))
+    x = dev(xb)
+    out = hum.moe_gemm(d13, p13, d2, p2, x, dev(ids), dev(wts))
+    hh = hum.linear(d13, p13, x).float()                # bf16-rounded h
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, "bf16")
+    assert_tol(out, ref, "E=1 vs oracle")
+    gate, up = hh[:, :inter], hh[:, inter:]
+    a = (gate / (1 + torch.exp(-gate)) * up).to(torch.bfloat16)
+    chain = hum.linear(d2, p2, a)
+    torch.cuda.synchronize()
+    assert_tol(out, chain.float().cpu().numpy().astype(np.float64), "E=1 vs dense chain")
