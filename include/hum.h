@@ -79,14 +79,20 @@ typedef struct hum_weight_desc {
   int64_t k;                 /* reduction length */
 } hum_weight_desc;
 
+typedef enum hum_kernel_kind {
+  HUM_KERNEL_TILE = 0,    /* prefill: 4 waves along N share an LDS activation tile */
+  HUM_KERNEL_STREAM = 1   /* decode: one 16-row tile, waves_k waves stream K */
+} hum_kernel_kind;
+
 /* Tile / split-K configuration (output of the selector, or forced). */
 typedef struct hum_tile_config {
+  int32_t kind;      /* hum_kernel_kind */
   int32_t wave_m;    /* 16-row MFMA sub-tiles per wave (rows per WG = 16*wave_m) */
   int32_t wave_n;    /* 16-column sub-tiles per wave */
   int32_t waves_n;   /* waves of a workgroup side by side along N */
   int32_t waves_k;   /* waves of a workgroup splitting K (in-WG split-K) */
-  int32_t split_k;   /* workgroups splitting K (cross-WG split-K, fp32 partials) */
-  int32_t block_m;   /* MoE: rows per expert block (multiple of 16*wave_m) */
+  int32_t split_k;   /* workgroups splitting K (fp32 partials + reduce kernel) */
+  int32_t block_m;   /* rows per workgroup tile = MoE expert block (16*wave_m) */
 } hum_tile_config;
 
 /* ---- weight preparation ------------------------------------------------ */
@@ -141,13 +147,10 @@ size_t hum_linear_workspace_bytes(const hum_weight_desc* desc, int64_t m);
  *              (f32 [m] for FP8_TOKEN, u8 [m][k/32] for MXFP8)
  *   bias     : bf16 [n] or NULL
  *   out      : bf16 [m][n] (row stride n)
- *   workspace: device buffer of hum_linear_workspace_bytes(desc, m) bytes.
- *              Its first 256 KiB are split-K tickets: they must be zero
- *              before the first call (hum_prepare_workspace() zeroes a
- *              buffer) and every call leaves them zero again, so one buffer
- *              serves any sequence of hum_linear / hum_moe_gemm calls that
- *              are ordered on one stream.  Calls that overlap in time must
- *              use different workspaces.
+ *   workspace: device buffer of hum_linear_workspace_bytes(desc, m) bytes
+ *              (quantized activations, row sums, split-K partials); its
+ *              contents need no initialisation.  Calls that overlap in time
+ *              must use different workspaces.
  * Only num_experts == 1 descriptions are dense layers. */
 hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m,
                       const void* a, const void* a_scales, const void* bias,
@@ -164,7 +167,8 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
 size_t hum_linear_workspace_bytes_ex(const hum_weight_desc* desc, int64_t m,
                                      const hum_tile_config* cfg);
 
-/* Zero a workspace before its first use (enqueued on `stream`). */
+/* Zero a device buffer (enqueued on `stream`; a fill kernel, so it can be
+ * captured in a HIP graph).  Workspaces need no zeroing; this is a helper. */
 hum_status hum_prepare_workspace(void* workspace, size_t ws_bytes, void* stream);
 
 /* Selector: the tile / split-K configuration hum_linear would use for m

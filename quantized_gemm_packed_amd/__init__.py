@@ -23,6 +23,7 @@ __all__ = [
 ]
 
 BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0 = range(7)
+KERNEL_TILE, KERNEL_STREAM = range(2)
 SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP = range(3)
 ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8 = range(3)
 
@@ -55,6 +56,7 @@ class WeightDesc(ctypes.Structure):
 
 class TileConfig(ctypes.Structure):
     _fields_ = [
+        ("kind", ctypes.c_int32),
         ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32), ("waves_n", ctypes.c_int32),
         ("waves_k", ctypes.c_int32), ("split_k", ctypes.c_int32), ("block_m", ctypes.c_int32),
     ]
@@ -227,9 +229,8 @@ def linear_workspace_bytes(desc: WeightDesc, m: int, cfg: TileConfig | None = No
 
 
 class Workspace:
-    """A zero-initialised device buffer that grows on demand.  The library
-    leaves its split-K counters zero after every call, so one buffer serves
-    any sequence of calls on one stream."""
+    """A device buffer that grows on demand (its contents need no
+    initialisation); one buffer serves any sequence of calls on one stream."""
 
     def __init__(self, device):
         self.device = device

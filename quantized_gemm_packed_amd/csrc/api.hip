@@ -31,12 +31,6 @@ void clear_error() { g_err[0] = 0; }
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
-// Every workspace starts with the same ticket area for cross-workgroup
-// split-K.  The last workgroup of each tile resets its ticket, so the area is
-// zero after every call whatever layout the rest of the buffer had.
-static const int64_t kMaxTickets = 65536;
-static const int64_t kTicketBytes = kMaxTickets * 4;
-
 hum_status check_desc(const hum_weight_desc* d) {
   if (!d) return set_error(HUM_ERR_INVALID_ARG, "desc is NULL");
   if (d->num_experts < 1) return set_error(HUM_ERR_INVALID_ARG, "num_experts must be >= 1");
@@ -118,17 +112,30 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
 
 static const int kCUs = 256;
 
-static bool cfg_valid_dense(const hum_weight_desc* d, const hum_tile_config& c) {
-  KernelKey k{fmt_of(d), c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
-  return gemm_instance_exists(k) && c.split_k >= 1;
+static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
+  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
 }
 
-// Split so that the grid reaches `target` workgroups, keeping at least one
-// stage of K-blocks per split.
-static int pick_split(int64_t tiles, int64_t kb, int waves_k, int64_t target) {
-  int64_t s = 1;
-  while (tiles * s < target && kb / (waves_k * (s * 2)) >= 1 && s < 16) s *= 2;
-  return (int)s;
+static bool cfg_sane(const hum_tile_config& c) {
+  if (c.split_k < 1 || c.split_k > 64 || c.wave_m < 1 || c.wave_n < 1) return false;
+  if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 16;
+  if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1;
+  return false;
+}
+
+static int64_t tile_rows(const hum_tile_config& c) { return 16 * (int64_t)c.wave_m; }
+
+// Columns (16-wide sub-tiles) one workgroup covers.
+static int64_t tile_subtiles(const hum_tile_config& c) {
+  return (int64_t)c.wave_n * (c.kind == HUM_KERNEL_TILE ? 4 : 1);
+}
+
+// Grid split so that the launch reaches `target` waves, each split keeping
+// at least min_kb K-blocks per wave.
+static int pick_split(int64_t wgs, int waves_per_wg, int64_t kb, int k_waves, int min_kb, int64_t target_waves) {
+  int s = 1;
+  while (wgs * s * waves_per_wg < target_waves && kb / ((int64_t)k_waves * s * 2) >= min_kb && s < 16) s *= 2;
+  return s;
 }
 
 static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
@@ -136,37 +143,47 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
   if (m <= 16) {
-    c.wave_m = 1; c.wave_n = 1; c.waves_n = 1; c.waves_k = 4;
-  } else if (m <= 32) {
-    c.wave_m = 2; c.wave_n = 2; c.waves_n = 2; c.waves_k = 2;
-  } else if (m <= 64) {
-    c.wave_m = 4; c.wave_n = 2; c.waves_n = 2; c.waves_k = 2;
-  } else if (m <= 128) {
-    c.wave_m = 4; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+    // decode: one 16-row tile streamed by 8 waves; more sub-tiles per wave as
+    // m grows keeps the activation re-reads (L2) below the weight bytes.
+    c.kind = HUM_KERNEL_STREAM;
+    c.wave_m = 1;
+    c.wave_n = m <= 2 ? 1 : (m <= 8 ? 2 : 4);
+    c.waves_n = 1;
+    c.waves_k = 8;
+    const int64_t wgs = cdiv(nt, c.wave_n);
+    c.split_k = pick_split(wgs, 8, kb, 8, 2, 16 * kCUs);
+    // activation rows of one split must fit the dense LDS budget
+    while (c.split_k < 64 && stream_lds_per_kb(fmt_of(d), (int)m) * cdiv(cdiv(kb, c.split_k), 8) * 8 > kStreamLdsDense)
+      c.split_k *= 2;
   } else {
-    c.wave_m = 8; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
+    c.kind = HUM_KERNEL_TILE;
+    c.waves_n = 4;
+    c.waves_k = 1;
+    c.wave_n = 4;
+    if (m <= 32) c.wave_m = 2;
+    else if (m <= 64) c.wave_m = 4;
+    else c.wave_m = 4;
+    const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
+    c.split_k = pick_split(wgs, 4, kb, 1, 4, 4 * kCUs);
   }
-  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
-  const int64_t n_tiles = cdiv(nt, (int64_t)c.wave_n * c.waves_n);
-  c.split_k = (m_tiles * n_tiles > kMaxTickets) ? 1 : pick_split(m_tiles * n_tiles, kb, c.waves_k, 2 * kCUs);
-  c.block_m = 16 * c.wave_m;
+  c.block_m = (int32_t)tile_rows(c);
   return c;
 }
 
 static hum_tile_config select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   hum_tile_config c{};
   const double rows = (double)t * topk / w13->num_experts;
-  if (rows <= 16) {
-    c.wave_m = 1; c.wave_n = 4; c.waves_n = 1; c.waves_k = 4;
-  } else if (rows <= 48) {
-    c.wave_m = 2; c.wave_n = 4; c.waves_n = 2; c.waves_k = 2;
-  } else if (rows <= 160) {
-    c.wave_m = 4; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
-  } else {
-    c.wave_m = 8; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1;
-  }
+  c.wave_n = 4;
   c.split_k = 1;
-  c.block_m = 16 * c.wave_m;
+  if (rows <= 16) {
+    c.kind = HUM_KERNEL_STREAM;
+    c.wave_m = 1; c.waves_n = 1; c.waves_k = 8;
+  } else {
+    c.kind = HUM_KERNEL_TILE;
+    c.waves_n = 4; c.waves_k = 1;
+    c.wave_m = rows <= 48 ? 2 : 4;
+  }
+  c.block_m = (int32_t)tile_rows(c);
   return c;
 }
 
@@ -177,34 +194,31 @@ static void log_cfg(const char* what, const hum_tile_config& c, int64_t m) {
     on = e && e[0] == '1';
   }
   if (on)
-    fprintf(stderr, "[hum] %s m=%lld wave_m=%d wave_n=%d waves_n=%d waves_k=%d split_k=%d block_m=%d\n", what,
-            (long long)m, c.wave_m, c.wave_n, c.waves_n, c.waves_k, c.split_k, c.block_m);
+    fprintf(stderr, "[hum] %s m=%lld kind=%d wave_m=%d wave_n=%d waves_n=%d waves_k=%d split_k=%d block_m=%d\n",
+            what, (long long)m, c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, c.split_k, c.block_m);
 }
 
 // ---------------------------------------------------------------------------
-// Dense workspace: [counters][partials][quantized activations][scales].
+// Dense workspace: [split-K partials][quantized activations][scales][row sums].
 
 struct DenseWs {
-  int64_t counters = 0, partials = 0, aq = 0, as = 0, total = 0;
+  int64_t partials = 0, aq = 0, as = 0, rowsum = 0, total = 0;
 };
 
 static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_config& c, bool quant_a) {
   DenseWs w;
   const int64_t nt = cdiv(d->n, kNSub);
-  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
-  const int64_t n_tiles = cdiv(nt, (int64_t)c.wave_n * c.waves_n);
-  const int64_t tiles = m_tiles * n_tiles;
   int64_t off = 0;
-  w.counters = off;
-  off = kTicketBytes;
   w.partials = off;
-  off = align256(off + (c.split_k > 1 ? tiles * c.split_k * c.waves_n * (int64_t)c.wave_m * c.wave_n * 256 * 4 : 0));
+  if (c.split_k > 1) off = align256(off + (int64_t)c.split_k * m * nt * 16 * 4);
   w.aq = off;
   if (quant_a) {
     off = align256(off + m * d->k);
     w.as = off;
     off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 ? m * (d->k / 32) : m * 4));
   }
+  w.rowsum = off;
+  if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + m * (d->k / kKBlk) * 4);
   w.total = off;
   return w;
 }
@@ -307,11 +321,13 @@ static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const La
   p.has_zero = d->has_zero_point;
   p.n = d->n;
   p.swiglu_nt_off = 0;
+  p.a_rowsum = nullptr;
 }
 
-static bool cfg_sane(const hum_tile_config& c) {
-  return c.wave_m >= 1 && c.wave_n >= 1 && c.waves_n >= 1 && c.waves_k >= 1 && c.waves_n * c.waves_k == 4 &&
-         c.split_k >= 1 && c.split_k <= 64;
+// K-blocks per split: whole stages (waves_k K-blocks per wave-step).
+static int kb_per_split(int64_t kb, const hum_tile_config& c) {
+  const int64_t unit = c.kind == HUM_KERNEL_STREAM ? c.waves_k : 1;
+  return (int)(cdiv(cdiv(kb, c.split_k), unit) * unit);
 }
 
 hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a,
@@ -326,11 +342,11 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   if (m == 0) return HUM_OK;
   if (!packed || !a || !out) return set_error(HUM_ERR_INVALID_ARG, "packed, a and out must be non-NULL");
   hum_tile_config c = cfg ? *cfg : select_dense(desc, m);
-  if (!cfg_sane(c) || !cfg_valid_dense(desc, c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  if (!cfg_sane(c) || !gemm_instance_exists(dense_key(desc, c)))
+    return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  if (c.kind == HUM_KERNEL_STREAM && m > 16) return set_error(HUM_ERR_UNSUPPORTED, "the stream kernel takes m <= 16");
   const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
   const DenseWs w = dense_ws(desc, m, c, quant_a);
-  if (c.split_k > 1 && cdiv(m, 16 * c.wave_m) * cdiv(L.nt, (int64_t)c.wave_n * c.waves_n) > kMaxTickets)
-    return set_error(HUM_ERR_UNSUPPORTED, "split-K needs at most %lld output tiles", (long long)kMaxTickets);
   if (w.total > 0 && (!workspace || ws_bytes < (size_t)w.total))
     return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
   log_cfg("linear", c, m);
@@ -345,6 +361,11 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   }
   GemmParams p{};
   fill_weight_params(p, desc, L, packed);
+  if (fmt_of(desc) == F_INT && c.kind == HUM_KERNEL_TILE) {
+    st = launch_rowsum(a_use, desc->k, m, (int)L.kb, reinterpret_cast<float*>(ws + w.rowsum), stream);
+    if (st != HUM_OK) return st;
+    p.a_rowsum = reinterpret_cast<const float*>(ws + w.rowsum);
+  }
   p.a = a_use;
   p.lda = desc->k;
   p.a_scale = as_use;
@@ -358,14 +379,17 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.ldo = desc->n;
   p.out_scale = nullptr;
   p.bias = static_cast<const uint16_t*>(bias);
-  const int64_t m_tiles = cdiv(m, 16 * c.wave_m);
-  p.n_tiles = (int)cdiv(L.nt, (int64_t)c.wave_n * c.waves_n);
+  const int64_t m_tiles = cdiv(m, tile_rows(c));
+  p.n_tiles = (int)cdiv(L.nt, tile_subtiles(c));
   p.split_k = c.split_k;
-  p.kb_per_split = (int)cdiv(cdiv(L.kb, c.split_k), c.waves_k) * c.waves_k;
+  p.kb_per_split = kb_per_split(L.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
-  p.counters = reinterpret_cast<int32_t*>(ws + w.counters);
-  KernelKey key{fmt_of(desc), c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
-  return launch_gemm(key, p, m_tiles, stream);
+  p.stream_rows = (int)(m < 16 ? m : 16);
+  p.a_bytes = m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ? 2 : 1);
+  p.a_scale_bytes = desc->act_fmt == HUM_ACT_MXFP8 ? m * (desc->k / 32) : 0;
+  if (c.kind == HUM_KERNEL_STREAM && p.a_bytes >= ((int64_t)1 << 31))
+    return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: activations above 2 GiB");
+  return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);
 }
 
 hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a, const void* a_scales,
@@ -377,30 +401,25 @@ hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m
 // MoE.
 
 struct MoeWs {
-  int64_t counters = 0, partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0;
+  int64_t partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0;
   int64_t xq = 0, xs = 0, inter = 0, inter_s = 0, y = 0, total = 0;
-  int64_t cap = 0, nblocks = 0, tiles = 0;
+  int64_t cap = 0, nblocks = 0;
 };
 
 static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
                     const hum_tile_config& c) {
   MoeWs w;
   const int64_t E = w13->num_experts;
-  const int64_t bm = 16 * c.wave_m;
+  const int64_t bm = tile_rows(c);
   const int64_t inter = w2->k;
   const int64_t h = w13->k;
   w.cap = t * topk + E * (bm - 1);
   w.nblocks = cdiv(w.cap, bm);
-  const int64_t nt_i = cdiv(inter, kNSub), nt_h = cdiv(h, kNSub);
-  const int64_t tiles_up = w.nblocks * cdiv(nt_i, (int64_t)(c.wave_n / 2) * c.waves_n);
-  const int64_t tiles_dn = w.nblocks * cdiv(nt_h, (int64_t)c.wave_n * c.waves_n);
-  w.tiles = tiles_up > tiles_dn ? tiles_up : tiles_dn;
   const bool mx = w13->act_fmt == HUM_ACT_MXFP8;
+  const int64_t pcols = (2 * inter > cdiv(h, kNSub) * kNSub) ? 2 * inter : cdiv(h, kNSub) * kNSub;
   int64_t off = 0;
-  w.counters = off;
-  off = kTicketBytes;
   w.partials = off;
-  off = align256(off + (c.split_k > 1 ? w.tiles * c.split_k * c.waves_n * (int64_t)c.wave_m * c.wave_n * 256 * 4 : 0));
+  if (c.split_k > 1) off = align256(off + (int64_t)c.split_k * w.cap * pcols * 4);
   w.sorted = off;
   off = align256(off + w.cap * 4);
   w.offsets = off;
@@ -436,11 +455,13 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
   if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");
   if (w2->n != w13->k) return set_error(HUM_ERR_INVALID_ARG, "w2 n must equal the hidden size (w13 k)");
-  if (w2->k % 64) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 64");
-  if (w13->k % 8) return set_error(HUM_ERR_UNSUPPORTED, "hidden size must be a multiple of 8");
+  if (w2->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 128");
   if (t < 0 || topk < 1 || topk > 64) return set_error(HUM_ERR_INVALID_ARG, "bad num_tokens / topk");
   if (w13->num_experts > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
   if ((t * topk + (int64_t)w13->num_experts * 127) >= ((int64_t)1 << 31)) return set_error(HUM_ERR_UNSUPPORTED, "too many tokens");
+  // activation buffers read through 32-bit buffer offsets
+  if (t * w13->k * 2 >= ((int64_t)1 << 31) || (t * topk + (int64_t)w13->num_experts * 127) * w2->k * 2 >= ((int64_t)1 << 31))
+    return set_error(HUM_ERR_UNSUPPORTED, "MoE activations above 2 GiB");
   return HUM_OK;
 }
 
@@ -488,12 +509,10 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   if (!cfg_sane(c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
   const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
-  KernelKey kup{f, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_GATHER, epi_up};
-  KernelKey kdn{f, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_SCATTER};
+  KernelKey kup{f, c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_GATHER, epi_up};
+  KernelKey kdn{f, c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_SCATTER};
   if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const MoeWs w = moe_ws(w13, w2, t, topk, c);
-  if (c.split_k > 1 && w.tiles > kMaxTickets)
-    return set_error(HUM_ERR_UNSUPPORTED, "split-K needs at most %lld output tiles", (long long)kMaxTickets);
   if (!workspace || ws_bytes < (size_t)w.total)
     return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
   log_cfg("moe", c, t);
@@ -502,7 +521,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   compute_layout(w2, &L2);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t E = w13->num_experts, h = w13->k, inter = w2->k;
-  const int32_t bm = 16 * c.wave_m;
+  const int32_t bm = (int32_t)tile_rows(c);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
   st = launch_align(topk_ids, t, topk, (int32_t)E, bm, sorted, reinterpret_cast<int32_t*>(ws + w.offsets),
@@ -533,12 +552,14 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   p.ldo = inter;
   p.out_scale = mx ? ws + w.inter_s : nullptr;
   p.bias = nullptr;
-  p.n_tiles = (int)cdiv(cdiv(inter, kNSub), (int64_t)(c.wave_n / 2) * c.waves_n);
+  p.n_tiles = (int)cdiv(cdiv(inter, kNSub), tile_subtiles(c) / 2);
   p.split_k = c.split_k;
-  p.kb_per_split = (int)cdiv(cdiv(L13.kb, c.split_k), c.waves_k) * c.waves_k;
+  p.kb_per_split = kb_per_split(L13.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
-  p.counters = reinterpret_cast<int32_t*>(ws + w.counters);
-  st = launch_gemm(kup, p, w.nblocks, stream);
+  p.stream_rows = 16;
+  p.a_bytes = t * h * (mx ? 1 : 2);
+  p.a_scale_bytes = mx ? t * (h / 32) : 0;
+  st = launch_gemm(kup, p, w.nblocks, bm, stream);
   if (st != HUM_OK) return st;
   // down (rows scattered back to flat slots)
   GemmParams q{};
@@ -556,12 +577,14 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.ldo = h;
   q.out_scale = nullptr;
   q.bias = nullptr;
-  q.n_tiles = (int)cdiv(L2.nt, (int64_t)c.wave_n * c.waves_n);
+  q.n_tiles = (int)cdiv(L2.nt, tile_subtiles(c));
   q.split_k = c.split_k;
-  q.kb_per_split = (int)cdiv(cdiv(L2.kb, c.split_k), c.waves_k) * c.waves_k;
+  q.kb_per_split = kb_per_split(L2.kb, c);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
-  q.counters = reinterpret_cast<int32_t*>(ws + w.counters);
-  st = launch_gemm(kdn, q, w.nblocks, stream);
+  q.stream_rows = 16;
+  q.a_bytes = w.cap * inter * (mx ? 1 : 2);
+  q.a_scale_bytes = mx ? w.cap * (inter / 32) : 0;
+  st = launch_gemm(kdn, q, w.nblocks, bm, stream);
   if (st != HUM_OK) return st;
   return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
 }

@@ -3,34 +3,41 @@
 // What is computed is the WnA16 / W8A8 / W4A8 GEMM of "Announcing Humming:
 // Fast, Flexible Kernels for Quantized Inference" (sections "WnA16" and
 // "W8A8 / W4A8 / W4A4"): dequantization and scaling fused into the GEMM
-// (section "Shared CUDA components"), per-GEMM-type task mapping for dense and
-// MoE work, scale / bias epilogues.  The design is gfx950's own:
+// (section "Shared CUDA components"), a task mapping per GEMM type for dense
+// and MoE work, scale / bias epilogues.  The design is gfx950's own.
 //
-// * One workgroup = 4 wave64s.  All waves share the same 16*WM activation
-//   rows; waves sit side by side along N (WAVES_N) and/or split the K-blocks
-//   of a stage (WAVES_K, reduced through LDS at the end).
-// * Activations are staged through LDS per stage (WAVES_K K-blocks of 128),
-//   double buffered, XOR-swizzled so the MFMA operand reads are conflict
-//   free.  Weights stream from HBM straight into registers with one 16-byte
-//   load per lane per (16-column sub-tile, K-block) -- the packed layout puts
-//   exactly the MFMA operand of each lane there -- and are dequantized in
-//   registers.
-// * Formats:
-//     F_INT          INT4/UINT4 codes become bf16 (128 + u) with one AND-OR
-//                    per two codes; the MFMA accumulates a K-block in fp32
-//                    and s * (P - c * sum(a)) applies scale, zero point and
-//                    the 128 offset per K-block (exact for integer codes).
-//     F_MXFP4_BF16   E2M1 codes are converted with their E8M0 scale by
-//                    v_cvt_scalef32_pk_bf16_fp4 (exact) into bf16 MFMA.
-//     F_FP8          E4M3 x E4M3 on the 16x16x128 f8f6f4 MFMA, per-token and
-//                    per-channel scales in the epilogue.
-//     F_MXFP4_MXFP8  E4M3 activations x E2M1 weights on the block-scaled
-//                    16x16x128 MFMA with both E8M0 scales as operands.
-// * Split-K across workgroups writes fp32 partials; the last workgroup of a
-//   tile (atomic ticket) sums them in split order, so results are
-//   deterministic run to run, and resets its ticket.  Partial sums are never
-//   rounded below fp32 (the accuracy loss through a bf16 Stream-K reduction
-//   reported as issue #31 on the senn-tech.com review is the case avoided).
+// Two kernel families share the fragment, MFMA and epilogue code below:
+//
+// * stream_kernel (decode, one 16-row tile): KW wave64s of a workgroup walk
+//   interleaved K-blocks of the same WN 16-column sub-tiles.  Weights stream
+//   from HBM straight into a register ring PF K-blocks deep (one 16-byte
+//   load per lane per sub-tile and K-block -- the packed layout puts exactly
+//   each lane's MFMA operand there); activation fragments come straight from
+//   global memory (they are small and stay in L2).  No barrier until the
+//   final in-workgroup reduction through LDS.
+// * tile_kernel (prefill): 4 waves side by side along N share a 16*WM-row
+//   activation tile staged through LDS (double buffered, XOR swizzled so the
+//   operand reads are conflict free); each wave dequantizes its own weight
+//   columns in registers.  Workgroups are ordered so that the tiles of one
+//   activation row block land on one XCD (shared L2).
+//
+// Formats:
+//   F_INT          INT4/UINT4 -> bf16 (128 + u) with one AND-OR per two
+//                  codes; a K-block accumulates in fp32 and
+//                  s * (P - (128 + z) * sum(a)) applies scale, zero point and
+//                  the offset (exact for integer codes).
+//   F_MXFP4_BF16   E2M1 with its E8M0 scale -> bf16 through
+//                  v_cvt_scalef32_pk_bf16_fp4 (exact), bf16 MFMA.
+//   F_FP8          E4M3 x E4M3 on the 16x16x128 f8f6f4 MFMA; per-token and
+//                  per-channel scales in the epilogue.
+//   F_MXFP4_MXFP8  E4M3 activations x E2M1 weights on the block-scaled
+//                  16x16x128 MFMA, both E8M0 scales as operands.
+//
+// Split-K across workgroups writes fp32 partials; a separate reduce kernel
+// sums them in split order (deterministic) and applies the epilogue.
+// Partial sums are never rounded below fp32 (the accuracy loss through a bf16
+// Stream-K reduction, issue #31 in the senn-tech.com review, is what this
+// avoids).
 #include "dev_common.h"
 #include "hum_internal.h"
 
@@ -38,18 +45,63 @@
 
 namespace hum {
 
-using I0 = std::integral_constant<int, 0>;
-using I1 = std::integral_constant<int, 1>;
-
 template <int FMT>
-struct FmtTraits {
+struct Tr {
   static constexpr int kAElem = (FMT == F_INT || FMT == F_MXFP4_BF16) ? 2 : 1;  // activation bytes
-  static constexpr int kBWords = (FMT == F_FP8) ? 2 : 1;                         // 16-B weight words / lane / K-block
-  static constexpr bool kBf16Mfma = (FMT == F_INT || FMT == F_MXFP4_BF16);
+  static constexpr int kBWords = (FMT == F_FP8) ? 2 : 1;                         // 16-B words / lane / K-block
+  static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16);
 };
 
-__device__ __forceinline__ int swz(int r, int c, int a_elem) {
-  return a_elem == 2 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+// ---------------------------------------------------------------------------
+// Weight fragments
+
+template <int FMT>
+struct BFrag {
+  u32x4_t w[Tr<FMT>::kBWords];
+  uint32_t meta;  // INT: f32 scale bits; MX: E8M0 code of this K-block
+  uint32_t zero;  // INT: zero point nibble
+};
+
+struct WPtrs {
+  const uint8_t* codes;
+  const uint8_t* meta;
+  const uint8_t* zero;
+};
+
+// Loads of one weight fragment.  Every load is unconditional -- an invalid
+// (sub-tile, K-block) reads block 0 and is zeroed by a select -- because a
+// load inside a divergent branch makes the compiler wait for all
+// outstanding loads when the branch rejoins, which would serialize the
+// prefetch ring.
+template <int FMT>
+__device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WPtrs& w, int nt, bool ok, int kb,
+                                             int lane) {
+  BFrag<FMT> f;
+  const int ntc = ok ? nt : 0, kbc = ok ? kb : 0;
+  const int64_t blk = ((int64_t)ntc * p.kb_count + kbc) * 64 + lane;
+#pragma unroll
+  for (int i = 0; i < Tr<FMT>::kBWords; ++i) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w.codes + blk * (16 * Tr<FMT>::kBWords) + 16 * i);
+    const u32x4_t z = {0, 0, 0, 0};
+    f.w[i] = ok ? v : z;
+  }
+  f.meta = 0;
+  f.zero = 0;
+  if (FMT == F_INT) {
+    const int c16 = lane & 15;
+    const int64_t gi = (int64_t)ntc * p.ng + kbc / p.kb_per_group;
+    // bf16 scales: the dword holding the pair of column c16; f32: its dword
+    const int64_t off = p.scale_f32 ? (gi * 16 + c16) * 4 : (gi * 16 + (c16 & ~1)) * 2;
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(w.meta + off);
+    const uint32_t bits = p.scale_f32 ? sw : ((c16 & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+    const uint64_t zw = *reinterpret_cast<const uint64_t*>(w.zero + gi * 8);
+    f.meta = ok ? bits : 0u;
+    f.zero = (ok && p.has_zero) ? (uint32_t)(zw >> (4 * c16)) & 0xF : 0u;
+  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+    const uint32_t word = reinterpret_cast<const uint32_t*>(w.meta)[((int64_t)ntc * p.kb4 + kbc / 4) * 64 + lane];
+    f.meta = ok ? (word >> (8 * (kbc & 3))) & 0xFF : 127u;
+  }
+  return f;
 }
 
 __device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
@@ -62,55 +114,167 @@ __device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
 }
 
 __device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
-  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
   u32x4_t o;
-  o[0] = __builtin_bit_cast(uint32_t, p0);
-  o[1] = __builtin_bit_cast(uint32_t, p1);
-  o[2] = __builtin_bit_cast(uint32_t, p2);
-  o[3] = __builtin_bit_cast(uint32_t, p3);
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// bf16 B operand of the 4 k-steps of a K-block.
+template <int FMT>
+__device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, bf16x8_t (&d)[4]) {
+  if (FMT == F_INT) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) d[s] = int_dequant(f.w[0][s]);
+  } else {
+    const float fs = e8m0_to_f32(f.meta);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) d[s] = mx_dequant(f.w[0][s], fs);
+  }
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16_kblock(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], f32x4_t c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+template <int FMT>
+__device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, const BFrag<FMT>& f, f32x4_t c) {
+  i32x8_t b8;
+  b8[0] = f.w[0][0]; b8[1] = f.w[0][1]; b8[2] = f.w[0][2]; b8[3] = f.w[0][3];
+  if (FMT == F_FP8) {
+    b8[4] = f.w[Tr<FMT>::kBWords - 1][0]; b8[5] = f.w[Tr<FMT>::kBWords - 1][1];
+    b8[6] = f.w[Tr<FMT>::kBWords - 1][2]; b8[7] = f.w[Tr<FMT>::kBWords - 1][3];
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 127, 0, 127);
+  } else {
+    b8[4] = 0; b8[5] = 0; b8[6] = 0; b8[7] = 0;
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 4, 0, sa, 0, (int)f.meta);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue pieces
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
-template <int FMT, int WM, int WN, int WAVES_N, int WAVES_K, int AMODE, int EPI>
-struct GemmCfg {
-  using T = FmtTraits<FMT>;
-  static constexpr int kTM = 16 * WM;
-  static constexpr int kTNS = WN * WAVES_N;  // sub-tiles per workgroup (weight space)
-  static constexpr int kRowB = 128 * T::kAElem;
-  static constexpr int kCPR = kRowB / 16;
-  static constexpr int kKbBytes = kTM * kRowB;
-  static constexpr int kStageA = WAVES_K * kKbBytes;
-  static constexpr int kStageRs = (FMT == F_INT) ? WAVES_K * kTM * 4 : 0;
-  static constexpr int kStageAs = (FMT == F_MXFP4_MXFP8) ? WAVES_K * kTM * 4 : 0;
-  static constexpr int kStage = kStageA + kStageRs + kStageAs;
-  static constexpr int kChunks = WAVES_K * kTM * kCPR;
-  static constexpr int kCPT = (kChunks + 255) / 256;
-  static constexpr int kAccPerWave = WM * WN * 4 * 64;  // floats
-  static constexpr int kRedBytes = (WAVES_K - 1) * WAVES_N * kAccPerWave * 4;
-  static constexpr int kLds = (2 * kStage > kRedBytes) ? 2 * kStage : kRedBytes;
-  static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
-  static_assert(WAVES_N * WAVES_K == 4, "4 waves per workgroup");
-  static_assert(!kSwiglu || (WN % 2 == 0), "SwiGLU needs gate/up sub-tile pairs");
-  static_assert(EPI != EPI_SWIGLU_MXFP8 || (WN % 4 == 0), "MXFP8 epilogue needs 32-column blocks");
-  static_assert(kLds <= 160 * 1024, "LDS budget");
+// Column scale of the plain / scatter epilogues (per-channel FP8 scale and
+// the second-level scale); the per-token FP8 row scale is applied apart.
+template <int FMT>
+__device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, float gs) {
+  if (FMT == F_FP8) return gs * reinterpret_cast<const float*>(wmeta)[col];
+  return gs;
+}
+
+// Stores of one 16x16 accumulator tile held in the MFMA C layout (lane holds
+// rows 4*lg + i of column c16) for the plain and scatter epilogues.
+template <int FMT, int EPI>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* wmeta, float gs, int64_t row_base,
+                                           int64_t col, const f32x4_t& v, int lg) {
+  if (col >= p.n) return;
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const float cs = col_scale<FMT>(wmeta, col, gs);
+  const float bias = (EPI == EPI_BF16 && p.bias) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row_base + 4 * lg + i;
+    if (row >= p.m) continue;
+    float x = v[i] * cs;
+    if (FMT == F_FP8) x *= reinterpret_cast<const float*>(p.a_scale)[row];
+    x += bias;
+    if (EPI == EPI_SCATTER) {
+      const int32_t f = p.sorted[row];
+      if (f >= p.sentinel) continue;
+      out[(int64_t)f * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
+    } else {
+      out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
+    }
+  }
+}
+
+// SwiGLU epilogue of a gate / up tile pair in the C layout.
+__device__ __forceinline__ void store_swiglu_bf16(const GemmParams& p, float gs, int64_t row_base, int64_t col,
+                                                  const f32x4_t& g, const f32x4_t& u, int lg) {
+  if (col >= p.n) return;
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row_base + 4 * lg + i;
+    if (row >= p.m) continue;
+    out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(silu_f32(g[i] * gs) * (u[i] * gs));
+  }
+}
+
+// SwiGLU + MXFP8 requantization of 32 columns: two gate / up tile pairs.
+// The 16 lanes of a DPP row hold the 16 columns of the same 4 rows, so the
+// block absolute maximum is a row reduction.
+__device__ __forceinline__ void store_swiglu_mxfp8(const GemmParams& p, float gs, int64_t row_base, int64_t col0,
+                                                   const f32x4_t& g0, const f32x4_t& u0, const f32x4_t& g1,
+                                                   const f32x4_t& u1, int lg, int c16) {
+  uint8_t* outq = static_cast<uint8_t*>(p.out);
+  uint8_t* outs = static_cast<uint8_t*>(p.out_scale);
+  const bool ok = (col0 - c16) < p.n;  // whole 32-column block valid (I % 32 == 0)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row_base + 4 * lg + i;
+    const float a0 = silu_f32(g0[i] * gs) * (u0[i] * gs);
+    const float a1 = silu_f32(g1[i] * gs) * (u1[i] * gs);
+    const float amax = row16_max(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
+    const int e = mx_scale_code(amax);
+    const float inv = mx_inv_scale(e);
+    const uint32_t q = f32x2_to_e4m3x2(a0 * inv, a1 * inv);
+    if (ok && row < p.m) {
+      outq[row * p.ldo + col0] = (uint8_t)(q & 0xFF);
+      outq[row * p.ldo + col0 + 16] = (uint8_t)(q >> 8);
+      if (c16 == 0) outs[row * (p.ldo / 32) + (col0 - c16) / 32] = (uint8_t)e;
+    }
+  }
+}
+
+// Partial tile (fp32, natural [split][row][col] layout) of one 16x16 C tile.
+__device__ __forceinline__ void store_partial(const GemmParams& p, int split, int64_t row_base, int64_t col,
+                                              int64_t ncols, const f32x4_t& v, int lg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row_base + 4 * lg + i;
+    if (row >= p.m) continue;
+    if (p.sorted && p.sorted[row] >= p.sentinel) continue;
+    p.partials[((int64_t)split * p.m + row) * ncols + col] = v[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel: one 16-row tile (at most 16 valid rows), KW waves over
+// interleaved K-blocks.
+//
+// The activation rows of the workgroup's K range are staged into LDS once
+// (rows >= valid count are never stored: their fragments read as zero), so
+// the main loop's only vector-memory loads are the weight ring: PF K-blocks
+// per wave in flight, never stalled behind an activation load (vector memory
+// loads complete in order).  LDS row layout per K-block: 16-byte chunks
+// XOR-swizzled with the row, so the 16 rows of one fragment read hit 16
+// different bank groups.
+
+template <int FMT>
+struct StreamLds {
+  static constexpr int kRowB = 128 * Tr<FMT>::kAElem;  // bytes per row per K-block
 };
 
-template <int FMT, int WM, int WN, int WAVES_N, int WAVES_K, int AMODE, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
-  using C = GemmCfg<FMT, WM, WN, WAVES_N, WAVES_K, AMODE, EPI>;
-  using Tr = typename C::T;
-  constexpr int kAE = Tr::kAElem;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
-  __shared__ int s_last;
+template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
+__global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
+  using T = Tr<FMT>;
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
+  static_assert(EPI != EPI_SWIGLU_MXFP8 || WN % 4 == 0, "32-column MXFP8 blocks");
+  constexpr int kRowB = StreamLds<FMT>::kRowB;
+  constexpr int kCPR = kRowB / 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  __shared__ int32_t s_src[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WAVES_N, wk = wave / WAVES_N;
   const int c16 = lane & 15, lg = lane >> 4;
 
   int64_t bid = blockIdx.x;
@@ -118,27 +282,297 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   bid /= p.split_k;
   const int tn = (int)(bid % p.n_tiles);
   const int64_t tm = bid / p.n_tiles;
-  const int64_t tile_id = tm * p.n_tiles + tn;
 
   int expert = 0;
   if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
     expert = p.block_expert[tm];
-    if (expert < 0) return;  // block past the last expert segment
+    if (expert < 0) return;
   }
-  const int64_t row0 = tm * C::kTM;
-  const uint8_t* codes = p.codes + (int64_t)expert * p.codes_per_expert;
-  const uint8_t* wmeta = p.wscale + (int64_t)expert * p.scales_per_expert;
-  const uint8_t* wzero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : nullptr;
+  const int64_t row0 = tm * 16;
+  WPtrs wp;
+  wp.codes = p.codes + (int64_t)expert * p.codes_per_expert;
+  wp.meta = p.wscale + (int64_t)expert * p.scales_per_expert;
+  // without zero points the (unused) zero loads read the scale array
+  wp.zero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : wp.meta;
   const float gs = p.gscale[expert];
 
-  // This wave's 16-column sub-tiles (weight space) and their validity.
   int nts[WN];
   bool ntv[WN];
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) {
-    if (C::kSwiglu) {
-      const int j = ns % (WN / 2);
-      const int ntg = tn * (C::kTNS / 2) + wn * (WN / 2) + j;
+    if constexpr (kSwiglu) {
+      const int ntg = tn * (WN / 2) + ns % (WN / 2);
+      ntv[ns] = ntg * 16 < p.n;
+      nts[ns] = ntg + (ns >= WN / 2 ? p.swiglu_nt_off : 0);
+    } else {
+      nts[ns] = tn * WN + ns;
+      ntv[ns] = nts[ns] < p.nt_count;
+    }
+  }
+
+  const int kb_begin = split * p.kb_per_split;
+  int kb_end = kb_begin + p.kb_per_split;
+  if (kb_end > p.kb_count) kb_end = p.kb_count;
+  const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
+  const int first = kb_begin + wave;
+  const int nj = first < kb_end ? (kb_end - first + KW - 1) / KW : 0;
+
+  // source row of each tile row (-1: padding / past the end)
+  if (tid < 16) {
+    const int64_t row = row0 + tid;
+    int64_t src = -1;
+    if (AMODE == A_GATHER) {
+      const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
+      if (f < p.sentinel) src = f / p.topk;
+    } else if (row < p.m) {
+      src = row;
+    }
+    s_src[tid] = (int32_t)src;
+  }
+  __syncthreads();
+  // rows [0, nrows) are stored; tile rows are compacted only at the end
+  // (dense: rows < m are a prefix; MoE: valid rows of a block are a prefix)
+  int nrows = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nrows += s_src[r] >= 0 ? 1 : 0;
+
+  // 1) weight ring
+  BFrag<FMT> ring[PF][WN];
+#pragma unroll
+  for (int q = 0; q < PF; ++q)
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns] && q < nj, first + q * KW, lane);
+
+  // LDS: activation slots (rounded up to whole 64-lane DMA instructions),
+  // then the MX scale dwords (likewise rounded)
+  const int scale_off = ((nrows * kCPR * nkb + 63) & ~63) * 16;
+  // 2) activation rows -> LDS with LDS-DMA loads (no registers; each wave
+  //    instruction fills 64 consecutive 16-byte slots, slot s of the layout
+  //    [K-block][row][swizzled chunk] holds logical chunk phys ^ swizzle(row))
+  {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.a), (short)0,
+                                                                          (int)p.a_bytes, 0x00020000);
+    const int slots = nrows * kCPR * nkb;
+    // each DMA instruction writes all 64 lanes' slots (zeros past `slots`):
+    // the footprint is slots rounded up to 64, which the launch sizes for
+    for (int base = wave * 64; base < slots; base += 64 * KW) {
+      const int sidx = base + lane;
+      // lanes past `slots` fill unused slots of the footprint from offset 0
+      // (always a valid address): no reliance on range checking
+      uint32_t voff = 0;
+      if (sidx < slots) {
+        const int phys = sidx % kCPR;
+        const int r = (sidx / kCPR) % nrows;
+        const int kbl = sidx / (kCPR * nrows);
+        const int c = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
+        voff = (uint32_t)(((int64_t)s_src[r] * p.lda + (int64_t)(kb_begin + kbl) * 128) * T::kAElem + c * 16);
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dsm + base * 16, 16, voff, 0, 0, 0);
+    }
+    if (FMT == F_MXFP4_MXFP8) {
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.a_scale), (short)0,
+                                                                           (int)p.a_scale_bytes, 0x00020000);
+      const int n4 = nrows * nkb;
+      for (int base = wave * 64; base < n4; base += 64 * KW) {
+        const int sidx = base + lane;
+        uint32_t voff = 0;
+        if (sidx < n4) {
+          const int r = sidx % nrows, kbl = sidx / nrows;
+          voff = (uint32_t)((int64_t)s_src[r] * p.a_scale_ld + (int64_t)(kb_begin + kbl) * 4);
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, dsm + scale_off + base * 4, 4, voff, 0, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x4_t acc[WN];
+#pragma unroll
+  for (int ns = 0; ns < WN; ++ns) acc[ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const bool arow_ok = c16 < nrows;
+  const int rr = arow_ok ? c16 : 0;  // LDS row read (row 0 stands in for empty rows; nrows >= 1)
+
+  for (int j0 = 0; j0 < nj; j0 += PF) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int j = j0 + q;
+      if (j < nj) {
+        const int kb = first + j * KW;
+        const uint8_t* ab = dsm + ((kb - kb_begin) * nrows + rr) * kRowB;
+        if constexpr (T::kBf16) {
+          bf16x8_t af[4];
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ab + (((4 * lg + s) ^ rr) * 16));
+            const u32x4_t z = {0, 0, 0, 0};
+            af[s] = __builtin_bit_cast(bf16x8_t, arow_ok ? v : z);
+          }
+          f32x4_t rs = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (FMT == F_INT) {
+            // row sums of the K-block in the C layout: A x ones
+            const u32x4_t o = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+            const bf16x8_t one = __builtin_bit_cast(bf16x8_t, o);
+            const bf16x8_t on[4] = {one, one, one, one};
+            rs = mfma_bf16_kblock(af, on, rs);
+          }
+#pragma unroll
+          for (int ns = 0; ns < WN; ++ns) {
+            bf16x8_t d[4];
+            dequant_b<FMT>(ring[q][ns], d);
+            if (FMT == F_INT) {
+              const f32x4_t t = mfma_bf16_kblock(af, d, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+              const float sc = __uint_as_float(ring[q][ns].meta);
+              const float off = (float)(p.int_offset + (int)ring[q][ns].zero);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ns][i]);
+            } else {
+              acc[ns] = mfma_bf16_kblock(af, d, acc[ns]);
+            }
+          }
+        } else {
+          const int sw = (rr >> 1) & 7;
+          const u32x4_t z = {0, 0, 0, 0};
+          u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ab + ((lg ^ sw) * 16));
+          u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ab + (((4 + lg) ^ sw) * 16));
+          lo = arow_ok ? lo : z;
+          hi = arow_ok ? hi : z;
+          int sa = 127;
+          if (FMT == F_MXFP4_MXFP8) {
+            const uint32_t sw4 = reinterpret_cast<const uint32_t*>(dsm + scale_off)[(kb - kb_begin) * nrows + rr];
+            sa = arow_ok ? (int)((sw4 >> (8 * lg)) & 0xFF) : 127;
+          }
+          i32x8_t a8;
+          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
+          a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
+#pragma unroll
+          for (int ns = 0; ns < WN; ++ns) acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], acc[ns]);
+        }
+      }
+      // refill unconditionally (a conditional load would be waited on where
+      // the branch rejoins); past the end it re-reads the current block,
+      // which is an L2 hit and is never used
+      {
+        const int jn = (j + PF < nj) ? j + PF : (j < nj ? j : 0);
+        const int kbn = first + jn * KW;
+#pragma unroll
+        for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns] && nj > 0, kbn, lane);
+      }
+    }
+  }
+
+  // in-workgroup reduction over the KW waves (fixed order), through the LDS
+  // that held the activations
+  if constexpr (KW > 1) {
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(dsm);
+    __syncthreads();
+    if (wave > 0) {
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) red[((wave - 1) * WN + ns) * 64 + lane] = acc[ns];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < KW; ++w)
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) {
+        const f32x4_t v = red[((w - 1) * WN + ns) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ns][i] += v[i];
+      }
+  }
+
+  if (p.split_k > 1) {
+    const int64_t ncols = kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) {
+      if (!ntv[ns]) continue;
+      store_partial(p, split, row0, (int64_t)nts[ns] * 16 + c16, ncols, acc[ns], lg);
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg);
+  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+#pragma unroll
+    for (int j = 0; j < WN / 2; ++j)
+      store_swiglu_bf16(p, gs, row0, (int64_t)nts[j] * 16 + c16, acc[j], acc[j + WN / 2], lg);
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < WN / 4; ++jj)
+      store_swiglu_mxfp8(p, gs, row0, (int64_t)nts[2 * jj] * 16 + c16, acc[2 * jj], acc[2 * jj + WN / 2],
+                         acc[2 * jj + 1], acc[2 * jj + 1 + WN / 2], lg, c16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel: 4 waves along N share a (16*WM)-row activation tile in LDS.
+
+template <int FMT, int WM, int WN, int AMODE, int EPI>
+struct TileCfg {
+  using T = Tr<FMT>;
+  static constexpr int kTM = 16 * WM;
+  static constexpr int kTNS = 4 * WN;  // weight sub-tiles per workgroup
+  static constexpr int kRowB = 128 * T::kAElem;
+  static constexpr int kCPR = kRowB / 16;
+  static constexpr int kStageA = kTM * kRowB;
+  static constexpr int kStageX = (FMT == F_INT || FMT == F_MXFP4_MXFP8) ? kTM * 4 : 0;  // row sums / scales
+  static constexpr int kStage = kStageA + kStageX;
+  static constexpr int kChunks = kTM * kCPR;
+  static constexpr int kCPT = (kChunks + 255) / 256;
+  static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
+  static_assert(EPI != EPI_SWIGLU_MXFP8 || WN % 4 == 0, "32-column MXFP8 blocks");
+  static_assert(2 * kStage <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ int swz(int r, int c, int a_elem) {
+  return a_elem == 2 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+template <int FMT, int WM, int WN, int AMODE, int EPI>
+__global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
+  using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
+  using T = typename C::T;
+  constexpr int kAE = T::kAElem;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wn = tid >> 6;
+  const int c16 = lane & 15, lg = lane >> 4;
+
+  // XCD-aware order: consecutive workgroup ids go round-robin over the 8
+  // XCDs; remap them so that each XCD walks a contiguous range of
+  // (m-tile, n-tile, split) tiles -- n fastest -- and reuses its activation
+  // rows from its own L2.
+  const int64_t nwg = gridDim.x;
+  int64_t bid = blockIdx.x;
+  if (nwg % 8 == 0) bid = (bid % 8) * (nwg / 8) + bid / 8;
+  const int split = (int)(bid % p.split_k);
+  bid /= p.split_k;
+  const int tn = (int)(bid % p.n_tiles);
+  const int64_t tm = bid / p.n_tiles;
+
+  int expert = 0;
+  if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
+    expert = p.block_expert[tm];
+    if (expert < 0) return;
+  }
+  const int64_t row0 = tm * C::kTM;
+  WPtrs wp;
+  wp.codes = p.codes + (int64_t)expert * p.codes_per_expert;
+  wp.meta = p.wscale + (int64_t)expert * p.scales_per_expert;
+  // without zero points the (unused) zero loads read the scale array
+  wp.zero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : wp.meta;
+  const float gs = p.gscale[expert];
+
+  int nts[WN];
+  bool ntv[WN];
+#pragma unroll
+  for (int ns = 0; ns < WN; ++ns) {
+    if constexpr (C::kSwiglu) {
+      const int ntg = tn * (C::kTNS / 2) + wn * (WN / 2) + ns % (WN / 2);
       ntv[ns] = ntg * 16 < p.n;
       nts[ns] = ntg + (ns >= WN / 2 ? p.swiglu_nt_off : 0);
     } else {
@@ -150,25 +584,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const int kb_begin = split * p.kb_per_split;
   int kb_end = kb_begin + p.kb_per_split;
   if (kb_end > p.kb_count) kb_end = p.kb_count;
-  const int n_kb = kb_end > kb_begin ? kb_end - kb_begin : 0;
-  const int n_stages = (n_kb + WAVES_K - 1) / WAVES_K;
+  const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
 
-  // ---- activation row sources of this thread's staging chunks --------------
+  // staging chunks of this thread
   const uint8_t* a_row[C::kCPT];
-  int ch_off[C::kCPT];  // LDS offset inside a stage
-  int ch_kbl[C::kCPT];
-  int ch_col[C::kCPT];
-  bool ch_ok[C::kCPT];
+  int ch_off[C::kCPT], ch_col[C::kCPT];
+  bool ch_ok[C::kCPT], a_ok_[C::kCPT];
 #pragma unroll
   for (int i = 0; i < C::kCPT; ++i) {
     const int id = tid + 256 * i;
-    ch_ok[i] = id < C::kChunks;
-    const int kbl = id / (C::kTM * C::kCPR);
-    const int rem = id % (C::kTM * C::kCPR);
-    const int r = rem / C::kCPR, c = rem % C::kCPR;
-    ch_kbl[i] = kbl;
+    ch_ok[i] = (C::kChunks % 256 == 0) || id < C::kChunks;  // compile-time true for full tiles
+    const int r = (id / C::kCPR) % C::kTM, c = id % C::kCPR;
     ch_col[i] = c;
-    ch_off[i] = kbl * C::kKbBytes + r * C::kRowB + swz(r, c, kAE) * 16;
+    ch_off[i] = r * C::kRowB + swz(r, c, kAE) * 16;
     const int64_t row = row0 + r;
     const uint8_t* src = nullptr;
     if (ch_ok[i]) {
@@ -180,97 +608,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
       }
     }
     a_row[i] = src;
+    a_ok_[i] = src != nullptr;
+    if (!src) a_row[i] = static_cast<const uint8_t*>(p.a);  // valid stand-in, zeroed by a select
   }
-  // MXFP8 activation scale rows (one dword = the 4 E8M0 codes of a K-block)
-  const uint8_t* as_row = nullptr;
-  int as_off = 0, as_kbl = 0;
-  if (FMT == F_MXFP4_MXFP8 && tid < WAVES_K * C::kTM) {
-    as_kbl = tid / C::kTM;
-    const int r = tid % C::kTM;
-    as_off = C::kStageA + C::kStageRs + (as_kbl * C::kTM + r) * 4;
-    const int64_t row = row0 + r;
-    if (AMODE == A_GATHER) {
-      const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-      if (f < p.sentinel) as_row = static_cast<const uint8_t*>(p.a_scale) + (int64_t)(f / p.topk) * p.a_scale_ld;
-    } else if (row < p.m) {
-      as_row = static_cast<const uint8_t*>(p.a_scale) + row * p.a_scale_ld;
+  // per-row extra (INT row sums [m][kb_count] / MXFP8 scale dwords).  Every
+  // thread gets a valid address (row 0 stands in; zeroed by a select) since
+  // the load in load_a is unconditional; threads >= kTM never store it.
+  const uint8_t* x_row = nullptr;
+  bool x_ok = false;
+  if constexpr (FMT == F_INT || FMT == F_MXFP4_MXFP8) {
+    int64_t src = -1;
+    if (tid < C::kTM) {
+      const int64_t row = row0 + tid;
+      if (AMODE == A_GATHER) {
+        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
+        if (f < p.sentinel) src = f / p.topk;
+      } else if (row < p.m) {
+        src = row;
+      }
     }
+    x_ok = src >= 0;
+    const int64_t r = x_ok ? src : 0;
+    if (FMT == F_INT) x_row = reinterpret_cast<const uint8_t*>(p.a_rowsum + r * p.kb_count);
+    else x_row = static_cast<const uint8_t*>(p.a_scale) + r * p.a_scale_ld;
   }
 
   u32x4_t a_reg[C::kCPT];
-  uint32_t as_reg = 0x7F7F7F7Fu;
-  auto load_a = [&](int st) {
+  uint32_t x_reg = 0;
+  auto load_a = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < C::kCPT; ++i) {
-      const int kb = kb_begin + st * WAVES_K + ch_kbl[i];
-      u32x4_t v = {0, 0, 0, 0};
-      if (a_row[i] && kb < kb_end)
-        v = *reinterpret_cast<const u32x4_t*>(a_row[i] + (int64_t)kb * 128 * kAE + ch_col[i] * 16);
-      a_reg[i] = v;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a_row[i] + (int64_t)kb * 128 * kAE + ch_col[i] * 16);
+      const u32x4_t z = {0, 0, 0, 0};
+      a_reg[i] = a_ok_[i] ? v : z;
     }
-    if (FMT == F_MXFP4_MXFP8) {
-      const int kb = kb_begin + st * WAVES_K + as_kbl;
-      as_reg = 0x7F7F7F7Fu;
-      if (as_row && kb < kb_end) as_reg = *reinterpret_cast<const uint32_t*>(as_row + (int64_t)kb * 4);
+    if constexpr (FMT == F_INT || FMT == F_MXFP4_MXFP8) {
+      const uint32_t xv = reinterpret_cast<const uint32_t*>(x_row)[kb];
+      x_reg = x_ok ? xv : ((FMT == F_INT) ? 0u : 0x7F7F7F7Fu);
     }
   };
   auto store_a = [&](int buf) {
     uint8_t* base = smem + buf * C::kStage;
 #pragma unroll
-    for (int i = 0; i < C::kCPT; ++i) {
-      if (!ch_ok[i]) continue;
-      *reinterpret_cast<u32x4_t*>(base + ch_off[i]) = a_reg[i];
-      if (FMT == F_INT) {
-        float s = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s += bf16_bits_to_f32(a_reg[i][q] & 0xFFFF) + bf16_bits_to_f32(a_reg[i][q] >> 16);
-        s = row16_sum(s);  // the 16 chunks of one row's K-block are one DPP row
-        if (ch_col[i] == 0) {
-          const int id = tid + 256 * i;
-          const int r = (id % (C::kTM * C::kCPR)) / C::kCPR;
-          reinterpret_cast<float*>(base + C::kStageA)[ch_kbl[i] * C::kTM + r] = s;
-        }
-      }
-    }
-    if (FMT == F_MXFP4_MXFP8 && tid < WAVES_K * C::kTM)
-      *reinterpret_cast<uint32_t*>(base + as_off) = as_reg;
+    for (int i = 0; i < C::kCPT; ++i)
+      if (ch_ok[i]) *reinterpret_cast<u32x4_t*>(base + ch_off[i]) = a_reg[i];
+    if ((FMT == F_INT || FMT == F_MXFP4_MXFP8) && tid < C::kTM)
+      reinterpret_cast<uint32_t*>(base + C::kStageA)[tid] = x_reg;
   };
 
-  // ---- weights -------------------------------------------------------------
-  u32x4_t bw[2][WN][Tr::kBWords];
-  uint32_t bm[2][WN];   // meta: INT scale bits / MX scale dword
-  uint32_t bz[2][WN];   // INT zero nibble
-  auto load_b = [&](int st, auto set_c) {
+  BFrag<FMT> bq[2][WN];
+  auto load_bs = [&](int kb, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const int kb = kb_begin + st * WAVES_K + wk;
-    const bool kok = kb < kb_end;
 #pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-      const bool ok = kok && ntv[ns];
-      const int64_t blk = ((int64_t)nts[ns] * p.kb_count + kb) * 64 + lane;
-#pragma unroll
-      for (int w = 0; w < Tr::kBWords; ++w) {
-        u32x4_t v = {0, 0, 0, 0};
-        if (ok) v = *reinterpret_cast<const u32x4_t*>(codes + blk * (16 * Tr::kBWords) + 16 * w);
-        bw[set][ns][w] = v;
-      }
-      if (FMT == F_INT) {
-        uint32_t sbits = 0, z = 0;
-        if (ok) {
-          const int g = kb / p.kb_per_group;
-          const int64_t gi = (int64_t)nts[ns] * p.ng + g;
-          sbits = p.scale_f32 ? reinterpret_cast<const uint32_t*>(wmeta)[gi * 16 + c16]
-                              : (uint32_t)reinterpret_cast<const uint16_t*>(wmeta)[gi * 16 + c16] << 16;
-          if (p.has_zero) z = (uint32_t)(reinterpret_cast<const uint64_t*>(wzero)[gi] >> (4 * c16)) & 0xF;
-        }
-        bm[set][ns] = sbits;
-        bz[set][ns] = z;
-      } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
-        uint32_t word = 0x7F7F7F7Fu;
-        if (ok) word = reinterpret_cast<const uint32_t*>(wmeta)[((int64_t)nts[ns] * p.kb4 + kb / 4) * 64 + lane];
-        bm[set][ns] = (word >> (8 * (kb & 3))) & 0xFF;
-      }
-    }
+    for (int ns = 0; ns < WN; ++ns) bq[set][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns], kb, lane);
   };
 
   f32x4_t acc[WM][WN];
@@ -279,27 +669,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int st, int buf, auto set_c) {
+  auto compute = [&](int buf, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const int kb = kb_begin + st * WAVES_K + wk;
-    if (kb >= kb_end) return;
-    const uint8_t* abase = smem + buf * C::kStage + wk * C::kKbBytes;
-    if constexpr (Tr::kBf16Mfma) {
-      bf16x8_t deq[WN][4];
-      float sc[WN], off[WN];
+    const uint8_t* abase = smem + buf * C::kStage;
+    if constexpr (T::kBf16) {
+      bf16x8_t d[WN][4];
 #pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        if (FMT == F_INT) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) deq[ns][s] = int_dequant(bw[set][ns][0][s]);
-          sc[ns] = __uint_as_float(bm[set][ns]);
-          off[ns] = (float)(p.int_offset + (int)bz[set][ns]);
-        } else {
-          const float fs = e8m0_to_f32(bm[set][ns]);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) deq[ns][s] = mx_dequant(bw[set][ns][0][s], fs);
-        }
-      }
+      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bq[set][ns], d[ns]);
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
         const int r = ms * 16 + c16;
@@ -308,23 +684,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         for (int s = 0; s < 4; ++s)
           af[s] = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + (((4 * lg + s) ^ c16) * 16));
         if constexpr (FMT == F_INT) {
-          const f32x4_t rs = *reinterpret_cast<const f32x4_t*>(
-              smem + buf * C::kStage + C::kStageA + (wk * C::kTM + ms * 16 + 4 * lg) * 4);
+          const f32x4_t rs = *reinterpret_cast<const f32x4_t*>(abase + C::kStageA + (ms * 16 + 4 * lg) * 4);
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
-            f32x4_t t = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], deq[ns][s], t, 0, 0, 0);
+            const f32x4_t t = mfma_bf16_kblock(af, d[ns], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+            const float sc = __uint_as_float(bq[set][ns].meta);
+            const float off = (float)(p.int_offset + (int)bq[set][ns].zero);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              acc[ms][ns][i] = __builtin_fmaf(sc[ns], __builtin_fmaf(-off[ns], rs[i], t[i]), acc[ms][ns][i]);
+              acc[ms][ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ms][ns][i]);
           }
         } else {
 #pragma unroll
-          for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], deq[ns][s], acc[ms][ns], 0, 0, 0);
+          for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_bf16_kblock(af, d[ns], acc[ms][ns]);
         }
       }
     } else {
@@ -339,241 +711,249 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
         a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
         int sa = 127;
         if (FMT == F_MXFP4_MXFP8)
-          sa = (int)((reinterpret_cast<const uint32_t*>(smem + buf * C::kStage + C::kStageA + C::kStageRs)
-                          [wk * C::kTM + r] >> (8 * lg)) & 0xFF);
+          sa = (int)((reinterpret_cast<const uint32_t*>(abase + C::kStageA)[r] >> (8 * lg)) & 0xFF);
 #pragma unroll
-        for (int ns = 0; ns < WN; ++ns) {
-          i32x8_t b8;
-          if (FMT == F_FP8) {
-            b8[0] = bw[set][ns][0][0]; b8[1] = bw[set][ns][0][1]; b8[2] = bw[set][ns][0][2]; b8[3] = bw[set][ns][0][3];
-            b8[4] = bw[set][ns][Tr::kBWords - 1][0]; b8[5] = bw[set][ns][Tr::kBWords - 1][1];
-            b8[6] = bw[set][ns][Tr::kBWords - 1][2]; b8[7] = bw[set][ns][Tr::kBWords - 1][3];
-            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[ms][ns], 0, 0, 0, 127, 0, 127);
-          } else {
-            b8[0] = bw[set][ns][0][0]; b8[1] = bw[set][ns][0][1]; b8[2] = bw[set][ns][0][2]; b8[3] = bw[set][ns][0][3];
-            b8[4] = 0; b8[5] = 0; b8[6] = 0; b8[7] = 0;
-            acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[ms][ns], 0, 4, 0, sa, 0,
-                                                                           (int)bm[set][ns]);
-          }
-        }
+        for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bq[set][ns], acc[ms][ns]);
       }
     }
   };
 
-  // ---- main loop: A double-buffered in LDS, B double-buffered in registers --
-  if (n_stages > 0) {
-    load_a(0);
-    load_b(0, I0{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  // Prefetches are unconditional (a conditional load is waited on where the
+  // branch rejoins); past the last K-block they re-read it (L2 hit, unused).
+  if (nkb > 0) {
+    const int kb_last = kb_begin + nkb - 1;
+    load_a(kb_begin);
+    load_bs(kb_begin, I0{});
     store_a(0);
     __syncthreads();
-    for (int st = 0; st < n_stages; st += 2) {
-      const bool n1 = st + 1 < n_stages;
-      if (n1) {
-        load_a(st + 1);
-        load_b(st + 1, I1{});
-      }
-      compute(st, 0, I0{});
-      if (n1) store_a(1);
+    for (int j = 0; j < nkb; j += 2) {
+      const int k1 = kb_begin + j + 1 <= kb_last ? kb_begin + j + 1 : kb_last;
+      load_a(k1);
+      load_bs(k1, I1{});
+      compute(0, I0{});
+      store_a(1);
       __syncthreads();
-      if (!n1) break;
-      const bool n2 = st + 2 < n_stages;
-      if (n2) {
-        load_a(st + 2);
-        load_b(st + 2, I0{});
-      }
-      compute(st + 1, 1, I1{});
-      if (n2) store_a(0);
+      if (j + 1 >= nkb) break;
+      const int k2 = kb_begin + j + 2 <= kb_last ? kb_begin + j + 2 : kb_last;
+      load_a(k2);
+      load_bs(k2, I0{});
+      compute(1, I1{});
+      store_a(0);
       __syncthreads();
     }
   }
 
-  // ---- in-workgroup split-K: waves wk > 0 hand their sums to wk == 0 -------
-  if constexpr (WAVES_K > 1) {
-    float* red = reinterpret_cast<float*>(smem);
-    if (wk > 0) {
-      float* dst = red + ((wk - 1) * WAVES_N + wn) * C::kAccPerWave;
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[((ms * WN + ns) * 4 + i) * 64 + lane] = acc[ms][ns][i];
-    }
-    __syncthreads();
-    if (wk == 0) {
-      for (int q = 1; q < WAVES_K; ++q) {
-        const float* src = red + ((q - 1) * WAVES_N + wn) * C::kAccPerWave;
-#pragma unroll
-        for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[ms][ns][i] += src[((ms * WN + ns) * 4 + i) * 64 + lane];
-      }
-    }
-  }
-
-  // ---- cross-workgroup split-K: fp32 partials, last arrival reduces ---------
   if (p.split_k > 1) {
-    float* part = p.partials + (tile_id * p.split_k * WAVES_N) * (int64_t)C::kAccPerWave;
-    if (wk == 0) {
-      float* dst = part + ((int64_t)split * WAVES_N + wn) * C::kAccPerWave;
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[((ms * WN + ns) * 4 + i) * 64 + lane] = acc[ms][ns][i];
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&p.counters[tile_id], 1);
-      s_last = (prev == p.split_k - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (wk == 0) {
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int q = 0; q < p.split_k; ++q) {
-        const float* src = part + ((int64_t)q * WAVES_N + wn) * C::kAccPerWave;
-#pragma unroll
-        for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[ms][ns][i] += __builtin_nontemporal_load(&src[((ms * WN + ns) * 4 + i) * 64 + lane]);
-      }
-    }
-    if (tid == 0) p.counters[tile_id] = 0;  // ready for the next call
-  }
-
-  if (wk != 0) return;
-
-  // ---- epilogues -------------------------------------------------------------
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
-    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const int64_t ncols = C::kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) {
-      const int64_t col = (int64_t)nts[ns] * 16 + c16;
-      if (col >= p.n) continue;
-      float cs = gs;
-      if (FMT == F_FP8) cs *= reinterpret_cast<const float*>(wmeta)[col];
-      const float bias = (EPI == EPI_BF16 && p.bias) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
+      if (!ntv[ns]) continue;
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = row0 + ms * 16 + 4 * lg + i;
-          if (row >= p.m) continue;
-          float v = acc[ms][ns][i] * cs;
-          if (FMT == F_FP8) v *= reinterpret_cast<const float*>(p.a_scale)[row];
-          v += bias;
-          if (EPI == EPI_SCATTER) {
-            const int32_t f = p.sorted[row];
-            if (f >= p.sentinel) continue;
-            out[(int64_t)f * p.ldo + col] = (uint16_t)f32_to_bf16_bits(v);
-          } else {
-            out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(v);
-          }
-        }
+        store_partial(p, split, row0 + ms * 16, (int64_t)nts[ns] * 16 + c16, ncols, acc[ms][ns], lg);
     }
-  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-    uint16_t* out = static_cast<uint16_t*>(p.out);
+    return;
+  }
 #pragma unroll
-    for (int j = 0; j < WN / 2; ++j) {
-      const int64_t col = (int64_t)nts[j] * 16 + c16;
-      if (col >= p.n) continue;
+  for (int ms = 0; ms < WM; ++ms) {
+    const int64_t rb = row0 + ms * 16;
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
 #pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
+      for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, rb, (int64_t)nts[ns] * 16 + c16, acc[ms][ns], lg);
+    } else if constexpr (EPI == EPI_SWIGLU_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = row0 + ms * 16 + 4 * lg + i;
-          const float g = acc[ms][j][i] * gs, u = acc[ms][j + WN / 2][i] * gs;
-          out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
-        }
-    }
-  } else {  // EPI_SWIGLU_MXFP8: 32-column blocks = gate sub-tile pairs
-    uint8_t* outq = static_cast<uint8_t*>(p.out);
-    uint8_t* outs = static_cast<uint8_t*>(p.out_scale);
+      for (int j = 0; j < WN / 2; ++j)
+        store_swiglu_bf16(p, gs, rb, (int64_t)nts[j] * 16 + c16, acc[ms][j], acc[ms][j + WN / 2], lg);
+    } else {
 #pragma unroll
-    for (int jj = 0; jj < WN / 4; ++jj) {
-      const int j0 = 2 * jj, j1 = 2 * jj + 1;
-      const int64_t col0 = (int64_t)nts[j0] * 16 + c16, col1 = (int64_t)nts[j1] * 16 + c16;
-      const bool ok = nts[j0] * 16 < p.n;  // whole 32-block valid (I % 32 == 0)
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t row = row0 + ms * 16 + 4 * lg + i;
-          const float a0 = silu_f32(acc[ms][j0][i] * gs) * (acc[ms][j0 + WN / 2][i] * gs);
-          const float a1 = silu_f32(acc[ms][j1][i] * gs) * (acc[ms][j1 + WN / 2][i] * gs);
-          const float amax = row16_max(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
-          const int e = mx_scale_code(amax);
-          const float inv = mx_inv_scale(e);
-          const uint32_t q = f32x2_to_e4m3x2(a0 * inv, a1 * inv);
-          if (ok) {
-            outq[row * p.ldo + col0] = (uint8_t)(q & 0xFF);
-            outq[row * p.ldo + col1] = (uint8_t)(q >> 8);
-            if (c16 == 0) outs[row * (p.ldo / 32) + col0 / 32] = (uint8_t)e;
-          }
-        }
+      for (int jj = 0; jj < WN / 4; ++jj)
+        store_swiglu_mxfp8(p, gs, rb, (int64_t)nts[2 * jj] * 16 + c16, acc[ms][2 * jj], acc[ms][2 * jj + WN / 2],
+                           acc[ms][2 * jj + 1], acc[ms][2 * jj + 1 + WN / 2], lg, c16);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Instances.  The selector only returns keys listed here.
+// Split-K reduce + epilogue: one thread per (row, 32-column block) for the
+// MXFP8 epilogue, per (row, 8 columns) otherwise.  Partials are summed in
+// split order.
+
+template <int FMT, int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p, int block_m) {
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  constexpr int kCols = (EPI == EPI_SWIGLU_MXFP8) ? 32 : 8;
+  const int64_t ncols = kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
+  const int64_t outc = p.n;
+  const int64_t cpr = (outc + kCols - 1) / kCols;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= p.m * cpr) return;
+  const int64_t row = id / cpr;
+  const int64_t c0 = (id % cpr) * kCols;
+  int expert = 0;
+  if (p.sorted) {
+    if (p.sorted[row] >= p.sentinel) return;
+    expert = p.block_expert[row / block_m];
+  }
+  const float gs = p.gscale[expert];
+  const uint8_t* wmeta = p.wscale + (int64_t)expert * p.scales_per_expert;
+  float v[kCols], u[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) v[i] = u[i] = 0.0f;
+  for (int s = 0; s < p.split_k; ++s) {
+    const float* src = p.partials + ((int64_t)s * p.m + row) * ncols;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+      if (c0 + i < outc) {
+        v[i] += src[c0 + i];
+        if (kSwiglu) u[i] += src[c0 + i + p.n];
+      }
+    }
+  }
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const int64_t orow = (EPI == EPI_SCATTER) ? (int64_t)p.sorted[row] : row;
+    const float rsc = (FMT == F_FP8) ? reinterpret_cast<const float*>(p.a_scale)[row] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kCols; ++i) {
+      const int64_t col = c0 + i;
+      if (col >= outc) continue;
+      float x = v[i] * col_scale<FMT>(wmeta, col, gs) * rsc;
+      if (EPI == EPI_BF16 && p.bias) x += bf16_bits_to_f32(p.bias[col]);
+      out[orow * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < kCols; ++i)
+      if (c0 + i < outc) out[row * p.ldo + c0 + i] = (uint16_t)f32_to_bf16_bits(silu_f32(v[i] * gs) * (u[i] * gs));
+  } else {
+    float a[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      a[i] = silu_f32(v[i] * gs) * (u[i] * gs);
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(a[i]));
+    }
+    const int e = mx_scale_code(amax);
+    const float inv = mx_inv_scale(e);
+    uint8_t* outq = static_cast<uint8_t*>(p.out) + row * p.ldo + c0;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      const uint32_t q = f32x2_to_e4m3x2(a[i] * inv, a[i + 1] * inv);
+      outq[i] = (uint8_t)(q & 0xFF);
+      outq[i + 1] = (uint8_t)(q >> 8);
+    }
+    static_cast<uint8_t*>(p.out_scale)[row * (p.ldo / 32) + c0 / 32] = (uint8_t)e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row sums of bf16 activations per K-block (INT prefill correction term).
+
+__global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t m,
+                                                     int kb_count, float* __restrict__ out) {
+  // one DPP row of 16 lanes per (row, K-block): each lane sums 8 values
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t item = gid >> 4;
+  const int c = (int)(gid & 15);
+  const bool ok = item < m * kb_count;
+  float s = 0.0f;
+  if (ok) {
+    const int64_t row = item / kb_count, kb = item % kb_count;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + row * lda + kb * 128 + c * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += bf16_bits_to_f32(v[q] & 0xFFFF) + bf16_bits_to_f32(v[q] >> 16);
+  }
+  s = row16_sum(s);
+  if (ok && c == 0) out[item] = s;
+}
+
+hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, float* out, void* stream) {
+  if (m == 0) return HUM_OK;
+  const int64_t threads = m * kb_count * 16;
+  rowsum_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(a), lda, m, kb_count, out);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "rowsum launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Instances.
 
 typedef void (*gemm_fn)(const GemmParams);
+typedef void (*reduce_fn)(const GemmParams, int);
 
 struct Instance {
   KernelKey key;
   gemm_fn fn;
+  int threads;
 };
 
-#define HUM_INST(F, WM, WN, WVN, WVK, AM, EP) \
-  {{F, WM, WN, WVN, WVK, AM, EP}, gemm_kernel<F, WM, WN, WVN, WVK, AM, EP>}
+#define HUM_STREAM(F, WN, KW, PF, AM, EP) \
+  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * KW}
+#define HUM_TILE(F, WM, WN, AM, EP) \
+  {{F, KIND_TILE, WM, WN, 4, 1, AM, EP}, tile_kernel<F, WM, WN, AM, EP>, 256}
 
-#define HUM_DENSE_SET(F)                                 \
-  HUM_INST(F, 1, 1, 1, 4, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 1, 2, 2, 2, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 1, 4, 4, 1, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 2, 2, 2, 2, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 4, 2, 2, 2, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 4, 4, 4, 1, A_DIRECT, EPI_BF16),           \
-  HUM_INST(F, 8, 4, 4, 1, A_DIRECT, EPI_BF16)
+#define HUM_DENSE_SET(F)                                   \
+  HUM_STREAM(F, 1, 8, 8, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 2, 8, 4, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 1, 4, 8, A_DIRECT, EPI_BF16),              \
+  HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 2, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 4, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 4, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 8, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16)
 
-#define HUM_MOE_SET(F, EPI_UP)                           \
-  HUM_INST(F, 1, 4, 1, 4, A_GATHER, EPI_UP),             \
-  HUM_INST(F, 1, 4, 2, 2, A_GATHER, EPI_UP),             \
-  HUM_INST(F, 2, 4, 2, 2, A_GATHER, EPI_UP),             \
-  HUM_INST(F, 4, 4, 4, 1, A_GATHER, EPI_UP),             \
-  HUM_INST(F, 8, 4, 4, 1, A_GATHER, EPI_UP),             \
-  HUM_INST(F, 1, 4, 1, 4, A_DIRECT, EPI_SCATTER),        \
-  HUM_INST(F, 1, 4, 2, 2, A_DIRECT, EPI_SCATTER),        \
-  HUM_INST(F, 2, 4, 2, 2, A_DIRECT, EPI_SCATTER),        \
-  HUM_INST(F, 4, 4, 4, 1, A_DIRECT, EPI_SCATTER),        \
-  HUM_INST(F, 8, 4, 4, 1, A_DIRECT, EPI_SCATTER)
+#define HUM_MOE_SET(F, EPI_UP)                             \
+  HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
+  HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
+  HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 8, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 1, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 2, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 4, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 8, 4, A_DIRECT, EPI_SCATTER)
 
 static const Instance kInstances[] = {
     HUM_DENSE_SET(F_INT),
     HUM_DENSE_SET(F_FP8),
     HUM_DENSE_SET(F_MXFP4_BF16),
+    HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
+    HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_MOE_SET(F_MXFP4_BF16, EPI_SWIGLU_BF16),
     HUM_MOE_SET(F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8),
 };
 
+struct ReduceInstance {
+  int fmt, epi;
+  reduce_fn fn;
+};
+
+static const ReduceInstance kReduces[] = {
+    {F_INT, EPI_BF16, splitk_reduce_kernel<F_INT, EPI_BF16>},
+    {F_FP8, EPI_BF16, splitk_reduce_kernel<F_FP8, EPI_BF16>},
+    {F_MXFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_BF16>},
+    {F_MXFP4_BF16, EPI_SWIGLU_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SWIGLU_BF16>},
+    {F_MXFP4_BF16, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SCATTER>},
+    {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
+    {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
+};
+
+static bool g_big_lds[sizeof(kInstances) / sizeof(kInstances[0])];
+
 static const Instance* find_instance(const KernelKey& k) {
   for (const Instance& in : kInstances) {
     const KernelKey& q = in.key;
-    if (q.fmt == k.fmt && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n && q.waves_k == k.waves_k &&
-        q.amode == k.amode && q.epi == k.epi)
+    if (q.fmt == k.fmt && q.kind == k.kind && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n &&
+        q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi)
       return &in;
   }
   return nullptr;
@@ -581,17 +961,48 @@ static const Instance* find_instance(const KernelKey& k) {
 
 bool gemm_instance_exists(const KernelKey& key) { return find_instance(key) != nullptr; }
 
-hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, void* stream) {
+hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, int block_m, void* stream) {
   const Instance* in = find_instance(key);
   if (!in)
-    return set_error(HUM_ERR_UNSUPPORTED, "no GEMM instance fmt=%d wm=%d wn=%d waves_n=%d waves_k=%d amode=%d epi=%d",
-                     key.fmt, key.wm, key.wn, key.waves_n, key.waves_k, key.amode, key.epi);
+    return set_error(HUM_ERR_UNSUPPORTED,
+                     "no GEMM instance fmt=%d kind=%d wm=%d wn=%d waves_n=%d waves_k=%d amode=%d epi=%d", key.fmt,
+                     key.kind, key.wm, key.wn, key.waves_n, key.waves_k, key.amode, key.epi);
   const int64_t grid = m_tiles * (int64_t)p.n_tiles * p.split_k;
   if (grid <= 0) return HUM_OK;
   if (grid > 0x7FFFFFFF) return set_error(HUM_ERR_UNSUPPORTED, "grid too large");
-  hipLaunchKernelGGL(in->fn, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  size_t dyn = 0;
+  if (key.kind == KIND_STREAM) {
+    const int64_t stage = stream_lds_footprint(key.fmt, p.stream_rows, p.kb_per_split);
+    const int64_t red = (int64_t)(key.waves_k - 1) * key.wn * 64 * 16;
+    dyn = (size_t)(stage > red ? stage : red);
+    if ((int64_t)dyn > kStreamLdsMax) return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per split too long for LDS");
+    if (dyn > 64 * 1024) {
+      const int idx = (int)(in - kInstances);
+      if (!g_big_lds[idx]) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(in->fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)kStreamLdsMax) != hipSuccess)
+          return set_error(HUM_ERR_HIP, "cannot raise the LDS limit of the stream kernel");
+        g_big_lds[idx] = true;
+      }
+    }
+  }
+  hipLaunchKernelGGL(in->fn, dim3((unsigned)grid), dim3(in->threads), dyn, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "gemm launch: %s", hipGetErrorString(err));
+  if (p.split_k > 1) {
+    const ReduceInstance* r = nullptr;
+    for (const ReduceInstance& q : kReduces)
+      if (q.fmt == key.fmt && q.epi == key.epi) r = &q;
+    if (!r) return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for fmt=%d epi=%d", key.fmt, key.epi);
+    const int64_t cols = (key.epi == EPI_SWIGLU_MXFP8) ? 32 : 8;
+    const int64_t threads = p.m * ((p.n + cols - 1) / cols);
+    if (threads > 0) {
+      hipLaunchKernelGGL(r->fn, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, block_m);
+      err = hipGetLastError();
+      if (err != hipSuccess) return set_error(HUM_ERR_HIP, "split-K reduce launch: %s", hipGetErrorString(err));
+    }
+  }
   return HUM_OK;
 }
 

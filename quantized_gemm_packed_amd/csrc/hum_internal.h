@@ -94,6 +94,9 @@ struct GemmParams {
   int64_t lda;        // elements (bytes for fp8)
   const void* a_scale;
   int64_t a_scale_ld; // MXFP8: scale bytes per row
+  const float* a_rowsum;  // INT tile kernel: activation sums per (row, K-block)
+  int64_t a_bytes;        // bytes of the activation buffer (< 2 GiB for buffer loads)
+  int64_t a_scale_bytes;  // bytes of the MXFP8 activation scale buffer
   int64_t m;          // rows (dense) / padded sorted length (MoE)
   // MoE
   const int32_t* sorted;
@@ -105,21 +108,46 @@ struct GemmParams {
   int64_t ldo;        // elements
   void* out_scale;    // MXFP8 epilogue scales, [rows][ldo/32]
   const uint16_t* bias;
-  float* partials;
-  int32_t* counters;
+  float* partials;    // split-K partials, [split][m][columns] fp32
   int split_k;
   int kb_per_split;
   int n_tiles;
+  int stream_rows;    // stream kernel: most valid rows of one 16-row tile
 };
 
+enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1 };
+
+// The decode (stream) kernel stages the activation rows of its K range in
+// LDS (rows x K-blocks x 256 B for bf16, 128 B (+4 B of MX scales) for
+// FP8).  Dense launches keep it within kStreamLdsDense so that several
+// workgroups share a CU; a MoE launch may take up to kStreamLdsMax.
+constexpr int64_t kStreamLdsDense = 64 * 1024;
+constexpr int64_t kStreamLdsMax = 159 * 1024;
+constexpr int64_t stream_lds_per_kb(int fmt, int rows) {
+  return (int64_t)rows * ((fmt == F_INT || fmt == F_MXFP4_BF16) ? 256 : (fmt == F_MXFP4_MXFP8 ? 132 : 128));
+}
+// Exact LDS footprint of the stream kernel's staging for at most `rows`
+// rows and `kb` K-blocks: 16-byte activation slots and 4-byte MX scale
+// slots, each rounded up to whole 64-lane LDS-DMA instructions (every lane
+// of an instruction writes its slot).
+constexpr int64_t stream_lds_footprint(int fmt, int rows, int64_t kb) {
+  const int64_t cpr = (fmt == F_INT || fmt == F_MXFP4_BF16) ? 16 : 8;
+  const int64_t a = ((rows * cpr * kb + 63) / 64) * 64 * 16;
+  const int64_t sc = (fmt == F_MXFP4_MXFP8) ? ((rows * kb + 63) / 64) * 64 * 4 : 0;
+  return a + sc;
+}
+
 struct KernelKey {
-  int fmt, wm, wn, waves_n, waves_k, amode, epi;
+  int fmt, kind, wm, wn, waves_n, waves_k, amode, epi;
 };
 
 // Launches the GEMM kernel instance matching `key` (HUM_ERR_UNSUPPORTED if
-// no such instance is compiled).  Grid = m_tiles * n_tiles * split_k.
-hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles,
+// no such instance is compiled), followed by the split-K reduce kernel when
+// p.split_k > 1.  Grid = m_tiles * n_tiles * split_k.
+hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, int block_m,
                        void* stream);
 bool gemm_instance_exists(const KernelKey& key);
+hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, float* out,
+                         void* stream);
 
 }  // namespace hum

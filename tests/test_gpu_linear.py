@@ -17,15 +17,24 @@ from gpu_util import assert_bf16_exact, assert_tol, descs, dev, prepare
 
 pytestmark = pytest.mark.gpu
 
-DENSE_TILES = [(1, 1, 1, 4), (1, 2, 2, 2), (1, 4, 4, 1), (2, 2, 2, 2), (4, 2, 2, 2), (4, 4, 4, 1), (8, 4, 4, 1)]
+# (kind, wave_m, wave_n, waves_n, waves_k): every compiled dense instance
+STREAM_TILES = [(1, 1, 1, 1, 8), (1, 1, 2, 1, 8), (1, 1, 4, 1, 8), (1, 1, 1, 1, 4)]
+TILE_TILES = [(0, 1, 4, 4, 1), (0, 2, 2, 4, 1), (0, 2, 4, 4, 1), (0, 4, 2, 4, 1), (0, 4, 4, 4, 1),
+              (0, 8, 2, 4, 1), (0, 8, 4, 4, 1)]
+DENSE_TILES = STREAM_TILES + TILE_TILES
 
 
 def cfg(t, split):
     c = hum.TileConfig()
-    c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
     c.split_k = split
-    c.block_m = 16 * t[0]
+    c.block_m = 16 * t[1]
     return c
+
+
+def rows_for(tile, m):
+    """The stream kernel takes at most 16 rows."""
+    return min(m, 13) if tile[0] == 1 else m
 
 
 def _int_exact_case(seed, wd, m, n, k, gs, zero):
@@ -40,7 +49,7 @@ def _int_exact_case(seed, wd, m, n, k, gs, zero):
 @pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 @pytest.mark.parametrize("split", [1, 2, 4])
 def test_int_exact_every_tile(tile, split):
-    m, n, k, gs = 37, 640, 1024, 128
+    m, n, k, gs = rows_for(tile, 37), 640, 2048, 128
     w, xb = _int_exact_case(31, "uint4", m, n, k, gs, True)
     hd, od = descs("uint4", "group", gs, "bf16", 1, n, k, zero=True)
     print(f"case uint4 exact tile={tile} split={split}", flush=True)
@@ -53,7 +62,7 @@ def test_int_exact_every_tile(tile, split):
 
 @pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_int4_sym_exact_every_tile(tile):
-    m, n, k, gs = 5, 200, 512, 256
+    m, n, k, gs = 5, 200, 1024, 256
     w, xb = _int_exact_case(32, "int4", m, n, k, gs, False)
     hd, od = descs("int4", "group", gs, "bf16", 1, n, k)
     packed = prepare(hd, w, "bf16")
@@ -65,7 +74,7 @@ def test_int4_sym_exact_every_tile(tile):
 
 @pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_mxfp4_bf16_exact_every_tile(tile):
-    m, n, k = 9, 96, 512
+    m, n, k = 9, 96, 1024
     g = synth.rng(33)
     w = synth.quant_weights(33, "e2m1", "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
     xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
@@ -102,7 +111,7 @@ def test_uint4_zp_random_vs_oracle(m):
 
 @pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_fp8_w8a8_every_tile(tile):
-    m, n, k = 21, 320, 1024
+    m, n, k = rows_for(tile, 21), 320, 1024
     case = synth.dense_w8a8(synth.seed_for(3, 7), m, n, k)
     hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
     packed = prepare(hd, case, "f32")

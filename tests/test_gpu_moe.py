@@ -12,14 +12,15 @@ from gpu_util import assert_tol, descs, dev, prepare
 
 pytestmark = pytest.mark.gpu
 
-MOE_TILES = [(1, 4, 1, 4), (1, 4, 2, 2), (2, 4, 2, 2), (4, 4, 4, 1), (8, 4, 4, 1)]
+# (kind, wave_m, wave_n, waves_n, waves_k): every compiled MoE instance
+MOE_TILES = [(1, 1, 4, 1, 8), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 4, 4, 4, 1), (0, 8, 4, 4, 1)]
 
 
 def cfg(t, split=1):
     c = hum.TileConfig()
-    c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
     c.split_k = split
-    c.block_m = 16 * t[0]
+    c.block_m = 16 * t[1]
     return c
 
 
@@ -83,15 +84,27 @@ def test_moe_layer_every_tile(act, tile, t):
 
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8"])
-def test_moe_split_k(act):
-    e, h, inter, k, t = 4, 512, 256, 2, 3
+@pytest.mark.parametrize("tile", [(1, 1, 4, 1, 8), (0, 2, 4, 4, 1)], ids=["stream", "tile"])
+def test_moe_split_k(act, tile):
+    e, h, inter, k, t = 4, 2048, 256, 2, 3
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(710, e, h, inter, act)
     ids, wts = synth.routing(711, t, e, k)
     xb = synth.bf16_normal(synth.rng(712), (t, h))
-    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg((1, 4, 1, 4), split=2))
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg(tile, split=2))
     torch.cuda.synchronize()
     ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
     assert_tol(out, ref, f"split act={act}")
+
+
+def test_moe_stream_wave_n2_bf16():
+    e, h, inter, k, t = 8, 256, 128, 2, 9
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(705, e, h, inter, "bf16")
+    ids, wts = synth.routing(706, t, e, k)
+    xb = synth.bf16_normal(synth.rng(707), (t, h))
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg((1, 1, 2, 1, 8)))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, "bf16")
+    assert_tol(out, ref, "stream wave_n=2")
 
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8"])
