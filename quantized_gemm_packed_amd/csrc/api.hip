@@ -556,7 +556,10 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   p.split_k = c.split_k;
   p.kb_per_split = kb_per_split(L13.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
-  p.stream_rows = 16;
+  // upper bound of the valid rows of one expert block (any routing, also
+  // repeated ids within a token): the LDS staging is sized for it
+  const int64_t slots = t * topk;
+  p.stream_rows = (int)(slots < 16 ? slots : 16);
   p.a_bytes = t * h * (mx ? 1 : 2);
   p.a_scale_bytes = mx ? t * (h / 32) : 0;
   st = launch_gemm(kup, p, w.nblocks, bm, stream);
@@ -581,7 +584,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.split_k = c.split_k;
   q.kb_per_split = kb_per_split(L2.kb, c);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
-  q.stream_rows = 16;
+  q.stream_rows = p.stream_rows;  // valid (non-padding) rows of a block
   q.a_bytes = w.cap * inter * (mx ? 1 : 2);
   q.a_scale_bytes = mx ? w.cap * (inter / 32) : 0;
   st = launch_gemm(kdn, q, w.nblocks, bm, stream);

@@ -325,7 +325,8 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
       const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
       if (f < p.sentinel) src = f / p.topk;
     } else if (row < p.m) {
-      src = row;
+      // grouped rows in sorted order: padding slots (sentinel) are skipped
+      src = (p.sorted && p.sorted[row] >= p.sentinel) ? -1 : row;
     }
     s_src[tid] = (int32_t)src;
   }
@@ -899,8 +900,11 @@ struct Instance {
 
 #define HUM_DENSE_SET(F)                                   \
   HUM_STREAM(F, 1, 8, 8, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 1, 16, 4, A_DIRECT, EPI_BF16),             \
   HUM_STREAM(F, 2, 8, 4, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 2, 16, 4, A_DIRECT, EPI_BF16),             \
   HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 4, 16, 2, A_DIRECT, EPI_BF16),             \
   HUM_STREAM(F, 1, 4, 8, A_DIRECT, EPI_BF16),              \
   HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
   HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
@@ -913,6 +917,8 @@ struct Instance {
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
   HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
+  HUM_STREAM(F, 4, 16, 2, A_GATHER, EPI_UP),               \
+  HUM_STREAM(F, 4, 16, 2, A_DIRECT, EPI_SCATTER),          \
   HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
   HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
   HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
@@ -928,6 +934,8 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_MXFP4_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
+    HUM_STREAM(F_MXFP4_BF16, 2, 16, 4, A_GATHER, EPI_SWIGLU_BF16),
+    HUM_STREAM(F_MXFP4_BF16, 2, 16, 4, A_DIRECT, EPI_SCATTER),
     HUM_MOE_SET(F_MXFP4_BF16, EPI_SWIGLU_BF16),
     HUM_MOE_SET(F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8),
 };

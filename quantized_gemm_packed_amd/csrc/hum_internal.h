@@ -121,7 +121,7 @@ enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1 };
 // LDS (rows x K-blocks x 256 B for bf16, 128 B (+4 B of MX scales) for
 // FP8).  Dense launches keep it within kStreamLdsDense so that several
 // workgroups share a CU; a MoE launch may take up to kStreamLdsMax.
-constexpr int64_t kStreamLdsDense = 64 * 1024;
+constexpr int64_t kStreamLdsDense = 128 * 1024;
 constexpr int64_t kStreamLdsMax = 159 * 1024;
 constexpr int64_t stream_lds_per_kb(int fmt, int rows) {
   return (int64_t)rows * ((fmt == F_INT || fmt == F_MXFP4_BF16) ? 256 : (fmt == F_MXFP4_MXFP8 ? 132 : 128));
