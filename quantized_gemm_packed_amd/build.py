@@ -53,6 +53,12 @@ def build_library(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
+    # every symbol of the library's own namespace must be defined (a kernel
+    # whose host stub the compiler dropped shows up here, not at load time)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "3hum" in ln]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"{tmp}: undefined library symbols: {missing[:5]}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)

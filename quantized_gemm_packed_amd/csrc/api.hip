@@ -36,7 +36,9 @@ hum_status check_desc(const hum_weight_desc* d) {
   if (d->num_experts < 1) return set_error(HUM_ERR_INVALID_ARG, "num_experts must be >= 1");
   if (d->n < 1) return set_error(HUM_ERR_INVALID_ARG, "n must be >= 1");
   if (d->k < 128 || d->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "k must be a positive multiple of 128 (got %lld)", (long long)d->k);
-  if (d->n > (int64_t)1 << 30 || d->k > (int64_t)1 << 30) return set_error(HUM_ERR_UNSUPPORTED, "n/k too large");
+  // k < 2^21: a sub-tile's weight stripe stays far below the 2 GiB reach of
+  // a buffer resource, and K-block / group indices stay exact in fp32
+  if (d->n > (int64_t)1 << 30 || d->k > (int64_t)1 << 21) return set_error(HUM_ERR_UNSUPPORTED, "n/k too large");
   if (d->has_zero_point != 0 && d->has_zero_point != 1) return set_error(HUM_ERR_INVALID_ARG, "has_zero_point must be 0/1");
   if (d->has_global_scale != 0 && d->has_global_scale != 1) return set_error(HUM_ERR_INVALID_ARG, "has_global_scale must be 0/1");
   if (d->scale_gran < HUM_SCALE_TENSOR || d->scale_gran > HUM_SCALE_GROUP) return set_error(HUM_ERR_INVALID_ARG, "bad scale_gran");
@@ -118,7 +120,7 @@ static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
 
 static bool cfg_sane(const hum_tile_config& c) {
   if (c.split_k < 1 || c.split_k > 64 || c.wave_m < 1 || c.wave_n < 1) return false;
-  if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 16;
+  if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 15;
   if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1;
   return false;
 }
@@ -138,6 +140,12 @@ static int pick_split(int64_t wgs, int waves_per_wg, int64_t kb, int k_waves, in
   return s;
 }
 
+// K-blocks per split: whole stages (waves_k K-blocks per wave-step).
+static int kb_per_split(int64_t kb, const hum_tile_config& c) {
+  const int64_t unit = c.kind == HUM_KERNEL_STREAM ? c.waves_k : 1;
+  return (int)(cdiv(cdiv(kb, c.split_k), unit) * unit);
+}
+
 static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
@@ -152,9 +160,22 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     c.waves_k = 8;
     const int64_t wgs = cdiv(nt, c.wave_n);
     c.split_k = pick_split(wgs, 8, kb, 8, 2, 16 * kCUs);
-    // activation rows of one split must fit the dense LDS budget
-    while (c.split_k < 64 && stream_lds_per_kb(fmt_of(d), (int)m) * cdiv(cdiv(kb, c.split_k), 8) * 8 > kStreamLdsDense)
-      c.split_k *= 2;
+    // the LDS plan of one split must fit the dense LDS budget
+    Layout L;
+    compute_layout(d, &L);
+    auto lds = [&](int split) {
+      hum_tile_config t = c;
+      t.split_k = split;
+      return stream_lds_plan(fmt_of(d), (int)m, kb_per_split(kb, t), c.wave_n, L.kb_per_group, L.scale_f32, L.ng,
+                             L.kb4).total;
+    };
+    auto fits = [&](int split) {
+      hum_tile_config t = c;
+      t.split_k = split;
+      return lds(split) <= kStreamLdsDense &&
+             stream_self_stage_fits(fmt_of(d), (int)m, kb_per_split(kb, t), c.waves_k, L.kb_per_group, L.scale_f32);
+    };
+    while (c.split_k < 64 && !fits(c.split_k)) c.split_k *= 2;
   } else {
     c.kind = HUM_KERNEL_TILE;
     c.waves_n = 4;
@@ -315,6 +336,7 @@ static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const La
   p.kb_count = (int)L.kb;
   p.ng = (int)L.ng;
   p.kb_per_group = L.kb_per_group;
+  p.inv_kbg = 1.0f / (float)L.kb_per_group;
   p.kb4 = (int)L.kb4;
   p.scale_f32 = L.scale_f32;
   p.int_offset = (d->weight_dtype == HUM_INT4) ? 136 : 128;
@@ -324,11 +346,6 @@ static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const La
   p.a_rowsum = nullptr;
 }
 
-// K-blocks per split: whole stages (waves_k K-blocks per wave-step).
-static int kb_per_split(int64_t kb, const hum_tile_config& c) {
-  const int64_t unit = c.kind == HUM_KERNEL_STREAM ? c.waves_k : 1;
-  return (int)(cdiv(cdiv(kb, c.split_k), unit) * unit);
-}
 
 hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a,
                          const void* a_scales, const void* bias, void* out, void* workspace, size_t ws_bytes,

@@ -58,8 +58,10 @@ struct Tr {
 template <int FMT>
 struct BFrag {
   u32x4_t w[Tr<FMT>::kBWords];
-  uint32_t meta;  // INT: f32 scale bits; MX: E8M0 code of this K-block
-  uint32_t zero;  // INT: zero point nibble
+  // raw metadata words as loaded (decoded where the fragment is used, so
+  // that no arithmetic waits on a load where it is issued)
+  uint32_t meta;  // INT: dword holding the column's scale; MX: E8M0 codes of 4 K-blocks
+  uint32_t zero;  // INT: dword holding the column's zero-point nibble
 };
 
 struct WPtrs {
@@ -68,48 +70,110 @@ struct WPtrs {
   const uint8_t* zero;
 };
 
-// Loads of one weight fragment.  Every load is unconditional -- an invalid
-// (sub-tile, K-block) reads block 0 and is zeroed by a select -- because a
-// load inside a divergent branch makes the compiler wait for all
-// outstanding loads when the branch rejoins, which would serialize the
-// prefetch ring.
+// Buffer resources over the weight stripe of one 16-column sub-tile (its
+// codes and metadata for the whole K).  A fragment outside the stripe -- a
+// K-block past the end of the wave's range, or a sub-tile past N (range 0)
+// -- is read at an offset beyond the range: the hardware returns zeros and
+// touches no memory.  So every weight load is unconditional (a load inside a
+// branch makes the compiler wait for all outstanding loads where the branch
+// rejoins, which would serialize the prefetch ring) and costs nothing when
+// unused.
+struct WStripe {
+  __amdgpu_buffer_rsrc_t codes, meta, zero;
+};
+
+constexpr uint32_t kOob = 0x80000000u;  // beyond every stripe (stripes are < 2 GiB)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int FMT>
-__device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WPtrs& w, int nt, bool ok, int kb,
-                                             int lane) {
-  BFrag<FMT> f;
-  const int ntc = ok ? nt : 0, kbc = ok ? kb : 0;
-  const int64_t blk = ((int64_t)ntc * p.kb_count + kbc) * 64 + lane;
-#pragma unroll
-  for (int i = 0; i < Tr<FMT>::kBWords; ++i) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(w.codes + blk * (16 * Tr<FMT>::kBWords) + 16 * i);
-    const u32x4_t z = {0, 0, 0, 0};
-    f.w[i] = ok ? v : z;
+__device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs& w, int nt, bool valid) {
+  constexpr int kCB = 16 * Tr<FMT>::kBWords;  // code bytes per lane per K-block
+  const int64_t ntc = valid ? nt : 0;
+  WStripe s;
+  const int64_t cb = (int64_t)p.kb_count * 64 * kCB;
+  s.codes = make_rsrc(w.codes + ntc * cb, valid ? cb : 0);
+  s.meta = s.codes;
+  s.zero = s.codes;
+  if (FMT == F_INT) {
+    const int64_t sb = (int64_t)p.ng * 16 * (p.scale_f32 ? 4 : 2);
+    s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
+    const int64_t zb = (int64_t)p.ng * 8;
+    s.zero = make_rsrc(w.zero + ntc * zb, (valid && p.has_zero) ? zb : 0);
+  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+    const int64_t sb = (int64_t)p.kb4 * 256;
+    s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
   }
+  return s;
+}
+
+// Loads of one weight fragment (K-block kb of the stripe; zeros when !ok).
+// META = false loads the codes only (the caller holds the metadata).
+template <int FMT, bool META = true>
+__device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe& s, bool ok, int kb, int lane) {
+  constexpr int kCB = 16 * Tr<FMT>::kBWords;
+  BFrag<FMT> f;
+  const uint32_t co = ok ? (uint32_t)(kb * 64 + lane) * kCB : kOob;
+#pragma unroll
+  for (int i = 0; i < Tr<FMT>::kBWords; ++i) f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(s.codes, co + 16 * i, 0, 0);
   f.meta = 0;
   f.zero = 0;
-  if (FMT == F_INT) {
+  if (META && FMT == F_INT) {
     const int c16 = lane & 15;
-    const int64_t gi = (int64_t)ntc * p.ng + kbc / p.kb_per_group;
+    // floor(kb / kb_per_group), exact in fp32: kb < 2^14, and the quotient
+    // of (kb + 1/2) sits at least 1/(2 kb_per_group) from an integer
+    const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
     // bf16 scales: the dword holding the pair of column c16; f32: its dword
-    const int64_t off = p.scale_f32 ? (gi * 16 + c16) * 4 : (gi * 16 + (c16 & ~1)) * 2;
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(w.meta + off);
-    const uint32_t bits = p.scale_f32 ? sw : ((c16 & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
-    const uint64_t zw = *reinterpret_cast<const uint64_t*>(w.zero + gi * 8);
-    f.meta = ok ? bits : 0u;
-    f.zero = (ok && p.has_zero) ? (uint32_t)(zw >> (4 * c16)) & 0xF : 0u;
-  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
-    const uint32_t word = reinterpret_cast<const uint32_t*>(w.meta)[((int64_t)ntc * p.kb4 + kbc / 4) * 64 + lane];
-    f.meta = ok ? (word >> (8 * (kbc & 3))) & 0xFF : 127u;
+    // (arithmetic rather than a select on the uniform format flag, which
+    // the compiler would turn into a branch around the load)
+    const int sf = p.scale_f32;
+    const uint32_t so = ok ? (uint32_t)(gi * 16 + (c16 & (14 | sf))) << (1 + sf) : kOob;
+    f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
+    const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
+    f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
+  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)) {
+    const uint32_t mo = ok ? (uint32_t)((kb >> 2) * 64 + lane) * 4 : kOob;
+    f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
   }
   return f;
 }
 
+// Decoders of a fragment's metadata words.  The INT scale of column c16 is
+// (raw << sh) & mk: f32 scales sh = 0, mk = ~0; bf16 pairs take the low
+// half (sh = 16) for even columns and the high half (mk = 0xFFFF0000) for
+// odd ones.
+struct IntScaleSel {
+  uint32_t sh, mk;
+};
+__device__ __forceinline__ IntScaleSel int_scale_sel(const GemmParams& p, int c16) {
+  const bool half = p.scale_f32 == 0;
+  return IntScaleSel{(half && !(c16 & 1)) ? 16u : 0u, (half && (c16 & 1)) ? 0xFFFF0000u : 0xFFFFFFFFu};
+}
+__device__ __forceinline__ float frag_int_scale(uint32_t raw, const IntScaleSel& sel) {
+  return __uint_as_float((raw << sel.sh) & sel.mk);
+}
+__device__ __forceinline__ int frag_int_zero(uint32_t raw, int c16) { return (int)((raw >> (4 * (c16 & 7))) & 0xF); }
+__device__ __forceinline__ uint32_t frag_mx_code(uint32_t raw, int kb) { return (raw >> (8 * (kb & 3))) & 0xFF; }
+
+// (x & mask) | magic in one instruction.  gfx9 encodes no literal in the
+// three-operand form, so the compiler would split it into two
+// literal-carrying ones; here the mask rides in an SGPR and the magic in a
+// VGPR.  ALU only.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+  return r;
+}
+
 __device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, g = 0x43004300u;
   u32x4_t o;
-  o[0] = (w & 0x000F000Fu) | 0x43004300u;
-  o[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  o[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  o[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  o[0] = and_or(w, m, g);
+  o[1] = and_or(w >> 4, m, g);
+  o[2] = and_or(w >> 8, m, g);
+  o[3] = and_or(w >> 12, m, g);
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
@@ -124,12 +188,12 @@ __device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
 
 // bf16 B operand of the 4 k-steps of a K-block.
 template <int FMT>
-__device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, bf16x8_t (&d)[4]) {
+__device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, int kb, bf16x8_t (&d)[4]) {
   if (FMT == F_INT) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) d[s] = int_dequant(f.w[0][s]);
   } else {
-    const float fs = e8m0_to_f32(f.meta);
+    const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
 #pragma unroll
     for (int s = 0; s < 4; ++s) d[s] = mx_dequant(f.w[0][s], fs);
   }
@@ -142,7 +206,8 @@ __device__ __forceinline__ f32x4_t mfma_bf16_kblock(const bf16x8_t (&a)[4], cons
 }
 
 template <int FMT>
-__device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, const BFrag<FMT>& f, f32x4_t c) {
+__device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, const BFrag<FMT>& f, uint32_t meta, int kb,
+                                                  f32x4_t c) {
   i32x8_t b8;
   b8[0] = f.w[0][0]; b8[1] = f.w[0][1]; b8[2] = f.w[0][2]; b8[3] = f.w[0][3];
   if (FMT == F_FP8) {
@@ -151,7 +216,7 @@ __device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, con
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 127, 0, 127);
   } else {
     b8[4] = 0; b8[5] = 0; b8[6] = 0; b8[7] = 0;
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 4, 0, sa, 0, (int)f.meta);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 4, 0, sa, 0, (int)frag_mx_code(meta, kb));
   }
 }
 
@@ -246,24 +311,34 @@ __device__ __forceinline__ void store_partial(const GemmParams& p, int split, in
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel: one 16-row tile (at most 16 valid rows), KW waves over
-// interleaved K-blocks.
+// Decode kernel: one 16-row tile (at most 16 valid rows) of WN 16-column
+// sub-tiles, KW compute waves splitting the workgroup's K range.
 //
-// The activation rows of the workgroup's K range are staged into LDS once
-// (rows >= valid count are never stored: their fragments read as zero), so
-// the main loop's only vector-memory loads are the weight ring: PF K-blocks
-// per wave in flight, never stalled behind an activation load (vector memory
-// loads complete in order).  LDS row layout per K-block: 16-byte chunks
-// XOR-swizzled with the row, so the 16 rows of one fragment read hit 16
-// different bank groups.
+// The activation rows of the K range and the weight metadata (scales, zero
+// points, E8M0 rows) are staged in LDS; each wave's only other loads are
+// its weight ring, PF K-blocks deep, whose slots it consumes as they land
+// (vector-memory loads complete in order).  Dense workgroups stage wave by
+// wave (each wave copies its own contiguous K-blocks with plain loads issued
+// ahead of its ring); MoE workgroups gather their rows through a loader wave
+// with LDS-DMA.  Rows >= the valid count are never stored; their fragments
+// repeat row 0 (an output row depends on its own A row alone).  LDS row
+// layout per K-block: 16-byte chunks XOR-swizzled with the row, so the 16
+// rows of one fragment read hit 16 different bank groups.  The KW partial
+// sums are added in a fixed order through LDS at the end.
 
 template <int FMT>
 struct StreamLds {
   static constexpr int kRowB = 128 * Tr<FMT>::kAElem;  // bytes per row per K-block
 };
 
+// Waves of a stream workgroup: KW compute waves, plus a loader wave where
+// the activation rows are gathered (MoE).  Dense workgroups stage their
+// activations wave by wave and need none.
+constexpr bool stream_self_staged(int amode, int epi) { return amode == A_DIRECT && epi == EPI_BF16; }
+constexpr int stream_waves(int kw, int amode, int epi) { return kw + (stream_self_staged(amode, epi) ? 0 : 1); }
+
 template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
-__global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
+__global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
   using T = Tr<FMT>;
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
@@ -271,17 +346,16 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
   constexpr int kRowB = StreamLds<FMT>::kRowB;
   constexpr int kCPR = kRowB / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-  __shared__ int32_t s_src[16];
+  __shared__ int s_nrows;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, lg = lane >> 4;
 
-  int64_t bid = blockIdx.x;
-  const int split = (int)(bid % p.split_k);
-  bid /= p.split_k;
-  const int tn = (int)(bid % p.n_tiles);
-  const int64_t tm = bid / p.n_tiles;
+  // grid (n-tile, m-tile, split): no index arithmetic
+  const int tn = (int)blockIdx.x;
+  const int tm = (int)blockIdx.y;
+  const int split = (int)blockIdx.z;
 
   int expert = 0;
   if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
@@ -314,101 +388,279 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
   int kb_end = kb_begin + p.kb_per_split;
   if (kb_end > p.kb_count) kb_end = p.kb_count;
   const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
-  const int first = kb_begin + wave;
-  const int nj = first < kb_end ? (kb_end - first + KW - 1) / KW : 0;
-
-  // source row of each tile row (-1: padding / past the end)
-  if (tid < 16) {
-    const int64_t row = row0 + tid;
-    int64_t src = -1;
-    if (AMODE == A_GATHER) {
-      const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-      if (f < p.sentinel) src = f / p.topk;
-    } else if (row < p.m) {
-      // grouped rows in sorted order: padding slots (sentinel) are skipped
-      src = (p.sorted && p.sorted[row] >= p.sentinel) ? -1 : row;
-    }
-    s_src[tid] = (int32_t)src;
+  constexpr bool kSelf = stream_self_staged(AMODE, EPI);
+  // Self-staged (dense) workgroups give compute wave w the contiguous
+  // K-blocks [kw0, kw0 + nj); otherwise wave w takes kb_begin + w, + KW, ...
+  // (wave KW, the loader, takes none).
+  int kw0, nj;
+  if constexpr (kSelf) {
+    const int per = (nkb + KW - 1) / KW;
+    kw0 = kb_begin + wave * per;
+    const int kw1 = kw0 + per < kb_end ? kw0 + per : kb_end;
+    nj = kw1 > kw0 ? kw1 - kw0 : 0;
+  } else {
+    kw0 = kb_begin + wave;
+    nj = (wave < KW && kw0 < kb_end) ? (kb_end - kw0 + KW - 1) / KW : 0;
   }
-  __syncthreads();
-  // rows [0, nrows) are stored; tile rows are compacted only at the end
-  // (dense: rows < m are a prefix; MoE: valid rows of a block are a prefix)
-  int nrows = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) nrows += s_src[r] >= 0 ? 1 : 0;
+  // the wave's j-th K-block (j < nj + PF; it matters only for j < nj)
+  auto kb_at = [&](int j) { return kSelf ? kw0 + j : kw0 + j * KW; };
 
-  // 1) weight ring
-  BFrag<FMT> ring[PF][WN];
+  // The loader wave finds the source row of each tile row (-1: padding /
+  // past the end) and stages the activation rows of the K range into LDS
+  // with LDS-DMA loads; the compute waves issue their weight rings (the
+  // loader's range is empty, so its ring loads return zeros at once).
+  WStripe st[WN];
 #pragma unroll
-  for (int q = 0; q < PF; ++q)
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns] && q < nj, first + q * KW, lane);
-
-  // LDS: activation slots (rounded up to whole 64-lane DMA instructions),
-  // then the MX scale dwords (likewise rounded)
-  const int scale_off = ((nrows * kCPR * nkb + 63) & ~63) * 16;
-  // 2) activation rows -> LDS with LDS-DMA loads (no registers; each wave
-  //    instruction fills 64 consecutive 16-byte slots, slot s of the layout
-  //    [K-block][row][swizzled chunk] holds logical chunk phys ^ swizzle(row))
-  {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.a), (short)0,
-                                                                          (int)p.a_bytes, 0x00020000);
-    const int slots = nrows * kCPR * nkb;
-    // each DMA instruction writes all 64 lanes' slots (zeros past `slots`):
-    // the footprint is slots rounded up to 64, which the launch sizes for
-    for (int base = wave * 64; base < slots; base += 64 * KW) {
+  for (int ns = 0; ns < WN; ++ns) st[ns] = make_stripe<FMT>(p, wp, nts[ns], ntv[ns]);
+  // first scale group / first 4-K-block E8M0 row of the K range (the LDS
+  // metadata starts there)
+  const int g0 = (FMT == F_INT) ? kb_begin / p.kb_per_group : 0;
+  const int r0 = kb_begin >> 2;
+  auto stage = [&]() {
+    // source row of tile row `lane` (lanes 0..15; -1: padding / past the end)
+    int src = -1;
+    if (lane < 16) {
+      const int64_t row = row0 + lane;
+      if (AMODE == A_GATHER) {
+        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
+        if (f < p.sentinel) src = f / p.topk;
+      } else if (row < p.m) {
+        // grouped rows in sorted order: padding slots (sentinel) are skipped
+        src = (p.sorted && p.sorted[row] >= p.sentinel) ? -1 : (int)row;
+      }
+    }
+    // rows [0, nr) are stored (dense: rows < m are a prefix; MoE: the valid
+    // rows of a block are a prefix).  Direct rows are row0 + r; gathered
+    // ones are read from lane r.
+    const int nr = __builtin_popcountll(__builtin_amdgcn_ballot_w64(src >= 0));
+    if (lane == 0) s_nrows = nr;
+    if (nr == 0) return;
+    auto src_row = [&](int r) -> int64_t {
+      if constexpr (AMODE == A_GATHER) return __builtin_amdgcn_ds_bpermute(r << 2, src);
+      return row0 + r;
+    };
+    // x / nr for x < 2^14 (nr <= 16) as a multiply-shift: exact while
+    // x * nr < 2^20
+    const uint32_t mnr = ((1u << 20) + nr - 1) / nr;
+    // LDS: activation slots (rounded up to whole 64-lane DMA instructions),
+    // then the MX scale dwords (likewise rounded).  Each DMA instruction
+    // fills 64 consecutive 16-byte slots; slot s of the layout
+    // [K-block][row][swizzled chunk] holds logical chunk phys ^ swizzle(row).
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a, p.a_bytes);
+    const int slots = nr * kCPR * nkb;
+#pragma unroll 1
+    for (int base = 0; base < slots; base += 64) {
       const int sidx = base + lane;
+      const int phys = sidx & (kCPR - 1);
+      const uint32_t rowkb = (uint32_t)sidx / kCPR;
+      const int kbl = (int)((rowkb * mnr) >> 20);
+      const int r = (int)rowkb - kbl * nr;
+      const int c = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
+      const int64_t sr = src_row(r < nr ? r : 0);
       // lanes past `slots` fill unused slots of the footprint from offset 0
       // (always a valid address): no reliance on range checking
-      uint32_t voff = 0;
-      if (sidx < slots) {
-        const int phys = sidx % kCPR;
-        const int r = (sidx / kCPR) % nrows;
-        const int kbl = sidx / (kCPR * nrows);
-        const int c = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
-        voff = (uint32_t)(((int64_t)s_src[r] * p.lda + (int64_t)(kb_begin + kbl) * 128) * T::kAElem + c * 16);
-      }
+      const uint32_t voff = sidx < slots
+                                ? (uint32_t)((sr * p.lda + (int64_t)(kb_begin + kbl) * 128) * T::kAElem + c * 16)
+                                : 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dsm + base * 16, 16, voff, 0, 0, 0);
     }
     if (FMT == F_MXFP4_MXFP8) {
-      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.a_scale), (short)0,
-                                                                           (int)p.a_scale_bytes, 0x00020000);
-      const int n4 = nrows * nkb;
-      for (int base = wave * 64; base < n4; base += 64 * KW) {
+      const int scale_off = ((slots + 63) & ~63) * 16;
+      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale, p.a_scale_bytes);
+      const int n4 = nr * nkb;
+#pragma unroll 1
+      for (int base = 0; base < n4; base += 64) {
         const int sidx = base + lane;
-        uint32_t voff = 0;
-        if (sidx < n4) {
-          const int r = sidx % nrows, kbl = sidx / nrows;
-          voff = (uint32_t)((int64_t)s_src[r] * p.a_scale_ld + (int64_t)(kb_begin + kbl) * 4);
-        }
+        const int kbl = (int)(((uint32_t)sidx * mnr) >> 20);
+        const int r = sidx - kbl * nr;
+        const int64_t sr = src_row(r < nr ? r : 0);
+        const uint32_t voff = sidx < n4 ? (uint32_t)(sr * p.a_scale_ld + (int64_t)(kb_begin + kbl) * 4) : 0u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, dsm + scale_off + base * 4, 4, voff, 0, 0, 0);
       }
     }
+    // weight metadata of the K range, per valid sub-tile (filler lanes read
+    // the stripe's first bytes, which always exist)
+    if (FMT == F_INT && nkb > 0) {
+      const int g1 = (kb_end - 1) / p.kb_per_group + 1;
+      const int ss = p.scale_f32 ? 4 : 2;
+      const int n16 = (g1 - g0) * ss;  // 16-byte slots of scales
+      const int n4 = (g1 - g0) * 2;    // 4-byte slots of zero points
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) {
+        if (!ntv[ns]) continue;
+        uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
+        // (resources copied to locals: a captured array member passed to
+        // the LDS-DMA builtin makes the host pass drop the kernel's stub)
+        const __amdgpu_buffer_rsrc_t rm = st[ns].meta, rz = st[ns].zero;
+#pragma unroll 1
+        for (int base = 0; base < n16; base += 64) {
+          const int sl = base + lane;
+          const uint32_t voff = sl < n16 ? (uint32_t)(g0 * 16 * ss + sl * 16) : 0u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, mb + base * 16, 16, voff, 0, 0, 0);
+        }
+        if (p.has_zero) {
+#pragma unroll 1
+          for (int base = 0; base < n4; base += 64) {
+            const int sl = base + lane;
+            const uint32_t voff = sl < n4 ? (uint32_t)(g0 * 8 + sl * 4) : 0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, mb + p.lds_zero_off + base * 4, 4, voff, 0, 0, 0);
+          }
+        }
+      }
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) && nkb > 0) {
+      const int n16 = (((kb_end + 3) >> 2) - r0) * 16;  // 16-byte slots of E8M0 rows
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) {
+        if (!ntv[ns]) continue;
+        uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
+        const __amdgpu_buffer_rsrc_t rm = st[ns].meta;
+#pragma unroll 1
+        for (int base = 0; base < n16; base += 64) {
+          const int sl = base + lane;
+          const uint32_t voff = sl < n16 ? (uint32_t)(r0 * 256 + sl * 16) : 0u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, mb + base * 16, 16, voff, 0, 0, 0);
+        }
+      }
+    }
+  };
+  BFrag<FMT> ring[PF][WN];
+  auto issue_ring = [&]() {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT, false>(p, st[ns], q < nj, kb_at(q), lane);
+      // issue slot by slot, in the order of use (they land in issue order)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Loader path (gathered rows): the rings go out first, the loader wave
+  // looks the rows up and DMAs them, and waits for its DMA inside its own
+  // branch (the compiler waits for every outstanding vector-memory load
+  // before an LDS read that follows an LDS-DMA it cannot prove finished, so
+  // the wait must close the branch).
+  auto stage_via_loader = [&]() {
+    issue_ring();
+    if (wave == KW) {
+      stage();
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+  };
+  auto self_stage = [&](int nr) {
+    const int nch = nj * nr * kCPR;                  // 16-byte activation chunks (<= 512)
+    const int slot0 = (kw0 - kb_begin) * nr * kCPR;  // first LDS slot of the wave's K-blocks
+    const uint32_t mnr = ((1u << 20) + nr - 1) / nr; // x / nr as a multiply-shift (x * nr < 2^20)
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    u32x4_t abuf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = i * 64 + lane;
+      const uint32_t rowkb = (uint32_t)c / kCPR;
+      const int kbl = (int)((rowkb * mnr) >> 20);
+      const int r = (int)rowkb - kbl * nr;
+      const int phys = c & (kCPR - 1);
+      const int lc = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
+      const uint32_t off = (uint32_t)(((row0 + r) * p.lda + (int64_t)(kw0 + kbl) * 128) * T::kAElem + lc * 16);
+      abuf[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off : kOob, 0, 0);
+    }
+    // weight metadata of the wave's K-blocks (INT: scales and zero points of
+    // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
+    constexpr int kML = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? 2 : 0);
+    u32x4_t mbuf[WN][kML > 0 ? kML : 1];
+    uint32_t zbuf[WN];
+    int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
+    if (FMT == F_INT && nj > 0) {
+      const int g0w = kw0 / p.kb_per_group, g1w = (kw0 + nj - 1) / p.kb_per_group + 1;
+      const int ss = p.scale_f32 ? 4 : 2;
+      mb0 = g0w * 16 * ss;
+      mbytes = (g1w - g0w) * 16 * ss;  // <= 1 KB
+      mdst = (g0w - g0) * 16 * ss;
+      zb0 = g0w * 8;
+      zbytes = p.has_zero ? (g1w - g0w) * 8 : 0;  // <= 256 B
+      zdst = p.lds_zero_off + (g0w - g0) * 8;
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) && nj > 0) {
+      const int rw0 = kw0 >> 2, rw1 = (kw0 + nj + 3) >> 2;
+      mb0 = rw0 * 256;
+      mbytes = (rw1 - rw0) * 256;  // <= 2 KB
+      mdst = (rw0 - r0) * 256;
+    }
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) {
+#pragma unroll
+      for (int i = 0; i < kML; ++i) {
+        const int b = (i * 64 + lane) * 16;
+        mbuf[ns][i] = __builtin_amdgcn_raw_buffer_load_b128(st[ns].meta, b < mbytes ? (uint32_t)(mb0 + b) : kOob, 0, 0);
+      }
+      if (FMT == F_INT)
+        zbuf[ns] = __builtin_amdgcn_raw_buffer_load_b32(st[ns].zero,
+                                                        lane * 4 < zbytes ? (uint32_t)(zb0 + lane * 4) : kOob, 0, 0);
+    }
+    issue_ring();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i * 64 + lane < nch) *reinterpret_cast<u32x4_t*>(dsm + (slot0 + i * 64 + lane) * 16) = abuf[i];
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) {
+      uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
+#pragma unroll
+      for (int i = 0; i < kML; ++i)
+        if ((i * 64 + lane) * 16 < mbytes) *reinterpret_cast<u32x4_t*>(mb + mdst + (i * 64 + lane) * 16) = mbuf[ns][i];
+      if (FMT == F_INT && lane * 4 < zbytes) *reinterpret_cast<uint32_t*>(mb + zdst + lane * 4) = zbuf[ns];
+    }
+  };
+
+  int nrows = 0;
+  if constexpr (kSelf) {
+    // Each wave copies the activation rows and weight metadata of its own
+    // K-blocks into their places of the workgroup's LDS layout with plain
+    // loads issued ahead of its ring (vector-memory loads land in issue
+    // order, so the copy waits for them alone), then reads only what it
+    // wrote: no barrier, no loader.  Rows < m of the tile are a prefix.
+    nrows = p.m - row0 < 16 ? (int)(p.m - row0) : 16;
+    self_stage(nrows);
+  } else {
+    stage_via_loader();
+    nrows = s_nrows;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+
+  const int scale_off = ((nrows * kCPR * nkb + 63) & ~63) * 16;
 
   f32x4_t acc[WN];
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) acc[ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const bool arow_ok = c16 < nrows;
-  const int rr = arow_ok ? c16 : 0;  // LDS row read (row 0 stands in for empty rows; nrows >= 1)
+  const int rr = arow_ok ? c16 : 0;  // LDS row read (row 0 stands in for empty rows)
+  const IntScaleSel ssel = int_scale_sel(p, c16);
+  // raw metadata words of sub-tile ns at K-block kb, from the LDS copy
+  auto lds_meta = [&](int ns, int kb, uint32_t& m, uint32_t& z) {
+    const uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
+    m = 0;
+    z = 0;
+    if (FMT == F_INT) {
+      const int gl = (int)(((float)kb + 0.5f) * p.inv_kbg) - g0;
+      const int sf = p.scale_f32;
+      m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
+      const uint32_t zr = *reinterpret_cast<const uint32_t*>(mb + p.lds_zero_off + gl * 8 + ((c16 >> 3) << 2));
+      z = p.has_zero ? zr : 0u;
+    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+      m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> 2) - r0) * 64 + lane) * 4);
+    }
+  };
 
   for (int j0 = 0; j0 < nj; j0 += PF) {
 #pragma unroll
     for (int q = 0; q < PF; ++q) {
       const int j = j0 + q;
       if (j < nj) {
-        const int kb = first + j * KW;
+        const int kb = kb_at(j);
         const uint8_t* ab = dsm + ((kb - kb_begin) * nrows + rr) * kRowB;
         if constexpr (T::kBf16) {
+          // (rows >= nrows read row 0: an output row depends on its own A
+          // row alone, and those rows are never stored)
           bf16x8_t af[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ab + (((4 * lg + s) ^ rr) * 16));
-            const u32x4_t z = {0, 0, 0, 0};
-            af[s] = __builtin_bit_cast(bf16x8_t, arow_ok ? v : z);
-          }
+          for (int s = 0; s < 4; ++s)
+            af[s] = *reinterpret_cast<const bf16x8_t*>(ab + (((4 * lg + s) ^ rr) * 16));
           f32x4_t rs = {0.0f, 0.0f, 0.0f, 0.0f};
           if (FMT == F_INT) {
             // row sums of the K-block in the C layout: A x ones
@@ -420,11 +672,13 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
             bf16x8_t d[4];
-            dequant_b<FMT>(ring[q][ns], d);
+            uint32_t mw, zw;
+            lds_meta(ns, kb, mw, zw);
+            dequant_b<FMT>(ring[q][ns], mw, kb, d);
             if (FMT == F_INT) {
               const f32x4_t t = mfma_bf16_kblock(af, d, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-              const float sc = __uint_as_float(ring[q][ns].meta);
-              const float off = (float)(p.int_offset + (int)ring[q][ns].zero);
+              const float sc = frag_int_scale(mw, ssel);
+              const float off = (float)(p.int_offset + frag_int_zero(zw, c16));
 #pragma unroll
               for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ns][i]);
             } else {
@@ -433,11 +687,8 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
           }
         } else {
           const int sw = (rr >> 1) & 7;
-          const u32x4_t z = {0, 0, 0, 0};
-          u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ab + ((lg ^ sw) * 16));
-          u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ab + (((4 + lg) ^ sw) * 16));
-          lo = arow_ok ? lo : z;
-          hi = arow_ok ? hi : z;
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ab + ((lg ^ sw) * 16));
+          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ab + (((4 + lg) ^ sw) * 16));
           int sa = 127;
           if (FMT == F_MXFP4_MXFP8) {
             const uint32_t sw4 = reinterpret_cast<const uint32_t*>(dsm + scale_off)[(kb - kb_begin) * nrows + rr];
@@ -447,18 +698,17 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
           a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
           a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
 #pragma unroll
-          for (int ns = 0; ns < WN; ++ns) acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], acc[ns]);
+          for (int ns = 0; ns < WN; ++ns) {
+            uint32_t mw, zw;
+            lds_meta(ns, kb, mw, zw);
+            acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], mw, kb, acc[ns]);
+          }
         }
       }
-      // refill unconditionally (a conditional load would be waited on where
-      // the branch rejoins); past the end it re-reads the current block,
-      // which is an L2 hit and is never used
-      {
-        const int jn = (j + PF < nj) ? j + PF : (j < nj ? j : 0);
-        const int kbn = first + jn * KW;
+      // refill (past the end of the range the load returns zeros without
+      // touching memory)
 #pragma unroll
-        for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns] && nj > 0, kbn, lane);
-      }
+      for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT, false>(p, st[ns], j + PF < nj, kb_at(j + PF), lane);
     }
   }
 
@@ -467,7 +717,7 @@ __global__ __launch_bounds__(64 * KW) void stream_kernel(const GemmParams p) {
   if constexpr (KW > 1) {
     f32x4_t* red = reinterpret_cast<f32x4_t*>(dsm);
     __syncthreads();
-    if (wave > 0) {
+    if (wave > 0 && wave < KW) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) red[((wave - 1) * WN + ns) * 64 + lane] = acc[ns];
     }
@@ -540,20 +790,20 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kStage];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wn = tid >> 6;
+  const int lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c16 = lane & 15, lg = lane >> 4;
 
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
   // XCDs; remap them so that each XCD walks a contiguous range of
   // (m-tile, n-tile, split) tiles -- n fastest -- and reuses its activation
   // rows from its own L2.
-  const int64_t nwg = gridDim.x;
-  int64_t bid = blockIdx.x;
+  const uint32_t nwg = gridDim.x;
+  uint32_t bid = blockIdx.x;
   if (nwg % 8 == 0) bid = (bid % 8) * (nwg / 8) + bid / 8;
-  const int split = (int)(bid % p.split_k);
-  bid /= p.split_k;
-  const int tn = (int)(bid % p.n_tiles);
-  const int64_t tm = bid / p.n_tiles;
+  const int split = (int)(bid % (uint32_t)p.split_k);
+  bid /= (uint32_t)p.split_k;
+  const int tn = (int)(bid % (uint32_t)p.n_tiles);
+  const int64_t tm = bid / (uint32_t)p.n_tiles;
 
   int expert = 0;
   if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
@@ -657,11 +907,14 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       reinterpret_cast<uint32_t*>(base + C::kStageA)[tid] = x_reg;
   };
 
+  WStripe st[WN];
+#pragma unroll
+  for (int ns = 0; ns < WN; ++ns) st[ns] = make_stripe<FMT>(p, wp, nts[ns], ntv[ns]);
   BFrag<FMT> bq[2][WN];
-  auto load_bs = [&](int kb, auto set_c) {
+  auto load_bs = [&](int kb, bool ok, auto set_c) {
     constexpr int set = decltype(set_c)::value;
 #pragma unroll
-    for (int ns = 0; ns < WN; ++ns) bq[set][ns] = load_b<FMT>(p, wp, nts[ns], ntv[ns], kb, lane);
+    for (int ns = 0; ns < WN; ++ns) bq[set][ns] = load_b<FMT>(p, st[ns], ok, kb, lane);
   };
 
   f32x4_t acc[WM][WN];
@@ -670,13 +923,14 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int buf, auto set_c) {
+  const IntScaleSel ssel = int_scale_sel(p, c16);
+  auto compute = [&](int buf, int kb, auto set_c) {
     constexpr int set = decltype(set_c)::value;
     const uint8_t* abase = smem + buf * C::kStage;
     if constexpr (T::kBf16) {
       bf16x8_t d[WN][4];
 #pragma unroll
-      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bq[set][ns], d[ns]);
+      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bq[set][ns], bq[set][ns].meta, kb, d[ns]);
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
         const int r = ms * 16 + c16;
@@ -689,8 +943,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
             const f32x4_t t = mfma_bf16_kblock(af, d[ns], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-            const float sc = __uint_as_float(bq[set][ns].meta);
-            const float off = (float)(p.int_offset + (int)bq[set][ns].zero);
+            const float sc = frag_int_scale(bq[set][ns].meta, ssel);
+            const float off = (float)(p.int_offset + frag_int_zero(bq[set][ns].zero, c16));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               acc[ms][ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ms][ns][i]);
@@ -714,7 +968,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         if (FMT == F_MXFP4_MXFP8)
           sa = (int)((reinterpret_cast<const uint32_t*>(abase + C::kStageA)[r] >> (8 * lg)) & 0xFF);
 #pragma unroll
-        for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bq[set][ns], acc[ms][ns]);
+        for (int ns = 0; ns < WN; ++ns)
+          acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bq[set][ns], bq[set][ns].meta, kb, acc[ms][ns]);
       }
     }
   };
@@ -722,25 +977,26 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   // Prefetches are unconditional (a conditional load is waited on where the
-  // branch rejoins); past the last K-block they re-read it (L2 hit, unused).
+  // branch rejoins); past the last K-block the activation prefetch re-reads
+  // it (L2 hit, unused) and the weight prefetch reads nothing.
   if (nkb > 0) {
     const int kb_last = kb_begin + nkb - 1;
     load_a(kb_begin);
-    load_bs(kb_begin, I0{});
+    load_bs(kb_begin, true, I0{});
     store_a(0);
     __syncthreads();
     for (int j = 0; j < nkb; j += 2) {
       const int k1 = kb_begin + j + 1 <= kb_last ? kb_begin + j + 1 : kb_last;
       load_a(k1);
-      load_bs(k1, I1{});
-      compute(0, I0{});
+      load_bs(k1, kb_begin + j + 1 <= kb_last, I1{});
+      compute(0, kb_begin + j, I0{});
       store_a(1);
       __syncthreads();
       if (j + 1 >= nkb) break;
       const int k2 = kb_begin + j + 2 <= kb_last ? kb_begin + j + 2 : kb_last;
       load_a(k2);
-      load_bs(k2, I0{});
-      compute(1, I1{});
+      load_bs(k2, kb_begin + j + 2 <= kb_last, I0{});
+      compute(1, kb_begin + j + 1, I1{});
       store_a(0);
       __syncthreads();
     }
@@ -894,18 +1150,21 @@ struct Instance {
 };
 
 #define HUM_STREAM(F, WN, KW, PF, AM, EP) \
-  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * KW}
+  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(KW, AM, EP)}
 #define HUM_TILE(F, WM, WN, AM, EP) \
   {{F, KIND_TILE, WM, WN, 4, 1, AM, EP}, tile_kernel<F, WM, WN, AM, EP>, 256}
 
+// Ring depth in 1-KB weight fragments per sub-tile (FP8 fragments are 2 KB:
+// half as many).  A CU keeps about 64-128 KB of weights in flight.
+#define HUM_PF(F, n) ((F) == F_FP8 ? ((n) > 1 ? (n) / 2 : 1) : (n))
 #define HUM_DENSE_SET(F)                                   \
-  HUM_STREAM(F, 1, 8, 8, A_DIRECT, EPI_BF16),              \
-  HUM_STREAM(F, 1, 16, 4, A_DIRECT, EPI_BF16),             \
-  HUM_STREAM(F, 2, 8, 4, A_DIRECT, EPI_BF16),              \
-  HUM_STREAM(F, 2, 16, 4, A_DIRECT, EPI_BF16),             \
-  HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_BF16),              \
-  HUM_STREAM(F, 4, 16, 2, A_DIRECT, EPI_BF16),             \
-  HUM_STREAM(F, 1, 4, 8, A_DIRECT, EPI_BF16),              \
+  HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
+  HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \
+  HUM_STREAM(F, 2, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
+  HUM_STREAM(F, 2, 15, HUM_PF(F, 4), A_DIRECT, EPI_BF16),  \
+  HUM_STREAM(F, 4, 8, HUM_PF(F, 4), A_DIRECT, EPI_BF16),   \
+  HUM_STREAM(F, 4, 15, HUM_PF(F, 2), A_DIRECT, EPI_BF16),  \
+  HUM_STREAM(F, 1, 4, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
   HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
   HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
   HUM_TILE(F, 2, 4, A_DIRECT, EPI_BF16),                   \
@@ -917,8 +1176,8 @@ struct Instance {
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
   HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
-  HUM_STREAM(F, 4, 16, 2, A_GATHER, EPI_UP),               \
-  HUM_STREAM(F, 4, 16, 2, A_DIRECT, EPI_SCATTER),          \
+  HUM_STREAM(F, 4, 15, 2, A_GATHER, EPI_UP),               \
+  HUM_STREAM(F, 4, 15, 2, A_DIRECT, EPI_SCATTER),          \
   HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
   HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
   HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
@@ -934,8 +1193,8 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_MXFP4_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
-    HUM_STREAM(F_MXFP4_BF16, 2, 16, 4, A_GATHER, EPI_SWIGLU_BF16),
-    HUM_STREAM(F_MXFP4_BF16, 2, 16, 4, A_DIRECT, EPI_SCATTER),
+    HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
+    HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_DIRECT, EPI_SCATTER),
     HUM_MOE_SET(F_MXFP4_BF16, EPI_SWIGLU_BF16),
     HUM_MOE_SET(F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8),
 };
@@ -969,7 +1228,8 @@ static const Instance* find_instance(const KernelKey& k) {
 
 bool gemm_instance_exists(const KernelKey& key) { return find_instance(key) != nullptr; }
 
-hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, int block_m, void* stream) {
+hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_tiles, int block_m, void* stream) {
+  GemmParams p = p_in;
   const Instance* in = find_instance(key);
   if (!in)
     return set_error(HUM_ERR_UNSUPPORTED,
@@ -981,9 +1241,16 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tile
   hipStream_t s = static_cast<hipStream_t>(stream);
   size_t dyn = 0;
   if (key.kind == KIND_STREAM) {
-    const int64_t stage = stream_lds_footprint(key.fmt, p.stream_rows, p.kb_per_split);
+    const StreamLdsPlan L = stream_lds_plan(key.fmt, p.stream_rows, p.kb_per_split, key.wn, p.kb_per_group,
+                                            p.scale_f32, p.ng, p.kb4);
+    if (key.amode == A_DIRECT && key.epi == EPI_BF16 &&
+        !stream_self_stage_fits(key.fmt, p.stream_rows, p.kb_per_split, key.waves_k, p.kb_per_group, p.scale_f32))
+      return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per wave too long (raise split_k)");
+    p.lds_meta_off = (int)L.meta_off;
+    p.lds_meta_stride = (int)L.meta_stride;
+    p.lds_zero_off = (int)L.zero_off;
     const int64_t red = (int64_t)(key.waves_k - 1) * key.wn * 64 * 16;
-    dyn = (size_t)(stage > red ? stage : red);
+    dyn = (size_t)(L.total > red ? L.total : red);
     if ((int64_t)dyn > kStreamLdsMax) return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per split too long for LDS");
     if (dyn > 64 * 1024) {
       const int idx = (int)(in - kInstances);
@@ -995,7 +1262,12 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tile
       }
     }
   }
-  hipLaunchKernelGGL(in->fn, dim3((unsigned)grid), dim3(in->threads), dyn, s, p);
+  dim3 g((unsigned)grid);
+  if (key.kind == KIND_STREAM) {
+    if (m_tiles > 65535) return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: more than 65535 row tiles");
+    g = dim3((unsigned)p.n_tiles, (unsigned)m_tiles, (unsigned)p.split_k);
+  }
+  hipLaunchKernelGGL(in->fn, g, dim3(in->threads), dyn, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "gemm launch: %s", hipGetErrorString(err));
   if (p.split_k > 1) {

@@ -86,6 +86,7 @@ struct GemmParams {
   const float* gscale;
   int64_t codes_per_expert, scales_per_expert, zeros_per_expert;
   int nt_count, kb_count, ng, kb_per_group, kb4;
+  float inv_kbg;      // 1 / kb_per_group (group of K-block kb: floor((kb + 0.5) * inv_kbg))
   int scale_f32, int_offset, has_zero;
   int64_t n;          // valid output columns (I for the SwiGLU epilogues)
   int swiglu_nt_off;  // up sub-tile offset (I / 16) for SwiGLU
@@ -113,6 +114,10 @@ struct GemmParams {
   int kb_per_split;
   int n_tiles;
   int stream_rows;    // stream kernel: most valid rows of one 16-row tile
+  // stream kernel LDS plan (bytes): weight metadata of sub-tile ns at
+  // lds_meta_off + ns * lds_meta_stride, INT zero points lds_zero_off
+  // further
+  int lds_meta_off, lds_meta_stride, lds_zero_off;
 };
 
 enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1 };
@@ -135,6 +140,48 @@ constexpr int64_t stream_lds_footprint(int fmt, int rows, int64_t kb) {
   const int64_t a = ((rows * cpr * kb + 63) / 64) * 64 * 16;
   const int64_t sc = (fmt == F_MXFP4_MXFP8) ? ((rows * kb + 63) / 64) * 64 * 4 : 0;
   return a + sc;
+}
+
+// Full LDS plan of a stream launch: the activation staging, then per
+// sub-tile the weight metadata of the K range (INT: scales then zero points
+// of the groups it touches; MX: the E8M0 rows of its 4-K-block steps), each
+// rounded up to whole 64-lane LDS-DMA instructions.
+struct StreamLdsPlan {
+  int64_t meta_off, meta_stride, zero_off, total;
+};
+constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, int64_t kb_per_group, int scale_f32,
+                                        int64_t ng, int64_t kb4) {
+  StreamLdsPlan L{stream_lds_footprint(fmt, rows, kb), 0, 0, 0};
+  if (fmt == F_INT) {
+    int64_t groups = (kb + kb_per_group - 1) / kb_per_group + 1;  // groups a range of kb blocks touches
+    if (groups > ng) groups = ng;
+    const int64_t sc = ((groups * 16 * (scale_f32 ? 4 : 2) + 1023) / 1024) * 1024;
+    const int64_t zr = ((groups * 8 + 255) / 256) * 256;
+    L.zero_off = sc;
+    L.meta_stride = sc + zr;
+  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8) {
+    int64_t r = kb / 4 + 2;  // 4-K-block rows a range of kb blocks touches
+    if (r > kb4) r = kb4;
+    L.meta_stride = ((r * 256 + 1023) / 1024) * 1024;
+  }
+  L.total = L.meta_off + wn * L.meta_stride;
+  return L;
+}
+
+// A self-staged (dense) stream workgroup: each of the kw compute waves
+// copies its own K-blocks' activations (at most 8 16-byte chunks per lane)
+// and weight metadata (INT: at most 1 KB of scales and 256 B of zero
+// points; MX: at most 2 KB of E8M0 rows) with one pass of loads.
+constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int64_t kb_per_group, int scale_f32) {
+  const int64_t per = (kb + kw - 1) / kw;
+  const int64_t cpr = (fmt == F_INT || fmt == F_MXFP4_BF16) ? 16 : 8;
+  if (rows * per * cpr > 512) return false;
+  if (fmt == F_INT) {
+    const int64_t groups = (per + kb_per_group - 1) / kb_per_group + 1;
+    return groups * 16 * (scale_f32 ? 4 : 2) <= 1024 && groups * 8 <= 256;
+  }
+  if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8) return (per / 4 + 2) * 256 <= 2048;
+  return true;
 }
 
 struct KernelKey {

@@ -3,6 +3,7 @@ include/hum.h declares, and its host-side validation / sizing / selector
 paths answer without touching a GPU."""
 import ctypes
 
+import numpy as np
 import pytest
 
 import quantized_gemm_packed_amd as hum
@@ -95,3 +96,23 @@ def test_workspace_sizes(lib):
     w2 = hum.make_desc("e2m1", "group", 32, "e8m0", 4096, 1024, num_experts=128)
     nb = hum.moe_workspace_bytes(w13, w2, 64, 8)
     assert nb >= 64 * 8 * 4096 * 2
+
+
+def test_k_beyond_limit_rejected(lib):
+    ok = hum.make_desc("int4", "group", 128, "bf16", 64, 1 << 21)
+    assert lib.hum_packed_weight_bytes(ctypes.byref(ok)) > 0
+    d = hum.make_desc("int4", "group", 128, "bf16", 64, (1 << 21) + 128)
+    assert lib.hum_packed_weight_bytes(ctypes.byref(d)) == 0
+    assert b"too large" in lib.hum_last_error()
+
+
+def test_group_index_by_fp32_reciprocal_is_exact():
+    """The GEMM kernels find the scale group of K-block kb as
+    floor((kb + 1/2) * fl(1 / d)) in fp32 (d = K-blocks per group).  Check it
+    against integer division for every kb < 2^14 (k <= 2^21) and every d."""
+    kb = np.arange(1 << 14, dtype=np.float32) + np.float32(0.5)
+    kbi = np.arange(1 << 14, dtype=np.int64)
+    for d in range(1, (1 << 14) + 1):
+        inv = np.float32(1.0) / np.float32(d)
+        q = np.floor(kb * inv).astype(np.int64)   # fp32 product, rounded to nearest
+        assert np.array_equal(q, kbi // d), d

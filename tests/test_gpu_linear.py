@@ -18,7 +18,8 @@ from gpu_util import assert_bf16_exact, assert_tol, descs, dev, prepare
 pytestmark = pytest.mark.gpu
 
 # (kind, wave_m, wave_n, waves_n, waves_k): every compiled dense instance
-STREAM_TILES = [(1, 1, 1, 1, 8), (1, 1, 2, 1, 8), (1, 1, 4, 1, 8), (1, 1, 1, 1, 4)]
+STREAM_TILES = [(1, 1, 1, 1, 8), (1, 1, 2, 1, 8), (1, 1, 4, 1, 8), (1, 1, 1, 1, 4), (1, 1, 1, 1, 15), (1, 1, 2, 1, 15),
+                (1, 1, 4, 1, 15)]
 TILE_TILES = [(0, 1, 4, 4, 1), (0, 2, 2, 4, 1), (0, 2, 4, 4, 1), (0, 4, 2, 4, 1), (0, 4, 4, 4, 1),
               (0, 8, 2, 4, 1), (0, 8, 4, 4, 1)]
 DENSE_TILES = STREAM_TILES + TILE_TILES
@@ -35,6 +36,17 @@ def cfg(t, split):
 def rows_for(tile, m):
     """The stream kernel takes at most 16 rows."""
     return min(m, 13) if tile[0] == 1 else m
+
+
+def stream_fits(tile, m, k, split, chunk_per_row_kb=16):
+    """A dense stream launch gives each of its waves_k waves a contiguous
+    K range whose activation rows it copies in at most 8 16-byte chunks per
+    lane; longer ranges are rejected (a larger split_k fits)."""
+    if tile[0] != 1:
+        return True
+    kb, kw = k // 128, tile[4]
+    kbps = -(-(-(-kb // split)) // kw) * kw
+    return m * (-(-kbps // kw)) * chunk_per_row_kb <= 512
 
 
 def _int_exact_case(seed, wd, m, n, k, gs, zero):
@@ -54,6 +66,10 @@ def test_int_exact_every_tile(tile, split):
     hd, od = descs("uint4", "group", gs, "bf16", 1, n, k, zero=True)
     print(f"case uint4 exact tile={tile} split={split}", flush=True)
     packed = prepare(hd, w, "bf16")
+    if not stream_fits(tile, m, k, split):
+        with pytest.raises(hum.HumError, match="raise split_k"):
+            hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+        return
     out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
     torch.cuda.synchronize()
     ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w["zeros"])

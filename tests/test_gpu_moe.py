@@ -13,7 +13,7 @@ from gpu_util import assert_tol, descs, dev, prepare
 pytestmark = pytest.mark.gpu
 
 # (kind, wave_m, wave_n, waves_n, waves_k): every compiled MoE instance
-MOE_TILES = [(1, 1, 4, 1, 8), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 4, 4, 4, 1), (0, 8, 4, 4, 1)]
+MOE_TILES = [(1, 1, 4, 1, 8), (1, 1, 4, 1, 15), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 4, 4, 4, 1), (0, 8, 4, 4, 1)]
 
 
 def cfg(t, split=1):
