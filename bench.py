@@ -13,7 +13,8 @@ Kernels for Quantized Inference", section "Performance": warmed kernels, cold
 caches between samples -- here R rotating copies of the weights (> 1 GiB in
 total) defeat the 4 MB L2 per XCD and the 256 MB Infinity Cache; MoE time is
 the whole layer (align, gate_up, down, reduce).  Times come from HIP events
-recorded on the stream the kernels run on.
+recorded around HIP-graph replays of the calls (so host-side launch cost is
+excluded), on the stream the kernels run on.
 
 The CPU baseline is the oracle (NumPy float64) timed on the host on a
 bounded sample of the same sweep.
@@ -45,6 +46,10 @@ def parse():
     ap.add_argument("--suite", choices=["dense", "all"], default="all")
     ap.add_argument("--iters", type=int, default=50, help="launches per timing sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every timed call directly instead of replaying a HIP graph (for counter runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device copies of BYTES bytes (calibrates HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -57,23 +62,45 @@ def _dev(a):
 
 
 class Timer:
-    """HIP-event timing on the current stream (the one the library uses)."""
+    """Device time per call: `iters` calls are captured into one HIP graph
+    (the library launches kernels only, on torch's current stream, and
+    allocates nothing when given its output and workspace), and the graph's
+    replay is bracketed by HIP events on the replay stream -- so host-side
+    call overhead does not enter the figure."""
 
-    def __init__(self):
+    def __init__(self, eager=False):
         import torch
         self.torch = torch
+        self.eager = eager
 
     def run(self, fn, iters):
         torch = self.torch
+        if self.eager:
+            s = torch.cuda.current_stream()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for i in range(iters):
+                fn(i)
+            e1.record(s)
+            e1.synchronize()
+            return e0.elapsed_time(e1) * 1e-3 / iters
+        fn(0)                       # first-call setup (kernel attributes) outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                fn(i)
+        g.replay()                  # warm replay
+        torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         e0.record(s)
-        for i in range(iters):
-            fn(i)
+        g.replay()
         e1.record(s)
         e1.synchronize()
+        del g
         return e0.elapsed_time(e1) * 1e-3 / iters   # seconds per call
 
 
@@ -123,7 +150,10 @@ def dense_tiny(hum, timer, iters):
     desc = hum.make_desc("int4", "group", 128, "bf16", 512, 1024)
     packed = hum.prepare_weight(desc, _dev(case["codes"]), _dev(case["scales"]))
     x = _dev(case["x"])
-    t = timer.run(lambda i: hum.linear(desc, packed, x), iters)
+    import torch
+    o = torch.empty((16, 512), dtype=torch.bfloat16, device="cuda")
+    ws = hum.Workspace("cuda").get(hum.linear_workspace_bytes(desc, 16))
+    t = timer.run(lambda i: hum.linear(desc, packed, x, out=o, workspace=ws), iters)
     wbytes = 512 * 1024 // 2 + 512 * 8 * 2
     return [{"m": 16, "us": t * 1e6, "tflops": 2 * 16 * 512 * 1024 / t / 1e12, "weight_gbs": wbytes / t / 1e9,
              "bound": "latency", "frac": wbytes / t / HBM_PEAK}]
@@ -247,10 +277,19 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
+    if args.copy_probe:
+        torch.cuda.set_device(0)
+        src = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "launches": 5}))
+        return
     import quantized_gemm_packed_amd as hum
     hum.load_library()
     torch.cuda.set_device(0)
-    timer = Timer()
+    timer = Timer(eager=args.eager)
     iters = args.iters
     d = dense_w4a16_sweep(hum, timer, iters)
     # timed steps
@@ -267,7 +306,7 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": dom["tflops"], "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s",
         "frac": dom["tflops"] * 1e12 / BF16_PEAK, "traffic": traffic_for(src_hash),
-        "kernel": f"gemm_kernel F_INT m={dom['m']} tile={dom['tile']}", "flops_per_launch": dom_flops,
+        "kernel": f"tile_kernel F_INT m={dom['m']} tile={dom['tile']} (+ rowsum_kernel)", "flops_per_launch": dom_flops,
         "us_per_launch": dom["us"],
     }
     sweep = {"dense_w4a16_uint4_zp_g128_n8192_k8192": d["res"]}

@@ -180,12 +180,12 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     c.kind = HUM_KERNEL_TILE;
     c.waves_n = 4;
     c.waves_k = 1;
-    c.wave_n = 4;
-    if (m <= 32) c.wave_m = 2;
-    else if (m <= 64) c.wave_m = 4;
-    else c.wave_m = 4;
+    // 2 sub-tiles per wave: with 3 K-blocks of LDS in flight, 64 x 128
+    // tiles keep two workgroups per CU (measured best from M = 64 to 4096)
+    c.wave_n = 2;
+    c.wave_m = m <= 128 ? 2 : 4;
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
-    c.split_k = pick_split(wgs, 4, kb, 1, 4, 4 * kCUs);
+    c.split_k = pick_split(wgs, 4, kb, 1, 4, 3 * kCUs);
   }
   c.block_m = (int32_t)tile_rows(c);
   return c;
@@ -404,8 +404,6 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ? 2 : 1);
   p.a_scale_bytes = desc->act_fmt == HUM_ACT_MXFP8 ? m * (desc->k / 32) : 0;
-  if (c.kind == HUM_KERNEL_STREAM && p.a_bytes >= ((int64_t)1 << 31))
-    return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: activations above 2 GiB");
   return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);
 }
 

@@ -140,6 +140,21 @@ __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe&
   return f;
 }
 
+// INT metadata words of one K-block of a stripe (zeros when !ok): the
+// scale dword and zero-point dword of column lane & 15.
+__device__ __forceinline__ BFrag<F_INT> load_b_meta_int(const GemmParams& p, const WStripe& s, bool ok, int kb,
+                                                        int lane) {
+  BFrag<F_INT> f;
+  const int c16 = lane & 15;
+  const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
+  const int sf = p.scale_f32;
+  const uint32_t so = ok ? (uint32_t)(gi * 16 + (c16 & (14 | sf))) << (1 + sf) : kOob;
+  f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
+  const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
+  f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
+  return f;
+}
+
 // Decoders of a fragment's metadata words.  The INT scale of column c16 is
 // (raw << sh) & mk: f32 scales sh = 0, mk = ~0; bf16 pairs take the low
 // half (sh = 16) for even columns and the high half (mk = 0xFFFF0000) for
@@ -758,36 +773,73 @@ __global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kern
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: 4 waves along N share a (16*WM)-row activation tile in LDS.
+// Prefill kernel: a (16 WM) x (64 WN) output tile per workgroup of 4 waves;
+// wave w owns columns [16 WN w, 16 WN (w + 1)) of the tile for all its rows.
+//
+// Every K-block's operands go from global memory straight into LDS by
+// LDS-DMA, kS - 1 K-blocks ahead of their use: the activation tile (16 WM
+// rows, 16-byte chunks XOR-swizzled with the row) with the INT row sums or
+// MXFP8 scale words of its rows, each wave's weight-code fragments (1 KB per
+// sub-tile, lane-linear, as packed) and its metadata words (INT scale and
+// zero-point dwords, or E8M0 rows).  Each pipeline stage lives in its own
+// LDS arrays, so the compiler can tell which DMA a read depends on and
+// waits for exactly that one.  A K-block step is: issue the DMA of K-block
+// j + kS - 1, compute K-block j from LDS, wait for this wave's own DMA of
+// K-block j + 1, barrier.  Registers hold only the current fragments and
+// the accumulators.
 
 template <int FMT, int WM, int WN, int AMODE, int EPI>
 struct TileCfg {
   using T = Tr<FMT>;
+  static constexpr int kS = 3;                                   // pipeline stages
   static constexpr int kTM = 16 * WM;
-  static constexpr int kTNS = 4 * WN;  // weight sub-tiles per workgroup
-  static constexpr int kRowB = 128 * T::kAElem;
-  static constexpr int kCPR = kRowB / 16;
-  static constexpr int kStageA = kTM * kRowB;
-  static constexpr int kStageX = (FMT == F_INT || FMT == F_MXFP4_MXFP8) ? kTM * 4 : 0;  // row sums / scales
-  static constexpr int kStage = kStageA + kStageX;
-  static constexpr int kChunks = kTM * kCPR;
-  static constexpr int kCPT = (kChunks + 255) / 256;
+  static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
+  static constexpr int kRowB = 128 * T::kAElem;                  // activation bytes per row per K-block
+  static constexpr int kCPR = kRowB / 16;                        // 16-byte chunks per row
+  static constexpr int kA = kTM * kRowB;                         // activation tile (whole KB)
+  static constexpr int kAI = kA / 1024;                          // its 1-KB DMA instructions
+  static constexpr int kAIW = (kAI + 3) / 4;                     // ... per wave
+  static constexpr bool kX = (FMT == F_INT || FMT == F_MXFP4_MXFP8);  // a dword per row (sum / MX scales)
+  static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
+  static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
+  static constexpr int kB = kTNS * kCB;
+  static constexpr int kMI = (FMT == F_INT) ? 2 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
+  static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
+  static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
   static_assert(EPI != EPI_SWIGLU_MXFP8 || WN % 4 == 0, "32-column MXFP8 blocks");
-  static_assert(2 * kStage <= 160 * 1024, "LDS budget");
+  static_assert(kA % 1024 == 0, "whole 1-KB activation DMA instructions");
+  static_assert(kS * kStage <= 160 * 1024, "LDS budget");
+  static_assert(FMT != F_INT || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
 };
 
 __device__ __forceinline__ int swz(int r, int c, int a_elem) {
   return a_elem == 2 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
+// LDS of one pipeline stage: one object per stage (the compiler tells LDS
+// DMA targets apart per object, and only a few of them), holding the
+// activation tile, the per-row words, the code fragments and the metadata
+// words at fixed offsets.
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
+struct TileStage {
+  using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
+  static __device__ __forceinline__ uint8_t* base() {
+    __shared__ __attribute__((aligned(16))) uint8_t v[C::kStage];
+    return v;
+  }
+  static __device__ __forceinline__ uint8_t* a() { return base(); }
+  static __device__ __forceinline__ uint8_t* x() { return base() + C::kA; }
+  static __device__ __forceinline__ uint8_t* b() { return base() + C::kA + C::kXI * 256; }
+  static __device__ __forceinline__ uint8_t* m() { return base() + C::kA + C::kXI * 256 + C::kB; }
+};
+
 template <int FMT, int WM, int WN, int AMODE, int EPI>
 __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
   using T = typename C::T;
   constexpr int kAE = T::kAElem;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -814,7 +866,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   WPtrs wp;
   wp.codes = p.codes + (int64_t)expert * p.codes_per_expert;
   wp.meta = p.wscale + (int64_t)expert * p.scales_per_expert;
-  // without zero points the (unused) zero loads read the scale array
+  // without zero points the (unused) zero words come from the scale array
   wp.zero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : wp.meta;
   const float gs = p.gscale[expert];
 
@@ -837,84 +889,141 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   if (kb_end > p.kb_count) kb_end = p.kb_count;
   const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
 
-  // staging chunks of this thread
-  const uint8_t* a_row[C::kCPT];
-  int ch_off[C::kCPT], ch_col[C::kCPT];
-  bool ch_ok[C::kCPT], a_ok_[C::kCPT];
-#pragma unroll
-  for (int i = 0; i < C::kCPT; ++i) {
-    const int id = tid + 256 * i;
-    ch_ok[i] = (C::kChunks % 256 == 0) || id < C::kChunks;  // compile-time true for full tiles
-    const int r = (id / C::kCPR) % C::kTM, c = id % C::kCPR;
-    ch_col[i] = c;
-    ch_off[i] = r * C::kRowB + swz(r, c, kAE) * 16;
+  // --- DMA sources (every lane always gets a valid address: rows past the
+  // end or padding read row 0 / slot 0, whose outputs are never stored) ---
+  auto src_row = [&](int r) -> int64_t {
     const int64_t row = row0 + r;
-    const uint8_t* src = nullptr;
-    if (ch_ok[i]) {
-      if (AMODE == A_GATHER) {
-        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-        if (f < p.sentinel) src = static_cast<const uint8_t*>(p.a) + (int64_t)(f / p.topk) * p.lda * kAE;
-      } else if (row < p.m) {
-        src = static_cast<const uint8_t*>(p.a) + row * p.lda * kAE;
-      }
+    if (AMODE == A_GATHER) {
+      const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
+      return f < p.sentinel ? (int64_t)(f / p.topk) : 0;
     }
-    a_row[i] = src;
-    a_ok_[i] = src != nullptr;
-    if (!src) a_row[i] = static_cast<const uint8_t*>(p.a);  // valid stand-in, zeroed by a select
+    return row < p.m ? row : 0;
+  };
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  uint32_t a_off[C::kAIW];  // activation chunk of this lane in each of the wave's instructions (K-block 0)
+  // (every wave issues kAIW instructions; with fewer than 4 in the tile,
+  // waves repeat one -- same bytes to the same place -- so that the count of
+  // DMAs in flight is the same on every path, which the compiler's waits
+  // rely on)
+#pragma unroll
+  for (int i = 0; i < C::kAIW; ++i) {
+    const int ins = (wn + 4 * i) % C::kAI;
+    const int slot = ins * 64 + lane;
+    const int r = slot / C::kCPR;
+    const int lc = swz(r, slot % C::kCPR, kAE);
+    a_off[i] = (uint32_t)(src_row(r) * p.lda * kAE + lc * 16);
   }
-  // per-row extra (INT row sums [m][kb_count] / MXFP8 scale dwords).  Every
-  // thread gets a valid address (row 0 stands in; zeroed by a select) since
-  // the load in load_a is unconditional; threads >= kTM never store it.
-  const uint8_t* x_row = nullptr;
-  bool x_ok = false;
-  if constexpr (FMT == F_INT || FMT == F_MXFP4_MXFP8) {
-    int64_t src = -1;
-    if (tid < C::kTM) {
-      const int64_t row = row0 + tid;
-      if (AMODE == A_GATHER) {
-        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-        if (f < p.sentinel) src = f / p.topk;
-      } else if (row < p.m) {
-        src = row;
-      }
+  __amdgpu_buffer_rsrc_t rx = ra;
+  uint32_t x_off[C::kXI > 0 ? C::kXI : 1];
+  if constexpr (C::kX) {
+    if (FMT == F_INT) rx = make_rsrc(p.a_rowsum, p.m * (int64_t)p.kb_count * 4);
+    else rx = make_rsrc(p.a_scale, p.a_scale_bytes);
+#pragma unroll
+    for (int i = 0; i < C::kXI; ++i) {
+      const int r = i * 64 + lane < C::kTM ? i * 64 + lane : 0;
+      const int64_t sr = src_row(r);
+      x_off[i] = (uint32_t)(FMT == F_INT ? sr * p.kb_count * 4 : sr * p.a_scale_ld);
     }
-    x_ok = src >= 0;
-    const int64_t r = x_ok ? src : 0;
-    if (FMT == F_INT) x_row = reinterpret_cast<const uint8_t*>(p.a_rowsum + r * p.kb_count);
-    else x_row = static_cast<const uint8_t*>(p.a_scale) + r * p.a_scale_ld;
+  }
+  __amdgpu_buffer_rsrc_t rb[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
+#pragma unroll
+  for (int ns = 0; ns < WN; ++ns) {
+    const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
+    rb[ns] = make_rsrc(wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb, cb);
+  }
+  // metadata words of the wave's sub-tiles, INT: lane l fetches scale dword
+  // l / WN (of 8 for bf16 scales, 16 for f32) and zero-point dword l / WN
+  // (of 2) of sub-tile l % WN, so that a lane finds its word of every
+  // sub-tile side by side (one vector read); MX: lane l its E8M0 word
+  __amdgpu_buffer_rsrc_t rms = ra;
+  const int sf = p.scale_f32;
+  // INT: 128 metadata dwords per wave and K-block, copied by two
+  // instructions (lane l of instruction i takes word 64 i + l): scale dword
+  // d of sub-tile s at word d * WN + s, then zero-point dword d of sub-tile
+  // s at word (8 << sf) * WN + d * WN + s -- a lane finds its word of every
+  // sub-tile side by side.  Scales and zero points both lie in the packed
+  // buffer, reached through one resource based at this expert's scales.
+  uint32_t mi_off[2] = {0, 0}, mi_gmul[2] = {0, 0};
+  if constexpr (FMT == F_INT) {
+    const int64_t zrel = wp.zero - wp.meta;  // >= 0: zero points follow the scales in the packed layout
+    rms = make_rsrc(wp.meta, p.wzero ? zrel + p.zeros_per_expert : p.scales_per_expert);
+    const int nsw = (8 << sf) * WN;  // scale words
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int w = 64 * i + lane;
+      const bool z = p.wzero && w >= nsw && w < nsw + 2 * WN;
+      const int ww = z ? w - nsw : (w < nsw ? w : 0);
+      const int sub = ww % WN, d = ww / WN;
+      const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
+      mi_off[i] = z ? (uint32_t)zrel + nt * p.ng * 8 + d * 4 : nt * p.ng * 16 * (2 << sf) + d * 4;
+      mi_gmul[i] = z ? 8u : 16u * (2u << sf);
+    }
+  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+    rms = make_rsrc(wp.meta, p.scales_per_expert);
   }
 
-  u32x4_t a_reg[C::kCPT];
-  uint32_t x_reg = 0;
-  auto load_a = [&](int kb) {
+  // DMA of K-block kb into stage St (this wave's share)
+  auto issue = [&](int kb, auto st) -> void {
+    using St = TileStage<FMT, WM, WN, AMODE, EPI, decltype(st)::value>;
 #pragma unroll
-    for (int i = 0; i < C::kCPT; ++i) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a_row[i] + (int64_t)kb * 128 * kAE + ch_col[i] * 16);
-      const u32x4_t z = {0, 0, 0, 0};
-      a_reg[i] = a_ok_[i] ? v : z;
+    for (int i = 0; i < C::kAIW; ++i) {
+      const int ins = (wn + 4 * i) % C::kAI;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, St::a() + ins * 1024, 16, a_off[i] + (uint32_t)kb * C::kRowB, 0, 0,
+                                               0);
     }
-    if constexpr (FMT == F_INT || FMT == F_MXFP4_MXFP8) {
-      const uint32_t xv = reinterpret_cast<const uint32_t*>(x_row)[kb];
-      x_reg = x_ok ? xv : ((FMT == F_INT) ? 0u : 0x7F7F7F7Fu);
+    // per-row words: every wave copies them all (same bytes, same place)
+    if constexpr (C::kX) {
+#pragma unroll
+      for (int i = 0; i < C::kXI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, St::x() + i * 256, 4, x_off[i] + (uint32_t)kb * 4, 0, 0, 0);
     }
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns)
+#pragma unroll
+      for (int h = 0; h < T::kBWords; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[ns], St::b() + (wn * WN + ns) * C::kCB + h * 1024, 16,
+                                                 (uint32_t)kb * C::kCB + h * 1024 + lane * 16, 0, 0, 0);
+    uint8_t* mw = St::m() + wn * C::kMI * 256;
+    if constexpr (FMT == F_INT) {
+      const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // (through a local: a captured array element handed to the LDS-DMA
+        // builtin trips the host compilation pass)
+        const uint32_t o = mi_off[i] + (uint32_t)gi * mi_gmul[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rms, mw + i * 256, 4, o, 0, 0, 0);
+      }
+    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) {
+        const uint32_t o = ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rms, mw + ns * 256, 4, o, 0, 0, 0);
+      }
+    }
+    // keep the issue ahead of the compute (the waits count on it)
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto store_a = [&](int buf) {
-    uint8_t* base = smem + buf * C::kStage;
-#pragma unroll
-    for (int i = 0; i < C::kCPT; ++i)
-      if (ch_ok[i]) *reinterpret_cast<u32x4_t*>(base + ch_off[i]) = a_reg[i];
-    if ((FMT == F_INT || FMT == F_MXFP4_MXFP8) && tid < C::kTM)
-      reinterpret_cast<uint32_t*>(base + C::kStageA)[tid] = x_reg;
+  // this wave's DMA into the next stage has landed: vector-memory loads
+  // complete in order, and after it the wave has issued only the DMA of the
+  // stage after (kIss instructions, the loop holds no other vector-memory
+  // access).  The wait is explicit: the compiler's own waits for LDS DMA
+  // follow its alias analysis, which loses track of some of these arrays.
+  constexpr int kIss = C::kAIW + C::kXI + WN * T::kBWords + C::kMI;
+  static_assert(kIss < 64, "vmcnt range");
+  auto wait_own = [&]() -> void {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((kIss & 15) | ((kIss >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_sched_barrier(0);
   };
-
-  WStripe st[WN];
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) st[ns] = make_stripe<FMT>(p, wp, nts[ns], ntv[ns]);
-  BFrag<FMT> bq[2][WN];
-  auto load_bs = [&](int kb, bool ok, auto set_c) {
-    constexpr int set = decltype(set_c)::value;
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) bq[set][ns] = load_b<FMT>(p, st[ns], ok, kb, lane);
+  // workgroup barrier without a memory fence (the fence of __syncthreads()
+  // would wait for every DMA in flight, prefetches included); the empty asm
+  // keeps the compiler from moving memory accesses across it
+  auto barrier = [&]() -> void {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
   };
 
   f32x4_t acc[WM][WN];
@@ -924,13 +1033,42 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const IntScaleSel ssel = int_scale_sel(p, c16);
-  auto compute = [&](int buf, int kb, auto set_c) {
-    constexpr int set = decltype(set_c)::value;
-    const uint8_t* abase = smem + buf * C::kStage;
+  auto compute = [&](int kb, auto st) -> void {
+    using St = TileStage<FMT, WM, WN, AMODE, EPI, decltype(st)::value>;
+    const uint8_t* abase = St::a();
+    const uint8_t* bbase = St::b() + wn * WN * C::kCB;
+    const uint8_t* mbase = St::m() + wn * C::kMI * 256;
+    BFrag<FMT> bf[WN];
+    uint32_t mw[WN], zw[WN];
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) {
+#pragma unroll
+      for (int h = 0; h < T::kBWords; ++h)
+        bf[ns].w[h] = *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
+      mw[ns] = 0;
+      zw[ns] = 0;
+      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)
+        mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
+    }
+    if constexpr (FMT == F_INT) {
+      // this lane's scale / zero-point words of the WN sub-tiles, side by
+      // side (single aligned reads: the compiler keeps their alias
+      // information, which split reads lose -- it would then wait for
+      // every DMA)
+      struct alignas(4 * WN) Words { uint32_t w[WN]; };
+      const Words sw = *reinterpret_cast<const Words*>(mbase + (sf ? c16 : (c16 >> 1)) * WN * 4);
+      const Words zv = *reinterpret_cast<const Words*>(mbase + ((8 << sf) + (c16 >> 3)) * WN * 4);
+      const uint32_t zmask = p.wzero ? ~0u : 0u;  // (a mask, not a select the compiler would turn into a branch)
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns) {
+        mw[ns] = sw.w[ns];
+        zw[ns] = zv.w[ns] & zmask;
+      }
+    }
     if constexpr (T::kBf16) {
       bf16x8_t d[WN][4];
 #pragma unroll
-      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bq[set][ns], bq[set][ns].meta, kb, d[ns]);
+      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bf[ns], mw[ns], kb, d[ns]);
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
         const int r = ms * 16 + c16;
@@ -939,12 +1077,12 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         for (int s = 0; s < 4; ++s)
           af[s] = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + (((4 * lg + s) ^ c16) * 16));
         if constexpr (FMT == F_INT) {
-          const f32x4_t rs = *reinterpret_cast<const f32x4_t*>(abase + C::kStageA + (ms * 16 + 4 * lg) * 4);
+          const f32x4_t rs = *reinterpret_cast<const f32x4_t*>(St::x() + (ms * 16 + 4 * lg) * 4);
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
             const f32x4_t t = mfma_bf16_kblock(af, d[ns], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-            const float sc = frag_int_scale(bq[set][ns].meta, ssel);
-            const float off = (float)(p.int_offset + frag_int_zero(bq[set][ns].zero, c16));
+            const float sc = frag_int_scale(mw[ns], ssel);
+            const float off = (float)(p.int_offset + frag_int_zero(zw[ns], c16));
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               acc[ms][ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ms][ns][i]);
@@ -965,42 +1103,47 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
         a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
         int sa = 127;
-        if (FMT == F_MXFP4_MXFP8)
-          sa = (int)((reinterpret_cast<const uint32_t*>(abase + C::kStageA)[r] >> (8 * lg)) & 0xFF);
+        if (FMT == F_MXFP4_MXFP8) sa = (int)((reinterpret_cast<const uint32_t*>(St::x())[r] >> (8 * lg)) & 0xFF);
 #pragma unroll
-        for (int ns = 0; ns < WN; ++ns)
-          acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bq[set][ns], bq[set][ns].meta, kb, acc[ms][ns]);
+        for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bf[ns], mw[ns], kb, acc[ms][ns]);
       }
     }
   };
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  // Prefetches are unconditional (a conditional load is waited on where the
-  // branch rejoins); past the last K-block the activation prefetch re-reads
-  // it (L2 hit, unused) and the weight prefetch reads nothing.
+  using I2 = std::integral_constant<int, 2>;
   if (nkb > 0) {
+    // K-block j uses stage j % 3
+    issue(kb_begin, I0{});
+    issue(nkb > 1 ? kb_begin + 1 : kb_begin, I1{});
+    wait_own();
+    barrier();
+    // The DMA is issued unconditionally (past the last K-block it re-reads
+    // that block into a stage that is never consumed): with a conditional
+    // issue the compiler could not count the DMAs in flight and would wait
+    // for all of them.
     const int kb_last = kb_begin + nkb - 1;
-    load_a(kb_begin);
-    load_bs(kb_begin, true, I0{});
-    store_a(0);
-    __syncthreads();
-    for (int j = 0; j < nkb; j += 2) {
-      const int k1 = kb_begin + j + 1 <= kb_last ? kb_begin + j + 1 : kb_last;
-      load_a(k1);
-      load_bs(k1, kb_begin + j + 1 <= kb_last, I1{});
-      compute(0, kb_begin + j, I0{});
-      store_a(1);
-      __syncthreads();
+    // (the three steps written out: a generic lambda calling these lambdas
+    // does not compile on the host side)
+    for (int j = 0; j < nkb; j += 3) {
+      issue(kb_begin + j + 2 <= kb_last ? kb_begin + j + 2 : kb_last, I2{});
+      compute(kb_begin + j, I0{});
+      if (j + 1 < nkb) wait_own();
+      barrier();
       if (j + 1 >= nkb) break;
-      const int k2 = kb_begin + j + 2 <= kb_last ? kb_begin + j + 2 : kb_last;
-      load_a(k2);
-      load_bs(k2, kb_begin + j + 2 <= kb_last, I0{});
-      compute(1, kb_begin + j + 1, I1{});
-      store_a(0);
-      __syncthreads();
+      issue(kb_begin + j + 3 <= kb_last ? kb_begin + j + 3 : kb_last, I0{});
+      compute(kb_begin + j + 1, I1{});
+      if (j + 2 < nkb) wait_own();
+      barrier();
+      if (j + 2 >= nkb) break;
+      issue(kb_begin + j + 4 <= kb_last ? kb_begin + j + 4 : kb_last, I1{});
+      compute(kb_begin + j + 2, I2{});
+      if (j + 3 < nkb) wait_own();
+      barrier();
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
 
   if (p.split_k > 1) {
     const int64_t ncols = C::kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
@@ -1238,6 +1381,13 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
   const int64_t grid = m_tiles * (int64_t)p.n_tiles * p.split_k;
   if (grid <= 0) return HUM_OK;
   if (grid > 0x7FFFFFFF) return set_error(HUM_ERR_UNSUPPORTED, "grid too large");
+  // buffer resources take 32-bit sizes and offsets
+  constexpr int64_t kRsrcMax = (int64_t)1 << 31;
+  if (p.a_bytes >= kRsrcMax || p.a_scale_bytes >= kRsrcMax)
+    return set_error(HUM_ERR_UNSUPPORTED, "activations above 2 GiB");
+  if (p.scales_per_expert >= kRsrcMax ||
+      (p.wzero && (int64_t)(p.wzero - p.wscale) + p.zeros_per_expert >= kRsrcMax))
+    return set_error(HUM_ERR_UNSUPPORTED, "weight metadata above 2 GiB");
   hipStream_t s = static_cast<hipStream_t>(stream);
   size_t dyn = 0;
   if (key.kind == KIND_STREAM) {

@@ -84,7 +84,7 @@ def test_selector_is_deterministic_and_covers_m_range(lib):
         kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m = c1
         assert split_k >= 1 and block_m == 16 * wave_m
         assert kind == (1 if m <= 16 else 0)
-        assert 16 * wave_m >= min(m, 64)
+        assert 16 * wave_m >= min(m, 32)
         seen.add(c1)
     assert len(seen) >= 3
 
