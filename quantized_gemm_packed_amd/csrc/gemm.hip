@@ -8,18 +8,20 @@
 //
 // Two kernel families share the fragment, MFMA and epilogue code below:
 //
-// * stream_kernel (decode, one 16-row tile): KW wave64s of a workgroup walk
-//   interleaved K-blocks of the same WN 16-column sub-tiles.  Weights stream
-//   from HBM straight into a register ring PF K-blocks deep (one 16-byte
-//   load per lane per sub-tile and K-block -- the packed layout puts exactly
-//   each lane's MFMA operand there); activation fragments come straight from
-//   global memory (they are small and stay in L2).  No barrier until the
-//   final in-workgroup reduction through LDS.
+// * stream_kernel (decode, one 16-row tile): KW wave64s of a workgroup split
+//   the K range of the same WN 16-column sub-tiles.  Weights stream from HBM
+//   straight into a register ring PF K-blocks deep (one 16-byte load per
+//   lane per sub-tile and K-block -- the packed layout puts exactly each
+//   lane's MFMA operand there); the activation rows and the weight metadata
+//   of the K range are staged in LDS once.  No barrier until the final
+//   in-workgroup reduction through LDS.
 // * tile_kernel (prefill): 4 waves side by side along N share a 16*WM-row
-//   activation tile staged through LDS (double buffered, XOR swizzled so the
-//   operand reads are conflict free); each wave dequantizes its own weight
-//   columns in registers.  Workgroups are ordered so that the tiles of one
-//   activation row block land on one XCD (shared L2).
+//   activation tile.  Each K-block's activation tile (XOR swizzled so the
+//   operand reads are conflict free), weight fragments and metadata are
+//   copied global -> LDS by buffer-load-to-LDS DMA, three K-blocks deep;
+//   each wave dequantizes its own weight columns from LDS into registers.
+//   Workgroups are ordered so that the tiles of one activation row block
+//   land on one XCD (shared L2).
 //
 // Formats:
 //   F_INT          INT4/UINT4 -> bf16 (128 + u) with one AND-OR per two
