@@ -398,6 +398,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.bias = static_cast<const uint16_t*>(bias);
   const int64_t m_tiles = cdiv(m, tile_rows(c));
   p.n_tiles = (int)cdiv(L.nt, tile_subtiles(c));
+  p.group_m = 8;  // 8 M-tiles x all N-tiles share one XCD's L2
   p.split_k = c.split_k;
   p.kb_per_split = kb_per_split(L.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);

@@ -90,6 +90,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same descriptor as four words, for LDS DMA issued from inline assembly.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
+}
+
+// LDS DMA (buffer_load ... lds): lane l's 16 (4) bytes at byte offset voff of
+// the buffer land at lds + 16 l (4 l).  Issued from inline assembly so that
+// the compiler keeps no count of it and adds no waits of its own for the
+// LDS it writes: the kernel waits itself (s_waitcnt vmcnt), knowing which
+// copies it needs.  The instruction has no register result, so nothing of
+// the asm statement is left in flight but the copy itself.
+__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
+}
+__device__ __forceinline__ void dma_b128(u32x4_t r, const void* lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(u32x4_t r, const void* lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr(lds)), "v"(voff), "s"(r) : "memory", "m0");
+}
+
 template <int FMT>
 __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs& w, int nt, bool valid) {
   constexpr int kCB = 16 * Tr<FMT>::kBWords;  // code bytes per lane per K-block
@@ -848,16 +872,27 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   const int c16 = lane & 15, lg = lane >> 4;
 
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
-  // XCDs; remap them so that each XCD walks a contiguous range of
-  // (m-tile, n-tile, split) tiles -- n fastest -- and reuses its activation
-  // rows from its own L2.
+  // XCDs; remap them so that each XCD walks a contiguous range of tiles.
+  // Within it, tiles go in groups of group_m M-tiles by all N-tiles, M
+  // fastest: the workgroups one XCD runs at a time then share both their
+  // activation rows and their weight columns through that XCD's L2.  (MoE
+  // M-tiles belong to different experts and take group_m = 1.)
   const uint32_t nwg = gridDim.x;
   uint32_t bid = blockIdx.x;
   if (nwg % 8 == 0) bid = (bid % 8) * (nwg / 8) + bid / 8;
   const int split = (int)(bid % (uint32_t)p.split_k);
   bid /= (uint32_t)p.split_k;
-  const int tn = (int)(bid % (uint32_t)p.n_tiles);
-  const int64_t tm = bid / (uint32_t)p.n_tiles;
+  int tn;
+  int64_t tm;
+  {
+    const uint32_t m_tiles = nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
+    const uint32_t per_group = (uint32_t)p.group_m * (uint32_t)p.n_tiles;
+    const uint32_t g = bid / per_group, r = bid % per_group;
+    const uint32_t m0 = g * (uint32_t)p.group_m;
+    const uint32_t gm = m_tiles - m0 < (uint32_t)p.group_m ? m_tiles - m0 : (uint32_t)p.group_m;
+    tm = m0 + r % gm;
+    tn = (int)(r / gm);
+  }
 
   int expert = 0;
   if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
@@ -901,7 +936,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     }
     return row < p.m ? row : 0;
   };
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  const u32x4_t ra = rsrc_words(p.a, p.a_bytes);
   uint32_t a_off[C::kAIW];  // activation chunk of this lane in each of the wave's instructions (K-block 0)
   // (every wave issues kAIW instructions; with fewer than 4 in the tile,
   // waves repeat one -- same bytes to the same place -- so that the count of
@@ -915,11 +950,11 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const int lc = swz(r, slot % C::kCPR, kAE);
     a_off[i] = (uint32_t)(src_row(r) * p.lda * kAE + lc * 16);
   }
-  __amdgpu_buffer_rsrc_t rx = ra;
+  u32x4_t rx = ra;
   uint32_t x_off[C::kXI > 0 ? C::kXI : 1];
   if constexpr (C::kX) {
-    if (FMT == F_INT) rx = make_rsrc(p.a_rowsum, p.m * (int64_t)p.kb_count * 4);
-    else rx = make_rsrc(p.a_scale, p.a_scale_bytes);
+    if (FMT == F_INT) rx = rsrc_words(p.a_rowsum, p.m * (int64_t)p.kb_count * 4);
+    else rx = rsrc_words(p.a_scale, p.a_scale_bytes);
 #pragma unroll
     for (int i = 0; i < C::kXI; ++i) {
       const int r = i * 64 + lane < C::kTM ? i * 64 + lane : 0;
@@ -927,17 +962,17 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       x_off[i] = (uint32_t)(FMT == F_INT ? sr * p.kb_count * 4 : sr * p.a_scale_ld);
     }
   }
-  __amdgpu_buffer_rsrc_t rb[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
+  u32x4_t rb[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) {
     const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
-    rb[ns] = make_rsrc(wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb, cb);
+    rb[ns] = rsrc_words(wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb, cb);
   }
   // metadata words of the wave's sub-tiles, INT: lane l fetches scale dword
   // l / WN (of 8 for bf16 scales, 16 for f32) and zero-point dword l / WN
   // (of 2) of sub-tile l % WN, so that a lane finds its word of every
   // sub-tile side by side (one vector read); MX: lane l its E8M0 word
-  __amdgpu_buffer_rsrc_t rms = ra;
+  u32x4_t rms = ra;
   const int sf = p.scale_f32;
   // INT: 128 metadata dwords per wave and K-block, copied by two
   // instructions (lane l of instruction i takes word 64 i + l): scale dword
@@ -948,7 +983,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   uint32_t mi_off[2] = {0, 0}, mi_gmul[2] = {0, 0};
   if constexpr (FMT == F_INT) {
     const int64_t zrel = wp.zero - wp.meta;  // >= 0: zero points follow the scales in the packed layout
-    rms = make_rsrc(wp.meta, p.wzero ? zrel + p.zeros_per_expert : p.scales_per_expert);
+    rms = rsrc_words(wp.meta, p.wzero ? zrel + p.zeros_per_expert : p.scales_per_expert);
     const int nsw = (8 << sf) * WN;  // scale words
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -961,7 +996,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       mi_gmul[i] = z ? 8u : 16u * (2u << sf);
     }
   } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
-    rms = make_rsrc(wp.meta, p.scales_per_expert);
+    rms = rsrc_words(wp.meta, p.scales_per_expert);
   }
 
   // DMA of K-block kb into stage St (this wave's share)
@@ -970,36 +1005,30 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < C::kAIW; ++i) {
       const int ins = (wn + 4 * i) % C::kAI;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, St::a() + ins * 1024, 16, a_off[i] + (uint32_t)kb * C::kRowB, 0, 0,
-                                               0);
+      dma_b128(ra, St::a() + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
     }
     // per-row words: every wave copies them all (same bytes, same place)
     if constexpr (C::kX) {
 #pragma unroll
       for (int i = 0; i < C::kXI; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, St::x() + i * 256, 4, x_off[i] + (uint32_t)kb * 4, 0, 0, 0);
+        dma_b32(rx, St::x() + i * 256, x_off[i] + (uint32_t)kb * 4);
     }
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns)
 #pragma unroll
       for (int h = 0; h < T::kBWords; ++h)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[ns], St::b() + (wn * WN + ns) * C::kCB + h * 1024, 16,
-                                                 (uint32_t)kb * C::kCB + h * 1024 + lane * 16, 0, 0, 0);
+        dma_b128(rb[ns], St::b() + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
     uint8_t* mw = St::m() + wn * C::kMI * 256;
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        // (through a local: a captured array element handed to the LDS-DMA
-        // builtin trips the host compilation pass)
-        const uint32_t o = mi_off[i] + (uint32_t)gi * mi_gmul[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rms, mw + i * 256, 4, o, 0, 0, 0);
+        dma_b32(rms, mw + i * 256, mi_off[i] + (uint32_t)gi * mi_gmul[i]);
       }
     } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
-        const uint32_t o = ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rms, mw + ns * 256, 4, o, 0, 0, 0);
+        dma_b32(rms, mw + ns * 256, ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4);
       }
     }
     // keep the issue ahead of the compute (the waits count on it)
@@ -1375,6 +1404,7 @@ bool gemm_instance_exists(const KernelKey& key) { return find_instance(key) != n
 
 hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_tiles, int block_m, void* stream) {
   GemmParams p = p_in;
+  if (p.group_m < 1) p.group_m = 1;
   const Instance* in = find_instance(key);
   if (!in)
     return set_error(HUM_ERR_UNSUPPORTED,

@@ -113,6 +113,7 @@ struct GemmParams {
   int split_k;
   int kb_per_split;
   int n_tiles;
+  int group_m;        // tile kernel: M-tiles walked together (M fastest) per N sweep
   int stream_rows;    // stream kernel: most valid rows of one 16-row tile
   // stream kernel LDS plan (bytes): weight metadata of sub-tile ns at
   // lds_meta_off + ns * lds_meta_stride, INT zero points lds_zero_off
