@@ -33,9 +33,15 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source flags.  The GEMM kernels keep MFMA results in ordinary VGPRs:
+# the INT path scales every K-block's MFMA result on the VALU, which reads
+# VGPRs only (AGPR results would cost one v_accvgpr_read per element).
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")

@@ -180,32 +180,67 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     c.kind = HUM_KERNEL_TILE;
     c.waves_n = 4;
     c.waves_k = 1;
-    // 2 sub-tiles per wave: with 3 K-blocks of LDS in flight, 64 x 128
-    // tiles keep two workgroups per CU (measured best from M = 64 to 4096)
-    c.wave_n = 2;
-    c.wave_m = m <= 128 ? 2 : 4;
+    // Measured on MI355X (dense N = K = 8192 and N = 7168, K = 2048): small
+    // tiles with split-K while the tile count is low; 64 x 256 tiles for
+    // bf16 activations from M = 512 (fewer LDS activation reads per MFMA);
+    // 128 x 128 / 64 x 128 for FP8 activations.
+    const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16;
+    int64_t target = 3 * kCUs;
+    if (m <= 256) {
+      c.wave_m = 2;
+      c.wave_n = 2;
+      if (bf16_act) target = 8 * kCUs;
+    } else if (bf16_act) {
+      c.wave_m = 4;
+      c.wave_n = m >= 512 ? 4 : 2;
+    } else {
+      c.wave_m = m <= 2048 ? 8 : 4;
+      c.wave_n = 2;
+    }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
-    c.split_k = pick_split(wgs, 4, kb, 1, 4, 3 * kCUs);
+    c.split_k = pick_split(wgs, 4, kb, 1, 4, target);
   }
   c.block_m = (int32_t)tile_rows(c);
   return c;
 }
 
-static hum_tile_config select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
+// The gate_up and down GEMMs of a MoE layer may run different kernels; they
+// share the expert block size (one align).
+struct MoeCfg {
+  hum_tile_config up, dn;
+};
+
+static hum_tile_config moe_stream_cfg() {
   hum_tile_config c{};
-  const double rows = (double)t * topk / w13->num_experts;
-  c.wave_n = 4;
-  c.split_k = 1;
-  if (rows <= 16) {
-    c.kind = HUM_KERNEL_STREAM;
-    c.wave_m = 1; c.waves_n = 1; c.waves_k = 8;
-  } else {
-    c.kind = HUM_KERNEL_TILE;
-    c.waves_n = 4; c.waves_k = 1;
-    c.wave_m = rows <= 48 ? 2 : 4;
-  }
+  c.kind = HUM_KERNEL_STREAM;
+  c.wave_m = 1; c.wave_n = 4; c.waves_n = 1; c.waves_k = 8; c.split_k = 1;
   c.block_m = (int32_t)tile_rows(c);
   return c;
+}
+
+static hum_tile_config moe_tile_cfg(int wm) {
+  hum_tile_config c{};
+  c.kind = HUM_KERNEL_TILE;
+  c.wave_m = wm; c.wave_n = 4; c.waves_n = 4; c.waves_k = 1; c.split_k = 1;
+  c.block_m = (int32_t)tile_rows(c);
+  return c;
+}
+
+// Measured on MI355X (E = 128, top-8, H = 4096, I = 1024) over the mean
+// rows per expert: the decode kernel only while most experts see at most a
+// row or two (it reads each weight once, but its bf16 path is VALU heavy);
+// 16-row tiles up to ~100 rows, larger tiles beyond.
+static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
+  const double rows = (double)t * topk / w13->num_experts;
+  if (fmt_of(w13) != F_MXFP4_MXFP8) {
+    if (rows < 0.5) return {moe_stream_cfg(), moe_stream_cfg()};
+    const int wm = rows <= 96 ? 1 : (rows <= 192 ? 2 : 4);
+    return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
+  }
+  if (rows <= 2) return {moe_stream_cfg(), moe_stream_cfg()};
+  if (rows <= 16) return {moe_stream_cfg(), moe_tile_cfg(1)};
+  const int wm = rows <= 256 ? 2 : 4;
+  return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
 }
 
 static void log_cfg(const char* what, const hum_tile_config& c, int64_t m) {
@@ -423,10 +458,11 @@ struct MoeWs {
 };
 
 static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
-                    const hum_tile_config& c) {
+                    const MoeCfg& mc) {
   MoeWs w;
   const int64_t E = w13->num_experts;
-  const int64_t bm = tile_rows(c);
+  const int64_t bm = tile_rows(mc.up);
+  const int split = mc.up.split_k > mc.dn.split_k ? mc.up.split_k : mc.dn.split_k;
   const int64_t inter = w2->k;
   const int64_t h = w13->k;
   w.cap = t * topk + E * (bm - 1);
@@ -435,7 +471,7 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   const int64_t pcols = (2 * inter > cdiv(h, kNSub) * kNSub) ? 2 * inter : cdiv(h, kNSub) * kNSub;
   int64_t off = 0;
   w.partials = off;
-  if (c.split_k > 1) off = align256(off + (int64_t)c.split_k * w.cap * pcols * 4);
+  if (split > 1) off = align256(off + (int64_t)split * w.cap * pcols * 4);
   w.sorted = off;
   off = align256(off + w.cap * 4);
   w.offsets = off;
@@ -485,8 +521,8 @@ size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_d
                                   const hum_tile_config* cfg) {
   clear_error();
   if (check_moe(w13, w2, t, topk) != HUM_OK) return 0;
-  const hum_tile_config c = cfg ? *cfg : select_moe(w13, t, topk);
-  return (size_t)moe_ws(w13, w2, t, topk, c).total;
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+  return (size_t)moe_ws(w13, w2, t, topk, mc).total;
 }
 
 size_t hum_moe_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk) {
@@ -521,23 +557,27 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   if (t == 0) return HUM_OK;
   if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
     return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
-  const hum_tile_config c = cfg ? *cfg : select_moe(w13, t, topk);
-  if (!cfg_sane(c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+  const hum_tile_config& cu = mc.up;
+  const hum_tile_config& cd = mc.dn;
+  if (!cfg_sane(cu) || !cfg_sane(cd) || tile_rows(cu) != tile_rows(cd))
+    return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
   const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
-  KernelKey kup{f, c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_GATHER, epi_up};
-  KernelKey kdn{f, c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_SCATTER};
+  KernelKey kup{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up};
+  KernelKey kdn{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER};
   if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
-  const MoeWs w = moe_ws(w13, w2, t, topk, c);
+  const MoeWs w = moe_ws(w13, w2, t, topk, mc);
   if (!workspace || ws_bytes < (size_t)w.total)
     return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
-  log_cfg("moe", c, t);
+  log_cfg("moe up", cu, t);
+  log_cfg("moe down", cd, t);
   Layout L13, L2;
   compute_layout(w13, &L13);
   compute_layout(w2, &L2);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t E = w13->num_experts, h = w13->k, inter = w2->k;
-  const int32_t bm = (int32_t)tile_rows(c);
+  const int32_t bm = (int32_t)tile_rows(cu);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
   st = launch_align(topk_ids, t, topk, (int32_t)E, bm, sorted, reinterpret_cast<int32_t*>(ws + w.offsets),
@@ -568,9 +608,9 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   p.ldo = inter;
   p.out_scale = mx ? ws + w.inter_s : nullptr;
   p.bias = nullptr;
-  p.n_tiles = (int)cdiv(cdiv(inter, kNSub), tile_subtiles(c) / 2);
-  p.split_k = c.split_k;
-  p.kb_per_split = kb_per_split(L13.kb, c);
+  p.n_tiles = (int)cdiv(cdiv(inter, kNSub), tile_subtiles(cu) / 2);
+  p.split_k = cu.split_k;
+  p.kb_per_split = kb_per_split(L13.kb, cu);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
   // upper bound of the valid rows of one expert block (any routing, also
   // repeated ids within a token): the LDS staging is sized for it
@@ -596,9 +636,9 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.ldo = h;
   q.out_scale = nullptr;
   q.bias = nullptr;
-  q.n_tiles = (int)cdiv(L2.nt, tile_subtiles(c));
-  q.split_k = c.split_k;
-  q.kb_per_split = kb_per_split(L2.kb, c);
+  q.n_tiles = (int)cdiv(L2.nt, tile_subtiles(cd));
+  q.split_k = cd.split_k;
+  q.kb_per_split = kb_per_split(L2.kb, cd);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
   q.stream_rows = p.stream_rows;  // valid (non-padding) rows of a block
   q.a_bytes = w.cap * inter * (mx ? 1 : 2);

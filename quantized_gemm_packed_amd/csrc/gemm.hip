@@ -807,17 +807,23 @@ __global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kern
 // rows, 16-byte chunks XOR-swizzled with the row) with the INT row sums or
 // MXFP8 scale words of its rows, each wave's weight-code fragments (1 KB per
 // sub-tile, lane-linear, as packed) and its metadata words (INT scale and
-// zero-point dwords, or E8M0 rows).  Each pipeline stage lives in its own
-// LDS arrays, so the compiler can tell which DMA a read depends on and
-// waits for exactly that one.  A K-block step is: issue the DMA of K-block
-// j + kS - 1, compute K-block j from LDS, wait for this wave's own DMA of
-// K-block j + 1, barrier.  Registers hold only the current fragments and
-// the accumulators.
+// zero-point dwords, or E8M0 rows).  Each pipeline stage is one LDS array.
+// The copies are issued from inline assembly, which the compiler does not
+// track, and the kernel waits for them itself.  A K-block step is: issue
+// the copies of K-block j + kS - 1, compute K-block j from LDS, wait until
+// this wave's copies of K-block j + 1 have landed (with three stages the
+// copies of K-block j + 2 stay in flight), barrier.  Registers hold only the
+// current fragments and the accumulators.
 
 template <int FMT, int WM, int WN, int AMODE, int EPI>
 struct TileCfg {
   using T = Tr<FMT>;
-  static constexpr int kS = 3;                                   // pipeline stages
+#ifndef HUM_TILE_STAGES
+#define HUM_TILE_STAGES 2
+#endif
+  // pipeline stages (2 or 3): with two, a K-block's copy overlaps one
+  // K-block of compute, and twice as many tiles fit the LDS of a CU
+  static constexpr int kS = HUM_TILE_STAGES;
   static constexpr int kTM = 16 * WM;
   static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
   static constexpr int kRowB = 128 * T::kAElem;                  // activation bytes per row per K-block
@@ -1041,9 +1047,10 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   // follow its alias analysis, which loses track of some of these arrays.
   constexpr int kIss = C::kAIW + C::kXI + WN * T::kBWords + C::kMI;
   static_assert(kIss < 64, "vmcnt range");
+  constexpr int kAhead = C::kS == 3 ? kIss : 0;  // DMAs left in flight after the wait
   auto wait_own = [&]() -> void {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((kIss & 15) | ((kIss >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4) | (15 << 8));
     __builtin_amdgcn_sched_barrier(0);
   };
   // workgroup barrier without a memory fence (the fence of __syncthreads()
@@ -1145,33 +1152,49 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   if (nkb > 0) {
-    // K-block j uses stage j % 3
-    issue(kb_begin, I0{});
-    issue(nkb > 1 ? kb_begin + 1 : kb_begin, I1{});
-    wait_own();
-    barrier();
-    // The DMA is issued unconditionally (past the last K-block it re-reads
-    // that block into a stage that is never consumed): with a conditional
-    // issue the compiler could not count the DMAs in flight and would wait
-    // for all of them.
+    // K-block j uses stage j % kS.  The DMA is issued unconditionally (past
+    // the last K-block it re-reads that block into a stage that is never
+    // consumed): the count of DMAs in flight is then the same on every path.
     const int kb_last = kb_begin + nkb - 1;
-    // (the three steps written out: a generic lambda calling these lambdas
-    // does not compile on the host side)
-    for (int j = 0; j < nkb; j += 3) {
-      issue(kb_begin + j + 2 <= kb_last ? kb_begin + j + 2 : kb_last, I2{});
-      compute(kb_begin + j, I0{});
-      if (j + 1 < nkb) wait_own();
+    auto kb_at = [&](int j) -> int { return kb_begin + j <= kb_last ? kb_begin + j : kb_last; };
+    // (the steps written out: a generic lambda calling these lambdas does
+    // not compile on the host side)
+    if constexpr (C::kS == 3) {
+      issue(kb_at(0), I0{});
+      issue(kb_at(1), I1{});
+      wait_own();
       barrier();
-      if (j + 1 >= nkb) break;
-      issue(kb_begin + j + 3 <= kb_last ? kb_begin + j + 3 : kb_last, I0{});
-      compute(kb_begin + j + 1, I1{});
-      if (j + 2 < nkb) wait_own();
+      for (int j = 0; j < nkb; j += 3) {
+        issue(kb_at(j + 2), I2{});
+        compute(kb_begin + j, I0{});
+        if (j + 1 < nkb) wait_own();
+        barrier();
+        if (j + 1 >= nkb) break;
+        issue(kb_at(j + 3), I0{});
+        compute(kb_begin + j + 1, I1{});
+        if (j + 2 < nkb) wait_own();
+        barrier();
+        if (j + 2 >= nkb) break;
+        issue(kb_at(j + 4), I1{});
+        compute(kb_begin + j + 2, I2{});
+        if (j + 3 < nkb) wait_own();
+        barrier();
+      }
+    } else {
+      issue(kb_at(0), I0{});
+      wait_own();
       barrier();
-      if (j + 2 >= nkb) break;
-      issue(kb_begin + j + 4 <= kb_last ? kb_begin + j + 4 : kb_last, I1{});
-      compute(kb_begin + j + 2, I2{});
-      if (j + 3 < nkb) wait_own();
-      barrier();
+      for (int j = 0; j < nkb; j += 2) {
+        issue(kb_at(j + 1), I1{});
+        compute(kb_begin + j, I0{});
+        if (j + 1 < nkb) wait_own();
+        barrier();
+        if (j + 1 >= nkb) break;
+        issue(kb_at(j + 2), I0{});
+        compute(kb_begin + j + 1, I1{});
+        if (j + 2 < nkb) wait_own();
+        barrier();
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS

@@ -140,3 +140,19 @@ def test_moe_single_expert_equals_dense_chain():
     chain = hum.linear(d2, p2, a)
     torch.cuda.synchronize()
     assert_tol(out, chain.float().cpu().numpy().astype(np.float64), "E=1 vs dense chain")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("t", [1, 16, 100, 500, 1200])
+def test_moe_default_selection_every_regime(act, t):
+    """The selector's choices over the rows-per-expert range (decode kernel,
+    16-row tiles, decode gate_up with a tiled down GEMM, larger tiles)."""
+    e, h, inter, k = 8, 256, 128, 2
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(740, e, h, inter, act)
+    ids, wts = synth.routing(741 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(742 + t), (t, h))
+    print(f"case moe default act={act} t={t}", flush=True)
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"default act={act} t={t}")
