@@ -93,6 +93,8 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
     L->scale_f32 = d->scale_dtype == HUM_F32;
     L->scales_per_expert = align256(L->nt * L->ng * 16 * (L->scale_f32 ? 4 : 2));
     L->zeros_per_expert = d->has_zero_point ? align256(L->nt * L->ng * 8) : 0;
+    L->kbc = cdiv(L->kb, 32);
+    L->co_per_expert = L->nt * L->kbc * 1024 * 2;
   } else if (f == F_FP8) {
     L->ng = 1;
     L->scales_per_expert = align256(L->nt * 16 * 4);
@@ -104,7 +106,8 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   L->codes_off = 0;
   L->scales_off = align256(E * L->codes_per_expert);
   L->zeros_off = align256(L->scales_off + E * L->scales_per_expert);
-  L->gscale_off = align256(L->zeros_off + E * L->zeros_per_expert);
+  L->co_off = align256(L->zeros_off + E * L->zeros_per_expert);
+  L->gscale_off = align256(L->co_off + E * L->co_per_expert);
   L->total = align256(L->gscale_off + E * 4);
   return HUM_OK;
 }
@@ -274,7 +277,7 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
     off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 ? m * (d->k / 32) : m * 4));
   }
   w.rowsum = off;
-  if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + m * (d->k / kKBlk) * 4);
+  if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
   w.total = off;
   return w;
 }
@@ -379,6 +382,9 @@ static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const La
   p.n = d->n;
   p.swiglu_nt_off = 0;
   p.a_rowsum = nullptr;
+  p.wco = pk + L.co_off;
+  p.co_per_expert = L.co_per_expert;
+  p.kbc = (int)L.kbc;
 }
 
 
@@ -414,9 +420,9 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   GemmParams p{};
   fill_weight_params(p, desc, L, packed);
   if (fmt_of(desc) == F_INT && c.kind == HUM_KERNEL_TILE) {
-    st = launch_rowsum(a_use, desc->k, m, (int)L.kb, reinterpret_cast<float*>(ws + w.rowsum), stream);
+    st = launch_rowsum(a_use, desc->k, m, (int)L.kb, (int)L.kbc, ws + w.rowsum, stream);
     if (st != HUM_OK) return st;
-    p.a_rowsum = reinterpret_cast<const float*>(ws + w.rowsum);
+    p.a_rowsum = ws + w.rowsum;
   }
   p.a = a_use;
   p.lda = desc->k;

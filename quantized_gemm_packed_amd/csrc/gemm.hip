@@ -831,11 +831,11 @@ struct TileCfg {
   static constexpr int kA = kTM * kRowB;                         // activation tile (whole KB)
   static constexpr int kAI = kA / 1024;                          // its 1-KB DMA instructions
   static constexpr int kAIW = (kAI + 3) / 4;                     // ... per wave
-  static constexpr bool kX = (FMT == F_INT || FMT == F_MXFP4_MXFP8);  // a dword per row (sum / MX scales)
+  static constexpr bool kX = (FMT == F_MXFP4_MXFP8);           // a dword per row (MX scales)
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
   static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
   static constexpr int kB = kTNS * kCB;
-  static constexpr int kMI = (FMT == F_INT) ? 2 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
+  static constexpr int kMI = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
@@ -959,13 +959,12 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   u32x4_t rx = ra;
   uint32_t x_off[C::kXI > 0 ? C::kXI : 1];
   if constexpr (C::kX) {
-    if (FMT == F_INT) rx = rsrc_words(p.a_rowsum, p.m * (int64_t)p.kb_count * 4);
-    else rx = rsrc_words(p.a_scale, p.a_scale_bytes);
+    rx = rsrc_words(p.a_scale, p.a_scale_bytes);
 #pragma unroll
     for (int i = 0; i < C::kXI; ++i) {
       const int r = i * 64 + lane < C::kTM ? i * 64 + lane : 0;
       const int64_t sr = src_row(r);
-      x_off[i] = (uint32_t)(FMT == F_INT ? sr * p.kb_count * 4 : sr * p.a_scale_ld);
+      x_off[i] = (uint32_t)(sr * p.a_scale_ld);
     }
   }
   u32x4_t rb[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
@@ -974,33 +973,22 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
     rb[ns] = rsrc_words(wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb, cb);
   }
-  // metadata words of the wave's sub-tiles, INT: lane l fetches scale dword
-  // l / WN (of 8 for bf16 scales, 16 for f32) and zero-point dword l / WN
-  // (of 2) of sub-tile l % WN, so that a lane finds its word of every
-  // sub-tile side by side (one vector read); MX: lane l its E8M0 word
+  // metadata words of the wave's sub-tiles.  INT: one copy per K-block, lane
+  // l takes scale dword l / WN (of 8 for bf16 scales, 16 for f32) of
+  // sub-tile l % WN, so that a lane finds its word of every sub-tile side by
+  // side (one vector read).  (Zero points enter through the offset terms
+  // after the K loop.)  MX: lane l its E8M0 word of each sub-tile.
   u32x4_t rms = ra;
   const int sf = p.scale_f32;
-  // INT: 128 metadata dwords per wave and K-block, copied by two
-  // instructions (lane l of instruction i takes word 64 i + l): scale dword
-  // d of sub-tile s at word d * WN + s, then zero-point dword d of sub-tile
-  // s at word (8 << sf) * WN + d * WN + s -- a lane finds its word of every
-  // sub-tile side by side.  Scales and zero points both lie in the packed
-  // buffer, reached through one resource based at this expert's scales.
-  uint32_t mi_off[2] = {0, 0}, mi_gmul[2] = {0, 0};
+  uint32_t mi_off = 0, mi_gmul = 0;
   if constexpr (FMT == F_INT) {
-    const int64_t zrel = wp.zero - wp.meta;  // >= 0: zero points follow the scales in the packed layout
-    rms = rsrc_words(wp.meta, p.wzero ? zrel + p.zeros_per_expert : p.scales_per_expert);
-    const int nsw = (8 << sf) * WN;  // scale words
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int w = 64 * i + lane;
-      const bool z = p.wzero && w >= nsw && w < nsw + 2 * WN;
-      const int ww = z ? w - nsw : (w < nsw ? w : 0);
-      const int sub = ww % WN, d = ww / WN;
-      const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
-      mi_off[i] = z ? (uint32_t)zrel + nt * p.ng * 8 + d * 4 : nt * p.ng * 16 * (2 << sf) + d * 4;
-      mi_gmul[i] = z ? 8u : 16u * (2u << sf);
-    }
+    rms = rsrc_words(wp.meta, p.scales_per_expert);
+    const int nsw = (8 << sf) * WN;  // scale words (<= 64)
+    const int ww = lane < nsw ? lane : 0;
+    const int sub = ww % WN, d = ww / WN;
+    const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
+    mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
+    mi_gmul = 16u * (2u << sf);
   } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
   }
@@ -1027,10 +1015,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     uint8_t* mw = St::m() + wn * C::kMI * 256;
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        dma_b32(rms, mw + i * 256, mi_off[i] + (uint32_t)gi * mi_gmul[i]);
-      }
+      dma_b32(rms, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
@@ -1077,31 +1062,23 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const uint8_t* bbase = St::b() + wn * WN * C::kCB;
     const uint8_t* mbase = St::m() + wn * C::kMI * 256;
     BFrag<FMT> bf[WN];
-    uint32_t mw[WN], zw[WN];
+    uint32_t mw[WN];
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) {
 #pragma unroll
       for (int h = 0; h < T::kBWords; ++h)
         bf[ns].w[h] = *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
       mw[ns] = 0;
-      zw[ns] = 0;
       if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
     }
     if constexpr (FMT == F_INT) {
-      // this lane's scale / zero-point words of the WN sub-tiles, side by
-      // side (single aligned reads: the compiler keeps their alias
-      // information, which split reads lose -- it would then wait for
-      // every DMA)
+      // this lane's scale words of the WN sub-tiles, side by side (one
+      // aligned vector read)
       struct alignas(4 * WN) Words { uint32_t w[WN]; };
       const Words sw = *reinterpret_cast<const Words*>(mbase + (sf ? c16 : (c16 >> 1)) * WN * 4);
-      const Words zv = *reinterpret_cast<const Words*>(mbase + ((8 << sf) + (c16 >> 3)) * WN * 4);
-      const uint32_t zmask = p.wzero ? ~0u : 0u;  // (a mask, not a select the compiler would turn into a branch)
 #pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        mw[ns] = sw.w[ns];
-        zw[ns] = zv.w[ns] & zmask;
-      }
+      for (int ns = 0; ns < WN; ++ns) mw[ns] = sw.w[ns];
     }
     if constexpr (T::kBf16) {
       bf16x8_t d[WN][4];
@@ -1115,15 +1092,14 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         for (int s = 0; s < 4; ++s)
           af[s] = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + (((4 * lg + s) ^ c16) * 16));
         if constexpr (FMT == F_INT) {
-          const f32x4_t rs = *reinterpret_cast<const f32x4_t*>(St::x() + (ms * 16 + 4 * lg) * 4);
+          // one K-block of (128 + u) codes, scaled; the offset it carries
+          // is taken off after the K loop
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
             const f32x4_t t = mfma_bf16_kblock(af, d[ns], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
             const float sc = frag_int_scale(mw[ns], ssel);
-            const float off = (float)(p.int_offset + frag_int_zero(zw[ns], c16));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[ms][ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ms][ns][i]);
+            for (int i = 0; i < 4; ++i) acc[ms][ns][i] = __builtin_fmaf(sc, t[i], acc[ms][ns][i]);
           }
         } else {
 #pragma unroll
@@ -1198,6 +1174,44 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
+
+  if constexpr (FMT == F_INT) {
+    // The K loop summed s * (128 + u) a per K-block; the offset part,
+    // sum over K-blocks of s (offset + z) * (sum of the block's a), is one
+    // more small product, taken here on the MFMA: row sums (A) times the
+    // weight's offset terms (B, stored negated) with K running over
+    // K-blocks, each operand as a bf16 hi / lo pair (hi*hi + hi*lo + lo*hi).
+    // The first split adds the whole of it.
+    if (split == 0) {
+      const int64_t mt16 = (p.m + 15) / 16;
+      const int64_t rs_half = mt16 * p.kbc * 1024;
+      const int64_t co_half = (int64_t)p.nt_count * p.kbc * 1024;
+      const uint8_t* cob = p.wco + (int64_t)expert * p.co_per_expert;
+      for (int cc = 0; cc < p.kbc; ++cc) {
+        bf16x8_t ch[WN], cl[WN];
+#pragma unroll
+        for (int ns = 0; ns < WN; ++ns) {
+          const int64_t o = (((int64_t)(ntv[ns] ? nts[ns] : 0) * p.kbc + cc) * 64 + lane) * 16;
+          ch[ns] = *reinterpret_cast<const bf16x8_t*>(cob + o);
+          cl[ns] = *reinterpret_cast<const bf16x8_t*>(cob + co_half + o);
+        }
+#pragma unroll
+        for (int ms = 0; ms < WM; ++ms) {
+          const int64_t mt = row0 / 16 + ms;
+          if (mt >= mt16) break;  // rows past m: never stored
+          const int64_t o = ((mt * p.kbc + cc) * 64 + lane) * 16;
+          const bf16x8_t rh = *reinterpret_cast<const bf16x8_t*>(p.a_rowsum + o);
+          const bf16x8_t rl = *reinterpret_cast<const bf16x8_t*>(p.a_rowsum + rs_half + o);
+#pragma unroll
+          for (int ns = 0; ns < WN; ++ns) {
+            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, ch[ns], acc[ms][ns], 0, 0, 0);
+            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, cl[ns], acc[ms][ns], 0, 0, 0);
+            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, ch[ns], acc[ms][ns], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
 
   if (p.split_k > 1) {
     const int64_t ncols = C::kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
@@ -1304,31 +1318,43 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p, 
 }
 
 // ---------------------------------------------------------------------------
-// Row sums of bf16 activations per K-block (INT prefill correction term).
+// Row sums of bf16 activations per K-block (the INT prefill offset term), as
+// bf16 hi / lo pairs in the A-operand layout the tile kernel reads (rows
+// padded to 16, K-blocks to 32, with zeros).
 
 __global__ __launch_bounds__(256) void rowsum_kernel(const uint16_t* __restrict__ a, int64_t lda, int64_t m,
-                                                     int kb_count, float* __restrict__ out) {
-  // one DPP row of 16 lanes per (row, K-block): each lane sums 8 values
+                                                     int kb_count, int kbc, int64_t mt16,
+                                                     uint16_t* __restrict__ out) {
+  // one DPP row of 16 lanes per (row, K-block), K-blocks fastest: each lane
+  // sums 8 values
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t item = gid >> 4;
   const int c = (int)(gid & 15);
-  const bool ok = item < m * kb_count;
+  const int64_t kbp = (int64_t)kbc * 32;
+  const bool in = item < mt16 * 16 * kbp;
+  const int64_t row = in ? item / kbp : 0, kb = in ? item % kbp : 0;
   float s = 0.0f;
-  if (ok) {
-    const int64_t row = item / kb_count, kb = item % kb_count;
+  if (in && row < m && kb < kb_count) {
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + row * lda + kb * 128 + c * 8);
 #pragma unroll
     for (int q = 0; q < 4; ++q) s += bf16_bits_to_f32(v[q] & 0xFFFF) + bf16_bits_to_f32(v[q] >> 16);
   }
   s = row16_sum(s);
-  if (ok && c == 0) out[item] = s;
+  if (in && c == 0) {
+    const uint32_t hi = f32_to_bf16_bits(s);
+    const uint32_t lo = f32_to_bf16_bits(s - bf16_bits_to_f32(hi));
+    const int64_t idx = (((row >> 4) * kbc + (kb >> 5)) * 64 + (row & 15) + 16 * ((kb >> 3) & 3)) * 8 + (kb & 7);
+    out[idx] = (uint16_t)hi;
+    out[mt16 * kbc * 512 + idx] = (uint16_t)lo;
+  }
 }
 
-hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, float* out, void* stream) {
+hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, int kbc, uint8_t* out, void* stream) {
   if (m == 0) return HUM_OK;
-  const int64_t threads = m * kb_count * 16;
+  const int64_t mt16 = (m + 15) / 16;
+  const int64_t threads = mt16 * 16 * (int64_t)kbc * 32 * 16;
   rowsum_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(a), lda, m, kb_count, out);
+      static_cast<const uint16_t*>(a), lda, m, kb_count, kbc, mt16, reinterpret_cast<uint16_t*>(out));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "rowsum launch: %s", hipGetErrorString(err));
   return HUM_OK;

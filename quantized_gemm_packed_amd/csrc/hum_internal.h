@@ -22,6 +22,13 @@
 //                        dword of lane l is the E8M0 code of column c and
 //                        32-block lg of K-block 4*kb4 + i
 //           E4M3       : scales f32 [NT*16]
+//   offset terms (INT4 / UINT4 only): -s * (offset + z) per column and
+//           K-block, where offset + z is what the bf16 (128 + u) codes carry
+//           beyond the code's value (INT4: 136, UINT4: 128 + zero point).  As
+//           bf16 hi / lo pairs, [NT][KBC][64 lanes][8] hi then the same for
+//           lo, KBC = ceil(KB / 32): lane l = c + 16*lg holds K-blocks
+//           32*kbc + 8*lg + (0..7) of column c -- the B operand of a 16x16x32
+//           bf16 MFMA whose K runs over K-blocks.  (Zero past N and KB.)
 //   global scale : f32 [E] (1.0 when absent)
 #pragma once
 
@@ -40,7 +47,9 @@ struct Layout {
   int64_t codes_per_expert = 0;   // bytes
   int64_t scales_per_expert = 0;  // bytes
   int64_t zeros_per_expert = 0;   // bytes
-  int64_t codes_off = 0, scales_off = 0, zeros_off = 0, gscale_off = 0, total = 0;
+  int64_t kbc = 0;                // INT formats: K-block chunks of 32 (offset terms)
+  int64_t co_per_expert = 0;      // bytes of offset terms (hi and lo)
+  int64_t codes_off = 0, scales_off = 0, zeros_off = 0, co_off = 0, gscale_off = 0, total = 0;
   int code_bytes = 16;            // per lane per (nt, kb)
   int kb_per_group = 1;           // INT formats
   int scale_f32 = 0;              // INT formats: 1 = f32 scales, 0 = bf16
@@ -95,7 +104,15 @@ struct GemmParams {
   int64_t lda;        // elements (bytes for fp8)
   const void* a_scale;
   int64_t a_scale_ld; // MXFP8: scale bytes per row
-  const float* a_rowsum;  // INT tile kernel: activation sums per (row, K-block)
+  // INT tile kernel: activation sums per (row, K-block) as bf16 hi / lo
+  // pairs, [ceil(m/16)][kbc][64 lanes][8] hi then lo (lane l = r + 16*lg
+  // holds K-blocks 32*kbc + 8*lg + (0..7) of row r: the A operand of a
+  // 16x16x32 bf16 MFMA whose K runs over K-blocks), and the weight's offset
+  // terms in the matching B-operand layout
+  const uint8_t* a_rowsum;
+  const uint8_t* wco;
+  int64_t co_per_expert;
+  int kbc;
   int64_t a_bytes;        // bytes of the activation buffer (< 2 GiB for buffer loads)
   int64_t a_scale_bytes;  // bytes of the MXFP8 activation scale buffer
   int64_t m;          // rows (dense) / padded sorted length (MoE)
@@ -195,7 +212,7 @@ struct KernelKey {
 hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, int block_m,
                        void* stream);
 bool gemm_instance_exists(const KernelKey& key);
-hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, float* out,
+hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, int kbc, uint8_t* out,
                          void* stream);
 
 }  // namespace hum

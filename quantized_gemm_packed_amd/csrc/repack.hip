@@ -17,8 +17,9 @@ struct RepackArgs {
   uint8_t* packed;
   int64_t n, k;
   int64_t nt, kb, ng, kb4;
-  int64_t codes_off, scales_off, zeros_off, gscale_off;
-  int64_t codes_pe, scales_pe, zeros_pe;
+  int64_t codes_off, scales_off, zeros_off, co_off, gscale_off;
+  int64_t codes_pe, scales_pe, zeros_pe, co_pe;
+  int64_t kbc, kb_per_group;
   int64_t src_ng;      // scale columns per canonical row (K/G or 1)
   int64_t src_n;       // canonical scale rows per expert (N or 1)
   int num_experts;
@@ -115,6 +116,54 @@ __global__ void repack_int_meta_kernel(RepackArgs a) {
   }
 }
 
+// INT offset terms: one thread per (e, nt, kbc, lane) writes the 8 K-blocks
+// 32 kbc + 8 lg + j of column c as -s * (offset + z), split into a bf16
+// high part and the bf16 of the remainder.  s * (offset + z) is exact in
+// f32 for bf16 scales (at most 8 + 8 significant bits).
+__global__ void repack_int_co_kernel(RepackArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.num_experts * a.nt * a.kbc * 64;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  int64_t rest = tid >> 6;
+  const int64_t cc = rest % a.kbc;
+  rest /= a.kbc;
+  const int64_t nt = rest % a.nt;
+  const int64_t e = rest / a.nt;
+  const int c = lane & 15, lg = lane >> 4;
+  const int64_t n = nt * kNSub + c;
+  const float offset = (a.wdt == HUM_INT4) ? 136.0f : 128.0f;
+  u32x4_t hi, lo;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    float v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t kb = cc * 32 + 8 * lg + j + q;
+      v[q] = 0.0f;
+      if (n < a.n && kb < a.kb) {
+        const int64_t g = kb / a.kb_per_group;
+        const int64_t sr = (a.src_n == 1) ? 0 : n;
+        const int64_t sg = (a.src_ng == 1) ? 0 : g;
+        const int64_t sidx = (e * a.src_n + sr) * a.src_ng + sg;
+        const float sc = (a.scale_elem == 2) ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.scales)[sidx])
+                                             : reinterpret_cast<const float*>(a.scales)[sidx];
+        const float z = a.has_zero ? (float)(a.zeros[sidx] & 0xF) : 0.0f;
+        v[q] = -(sc * (offset + z));
+      }
+    }
+    const uint32_t h0 = f32_to_bf16_bits(v[0]), h1 = f32_to_bf16_bits(v[1]);
+    const uint32_t l0 = f32_to_bf16_bits(v[0] - bf16_bits_to_f32(h0));
+    const uint32_t l1 = f32_to_bf16_bits(v[1] - bf16_bits_to_f32(h1));
+    hi[j / 2] = h0 | (h1 << 16);
+    lo[j / 2] = l0 | (l1 << 16);
+  }
+  uint8_t* base = a.packed + a.co_off + e * a.co_pe;
+  const int64_t idx = ((nt * a.kbc + cc) * 64 + lane) * 16;
+  *reinterpret_cast<u32x4_t*>(base + idx) = hi;
+  *reinterpret_cast<u32x4_t*>(base + a.nt * a.kbc * 1024 + idx) = lo;
+}
+
 // MX meta: one thread per (e, nt, kb4, lane): E8M0 codes of 4 K-blocks.
 __global__ void repack_mx_meta_kernel(RepackArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -181,10 +230,14 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   a.codes_off = L.codes_off;
   a.scales_off = L.scales_off;
   a.zeros_off = L.zeros_off;
+  a.co_off = L.co_off;
   a.gscale_off = L.gscale_off;
   a.codes_pe = L.codes_per_expert;
   a.scales_pe = L.scales_per_expert;
   a.zeros_pe = L.zeros_per_expert;
+  a.co_pe = L.co_per_expert;
+  a.kbc = L.kbc;
+  a.kb_per_group = L.kb_per_group;
   a.src_n = (d->scale_gran == HUM_SCALE_TENSOR) ? 1 : d->n;
   a.src_ng = (d->scale_gran == HUM_SCALE_GROUP) ? d->k / d->group_size : 1;
   a.num_experts = d->num_experts;
@@ -199,6 +252,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   const int f = fmt_of(d);
   if (f == F_INT) {
     repack_int_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.ng, B), B, 0, s>>>(a);
+    repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
   } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else {

@@ -29,7 +29,10 @@ def test_packed_size_dense_int4(lib):
     codes = 8192 * 8192 // 2
     scales = 8192 * 64 * 2
     zeros = 8192 * 64 // 2
-    assert codes + scales + zeros <= nb <= codes + scales + zeros + 4096
+    # per column and K-block, the offset term as a bf16 hi / lo pair (K-blocks
+    # padded to 32)
+    offsets = 8192 * 64 * 4
+    assert codes + scales + zeros + offsets <= nb <= codes + scales + zeros + offsets + 4096
 
 
 def test_packed_size_ragged_n_pads_to_16(lib):
