@@ -186,7 +186,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     // Measured on MI355X (dense N = K = 8192 and N = 7168, K = 2048): small
     // tiles with split-K while the tile count is low; 64 x 256 tiles for
     // bf16 activations from M = 512 (fewer LDS activation reads per MFMA);
-    // 128 x 128 / 64 x 128 for FP8 activations.
+    // 128 x 128 for FP8 activations.
     const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16;
     int64_t target = 3 * kCUs;
     if (m <= 256) {
@@ -197,7 +197,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       c.wave_m = 4;
       c.wave_n = m >= 512 ? 4 : 2;
     } else {
-      c.wave_m = m <= 2048 ? 8 : 4;
+      c.wave_m = 8;
       c.wave_n = 2;
     }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));

@@ -25,11 +25,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// E8M0 code -> float 2^(c-127); 255 -> NaN.
+// E8M0 code -> float 2^(c-127); 255 -> NaN.  Branch free: code 0 is the
+// subnormal 2^-127 (mantissa bit 22 alone), code 255 the quiet NaN
+// (all-ones exponent and mantissa bit 22).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
-  if (c == 0) return __uint_as_float(0x00400000u);  // 2^-127 (subnormal)
-  if (c == 255) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float(c << 23);
+  const uint32_t edge = (((c + 1u) & 0xFFu) <= 1u) ? 0x00400000u : 0u;
+  return __uint_as_float((c << 23) | edge);
 }
 
 // Two floats -> two E4M3 codes (RNE, saturated to +-448, signed zero kept).

@@ -850,21 +850,20 @@ __device__ __forceinline__ int swz(int r, int c, int a_elem) {
   return a_elem == 2 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
-// LDS of one pipeline stage: one object per stage (the compiler tells LDS
-// DMA targets apart per object, and only a few of them), holding the
+// LDS of the pipeline: kS stages of kStage bytes, each holding the
 // activation tile, the per-row words, the code fragments and the metadata
 // words at fixed offsets.
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
-struct TileStage {
+template <int FMT, int WM, int WN, int AMODE, int EPI>
+struct TileLds {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
   static __device__ __forceinline__ uint8_t* base() {
-    __shared__ __attribute__((aligned(16))) uint8_t v[C::kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
     return v;
   }
-  static __device__ __forceinline__ uint8_t* a() { return base(); }
-  static __device__ __forceinline__ uint8_t* x() { return base() + C::kA; }
-  static __device__ __forceinline__ uint8_t* b() { return base() + C::kA + C::kXI * 256; }
-  static __device__ __forceinline__ uint8_t* m() { return base() + C::kA + C::kXI * 256 + C::kB; }
+  static __device__ __forceinline__ uint8_t* a(int st) { return base() + st * C::kStage; }
+  static __device__ __forceinline__ uint8_t* x(int st) { return a(st) + C::kA; }
+  static __device__ __forceinline__ uint8_t* b(int st) { return a(st) + C::kA + C::kXI * 256; }
+  static __device__ __forceinline__ uint8_t* m(int st) { return a(st) + C::kA + C::kXI * 256 + C::kB; }
 };
 
 template <int FMT, int WM, int WN, int AMODE, int EPI>
@@ -994,25 +993,25 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   }
 
   // DMA of K-block kb into stage St (this wave's share)
-  auto issue = [&](int kb, auto st) -> void {
-    using St = TileStage<FMT, WM, WN, AMODE, EPI, decltype(st)::value>;
+  using St = TileLds<FMT, WM, WN, AMODE, EPI>;
+  auto issue = [&](int kb, int st) -> void {
 #pragma unroll
     for (int i = 0; i < C::kAIW; ++i) {
       const int ins = (wn + 4 * i) % C::kAI;
-      dma_b128(ra, St::a() + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
+      dma_b128(ra, St::a(st) + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
     }
     // per-row words: every wave copies them all (same bytes, same place)
     if constexpr (C::kX) {
 #pragma unroll
       for (int i = 0; i < C::kXI; ++i)
-        dma_b32(rx, St::x() + i * 256, x_off[i] + (uint32_t)kb * 4);
+        dma_b32(rx, St::x(st) + i * 256, x_off[i] + (uint32_t)kb * 4);
     }
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns)
 #pragma unroll
       for (int h = 0; h < T::kBWords; ++h)
-        dma_b128(rb[ns], St::b() + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
-    uint8_t* mw = St::m() + wn * C::kMI * 256;
+        dma_b128(rb[ns], St::b(st) + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
+    uint8_t* mw = St::m(st) + wn * C::kMI * 256;
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
       dma_b32(rms, mw, mi_off + (uint32_t)gi * mi_gmul);
@@ -1056,11 +1055,10 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const IntScaleSel ssel = int_scale_sel(p, c16);
-  auto compute = [&](int kb, auto st) -> void {
-    using St = TileStage<FMT, WM, WN, AMODE, EPI, decltype(st)::value>;
-    const uint8_t* abase = St::a();
-    const uint8_t* bbase = St::b() + wn * WN * C::kCB;
-    const uint8_t* mbase = St::m() + wn * C::kMI * 256;
+  auto compute = [&](int kb, int st) -> void {
+    const uint8_t* abase = St::a(st);
+    const uint8_t* bbase = St::b(st) + wn * WN * C::kCB;
+    const uint8_t* mbase = St::m(st) + wn * C::kMI * 256;
     BFrag<FMT> bf[WN];
     uint32_t mw[WN];
 #pragma unroll
@@ -1117,60 +1115,33 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
         a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
         int sa = 127;
-        if (FMT == F_MXFP4_MXFP8) sa = (int)((reinterpret_cast<const uint32_t*>(St::x())[r] >> (8 * lg)) & 0xFF);
+        if (FMT == F_MXFP4_MXFP8) sa = (int)((reinterpret_cast<const uint32_t*>(St::x(st))[r] >> (8 * lg)) & 0xFF);
 #pragma unroll
         for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bf[ns], mw[ns], kb, acc[ms][ns]);
       }
     }
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
   if (nkb > 0) {
-    // K-block j uses stage j % kS.  The DMA is issued unconditionally (past
+    // K-block j uses stage j % kS.  The copy is issued unconditionally (past
     // the last K-block it re-reads that block into a stage that is never
-    // consumed): the count of DMAs in flight is then the same on every path.
+    // consumed): the count of copies in flight is then the same on every
+    // path, which the explicit waits rely on.  One loop body for every stage
+    // keeps the accumulators in the same registers across iterations.
     const int kb_last = kb_begin + nkb - 1;
     auto kb_at = [&](int j) -> int { return kb_begin + j <= kb_last ? kb_begin + j : kb_last; };
-    // (the steps written out: a generic lambda calling these lambdas does
-    // not compile on the host side)
-    if constexpr (C::kS == 3) {
-      issue(kb_at(0), I0{});
-      issue(kb_at(1), I1{});
+#pragma unroll
+    for (int j = 0; j < C::kS - 1; ++j) issue(kb_at(j), j);
+    wait_own();
+    barrier();
+    int st = 0, st_ahead = C::kS - 1;
+    for (int j = 0; j < nkb; ++j) {
+      issue(kb_at(j + C::kS - 1), st_ahead);
+      compute(kb_begin + j, st);
       wait_own();
       barrier();
-      for (int j = 0; j < nkb; j += 3) {
-        issue(kb_at(j + 2), I2{});
-        compute(kb_begin + j, I0{});
-        if (j + 1 < nkb) wait_own();
-        barrier();
-        if (j + 1 >= nkb) break;
-        issue(kb_at(j + 3), I0{});
-        compute(kb_begin + j + 1, I1{});
-        if (j + 2 < nkb) wait_own();
-        barrier();
-        if (j + 2 >= nkb) break;
-        issue(kb_at(j + 4), I1{});
-        compute(kb_begin + j + 2, I2{});
-        if (j + 3 < nkb) wait_own();
-        barrier();
-      }
-    } else {
-      issue(kb_at(0), I0{});
-      wait_own();
-      barrier();
-      for (int j = 0; j < nkb; j += 2) {
-        issue(kb_at(j + 1), I1{});
-        compute(kb_begin + j, I0{});
-        if (j + 1 < nkb) wait_own();
-        barrier();
-        if (j + 1 >= nkb) break;
-        issue(kb_at(j + 2), I0{});
-        compute(kb_begin + j + 1, I1{});
-        if (j + 2 < nkb) wait_own();
-        barrier();
-      }
+      st = st + 1 == C::kS ? 0 : st + 1;
+      st_ahead = st_ahead + 1 == C::kS ? 0 : st_ahead + 1;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
