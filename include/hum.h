@@ -93,6 +93,8 @@ typedef struct hum_tile_config {
   int32_t waves_k;   /* waves of a workgroup splitting K (in-WG split-K) */
   int32_t split_k;   /* workgroups splitting K (fp32 partials + reduce kernel) */
   int32_t block_m;   /* rows per workgroup tile = MoE expert block (16*wave_m) */
+  int32_t stages;    /* tile kernel: K-blocks of operands staged in LDS at once
+                        (2 or 3; 0 = 2); ignored by the stream kernel */
 } hum_tile_config;
 
 /* ---- weight preparation ------------------------------------------------ */

@@ -117,14 +117,18 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
 
 static const int kCUs = 256;
 
+static int key_stages(const hum_tile_config& c) {
+  return c.kind == HUM_KERNEL_TILE ? (c.stages == 0 ? 2 : c.stages) : 0;
+}
+
 static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
-  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16};
+  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16, key_stages(c)};
 }
 
 static bool cfg_sane(const hum_tile_config& c) {
   if (c.split_k < 1 || c.split_k > 64 || c.wave_m < 1 || c.wave_n < 1) return false;
   if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 15;
-  if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1;
+  if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1 && (c.stages == 0 || c.stages == 2 || c.stages == 3);
   return false;
 }
 
@@ -192,6 +196,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     if (m <= 256) {
       c.wave_m = 2;
       c.wave_n = 2;
+      c.stages = 3;  // small tiles: room in LDS for a deeper pipeline
       if (bf16_act) target = 8 * kCUs;
     } else if (bf16_act) {
       c.wave_m = 4;
@@ -570,8 +575,8 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
   const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
-  KernelKey kup{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up};
-  KernelKey kdn{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER};
+  KernelKey kup{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
+  KernelKey kdn{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
   if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const MoeWs w = moe_ws(w13, w2, t, topk, mc);
   if (!workspace || ws_bytes < (size_t)w.total)

@@ -815,15 +815,13 @@ __global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kern
 // copies of K-block j + 2 stay in flight), barrier.  Registers hold only the
 // current fragments and the accumulators.
 
-template <int FMT, int WM, int WN, int AMODE, int EPI>
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 struct TileCfg {
   using T = Tr<FMT>;
-#ifndef HUM_TILE_STAGES
-#define HUM_TILE_STAGES 2
-#endif
   // pipeline stages (2 or 3): with two, a K-block's copy overlaps one
-  // K-block of compute, and twice as many tiles fit the LDS of a CU
-  static constexpr int kS = HUM_TILE_STAGES;
+  // K-block of compute and twice as many tiles fit the LDS of a CU; with
+  // three it has two K-blocks of compute to land
+  static constexpr int kS = S;
   static constexpr int kTM = 16 * WM;
   static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
   static constexpr int kRowB = 128 * T::kAElem;                  // activation bytes per row per K-block
@@ -853,9 +851,9 @@ __device__ __forceinline__ int swz(int r, int c, int a_elem) {
 // LDS of the pipeline: kS stages of kStage bytes, each holding the
 // activation tile, the per-row words, the code fragments and the metadata
 // words at fixed offsets.
-template <int FMT, int WM, int WN, int AMODE, int EPI>
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 struct TileLds {
-  using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
+  using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
   static __device__ __forceinline__ uint8_t* base() {
     __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
     return v;
@@ -866,9 +864,9 @@ struct TileLds {
   static __device__ __forceinline__ uint8_t* m(int st) { return a(st) + C::kA + C::kXI * 256 + C::kB; }
 };
 
-template <int FMT, int WM, int WN, int AMODE, int EPI>
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
-  using C = TileCfg<FMT, WM, WN, AMODE, EPI>;
+  using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
   using T = typename C::T;
   constexpr int kAE = T::kAElem;
 
@@ -993,7 +991,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   }
 
   // DMA of K-block kb into stage St (this wave's share)
-  using St = TileLds<FMT, WM, WN, AMODE, EPI>;
+  using St = TileLds<FMT, WM, WN, AMODE, EPI, S>;
   auto issue = [&](int kb, int st) -> void {
 #pragma unroll
     for (int i = 0; i < C::kAIW; ++i) {
@@ -1344,9 +1342,10 @@ struct Instance {
 };
 
 #define HUM_STREAM(F, WN, KW, PF, AM, EP) \
-  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(KW, AM, EP)}
-#define HUM_TILE(F, WM, WN, AM, EP) \
-  {{F, KIND_TILE, WM, WN, 4, 1, AM, EP}, tile_kernel<F, WM, WN, AM, EP>, 256}
+  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP, 0}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(KW, AM, EP)}
+#define HUM_TILE_S(F, WM, WN, AM, EP, S) \
+  {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
+#define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
 
 // Ring depth in 1-KB weight fragments per sub-tile (FP8 fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.
@@ -1365,7 +1364,12 @@ struct Instance {
   HUM_TILE(F, 4, 2, A_DIRECT, EPI_BF16),                   \
   HUM_TILE(F, 4, 4, A_DIRECT, EPI_BF16),                   \
   HUM_TILE(F, 8, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16)
+  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE_S(F, 2, 2, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 2, 4, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 4, 2, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
 
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
@@ -1414,7 +1418,7 @@ static const Instance* find_instance(const KernelKey& k) {
   for (const Instance& in : kInstances) {
     const KernelKey& q = in.key;
     if (q.fmt == k.fmt && q.kind == k.kind && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n &&
-        q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi)
+        q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi && q.stages == k.stages)
       return &in;
   }
   return nullptr;
@@ -1428,8 +1432,8 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
   const Instance* in = find_instance(key);
   if (!in)
     return set_error(HUM_ERR_UNSUPPORTED,
-                     "no GEMM instance fmt=%d kind=%d wm=%d wn=%d waves_n=%d waves_k=%d amode=%d epi=%d", key.fmt,
-                     key.kind, key.wm, key.wn, key.waves_n, key.waves_k, key.amode, key.epi);
+                     "no GEMM instance fmt=%d kind=%d wm=%d wn=%d waves_n=%d waves_k=%d amode=%d epi=%d stages=%d",
+                     key.fmt, key.kind, key.wm, key.wn, key.waves_n, key.waves_k, key.amode, key.epi, key.stages);
   const int64_t grid = m_tiles * (int64_t)p.n_tiles * p.split_k;
   if (grid <= 0) return HUM_OK;
   if (grid > 0x7FFFFFFF) return set_error(HUM_ERR_UNSUPPORTED, "grid too large");

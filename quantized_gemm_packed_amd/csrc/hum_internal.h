@@ -204,6 +204,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
 
 struct KernelKey {
   int fmt, kind, wm, wn, waves_n, waves_k, amode, epi;
+  int stages;  // tile kernel: LDS pipeline stages (2 or 3); 0 for the stream kernel
 };
 
 // Launches the GEMM kernel instance matching `key` (HUM_ERR_UNSUPPORTED if

@@ -84,7 +84,7 @@ def test_selector_is_deterministic_and_covers_m_range(lib):
         c1 = hum.select_config(d, m).as_tuple()
         c2 = hum.select_config(d, m).as_tuple()
         assert c1 == c2
-        kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m = c1
+        kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m, stages = c1
         assert split_k >= 1 and block_m == 16 * wave_m
         assert kind == (1 if m <= 16 else 0)
         assert 16 * wave_m >= min(m, 32)

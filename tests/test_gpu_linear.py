@@ -17,17 +17,19 @@ from gpu_util import assert_bf16_exact, assert_tol, descs, dev, prepare
 
 pytestmark = pytest.mark.gpu
 
-# (kind, wave_m, wave_n, waves_n, waves_k): every compiled dense instance
+# (kind, wave_m, wave_n, waves_n, waves_k[, stages]): every compiled dense instance
 STREAM_TILES = [(1, 1, 1, 1, 8), (1, 1, 2, 1, 8), (1, 1, 4, 1, 8), (1, 1, 1, 1, 4), (1, 1, 1, 1, 15), (1, 1, 2, 1, 15),
                 (1, 1, 4, 1, 15)]
 TILE_TILES = [(0, 1, 4, 4, 1), (0, 2, 2, 4, 1), (0, 2, 4, 4, 1), (0, 4, 2, 4, 1), (0, 4, 4, 4, 1),
-              (0, 8, 2, 4, 1), (0, 8, 4, 4, 1)]
+              (0, 8, 2, 4, 1), (0, 8, 4, 4, 1),
+              (0, 2, 2, 4, 1, 3), (0, 2, 4, 4, 1, 3), (0, 4, 2, 4, 1, 3), (0, 4, 4, 4, 1, 3), (0, 8, 2, 4, 1, 3)]
 DENSE_TILES = STREAM_TILES + TILE_TILES
 
 
 def cfg(t, split):
     c = hum.TileConfig()
-    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = t[:5]
+    c.stages = t[5] if len(t) > 5 else 0
     c.split_k = split
     c.block_m = 16 * t[1]
     return c
