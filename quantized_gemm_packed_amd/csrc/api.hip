@@ -179,8 +179,10 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     auto fits = [&](int split) {
       hum_tile_config t = c;
       t.split_k = split;
+      // (MXFP8 activations are staged by a loader wave, whole split at once)
       return lds(split) <= kStreamLdsDense &&
-             stream_self_stage_fits(fmt_of(d), (int)m, kb_per_split(kb, t), c.waves_k, L.kb_per_group, L.scale_f32);
+             (fmt_of(d) == F_MXFP4_MXFP8 ||
+              stream_self_stage_fits(fmt_of(d), (int)m, kb_per_split(kb, t), c.waves_k, L.kb_per_group, L.scale_f32));
     };
     while (c.split_k < 64 && !fits(c.split_k)) c.split_k *= 2;
   } else {

@@ -375,11 +375,16 @@ struct StreamLds {
 // Waves of a stream workgroup: KW compute waves, plus a loader wave where
 // the activation rows are gathered (MoE).  Dense workgroups stage their
 // activations wave by wave and need none.
-constexpr bool stream_self_staged(int amode, int epi) { return amode == A_DIRECT && epi == EPI_BF16; }
-constexpr int stream_waves(int kw, int amode, int epi) { return kw + (stream_self_staged(amode, epi) ? 0 : 1); }
+// (MXFP8 activations carry per-32 scales, which the loader wave stages.)
+constexpr bool stream_self_staged(int fmt, int amode, int epi) {
+  return amode == A_DIRECT && epi == EPI_BF16 && fmt != F_MXFP4_MXFP8;
+}
+constexpr int stream_waves(int fmt, int kw, int amode, int epi) {
+  return kw + (stream_self_staged(fmt, amode, epi) ? 0 : 1);
+}
 
 template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
-__global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
+__global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
   using T = Tr<FMT>;
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(64 * stream_waves(KW, AMODE, EPI)) void stream_kern
   int kb_end = kb_begin + p.kb_per_split;
   if (kb_end > p.kb_count) kb_end = p.kb_count;
   const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
-  constexpr bool kSelf = stream_self_staged(AMODE, EPI);
+  constexpr bool kSelf = stream_self_staged(FMT, AMODE, EPI);
   // Self-staged (dense) workgroups give compute wave w the contiguous
   // K-blocks [kw0, kw0 + nj); otherwise wave w takes kb_begin + w, + KW, ...
   // (wave KW, the loader, takes none).
@@ -1342,7 +1347,7 @@ struct Instance {
 };
 
 #define HUM_STREAM(F, WN, KW, PF, AM, EP) \
-  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP, 0}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(KW, AM, EP)}
+  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP, 0}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(F, KW, AM, EP)}
 #define HUM_TILE_S(F, WM, WN, AM, EP, S) \
   {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
 #define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
@@ -1389,6 +1394,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_INT),
     HUM_DENSE_SET(F_FP8),
     HUM_DENSE_SET(F_MXFP4_BF16),
+    HUM_DENSE_SET(F_MXFP4_MXFP8),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1408,6 +1414,7 @@ static const ReduceInstance kReduces[] = {
     {F_MXFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_BF16>},
     {F_MXFP4_BF16, EPI_SWIGLU_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SWIGLU_BF16>},
     {F_MXFP4_BF16, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SCATTER>},
+    {F_MXFP4_MXFP8, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };
@@ -1449,7 +1456,7 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
   if (key.kind == KIND_STREAM) {
     const StreamLdsPlan L = stream_lds_plan(key.fmt, p.stream_rows, p.kb_per_split, key.wn, p.kb_per_group,
                                             p.scale_f32, p.ng, p.kb4);
-    if (key.amode == A_DIRECT && key.epi == EPI_BF16 &&
+    if (stream_self_staged(key.fmt, key.amode, key.epi) &&
         !stream_self_stage_fits(key.fmt, p.stream_rows, p.kb_per_split, key.waves_k, p.kb_per_group, p.scale_f32))
       return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per wave too long (raise split_k)");
     p.lds_meta_off = (int)L.meta_off;

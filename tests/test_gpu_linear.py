@@ -104,6 +104,41 @@ def test_mxfp4_bf16_exact_every_tile(tile):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_mxfp4_mxfp8_exact_every_tile(tile):
+    """Dense W4A8: integer activations in [-8, 8] quantize to MXFP8 exactly
+    (shared exponent 2^-5, codes 32 x), E2M1 x E8M0 weights are exact, and
+    every partial sum is exact in fp32: bitwise equal to the oracle."""
+    m, n, k = rows_for(tile, 19), 96, 1024
+    g = synth.rng(34)
+    w = synth.quant_weights(34, "e2m1", "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp8")
+    packed = prepare(hd, w, "e8m0")
+    print(f"case w4a8 exact tile={tile}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    q, e = oracle.quant.quant_mxfp8(oracle.formats.decode_bf16(xb).astype(np.float32))
+    a = oracle.quant.dequant_mxfp8(q, e)
+    ref = oracle.gemm.linear(od, a, w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
+def test_w4a8_dense_random_vs_oracle(m):
+    """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
+    n, k = 640, 2048
+    w = synth.moe_weights_mxfp4(synth.seed_for(5, m), 1, n, k)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(5, 100 + m)), (m, k))
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp8")
+    packed = prepare(hd, w, "e8m0")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    q, e = oracle.quant.quant_mxfp8(oracle.formats.decode_bf16(xb).astype(np.float32))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_mxfp8(q, e), w["codes"], w["scales"])
+    assert_tol(out, ref, f"w4a8 m={m}")
+
+
 def test_workload_dense_int4_sym_g128_tiny():
     """Dense W4A16 INT4 symmetric G128, M=16 N=512 K=1024 (selector config)."""
     case = synth.dense_w4a16(synth.seed_for(1), 16, 512, 1024, group=128)
