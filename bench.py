@@ -225,7 +225,7 @@ def moe(hum, timer, iters, act):
     return out
 
 
-def cpu_baseline(case, budget_s=15.0):
+def cpu_baseline(case, budget_s=30.0):
     """Oracle (NumPy float64) on the host: the same M sweep restricted to a
     column sample of the weights."""
     import oracle
