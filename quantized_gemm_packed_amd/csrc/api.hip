@@ -158,33 +158,38 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
   if (m <= 16) {
-    // decode: one 16-row tile streamed by 8 waves; more sub-tiles per wave as
-    // m grows keeps the activation re-reads (L2) below the weight bytes.
+    // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
+    // wave: the fewest that keep the activation bytes each workgroup reads
+    // (from L2) at or below its weight bytes.  Four K-waves when their K
+    // ranges fit the self-staging limits without more split-K, else eight
+    // (measured on MI355X: INT M = 1, FP8 M = 1..16 run best on four).
     c.kind = HUM_KERNEL_STREAM;
     c.wave_m = 1;
-    c.wave_n = m <= 2 ? 1 : (m <= 8 ? 2 : 4);
     c.waves_n = 1;
-    c.waves_k = 8;
+    const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16;
+    const int64_t a_bytes = m * (bf16_act ? 2 : 1);            // per k
+    const int64_t w_bytes16 = fmt_of(d) == F_FP8 ? 16 : 8;      // per k of a 16-column sub-tile
+    const int64_t need = cdiv(a_bytes, w_bytes16);
+    c.wave_n = need <= 1 ? 1 : (need <= 2 ? 2 : 4);
     const int64_t wgs = cdiv(nt, c.wave_n);
-    c.split_k = pick_split(wgs, 8, kb, 8, 2, 16 * kCUs);
-    // the LDS plan of one split must fit the dense LDS budget
     Layout L;
     compute_layout(d, &L);
-    auto lds = [&](int split) {
-      hum_tile_config t = c;
-      t.split_k = split;
-      return stream_lds_plan(fmt_of(d), (int)m, kb_per_split(kb, t), c.wave_n, L.kb_per_group, L.scale_f32, L.ng,
-                             L.kb4).total;
-    };
-    auto fits = [&](int split) {
-      hum_tile_config t = c;
-      t.split_k = split;
+    auto fits = [&](const hum_tile_config& t) {
       // (MXFP8 activations are staged by a loader wave, whole split at once)
-      return lds(split) <= kStreamLdsDense &&
+      return stream_lds_plan(fmt_of(d), (int)m, kb_per_split(kb, t), t.wave_n, L.kb_per_group, L.scale_f32, L.ng,
+                             L.kb4).total <= kStreamLdsDense &&
              (fmt_of(d) == F_MXFP4_MXFP8 ||
-              stream_self_stage_fits(fmt_of(d), (int)m, kb_per_split(kb, t), c.waves_k, L.kb_per_group, L.scale_f32));
+              stream_self_stage_fits(fmt_of(d), (int)m, kb_per_split(kb, t), t.waves_k, L.kb_per_group, L.scale_f32));
     };
-    while (c.split_k < 64 && !fits(c.split_k)) c.split_k *= 2;
+    c.waves_k = 8;
+    c.split_k = pick_split(wgs, 8, kb, 8, 2, 16 * kCUs);
+    hum_tile_config c4 = c;
+    c4.waves_k = 4;
+    if (gemm_instance_exists(dense_key(d, c4)) && fits(c4)) {
+      c = c4;
+    } else {
+      while (c.split_k < 64 && !fits(c)) c.split_k *= 2;
+    }
   } else {
     c.kind = HUM_KERNEL_TILE;
     c.waves_n = 4;
