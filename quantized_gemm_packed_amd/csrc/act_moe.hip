@@ -142,6 +142,7 @@ hum_status launch_zero(void* p, size_t bytes, void* stream) {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 512;
+static_assert(kAlignThreads >= kMaxExperts, "one thread per expert in the offset scan");
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __restrict__ ids, int64_t n,
                                                               int32_t num_experts, int32_t block_m,
@@ -169,13 +170,26 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __r
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    off[0] = 0;
-    for (int e = 0; e < E; ++e) {
-      acc += (cnt[e] + block_m - 1) / block_m * block_m;
-      off[e + 1] = acc;
+  // padded segment sizes, exclusive scan over the experts: a shuffle scan
+  // inside each wave (64 experts), then the wave totals (at most 8 waves)
+  {
+    __shared__ int32_t wsum[kMaxExperts / 64];
+    const int e = tid;
+    int32_t v = 0;
+    if (e < E) v = (cnt[e] + block_m - 1) / block_m * block_m;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t u = __shfl_up(v, d);
+      if (lane >= d) v += u;
     }
+    if (e < kMaxExperts && lane == 63) wsum[wave] = v;
+    __syncthreads();
+    if (e < E) {
+      int32_t before = 0;
+      for (int w = 0; w < wave; ++w) before += wsum[w];
+      off[e + 1] = before + v;
+    }
+    if (tid == 0) off[0] = 0;
   }
   __syncthreads();
   for (int e = tid; e <= E; e += kAlignThreads) offsets[e] = off[e];
