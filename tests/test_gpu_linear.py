@@ -263,3 +263,25 @@ def test_repeat_runs_are_bitwise_identical():
     o2 = hum.linear(hd, packed, x)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e2m1_mxfp8"])
+def test_empty_m_is_a_no_op(fmt):
+    """M = 0: a valid call that writes nothing (every format's path)."""
+    n, k = 256, 512
+    if fmt == "uint4":
+        w = synth.quant_weights(50, "uint4", "group", 128, "bf16", 1, n, k, zero=True)
+        hd, _ = descs("uint4", "group", 128, "bf16", 1, n, k, zero=True)
+        packed = prepare(hd, w, "bf16")
+    elif fmt == "e4m3":
+        w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
+        hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+        packed = prepare(hd, w, "f32")
+    else:
+        w = synth.moe_weights_mxfp4(51, 1, n, k)
+        hd, _ = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp8")
+        packed = prepare(hd, w, "e8m0")
+    x = torch.empty((0, k), dtype=torch.bfloat16, device="cuda")
+    out = hum.linear(hd, packed, x)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, n)

@@ -156,3 +156,15 @@ def test_moe_default_selection_every_regime(act, t):
     torch.cuda.synchronize()
     ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
     assert_tol(out, ref, f"default act={act} t={t}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_moe_zero_tokens_is_a_no_op(act):
+    e, h, inter, k = 8, 256, 128, 2
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(750, e, h, inter, act)
+    x = torch.empty((0, h), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((0, k), dtype=torch.float32, device="cuda")
+    out = hum.moe_gemm(d13, p13, d2, p2, x, ids, wts)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, h)
