@@ -199,13 +199,16 @@ __device__ __forceinline__ int frag_int_zero(uint32_t raw, int c16) { return (in
 __device__ __forceinline__ uint32_t frag_mx_code(uint32_t raw, int kb) { return (raw >> (8 * (kb & 3))) & 0xFF; }
 
 // (x & mask) | magic in one instruction.  gfx9 encodes no literal in the
-// three-operand form, so the compiler would split it into two
-// literal-carrying ones; here the mask rides in an SGPR and the magic in a
-// VGPR.  ALU only.
+// three-operand form, so with the constants in sight the compiler would
+// split it into two literal-carrying ones.  The empty asm statements (they
+// emit nothing) hide the constants: the mask then rides in an SGPR and the
+// magic in a VGPR, and the operation stays ordinary compiler-scheduled code,
+// whose hazards against matrix instructions in flight the compiler tracks
+// (a VALU instruction written in asm is outside that tracking).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
-  return r;
+  asm("" : "+s"(mask));
+  asm("" : "+v"(magic));
+  return (x & mask) | magic;
 }
 
 __device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
@@ -837,7 +840,12 @@ struct TileCfg {
   static constexpr bool kX = (FMT == F_MXFP4_MXFP8);           // a dword per row (MX scales)
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
   static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
-  static constexpr int kB = kTNS * kCB;
+  // With two stages each wave loads its own weight fragments straight into
+  // registers, one K-block ahead (they are private to the wave: staging
+  // them through LDS would only add LDS traffic); with three they go
+  // through LDS like the rest.
+  static constexpr bool kBReg = (kS == 2);
+  static constexpr int kB = kBReg ? 0 : kTNS * kCB;
   static constexpr int kMI = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
@@ -863,10 +871,10 @@ struct TileLds {
     __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
     return v;
   }
-  static __device__ __forceinline__ uint8_t* a(int st) { return base() + st * C::kStage; }
+  static __device__ __forceinline__ uint8_t* m(int st) { return base() + st * C::kStage; }
+  static __device__ __forceinline__ uint8_t* a(int st) { return m(st) + C::kM; }
   static __device__ __forceinline__ uint8_t* x(int st) { return a(st) + C::kA; }
   static __device__ __forceinline__ uint8_t* b(int st) { return a(st) + C::kA + C::kXI * 256; }
-  static __device__ __forceinline__ uint8_t* m(int st) { return a(st) + C::kA + C::kXI * 256 + C::kB; }
 };
 
 template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
@@ -969,12 +977,17 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       x_off[i] = (uint32_t)(sr * p.a_scale_ld);
     }
   }
-  u32x4_t rb[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
+  u32x4_t rb[WN];                  // code stripes (invalid sub-tiles read sub-tile 0)
+  __amdgpu_buffer_rsrc_t rbr[WN];  // the same, for the register loads
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) {
     const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
-    rb[ns] = rsrc_words(wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb, cb);
+    const uint8_t* base = wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb;
+    rb[ns] = rsrc_words(base, cb);
+    rbr[ns] = make_rsrc(base, cb);
   }
+  // register-loaded fragments of even and odd K-blocks (two stages)
+  BFrag<FMT> bA[WN], bB[WN];
   // metadata words of the wave's sub-tiles.  INT: one copy per K-block, lane
   // l takes scale dword l / WN (of 8 for bf16 scales, 16 for f32) of
   // sub-tile l % WN, so that a lane finds its word of every sub-tile side by
@@ -997,7 +1010,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 
   // DMA of K-block kb into stage St (this wave's share)
   using St = TileLds<FMT, WM, WN, AMODE, EPI, S>;
-  auto issue = [&](int kb, int st) -> void {
+  auto issue = [&](int kb, int st, BFrag<FMT>* bdst) -> void {
 #pragma unroll
     for (int i = 0; i < C::kAIW; ++i) {
       const int ins = (wn + 4 * i) % C::kAI;
@@ -1009,11 +1022,26 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       for (int i = 0; i < C::kXI; ++i)
         dma_b32(rx, St::x(st) + i * 256, x_off[i] + (uint32_t)kb * 4);
     }
+    if constexpr (C::kBReg) {
+      // (compiler-tracked loads: the kernel's full wait at the end of the
+      // step covers them, so the compiler adds none before their use).  A
+      // lane's kBWords 16-byte words sit side by side in the packed layout.
+      const uint32_t boff = (uint32_t)kb * C::kCB + lane * 16 * T::kBWords;
 #pragma unroll
-    for (int ns = 0; ns < WN; ++ns)
+      for (int ns = 0; ns < WN; ++ns)
 #pragma unroll
-      for (int h = 0; h < T::kBWords; ++h)
-        dma_b128(rb[ns], St::b(st) + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
+        for (int h = 0; h < T::kBWords; ++h)
+          bdst[ns].w[h] = __builtin_amdgcn_raw_buffer_load_b128(rbr[ns], boff + h * 16, 0, 0);
+      // (the offset stays live past the loads: no load's destination
+      // reuses the register another load reads its address from)
+      asm volatile("" ::"v"(boff));
+    } else {
+#pragma unroll
+      for (int ns = 0; ns < WN; ++ns)
+#pragma unroll
+        for (int h = 0; h < T::kBWords; ++h)
+          dma_b128(rb[ns], St::b(st) + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
+    }
     uint8_t* mw = St::m(st) + wn * C::kMI * 256;
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
@@ -1032,7 +1060,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   // stage after (kIss instructions, the loop holds no other vector-memory
   // access).  The wait is explicit: the compiler's own waits for LDS DMA
   // follow its alias analysis, which loses track of some of these arrays.
-  constexpr int kIss = C::kAIW + C::kXI + WN * T::kBWords + C::kMI;
+  constexpr int kIss = C::kAIW + C::kXI + (C::kBReg ? 0 : WN * T::kBWords) + C::kMI;
   static_assert(kIss < 64, "vmcnt range");
   constexpr int kAhead = C::kS == 3 ? kIss : 0;  // DMAs left in flight after the wait
   auto wait_own = [&]() -> void {
@@ -1058,7 +1086,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const IntScaleSel ssel = int_scale_sel(p, c16);
-  auto compute = [&](int kb, int st) -> void {
+  auto compute = [&](int kb, int st, const BFrag<FMT>* bsrc) -> void {
     const uint8_t* abase = St::a(st);
     const uint8_t* bbase = St::b(st) + wn * WN * C::kCB;
     const uint8_t* mbase = St::m(st) + wn * C::kMI * 256;
@@ -1068,7 +1096,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     for (int ns = 0; ns < WN; ++ns) {
 #pragma unroll
       for (int h = 0; h < T::kBWords; ++h)
-        bf[ns].w[h] = *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
+        bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
+                               : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
       mw[ns] = 0;
       if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
@@ -1133,18 +1162,43 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     // keeps the accumulators in the same registers across iterations.
     const int kb_last = kb_begin + nkb - 1;
     auto kb_at = [&](int j) -> int { return kb_begin + j <= kb_last ? kb_begin + j : kb_last; };
-#pragma unroll
-    for (int j = 0; j < C::kS - 1; ++j) issue(kb_at(j), j);
-    wait_own();
-    barrier();
-    int st = 0, st_ahead = C::kS - 1;
-    for (int j = 0; j < nkb; ++j) {
-      issue(kb_at(j + C::kS - 1), st_ahead);
-      compute(kb_begin + j, st);
+    if constexpr (C::kS == 2) {
+      // two K-blocks per iteration, so that even and odd K-blocks keep
+      // their weight fragments in fixed registers; one exit
+      issue(kb_at(0), 0, bA);
       wait_own();
       barrier();
-      st = st + 1 == C::kS ? 0 : st + 1;
-      st_ahead = st_ahead + 1 == C::kS ? 0 : st_ahead + 1;
+      int j = 0;
+      for (; j + 1 < nkb; j += 2) {
+        issue(kb_at(j + 1), 1, bB);
+        compute(kb_begin + j, 0, bA);
+        wait_own();
+        barrier();
+        issue(kb_at(j + 2), 0, bA);
+        compute(kb_begin + j + 1, 1, bB);
+        wait_own();
+        barrier();
+      }
+      if (j < nkb) {
+        issue(kb_at(j + 1), 1, bB);
+        compute(kb_begin + j, 0, bA);
+        wait_own();
+        barrier();
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::kS - 1; ++j) issue(kb_at(j), j, bA);
+      wait_own();
+      barrier();
+      int st = 0, st_ahead = C::kS - 1;
+      for (int j = 0; j < nkb; ++j) {
+        issue(kb_at(j + C::kS - 1), st_ahead, bA);
+        compute(kb_begin + j, st, bA);
+        wait_own();
+        barrier();
+        st = st + 1 == C::kS ? 0 : st + 1;
+        st_ahead = st_ahead + 1 == C::kS ? 0 : st_ahead + 1;
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
