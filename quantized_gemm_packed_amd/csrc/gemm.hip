@@ -827,8 +827,7 @@ template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 struct TileCfg {
   using T = Tr<FMT>;
   // pipeline stages (2 or 3): with two, a K-block's copy overlaps one
-  // K-block of compute and twice as many tiles fit the LDS of a CU; with
-  // three it has two K-blocks of compute to land
+  // K-block of compute; with three it has two K-blocks of compute to land
   static constexpr int kS = S;
   static constexpr int kTM = 16 * WM;
   static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
@@ -840,12 +839,16 @@ struct TileCfg {
   static constexpr bool kX = (FMT == F_MXFP4_MXFP8);           // a dword per row (MX scales)
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
   static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
-  // With two stages each wave loads its own weight fragments straight into
-  // registers, one K-block ahead (they are private to the wave: staging
-  // them through LDS would only add LDS traffic); with three they go
-  // through LDS like the rest.
-  static constexpr bool kBReg = (kS == 2);
-  static constexpr int kB = kBReg ? 0 : kTNS * kCB;
+  // Each wave loads its own weight fragments straight into registers,
+  // kS - 1 K-blocks ahead, one register set per stage (they are private to
+  // the wave: staging them through LDS would only add LDS traffic).
+  static constexpr bool kBReg = true;
+  static constexpr int kB = 0;
+  // Three stages issue their LDS copies through the compiler's builtin, so
+  // that its count of loads in flight includes them and its waits for the
+  // register fragments (two stages deep) are exact; two stages issue them
+  // from inline assembly and wait for everything at the end of each step.
+  static constexpr bool kTracked = (kS == 3);
   static constexpr int kMI = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
@@ -867,11 +870,21 @@ __device__ __forceinline__ int swz(int r, int c, int a_elem) {
 template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 struct TileLds {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
-  static __device__ __forceinline__ uint8_t* base() {
-    __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
-    return v;
+  // (three stages: one array each, so that the compiler can tell a copy
+  // into one stage from a read of another and adds no wait between them;
+  // the stage is a constant wherever this is called)
+  static __device__ __forceinline__ uint8_t* stage(int st) {
+    if constexpr (C::kTracked) {
+      __shared__ __attribute__((aligned(16))) uint8_t s0[C::kStage];
+      __shared__ __attribute__((aligned(16))) uint8_t s1[C::kStage];
+      __shared__ __attribute__((aligned(16))) uint8_t s2[C::kStage];
+      return st == 0 ? s0 : (st == 1 ? s1 : s2);
+    } else {
+      __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
+      return v + st * C::kStage;
+    }
   }
-  static __device__ __forceinline__ uint8_t* m(int st) { return base() + st * C::kStage; }
+  static __device__ __forceinline__ uint8_t* m(int st) { return stage(st); }
   static __device__ __forceinline__ uint8_t* a(int st) { return m(st) + C::kM; }
   static __device__ __forceinline__ uint8_t* x(int st) { return a(st) + C::kA; }
   static __device__ __forceinline__ uint8_t* b(int st) { return a(st) + C::kA + C::kXI * 256; }
@@ -952,7 +965,10 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     }
     return row < p.m ? row : 0;
   };
+  // each buffer resource twice: as words for the inline-assembly copies and
+  // as the builtin's type for the tracked ones
   const u32x4_t ra = rsrc_words(p.a, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rar = make_rsrc(p.a, p.a_bytes);
   uint32_t a_off[C::kAIW];  // activation chunk of this lane in each of the wave's instructions (K-block 0)
   // (every wave issues kAIW instructions; with fewer than 4 in the tile,
   // waves repeat one -- same bytes to the same place -- so that the count of
@@ -967,9 +983,11 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     a_off[i] = (uint32_t)(src_row(r) * p.lda * kAE + lc * 16);
   }
   u32x4_t rx = ra;
+  __amdgpu_buffer_rsrc_t rxr = rar;
   uint32_t x_off[C::kXI > 0 ? C::kXI : 1];
   if constexpr (C::kX) {
     rx = rsrc_words(p.a_scale, p.a_scale_bytes);
+    rxr = make_rsrc(p.a_scale, p.a_scale_bytes);
 #pragma unroll
     for (int i = 0; i < C::kXI; ++i) {
       const int r = i * 64 + lane < C::kTM ? i * 64 + lane : 0;
@@ -977,27 +995,27 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       x_off[i] = (uint32_t)(sr * p.a_scale_ld);
     }
   }
-  u32x4_t rb[WN];                  // code stripes (invalid sub-tiles read sub-tile 0)
-  __amdgpu_buffer_rsrc_t rbr[WN];  // the same, for the register loads
+  __amdgpu_buffer_rsrc_t rbr[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) {
     const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
     const uint8_t* base = wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb;
-    rb[ns] = rsrc_words(base, cb);
     rbr[ns] = make_rsrc(base, cb);
   }
-  // register-loaded fragments of even and odd K-blocks (two stages)
-  BFrag<FMT> bA[WN], bB[WN];
+  // register-loaded fragments, one set per stage
+  BFrag<FMT> bA[WN], bB[WN], bC[WN];
   // metadata words of the wave's sub-tiles.  INT: one copy per K-block, lane
   // l takes scale dword l / WN (of 8 for bf16 scales, 16 for f32) of
   // sub-tile l % WN, so that a lane finds its word of every sub-tile side by
   // side (one vector read).  (Zero points enter through the offset terms
   // after the K loop.)  MX: lane l its E8M0 word of each sub-tile.
   u32x4_t rms = ra;
+  __amdgpu_buffer_rsrc_t rmsr = rar;
   const int sf = p.scale_f32;
   uint32_t mi_off = 0, mi_gmul = 0;
   if constexpr (FMT == F_INT) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
+    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
     const int nsw = (8 << sf) * WN;  // scale words (<= 64)
     const int ww = lane < nsw ? lane : 0;
     const int sub = ww % WN, d = ww / WN;
@@ -1006,26 +1024,41 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     mi_gmul = 16u * (2u << sf);
   } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
+    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
   }
 
-  // DMA of K-block kb into stage St (this wave's share)
+  // copies of K-block kb into stage st (this wave's share) and its weight
+  // fragments into registers bdst
   using St = TileLds<FMT, WM, WN, AMODE, EPI, S>;
+  // LDS DMA: inline assembly (untracked) or the builtin (tracked)
+  using LdsPtr = __attribute__((address_space(3))) void*;
+  auto dma16 = [&](const u32x4_t& rw, __amdgpu_buffer_rsrc_t rr, uint8_t* lds, uint32_t voff) -> void {
+    if constexpr (C::kTracked)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)lds, 16, voff, 0, 0, 0);
+    else
+      dma_b128(rw, lds, voff);
+  };
+  auto dma4 = [&](const u32x4_t& rw, __amdgpu_buffer_rsrc_t rr, uint8_t* lds, uint32_t voff) -> void {
+    if constexpr (C::kTracked)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)lds, 4, voff, 0, 0, 0);
+    else
+      dma_b32(rw, lds, voff);
+  };
   auto issue = [&](int kb, int st, BFrag<FMT>* bdst) -> void {
 #pragma unroll
     for (int i = 0; i < C::kAIW; ++i) {
       const int ins = (wn + 4 * i) % C::kAI;
-      dma_b128(ra, St::a(st) + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
+      dma16(ra, rar, St::a(st) + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
     }
     // per-row words: every wave copies them all (same bytes, same place)
     if constexpr (C::kX) {
 #pragma unroll
       for (int i = 0; i < C::kXI; ++i)
-        dma_b32(rx, St::x(st) + i * 256, x_off[i] + (uint32_t)kb * 4);
+        dma4(rx, rxr, St::x(st) + i * 256, x_off[i] + (uint32_t)kb * 4);
     }
-    if constexpr (C::kBReg) {
-      // (compiler-tracked loads: the kernel's full wait at the end of the
-      // step covers them, so the compiler adds none before their use).  A
-      // lane's kBWords 16-byte words sit side by side in the packed layout.
+    {
+      // (compiler-tracked loads.  A lane's kBWords 16-byte words sit side
+      // by side in the packed layout.)
       const uint32_t boff = (uint32_t)kb * C::kCB + lane * 16 * T::kBWords;
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns)
@@ -1035,34 +1068,30 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       // (the offset stays live past the loads: no load's destination
       // reuses the register another load reads its address from)
       asm volatile("" ::"v"(boff));
-    } else {
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-        for (int h = 0; h < T::kBWords; ++h)
-          dma_b128(rb[ns], St::b(st) + (wn * WN + ns) * C::kCB + h * 1024, (uint32_t)kb * C::kCB + h * 1024 + lane * 16);
     }
     uint8_t* mw = St::m(st) + wn * C::kMI * 256;
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-      dma_b32(rms, mw, mi_off + (uint32_t)gi * mi_gmul);
+      dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
-        dma_b32(rms, mw + ns * 256, ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4);
+        dma4(rms, rmsr, mw + ns * 256, ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4);
       }
     }
     // keep the issue ahead of the compute (the waits count on it)
     __builtin_amdgcn_sched_barrier(0);
   };
-  // this wave's DMA into the next stage has landed: vector-memory loads
-  // complete in order, and after it the wave has issued only the DMA of the
-  // stage after (kIss instructions, the loop holds no other vector-memory
-  // access).  The wait is explicit: the compiler's own waits for LDS DMA
-  // follow its alias analysis, which loses track of some of these arrays.
-  constexpr int kIss = C::kAIW + C::kXI + (C::kBReg ? 0 : WN * T::kBWords) + C::kMI;
+  // this wave's copies into the next stage have landed, so that after the
+  // barrier every wave may read them.  Vector-memory loads complete in
+  // order; with three stages the wave has issued since then only the kIss
+  // loads of the stage after (the loop holds no other vector-memory
+  // access), which stay in flight; with two, everything is waited for.
+  // The compiler's own waits cover only this wave's reads of its own
+  // copies, hence this one.
+  constexpr int kIss = C::kAIW + C::kXI + WN * T::kBWords + C::kMI;
   static_assert(kIss < 64, "vmcnt range");
-  constexpr int kAhead = C::kS == 3 ? kIss : 0;  // DMAs left in flight after the wait
+  constexpr int kAhead = C::kS == 3 ? kIss : 0;  // loads left in flight after the wait
   auto wait_own = [&]() -> void {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4) | (15 << 8));
@@ -1155,16 +1184,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   };
 
   if (nkb > 0) {
-    // K-block j uses stage j % kS.  The copy is issued unconditionally (past
-    // the last K-block it re-reads that block into a stage that is never
-    // consumed): the count of copies in flight is then the same on every
-    // path, which the explicit waits rely on.  One loop body for every stage
-    // keeps the accumulators in the same registers across iterations.
+    // K-block j uses stage j % kS and register set j % kS.  In the loop the
+    // copies are issued unconditionally (past the last K-block they re-read
+    // that block into a stage that is never consumed): the count of loads in
+    // flight is then the same on every path, which the explicit waits rely
+    // on.  The loop is unrolled kS times, so that every stage and register
+    // set is a constant and the accumulators stay in the same registers.
     const int kb_last = kb_begin + nkb - 1;
     auto kb_at = [&](int j) -> int { return kb_begin + j <= kb_last ? kb_begin + j : kb_last; };
     if constexpr (C::kS == 2) {
-      // two K-blocks per iteration, so that even and odd K-blocks keep
-      // their weight fragments in fixed registers; one exit
       issue(kb_at(0), 0, bA);
       wait_own();
       barrier();
@@ -1179,25 +1207,36 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         wait_own();
         barrier();
       }
-      if (j < nkb) {
-        issue(kb_at(j + 1), 1, bB);
+      if (j < nkb) compute(kb_begin + j, 0, bA);
+    } else {
+      issue(kb_at(0), 0, bA);
+      issue(kb_at(1), 1, bB);
+      wait_own();
+      barrier();
+      int j = 0;
+      for (; j + 2 < nkb; j += 3) {
+        issue(kb_at(j + 2), 2, bC);
         compute(kb_begin + j, 0, bA);
         wait_own();
         barrier();
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::kS - 1; ++j) issue(kb_at(j), j, bA);
-      wait_own();
-      barrier();
-      int st = 0, st_ahead = C::kS - 1;
-      for (int j = 0; j < nkb; ++j) {
-        issue(kb_at(j + C::kS - 1), st_ahead, bA);
-        compute(kb_begin + j, st, bA);
+        issue(kb_at(j + 3), 0, bA);
+        compute(kb_begin + j + 1, 1, bB);
         wait_own();
         barrier();
-        st = st + 1 == C::kS ? 0 : st + 1;
-        st_ahead = st_ahead + 1 == C::kS ? 0 : st_ahead + 1;
+        issue(kb_at(j + 4), 1, bB);
+        compute(kb_begin + j + 2, 2, bC);
+        wait_own();
+        barrier();
+      }
+      // one or two K-blocks left, their copies issued: nothing more to
+      // issue, so wait for everything
+      if (j < nkb) {
+        compute(kb_begin + j, 0, bA);
+        if (j + 1 < nkb) {
+          __builtin_amdgcn_s_waitcnt(0);
+          barrier();
+          compute(kb_begin + j + 1, 1, bB);
+        }
       }
     }
   }
