@@ -1336,27 +1336,44 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p, 
   float v[kCols], u[kCols];
 #pragma unroll
   for (int i = 0; i < kCols; ++i) v[i] = u[i] = 0.0f;
+  // The loads are unconditional (columns past the end re-read the last
+  // column, whose sums are never stored): a branch around each load would
+  // make the compiler wait for it before the next one.  Four splits' loads
+  // go out together.
+  int cc[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) cc[i] = (int)(c0 + i < outc ? c0 + i : outc - 1);
+#pragma unroll 4
   for (int s = 0; s < p.split_k; ++s) {
     const float* src = p.partials + ((int64_t)s * p.m + row) * ncols;
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
-      if (c0 + i < outc) {
-        v[i] += src[c0 + i];
-        if (kSwiglu) u[i] += src[c0 + i + p.n];
-      }
+      v[i] += src[cc[i]];
+      if (kSwiglu) u[i] += src[cc[i] + p.n];
     }
   }
   if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
     uint16_t* out = static_cast<uint16_t*>(p.out);
     const int64_t orow = (EPI == EPI_SCATTER) ? (int64_t)p.sorted[row] : row;
     const float rsc = (FMT == F_FP8) ? reinterpret_cast<const float*>(p.a_scale)[row] : 1.0f;
+    uint32_t h[kCols];
 #pragma unroll
     for (int i = 0; i < kCols; ++i) {
-      const int64_t col = c0 + i;
-      if (col >= outc) continue;
-      float x = v[i] * col_scale<FMT>(wmeta, col, gs) * rsc;
-      if (EPI == EPI_BF16 && p.bias) x += bf16_bits_to_f32(p.bias[col]);
-      out[orow * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
+      float x = v[i] * col_scale<FMT>(wmeta, cc[i], gs) * rsc;
+      if (EPI == EPI_BF16 && p.bias) x += bf16_bits_to_f32(p.bias[cc[i]]);
+      h[i] = f32_to_bf16_bits(x);
+    }
+    uint16_t* dst = out + orow * p.ldo + c0;
+    if (c0 + kCols <= outc && ((uintptr_t)dst & 15) == 0) {
+      // a whole 16-byte group: one store
+      u32x4_t w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = h[2 * i] | (h[2 * i + 1] << 16);
+      *reinterpret_cast<u32x4_t*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kCols; ++i)
+        if (c0 + i < outc) dst[i] = (uint16_t)h[i];
     }
   } else if constexpr (EPI == EPI_SWIGLU_BF16) {
     uint16_t* out = static_cast<uint16_t*>(p.out);
