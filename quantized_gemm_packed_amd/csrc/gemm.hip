@@ -810,18 +810,19 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
 // Prefill kernel: a (16 WM) x (64 WN) output tile per workgroup of 4 waves;
 // wave w owns columns [16 WN w, 16 WN (w + 1)) of the tile for all its rows.
 //
-// Every K-block's operands go from global memory straight into LDS by
-// LDS-DMA, kS - 1 K-blocks ahead of their use: the activation tile (16 WM
-// rows, 16-byte chunks XOR-swizzled with the row) with the INT row sums or
-// MXFP8 scale words of its rows, each wave's weight-code fragments (1 KB per
-// sub-tile, lane-linear, as packed) and its metadata words (INT scale and
-// zero-point dwords, or E8M0 rows).  Each pipeline stage is one LDS array.
-// The copies are issued from inline assembly, which the compiler does not
-// track, and the kernel waits for them itself.  A K-block step is: issue
-// the copies of K-block j + kS - 1, compute K-block j from LDS, wait until
-// this wave's copies of K-block j + 1 have landed (with three stages the
-// copies of K-block j + 2 stay in flight), barrier.  Registers hold only the
-// current fragments and the accumulators.
+// Every K-block's activation tile (16 WM rows, 16-byte chunks XOR-swizzled
+// with the row), with the MXFP8 scale words of its rows and each wave's
+// metadata words (INT scale dwords or E8M0 rows), goes from global memory
+// straight into LDS by LDS-DMA, kS - 1 K-blocks ahead of its use.  Each
+// wave's weight-code fragments (private to the wave) go straight into
+// registers, one register set per stage.  A K-block step is: issue the
+// copies of K-block j + kS - 1, compute K-block j, wait until this wave's
+// copies of K-block j + 1 have landed (with three stages the copies of
+// K-block j + 2 stay in flight), barrier.  With two stages the LDS copies
+// are issued from inline assembly, which the compiler does not track, and
+// every step ends with a full wait; with three they are issued through the
+// compiler's builtin into one LDS array per stage, so that the compiler's
+// own waits for the register fragments count them too.
 
 template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
 struct TileCfg {
