@@ -14,7 +14,8 @@ bit layouts.  The readings below are the OCP definitions:
 * E8M0 (OCP MX v1.0): 2^(c-127); c = 255 is NaN.
 * BF16: the upper 16 bits of an IEEE float32.
 
-Encoders round to nearest, ties to even, and saturate (E4M3) where noted.
+Encoders round to nearest, ties to even, and saturate (E4M3, E2M1) where
+noted.
 All values are returned as float64.
 """
 from __future__ import annotations
@@ -115,6 +116,40 @@ def encode_e4m3(v):
     exp_field = np.where(a == 0, 0, exp_field)
     code = (sign << 7) | (exp_field.astype(np.int64) << 3) | man.astype(np.int64)
     return code.astype(np.uint8)
+
+
+E2M1_MAX = 6.0
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def round_e2m1(v):
+    """float64 -> nearest E2M1 value (RNE on the one mantissa bit; quantum
+    0.5 below 2, 1 in [2, 4), 2 from 4), saturated to +-6, signed zero
+    kept.  Returns float64 values that are exactly representable."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                      # a in [2^(e-1), 2^e)
+    e = np.where(a == 0, -200, e)
+    q_exp = np.maximum(e - 2, -1)            # 1 mantissa bit, subnormal quantum 2^-1
+    r = np.ldexp(_rne(np.ldexp(a, -q_exp)), q_exp)
+    r = np.minimum(r, E2M1_MAX)
+    return np.copysign(r, v)
+
+
+def encode_e2m1(v):
+    """float64 -> E2M1 code (uint8, one code per byte), RNE with saturation
+    to +-6; the sign bit follows the sign of the (rounded) value."""
+    r = round_e2m1(v)
+    sign = np.signbit(r).astype(np.int64)
+    idx = np.searchsorted(np.asarray(E2M1_VALUES), np.abs(r))
+    return ((sign << 3) | idx).astype(np.uint8)
+
+
+def pack_nibbles(codes):
+    """uint8 [..., K] (one 4-bit code each) -> uint8 [..., K/2]; even k in
+    the low nibble (the inverse of unpack_nibbles)."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
 def floor_log2(a):

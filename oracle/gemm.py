@@ -24,7 +24,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import decode_bf16, decode_scale, decode_weight_codes, decode_e4m3
-from .quant import dequant_fp8_per_token, dequant_mxfp8
+from .quant import dequant_fp8_per_token, dequant_mxfp4, dequant_mxfp8
 
 
 @dataclass
@@ -86,6 +86,8 @@ def activations(act_fmt: str, x=None, q=None, scales=None):
         return dequant_fp8_per_token(q, scales)
     if act_fmt == "mxfp8":
         return dequant_mxfp8(q, scales)
+    if act_fmt == "mxfp4":
+        return dequant_mxfp4(q, scales)
     raise ValueError(act_fmt)
 
 

@@ -14,12 +14,19 @@ scaling rule; the readings taken here are:
   E = clamp(floor(log2 amax) - 8 + 127, 0, 254) (8 = emax of E4M3), an
   all-zero block takes E = 127; X = 2^(E-127); q = E4M3_RNE_SAT(x / X).
   floor(log2) is read from the exponent field, never from a rounded log.
+* MXFP4 activations (the W4A4 = MXFP4 x MXFP4 combination of the section
+  "W8A8 / W4A8 / W4A4"): the same OCP rule with the emax of E2M1 (2):
+  E = clamp(floor(log2 amax) - 2 + 127, 0, 254), an all-zero block takes
+  E = 127; q = E2M1_RNE_SAT(x / X).  A block's largest element lands in
+  [4, 8) before rounding and saturates to 6 above 6 (the OCP rule's own
+  clipping).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_e4m3, decode_e8m0, encode_e4m3, floor_log2
+from .formats import (decode_e2m1, decode_e4m3, decode_e8m0, encode_e2m1, encode_e4m3, floor_log2, pack_nibbles,
+                      unpack_nibbles)
 
 
 def quant_fp8_per_token(x_f32):
@@ -58,3 +65,30 @@ def dequant_mxfp8(codes, e8m0):
     m, k = codes.shape
     v = decode_e4m3(codes).reshape(m, k // 32, 32)
     return (v * decode_e8m0(e8m0)[..., None]).reshape(m, k)
+
+
+def mxfp4_exponent(amax):
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.clip(floor_log2(safe) - 2 + 127, 0, 254)
+    return np.where(amax > 0, e, 127).astype(np.int64)
+
+
+def quant_mxfp4(x):
+    """x: [M, K] (any float dtype; taken as exact float64), K % 32 == 0
+    -> (packed codes uint8 [M, K/2], even k in the low nibble;
+        E8M0 codes uint8 [M, K/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    m, k = x.shape
+    assert k % 32 == 0
+    xb = x.reshape(m, k // 32, 32)
+    e = mxfp4_exponent(np.abs(xb).max(axis=2))
+    scaled = xb / np.ldexp(1.0, e - 127)[..., None]
+    return pack_nibbles(encode_e2m1(scaled).reshape(m, k)), e.astype(np.uint8)
+
+
+def dequant_mxfp4(packed, e8m0):
+    m = packed.shape[0]
+    v = decode_e2m1(unpack_nibbles(packed))
+    k = v.shape[1]
+    return (v.reshape(m, k // 32, 32) * decode_e8m0(e8m0)[..., None]).reshape(m, k)

@@ -166,3 +166,28 @@ def test_bf16_encode_float64_brute():
         cands = sorted(cands, key=lambda c: (abs(Fraction(c) - Fraction(float(x))),
                                               (struct.unpack("<I", struct.pack("<f", c))[0] >> 16) & 1))
         assert r == cands[0], (x, r, cands)
+
+
+def test_e2m1_round_brute_force():
+    codes = np.arange(8)                          # non-negative codes
+    vals = F.decode_e2m1(codes)
+    g = np.random.default_rng(5)
+    xs = np.concatenate([g.standard_normal(300) * 3, g.uniform(-9, 9, 200), g.standard_normal(50) * 0.2,
+                         # exact midpoints between neighbours, both signs
+                         (vals[1:] + vals[:-1]) / 2, -(vals[1:] + vals[:-1]) / 2])
+    got = F.round_e2m1(xs)
+    for x, r in zip(xs, got):
+        ref = _nearest_brute(float(x), vals.tolist(), codes.tolist(), 6.0)
+        assert r == ref, (x, r, ref)
+
+
+def test_e2m1_encode_round_trip_and_signed_zero():
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(F.encode_e2m1(F.decode_e2m1(codes)), codes)
+    assert F.encode_e2m1(np.array([-0.0, -0.2, 0.2, 100.0, -100.0])).tolist() == [8, 8, 0, 7, 15]
+
+
+def test_pack_nibbles_inverts_unpack():
+    g = np.random.default_rng(6)
+    p = g.integers(0, 256, size=(5, 12)).astype(np.uint8)
+    assert np.array_equal(F.pack_nibbles(F.unpack_nibbles(p)), p)

@@ -168,3 +168,30 @@ def test_dequant_weight_per_expert_selection():
         # one element by hand
         c = int(codes[i, 1, 3] >> 4)            # k = 7 -> high nibble of byte 3
         assert full[i, 1, 7] == s_e2m1(c) * math.ldexp(1.0, int(sc[i, 1, 0]) - 127)
+
+
+def test_w4a4_mxfp4_linear_vs_fraction_brute_force():
+    """MXFP4 activations x MXFP4 weights (W4A4): the oracle's composition
+    (activation dequant, weight dequant, float64 product) against a scalar
+    Fraction sum over E2M1 codes and E8M0 exponents."""
+    g = np.random.default_rng(40)
+    m, n, k = 3, 5, 64
+    from oracle import quant as Q
+    x = g.standard_normal((m, k)) * 2.0
+    qa, ea = Q.quant_mxfp4(x)
+    wc = g.integers(0, 256, size=(1, n, k // 2)).astype(np.uint8)
+    we = g.integers(120, 134, size=(1, n, k // 32)).astype(np.uint8)
+    od = G.WeightDesc("e2m1", "group", 32, "e8m0", False, False, 1, n, k)
+    got = G.linear(od, G.activations("mxfp4", q=qa, scales=ea), wc, we)
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    dec = lambda c: Fraction(vals[c & 7]) * (-1 if c & 8 else 1)
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                ca = (int(qa[i, kk // 2]) >> (4 * (kk & 1))) & 0xF
+                cw = (int(wc[0, j, kk // 2]) >> (4 * (kk & 1))) & 0xF
+                sa = Fraction(2) ** (int(ea[i, kk // 32]) - 127)
+                sw = Fraction(2) ** (int(we[0, j, kk // 32]) - 127)
+                acc += dec(ca) * sa * dec(cw) * sw
+            assert got[i, j] == float(acc)

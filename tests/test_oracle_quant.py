@@ -104,3 +104,58 @@ def test_mxfp8_representable_round_trip():
     x = Q.dequant_mxfp8(codes, e)
     q2, e2 = Q.quant_mxfp8(x)
     assert np.array_equal(e2, e) and np.array_equal(q2, codes)
+
+
+def _mx4_scalar(block):
+    """Independent scalar statement of the MX scale rule with E2M1 elements."""
+    amax = max(abs(float(v)) for v in block)
+    if amax == 0:
+        e = 127
+    else:
+        _, ex = math.frexp(amax)
+        e = min(max((ex - 1) - 2 + 127, 0), 254)
+    x_scale = Fraction(2) ** (e - 127)
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    out = []
+    for v in block:
+        t = Fraction(float(v)) / x_scale
+        a = min(abs(t), Fraction(6))
+        best = min(range(8), key=lambda c: (abs(Fraction(vals[c]) - a), c & 1))
+        code = best | (8 if (float(v) < 0 or (float(v) == 0 and math.copysign(1, float(v)) < 0)) else 0)
+        out.append(code)
+    return e, out
+
+
+def test_mxfp4_matches_scalar_statement():
+    g = np.random.default_rng(15)
+    x = _bf16_vals(g, (4, 64), scale=3.0)
+    x[1, :32] = 0.0
+    x[2, 32:] *= 1e-30
+    x[3, 7] = -0.0
+    q, e = Q.quant_mxfp4(x)
+    codes = F.unpack_nibbles(q)
+    for r in range(4):
+        for b in range(2):
+            es, ref = _mx4_scalar(x[r, 32 * b:32 * b + 32])
+            assert e[r, b] == es
+            assert codes[r, 32 * b:32 * b + 32].tolist() == ref
+
+
+def test_mxfp4_exponent_minimal():
+    g = np.random.default_rng(16)
+    x = _bf16_vals(g, (128, 256), scale=10.0)
+    q, e = Q.quant_mxfp4(x)
+    amax = np.abs(x.reshape(128, 8, 32)).max(axis=2).astype(np.float64)
+    X = np.ldexp(1.0, e.astype(np.int64) - 127)
+    assert np.all(amax / X < 8) and np.all(amax / (X / 2) >= 8)
+
+
+def test_mxfp4_representable_round_trip():
+    g = np.random.default_rng(17)
+    codes = g.integers(0, 16, size=(16, 128)).astype(np.uint8)
+    codes[:, ::32] = 6 | (g.integers(0, 2, size=(16, 4)) * 9).astype(np.uint8)  # +-4 or +-6 (amax in [4, 8))
+    e = g.integers(110, 140, size=(16, 4)).astype(np.uint8)
+    packed = F.pack_nibbles(codes)
+    x = Q.dequant_mxfp4(packed, e)
+    q2, e2 = Q.quant_mxfp4(x)
+    assert np.array_equal(e2, e) and np.array_equal(q2, packed)
