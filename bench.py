@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12            # B/s
 BF16_PEAK = 2.5e15           # FLOP/s dense
 FP8_PEAK = 5.0e15
+FP4_PEAK = 10.1e15
 
 
 def parse():
@@ -185,6 +186,34 @@ def dense_w8a8(hum, timer, iters):
     return out
 
 
+def dense_w4a4(hum, timer, iters):
+    """Dense W4A4 (MXFP4 weights x MXFP4 activations quantized in the call),
+    at the W8A8 layer's shape N = 7168, K = 2048."""
+    import synth
+    import torch
+    n, k = 7168, 2048
+    w = synth.moe_weights_mxfp4(synth.seed_for(6), 1, n, k)
+    desc = hum.make_desc("e2m1", "group", 32, "e8m0", n, k, act_fmt="mxfp4")
+    packed = hum.prepare_weight(desc, _dev(w["codes"]), _dev(w["scales"]))
+    copies = rotate_copies(packed)
+    g = synth.rng(synth.seed_for(6, 1))
+    wbytes = n * k // 2 + n * k // 32
+    out = []
+    for m in synth.FP8_SWEEP_M:
+        x = _dev(synth.bf16_normal(g, (m, k)))
+        o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = hum.Workspace("cuda").get(hum.linear_workspace_bytes(desc, m))
+        fn = lambda i: hum.linear(desc, copies[i % len(copies)], x, out=o, workspace=ws)
+        timer.run(fn, 3)
+        t = timer.run(fn, iters)
+        flops = 2.0 * m * n * k
+        bound = "hbm" if m <= 128 else "mfma"
+        out.append({"m": m, "us": t * 1e6, "tflops": flops / t / 1e12, "weight_gbs": wbytes / t / 1e9,
+                    "bound": bound, "frac": (wbytes / t / HBM_PEAK) if bound == "hbm" else flops / t / FP4_PEAK,
+                    "tile": list(hum.select_config(desc, m).as_tuple())})
+    return out
+
+
 def moe(hum, timer, iters, act):
     import synth
     import torch
@@ -313,6 +342,7 @@ def main():
     if args.suite == "all":
         sweep["dense_w4a16_int4_g128_m16_n512_k1024"] = dense_tiny(hum, timer, iters)
         sweep["dense_w8a8_fp8_n7168_k2048"] = dense_w8a8(hum, timer, iters)
+        sweep["dense_w4a4_mxfp4_n7168_k2048"] = dense_w4a4(hum, timer, iters)
         del d["copies"]
         torch.cuda.empty_cache()
         sweep["moe_w4a16_mxfp4_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "bf16")

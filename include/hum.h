@@ -62,7 +62,9 @@ typedef enum hum_scale_gran {
 typedef enum hum_act_fmt {
   HUM_ACT_BF16 = 0,       /* bf16 activations as given (WnA16) */
   HUM_ACT_FP8_TOKEN = 1,  /* E4M3 codes + one f32 scale per row (W8A8) */
-  HUM_ACT_MXFP8 = 2       /* E4M3 codes + one E8M0 scale per 32 along K (W4A8) */
+  HUM_ACT_MXFP8 = 2,      /* E4M3 codes + one E8M0 scale per 32 along K (W4A8) */
+  HUM_ACT_MXFP4 = 3       /* E2M1 codes, two per byte (even k in the low nibble),
+                             + one E8M0 scale per 32 along K (W4A4, dense only) */
 } hum_act_fmt;
 
 /* The quantization description of one weight tensor [E][N][K]. */
@@ -128,18 +130,23 @@ hum_status hum_dequant_weight(const hum_weight_desc* desc, const void* packed,
  *                       q = E4M3_RNE_SAT(x / s) with an IEEE f32 division;
  *   HUM_ACT_MXFP8     : scales u8 [m][k/32], E = clamp(floor(log2 amax) - 8
  *                       + 127, 0, 254) (127 for a zero block),
- *                       q = E4M3_RNE_SAT(x / 2^(E-127)).
+ *                       q = E4M3_RNE_SAT(x / 2^(E-127));
+ *   HUM_ACT_MXFP4     : E2M1 codes q [m][k/2] (two per byte, even k in the
+ *                       low nibble), scales u8 [m][k/32], E = clamp(floor(
+ *                       log2 amax) - 2 + 127, 0, 254) (127 for a zero block),
+ *                       q = E2M1_RNE_SAT(x / 2^(E-127)) (saturated to +-6).
  * The formats are those named in the "End-to-end inference performance"
- * ("tokenwise FP8") and "Choosing the activation type" (MXFP8) sections of
- * the Humming announcement; the scale rules are the OCP ones.
- * k must be a multiple of 32 for MXFP8. */
+ * ("tokenwise FP8"), "Choosing the activation type" (MXFP8) and "W8A8 /
+ * W4A8 / W4A4" (MXFP4 activations) sections of the Humming announcement;
+ * the scale rules are the OCP ones.  k must be a multiple of 32 for MXFP8
+ * and MXFP4. */
 hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf16,
                          int64_t ld_x, void* q, void* scales, void* stream);
 
 /* ---- dense layer --------------------------------------------------------- */
 
 /* Workspace bytes hum_linear needs for m rows (quantized activations,
- * row sums, split-K partials and counters). */
+ * row sums, split-K partials). */
 size_t hum_linear_workspace_bytes(const hum_weight_desc* desc, int64_t m);
 
 /* C[m][n] = A[m][:] . W[n][:] (+ bias[n]) -> bf16, fp32 accumulation

@@ -16,7 +16,7 @@ __all__ = [
     "HumError", "WeightDesc", "TileConfig", "lib_path", "load_library",
     "BF16", "F32", "INT4", "UINT4", "E2M1", "E4M3", "E8M0",
     "SCALE_TENSOR", "SCALE_CHANNEL", "SCALE_GROUP",
-    "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8",
+    "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8", "ACT_MXFP4",
     "packed_weight_bytes", "prepare_weight", "dequant_weight", "quant_act",
     "select_config", "linear_workspace_bytes", "linear", "moe_workspace_bytes",
     "moe_gemm", "moe_align", "moe_reduce", "Workspace", "header_functions",
@@ -25,7 +25,7 @@ __all__ = [
 BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0 = range(7)
 KERNEL_TILE, KERNEL_STREAM = range(2)
 SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP = range(3)
-ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8 = range(3)
+ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4 = range(4)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "hum.h")
@@ -149,7 +149,7 @@ def _gpu(t, name):
 _DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3}
 _GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP}
 _SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0}
-_AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8}
+_AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4}
 
 
 def make_desc(weight_dtype, scale_gran, group_size, scale_dtype, n, k, num_experts=1,
@@ -202,12 +202,13 @@ def dequant_weight(desc: WeightDesc, packed):
 
 
 def quant_act(act_fmt, x):
-    """bf16 x [m, k] -> (E4M3 codes uint8 [m, k], scales)."""
+    """bf16 x [m, k] -> (codes, scales): E4M3 codes uint8 [m, k], or for
+    MXFP4 E2M1 codes two per byte uint8 [m, k/2] (even k in the low nibble)."""
     import torch
     _gpu(x, "x")
     fmt = _AF.get(act_fmt, act_fmt)
     m, k = x.shape
-    q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    q = torch.empty((m, k // 2 if fmt == ACT_MXFP4 else k), dtype=torch.uint8, device=x.device)
     if fmt == ACT_FP8_TOKEN:
         s = torch.empty((m,), dtype=torch.float32, device=x.device)
     else:

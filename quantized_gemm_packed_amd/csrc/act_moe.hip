@@ -116,6 +116,68 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4: each thread quantizes 8 elements into 4 bytes of E2M1 pairs (even k
+// in the low nibble); a DPP quad owns one 32-block.  The block scale follows
+// the MXFP8 rule with E2M1's emax (2); x / 2^(E-127) is exact in f32 (a
+// power-of-two scaling of a bf16 value, at most 8 in magnitude; results
+// below f32's range round to 0 in E2M1 either way), and the rounding to the
+// E2M1 grid is a comparison against the midpoints, ties to the even code.
+
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u
+                     : a < 0.75f ? 1u
+                     : a <= 1.25f ? 2u
+                     : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u
+                     : a < 3.5f ? 5u
+                     : a <= 5.0f ? 6u
+                     : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ s) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;  // chunks per row
+  const bool valid = id < m * cpr;
+  const int64_t row = valid ? id / cpr : 0;
+  const int64_t c8 = valid ? id % cpr : 0;
+  u32x4_t v = {0, 0, 0, 0};
+  if (valid) v = *reinterpret_cast<const u32x4_t*>(x + row * ldx + c8 * 8);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFF);
+    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+  amax = quad_max(amax);  // the 4 chunks of one 32-block are one DPP quad
+  const int e = mx_scale_code_emax(amax, 2);
+  const float inv = mx_inv_scale(e);
+  if (!valid) return;
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o |= f32_to_e2m1(f[i] * inv) << (4 * i);
+  *reinterpret_cast<uint32_t*>(q + row * (k / 2) + c8 * 4) = o;
+  if ((c8 & 3) == 0) s[row * (k / 32) + c8 / 4] = (uint8_t)e;
+}
+
+hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
+                              uint8_t* s, void* stream) {
+  if (m == 0) return HUM_OK;
+  const int64_t chunks = m * (k / 8);
+  quant_mxfp4_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp4 launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Fill kernel (used instead of hipMemsetAsync so the path stays capturable).
 
 __global__ void zero_kernel(uint32_t* p, int64_t words) {

@@ -57,7 +57,8 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32 || d->scale_dtype != HUM_E8M0)
         return set_error(HUM_ERR_UNSUPPORTED, "E2M1 weights need E8M0 scales per 32 along K (MXFP4)");
       if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E2M1 takes no zero point");
-      if (d->act_fmt != HUM_ACT_BF16 && d->act_fmt != HUM_ACT_MXFP8) return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 runs with bf16 or MXFP8 activations");
+      if (d->act_fmt != HUM_ACT_BF16 && d->act_fmt != HUM_ACT_MXFP8 && d->act_fmt != HUM_ACT_MXFP4)
+        return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 runs with bf16, MXFP8 or MXFP4 activations");
       return HUM_OK;
     case HUM_E4M3:
       if (d->scale_gran == HUM_SCALE_GROUP) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take per-channel or per-tensor scales");
@@ -73,7 +74,8 @@ hum_status check_desc(const hum_weight_desc* d) {
 int fmt_of(const hum_weight_desc* d) {
   if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
   if (d->weight_dtype == HUM_E4M3) return F_FP8;
-  return d->act_fmt == HUM_ACT_MXFP8 ? F_MXFP4_MXFP8 : F_MXFP4_BF16;
+  if (d->act_fmt == HUM_ACT_MXFP8) return F_MXFP4_MXFP8;
+  return d->act_fmt == HUM_ACT_MXFP4 ? F_MXFP4_MXFP4 : F_MXFP4_BF16;
 }
 
 hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
@@ -157,7 +159,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
-  if (m <= 16) {
+  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4) {
     // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
     // wave: the fewest that keep the activation bytes each workgroup reads
     // (from L2) at or below its weight bytes.  Four K-waves when their K
@@ -197,7 +199,8 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     // Measured on MI355X (dense N = K = 8192 and N = 7168, K = 2048): small
     // tiles with split-K while the tile count is low; 64 x 256 tiles for
     // bf16 activations from M = 512 (fewer LDS activation reads per MFMA);
-    // 128 x 128 for FP8 activations.
+    // 128 x 128 for FP8 activations.  W4A4 (no decode kernel) takes the
+    // small tiles from M = 1.
     const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16;
     int64_t target = 3 * kCUs;
     if (m <= 256) {
@@ -214,6 +217,15 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
     c.split_k = pick_split(wgs, 4, kb, 1, 4, target);
+    if (fmt_of(d) == F_MXFP4_MXFP4) {
+      // W4A4 (N = 7168, K = 2048): three stages throughout, 32 x 128 tiles
+      // to M = 256 and 64 x 256 above, no split-K (its reduce launch costs
+      // more than the parallelism gains at these weight sizes)
+      c.wave_m = m <= 256 ? 2 : 4;
+      c.wave_n = m <= 256 ? 2 : 4;
+      c.stages = 3;
+      c.split_k = 1;
+    }
   }
   c.block_m = (int32_t)tile_rows(c);
   return c;
@@ -284,9 +296,9 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
   if (c.split_k > 1) off = align256(off + (int64_t)c.split_k * m * nt * 16 * 4);
   w.aq = off;
   if (quant_a) {
-    off = align256(off + m * d->k);
+    off = align256(off + (d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 2) : m * d->k));
     w.as = off;
-    off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 ? m * (d->k / 32) : m * 4));
+    off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 || d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 32) : m * 4));
   }
   w.rowsum = off;
   if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
@@ -343,7 +355,11 @@ hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf
     if (k % 32) return set_error(HUM_ERR_UNSUPPORTED, "MXFP8 needs k % 32 == 0");
     return launch_quant_mxfp8(m, k, x_bf16, ld_x, q, static_cast<uint8_t*>(scales), stream);
   }
-  return set_error(HUM_ERR_INVALID_ARG, "act_fmt must be FP8_TOKEN or MXFP8");
+  if (act_fmt == HUM_ACT_MXFP4) {
+    if (k % 32) return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 needs k % 32 == 0");
+    return launch_quant_mxfp4(m, k, x_bf16, ld_x, q, static_cast<uint8_t*>(scales), stream);
+  }
+  return set_error(HUM_ERR_INVALID_ARG, "act_fmt must be FP8_TOKEN, MXFP8 or MXFP4");
 }
 
 hum_status hum_select_config(const hum_weight_desc* desc, int64_t m, hum_tile_config* cfg_out) {
@@ -456,8 +472,9 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.kb_per_split = kb_per_split(L.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
   p.stream_rows = (int)(m < 16 ? m : 16);
-  p.a_bytes = m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ? 2 : 1);
-  p.a_scale_bytes = desc->act_fmt == HUM_ACT_MXFP8 ? m * (desc->k / 32) : 0;
+  p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
+                                            : m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ? 2 : 1);
+  p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32) : 0;
   return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);
 }
 
@@ -523,6 +540,7 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1)
     return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs MXFP4 (E2M1 + E8M0) expert weights");
   if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
+  if (w13->act_fmt == HUM_ACT_MXFP4) return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs bf16 or MXFP8 activations");
   if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");
   if (w2->n != w13->k) return set_error(HUM_ERR_INVALID_ARG, "w2 n must equal the hidden size (w13 k)");
   if (w2->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 128");

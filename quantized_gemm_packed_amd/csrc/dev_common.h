@@ -75,12 +75,14 @@ __device__ __forceinline__ int floor_log2_f32(float a) {
   return e - 127;
 }
 
-// MX scale exponent code for a block whose absolute maximum is `amax`.
-__device__ __forceinline__ int mx_scale_code(float amax) {
+// MX scale exponent code for a block whose absolute maximum is `amax`, for
+// elements whose largest power of two is 2^emax (E4M3: 8, E2M1: 2).
+__device__ __forceinline__ int mx_scale_code_emax(float amax, int emax) {
   if (!(amax > 0.0f)) return 127;
-  int e = floor_log2_f32(amax) - 8 + 127;
+  int e = floor_log2_f32(amax) - emax + 127;
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }
+__device__ __forceinline__ int mx_scale_code(float amax) { return mx_scale_code_emax(amax, 8); }
 
 // 2^(127 - e) as an exact float for e in [0, 254] (the reciprocal of the
 // MX block scale 2^(e-127)).

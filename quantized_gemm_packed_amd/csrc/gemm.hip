@@ -17,11 +17,11 @@
 //   in-workgroup reduction through LDS.
 // * tile_kernel (prefill): 4 waves side by side along N share a 16*WM-row
 //   activation tile.  Each K-block's activation tile (XOR swizzled so the
-//   operand reads are conflict free), weight fragments and metadata are
-//   copied global -> LDS by buffer-load-to-LDS DMA, three K-blocks deep;
-//   each wave dequantizes its own weight columns from LDS into registers.
-//   Workgroups are ordered so that the tiles of one activation row block
-//   land on one XCD (shared L2).
+//   operand reads are conflict free) and metadata are copied global -> LDS
+//   by buffer-load-to-LDS DMA, one or two K-blocks ahead; each wave loads
+//   its own weight fragments straight into registers and dequantizes them
+//   there.  Workgroups are ordered so that the tiles one XCD runs at a time
+//   share activation rows and weight columns in its L2.
 //
 // Formats:
 //   F_INT          INT4/UINT4 -> bf16 (128 + u) with one AND-OR per two
@@ -34,6 +34,8 @@
 //                  per-channel scales in the epilogue.
 //   F_MXFP4_MXFP8  E4M3 activations x E2M1 weights on the block-scaled
 //                  16x16x128 MFMA, both E8M0 scales as operands.
+//   F_MXFP4_MXFP4  E2M1 activations x E2M1 weights (W4A4) on the same
+//                  MFMA; prefill-tile kernel only.
 //
 // Split-K across workgroups writes fp32 partials; a separate reduce kernel
 // sums them in split order (deterministic) and applies the epilogue.
@@ -49,9 +51,13 @@ namespace hum {
 
 template <int FMT>
 struct Tr {
-  static constexpr int kAElem = (FMT == F_INT || FMT == F_MXFP4_BF16) ? 2 : 1;  // activation bytes
+  static constexpr int kAElem = (FMT == F_INT || FMT == F_MXFP4_BF16) ? 2 : 1;  // activation bytes (FP4: 1/2)
+  static constexpr bool kA4 = (FMT == F_MXFP4_MXFP4);                           // 4-bit activations
+  static constexpr int kARowB = kA4 ? 64 : 128 * kAElem;                        // activation bytes per row per K-block
   static constexpr int kBWords = (FMT == F_FP8) ? 2 : 1;                         // 16-B words / lane / K-block
   static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16);
+  // bytes of an activation row of `ld` elements
+  static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
 };
 
 // ---------------------------------------------------------------------------
@@ -260,7 +266,9 @@ __device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, con
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 127, 0, 127);
   } else {
     b8[4] = 0; b8[5] = 0; b8[6] = 0; b8[7] = 0;
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 4, 0, sa, 0, (int)frag_mx_code(meta, kb));
+    // A format: E4M3 (0) or E2M1 (4, only the low 4 dwords of a8 are read)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, FMT == F_MXFP4_MXFP4 ? 4 : 0, 4, 0, sa, 0,
+                                                            (int)frag_mx_code(meta, kb));
   }
 }
 
@@ -832,12 +840,12 @@ struct TileCfg {
   static constexpr int kS = S;
   static constexpr int kTM = 16 * WM;
   static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
-  static constexpr int kRowB = 128 * T::kAElem;                  // activation bytes per row per K-block
+  static constexpr int kRowB = T::kARowB;                        // activation bytes per row per K-block
   static constexpr int kCPR = kRowB / 16;                        // 16-byte chunks per row
   static constexpr int kA = kTM * kRowB;                         // activation tile (whole KB)
   static constexpr int kAI = kA / 1024;                          // its 1-KB DMA instructions
   static constexpr int kAIW = (kAI + 3) / 4;                     // ... per wave
-  static constexpr bool kX = (FMT == F_MXFP4_MXFP8);           // a dword per row (MX scales)
+  static constexpr bool kX = (FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4);  // a dword per row (MX scales)
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
   static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
   // Each wave loads its own weight fragments straight into registers,
@@ -850,7 +858,8 @@ struct TileCfg {
   // register fragments (two stages deep) are exact; two stages issue them
   // from inline assembly and wait for everything at the end of each step.
   static constexpr bool kTracked = (kS == 3);
-  static constexpr int kMI = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? WN : 0);
+  static constexpr int kMI =
+      (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
@@ -861,8 +870,11 @@ struct TileCfg {
   static_assert(FMT != F_INT || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
 };
 
-__device__ __forceinline__ int swz(int r, int c, int a_elem) {
-  return a_elem == 2 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+// Physical 16-byte chunk of logical chunk c of LDS tile row r, for rows of
+// cpr chunks (16: bf16, 8: FP8, 4: FP4): the 16 rows of one fragment read
+// land on different banks.
+__device__ __forceinline__ int swz(int r, int c, int cpr) {
+  return cpr == 16 ? (c ^ (r & 15)) : (cpr == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3)));
 }
 
 // LDS of the pipeline: kS stages of kStage bytes, each holding the
@@ -980,8 +992,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const int ins = (wn + 4 * i) % C::kAI;
     const int slot = ins * 64 + lane;
     const int r = slot / C::kCPR;
-    const int lc = swz(r, slot % C::kCPR, kAE);
-    a_off[i] = (uint32_t)(src_row(r) * p.lda * kAE + lc * 16);
+    const int lc = swz(r, slot % C::kCPR, C::kCPR);
+    a_off[i] = (uint32_t)(src_row(r) * T::row_bytes(p.lda) + lc * 16);
   }
   u32x4_t rx = ra;
   __amdgpu_buffer_rsrc_t rxr = rar;
@@ -1023,7 +1035,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
     mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
     mi_gmul = 16u * (2u << sf);
-  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
   }
@@ -1074,7 +1086,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
-    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
         dma4(rms, rmsr, mw + ns * 256, ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4);
@@ -1129,7 +1141,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
                                : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
       mw[ns] = 0;
-      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)
+      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
     }
     if constexpr (FMT == F_INT) {
@@ -1170,14 +1182,21 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int ms = 0; ms < WM; ++ms) {
         const int r = ms * 16 + c16;
-        const int sw = (r >> 1) & 7;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + ((lg ^ sw) * 16));
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (((4 + lg) ^ sw) * 16));
         i32x8_t a8;
-        a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
-        a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
+        if constexpr (T::kA4) {
+          // 32 E2M1 codes of k = 32 lg + j: one 16-byte chunk
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (swz(r, lg, 4) * 16));
+          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
+          a8[4] = 0; a8[5] = 0; a8[6] = 0; a8[7] = 0;
+        } else {
+          const int sw = (r >> 1) & 7;
+          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + ((lg ^ sw) * 16));
+          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (((4 + lg) ^ sw) * 16));
+          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
+          a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
+        }
         int sa = 127;
-        if (FMT == F_MXFP4_MXFP8) sa = (int)((reinterpret_cast<const uint32_t*>(St::x(st))[r] >> (8 * lg)) & 0xFF);
+        if (C::kX) sa = (int)((reinterpret_cast<const uint32_t*>(St::x(st))[r] >> (8 * lg)) & 0xFF);
 #pragma unroll
         for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bf[ns], mw[ns], kb, acc[ms][ns]);
       }
@@ -1487,6 +1506,21 @@ struct Instance {
   HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
   HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
 
+// Tile instances only (formats without a decode-kernel path)
+#define HUM_DENSE_TILE_SET(F)                              \
+  HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 2, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 4, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 4, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 8, 2, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16),                   \
+  HUM_TILE_S(F, 2, 2, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 2, 4, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 4, 2, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
+  HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
+
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
   HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
@@ -1506,6 +1540,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_FP8),
     HUM_DENSE_SET(F_MXFP4_BF16),
     HUM_DENSE_SET(F_MXFP4_MXFP8),
+    HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1526,6 +1561,7 @@ static const ReduceInstance kReduces[] = {
     {F_MXFP4_BF16, EPI_SWIGLU_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SWIGLU_BF16>},
     {F_MXFP4_BF16, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SCATTER>},
     {F_MXFP4_MXFP8, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_BF16>},
+    {F_MXFP4_MXFP4, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP4, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

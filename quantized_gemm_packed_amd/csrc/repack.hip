@@ -253,7 +253,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   if (f == F_INT) {
     repack_int_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.ng, B), B, 0, s>>>(a);
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
-  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8) {
+  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else {
     repack_fp8_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * kNSub, B), B, 0, s>>>(a);

@@ -124,6 +124,47 @@ def test_mxfp4_mxfp8_exact_every_tile(tile):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("tile", TILE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_mxfp4_mxfp4_exact_every_tile(tile, split):
+    """Dense W4A4: activations drawn from the E2M1 grid with one +-4 or +-6
+    per 32-block quantize to MXFP4 exactly (block scale 2^0), E2M1 x E8M0
+    weights are exact, and every partial sum is exact in fp32: bitwise equal
+    to the oracle."""
+    m, n, k = 19, 96, 1024
+    g = synth.rng(36)
+    w = synth.quant_weights(36, "e2m1", "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    x = grid[g.integers(0, 8, size=(m, k))] * np.where(g.integers(0, 2, size=(m, k)) == 1, -1.0, 1.0)
+    x[:, ::32] = np.where(g.integers(0, 2, size=(m, k // 32)) == 1, 4.0, -6.0)
+    xb = oracle.formats.encode_bf16(x)
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp4")
+    packed = prepare(hd, w, "e8m0")
+    print(f"case w4a4 exact tile={tile} split={split}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+    torch.cuda.synchronize()
+    q, e = oracle.quant.quant_mxfp4(oracle.formats.decode_bf16(xb))
+    a = oracle.quant.dequant_mxfp4(q, e)
+    assert np.array_equal(a, oracle.formats.decode_bf16(xb))
+    ref = oracle.gemm.linear(od, a, w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
+def test_w4a4_dense_random_vs_oracle(m):
+    """Dense W4A4 (MXFP4 weights x MXFP4 activations) at the selector's config."""
+    n, k = 640, 2048
+    w = synth.moe_weights_mxfp4(synth.seed_for(6, m), 1, n, k)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(6, 100 + m)), (m, k))
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp4")
+    packed = prepare(hd, w, "e8m0")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    q, e = oracle.quant.quant_mxfp4(oracle.formats.decode_bf16(xb))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_mxfp4(q, e), w["codes"], w["scales"])
+    assert_tol(out, ref, f"w4a4 m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -265,7 +306,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e2m1_mxfp8"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -279,7 +320,7 @@ def test_empty_m_is_a_no_op(fmt):
         packed = prepare(hd, w, "f32")
     else:
         w = synth.moe_weights_mxfp4(51, 1, n, k)
-        hd, _ = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp8")
+        hd, _ = descs("e2m1", "group", 32, "e8m0", 1, n, k, act=fmt.split("_")[1])
         packed = prepare(hd, w, "e8m0")
     x = torch.empty((0, k), dtype=torch.bfloat16, device="cuda")
     out = hum.linear(hd, packed, x)

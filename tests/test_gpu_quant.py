@@ -45,6 +45,35 @@ def test_mxfp8_codes_bit_exact(m, k):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("m,k", [(1, 128), (6, 2048), (37, 4096), (130, 1024)])
+def test_mxfp4_codes_bit_exact(m, k):
+    xb = _inputs(300 + m, m, k)
+    q, s = hum.quant_act("mxfp4", dev(xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant.quant_mxfp4(oracle.formats.decode_bf16(xb))
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def test_mxfp4_ties_saturation_and_signed_zero():
+    """Blocks built so that x / X hits every E2M1 rounding midpoint, values
+    above 6 and negative values that round to zero."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, 7.0, 7.9]
+    row = np.zeros(64, np.float64)
+    row[:len(mids)] = mids
+    row[16:16 + len(mids)] = [-v for v in mids]
+    row[30] = -0.1
+    row[31] = -0.0
+    row[32:64] = np.linspace(-3.0, 3.0, 32)
+    row[40] = 6.0                                  # amax 6: X = 2^0 for both blocks
+    xb = oracle.formats.encode_bf16(row[None, :])
+    q, s = hum.quant_act("mxfp4", dev(xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant.quant_mxfp4(oracle.formats.decode_bf16(xb))
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
 def test_fp8_representable_round_trip():
     g = synth.rng(7)
     codes = g.integers(0, 0x7E, size=(16, 256), dtype=np.uint8) | (g.integers(0, 2, (16, 256), dtype=np.uint8) << 7)
