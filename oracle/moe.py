@@ -15,8 +15,8 @@ Readings where the pages are silent:
   gate = first I rows of the fused weight, up = last I rows; no clamp and a
   routed scaling factor of 1.
 * precision at the stage boundary follows the activation format: bf16 (RNE)
-  for W4A16, MXFP8 of the float value for W4A8; the token activations are
-  MXFP8-quantized for W4A8.
+  for W4A16, MXFP8 of the float value for W4A8, MXFP4 of it for W4A4; the
+  token activations are MXFP8- (W4A8) or MXFP4- (W4A4) quantized.
 * align: flat index f = t*topk + j; experts' segments in expert order, each
   padded to a multiple of block_m; inside a segment ascending f (stable);
   padding slots hold the sentinel T*topk.
@@ -28,7 +28,7 @@ import numpy as np
 
 from .formats import decode_bf16, encode_bf16
 from .gemm import WeightDesc, dequant_weight
-from .quant import dequant_mxfp8, quant_mxfp8
+from .quant import dequant_mxfp4, dequant_mxfp8, quant_mxfp4, quant_mxfp8
 
 
 def align_capacity(num_tokens: int, topk: int, num_experts: int, block_m: int) -> int:
@@ -77,6 +77,11 @@ def qdq_mxfp8(a):
     return dequant_mxfp8(q, e)
 
 
+def qdq_mxfp4(a):
+    q, e = quant_mxfp4(a)
+    return dequant_mxfp4(q, e)
+
+
 def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
                 x_bits, ids, weights, act_fmt: str, experts=None,
                 return_y: bool = False):
@@ -85,8 +90,9 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
     flat routing index.
 
     ``w13`` / ``w2``: dicts with canonical ``codes``, ``scales`` and optional
-    ``zeros`` / ``global_scale``.  ``act_fmt``: "bf16" (W4A16) or "mxfp8"
-    (W4A8).  ``experts``: restrict to these experts (bounded samples).
+    ``zeros`` / ``global_scale``.  ``act_fmt``: "bf16" (W4A16), "mxfp8"
+    (W4A8) or "mxfp4" (W4A4: the layer input and the SwiGLU output are
+    quantized to MXFP4 the way MXFP8 is for W4A8).  ``experts``: restrict to these experts (bounded samples).
     """
     ids = np.asarray(ids, dtype=np.int64)
     wts = np.asarray(weights, dtype=np.float32).astype(np.float64)
@@ -97,6 +103,8 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
     x = decode_bf16(x_bits)
     if act_fmt == "mxfp8":
         a_in = qdq_mxfp8(x)
+    elif act_fmt == "mxfp4":
+        a_in = qdq_mxfp4(x)
     elif act_fmt == "bf16":
         a_in = x
     else:
@@ -115,7 +123,7 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
         h = a_in[tok] @ w_gu.T
         del w_gu
         a = swiglu(h, inter)
-        a = round_bf16(a) if act_fmt == "bf16" else qdq_mxfp8(a)
+        a = round_bf16(a) if act_fmt == "bf16" else (qdq_mxfp8(a) if act_fmt == "mxfp8" else qdq_mxfp4(a))
         w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
                               w2.get("global_scale"), experts=[e])[0]
         y = a @ w_dn.T

@@ -57,7 +57,7 @@ def _small_layer(seed, e, hdim, inter):
     return d13, w13, d2, w2
 
 
-@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
 def test_moe_equals_loop_of_dense(act):
     e, hdim, inter, t, k = 6, 64, 32, 9, 3
     d13, w13, d2, w2 = _small_layer(30, e, hdim, inter)
@@ -65,14 +65,15 @@ def test_moe_equals_loop_of_dense(act):
     x = bf16_bits(g.standard_normal((t, hdim)).astype(np.float32))
     ids, wts = routing(32, t, e, k)
     out = M.moe_forward(d13, w13, d2, w2, x, ids, wts, act)
-    a_in = decode_bf16(x) if act == "bf16" else M.qdq_mxfp8(decode_bf16(x))
+    qdq = {"mxfp8": M.qdq_mxfp8, "mxfp4": M.qdq_mxfp4}.get(act)
+    a_in = decode_bf16(x) if act == "bf16" else qdq(decode_bf16(x))
     ref = np.zeros_like(out)
     for tt in range(t):
         for j in range(k):
             ex = int(ids[tt, j])
             h = G.linear(d13, a_in[tt:tt + 1], w13["codes"], w13["scales"], expert=ex)
             a = M.silu(h[:, :inter]) * h[:, inter:]
-            a = decode_bf16(encode_bf16(a)) if act == "bf16" else M.qdq_mxfp8(a)
+            a = decode_bf16(encode_bf16(a)) if act == "bf16" else qdq(a)
             y = G.linear(d2, a, w2["codes"], w2["scales"], expert=ex)
             ref[tt] += float(wts[tt, j]) * y[0]
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
