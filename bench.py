@@ -244,7 +244,7 @@ def moe(hum, timer, iters, act):
         flops = 2.0 * t * topk * (2 * inter * h + h * inter)
         wb = touched * per_expert
         bound = "hbm" if t * topk < 8 * 1024 else "mfma"
-        peak = BF16_PEAK if act == "bf16" else FP8_PEAK
+        peak = {"bf16": BF16_PEAK, "mxfp8": FP8_PEAK, "mxfp4": FP4_PEAK}[act]
         cnt = np.bincount(ids.reshape(-1), minlength=e)
         out.append({"tokens": t, "us": tt * 1e6, "tflops": flops / tt / 1e12, "weight_gbs": wb / tt / 1e9,
                     "experts_touched": touched, "max_rows": int(cnt.max()), "bound": bound,
@@ -347,6 +347,7 @@ def main():
         torch.cuda.empty_cache()
         sweep["moe_w4a16_mxfp4_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "bf16")
         sweep["moe_w4a8_mxfp4_mxfp8_zipf1.1_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "mxfp8")
+        sweep["moe_w4a4_mxfp4_mxfp4_zipf1.1_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "mxfp4")
     cpu = None if args.no_cpu else cpu_baseline(d["case"])
     line = {
         "metric": "quant GEMM TFLOP/s + weight HBM GB/s vs roofline, dense & MoE, M=1..4096",

@@ -123,18 +123,6 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
 // below f32's range round to 0 in E2M1 either way), and the rounding to the
 // E2M1 grid is a comparison against the midpoints, ties to the even code.
 
-__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
-  const float a = __builtin_fabsf(v);
-  const uint32_t c = a <= 0.25f ? 0u
-                     : a < 0.75f ? 1u
-                     : a <= 1.25f ? 2u
-                     : a < 1.75f ? 3u
-                     : a <= 2.5f ? 4u
-                     : a < 3.5f ? 5u
-                     : a <= 5.0f ? 6u
-                     : 7u;
-  return c | ((__float_as_uint(v) >> 28) & 8u);
-}
 
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                           int64_t m, int64_t k, uint8_t* __restrict__ q,

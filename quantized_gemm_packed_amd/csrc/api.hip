@@ -259,6 +259,11 @@ static hum_tile_config moe_tile_cfg(int wm) {
 // 16-row tiles up to ~100 rows, larger tiles beyond.
 static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   const double rows = (double)t * topk / w13->num_experts;
+  if (fmt_of(w13) == F_MXFP4_MXFP4) {
+    // W4A4: tile kernels only (no decode-kernel path)
+    const int wm = rows <= 16 ? 1 : (rows <= 256 ? 2 : 4);
+    return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
+  }
   if (fmt_of(w13) != F_MXFP4_MXFP8) {
     if (rows < 0.5) return {moe_stream_cfg(), moe_stream_cfg()};
     const int wm = rows <= 96 ? 1 : (rows <= 192 ? 2 : 4);
@@ -502,7 +507,8 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   const int64_t h = w13->k;
   w.cap = t * topk + E * (bm - 1);
   w.nblocks = cdiv(w.cap, bm);
-  const bool mx = w13->act_fmt == HUM_ACT_MXFP8;
+  const bool mx = w13->act_fmt == HUM_ACT_MXFP8 || w13->act_fmt == HUM_ACT_MXFP4;
+  const bool mx4 = w13->act_fmt == HUM_ACT_MXFP4;  // E2M1 codes, two per byte
   const int64_t pcols = (2 * inter > cdiv(h, kNSub) * kNSub) ? 2 * inter : cdiv(h, kNSub) * kNSub;
   int64_t off = 0;
   w.partials = off;
@@ -517,12 +523,12 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   off = align256(off + w.nblocks * 4);
   w.xq = off;
   if (mx) {
-    off = align256(off + t * h);
+    off = align256(off + (mx4 ? t * (h / 2) : t * h));
     w.xs = off;
     off = align256(off + t * (h / 32));
   }
   w.inter = off;
-  off = align256(off + w.cap * inter * (mx ? 1 : 2));
+  off = align256(off + (mx4 ? w.cap * (inter / 2) : w.cap * inter * (mx ? 1 : 2)));
   w.inter_s = off;
   if (mx) off = align256(off + w.cap * (inter / 32));
   w.y = off;
@@ -540,7 +546,6 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1)
     return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs MXFP4 (E2M1 + E8M0) expert weights");
   if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
-  if (w13->act_fmt == HUM_ACT_MXFP4) return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs bf16 or MXFP8 activations");
   if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");
   if (w2->n != w13->k) return set_error(HUM_ERR_INVALID_ARG, "w2 n must equal the hidden size (w13 k)");
   if (w2->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 128");
@@ -599,7 +604,8 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   if (!cfg_sane(cu) || !cfg_sane(cd) || tile_rows(cu) != tile_rows(cd))
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
-  const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
+  const int epi_up =
+      (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : (f == F_MXFP4_MXFP4 ? EPI_SWIGLU_MXFP4 : EPI_SWIGLU_BF16);
   KernelKey kup{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
   KernelKey kdn{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
   if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
@@ -619,10 +625,12 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   st = launch_align(topk_ids, t, topk, (int32_t)E, bm, sorted, reinterpret_cast<int32_t*>(ws + w.offsets),
                     reinterpret_cast<int32_t*>(ws + w.counts), bexp, w.nblocks, stream);
   if (st != HUM_OK) return st;
-  const bool mx = f == F_MXFP4_MXFP8;
+  const bool mx4 = f == F_MXFP4_MXFP4;
+  const bool mx = f == F_MXFP4_MXFP8 || mx4;
   const void* x_use = x_bf16;
   if (mx) {
-    st = launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
+    st = mx4 ? launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream)
+             : launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
     if (st != HUM_OK) return st;
     x_use = ws + w.xq;
   }
@@ -652,7 +660,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   // repeated ids within a token): the LDS staging is sized for it
   const int64_t slots = t * topk;
   p.stream_rows = (int)(slots < 16 ? slots : 16);
-  p.a_bytes = t * h * (mx ? 1 : 2);
+  p.a_bytes = mx4 ? t * (h / 2) : t * h * (mx ? 1 : 2);
   p.a_scale_bytes = mx ? t * (h / 32) : 0;
   st = launch_gemm(kup, p, w.nblocks, bm, stream);
   if (st != HUM_OK) return st;
@@ -677,7 +685,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.kb_per_split = kb_per_split(L2.kb, cd);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
   q.stream_rows = p.stream_rows;  // valid (non-padding) rows of a block
-  q.a_bytes = w.cap * inter * (mx ? 1 : 2);
+  q.a_bytes = mx4 ? w.cap * (inter / 2) : w.cap * inter * (mx ? 1 : 2);
   q.a_scale_bytes = mx ? w.cap * (inter / 32) : 0;
   st = launch_gemm(kdn, q, w.nblocks, bm, stream);
   if (st != HUM_OK) return st;

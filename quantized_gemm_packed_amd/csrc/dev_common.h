@@ -42,6 +42,22 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// One float -> E2M1 code (nearest, ties to the even code, saturated to +-6,
+// sign bit kept for values that round to zero): a comparison against the
+// midpoints of the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = __builtin_fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u
+                     : a < 0.75f ? 1u
+                     : a <= 1.25f ? 2u
+                     : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u
+                     : a < 3.5f ? 5u
+                     : a <= 5.0f ? 6u
+                     : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
 // Sum / max over the 16 lanes of a DPP row (lanes 16r .. 16r+15); every lane
 // of the row receives the result.
 __device__ __forceinline__ float row16_sum(float v) {

@@ -350,6 +350,36 @@ __device__ __forceinline__ void store_swiglu_mxfp8(const GemmParams& p, float gs
   }
 }
 
+// SwiGLU + MXFP4 requantization of 32 columns (W4A4): as the MXFP8 one,
+// with E2M1 codes two per byte (even column in the low nibble): the lane of
+// an even column takes its odd neighbour's code across the DPP quad and
+// stores the byte.
+__device__ __forceinline__ void store_swiglu_mxfp4(const GemmParams& p, float gs, int64_t row_base, int64_t col0,
+                                                   const f32x4_t& g0, const f32x4_t& u0, const f32x4_t& g1,
+                                                   const f32x4_t& u1, int lg, int c16) {
+  uint8_t* outq = static_cast<uint8_t*>(p.out);
+  uint8_t* outs = static_cast<uint8_t*>(p.out_scale);
+  const bool ok = (col0 - c16) < p.n;  // whole 32-column block valid (I % 32 == 0)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = row_base + 4 * lg + i;
+    const float a0 = silu_f32(g0[i] * gs) * (u0[i] * gs);
+    const float a1 = silu_f32(g1[i] * gs) * (u1[i] * gs);
+    const float amax = row16_max(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
+    const int e = mx_scale_code_emax(amax, 2);
+    const float inv = mx_inv_scale(e);
+    const uint32_t q0 = f32_to_e2m1(a0 * inv), q1 = f32_to_e2m1(a1 * inv);
+    const uint32_t n0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q0, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    const uint32_t n1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q1, 0xB1, 0xF, 0xF, false);
+    if (ok && row < p.m && (c16 & 1) == 0) {
+      uint8_t* rq = outq + row * (p.ldo / 2);
+      rq[col0 / 2] = (uint8_t)(q0 | (n0 << 4));
+      rq[(col0 + 16) / 2] = (uint8_t)(q1 | (n1 << 4));
+      if (c16 == 0) outs[row * (p.ldo / 32) + (col0 - c16) / 32] = (uint8_t)e;
+    }
+  }
+}
+
 // Partial tile (fp32, natural [split][row][col] layout) of one 16x16 C tile.
 __device__ __forceinline__ void store_partial(const GemmParams& p, int split, int64_t row_base, int64_t col,
                                               int64_t ncols, const f32x4_t& v, int lg) {
@@ -397,9 +427,10 @@ constexpr int stream_waves(int fmt, int kw, int amode, int epi) {
 template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
 __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
   using T = Tr<FMT>;
-  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
+  static_assert(EPI != EPI_SWIGLU_MXFP4 && FMT != F_MXFP4_MXFP4, "W4A4 runs on the tile kernel only");
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
-  static_assert(EPI != EPI_SWIGLU_MXFP8 || WN % 4 == 0, "32-column MXFP8 blocks");
+  static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
   constexpr int kRowB = StreamLds<FMT>::kRowB;
   constexpr int kCPR = kRowB / 16;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
@@ -862,9 +893,9 @@ struct TileCfg {
       (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
-  static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
-  static_assert(EPI != EPI_SWIGLU_MXFP8 || WN % 4 == 0, "32-column MXFP8 blocks");
+  static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
   static_assert(kA % 1024 == 0, "whole 1-KB activation DMA instructions");
   static_assert(kS * kStage <= 160 * 1024, "LDS budget");
   static_assert(FMT != F_INT || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
@@ -1321,6 +1352,11 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int j = 0; j < WN / 2; ++j)
         store_swiglu_bf16(p, gs, rb, (int64_t)nts[j] * 16 + c16, acc[ms][j], acc[ms][j + WN / 2], lg);
+    } else if constexpr (EPI == EPI_SWIGLU_MXFP4) {
+#pragma unroll
+      for (int jj = 0; jj < WN / 4; ++jj)
+        store_swiglu_mxfp4(p, gs, rb, (int64_t)nts[2 * jj] * 16 + c16, acc[ms][2 * jj], acc[ms][2 * jj + WN / 2],
+                           acc[ms][2 * jj + 1], acc[ms][2 * jj + 1 + WN / 2], lg, c16);
     } else {
 #pragma unroll
       for (int jj = 0; jj < WN / 4; ++jj)
@@ -1337,7 +1373,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 
 template <int FMT, int EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p, int block_m) {
-  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8);
+  static_assert(EPI != EPI_SWIGLU_MXFP4, "no split-K for the MXFP4 SwiGLU epilogue");
+  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
   constexpr int kCols = (EPI == EPI_SWIGLU_MXFP8) ? 32 : 8;
   const int64_t ncols = kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
   const int64_t outc = p.n;
@@ -1521,6 +1558,17 @@ struct Instance {
   HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
   HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
 
+// Tile-only MoE instances (W4A4)
+#define HUM_MOE_TILE_SET(F, EPI_UP)                        \
+  HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 8, 4, A_GATHER, EPI_UP),                     \
+  HUM_TILE(F, 1, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 2, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 4, 4, A_DIRECT, EPI_SCATTER),                \
+  HUM_TILE(F, 8, 4, A_DIRECT, EPI_SCATTER)
+
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
   HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
@@ -1547,6 +1595,7 @@ static const Instance kInstances[] = {
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_DIRECT, EPI_SCATTER),
     HUM_MOE_SET(F_MXFP4_BF16, EPI_SWIGLU_BF16),
     HUM_MOE_SET(F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8),
+    HUM_MOE_TILE_SET(F_MXFP4_MXFP4, EPI_SWIGLU_MXFP4),
 };
 
 struct ReduceInstance {

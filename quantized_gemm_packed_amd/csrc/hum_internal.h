@@ -86,7 +86,7 @@ hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t t
                              int64_t h, void* out, void* stream);
 
 // GEMM epilogues / A-row modes
-enum Epi : int { EPI_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_SWIGLU_MXFP8 = 2, EPI_SCATTER = 3 };
+enum Epi : int { EPI_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_SWIGLU_MXFP8 = 2, EPI_SCATTER = 3, EPI_SWIGLU_MXFP4 = 4 };
 enum AMode : int { A_DIRECT = 0, A_GATHER = 1 };
 
 struct GemmParams {
