@@ -13,6 +13,10 @@ carry their own format.  Readings where the page is silent:
   tensor granularity is one scale per expert.
 * the second-level scale is one float32 per expert, multiplied after the
   first-level scale.
+* "block" granularity (the block-scaled FP8 W8A8 of section "W8A8 / W4A8 /
+  W4A4", whose block shape the page does not give): one scale per
+  group_size x group_size block of W (rows n, columns k), block (n // G,
+  k // G); scales are [E][ceil(N/G)][K/G].
 
 The layer is C[m, n] = sum_k A[m, k] * W[n, k] (+ bias[n]) evaluated in
 float64 from the exactly dequantized operands; the GPU returns bf16(C).
@@ -24,7 +28,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .formats import decode_bf16, decode_scale, decode_weight_codes, decode_e4m3
-from .quant import dequant_fp8_per_token, dequant_mxfp4, dequant_mxfp8
+from .quant import dequant_fp8_group, dequant_fp8_per_token, dequant_mxfp4, dequant_mxfp8
 
 
 @dataclass
@@ -40,7 +44,7 @@ class WeightDesc:
     k: int
 
     def groups(self) -> int:
-        if self.scale_gran == "group":
+        if self.scale_gran in ("group", "block"):
             return self.k // self.group_size
         return 1
 
@@ -48,6 +52,9 @@ class WeightDesc:
 def _expand_groups(a, desc: WeightDesc):
     """[E][N or 1][groups] -> [E][N][K] by repeating each group along K."""
     a = np.asarray(a, dtype=np.float64)
+    if desc.scale_gran == "block":
+        rep = np.repeat(np.repeat(a, desc.group_size, axis=2), desc.group_size, axis=1)[:, :desc.n, :]
+        return rep
     if desc.scale_gran == "group":
         rep = np.repeat(a, desc.group_size, axis=2)
     else:
@@ -88,6 +95,8 @@ def activations(act_fmt: str, x=None, q=None, scales=None):
         return dequant_mxfp8(q, scales)
     if act_fmt == "mxfp4":
         return dequant_mxfp4(q, scales)
+    if act_fmt == "fp8_group":
+        return dequant_fp8_group(q, scales)
     raise ValueError(act_fmt)
 
 

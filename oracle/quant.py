@@ -14,6 +14,10 @@ scaling rule; the readings taken here are:
   E = clamp(floor(log2 amax) - 8 + 127, 0, 254) (8 = emax of E4M3), an
   all-zero block takes E = 127; X = 2^(E-127); q = E4M3_RNE_SAT(x / X).
   floor(log2) is read from the exponent field, never from a rounded log.
+* per-token-group FP8 (the activations of block-scaled FP8 W8A8, section
+  "W8A8 / W4A8 / W4A4"; groups of 128 along K, the page gives no shape):
+  the per-token rule applied to each group of 128: s = fl32(amax / 448)
+  (1.0 for an all-zero group), q = E4M3_RNE_SAT(fl32(x / s)).
 * MXFP4 activations (the W4A4 = MXFP4 x MXFP4 combination of the section
   "W8A8 / W4A8 / W4A4"): the same OCP rule with the emax of E2M1 (2):
   E = clamp(floor(log2 amax) - 2 + 127, 0, 254), an all-zero block takes
@@ -92,3 +96,22 @@ def dequant_mxfp4(packed, e8m0):
     v = decode_e2m1(unpack_nibbles(packed))
     k = v.shape[1]
     return (v.reshape(m, k // 32, 32) * decode_e8m0(e8m0)[..., None]).reshape(m, k)
+
+
+def quant_fp8_group(x_f32, group: int = 128):
+    """x: float32 [M, K] (bf16 values widened), K % group == 0
+    -> (codes uint8 [M, K], scales f32 [M, K/group])."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    m, k = x.shape
+    assert k % group == 0
+    xg = x.reshape(m, k // group, group)
+    amax = np.abs(xg).max(axis=2) if k else np.zeros((m, 0), np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    r = (xg / s[..., None]).astype(np.float32)         # IEEE fp32 division
+    return encode_e4m3(r.astype(np.float64)).reshape(m, k), s
+
+
+def dequant_fp8_group(codes, s, group: int = 128):
+    m, k = codes.shape
+    v = decode_e4m3(codes).reshape(m, k // group, group)
+    return (v * np.asarray(s, np.float32).astype(np.float64)[..., None]).reshape(m, k)

@@ -52,7 +52,9 @@ def brute_linear(desc, a_vals, codes_unpacked, scales, zeros, gscale):
         for n in range(desc.n):
             acc = Fraction(0)
             for kk in range(k):
-                if desc.scale_gran == "group":
+                if desc.scale_gran == "block":
+                    gi, ni = kk // desc.group_size, n // desc.group_size
+                elif desc.scale_gran == "group":
                     gi, ni = kk // desc.group_size, n
                 elif desc.scale_gran == "channel":
                     gi, ni = 0, n
@@ -78,16 +80,17 @@ CASES = [
     ("e2m1", "group", 32, "e8m0", False, False),
     ("e2m1", "group", 16, "bf16", False, True),
     ("e4m3", "channel", 0, "f32", False, False),
+    ("e4m3", "block", 16, "f32", False, False),
 ]
 
 
 @pytest.mark.parametrize("wd,gran,gs,sd,zp,gl", CASES)
 def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
     g = np.random.default_rng(hash((wd, gran, gs, sd)) & 0xFFFF)
-    m, n, k = 3, 5, 64
+    m, n, k = 3, (40 if gran == "block" else 5), 64
     desc = G.WeightDesc(wd, gran, gs, sd, zp, gl, 1, n, k)
     ng = desc.groups()
-    sn = 1 if gran == "tensor" else n
+    sn = 1 if gran == "tensor" else (-(-n // gs) if gran == "block" else n)
     if wd == "e4m3":
         cu = g.integers(0, 256, size=(n, k))
         cu = np.where((cu & 0x7F) == 0x7F, 0x7E, cu).astype(np.uint8)

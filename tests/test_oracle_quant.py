@@ -159,3 +159,44 @@ def test_mxfp4_representable_round_trip():
     x = Q.dequant_mxfp4(packed, e)
     q2, e2 = Q.quant_mxfp4(x)
     assert np.array_equal(e2, e) and np.array_equal(q2, packed)
+
+
+
+def test_fp8_group_amax_maps_to_448_per_group():
+    g = np.random.default_rng(18)
+    x = _bf16_vals(g, (16, 512))
+    x[3, 128:256] = 0.0
+    q, s = Q.quant_fp8_group(x)
+    assert s.shape == (16, 4) and s.dtype == np.float32
+    assert s[3, 1] == 1.0 and np.all(q[3, 128:256] == 0)
+    for r in range(16):
+        for b in range(4):
+            blk = x[r, 128 * b:128 * b + 128]
+            amax = Fraction(float(np.abs(blk).max()))
+            if amax == 0:
+                continue
+            assert s[r, b] == np.float32(float(amax / 448))
+            j = int(np.abs(blk).argmax())
+            assert q[r, 128 * b + j] == (0xFE if blk[j] < 0 else 0x7E)
+
+
+def test_fp8_group_equals_per_token_on_each_group():
+    g = np.random.default_rng(19)
+    x = _bf16_vals(g, (8, 384), scale=5.0)
+    q, s = Q.quant_fp8_group(x)
+    for b in range(3):
+        qt, st = Q.quant_fp8_per_token(x[:, 128 * b:128 * b + 128])
+        assert np.array_equal(q[:, 128 * b:128 * b + 128], qt) and np.array_equal(s[:, b], st)
+
+
+def test_fp8_group_representable_round_trip():
+    g = np.random.default_rng(20)
+    codes = g.integers(0, 0x7F, size=(8, 256)).astype(np.uint8)
+    codes |= (g.integers(0, 2, size=codes.shape) << 7).astype(np.uint8)
+    codes = np.where((codes & 0x7F) > 0x7E, 0x7E, codes).astype(np.uint8)
+    codes[:, 5] = 0x7E
+    codes[:, 133] = 0xFE
+    s = np.ldexp(1.0, g.integers(-10, 4, size=(8, 2))).astype(np.float32)
+    x = Q.dequant_fp8_group(codes, s).astype(np.float32)
+    q2, s2 = Q.quant_fp8_group(x)
+    assert np.array_equal(s2, s) and np.array_equal(q2, codes)
