@@ -56,22 +56,27 @@ typedef enum hum_dtype {
 typedef enum hum_scale_gran {
   HUM_SCALE_TENSOR = 0,   /* one scale per expert          : scales [E][1][1] */
   HUM_SCALE_CHANNEL = 1,  /* one scale per output channel  : scales [E][N][1] */
-  HUM_SCALE_GROUP = 2     /* one scale per group along K   : scales [E][N][K/G] */
+  HUM_SCALE_GROUP = 2,    /* one scale per group along K   : scales [E][N][K/G] */
+  HUM_SCALE_BLOCK = 3     /* one scale per G x G block of W (rows n, columns k):
+                             scales [E][ceil(N/G)][K/G]; E4M3 weights, G = 128
+                             (block-scaled FP8 W8A8) */
 } hum_scale_gran;
 
 typedef enum hum_act_fmt {
   HUM_ACT_BF16 = 0,       /* bf16 activations as given (WnA16) */
   HUM_ACT_FP8_TOKEN = 1,  /* E4M3 codes + one f32 scale per row (W8A8) */
   HUM_ACT_MXFP8 = 2,      /* E4M3 codes + one E8M0 scale per 32 along K (W4A8) */
-  HUM_ACT_MXFP4 = 3       /* E2M1 codes, two per byte (even k in the low nibble),
-                             + one E8M0 scale per 32 along K (W4A4, dense only) */
+  HUM_ACT_MXFP4 = 3,      /* E2M1 codes, two per byte (even k in the low nibble),
+                             + one E8M0 scale per 32 along K (W4A4) */
+  HUM_ACT_FP8_GROUP = 4   /* E4M3 codes + one f32 scale per row per 128 along K
+                             (block-scaled FP8 W8A8, dense only) */
 } hum_act_fmt;
 
 /* The quantization description of one weight tensor [E][N][K]. */
 typedef struct hum_weight_desc {
   int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_E2M1 | HUM_E4M3 */
   int32_t scale_gran;        /* hum_scale_gran */
-  int32_t group_size;        /* K elements per group (HUM_SCALE_GROUP only) */
+  int32_t group_size;        /* K elements per group (HUM_SCALE_GROUP), block edge (HUM_SCALE_BLOCK) */
   int32_t scale_dtype;       /* HUM_BF16 | HUM_F32 | HUM_E8M0 */
   int32_t has_zero_point;    /* 0/1; UINT4 only; zeros u8 [E][N][K/G] (0..15) */
   int32_t has_global_scale;  /* 0/1; second-level f32 scale per expert, [E] */
@@ -131,6 +136,8 @@ hum_status hum_dequant_weight(const hum_weight_desc* desc, const void* packed,
  *   HUM_ACT_MXFP8     : scales u8 [m][k/32], E = clamp(floor(log2 amax) - 8
  *                       + 127, 0, 254) (127 for a zero block),
  *                       q = E4M3_RNE_SAT(x / 2^(E-127));
+ *   HUM_ACT_FP8_GROUP : scales f32 [m][k/128], the FP8_TOKEN rule applied to
+ *                       each group of 128 along k;
  *   HUM_ACT_MXFP4     : E2M1 codes q [m][k/2] (two per byte, even k in the
  *                       low nibble), scales u8 [m][k/32], E = clamp(floor(
  *                       log2 amax) - 2 + 127, 0, 254) (127 for a zero block),
@@ -138,8 +145,9 @@ hum_status hum_dequant_weight(const hum_weight_desc* desc, const void* packed,
  * The formats are those named in the "End-to-end inference performance"
  * ("tokenwise FP8"), "Choosing the activation type" (MXFP8) and "W8A8 /
  * W4A8 / W4A4" (MXFP4 activations) sections of the Humming announcement;
- * the scale rules are the OCP ones.  k must be a multiple of 32 for MXFP8
- * and MXFP4. */
+ * the scale rules are the OCP ones (FP8_GROUP: the activations of the
+ * block-scaled FP8 W8A8 of the same section).  k must be a multiple of 32
+ * for MXFP8 and MXFP4, of 128 for FP8_GROUP. */
 hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf16,
                          int64_t ld_x, void* q, void* scales, void* stream);
 

@@ -15,8 +15,8 @@ from dataclasses import dataclass
 __all__ = [
     "HumError", "WeightDesc", "TileConfig", "lib_path", "load_library",
     "BF16", "F32", "INT4", "UINT4", "E2M1", "E4M3", "E8M0",
-    "SCALE_TENSOR", "SCALE_CHANNEL", "SCALE_GROUP",
-    "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8", "ACT_MXFP4",
+    "SCALE_TENSOR", "SCALE_CHANNEL", "SCALE_GROUP", "SCALE_BLOCK",
+    "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8", "ACT_MXFP4", "ACT_FP8_GROUP",
     "packed_weight_bytes", "prepare_weight", "dequant_weight", "quant_act",
     "select_config", "linear_workspace_bytes", "linear", "moe_workspace_bytes",
     "moe_gemm", "moe_align", "moe_reduce", "Workspace", "header_functions",
@@ -24,8 +24,8 @@ __all__ = [
 
 BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0 = range(7)
 KERNEL_TILE, KERNEL_STREAM = range(2)
-SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP = range(3)
-ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4 = range(4)
+SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP, SCALE_BLOCK = range(4)
+ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4, ACT_FP8_GROUP = range(5)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_HERE), "include", "hum.h")
@@ -147,9 +147,10 @@ def _gpu(t, name):
 
 
 _DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3}
-_GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP}
+_GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP, "block": SCALE_BLOCK}
 _SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0}
-_AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4}
+_AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4,
+       "fp8_group": ACT_FP8_GROUP}
 
 
 def make_desc(weight_dtype, scale_gran, group_size, scale_dtype, n, k, num_experts=1,
@@ -211,6 +212,8 @@ def quant_act(act_fmt, x):
     q = torch.empty((m, k // 2 if fmt == ACT_MXFP4 else k), dtype=torch.uint8, device=x.device)
     if fmt == ACT_FP8_TOKEN:
         s = torch.empty((m,), dtype=torch.float32, device=x.device)
+    elif fmt == ACT_FP8_GROUP:
+        s = torch.empty((m, k // 128), dtype=torch.float32, device=x.device)
     else:
         s = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
     _check(load_library().hum_quant_act(fmt, m, k, _ptr(x), k, _ptr(q), _ptr(s), _stream(x.device)))

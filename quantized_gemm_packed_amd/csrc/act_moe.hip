@@ -72,6 +72,52 @@ hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t l
 }
 
 // ---------------------------------------------------------------------------
+// Per-token-group FP8 (groups of 128 along K): each thread quantizes 8
+// elements; a DPP row of 16 lanes owns one group.  The per-token rule per
+// group: s = amax / 448 (IEEE f32 division; 1 for an all-zero group),
+// q = E4M3_RNE_SAT(x / s).
+
+__global__ __launch_bounds__(256) void quant_fp8_group_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                              int64_t m, int64_t k, uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;  // chunks per row
+  const bool valid = id < m * cpr;
+  const int64_t row = valid ? id / cpr : 0;
+  const int64_t c8 = valid ? id % cpr : 0;
+  u32x4_t v = {0, 0, 0, 0};
+  if (valid) v = *reinterpret_cast<const u32x4_t*>(x + row * ldx + c8 * 8);
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(v[i] & 0xFFFF);
+    f[2 * i + 1] = bf16_bits_to_f32(v[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[i]));
+  amax = row16_max(amax);  // the 16 chunks of one 128-group are one DPP row
+  const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (!valid) return;
+  uint2 o;
+  o.x = f32x2_to_e4m3x2(f[0] / sc, f[1] / sc) | (f32x2_to_e4m3x2(f[2] / sc, f[3] / sc) << 16);
+  o.y = f32x2_to_e4m3x2(f[4] / sc, f[5] / sc) | (f32x2_to_e4m3x2(f[6] / sc, f[7] / sc) << 16);
+  *reinterpret_cast<uint2*>(q + row * k + c8 * 8) = o;
+  if ((c8 & 15) == 0) s[row * (k / 128) + c8 / 16] = sc;
+}
+
+hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
+                                  void* stream) {
+  if (m == 0) return HUM_OK;
+  const int64_t chunks = m * (k / 8);
+  quant_fp8_group_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_fp8_group launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8: each thread quantizes 8 elements; a DPP quad owns one 32-block.
 
 __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t ldx,

@@ -41,8 +41,12 @@ hum_status check_desc(const hum_weight_desc* d) {
   if (d->n > (int64_t)1 << 30 || d->k > (int64_t)1 << 21) return set_error(HUM_ERR_UNSUPPORTED, "n/k too large");
   if (d->has_zero_point != 0 && d->has_zero_point != 1) return set_error(HUM_ERR_INVALID_ARG, "has_zero_point must be 0/1");
   if (d->has_global_scale != 0 && d->has_global_scale != 1) return set_error(HUM_ERR_INVALID_ARG, "has_global_scale must be 0/1");
-  if (d->scale_gran < HUM_SCALE_TENSOR || d->scale_gran > HUM_SCALE_GROUP) return set_error(HUM_ERR_INVALID_ARG, "bad scale_gran");
-  if (d->scale_gran == HUM_SCALE_GROUP) {
+  if (d->scale_gran < HUM_SCALE_TENSOR || d->scale_gran > HUM_SCALE_BLOCK) return set_error(HUM_ERR_INVALID_ARG, "bad scale_gran");
+  if (d->scale_gran == HUM_SCALE_BLOCK && (d->weight_dtype != HUM_E4M3 || d->group_size != 128))
+    return set_error(HUM_ERR_UNSUPPORTED, "2-D block scales take E4M3 weights and 128 x 128 blocks");
+  if ((d->act_fmt == HUM_ACT_FP8_GROUP) != (d->scale_gran == HUM_SCALE_BLOCK))
+    return set_error(HUM_ERR_UNSUPPORTED, "block-scaled weights run with per-group FP8 activations (and only they)");
+  if (d->scale_gran == HUM_SCALE_GROUP || d->scale_gran == HUM_SCALE_BLOCK) {
     if (d->group_size <= 0 || d->k % d->group_size) return set_error(HUM_ERR_INVALID_ARG, "group_size must divide k");
   }
   switch (d->weight_dtype) {
@@ -64,7 +68,8 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->scale_gran == HUM_SCALE_GROUP) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take per-channel or per-tensor scales");
       if (d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take f32 scales");
       if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 takes no zero point");
-      if (d->act_fmt != HUM_ACT_FP8_TOKEN) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights run with per-token FP8 activations");
+      if (d->act_fmt != HUM_ACT_FP8_TOKEN && d->act_fmt != HUM_ACT_FP8_GROUP)
+        return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights run with per-token or per-group FP8 activations");
       return HUM_OK;
     default:
       return set_error(HUM_ERR_UNSUPPORTED, "unsupported weight dtype %d", d->weight_dtype);
@@ -73,7 +78,7 @@ hum_status check_desc(const hum_weight_desc* d) {
 
 int fmt_of(const hum_weight_desc* d) {
   if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
-  if (d->weight_dtype == HUM_E4M3) return F_FP8;
+  if (d->weight_dtype == HUM_E4M3) return d->scale_gran == HUM_SCALE_BLOCK ? F_FP8_BLOCK : F_FP8;
   if (d->act_fmt == HUM_ACT_MXFP8) return F_MXFP4_MXFP8;
   return d->act_fmt == HUM_ACT_MXFP4 ? F_MXFP4_MXFP4 : F_MXFP4_BF16;
 }
@@ -86,7 +91,7 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   L->kb = d->k / kKBlk;
   L->kb4 = cdiv(L->kb, 4);
   const int f = fmt_of(d);
-  L->code_bytes = (f == F_FP8) ? 32 : 16;
+  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK) ? 32 : 16;
   L->codes_per_expert = L->nt * L->kb * 64 * L->code_bytes;
   if (f == F_INT) {
     const bool grp = d->scale_gran == HUM_SCALE_GROUP && d->group_size < d->k;
@@ -100,6 +105,11 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   } else if (f == F_FP8) {
     L->ng = 1;
     L->scales_per_expert = align256(L->nt * 16 * 4);
+  } else if (f == F_FP8_BLOCK) {
+    // one f32 per 16-column sub-tile and K-block (a sub-tile lies in one
+    // 128-row block)
+    L->ng = L->kb;
+    L->scales_per_expert = align256(L->nt * L->kb * 4);
   } else {
     L->ng = L->kb * 4;
     L->scales_per_expert = L->nt * L->kb4 * 64 * 4;
@@ -159,7 +169,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
-  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4) {
+  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK) {
     // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
     // wave: the fewest that keep the activation bytes each workgroup reads
     // (from L2) at or below its weight bytes.  Four K-waves when their K
@@ -217,6 +227,16 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
     c.split_k = pick_split(wgs, 4, kb, 1, 4, target);
+    if (fmt_of(d) == F_FP8_BLOCK) {
+      // block-scaled FP8 (no decode kernel): small tiles with three stages
+      // to M = 256, then the FP8 128 x 128 tiles
+      if (m <= 256) {
+        c.wave_m = 2;
+        c.wave_n = 2;
+        c.stages = 3;
+      }
+      c.split_k = 1;
+    }
     if (fmt_of(d) == F_MXFP4_MXFP4) {
       // W4A4 (N = 7168, K = 2048): three stages throughout, 32 x 128 tiles
       // to M = 256 and 64 x 256 above, no split-K (its reduce launch costs
@@ -303,7 +323,9 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
   if (quant_a) {
     off = align256(off + (d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 2) : m * d->k));
     w.as = off;
-    off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 || d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 32) : m * 4));
+    off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 || d->act_fmt == HUM_ACT_MXFP4
+                              ? m * (d->k / 32)
+                              : (d->act_fmt == HUM_ACT_FP8_GROUP ? m * (d->k / 128) * 4 : m * 4)));
   }
   w.rowsum = off;
   if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
@@ -364,7 +386,11 @@ hum_status hum_quant_act(int32_t act_fmt, int64_t m, int64_t k, const void* x_bf
     if (k % 32) return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 needs k % 32 == 0");
     return launch_quant_mxfp4(m, k, x_bf16, ld_x, q, static_cast<uint8_t*>(scales), stream);
   }
-  return set_error(HUM_ERR_INVALID_ARG, "act_fmt must be FP8_TOKEN, MXFP8 or MXFP4");
+  if (act_fmt == HUM_ACT_FP8_GROUP) {
+    if (k % 128) return set_error(HUM_ERR_UNSUPPORTED, "FP8_GROUP needs k % 128 == 0");
+    return launch_quant_fp8_group(m, k, x_bf16, ld_x, q, static_cast<float*>(scales), stream);
+  }
+  return set_error(HUM_ERR_INVALID_ARG, "act_fmt must be FP8_TOKEN, MXFP8, MXFP4 or FP8_GROUP");
 }
 
 hum_status hum_select_config(const hum_weight_desc* desc, int64_t m, hum_tile_config* cfg_out) {
@@ -460,7 +486,8 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.a = a_use;
   p.lda = desc->k;
   p.a_scale = as_use;
-  p.a_scale_ld = desc->k / 32;
+  // bytes per row of activation scales: E8M0 per 32, or f32 per 128
+  p.a_scale_ld = desc->act_fmt == HUM_ACT_FP8_GROUP ? (desc->k / 128) * 4 : desc->k / 32;
   p.m = m;
   p.sorted = nullptr;
   p.block_expert = nullptr;
@@ -479,7 +506,8 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
                                             : m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ? 2 : 1);
-  p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32) : 0;
+  p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32)
+                    : (desc->act_fmt == HUM_ACT_FP8_GROUP ? m * (desc->k / 128) * 4 : 0);
   return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);
 }
 

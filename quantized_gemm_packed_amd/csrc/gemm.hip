@@ -36,6 +36,10 @@
 //                  16x16x128 MFMA, both E8M0 scales as operands.
 //   F_MXFP4_MXFP4  E2M1 activations x E2M1 weights (W4A4) on the same
 //                  MFMA; prefill-tile kernel only.
+//   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
+//                  K-block (128) at a time, each K-block's result scaled by
+//                  the row's group scale times the 128 x 128 weight-block
+//                  scale (acc += sa * sw * P); prefill-tile kernel only.
 //
 // Split-K across workgroups writes fp32 partials; a separate reduce kernel
 // sums them in split order (deterministic) and applies the epilogue.
@@ -54,7 +58,7 @@ struct Tr {
   static constexpr int kAElem = (FMT == F_INT || FMT == F_MXFP4_BF16) ? 2 : 1;  // activation bytes (FP4: 1/2)
   static constexpr bool kA4 = (FMT == F_MXFP4_MXFP4);                           // 4-bit activations
   static constexpr int kARowB = kA4 ? 64 : 128 * kAElem;                        // activation bytes per row per K-block
-  static constexpr int kBWords = (FMT == F_FP8) ? 2 : 1;                         // 16-B words / lane / K-block
+  static constexpr int kBWords = (FMT == F_FP8 || FMT == F_FP8_BLOCK) ? 2 : 1;  // 16-B words / lane / K-block
   static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16);
   // bytes of an activation row of `ld` elements
   static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
@@ -260,7 +264,7 @@ __device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, con
                                                   f32x4_t c) {
   i32x8_t b8;
   b8[0] = f.w[0][0]; b8[1] = f.w[0][1]; b8[2] = f.w[0][2]; b8[3] = f.w[0][3];
-  if (FMT == F_FP8) {
+  if (FMT == F_FP8 || FMT == F_FP8_BLOCK) {
     b8[4] = f.w[Tr<FMT>::kBWords - 1][0]; b8[5] = f.w[Tr<FMT>::kBWords - 1][1];
     b8[6] = f.w[Tr<FMT>::kBWords - 1][2]; b8[7] = f.w[Tr<FMT>::kBWords - 1][3];
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 127, 0, 127);
@@ -876,7 +880,9 @@ struct TileCfg {
   static constexpr int kA = kTM * kRowB;                         // activation tile (whole KB)
   static constexpr int kAI = kA / 1024;                          // its 1-KB DMA instructions
   static constexpr int kAIW = (kAI + 3) / 4;                     // ... per wave
-  static constexpr bool kX = (FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4);  // a dword per row (MX scales)
+  // a dword per row and K-block: MX scales (E8M0 per 32) or the f32 scale of
+  // a per-group FP8 row
+  static constexpr bool kX = (FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_FP8_BLOCK);
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
   static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
   // Each wave loads its own weight fragments straight into registers,
@@ -889,8 +895,9 @@ struct TileCfg {
   // register fragments (two stages deep) are exact; two stages issue them
   // from inline assembly and wait for everything at the end of each step.
   static constexpr bool kTracked = (kS == 3);
-  static constexpr int kMI =
-      (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) ? WN : 0);
+  static constexpr int kMI = (FMT == F_INT || FMT == F_FP8_BLOCK)
+                                 ? 1
+                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
@@ -1069,6 +1076,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
+  } else if constexpr (FMT == F_FP8_BLOCK) {
+    // lane l < WN copies the f32 block scale of sub-tile l (per K-block)
+    rms = rsrc_words(wp.meta, p.scales_per_expert);
+    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
+    uint32_t ntl = 0;
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns)
+      if (lane == ns && ntv[ns]) ntl = (uint32_t)nts[ns];
+    mi_off = ntl * (uint32_t)p.kb_count * 4u;
   }
 
   // copies of K-block kb into stage st (this wave's share) and its weight
@@ -1117,6 +1133,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     if constexpr (FMT == F_INT) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
+    } else if constexpr (FMT == F_FP8_BLOCK) {
+      dma4(rms, rmsr, mw, mi_off + (uint32_t)kb * 4u);
     } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
@@ -1174,6 +1192,30 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       mw[ns] = 0;
       if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
+    }
+    if constexpr (FMT == F_FP8_BLOCK) {
+      // the WN block scales of this K-block, side by side
+      struct alignas(4 * WN) Words { float w[WN]; };
+      const Words sw = *reinterpret_cast<const Words*>(mbase);
+#pragma unroll
+      for (int ms = 0; ms < WM; ++ms) {
+        const int r = ms * 16 + c16;
+        const int swr = (r >> 1) & 7;
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + ((lg ^ swr) * 16));
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (((4 + lg) ^ swr) * 16));
+        i32x8_t a8;
+        a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
+        a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
+        // the f32 group scales of this lane's 4 output rows (C layout)
+        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(St::x(st) + (ms * 16 + 4 * lg) * 4);
+#pragma unroll
+        for (int ns = 0; ns < WN; ++ns) {
+          const f32x4_t t = mfma_f8_kblock<FMT>(a8, 127, bf[ns], 0u, kb, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[ms][ns][i] = __builtin_fmaf(sa[i] * sw.w[ns], t[i], acc[ms][ns][i]);
+        }
+      }
+      return;
     }
     if constexpr (FMT == F_INT) {
       // this lane's scale words of the WN sub-tiles, side by side (one
@@ -1589,6 +1631,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_MXFP4_BF16),
     HUM_DENSE_SET(F_MXFP4_MXFP8),
     HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
+    HUM_DENSE_TILE_SET(F_FP8_BLOCK),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1611,6 +1654,7 @@ static const ReduceInstance kReduces[] = {
     {F_MXFP4_BF16, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SCATTER>},
     {F_MXFP4_MXFP8, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_BF16>},
     {F_MXFP4_MXFP4, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP4, EPI_BF16>},
+    {F_FP8_BLOCK, EPI_BF16, splitk_reduce_kernel<F_FP8_BLOCK, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

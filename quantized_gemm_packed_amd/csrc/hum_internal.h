@@ -55,7 +55,7 @@ struct Layout {
   int scale_f32 = 0;              // INT formats: 1 = f32 scales, 0 = bf16
 };
 
-enum Fmt : int { F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4 };
+enum Fmt : int { F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5 };
 
 // Validates the description; on failure sets the thread-local error and
 // returns a non-OK status.
@@ -78,6 +78,8 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
                               uint8_t* s, void* stream);
 hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
                               uint8_t* s, void* stream);
+hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
+                                  void* stream);
 hum_status launch_zero(void* p, size_t bytes, void* stream);
 hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
                         int32_t block_m, int32_t* sorted, int32_t* offsets, int32_t* counts,

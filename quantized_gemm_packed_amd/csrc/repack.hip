@@ -202,6 +202,21 @@ __global__ void repack_fp8_meta_kernel(RepackArgs a) {
   reinterpret_cast<float*>(a.packed + a.scales_off + e * a.scales_pe)[n] = v;
 }
 
+// Block-scaled FP8 meta: one f32 per (e, 16-column sub-tile, K-block), the
+// scale of the 128 x 128 block the sub-tile's rows and the K-block lie in.
+__global__ void repack_fp8_block_meta_kernel(RepackArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = a.nt * a.kb;
+  if (tid >= (int64_t)a.num_experts * per) return;
+  const int64_t kb = tid % a.kb;
+  const int64_t nt = (tid / a.kb) % a.nt;
+  const int64_t e = tid / per;
+  const int64_t n = nt * kNSub;
+  float v = 1.0f;
+  if (n < a.n) v = reinterpret_cast<const float*>(a.scales)[(e * a.src_n + n / 128) * a.src_ng + kb];
+  reinterpret_cast<float*>(a.packed + a.scales_off + e * a.scales_pe)[nt * a.kb + kb] = v;
+}
+
 __global__ void repack_gscale_kernel(RepackArgs a) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= a.num_experts) return;
@@ -238,8 +253,8 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   a.co_pe = L.co_per_expert;
   a.kbc = L.kbc;
   a.kb_per_group = L.kb_per_group;
-  a.src_n = (d->scale_gran == HUM_SCALE_TENSOR) ? 1 : d->n;
-  a.src_ng = (d->scale_gran == HUM_SCALE_GROUP) ? d->k / d->group_size : 1;
+  a.src_n = (d->scale_gran == HUM_SCALE_TENSOR) ? 1 : (d->scale_gran == HUM_SCALE_BLOCK ? (d->n + 127) / 128 : d->n);
+  a.src_ng = (d->scale_gran == HUM_SCALE_GROUP || d->scale_gran == HUM_SCALE_BLOCK) ? d->k / d->group_size : 1;
   a.num_experts = d->num_experts;
   a.wdt = d->weight_dtype;
   a.scale_elem = d->scale_dtype == HUM_BF16 ? 2 : (d->scale_dtype == HUM_F32 ? 4 : 1);
@@ -255,6 +270,8 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
   } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
+  } else if (f == F_FP8_BLOCK) {
+    repack_fp8_block_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb, B), B, 0, s>>>(a);
   } else {
     repack_fp8_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * kNSub, B), B, 0, s>>>(a);
   }
@@ -274,6 +291,7 @@ struct DequantArgs {
   int64_t codes_off, scales_off, zeros_off;
   int64_t codes_pe, scales_pe, zeros_pe;
   int num_experts, wdt, scale_f32, has_zero;
+  int block;  // E4M3 with 2-D block scales
 };
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -308,7 +326,8 @@ __global__ void dequant_kernel(DequantArgs a) {
   float* orow = a.out + (e * a.n + n) * a.k + kb * kKBlk;
   if (a.wdt == HUM_E4M3) {
     const uint8_t* src = base + ((nt * a.kb + kb) * 64 + lane) * 32;
-    const float s = reinterpret_cast<const float*>(a.packed + a.scales_off + e * a.scales_pe)[n];
+    const float* sp = reinterpret_cast<const float*>(a.packed + a.scales_off + e * a.scales_pe);
+    const float s = a.block ? sp[nt * a.kb + kb] : sp[n];
     for (int j = 0; j < 32; ++j) {
       const int kk = (j < 16) ? (16 * lg + j) : (64 + 16 * lg + j - 16);
       orow[kk] = e4m3_value(src[j]) * s;
@@ -366,6 +385,7 @@ hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void*
   a.wdt = d->weight_dtype;
   a.scale_f32 = L.scale_f32;
   a.has_zero = d->has_zero_point;
+  a.block = d->scale_gran == HUM_SCALE_BLOCK;
   const int64_t total = (int64_t)d->num_experts * L.nt * L.kb * 64;
   dequant_kernel<<<grid_for(total, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(a);
   hipError_t err = hipGetLastError();

@@ -118,6 +118,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
     e = num_experts
     if scale_gran == "group":
         sn, sg = n, k // group
+    elif scale_gran == "block":
+        sn, sg = -(-n // group), k // group
     elif scale_gran == "channel":
         sn, sg = n, 1
     else:

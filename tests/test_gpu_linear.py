@@ -165,6 +165,53 @@ def test_w4a4_dense_random_vs_oracle(m):
     assert_tol(out, ref, f"w4a4 m={m}")
 
 
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("tile", TILE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_fp8_block_exact_every_tile(tile, split):
+    """Block-scaled FP8: every 128-group of a row holds small integers times a
+    power of two with one +-448 * 2^e, so its scale is 2^e and the codes are
+    exact; weights are E4M3 codes of small integers with power-of-two block
+    scales; every K-block's MFMA sum, scale product and accumulation is then
+    exact in fp32: bitwise equal to the oracle."""
+    m, n, k = 37, 272, 1024
+    g = synth.rng(38)
+    ints = g.integers(-8, 9, size=(m, k)).astype(np.float64)
+    ints[:, ::128] = np.where(g.integers(0, 2, size=(m, k // 128)) == 1, 448.0, -448.0)
+    # (exponent ranges kept narrow: the fp32 sums of a row then span < 2^24)
+    x = ints * np.ldexp(1.0, g.integers(-6, -3, size=(m, k // 128))).repeat(128, axis=1)
+    xb = oracle.formats.encode_bf16(x)
+    wv = g.integers(-8, 9, size=(1, n, k)).astype(np.float64)
+    codes = oracle.formats.encode_e4m3(wv)
+    scales = np.ldexp(1.0, g.integers(-9, -7, size=(1, -(-n // 128), k // 128))).astype(np.float32)
+    w = {"codes": codes, "scales": scales}
+    hd, od = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
+    packed = prepare(hd, w, "f32")
+    print(f"case fp8 block exact tile={tile} split={split}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_group(oracle.formats.decode_bf16(xb).astype(np.float32))
+    a = oracle.quant.dequant_fp8_group(q, s)
+    assert np.array_equal(a, oracle.formats.decode_bf16(xb))
+    ref = oracle.gemm.linear(od, a, w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
+def test_fp8_block_dense_random_vs_oracle(m):
+    """Block-scaled FP8 W8A8 at the selector's config (ragged N)."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_for(7, m), "e4m3", "block", 128, "f32", 1, n, k,
+                            scale_lo=0.0005, scale_hi=0.002)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(7, 100 + m)), (m, k))
+    hd, od = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
+    packed = prepare(hd, w, "f32")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_group(oracle.formats.decode_bf16(xb).astype(np.float32))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_fp8_group(q, s), w["codes"], w["scales"])
+    assert_tol(out, ref, f"fp8 block m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -306,7 +353,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e2m1_mxfp8", "e2m1_mxfp4"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -317,6 +364,10 @@ def test_empty_m_is_a_no_op(fmt):
     elif fmt == "e4m3":
         w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
         hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+        packed = prepare(hd, w, "f32")
+    elif fmt == "e4m3_block":
+        w = synth.quant_weights(52, "e4m3", "block", 128, "f32", 1, n, k)
+        hd, _ = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
         packed = prepare(hd, w, "f32")
     else:
         w = synth.moe_weights_mxfp4(51, 1, n, k)

@@ -46,6 +46,18 @@ def test_mxfp8_codes_bit_exact(m, k):
 
 
 @pytest.mark.parametrize("m,k", [(1, 128), (6, 2048), (37, 4096), (130, 1024)])
+def test_fp8_group_codes_bit_exact(m, k):
+    xb = _inputs(400 + m, m, k)
+    if m > 1:
+        xb[1, 128:256] = 0                                # an all-zero group
+    q, s = hum.quant_act("fp8_group", dev(xb))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant.quant_fp8_group(oracle.formats.decode_bf16(xb).astype(np.float32))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (6, 2048), (37, 4096), (130, 1024)])
 def test_mxfp4_codes_bit_exact(m, k):
     xb = _inputs(300 + m, m, k)
     q, s = hum.quant_act("mxfp4", dev(xb))

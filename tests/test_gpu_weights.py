@@ -23,6 +23,7 @@ FORMATS = [
     ("e2m1", "group", 32, "e8m0", False, False),
     ("e4m3", "channel", 0, "f32", False, False),
     ("e4m3", "tensor", 0, "f32", False, True),
+    ("e4m3", "block", 128, "f32", False, False),
 ]
 SHAPES = [(1, 40, 256), (3, 640, 1024), (2, 16, 128)]
 
@@ -34,9 +35,9 @@ def test_dequant_bit_exact(fmt, shape):
     e, n, k = shape
     if gran == "group" and gs == 0:
         gs = k
-    if gran == "group" and k % gs:
+    if gran in ("group", "block") and k % gs:
         pytest.skip("group does not divide k")
-    act = {"e4m3": "fp8_token"}.get(wd, "bf16")
+    act = {"e4m3": "fp8_group" if gran == "block" else "fp8_token"}.get(wd, "bf16")
     hd, od = descs(wd, gran, gs, sd, e, n, k, zero, glob, act)
     w = synth.quant_weights(hash((fmt, shape)) & 0xFFFF, wd, gran, gs, sd, e, n, k, zero, glob,
                             e8m0_lo=100, e8m0_hi=150)
