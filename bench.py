@@ -186,6 +186,34 @@ def dense_w8a8(hum, timer, iters):
     return out
 
 
+def dense_w8a16_fp8(hum, timer, iters):
+    """E4M3 weights (per-channel f32 scales) x bf16 activations, at the W8A8
+    layer's shape N = 7168, K = 2048."""
+    import synth
+    import torch
+    n, k = 7168, 2048
+    case = synth.dense_w8a8(synth.seed_for(8), 1, n, k)
+    desc = hum.make_desc("e4m3", "channel", 0, "f32", n, k, act_fmt="bf16")
+    packed = hum.prepare_weight(desc, _dev(case["codes"]), _dev(case["scales"]))
+    copies = rotate_copies(packed)
+    g = synth.rng(synth.seed_for(8, 1))
+    wbytes = n * k + n * 4
+    out = []
+    for m in synth.FP8_SWEEP_M:
+        x = _dev(synth.bf16_normal(g, (m, k)))
+        o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = hum.Workspace("cuda").get(hum.linear_workspace_bytes(desc, m))
+        fn = lambda i: hum.linear(desc, copies[i % len(copies)], x, out=o, workspace=ws)
+        timer.run(fn, 3)
+        t = timer.run(fn, iters)
+        flops = 2.0 * m * n * k
+        bound = "hbm" if m <= 128 else "mfma"
+        out.append({"m": m, "us": t * 1e6, "tflops": flops / t / 1e12, "weight_gbs": wbytes / t / 1e9,
+                    "bound": bound, "frac": (wbytes / t / HBM_PEAK) if bound == "hbm" else flops / t / BF16_PEAK,
+                    "tile": list(hum.select_config(desc, m).as_tuple())})
+    return out
+
+
 def dense_w8a8_block(hum, timer, iters):
     """Block-scaled FP8 W8A8 (128 x 128 weight-block scales, per-row groups of
     128 activations quantized in the call), at the W8A8 layer's shape."""
@@ -372,6 +400,7 @@ def main():
         sweep["dense_w4a16_int4_g128_m16_n512_k1024"] = dense_tiny(hum, timer, iters)
         sweep["dense_w8a8_fp8_n7168_k2048"] = dense_w8a8(hum, timer, iters)
         sweep["dense_w8a8_fp8_block128_n7168_k2048"] = dense_w8a8_block(hum, timer, iters)
+        sweep["dense_w8a16_fp8_n7168_k2048"] = dense_w8a16_fp8(hum, timer, iters)
         sweep["dense_w4a4_mxfp4_n7168_k2048"] = dense_w4a4(hum, timer, iters)
         del d["copies"]
         torch.cuda.empty_cache()

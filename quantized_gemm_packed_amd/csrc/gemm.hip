@@ -36,6 +36,9 @@
 //                  16x16x128 MFMA, both E8M0 scales as operands.
 //   F_MXFP4_MXFP4  E2M1 activations x E2M1 weights (W4A4) on the same
 //                  MFMA; prefill-tile kernel only.
+//   F_FP8_BF16     E4M3 weights x bf16 activations (W8A16): the hardware
+//                  FP8 -> bf16 conversion (exact), bf16 MFMA, per-channel
+//                  scales in the epilogue.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
@@ -55,11 +58,13 @@ namespace hum {
 
 template <int FMT>
 struct Tr {
-  static constexpr int kAElem = (FMT == F_INT || FMT == F_MXFP4_BF16) ? 2 : 1;  // activation bytes (FP4: 1/2)
+  static constexpr int kAElem =
+      (FMT == F_INT || FMT == F_MXFP4_BF16 || FMT == F_FP8_BF16) ? 2 : 1;  // activation bytes (FP4: 1/2)
   static constexpr bool kA4 = (FMT == F_MXFP4_MXFP4);                           // 4-bit activations
   static constexpr int kARowB = kA4 ? 64 : 128 * kAElem;                        // activation bytes per row per K-block
-  static constexpr int kBWords = (FMT == F_FP8 || FMT == F_FP8_BLOCK) ? 2 : 1;  // 16-B words / lane / K-block
-  static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16);
+  static constexpr int kBWords =
+      (FMT == F_FP8 || FMT == F_FP8_BLOCK || FMT == F_FP8_BF16) ? 2 : 1;  // 16-B words / lane / K-block
+  static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16 || FMT == F_FP8_BF16);
   // bytes of an activation row of `ld` elements
   static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
 };
@@ -246,6 +251,20 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
   if (FMT == F_INT) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) d[s] = int_dequant(f.w[0][s]);
+  } else if (FMT == F_FP8_BF16) {
+    // E4M3 -> bf16 is exact (3 mantissa bits, exponents within bf16's
+    // range): the hardware conversion with a unit scale, two codes per
+    // instruction; k-step s takes bytes 8s .. 8s+7 of the lane's 32
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w0 = f.w[s >> 1][2 * (s & 1)], w1 = f.w[s >> 1][2 * (s & 1) + 1];
+      u32x4_t o;
+      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+      d[s] = __builtin_bit_cast(bf16x8_t, o);
+    }
   } else {
     const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
 #pragma unroll
@@ -285,7 +304,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // the second-level scale); the per-token FP8 row scale is applied apart.
 template <int FMT>
 __device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, float gs) {
-  if (FMT == F_FP8) return gs * reinterpret_cast<const float*>(wmeta)[col];
+  if (FMT == F_FP8 || FMT == F_FP8_BF16) return gs * reinterpret_cast<const float*>(wmeta)[col];
   return gs;
 }
 
@@ -1561,9 +1580,9 @@ struct Instance {
   {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
 #define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
 
-// Ring depth in 1-KB weight fragments per sub-tile (FP8 fragments are 2 KB:
+// Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.
-#define HUM_PF(F, n) ((F) == F_FP8 ? ((n) > 1 ? (n) / 2 : 1) : (n))
+#define HUM_PF(F, n) (((F) == F_FP8 || (F) == F_FP8_BF16) ? ((n) > 1 ? (n) / 2 : 1) : (n))
 #define HUM_DENSE_SET(F)                                   \
   HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
   HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \
@@ -1632,6 +1651,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_MXFP4_MXFP8),
     HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
     HUM_DENSE_TILE_SET(F_FP8_BLOCK),
+    HUM_DENSE_SET(F_FP8_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1655,6 +1675,7 @@ static const ReduceInstance kReduces[] = {
     {F_MXFP4_MXFP8, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_BF16>},
     {F_MXFP4_MXFP4, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP4, EPI_BF16>},
     {F_FP8_BLOCK, EPI_BF16, splitk_reduce_kernel<F_FP8_BLOCK, EPI_BF16>},
+    {F_FP8_BF16, EPI_BF16, splitk_reduce_kernel<F_FP8_BF16, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

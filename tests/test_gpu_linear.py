@@ -212,6 +212,45 @@ def test_fp8_block_dense_random_vs_oracle(m):
     assert_tol(out, ref, f"fp8 block m={m}")
 
 
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_fp8_weights_bf16_act_exact_every_tile(tile):
+    """W8A16 with E4M3 weights: integer bf16 activations in [-8, 8], E4M3
+    codes of integers in [-8, 8] with power-of-two per-channel scales; every
+    sum is exact in fp32: bitwise equal to the oracle (decode and tile
+    kernels alike)."""
+    m, n, k = rows_for(tile, 23), 272, 1024
+    g = synth.rng(39)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    codes = oracle.formats.encode_e4m3(g.integers(-8, 9, size=(1, n, k)).astype(np.float64))
+    scales = np.ldexp(1.0, g.integers(-9, -6, size=(1, n, 1))).astype(np.float32)
+    w = {"codes": codes, "scales": scales}
+    hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="bf16")
+    packed = prepare(hd, w, "f32")
+    print(f"case w8a16 fp8 exact tile={tile}", flush=True)
+    if not stream_fits(tile, m, k, 2):
+        with pytest.raises(hum.HumError, match="raise split_k"):
+            hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+        return
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 100, 300])
+def test_fp8_weights_bf16_act_random_vs_oracle(m):
+    """W8A16 with E4M3 weights (per-channel scales) at the selector's config."""
+    n, k = 600, 2048
+    w = synth.dense_w8a8(synth.seed_for(8, m), 1, n, k)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(8, 100 + m)), (m, k))
+    hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="bf16")
+    packed = prepare(hd, w, "f32")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_tol(out, ref, f"w8a16 fp8 m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -353,7 +392,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e2m1_mxfp8", "e2m1_mxfp4"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -364,6 +403,10 @@ def test_empty_m_is_a_no_op(fmt):
     elif fmt == "e4m3":
         w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
         hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+        packed = prepare(hd, w, "f32")
+    elif fmt == "e4m3_bf16":
+        w = synth.dense_w8a8(synth.seed_for(3, 53), 1, n, k)
+        hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="bf16")
         packed = prepare(hd, w, "f32")
     elif fmt == "e4m3_block":
         w = synth.quant_weights(52, "e4m3", "block", 128, "f32", 1, n, k)

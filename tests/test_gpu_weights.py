@@ -52,6 +52,21 @@ def test_dequant_bit_exact(fmt, shape):
         f"{int((g.view(np.uint32) != ref.view(np.uint32)).sum())} mismatches"
 
 
+@pytest.mark.parametrize("gran", ["channel", "tensor"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dequant_bit_exact_fp8_weights_bf16_act(shape, gran):
+    """E4M3 weights packed for bf16 activations (their own fragment order)."""
+    e, n, k = shape
+    hd, od = descs("e4m3", gran, 0, "f32", e, n, k, act="bf16")
+    w = synth.quant_weights(hash(("w8a16", shape, gran)) & 0xFFFF, "e4m3", gran, 0, "f32", e, n, k)
+    packed = prepare(hd, w, "f32")
+    got = hum.dequant_weight(hd, packed)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.dequant_weight(od, w["codes"], w["scales"], include_global=False).astype(np.float32)
+    g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def test_group_k_equals_channel_bitwise():
     e, n, k = 1, 96, 512
     w = synth.quant_weights(5, "uint4", "group", k, "bf16", e, n, k, zero=True)
