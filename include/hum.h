@@ -195,6 +195,19 @@ hum_status hum_prepare_workspace(void* workspace, size_t ws_bytes, void* stream)
 hum_status hum_select_config(const hum_weight_desc* desc, int64_t m,
                              hum_tile_config* cfg_out);
 
+/* Selection flags. */
+#define HUM_SELECT_BATCH_INVARIANT 1u  /* every output row independent of m and
+                                          of the other rows of the call */
+
+/* hum_select_config with flags ("batch invariance" among the compute options
+ * in the Humming announcement's feature list).  HUM_SELECT_BATCH_INVARIANT
+ * returns a tile-kernel configuration without split-K: the tile kernel sums
+ * each row in one fixed order for every tile shape, so a row's bf16 output is
+ * bitwise the same for any m when hum_linear_ex runs with the configuration
+ * this returns for that m.  Other flag bits are an error (HUM_ERR_INVALID_ARG). */
+hum_status hum_select_config_ex(const hum_weight_desc* desc, int64_t m, uint32_t flags,
+                                hum_tile_config* cfg_out);
+
 /* ---- MoE layer ----------------------------------------------------------- */
 
 /* Workspace bytes hum_moe_gemm needs for T tokens routed to topk experts. */
@@ -226,6 +239,15 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13,
                            const int32_t* topk_ids, const float* topk_weights,
                            void* out_bf16, void* workspace, size_t ws_bytes,
                            const hum_tile_config* cfg, void* stream);
+
+/* The configuration for hum_moe_gemm_ex (both GEMMs) at T tokens.  flags = 0:
+ * the selector's down-GEMM configuration (hum_moe_gemm itself may run a small
+ * batch's gate_up GEMM on the decode kernel).  HUM_SELECT_BATCH_INVARIANT: a
+ * tile-kernel configuration, with which every token's output row is bitwise
+ * independent of T and of the other tokens' routing. */
+hum_status hum_moe_select_config(const hum_weight_desc* w13, const hum_weight_desc* w2,
+                                 int64_t num_tokens, int32_t topk, uint32_t flags,
+                                 hum_tile_config* cfg_out);
 
 /* Workspace bytes hum_moe_gemm_ex needs with configuration `cfg`. */
 size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_desc* w2,

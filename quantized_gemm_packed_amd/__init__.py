@@ -80,6 +80,8 @@ _CP = ctypes.POINTER(TileConfig)
 _SIGS = {
     "hum_last_error": (ctypes.c_char_p, []),
     "hum_packed_weight_bytes": (_SZ, [_DP]),
+    "hum_select_config_ex": (_I32, [_DP, _I64, ctypes.c_uint32, _CP]),
+    "hum_moe_select_config": (_I32, [_DP, _DP, _I64, _I32, ctypes.c_uint32, _CP]),
     "hum_prepare_weight": (_I32, [_DP, _P, _P, _P, _P, _P, _SZ, _P]),
     "hum_dequant_weight": (_I32, [_DP, _P, _P, _P]),
     "hum_quant_act": (_I32, [_I32, _I64, _I64, _P, _I64, _P, _P, _P]),
@@ -220,9 +222,23 @@ def quant_act(act_fmt, x):
     return q, s
 
 
-def select_config(desc: WeightDesc, m: int) -> TileConfig:
+SELECT_BATCH_INVARIANT = 1
+
+
+def select_config(desc: WeightDesc, m: int, batch_invariant: bool = False) -> TileConfig:
     c = TileConfig()
-    _check(load_library().hum_select_config(ctypes.byref(desc), int(m), ctypes.byref(c)))
+    if batch_invariant:
+        _check(load_library().hum_select_config_ex(ctypes.byref(desc), int(m), SELECT_BATCH_INVARIANT,
+                                                   ctypes.byref(c)))
+    else:
+        _check(load_library().hum_select_config(ctypes.byref(desc), int(m), ctypes.byref(c)))
+    return c
+
+
+def moe_select_config(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, batch_invariant: bool = False) -> TileConfig:
+    c = TileConfig()
+    _check(load_library().hum_moe_select_config(ctypes.byref(w13), ctypes.byref(w2), int(t), int(topk),
+                                                SELECT_BATCH_INVARIANT if batch_invariant else 0, ctypes.byref(c)))
     return c
 
 
@@ -262,12 +278,15 @@ def _workspace(device):
 
 
 def linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, cfg: TileConfig | None = None,
-           workspace=None):
-    """bf16 out [m, n] = A @ W^T (+ bias)."""
+           workspace=None, batch_invariant: bool = False):
+    """bf16 out [m, n] = A @ W^T (+ bias).  batch_invariant: every row's
+    result independent of m (the library's invariant configuration)."""
     import torch
     for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias")):
         _gpu(t, nm)
     m = a.shape[0]
+    if batch_invariant and cfg is None:
+        cfg = select_config(desc, m, batch_invariant=True)
     if out is None:
         out = torch.empty((m, desc.n), dtype=torch.bfloat16, device=a.device)
     need = linear_workspace_bytes(desc, m, cfg)
@@ -287,13 +306,16 @@ def moe_workspace_bytes(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, cfg:
 
 
 def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids, topk_weights, out=None,
-             cfg: TileConfig | None = None, workspace=None):
-    """bf16 out [T, H] of the MoE expert layer."""
+             cfg: TileConfig | None = None, workspace=None, batch_invariant: bool = False):
+    """bf16 out [T, H] of the MoE expert layer.  batch_invariant: every
+    token's result independent of the other tokens of the call."""
     import torch
     for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"), (topk_ids, "topk_ids"),
                   (topk_weights, "topk_weights")):
         _gpu(t, nm)
     t_count, topk = topk_ids.shape
+    if batch_invariant and cfg is None:
+        cfg = moe_select_config(w13, w2, t_count, topk, batch_invariant=True)
     if out is None:
         out = torch.empty((t_count, w13.k), dtype=torch.bfloat16, device=x.device)
     need = moe_workspace_bytes(w13, w2, t_count, topk, cfg)

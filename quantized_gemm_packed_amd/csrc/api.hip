@@ -406,6 +406,31 @@ hum_status hum_select_config(const hum_weight_desc* desc, int64_t m, hum_tile_co
   return HUM_OK;
 }
 
+// Batch invariance: the tile kernel sums every output row in one fixed
+// order (K-blocks in sequence, each through the same MFMA chain, scales
+// applied per row / column), whatever its tile shape and the other rows of
+// the call; split-K and the decode kernel's in-workgroup K split change that
+// order.  So the invariant choice keeps the selector's tile shape for m and
+// drops split-K, and replaces the decode kernel with the small-M tile.
+static hum_tile_config select_dense_invariant(const hum_weight_desc* d, int64_t m) {
+  hum_tile_config c = select_dense(d, m);
+  if (c.kind == HUM_KERNEL_STREAM) c = select_dense(d, 17);
+  c.split_k = 1;
+  c.block_m = (int32_t)tile_rows(c);
+  return c;
+}
+
+hum_status hum_select_config_ex(const hum_weight_desc* desc, int64_t m, uint32_t flags, hum_tile_config* cfg_out) {
+  clear_error();
+  hum_status st = check_desc(desc);
+  if (st != HUM_OK) return st;
+  if (!cfg_out || m < 0) return set_error(HUM_ERR_INVALID_ARG, "bad arguments");
+  if (flags & ~(uint32_t)HUM_SELECT_BATCH_INVARIANT) return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
+  *cfg_out = (flags & HUM_SELECT_BATCH_INVARIANT) ? select_dense_invariant(desc, m < 1 ? 1 : m)
+                                                   : select_dense(desc, m < 1 ? 1 : m);
+  return HUM_OK;
+}
+
 size_t hum_linear_workspace_bytes_ex(const hum_weight_desc* desc, int64_t m, const hum_tile_config* cfg) {
   clear_error();
   if (check_desc(desc) != HUM_OK || m < 0) return 0;
@@ -588,6 +613,21 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   // activation buffers read through 32-bit buffer offsets
   if (t * w13->k * 2 >= ((int64_t)1 << 31) || (t * topk + (int64_t)w13->num_experts * 127) * w2->k * 2 >= ((int64_t)1 << 31))
     return set_error(HUM_ERR_UNSUPPORTED, "MoE activations above 2 GiB");
+  return HUM_OK;
+}
+
+hum_status hum_moe_select_config(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
+                                 uint32_t flags, hum_tile_config* cfg_out) {
+  clear_error();
+  hum_status st = check_moe(w13, w2, t, topk);
+  if (st != HUM_OK) return st;
+  if (!cfg_out) return set_error(HUM_ERR_INVALID_ARG, "cfg_out is NULL");
+  if (flags & ~(uint32_t)HUM_SELECT_BATCH_INVARIANT) return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
+  hum_tile_config c = select_moe(w13, t < 1 ? 1 : t, topk).dn;
+  // the grouped tile kernel sums each slot's row in a fixed order (no split-K);
+  // the decode kernel splits K inside the workgroup
+  if ((flags & HUM_SELECT_BATCH_INVARIANT) && c.kind != HUM_KERNEL_TILE) c = moe_tile_cfg(1);
+  *cfg_out = c;
   return HUM_OK;
 }
 

@@ -92,6 +92,37 @@ def test_selector_is_deterministic_and_covers_m_range(lib):
     assert len(seen) >= 3
 
 
+@pytest.mark.parametrize("fmt", [
+    ("uint4", "group", 128, "bf16", dict(has_zero=True), 8192, 8192),
+    ("e4m3", "channel", 0, "f32", dict(act_fmt="fp8_token"), 7168, 2048),
+    ("e4m3", "channel", 0, "f32", dict(), 7168, 2048),
+    ("e2m1", "group", 32, "e8m0", dict(act_fmt="mxfp8"), 7168, 2048),
+])
+def test_batch_invariant_selection(lib, fmt):
+    """Every M gets a tile-kernel configuration without split-K; the tile
+    shape may still follow M."""
+    wd, gran, gs, sd, kw, n, k = fmt
+    d = hum.make_desc(wd, gran, gs, sd, n, k, **kw)
+    for m in (0, 1, 4, 16, 17, 64, 256, 1024, 4096):
+        c = hum.select_config(d, m, batch_invariant=True)
+        assert c.kind == hum.KERNEL_TILE and c.split_k == 1 and c.block_m == 16 * c.wave_m, (m, c)
+    bad = hum.TileConfig()
+    assert lib.hum_select_config_ex(ctypes.byref(d), 4, 2, ctypes.byref(bad)) != 0
+    assert b"flags" in lib.hum_last_error()
+
+
+def test_moe_batch_invariant_selection(lib):
+    w13 = hum.make_desc("e2m1", "group", 32, "e8m0", 2048, 4096, num_experts=128, act_fmt="mxfp8")
+    w2 = hum.make_desc("e2m1", "group", 32, "e8m0", 4096, 1024, num_experts=128, act_fmt="mxfp8")
+    kinds = set()
+    for t in (0, 1, 16, 64, 1024, 8192):
+        kinds.add(hum.moe_select_config(w13, w2, t, 8).kind)
+        c = hum.moe_select_config(w13, w2, t, 8, batch_invariant=True)
+        assert c.kind == hum.KERNEL_TILE and c.split_k == 1, (t, c)
+        assert hum.moe_workspace_bytes(w13, w2, max(t, 1), 8, c) > 0
+    assert hum.KERNEL_STREAM in kinds    # the default does use the decode kernel
+
+
 def test_workspace_sizes(lib):
     d = hum.make_desc("e4m3", "channel", 0, "f32", 7168, 2048, act_fmt="fp8_token")
     assert hum.linear_workspace_bytes(d, 128) >= 128 * 2048 + 128 * 4
