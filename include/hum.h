@@ -208,6 +208,22 @@ hum_status hum_select_config(const hum_weight_desc* desc, int64_t m,
 hum_status hum_select_config_ex(const hum_weight_desc* desc, int64_t m, uint32_t flags,
                                 hum_tile_config* cfg_out);
 
+/* On-device autotune ("Autotune" under future work in the Humming
+ * announcement): times every compiled dense configuration that fits
+ * `ws_bytes` (with HUM_SELECT_BATCH_INVARIANT, only the batch-invariant ones)
+ * on the caller's buffers -- one untimed call, then `iters` calls between
+ * two HIP events on `stream` -- and returns the fastest in *best_out and its
+ * mean time per call in µs in *best_us_out (may be NULL).  The arguments
+ * are those of hum_linear_ex; `out` ends holding the winner's result.
+ * Blocks the host until the timing completes: not for graph capture.
+ * Callers cache the result per (description, m).  HUM_ERR_UNSUPPORTED when
+ * no configuration fits the workspace. */
+hum_status hum_autotune_linear(const hum_weight_desc* desc, const void* packed, int64_t m,
+                               const void* a, const void* a_scales, const void* bias,
+                               void* out, void* workspace, size_t ws_bytes, int32_t iters,
+                               uint32_t flags, hum_tile_config* best_out, float* best_us_out,
+                               void* stream);
+
 /* ---- MoE layer ----------------------------------------------------------- */
 
 /* Workspace bytes hum_moe_gemm needs for T tokens routed to topk experts. */

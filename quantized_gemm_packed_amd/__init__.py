@@ -81,6 +81,8 @@ _SIGS = {
     "hum_last_error": (ctypes.c_char_p, []),
     "hum_packed_weight_bytes": (_SZ, [_DP]),
     "hum_select_config_ex": (_I32, [_DP, _I64, ctypes.c_uint32, _CP]),
+    "hum_autotune_linear": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _I32, ctypes.c_uint32, _CP,
+                                   ctypes.POINTER(ctypes.c_float), _P]),
     "hum_moe_select_config": (_I32, [_DP, _DP, _I64, _I32, ctypes.c_uint32, _CP]),
     "hum_prepare_weight": (_I32, [_DP, _P, _P, _P, _P, _P, _SZ, _P]),
     "hum_dequant_weight": (_I32, [_DP, _P, _P, _P]),
@@ -296,6 +298,32 @@ def linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, cfg:
     _check(lib.hum_linear_ex(ctypes.byref(desc), _ptr(packed), m, _ptr(a), _ptr(a_scales), _ptr(bias), _ptr(out),
                              _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg), _stream(a.device)))
     return out
+
+
+def autotune_linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, workspace=None,
+                    iters: int = 10, batch_invariant: bool = False):
+    """Time every compiled configuration on these buffers (on the device) ->
+    (fastest TileConfig, its µs per call).  `out`, if given, ends holding
+    the winner's result.  The workspace defaults to the largest any
+    candidate needs (a tile configuration with split-K 16)."""
+    import torch
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias")):
+        _gpu(t, nm)
+    m = a.shape[0]
+    if out is None:
+        out = torch.empty((m, desc.n), dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        big = select_config(desc, max(m, 17))
+        big.split_k = 16
+        workspace = _workspace(a.device).get(linear_workspace_bytes(desc, m, big))
+    wsb = 0 if workspace is None else workspace.numel()
+    best = TileConfig()
+    us = ctypes.c_float()
+    _check(load_library().hum_autotune_linear(ctypes.byref(desc), _ptr(packed), m, _ptr(a), _ptr(a_scales),
+                                              _ptr(bias), _ptr(out), _ptr(workspace), wsb, int(iters),
+                                              SELECT_BATCH_INVARIANT if batch_invariant else 0,
+                                              ctypes.byref(best), ctypes.byref(us), _stream(a.device)))
+    return best, us.value
 
 
 def moe_workspace_bytes(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, cfg: TileConfig | None = None) -> int:

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "hum_internal.h"
 
@@ -544,6 +545,98 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
 hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a, const void* a_scales,
                       const void* bias, void* out, void* workspace, size_t ws_bytes, void* stream) {
   return hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------
+// On-device autotune: every compiled dense configuration, timed on the
+// caller's own buffers.
+
+static void dense_candidates(const hum_weight_desc* d, int64_t m, uint32_t flags, std::vector<hum_tile_config>& out) {
+  const int64_t kb = d->k / kKBlk;
+  const bool inv = (flags & HUM_SELECT_BATCH_INVARIANT) != 0;
+  for (int split = 1; split <= 16; split *= 2) {
+    if (inv && split > 1) break;
+    for (int kind = HUM_KERNEL_TILE; kind <= HUM_KERNEL_STREAM; ++kind) {
+      if (kind == HUM_KERNEL_STREAM && (inv || m > 16)) continue;
+      for (int wm = 1; wm <= (kind == HUM_KERNEL_TILE ? 8 : 1); wm *= 2)
+        for (int wn = 1; wn <= 8; wn *= 2)
+          for (int wk = 1; wk <= (kind == HUM_KERNEL_TILE ? 1 : 15); ++wk)
+            for (int st = 0; st <= (kind == HUM_KERNEL_TILE ? 3 : 0); st += 3) {
+              hum_tile_config c{};
+              c.kind = kind;
+              c.wave_m = wm;
+              c.wave_n = wn;
+              c.waves_n = kind == HUM_KERNEL_TILE ? 4 : 1;
+              c.waves_k = wk;
+              c.split_k = split;
+              c.stages = st;
+              c.block_m = (int32_t)tile_rows(c);
+              // every split must own at least one K-block
+              if (split > 1 && (int64_t)kb_per_split(kb, c) * (split - 1) >= kb) continue;
+              if (cfg_sane(c) && gemm_instance_exists(dense_key(d, c))) out.push_back(c);
+            }
+    }
+  }
+}
+
+hum_status hum_autotune_linear(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a,
+                               const void* a_scales, const void* bias, void* out, void* workspace, size_t ws_bytes,
+                               int32_t iters, uint32_t flags, hum_tile_config* best_out, float* best_us_out,
+                               void* stream) {
+  clear_error();
+  hum_status st = check_desc(desc);
+  if (st != HUM_OK) return st;
+  if (desc->num_experts != 1) return set_error(HUM_ERR_INVALID_ARG, "autotune takes a dense (num_experts == 1) description");
+  if (m < 1 || iters < 1 || iters > 10000 || !best_out) return set_error(HUM_ERR_INVALID_ARG, "bad m / iters / best_out");
+  if (flags & ~(uint32_t)HUM_SELECT_BATCH_INVARIANT) return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
+  if (!packed || !a || !out) return set_error(HUM_ERR_INVALID_ARG, "packed, a and out must be non-NULL");
+  std::vector<hum_tile_config> cands;
+  dense_candidates(desc, m, flags, cands);
+  const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return set_error(HUM_ERR_HIP, "hipEventCreate failed");
+  }
+  float best_us = 0.0f;
+  hum_tile_config best{};
+  bool found = false;
+  for (const hum_tile_config& c : cands) {
+    const int64_t need = dense_ws(desc, m, c, quant_a).total;
+    if (need > 0 && (!workspace || (int64_t)ws_bytes < need)) continue;
+    // one untimed call: warms the code object and screens configurations the
+    // launcher refuses for this shape (the decode kernel's K-range limits)
+    st = hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, &c, stream);
+    if (st == HUM_ERR_UNSUPPORTED) continue;
+    if (st == HUM_OK && hipEventRecord(e0, s) != hipSuccess) st = set_error(HUM_ERR_HIP, "hipEventRecord failed");
+    for (int i = 0; i < iters && st == HUM_OK; ++i)
+      st = hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, &c, stream);
+    float ms = 0.0f;
+    if (st == HUM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                         hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      st = set_error(HUM_ERR_HIP, "timing events failed");
+    if (st != HUM_OK) {
+      (void)hipEventDestroy(e0);
+      (void)hipEventDestroy(e1);
+      return st;
+    }
+    const float us = ms * 1000.0f / (float)iters;
+    if (!found || us < best_us) {
+      best_us = us;
+      best = c;
+      found = true;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (!found) return set_error(HUM_ERR_UNSUPPORTED, "no compiled configuration fits this shape and workspace");
+  // leave the winner's result in out
+  st = hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, &best, stream);
+  if (st != HUM_OK) return st;
+  *best_out = best;
+  if (best_us_out) *best_us_out = best_us;
+  return HUM_OK;
 }
 
 // ---------------------------------------------------------------------------

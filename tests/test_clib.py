@@ -111,6 +111,22 @@ def test_batch_invariant_selection(lib, fmt):
     assert b"flags" in lib.hum_last_error()
 
 
+def test_autotune_argument_errors(lib):
+    """Rejected before any device work."""
+    d = hum.make_desc("int4", "group", 128, "bf16", 256, 1024)
+    best = hum.TileConfig()
+    us = ctypes.c_float()
+    f = lib.hum_autotune_linear
+    assert f(ctypes.byref(d), None, 4, None, None, None, None, None, 0, 10, 0, ctypes.byref(best), ctypes.byref(us),
+             None) == 1
+    p = ctypes.c_void_p(16)
+    assert f(ctypes.byref(d), p, 4, p, None, None, p, None, 0, 0, 0, ctypes.byref(best), None, None) == 1
+    assert f(ctypes.byref(d), p, 4, p, None, None, p, None, 0, 10, 4, ctypes.byref(best), None, None) == 1
+    assert b"flags" in lib.hum_last_error()
+    assert f(ctypes.byref(d), p, 0, p, None, None, p, None, 0, 10, 0, ctypes.byref(best), None, None) == 1
+    assert f(ctypes.byref(d), p, 4, p, None, None, p, None, 0, 10, 0, None, None, None) == 1
+
+
 def test_moe_batch_invariant_selection(lib):
     w13 = hum.make_desc("e2m1", "group", 32, "e8m0", 2048, 4096, num_experts=128, act_fmt="mxfp8")
     w2 = hum.make_desc("e2m1", "group", 32, "e8m0", 4096, 1024, num_experts=128, act_fmt="mxfp8")
