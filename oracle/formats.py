@@ -6,6 +6,8 @@ for Quantized Inference", sections "Background" and "WnA16"; they never give
 bit layouts.  The readings below are the OCP definitions:
 
 * INT4: two's complement nibble, values -8..7.  UINT4: 0..15.
+* INT8: two's complement byte, values -128..127 (one code per byte; the
+  pages list INT8 among the weight widths without a layout).
 * E2M1 (OCP MX v1.0): sign, 2 exponent bits (bias 1), 1 mantissa bit;
   magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; no Inf/NaN.
 * E4M3 "FN" (OCP FP8): sign, 4 exponent bits (bias 7), 3 mantissa bits;
@@ -28,6 +30,11 @@ E4M3_MAX = 448.0
 def decode_int4(c):
     c = np.asarray(c, dtype=np.int64) & 0xF
     return np.where(c >= 8, c - 16, c).astype(np.float64)
+
+
+def decode_int8(c):
+    c = np.asarray(c, dtype=np.int64) & 0xFF
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
 
 
 def decode_uint4(c):
@@ -185,4 +192,6 @@ def decode_weight_codes(codes, weight_dtype: str):
                 "e2m1": decode_e2m1}[weight_dtype](q)
     if weight_dtype == "e4m3":
         return decode_e4m3(codes)
+    if weight_dtype == "int8":
+        return decode_int8(codes)
     raise ValueError(f"unknown weight dtype {weight_dtype}")

@@ -33,7 +33,7 @@ from .quant import dequant_fp8_group, dequant_fp8_per_token, dequant_mxfp4, dequ
 
 @dataclass
 class WeightDesc:
-    weight_dtype: str          # "int4" | "uint4" | "e2m1" | "e4m3"
+    weight_dtype: str          # "int4" | "uint4" | "int8" | "e2m1" | "e4m3"
     scale_gran: str            # "tensor" | "channel" | "group"
     group_size: int            # along K (ignored unless scale_gran == "group")
     scale_dtype: str           # "bf16" | "f32" | "e8m0"

@@ -111,7 +111,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
                   scale_lo: float = 0.005, scale_hi: float = 0.02,
                   e8m0_lo: int = 119, e8m0_hi: int = 123):
     """Random canonical weights of any supported description: codes uniform
-    over the format's codes (E4M3 without its NaN codes), scales uniform in
+    over the format's codes (E4M3 without its NaN codes; INT8 one byte per
+    code, all 256), scales uniform in
     [scale_lo, scale_hi] (bf16 / f32) or E8M0 codes in [e8m0_lo, e8m0_hi],
     zero points uniform in [0, 15], global scales uniform in [0.5, 2]."""
     g = rng(seed)
@@ -127,6 +128,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
     if weight_dtype == "e4m3":
         c = g.integers(0, 256, size=(e, n, k), dtype=np.uint8)
         codes = np.where((c & 0x7F) == 0x7F, c & 0xFE, c).astype(np.uint8)
+    elif weight_dtype == "int8":
+        codes = g.integers(0, 256, size=(e, n, k), dtype=np.uint8)
     else:
         codes = pack_nibbles(g.integers(0, 16, size=(e, n, k), dtype=np.uint8))
     if scale_dtype == "bf16":

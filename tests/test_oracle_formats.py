@@ -34,6 +34,14 @@ def test_int4_two_complement():
     assert np.array_equal(F.decode_uint4(c), c.astype(np.float64))
 
 
+def test_int8_two_complement():
+    c = np.arange(256, dtype=np.uint8)
+    v = F.decode_int8(c)
+    assert np.array_equal(v, c.view(np.int8).astype(np.float64))
+    assert v.min() == -128 and v.max() == 127 and v[0x80] == -128 and v[0xFF] == -1
+    assert np.array_equal(F.decode_weight_codes(c.reshape(1, 2, 128), "int8").ravel(), v)
+
+
 def test_e2m1_golden_table():
     tab = _read_table("e2m1_values.txt")
     got = F.decode_e2m1(np.arange(16))

@@ -21,6 +21,10 @@ def s_int4(c):
     return c - 16 if c >= 8 else c
 
 
+def s_int8(c):
+    return c - 256 if c >= 128 else c
+
+
 def s_e2m1(c):
     v = E2M1[c & 7]
     return -v if c & 8 else v
@@ -44,7 +48,7 @@ def s_scale(v, dtype):
 
 def brute_linear(desc, a_vals, codes_unpacked, scales, zeros, gscale):
     """C[m][n] with exact rationals, one scalar at a time."""
-    dec = {"int4": s_int4, "uint4": lambda c: c, "e2m1": s_e2m1, "e4m3": s_e4m3}[desc.weight_dtype]
+    dec = {"int4": s_int4, "uint4": lambda c: c, "int8": s_int8, "e2m1": s_e2m1, "e4m3": s_e4m3}[desc.weight_dtype]
     m, k = len(a_vals), desc.k
     out = []
     for i in range(m):
@@ -81,6 +85,8 @@ CASES = [
     ("e2m1", "group", 16, "bf16", False, True),
     ("e4m3", "channel", 0, "f32", False, False),
     ("e4m3", "block", 16, "f32", False, False),
+    ("int8", "channel", 0, "f32", False, False),
+    ("int8", "tensor", 0, "f32", False, True),
 ]
 
 
@@ -94,6 +100,9 @@ def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
     if wd == "e4m3":
         cu = g.integers(0, 256, size=(n, k))
         cu = np.where((cu & 0x7F) == 0x7F, 0x7E, cu).astype(np.uint8)
+        codes = cu[None]
+    elif wd == "int8":
+        cu = g.integers(0, 256, size=(n, k)).astype(np.uint8)
         codes = cu[None]
     else:
         cu = g.integers(0, 16, size=(n, k)).astype(np.uint8)
@@ -198,3 +207,18 @@ def test_w4a4_mxfp4_linear_vs_fraction_brute_force():
                 sw = Fraction(2) ** (int(we[0, j, kk // 32]) - 127)
                 acc += dec(ca) * sa * dec(cw) * sw
             assert got[i, j] == float(acc)
+
+
+def test_int8_per_channel_equals_integer_matmul():
+    """Integer activations, INT8 codes and power-of-two per-channel scales:
+    the layer is an integer matrix product (numpy int64) times the scale."""
+    g = np.random.default_rng(81)
+    m, n, k = 4, 6, 256
+    cu = g.integers(0, 256, size=(n, k)).astype(np.uint8)
+    q = cu.view(np.int8).astype(np.int64)
+    x = g.integers(-20, 21, size=(m, k)).astype(np.int64)
+    sc = np.ldexp(1.0, g.integers(-12, -4, size=(n, 1))).astype(np.float32)
+    desc = G.WeightDesc("int8", "channel", 0, "f32", False, False, 1, n, k)
+    got = G.linear(desc, x.astype(np.float64), cu[None], sc[None])
+    ref = (x @ q.T).astype(np.float64) * sc[:, 0].astype(np.float64)[None, :]
+    assert np.array_equal(got, ref)
