@@ -186,14 +186,18 @@ def dense_w8a8(hum, timer, iters):
     return out
 
 
-def dense_w8a16_fp8(hum, timer, iters):
-    """E4M3 weights (per-channel f32 scales) x bf16 activations, at the W8A8
-    layer's shape N = 7168, K = 2048."""
+def dense_w8a16(hum, timer, iters, weight_dtype):
+    """8-bit weights (E4M3 or INT8, per-channel f32 scales) x bf16
+    activations, at the W8A8 layer's shape N = 7168, K = 2048."""
     import synth
     import torch
     n, k = 7168, 2048
-    case = synth.dense_w8a8(synth.seed_for(8), 1, n, k)
-    desc = hum.make_desc("e4m3", "channel", 0, "f32", n, k, act_fmt="bf16")
+    if weight_dtype == "e4m3":
+        case = synth.dense_w8a8(synth.seed_for(8), 1, n, k)
+    else:
+        case = synth.quant_weights(synth.seed_for(8, 2), "int8", "channel", 0, "f32", 1, n, k,
+                                   scale_lo=0.0002, scale_hi=0.001)
+    desc = hum.make_desc(weight_dtype, "channel", 0, "f32", n, k, act_fmt="bf16")
     packed = hum.prepare_weight(desc, _dev(case["codes"]), _dev(case["scales"]))
     copies = rotate_copies(packed)
     g = synth.rng(synth.seed_for(8, 1))
@@ -400,7 +404,8 @@ def main():
         sweep["dense_w4a16_int4_g128_m16_n512_k1024"] = dense_tiny(hum, timer, iters)
         sweep["dense_w8a8_fp8_n7168_k2048"] = dense_w8a8(hum, timer, iters)
         sweep["dense_w8a8_fp8_block128_n7168_k2048"] = dense_w8a8_block(hum, timer, iters)
-        sweep["dense_w8a16_fp8_n7168_k2048"] = dense_w8a16_fp8(hum, timer, iters)
+        sweep["dense_w8a16_fp8_n7168_k2048"] = dense_w8a16(hum, timer, iters, "e4m3")
+        sweep["dense_w8a16_int8_n7168_k2048"] = dense_w8a16(hum, timer, iters, "int8")
         sweep["dense_w4a4_mxfp4_n7168_k2048"] = dense_w4a4(hum, timer, iters)
         del d["copies"]
         torch.cuda.empty_cache()

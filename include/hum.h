@@ -50,7 +50,9 @@ typedef enum hum_dtype {
   HUM_UINT4 = 3,  /* unsigned nibble 0..15, optional zero point */
   HUM_E2M1 = 4,   /* FP4 (MXFP4 element) */
   HUM_E4M3 = 5,   /* FP8 E4M3 "FN": max 448, NaN = 0x7F/0xFF, no Inf */
-  HUM_E8M0 = 6    /* power-of-two scale 2^(c-127) */
+  HUM_E8M0 = 6,   /* power-of-two scale 2^(c-127) */
+  HUM_INT8 = 7    /* signed two's-complement byte, -128..127 (W8A16: bf16
+                     activations, per-channel or per-tensor f32 scales) */
 } hum_dtype;
 
 typedef enum hum_scale_gran {
@@ -74,7 +76,7 @@ typedef enum hum_act_fmt {
 
 /* The quantization description of one weight tensor [E][N][K]. */
 typedef struct hum_weight_desc {
-  int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_E2M1 | HUM_E4M3 */
+  int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_INT8 | HUM_E2M1 | HUM_E4M3 */
   int32_t scale_gran;        /* hum_scale_gran */
   int32_t group_size;        /* K elements per group (HUM_SCALE_GROUP), block edge (HUM_SCALE_BLOCK) */
   int32_t scale_dtype;       /* HUM_BF16 | HUM_F32 | HUM_E8M0 */
@@ -111,7 +113,7 @@ typedef struct hum_tile_config {
 size_t hum_packed_weight_bytes(const hum_weight_desc* desc);
 
 /* Canonical ("standard format") tensors -> packed kernel layout.
- *   codes  : u8 [E][N][K/2] (4-bit) or [E][N][K] (E4M3)
+ *   codes  : u8 [E][N][K/2] (4-bit) or [E][N][K] (INT8, E4M3)
  *   scales : [E][N'][K/G'] in scale_dtype (N' = 1 for TENSOR, G' per gran)
  *   zeros  : u8 [E][N'][K/G'] or NULL when has_zero_point == 0
  *   global_scale : f32 [E] or NULL when has_global_scale == 0

@@ -22,7 +22,7 @@ __all__ = [
     "moe_gemm", "moe_align", "moe_reduce", "Workspace", "header_functions",
 ]
 
-BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0 = range(7)
+BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0, INT8 = range(8)
 KERNEL_TILE, KERNEL_STREAM = range(2)
 SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP, SCALE_BLOCK = range(4)
 ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4, ACT_FP8_GROUP = range(5)
@@ -150,7 +150,7 @@ def _gpu(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-_DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3}
+_DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3, "int8": INT8}
 _GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP, "block": SCALE_BLOCK}
 _SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0}
 _AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4,

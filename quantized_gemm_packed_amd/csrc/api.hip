@@ -65,6 +65,13 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->act_fmt != HUM_ACT_BF16 && d->act_fmt != HUM_ACT_MXFP8 && d->act_fmt != HUM_ACT_MXFP4)
         return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 runs with bf16, MXFP8 or MXFP4 activations");
       return HUM_OK;
+    case HUM_INT8:
+      if (d->scale_gran != HUM_SCALE_CHANNEL && d->scale_gran != HUM_SCALE_TENSOR)
+        return set_error(HUM_ERR_UNSUPPORTED, "INT8 weights take per-channel or per-tensor scales");
+      if (d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "INT8 weights take f32 scales");
+      if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "INT8 takes no zero point");
+      if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "INT8 weights run with bf16 activations");
+      return HUM_OK;
     case HUM_E4M3:
       if (d->scale_gran == HUM_SCALE_GROUP) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take per-channel or per-tensor scales");
       if (d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "E4M3 weights take f32 scales");
@@ -79,6 +86,7 @@ hum_status check_desc(const hum_weight_desc* d) {
 
 int fmt_of(const hum_weight_desc* d) {
   if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
+  if (d->weight_dtype == HUM_INT8) return F_INT8_BF16;
   if (d->weight_dtype == HUM_E4M3)
     return d->scale_gran == HUM_SCALE_BLOCK ? F_FP8_BLOCK : (d->act_fmt == HUM_ACT_BF16 ? F_FP8_BF16 : F_FP8);
   if (d->act_fmt == HUM_ACT_MXFP8) return F_MXFP4_MXFP8;
@@ -93,7 +101,7 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   L->kb = d->k / kKBlk;
   L->kb4 = cdiv(L->kb, 4);
   const int f = fmt_of(d);
-  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || f == F_FP8_BF16) ? 32 : 16;
+  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || fmt_w8_bf16(f)) ? 32 : 16;
   L->codes_per_expert = L->nt * L->kb * 64 * L->code_bytes;
   if (f == F_INT) {
     const bool grp = d->scale_gran == HUM_SCALE_GROUP && d->group_size < d->k;
@@ -104,7 +112,7 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
     L->zeros_per_expert = d->has_zero_point ? align256(L->nt * L->ng * 8) : 0;
     L->kbc = cdiv(L->kb, 32);
     L->co_per_expert = L->nt * L->kbc * 1024 * 2;
-  } else if (f == F_FP8 || f == F_FP8_BF16) {
+  } else if (f == F_FP8 || fmt_w8_bf16(f)) {
     L->ng = 1;
     L->scales_per_expert = align256(L->nt * 16 * 4);
   } else if (f == F_FP8_BLOCK) {
@@ -180,9 +188,9 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     c.kind = HUM_KERNEL_STREAM;
     c.wave_m = 1;
     c.waves_n = 1;
-    const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16 || fmt_of(d) == F_FP8_BF16;
+    const bool bf16_act = fmt_bf16_act(fmt_of(d));
     const int64_t a_bytes = m * (bf16_act ? 2 : 1);            // per k
-    const int64_t w_bytes16 = (fmt_of(d) == F_FP8 || fmt_of(d) == F_FP8_BF16) ? 16 : 8;      // per k of a 16-column sub-tile
+    const int64_t w_bytes16 = (fmt_of(d) == F_FP8 || fmt_w8_bf16(fmt_of(d))) ? 16 : 8;      // per k of a 16-column sub-tile
     const int64_t need = cdiv(a_bytes, w_bytes16);
     c.wave_n = need <= 1 ? 1 : (need <= 2 ? 2 : 4);
     const int64_t wgs = cdiv(nt, c.wave_n);
@@ -213,7 +221,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     // bf16 activations from M = 512 (fewer LDS activation reads per MFMA);
     // 128 x 128 for FP8 activations.  W4A4 (no decode kernel) takes the
     // small tiles from M = 1.
-    const bool bf16_act = fmt_of(d) == F_INT || fmt_of(d) == F_MXFP4_BF16 || fmt_of(d) == F_FP8_BF16;
+    const bool bf16_act = fmt_bf16_act(fmt_of(d));
     int64_t target = 3 * kCUs;
     if (m <= 256) {
       c.wave_m = 2;
@@ -228,10 +236,10 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       c.wave_n = 2;
     }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
-    // FP8 weights with bf16 activations: split K only while every split
+    // 8-bit weights with bf16 activations: split K only while every split
     // keeps at least 16 K-blocks (so none at K = 2048, where one pass
     // measured 1.6-2.4x faster than split-K for M = 64..256 on MI355X)
-    c.split_k = pick_split(wgs, 4, kb, 1, fmt_of(d) == F_FP8_BF16 ? 16 : 4, target);
+    c.split_k = pick_split(wgs, 4, kb, 1, fmt_w8_bf16(fmt_of(d)) ? 16 : 4, target);
     if (fmt_of(d) == F_FP8_BLOCK) {
       // block-scaled FP8 (no decode kernel): small tiles with three stages
       // to M = 256, then the FP8 128 x 128 tiles
@@ -535,8 +543,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.partials = reinterpret_cast<float*>(ws + w.partials);
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
-                                            : m * desc->k * (fmt_of(desc) == F_INT || fmt_of(desc) == F_MXFP4_BF16 ||
-                                                               fmt_of(desc) == F_FP8_BF16 ? 2 : 1);
+                                            : m * desc->k * (fmt_bf16_act(fmt_of(desc)) ? 2 : 1);
   p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32)
                     : (desc->act_fmt == HUM_ACT_FP8_GROUP ? m * (desc->k / 128) * 4 : 0);
   return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);

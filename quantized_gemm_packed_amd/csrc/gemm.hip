@@ -39,6 +39,8 @@
 //   F_FP8_BF16     E4M3 weights x bf16 activations (W8A16): the hardware
 //                  FP8 -> bf16 conversion (exact), bf16 MFMA, per-channel
 //                  scales in the epilogue.
+//   F_INT8_BF16    INT8 weights x bf16 activations (W8A16): bytes widened
+//                  through f32 (exact), the FP8 path's layout and epilogue.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
@@ -58,13 +60,12 @@ namespace hum {
 
 template <int FMT>
 struct Tr {
-  static constexpr int kAElem =
-      (FMT == F_INT || FMT == F_MXFP4_BF16 || FMT == F_FP8_BF16) ? 2 : 1;  // activation bytes (FP4: 1/2)
+  static constexpr int kAElem = fmt_bf16_act(FMT) ? 2 : 1;  // activation bytes (FP4: 1/2)
   static constexpr bool kA4 = (FMT == F_MXFP4_MXFP4);                           // 4-bit activations
   static constexpr int kARowB = kA4 ? 64 : 128 * kAElem;                        // activation bytes per row per K-block
   static constexpr int kBWords =
-      (FMT == F_FP8 || FMT == F_FP8_BLOCK || FMT == F_FP8_BF16) ? 2 : 1;  // 16-B words / lane / K-block
-  static constexpr bool kBf16 = (FMT == F_INT || FMT == F_MXFP4_BF16 || FMT == F_FP8_BF16);
+      (FMT == F_FP8 || FMT == F_FP8_BLOCK || fmt_w8_bf16(FMT)) ? 2 : 1;  // 16-B words / lane / K-block
+  static constexpr bool kBf16 = fmt_bf16_act(FMT);
   // bytes of an activation row of `ld` elements
   static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
 };
@@ -245,6 +246,13 @@ __device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// Byte i of w as a signed integer, in f32.
+__device__ __forceinline__ float i8_to_f32(uint32_t w, int i) { return (float)(int)(int8_t)(w >> (8 * i)); }
+// bf16 bits of lo in the low half, of hi in the high half, by truncation.
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // bf16 B operand of the 4 k-steps of a K-block.
 template <int FMT>
 __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, int kb, bf16x8_t (&d)[4]) {
@@ -263,6 +271,20 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
       o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+      d[s] = __builtin_bit_cast(bf16x8_t, o);
+    }
+  } else if (FMT == F_INT8_BF16) {
+    // INT8 -> bf16 is exact (|q| <= 128): each byte sign-extended to f32,
+    // and two f32 packed by their upper halves (whose lower halves are zero
+    // for integers this small); same byte order as the FP8 branch
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w0 = f.w[s >> 1][2 * (s & 1)], w1 = f.w[s >> 1][2 * (s & 1) + 1];
+      u32x4_t o;
+      o[0] = pack_hi16(i8_to_f32(w0, 0), i8_to_f32(w0, 1));
+      o[1] = pack_hi16(i8_to_f32(w0, 2), i8_to_f32(w0, 3));
+      o[2] = pack_hi16(i8_to_f32(w1, 0), i8_to_f32(w1, 1));
+      o[3] = pack_hi16(i8_to_f32(w1, 2), i8_to_f32(w1, 3));
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
   } else {
@@ -304,7 +326,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // the second-level scale); the per-token FP8 row scale is applied apart.
 template <int FMT>
 __device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, float gs) {
-  if (FMT == F_FP8 || FMT == F_FP8_BF16) return gs * reinterpret_cast<const float*>(wmeta)[col];
+  if (FMT == F_FP8 || fmt_w8_bf16(FMT)) return gs * reinterpret_cast<const float*>(wmeta)[col];
   return gs;
 }
 
@@ -1582,7 +1604,7 @@ struct Instance {
 
 // Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.
-#define HUM_PF(F, n) (((F) == F_FP8 || (F) == F_FP8_BF16) ? ((n) > 1 ? (n) / 2 : 1) : (n))
+#define HUM_PF(F, n) (((F) == F_FP8 || fmt_w8_bf16(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
 #define HUM_DENSE_SET(F)                                   \
   HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
   HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \
@@ -1652,6 +1674,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
     HUM_DENSE_TILE_SET(F_FP8_BLOCK),
     HUM_DENSE_SET(F_FP8_BF16),
+    HUM_DENSE_SET(F_INT8_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1676,6 +1699,7 @@ static const ReduceInstance kReduces[] = {
     {F_MXFP4_MXFP4, EPI_BF16, splitk_reduce_kernel<F_MXFP4_MXFP4, EPI_BF16>},
     {F_FP8_BLOCK, EPI_BF16, splitk_reduce_kernel<F_FP8_BLOCK, EPI_BF16>},
     {F_FP8_BF16, EPI_BF16, splitk_reduce_kernel<F_FP8_BF16, EPI_BF16>},
+    {F_INT8_BF16, EPI_BF16, splitk_reduce_kernel<F_INT8_BF16, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

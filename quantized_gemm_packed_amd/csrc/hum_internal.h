@@ -55,7 +55,18 @@ struct Layout {
   int scale_f32 = 0;              // INT formats: 1 = f32 scales, 0 = bf16
 };
 
-enum Fmt : int { F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6 };
+enum Fmt : int {
+  F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6,
+  F_INT8_BF16 = 7
+};
+
+// Formats whose activations stay bf16 (bf16 MFMA on widened weights).
+constexpr bool fmt_bf16_act(int f) {
+  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16;
+}
+// 8-bit weight codes laid out for the bf16 MFMA: a lane's 32 codes of a
+// K-block contiguous (k = 32 * (lane / 16) + j), per-channel f32 scales.
+constexpr bool fmt_w8_bf16(int f) { return f == F_FP8_BF16 || f == F_INT8_BF16; }
 
 // Validates the description; on failure sets the thread-local error and
 // returns a non-OK status.
@@ -151,14 +162,14 @@ enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1 };
 constexpr int64_t kStreamLdsDense = 128 * 1024;
 constexpr int64_t kStreamLdsMax = 159 * 1024;
 constexpr int64_t stream_lds_per_kb(int fmt, int rows) {
-  return (int64_t)rows * ((fmt == F_INT || fmt == F_MXFP4_BF16 || fmt == F_FP8_BF16) ? 256 : (fmt == F_MXFP4_MXFP8 ? 132 : 128));
+  return (int64_t)rows * (fmt_bf16_act(fmt) ? 256 : (fmt == F_MXFP4_MXFP8 ? 132 : 128));
 }
 // Exact LDS footprint of the stream kernel's staging for at most `rows`
 // rows and `kb` K-blocks: 16-byte activation slots and 4-byte MX scale
 // slots, each rounded up to whole 64-lane LDS-DMA instructions (every lane
 // of an instruction writes its slot).
 constexpr int64_t stream_lds_footprint(int fmt, int rows, int64_t kb) {
-  const int64_t cpr = (fmt == F_INT || fmt == F_MXFP4_BF16 || fmt == F_FP8_BF16) ? 16 : 8;
+  const int64_t cpr = fmt_bf16_act(fmt) ? 16 : 8;
   const int64_t a = ((rows * cpr * kb + 63) / 64) * 64 * 16;
   const int64_t sc = (fmt == F_MXFP4_MXFP8) ? ((rows * kb + 63) / 64) * 64 * 4 : 0;
   return a + sc;
@@ -196,7 +207,7 @@ constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, i
 // points; MX: at most 2 KB of E8M0 rows) with one pass of loads.
 constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int64_t kb_per_group, int scale_f32) {
   const int64_t per = (kb + kw - 1) / kw;
-  const int64_t cpr = (fmt == F_INT || fmt == F_MXFP4_BF16 || fmt == F_FP8_BF16) ? 16 : 8;
+  const int64_t cpr = fmt_bf16_act(fmt) ? 16 : 8;
   if (rows * per * cpr > 512) return false;
   if (fmt == F_INT) {
     const int64_t groups = (per + kb_per_group - 1) / kb_per_group + 1;

@@ -27,7 +27,7 @@ struct RepackArgs {
   int scale_elem;      // bytes per scale element (1, 2 or 4)
   int has_zero;
   int has_gscale;
-  int fp8_bf16;        // E4M3 codes for the bf16 MFMA (bf16 activations)
+  int bf16_order;      // 8-bit codes for the bf16 MFMA (bf16 activations)
 };
 
 // 32 canonical 4-bit codes of (row n, k0 .. k0+31) as 4 dwords in the
@@ -71,15 +71,15 @@ __global__ void repack_codes_kernel(RepackArgs a) {
   const int c = lane & 15, lg = lane >> 4;
   const int64_t n = nt * kNSub + c;
   uint8_t* dst = a.packed + a.codes_off + e * a.codes_pe;
-  if (a.wdt == HUM_E4M3) {
+  if (a.wdt == HUM_E4M3 || a.wdt == HUM_INT8) {
     // the 16x16x128 FP8 MFMA takes k = 16 lg + [0, 16) and 64 + 16 lg +
     // [0, 16) per lane; the bf16 MFMA's four k-steps take k = 32 lg + 8 s +
     // [0, 8), i.e. 32 contiguous codes
     u32x4_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
     if (n < a.n) {
       const uint8_t* src = a.codes + (e * a.n + n) * a.k + kb * kKBlk;
-      lo = *reinterpret_cast<const u32x4_t*>(src + (a.fp8_bf16 ? 32 * lg : 16 * lg));
-      hi = *reinterpret_cast<const u32x4_t*>(src + (a.fp8_bf16 ? 32 * lg + 16 : 64 + 16 * lg));
+      lo = *reinterpret_cast<const u32x4_t*>(src + (a.bf16_order ? 32 * lg : 16 * lg));
+      hi = *reinterpret_cast<const u32x4_t*>(src + (a.bf16_order ? 32 * lg + 16 : 64 + 16 * lg));
     }
     u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 32);
     d[0] = lo;
@@ -264,7 +264,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   a.scale_elem = d->scale_dtype == HUM_BF16 ? 2 : (d->scale_dtype == HUM_F32 ? 4 : 1);
   a.has_zero = d->has_zero_point;
   a.has_gscale = d->has_global_scale;
-  a.fp8_bf16 = fmt_of(d) == F_FP8_BF16;
+  a.bf16_order = fmt_w8_bf16(fmt_of(d));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int B = 256;
   const int64_t ncode = (int64_t)d->num_experts * L.nt * L.kb * 64;
@@ -297,7 +297,7 @@ struct DequantArgs {
   int64_t codes_pe, scales_pe, zeros_pe;
   int num_experts, wdt, scale_f32, has_zero;
   int block;     // E4M3 with 2-D block scales
-  int fp8_bf16;  // E4M3 in the bf16 MFMA order
+  int bf16_order;  // 8-bit codes in the bf16 MFMA order
 };
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -330,13 +330,13 @@ __global__ void dequant_kernel(DequantArgs a) {
   if (n >= a.n) return;
   const uint8_t* base = a.packed + a.codes_off + e * a.codes_pe;
   float* orow = a.out + (e * a.n + n) * a.k + kb * kKBlk;
-  if (a.wdt == HUM_E4M3) {
+  if (a.wdt == HUM_E4M3 || a.wdt == HUM_INT8) {
     const uint8_t* src = base + ((nt * a.kb + kb) * 64 + lane) * 32;
     const float* sp = reinterpret_cast<const float*>(a.packed + a.scales_off + e * a.scales_pe);
     const float s = a.block ? sp[nt * a.kb + kb] : sp[n];
     for (int j = 0; j < 32; ++j) {
-      const int kk = a.fp8_bf16 ? (32 * lg + j) : ((j < 16) ? (16 * lg + j) : (64 + 16 * lg + j - 16));
-      orow[kk] = e4m3_value(src[j]) * s;
+      const int kk = a.bf16_order ? (32 * lg + j) : ((j < 16) ? (16 * lg + j) : (64 + 16 * lg + j - 16));
+      orow[kk] = (a.wdt == HUM_INT8 ? (float)(int8_t)src[j] : e4m3_value(src[j])) * s;
     }
     return;
   }
@@ -392,7 +392,7 @@ hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void*
   a.scale_f32 = L.scale_f32;
   a.has_zero = d->has_zero_point;
   a.block = d->scale_gran == HUM_SCALE_BLOCK;
-  a.fp8_bf16 = fmt_of(d) == F_FP8_BF16;
+  a.bf16_order = fmt_w8_bf16(fmt_of(d));
   const int64_t total = (int64_t)d->num_experts * L.nt * L.kb * 64;
   dequant_kernel<<<grid_for(total, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(a);
   hipError_t err = hipGetLastError();

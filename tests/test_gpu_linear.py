@@ -251,6 +251,45 @@ def test_fp8_weights_bf16_act_random_vs_oracle(m):
     assert_tol(out, ref, f"w8a16 fp8 m={m}")
 
 
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_int8_weights_exact_every_tile(tile):
+    """W8A16 with INT8 weights: integer bf16 activations in [-8, 8], every
+    INT8 code (-128..127), power-of-two per-channel scales; all sums are
+    exact in fp32: bitwise equal to the oracle (decode and tile kernels)."""
+    m, n, k = rows_for(tile, 23), 272, 1024
+    g = synth.rng(41)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    codes = g.integers(0, 256, size=(1, n, k), dtype=np.uint8)
+    scales = np.ldexp(1.0, g.integers(-12, -8, size=(1, n, 1))).astype(np.float32)
+    w = {"codes": codes, "scales": scales}
+    hd, od = descs("int8", "channel", 0, "f32", 1, n, k)
+    packed = prepare(hd, w, "f32")
+    print(f"case w8a16 int8 exact tile={tile}", flush=True)
+    if not stream_fits(tile, m, k, 2):
+        with pytest.raises(hum.HumError, match="raise split_k"):
+            hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+        return
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("gran", ["channel", "tensor"])
+@pytest.mark.parametrize("m", [1, 4, 16, 100, 300])
+def test_int8_weights_random_vs_oracle(m, gran):
+    """W8A16 with INT8 weights at the selector's config."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_for(9, m), "int8", gran, 0, "f32", 1, n, k, scale_lo=0.0002, scale_hi=0.001)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(9, 100 + m)), (m, k))
+    hd, od = descs("int8", gran, 0, "f32", 1, n, k)
+    packed = prepare(hd, w, "f32")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_tol(out, ref, f"w8a16 int8 m={m} {gran}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -392,7 +431,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "e2m1_mxfp8", "e2m1_mxfp4"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "int8", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -403,6 +442,10 @@ def test_empty_m_is_a_no_op(fmt):
     elif fmt == "e4m3":
         w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
         hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+        packed = prepare(hd, w, "f32")
+    elif fmt == "int8":
+        w = synth.quant_weights(synth.seed_for(3, 54), "int8", "channel", 0, "f32", 1, n, k)
+        hd, _ = descs("int8", "channel", 0, "f32", 1, n, k)
         packed = prepare(hd, w, "f32")
     elif fmt == "e4m3_bf16":
         w = synth.dense_w8a8(synth.seed_for(3, 53), 1, n, k)

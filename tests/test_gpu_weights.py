@@ -67,6 +67,21 @@ def test_dequant_bit_exact_fp8_weights_bf16_act(shape, gran):
     assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("gran", ["channel", "tensor"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dequant_bit_exact_int8(shape, gran):
+    """INT8 weights (the FP8-for-bf16 fragment order, every code)."""
+    e, n, k = shape
+    hd, od = descs("int8", gran, 0, "f32", e, n, k)
+    w = synth.quant_weights(hash(("int8", shape, gran)) & 0xFFFF, "int8", gran, 0, "f32", e, n, k)
+    packed = prepare(hd, w, "f32")
+    got = hum.dequant_weight(hd, packed)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.dequant_weight(od, w["codes"], w["scales"], include_global=False).astype(np.float32)
+    g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def test_group_k_equals_channel_bitwise():
     e, n, k = 1, 96, 512
     w = synth.quant_weights(5, "uint4", "group", k, "bf16", e, n, k, zero=True)
