@@ -101,14 +101,7 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
     inter = desc2.k
     assert desc13.n == 2 * inter and desc2.n == hdim
     x = decode_bf16(x_bits)
-    if act_fmt == "mxfp8":
-        a_in = qdq_mxfp8(x)
-    elif act_fmt == "mxfp4":
-        a_in = qdq_mxfp4(x)
-    elif act_fmt == "bf16":
-        a_in = x
-    else:
-        raise ValueError(act_fmt)
+    a_in = quant_input(x, act_fmt)
     out = np.zeros((t, hdim), dtype=np.float64)
     y_all = np.zeros((t * k, hdim), dtype=np.float64) if return_y else None
     flat = ids.reshape(-1)
@@ -118,20 +111,61 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
         if f.size == 0:
             continue
         tok = f // k
-        w_gu = dequant_weight(desc13, w13["codes"], w13["scales"], w13.get("zeros"),
-                              w13.get("global_scale"), experts=[e])[0]
-        h = a_in[tok] @ w_gu.T
-        del w_gu
-        a = swiglu(h, inter)
-        a = round_bf16(a) if act_fmt == "bf16" else (qdq_mxfp8(a) if act_fmt == "mxfp8" else qdq_mxfp4(a))
-        w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
-                              w2.get("global_scale"), experts=[e])[0]
-        y = a @ w_dn.T
-        del w_dn
+        y = expert_mlp(desc13, w13, desc2, w2, a_in[tok], e, act_fmt)
         if return_y:
             y_all[f] = y
         np.add.at(out, tok, wts.reshape(-1)[f][:, None] * y)
     return (out, y_all) if return_y else out
+
+
+def quant_input(x, act_fmt: str):
+    """The layer input as the GEMM sees it: MXFP8 / MXFP4 quantize-dequantize
+    per row and 32 along H, or the bf16 values themselves."""
+    if act_fmt == "mxfp8":
+        return qdq_mxfp8(x)
+    if act_fmt == "mxfp4":
+        return qdq_mxfp4(x)
+    if act_fmt == "bf16":
+        return x
+    raise ValueError(act_fmt)
+
+
+def expert_mlp(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict, a_in, e: int, act_fmt: str):
+    """One expert on its rows a_in (float64 [R, H], already in the input
+    format): h = a_in W13[e]^T, a = SwiGLU(h) at the stage precision,
+    y = a W2[e]^T (float64 [R, H])."""
+    inter = desc2.k
+    w_gu = dequant_weight(desc13, w13["codes"], w13["scales"], w13.get("zeros"),
+                          w13.get("global_scale"), experts=[e])[0]
+    h = np.asarray(a_in, dtype=np.float64) @ w_gu.T
+    del w_gu
+    a = swiglu(h, inter)
+    a = round_bf16(a) if act_fmt == "bf16" else (qdq_mxfp8(a) if act_fmt == "mxfp8" else qdq_mxfp4(a))
+    w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
+                          w2.get("global_scale"), experts=[e])[0]
+    return a @ w_dn.T
+
+
+def moe_masked(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict, x_bits, counts, act_fmt: str):
+    """The expert layer on the grouped_masked layout, a gemm_type of the MoE
+    runner (prhub.com.cn summary of SGLang PR #23754, "Key source
+    snippets"), whose arguments alone the pages give.  Reading: x_bits is
+    bf16 [E, max_m, H]; expert e's rows are the first counts[e] (clamped to
+    [0, max_m]); each runs the expert MLP of the indexed layer and its result
+    is that row's down output, without top-k weighting (the combine after
+    the layer applies it).  Returns (float64 [E, max_m, H], bool [E, max_m]
+    of the rows defined; the others are zero)."""
+    x = decode_bf16(x_bits)
+    e_count, max_m, hdim = x.shape
+    out = np.zeros((e_count, max_m, hdim), dtype=np.float64)
+    valid = np.zeros((e_count, max_m), dtype=bool)
+    for e in range(e_count):
+        c = int(min(max(int(counts[e]), 0), max_m))
+        if c == 0:
+            continue
+        out[e, :c] = expert_mlp(desc13, w13, desc2, w2, quant_input(x[e, :c], act_fmt), e, act_fmt)
+        valid[e, :c] = True
+    return out, valid
 
 
 def reduce(y, weights, topk: int):

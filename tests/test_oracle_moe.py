@@ -112,3 +112,30 @@ def test_routing_generator_properties():
     ids_z, _ = routing(8, 4096, 128, 8, zipf_s=1.1)
     cnt = np.bincount(ids_z.reshape(-1), minlength=128)
     assert cnt.max() > 5 * np.median(cnt)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+def test_masked_layout_equals_loop_of_dense(act):
+    """grouped_masked: every valid row of every expert buffer is that
+    expert's dense -> SwiGLU -> dense on the row alone; counts clamp to
+    [0, max_m]; the other rows are not defined (zero, flagged invalid)."""
+    e, hdim, inter, max_m = 4, 64, 32, 5
+    d13, w13, d2, w2 = _small_layer(50, e, hdim, inter)
+    g = np.random.default_rng(51)
+    x = bf16_bits(g.standard_normal((e, max_m, hdim)).astype(np.float32))
+    counts = np.array([5, 0, 2, 9], dtype=np.int32)
+    out, valid = M.moe_masked(d13, w13, d2, w2, x, counts, act)
+    assert valid.sum(axis=1).tolist() == [5, 0, 2, 5]
+    qdq = {"mxfp8": M.qdq_mxfp8, "mxfp4": M.qdq_mxfp4}.get(act)
+    for ex in range(e):
+        for i in range(max_m):
+            if not valid[ex, i]:
+                assert not out[ex, i].any()
+                continue
+            a_in = decode_bf16(x[ex, i:i + 1])
+            a_in = a_in if act == "bf16" else qdq(a_in)
+            h = G.linear(d13, a_in, w13["codes"], w13["scales"], expert=ex)
+            a = M.silu(h[:, :inter]) * h[:, inter:]
+            a = decode_bf16(encode_bf16(a)) if act == "bf16" else qdq(a)
+            y = G.linear(d2, a, w2["codes"], w2["scales"], expert=ex)[0]
+            assert np.allclose(out[ex, i], y, rtol=1e-12, atol=1e-12 * np.abs(y).max()), (ex, i)
