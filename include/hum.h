@@ -272,6 +272,33 @@ size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_d
                                   int64_t num_tokens, int32_t topk,
                                   const hum_tile_config* cfg);
 
+/* The expert layer on the "grouped_masked" layout (the EP low-latency
+ * receive format; a gemm_type of the MoE runner in the SGLang PR #23754
+ * summary, "Key source snippets"): expert e's rows are
+ * x[e][0 : expert_num_tokens[e]] of a bf16 [E][max_m][H] buffer, and
+ *   out[e][i] = down(SwiGLU(gate_up(x[e][i])))   for i < expert_num_tokens[e]
+ * in bf16 [E][max_m][H], with no top-k weighting (the combine after the
+ * layer applies it).  Rows i >= expert_num_tokens[e] of out are not written.
+ *   expert_num_tokens : i32 [E] on the device, each clamped to [0, max_m];
+ *                       read by the kernels only (no device->host copy)
+ *   max_m             : rows per expert buffer, a multiple of 16
+ *   expected_m        : the caller's host-side estimate of rows per expert;
+ *                       it picks the tile (the expert block must divide max_m)
+ *   cfg               : NULL = selector, else both GEMMs' configuration
+ * Same weight formats and activation formats as hum_moe_gemm; rows of x past
+ * an expert's count are read (quantized) but never reach out. */
+hum_status hum_moe_gemm_masked(const hum_weight_desc* w13, const void* packed_w13,
+                               const hum_weight_desc* w2, const void* packed_w2,
+                               int64_t max_m, int64_t expected_m, const void* x_bf16,
+                               const int32_t* expert_num_tokens, void* out_bf16,
+                               void* workspace, size_t ws_bytes,
+                               const hum_tile_config* cfg, void* stream);
+
+/* Workspace bytes hum_moe_gemm_masked needs (0 on invalid arguments). */
+size_t hum_moe_masked_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2,
+                                      int64_t max_m, int64_t expected_m,
+                                      const hum_tile_config* cfg);
+
 /* Stage export: sort the flat routing slots f = t*topk + j by expert.
  *   sorted  : i32 [T*topk + E*(block_m-1)]; segment of expert e starts at
  *             offsets[e], holds its slots in ascending f, is padded to a

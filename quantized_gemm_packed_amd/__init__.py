@@ -81,6 +81,8 @@ _SIGS = {
     "hum_last_error": (ctypes.c_char_p, []),
     "hum_packed_weight_bytes": (_SZ, [_DP]),
     "hum_select_config_ex": (_I32, [_DP, _I64, ctypes.c_uint32, _CP]),
+    "hum_moe_gemm_masked": (_I32, [_DP, _P, _DP, _P, _I64, _I64, _P, _P, _P, _P, _SZ, _CP, _P]),
+    "hum_moe_masked_workspace_bytes": (_SZ, [_DP, _DP, _I64, _I64, _CP]),
     "hum_autotune_linear": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _I32, ctypes.c_uint32, _CP,
                                    ctypes.POINTER(ctypes.c_float), _P]),
     "hum_moe_select_config": (_I32, [_DP, _DP, _I64, _I32, ctypes.c_uint32, _CP]),
@@ -355,6 +357,31 @@ def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids
                                           t_count, topk, _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
                                           _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg),
                                           _stream(x.device)))
+    return out
+
+
+def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, expert_num_tokens, expected_m: int,
+                    out=None, cfg: TileConfig | None = None, workspace=None):
+    """grouped_masked layout: x bf16 [E, max_m, H], expert_num_tokens int32
+    [E] (device) -> bf16 [E, max_m, H]; rows past an expert's count are left
+    as they were in `out`."""
+    import torch
+    for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"),
+                  (expert_num_tokens, "expert_num_tokens")):
+        _gpu(t, nm)
+    e, max_m, h = x.shape
+    if out is None:
+        out = torch.zeros((e, max_m, h), dtype=torch.bfloat16, device=x.device)
+    lib = load_library()
+    need = lib.hum_moe_masked_workspace_bytes(ctypes.byref(w13), ctypes.byref(w2), max_m, int(expected_m),
+                                              None if cfg is None else ctypes.byref(cfg))
+    if need == 0:
+        raise HumError(1, lib.hum_last_error().decode())
+    ws = workspace if workspace is not None else _workspace(x.device).get(need)
+    wsb = 0 if ws is None else ws.numel()
+    _check(lib.hum_moe_gemm_masked(ctypes.byref(w13), _ptr(packed_w13), ctypes.byref(w2), _ptr(packed_w2), max_m,
+                                   int(expected_m), _ptr(x), _ptr(expert_num_tokens), _ptr(out), _ptr(ws), wsb,
+                                   None if cfg is None else ctypes.byref(cfg), _stream(x.device)))
     return out
 
 

@@ -394,4 +394,33 @@ hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t t
   return HUM_OK;
 }
 
+// ---------------------------------------------------------------------------
+// grouped_masked layout: one thread per row position (and per block).
+
+__global__ void masked_align_kernel(const int32_t* __restrict__ counts, int32_t num_experts, int64_t max_m,
+                                    int32_t block_m, int32_t* __restrict__ sorted,
+                                    int32_t* __restrict__ block_expert) {
+  const int64_t total = (int64_t)num_experts * max_m;
+  const int64_t pos = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (pos >= total) return;
+  const int64_t e = pos / max_m;
+  const int64_t i = pos - e * max_m;
+  int64_t c = counts[e];
+  c = c < 0 ? 0 : (c > max_m ? max_m : c);
+  sorted[pos] = i < c ? (int32_t)pos : (int32_t)total;
+  if (i % block_m == 0) block_expert[pos / block_m] = i < c ? (int32_t)e : -1;
+}
+
+hum_status launch_masked_align(const int32_t* counts, int32_t e, int64_t max_m, int32_t block_m,
+                               int32_t* sorted, int32_t* block_expert, void* stream) {
+  const int64_t total = (int64_t)e * max_m;
+  if (total == 0) return HUM_OK;
+  const int B = 256;
+  masked_align_kernel<<<(unsigned)((total + B - 1) / B), B, 0, static_cast<hipStream_t>(stream)>>>(
+      counts, e, max_m, block_m, sorted, block_expert);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "masked align launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
 }  // namespace hum

@@ -655,15 +655,17 @@ struct MoeWs {
   int64_t cap = 0, nblocks = 0;
 };
 
+// masked: t rows of the [E][max_m] layout, one slot per row, slot = row
+// (no padding beyond max_m, output written by the down GEMM in place).
 static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk,
-                    const MoeCfg& mc) {
+                    const MoeCfg& mc, bool masked = false) {
   MoeWs w;
   const int64_t E = w13->num_experts;
   const int64_t bm = tile_rows(mc.up);
   const int split = mc.up.split_k > mc.dn.split_k ? mc.up.split_k : mc.dn.split_k;
   const int64_t inter = w2->k;
   const int64_t h = w13->k;
-  w.cap = t * topk + E * (bm - 1);
+  w.cap = masked ? t : t * topk + E * (bm - 1);
   w.nblocks = cdiv(w.cap, bm);
   const bool mx = w13->act_fmt == HUM_ACT_MXFP8 || w13->act_fmt == HUM_ACT_MXFP4;
   const bool mx4 = w13->act_fmt == HUM_ACT_MXFP4;  // E2M1 codes, two per byte
@@ -690,7 +692,7 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   w.inter_s = off;
   if (mx) off = align256(off + w.cap * (inter / 32));
   w.y = off;
-  off = align256(off + t * topk * h * 2);
+  if (!masked) off = align256(off + t * topk * h * 2);
   w.total = off;
   return w;
 }
@@ -761,17 +763,8 @@ hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights, int64_t
   return launch_moe_reduce(y_bf16, topk_weights, t, topk, h, out_bf16, stream);
 }
 
-hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
-                           const void* packed_w2, int64_t t, int32_t topk, const void* x_bf16,
-                           const int32_t* topk_ids, const float* topk_weights, void* out_bf16, void* workspace,
-                           size_t ws_bytes, const hum_tile_config* cfg, void* stream) {
-  clear_error();
-  hum_status st = check_moe(w13, w2, t, topk);
-  if (st != HUM_OK) return st;
-  if (t == 0) return HUM_OK;
-  if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
-    return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
-  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+// Kernel keys of a layer's two GEMMs; HUM_OK when both are compiled.
+static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelKey* kup, KernelKey* kdn) {
   const hum_tile_config& cu = mc.up;
   const hum_tile_config& cd = mc.dn;
   if (!cfg_sane(cu) || !cfg_sane(cd) || tile_rows(cu) != tile_rows(cd))
@@ -779,28 +772,41 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   const int f = fmt_of(w13);
   const int epi_up =
       (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : (f == F_MXFP4_MXFP4 ? EPI_SWIGLU_MXFP4 : EPI_SWIGLU_BF16);
-  KernelKey kup{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
-  KernelKey kdn{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
-  if (!gemm_instance_exists(kup) || !gemm_instance_exists(kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
-  const MoeWs w = moe_ws(w13, w2, t, topk, mc);
-  if (!workspace || ws_bytes < (size_t)w.total)
-    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
-  log_cfg("moe up", cu, t);
-  log_cfg("moe down", cd, t);
+  *kup = KernelKey{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
+  *kdn = KernelKey{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
+  if (!gemm_instance_exists(*kup) || !gemm_instance_exists(*kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  return HUM_OK;
+}
+
+// The rows of one expert layer call, as the two GEMMs see them.
+struct MoeRows {
+  int64_t x_rows;      // rows of x (activations quantized before gate_up)
+  int32_t topk;        // a sorted slot f reads x row f / topk
+  int32_t sentinel;    // slots >= sentinel are padding
+  int32_t stream_rows; // upper bound of the valid rows of one expert block
+};
+
+// gate_up (+ SwiGLU, + requantization) into the workspace, then down with
+// its rows scattered to y[slot] (row stride h), over the expert blocks that
+// ws.sorted / ws.bexp describe.
+static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                            const void* packed_w2, const MoeCfg& mc, const KernelKey& kup, const KernelKey& kdn,
+                            const MoeWs& w, uint8_t* ws, const MoeRows& r, const void* x_bf16, void* y,
+                            void* stream) {
   Layout L13, L2;
   compute_layout(w13, &L13);
   compute_layout(w2, &L2);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int64_t E = w13->num_experts, h = w13->k, inter = w2->k;
+  const int64_t h = w13->k, inter = w2->k, t = r.x_rows;
+  const hum_tile_config& cu = mc.up;
+  const hum_tile_config& cd = mc.dn;
   const int32_t bm = (int32_t)tile_rows(cu);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
-  st = launch_align(topk_ids, t, topk, (int32_t)E, bm, sorted, reinterpret_cast<int32_t*>(ws + w.offsets),
-                    reinterpret_cast<int32_t*>(ws + w.counts), bexp, w.nblocks, stream);
-  if (st != HUM_OK) return st;
+  const int f = fmt_of(w13);
   const bool mx4 = f == F_MXFP4_MXFP4;
   const bool mx = f == F_MXFP4_MXFP8 || mx4;
   const void* x_use = x_bf16;
+  hum_status st = HUM_OK;
   if (mx) {
     st = mx4 ? launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream)
              : launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
@@ -819,8 +825,8 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   p.m = w.cap;
   p.sorted = sorted;
   p.block_expert = bexp;
-  p.topk = topk;
-  p.sentinel = (int)(t * topk);
+  p.topk = r.topk;
+  p.sentinel = r.sentinel;
   p.out = ws + w.inter;
   p.ldo = inter;
   p.out_scale = mx ? ws + w.inter_s : nullptr;
@@ -829,10 +835,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   p.split_k = cu.split_k;
   p.kb_per_split = kb_per_split(L13.kb, cu);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
-  // upper bound of the valid rows of one expert block (any routing, also
-  // repeated ids within a token): the LDS staging is sized for it
-  const int64_t slots = t * topk;
-  p.stream_rows = (int)(slots < 16 ? slots : 16);
+  p.stream_rows = r.stream_rows;
   p.a_bytes = mx4 ? t * (h / 2) : t * h * (mx ? 1 : 2);
   p.a_scale_bytes = mx ? t * (h / 32) : 0;
   st = launch_gemm(kup, p, w.nblocks, bm, stream);
@@ -847,9 +850,9 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.m = w.cap;
   q.sorted = sorted;
   q.block_expert = bexp;
-  q.topk = topk;
-  q.sentinel = (int)(t * topk);
-  q.out = ws + w.y;
+  q.topk = r.topk;
+  q.sentinel = r.sentinel;
+  q.out = y;
   q.ldo = h;
   q.out_scale = nullptr;
   q.bias = nullptr;
@@ -857,12 +860,102 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   q.split_k = cd.split_k;
   q.kb_per_split = kb_per_split(L2.kb, cd);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
-  q.stream_rows = p.stream_rows;  // valid (non-padding) rows of a block
+  q.stream_rows = r.stream_rows;  // valid (non-padding) rows of a block
   q.a_bytes = mx4 ? w.cap * (inter / 2) : w.cap * inter * (mx ? 1 : 2);
   q.a_scale_bytes = mx ? w.cap * (inter / 32) : 0;
-  st = launch_gemm(kdn, q, w.nblocks, bm, stream);
+  return launch_gemm(kdn, q, w.nblocks, bm, stream);
+}
+
+hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                           const void* packed_w2, int64_t t, int32_t topk, const void* x_bf16,
+                           const int32_t* topk_ids, const float* topk_weights, void* out_bf16, void* workspace,
+                           size_t ws_bytes, const hum_tile_config* cfg, void* stream) {
+  clear_error();
+  hum_status st = check_moe(w13, w2, t, topk);
+  if (st != HUM_OK) return st;
+  if (t == 0) return HUM_OK;
+  if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
+    return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+  KernelKey kup, kdn;
+  st = moe_keys(w13, mc, &kup, &kdn);
+  if (st != HUM_OK) return st;
+  const MoeWs w = moe_ws(w13, w2, t, topk, mc);
+  if (!workspace || ws_bytes < (size_t)w.total)
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
+  log_cfg("moe up", mc.up, t);
+  log_cfg("moe down", mc.dn, t);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t E = w13->num_experts, h = w13->k;
+  st = launch_align(topk_ids, t, topk, (int32_t)E, (int32_t)tile_rows(mc.up), reinterpret_cast<int32_t*>(ws + w.sorted),
+                    reinterpret_cast<int32_t*>(ws + w.offsets), reinterpret_cast<int32_t*>(ws + w.counts),
+                    reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream);
+  if (st != HUM_OK) return st;
+  const int64_t slots = t * topk;
+  const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16)};
+  st = moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, rows, x_bf16, ws + w.y, stream);
   if (st != HUM_OK) return st;
   return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
+}
+
+// ---- the grouped_masked layout ---------------------------------------------
+
+// Validation shared by the masked entry points.
+static hum_status check_masked(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t max_m,
+                               int64_t expected_m) {
+  if (max_m < 0 || max_m % 16) return set_error(HUM_ERR_INVALID_ARG, "max_m must be a non-negative multiple of 16");
+  if (expected_m < 0) return set_error(HUM_ERR_INVALID_ARG, "expected_m < 0");
+  if (!w13 || !w2) return set_error(HUM_ERR_INVALID_ARG, "NULL description");
+  return check_moe(w13, w2, (int64_t)w13->num_experts * max_m, 1);
+}
+
+// Tile choice from the expected rows per expert; the expert block must
+// divide max_m, so a larger tile steps down to one that does.
+static MoeCfg select_masked(const hum_weight_desc* w13, int64_t max_m, int64_t expected_m) {
+  MoeCfg mc = select_moe(w13, (expected_m < 1 ? 1 : expected_m) * w13->num_experts, 1);
+  while (max_m % tile_rows(mc.up) && mc.up.wave_m > 1) {
+    const int wm = mc.up.wave_m / 2;
+    mc = MoeCfg{moe_tile_cfg(wm), moe_tile_cfg(wm)};
+  }
+  return mc;
+}
+
+size_t hum_moe_masked_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t max_m,
+                                      int64_t expected_m, const hum_tile_config* cfg) {
+  clear_error();
+  if (check_masked(w13, w2, max_m, expected_m) != HUM_OK) return 0;
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_masked(w13, max_m, expected_m);
+  return (size_t)moe_ws(w13, w2, (int64_t)w13->num_experts * (max_m < 16 ? 16 : max_m), 1, mc, true).total;
+}
+
+hum_status hum_moe_gemm_masked(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                               const void* packed_w2, int64_t max_m, int64_t expected_m, const void* x_bf16,
+                               const int32_t* expert_num_tokens, void* out_bf16, void* workspace, size_t ws_bytes,
+                               const hum_tile_config* cfg, void* stream) {
+  clear_error();
+  hum_status st = check_masked(w13, w2, max_m, expected_m);
+  if (st != HUM_OK) return st;
+  if (max_m == 0) return HUM_OK;
+  if (!packed_w13 || !packed_w2 || !x_bf16 || !expert_num_tokens || !out_bf16)
+    return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_masked(w13, max_m, expected_m);
+  KernelKey kup, kdn;
+  st = moe_keys(w13, mc, &kup, &kdn);
+  if (st != HUM_OK) return st;
+  const int32_t bm = (int32_t)tile_rows(mc.up);
+  if (max_m % bm) return set_error(HUM_ERR_UNSUPPORTED, "the expert block (%d rows) must divide max_m", bm);
+  const int64_t rows = (int64_t)w13->num_experts * max_m;
+  const MoeWs w = moe_ws(w13, w2, rows, 1, mc, true);
+  if (!workspace || ws_bytes < (size_t)w.total)
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
+  log_cfg("moe masked up", mc.up, rows);
+  log_cfg("moe masked down", mc.dn, rows);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  st = launch_masked_align(expert_num_tokens, w13->num_experts, max_m, bm, reinterpret_cast<int32_t*>(ws + w.sorted),
+                           reinterpret_cast<int32_t*>(ws + w.bexp), stream);
+  if (st != HUM_OK) return st;
+  const MoeRows r{rows, 1, (int32_t)rows, (int32_t)(max_m < 16 ? max_m : 16)};
+  return moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, r, x_bf16, out_bf16, stream);
 }
 
 hum_status hum_moe_gemm(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,

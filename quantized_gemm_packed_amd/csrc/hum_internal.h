@@ -95,6 +95,12 @@ hum_status launch_zero(void* p, size_t bytes, void* stream);
 hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
                         int32_t block_m, int32_t* sorted, int32_t* offsets, int32_t* counts,
                         int32_t* block_expert, int64_t nblocks, void* stream);
+// grouped_masked layout: sorted[e * max_m + i] = that position when
+// i < clamp(counts[e], 0, max_m), else the sentinel E * max_m; block b of
+// block_m rows belongs to expert b * block_m / max_m, or -1 when all its
+// rows are padding.
+hum_status launch_masked_align(const int32_t* counts, int32_t e, int64_t max_m, int32_t block_m,
+                               int32_t* sorted, int32_t* block_expert, void* stream);
 hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t topk,
                              int64_t h, void* out, void* stream);
 

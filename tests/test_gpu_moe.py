@@ -173,3 +173,105 @@ def test_moe_zero_tokens_is_a_no_op(act):
     out = hum.moe_gemm(d13, p13, d2, p2, x, ids, wts)
     torch.cuda.synchronize()
     assert tuple(out.shape) == (0, h)
+
+
+# ---- grouped_masked layout ---------------------------------------------------
+
+_UNTOUCHED = 0x3F81  # bf16 bits of 1.0078125: rows past a count must keep it
+
+
+def _masked_case(seed, e, max_m, h, counts):
+    xb = synth.bf16_normal(synth.rng(seed), (e, max_m, h))
+    cnt = np.asarray(counts, dtype=np.int32)
+    out = torch.full((e, max_m, h), _UNTOUCHED, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return xb, cnt, out
+
+
+def _check_masked(out, ref, valid, what):
+    bits = out.view(torch.int16).cpu().numpy()
+    assert np.all(bits[~valid] == _UNTOUCHED), f"{what}: rows past a count were written"
+    if valid.any():
+        assert_tol(out[torch.from_numpy(valid).cuda()], ref[valid], what)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_moe_masked_every_tile(act, tile):
+    e, h, inter, max_m = 8, 256, 128, 128
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(720, e, h, inter, act)
+    xb, cnt, out = _masked_case(721, e, max_m, h, [128, 0, 1, 17, 33, 140, 5, 100])
+    print(f"case moe masked act={act} tile={tile}", flush=True)
+    if act == "mxfp4" and tile[0] == 1:
+        with pytest.raises(hum.HumError, match="tile config not available"):
+            hum.moe_gemm_masked(d13, p13, d2, p2, dev(xb), dev(cnt), 16, out=out, cfg=cfg(tile))
+        return
+    hum.moe_gemm_masked(d13, p13, d2, p2, dev(xb), dev(cnt), 16, out=out, cfg=cfg(tile))
+    torch.cuda.synchronize()
+    ref, valid = oracle.moe.moe_masked(o13, w13, o2, w2, xb, cnt, act)
+    _check_masked(out, ref, valid, f"masked act={act} tile={tile}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("expected_m", [1, 20, 200])
+def test_moe_masked_selector(act, expected_m):
+    """Default tiles from expected_m; max_m = 48 makes 64-row tiles step down."""
+    e, h, inter, max_m = 8, 256, 128, 48
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(730, e, h, inter, act)
+    g = synth.rng(731 + expected_m)
+    xb, cnt, out = _masked_case(732 + expected_m, e, max_m, h, g.integers(0, max_m + 1, size=e))
+    hum.moe_gemm_masked(d13, p13, d2, p2, dev(xb), dev(cnt), expected_m, out=out)
+    torch.cuda.synchronize()
+    ref, valid = oracle.moe.moe_masked(o13, w13, o2, w2, xb, cnt, act)
+    _check_masked(out, ref, valid, f"masked act={act} expected_m={expected_m}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_moe_masked_equals_indexed_top1(act):
+    """Tokens routed top-1 with weight 1, laid out per expert: each masked
+    row equals that token's indexed-layer output bitwise (same tile kernels;
+    each row is summed in one order whatever the other rows are)."""
+    e, h, inter, t, max_m = 8, 256, 128, 40, 16
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(740, e, h, inter, act)
+    g = synth.rng(741)
+    ids = g.integers(0, e, size=(t, 1)).astype(np.int32)
+    cnt_all = np.bincount(ids[:, 0], minlength=e)
+    keep = np.ones(t, dtype=bool)
+    for ex in range(e):   # at most max_m tokens per expert
+        keep[np.nonzero(ids[:, 0] == ex)[0][max_m:]] = False
+    ids = ids[keep]
+    t = ids.shape[0]
+    wts = np.ones((t, 1), dtype=np.float32)
+    xb = synth.bf16_normal(synth.rng(742), (t, h))
+    xm = np.zeros((e, max_m, h), dtype=np.uint16)
+    slot = np.zeros(t, dtype=np.int64)
+    cnt = np.zeros(e, dtype=np.int32)
+    for tt in range(t):
+        ex = int(ids[tt, 0])
+        slot[tt] = ex * max_m + cnt[ex]
+        xm[ex, cnt[ex]] = xb[tt]
+        cnt[ex] += 1
+    assert cnt.sum() == t and cnt_all.sum() >= t
+    tile = (0, 1, 4, 4, 1)
+    ind = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg(tile))
+    msk = hum.moe_gemm_masked(d13, p13, d2, p2, dev(xm), dev(cnt), max_m, cfg=cfg(tile))
+    torch.cuda.synchronize()
+    got = msk.view(torch.int16).reshape(e * max_m, h).cpu().numpy()[slot]
+    assert np.array_equal(got, ind.view(torch.int16).cpu().numpy())
+
+
+def test_moe_masked_edges():
+    e, h, inter = 4, 256, 128
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(750, e, h, inter, "bf16")
+    empty = torch.zeros((e, 0, h), dtype=torch.bfloat16, device="cuda")
+    cnt = dev(np.zeros(e, dtype=np.int32))
+    assert hum.moe_gemm_masked(d13, p13, d2, p2, empty, cnt, 4).shape == (e, 0, h)
+    with pytest.raises(hum.HumError, match="multiple of 16"):
+        hum.moe_gemm_masked(d13, p13, d2, p2, torch.zeros((e, 24, h), dtype=torch.bfloat16, device="cuda"), cnt, 4)
+    with pytest.raises(hum.HumError, match="must divide max_m"):
+        hum.moe_gemm_masked(d13, p13, d2, p2, torch.zeros((e, 48, h), dtype=torch.bfloat16, device="cuda"), cnt, 4,
+                            cfg=cfg((0, 2, 4, 4, 1)))
+    # all counts zero: nothing written
+    xb, c0, out = _masked_case(751, e, 32, h, [0, 0, 0, 0])
+    hum.moe_gemm_masked(d13, p13, d2, p2, dev(xb), dev(c0), 4, out=out)
+    torch.cuda.synchronize()
+    assert np.all(out.view(torch.int16).cpu().numpy() == _UNTOUCHED)
