@@ -315,6 +315,50 @@ def moe(hum, timer, iters, act):
     return out
 
 
+def moe_masked(hum, timer, iters, act):
+    """The W4A8 expert layer on the grouped_masked layout (per-expert padded
+    buffers [E][max_m][H] with device-side row counts, no top-k combine), the
+    same 128 experts as the indexed sweep; counts from Zipf-skewed routing of
+    T tokens, clamped to max_m."""
+    import synth
+    import torch
+    e, h, inter, topk, max_m = 128, 4096, 1024, 8, 256
+    w13 = synth.moe_weights_mxfp4(synth.seed_for(4), e, 2 * inter, h)
+    w2 = synth.moe_weights_mxfp4(synth.seed_for(4, 1), e, h, inter)
+    d13 = hum.make_desc("e2m1", "group", 32, "e8m0", 2 * inter, h, num_experts=e, act_fmt=act)
+    d2 = hum.make_desc("e2m1", "group", 32, "e8m0", h, inter, num_experts=e, act_fmt=act)
+    p13 = [hum.prepare_weight(d13, _dev(w13["codes"]), _dev(w13["scales"]))]
+    p2 = [hum.prepare_weight(d2, _dev(w2["codes"]), _dev(w2["scales"]))]
+    del w13, w2
+    p13.append(p13[0].clone())
+    p2.append(p2[0].clone())
+    per_expert = (2 * inter * h // 2 + 2 * inter * h // 32) + (h * inter // 2 + h * inter // 32)
+    x = _dev(synth.bf16_normal(synth.rng(synth.seed_for(6, 100)), (e, max_m, h)))
+    o = torch.empty((e, max_m, h), dtype=torch.bfloat16, device="cuda")
+    out = []
+    for i, t in enumerate((16, 128, 1024)):
+        ids, _ = synth.routing(synth.seed_for(6, i), t, e, topk, zipf_s=1.1)
+        cnt = np.minimum(np.bincount(ids.reshape(-1), minlength=e), max_m).astype(np.int32)
+        expected = -(-t * topk // e)
+        dc = _dev(cnt)
+        ws = hum.Workspace("cuda").get(hum.moe_masked_workspace_bytes(d13, d2, max_m, expected))
+        fn = lambda j: hum.moe_gemm_masked(d13, p13[j % 2], d2, p2[j % 2], x, dc, expected, out=o, workspace=ws)
+        timer.run(fn, 2)
+        tt = timer.run(fn, max(5, iters // 2))
+        rows = int(cnt.sum())
+        flops = 2.0 * rows * (2 * inter * h + h * inter)
+        touched = int((cnt > 0).sum())
+        wb = touched * per_expert
+        bound = "hbm" if rows < 8 * 1024 else "mfma"
+        peak = {"bf16": BF16_PEAK, "mxfp8": FP8_PEAK, "mxfp4": FP4_PEAK}[act]
+        out.append({"tokens": t, "max_m": max_m, "expected_m": expected, "rows": rows, "us": tt * 1e6,
+                    "tflops": flops / tt / 1e12, "weight_gbs": wb / tt / 1e9, "experts_touched": touched,
+                    "bound": bound, "frac": (wb / tt / HBM_PEAK) if bound == "hbm" else flops / tt / peak})
+    del p13, p2
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, budget_s=30.0):
     """Oracle (NumPy float64) on the host: the same M sweep restricted to a
     column sample of the weights."""
@@ -412,6 +456,7 @@ def main():
         sweep["moe_w4a16_mxfp4_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "bf16")
         sweep["moe_w4a8_mxfp4_mxfp8_zipf1.1_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "mxfp8")
         sweep["moe_w4a4_mxfp4_mxfp4_zipf1.1_e128_top8_h4096_i1024"] = moe(hum, timer, iters, "mxfp4")
+        sweep["moe_masked_w4a8_mxfp4_mxfp8_e128_maxm256_h4096_i1024"] = moe_masked(hum, timer, iters, "mxfp8")
     cpu = None if args.no_cpu else cpu_baseline(d["case"])
     line = {
         "metric": "quant GEMM TFLOP/s + weight HBM GB/s vs roofline, dense & MoE, M=1..4096",

@@ -360,6 +360,16 @@ def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids
     return out
 
 
+def moe_masked_workspace_bytes(w13: WeightDesc, w2: WeightDesc, max_m: int, expected_m: int,
+                               cfg: TileConfig | None = None) -> int:
+    lib = load_library()
+    b = lib.hum_moe_masked_workspace_bytes(ctypes.byref(w13), ctypes.byref(w2), int(max_m), int(expected_m),
+                                           None if cfg is None else ctypes.byref(cfg))
+    if b == 0:
+        raise HumError(1, lib.hum_last_error().decode())
+    return b
+
+
 def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, expert_num_tokens, expected_m: int,
                     out=None, cfg: TileConfig | None = None, workspace=None):
     """grouped_masked layout: x bf16 [E, max_m, H], expert_num_tokens int32
@@ -373,10 +383,7 @@ def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, e
     if out is None:
         out = torch.zeros((e, max_m, h), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
-    need = lib.hum_moe_masked_workspace_bytes(ctypes.byref(w13), ctypes.byref(w2), max_m, int(expected_m),
-                                              None if cfg is None else ctypes.byref(cfg))
-    if need == 0:
-        raise HumError(1, lib.hum_last_error().decode())
+    need = moe_masked_workspace_bytes(w13, w2, max_m, expected_m, cfg)
     ws = workspace if workspace is not None else _workspace(x.device).get(need)
     wsb = 0 if ws is None else ws.numel()
     _check(lib.hum_moe_gemm_masked(ctypes.byref(w13), _ptr(packed_w13), ctypes.byref(w2), _ptr(packed_w2), max_m,

@@ -120,14 +120,12 @@ hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t l
 // ---------------------------------------------------------------------------
 // MXFP8: each thread quantizes 8 elements; a DPP quad owns one 32-block.
 
-__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
-                                                          uint8_t* __restrict__ s) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t cpr = k / 8;  // chunks per row
-  const bool valid = id < m * cpr;
-  const int64_t row = valid ? id / cpr : 0;
-  const int64_t c8 = valid ? id % cpr : 0;
+// One 8-element chunk (row, c8) of the MXFP8 quantizer; every lane of a
+// wave calls it together (the DPP quad reduction reads the quad's four
+// lanes), with valid = false for lanes that have no chunk.
+__device__ __forceinline__ void mxfp8_chunk(const uint16_t* __restrict__ x, int64_t ldx, int64_t k, int64_t row,
+                                              int64_t c8, bool valid, uint8_t* __restrict__ q,
+                                              uint8_t* __restrict__ s) {
   u32x4_t v = {0, 0, 0, 0};
   if (valid) v = *reinterpret_cast<const u32x4_t*>(x + row * ldx + c8 * 8);
   float f[8];
@@ -150,12 +148,49 @@ __global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __rest
   if ((c8 & 3) == 0) s[row * (k / 32) + c8 / 4] = (uint8_t)e;
 }
 
+__global__ __launch_bounds__(256) void quant_mxfp8_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ s) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;  // chunks per row
+  const bool valid = id < m * cpr;
+  mxfp8_chunk(x, ldx, k, valid ? id / cpr : 0, valid ? id % cpr : 0, valid, q, s);
+}
+
+// grouped_masked buffers: workgroup (e, slice) walks rows slice, slice +
+// slices, ... below expert e's count (clamped to [0, max_m]); rows past
+// it are not read.  Loop bounds are uniform over the workgroup.
+__global__ __launch_bounds__(256) void quant_mxfp8_masked_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                 int64_t k, const int32_t* __restrict__ counts,
+                                                                 int64_t max_m, int slices,
+                                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t e = blockIdx.x / slices;
+  const int slice = (int)(blockIdx.x % slices);
+  int64_t c = counts[e];
+  c = c < 0 ? 0 : (c > max_m ? max_m : c);
+  const int64_t cpr = k / 8;
+  for (int64_t i = slice; i < c; i += slices)
+    for (int64_t base = 0; base < cpr; base += 256) {
+      const int64_t c8 = base + threadIdx.x;
+      mxfp8_chunk(x, ldx, k, e * max_m + i, c8 < cpr ? c8 : 0, c8 < cpr, q, s);
+    }
+}
+
 hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
-                              uint8_t* s, void* stream) {
+                              uint8_t* s, void* stream, const int32_t* counts, int64_t max_m) {
   if (m == 0) return HUM_OK;
-  const int64_t chunks = m * (k / 8);
-  quant_mxfp8_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (counts) {
+    // m = E * max_m rows; about 2048 workgroups over the experts
+    const int64_t e = m / max_m;
+    const int slices = (int)(e >= 2048 ? 1 : (2048 + e - 1) / e);
+    quant_mxfp8_masked_kernel<<<(unsigned)(e * slices), 256, 0, st>>>(
+        static_cast<const uint16_t*>(x), ldx, k, counts, max_m, slices, static_cast<uint8_t*>(q), s);
+  } else {
+    const int64_t chunks = m * (k / 8);
+    quant_mxfp8_kernel<<<cdiv_u(chunks, 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), ldx, m, k,
+                                                              static_cast<uint8_t*>(q), s);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp8 launch: %s", hipGetErrorString(err));
   return HUM_OK;
@@ -170,14 +205,12 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
 // E2M1 grid is a comparison against the midpoints, ties to the even code.
 
 
-__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
-                                                          uint8_t* __restrict__ s) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t cpr = k / 8;  // chunks per row
-  const bool valid = id < m * cpr;
-  const int64_t row = valid ? id / cpr : 0;
-  const int64_t c8 = valid ? id % cpr : 0;
+// One 8-element chunk (row, c8) of the MXFP4 quantizer; every lane of a
+// wave calls it together (the DPP quad reduction reads the quad's four
+// lanes), with valid = false for lanes that have no chunk.
+__device__ __forceinline__ void mxfp4_chunk(const uint16_t* __restrict__ x, int64_t ldx, int64_t k, int64_t row,
+                                              int64_t c8, bool valid, uint8_t* __restrict__ q,
+                                              uint8_t* __restrict__ s) {
   u32x4_t v = {0, 0, 0, 0};
   if (valid) v = *reinterpret_cast<const u32x4_t*>(x + row * ldx + c8 * 8);
   float f[8];
@@ -200,12 +233,49 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   if ((c8 & 3) == 0) s[row * (k / 32) + c8 / 4] = (uint8_t)e;
 }
 
+__global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                          int64_t m, int64_t k, uint8_t* __restrict__ q,
+                                                          uint8_t* __restrict__ s) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cpr = k / 8;  // chunks per row
+  const bool valid = id < m * cpr;
+  mxfp4_chunk(x, ldx, k, valid ? id / cpr : 0, valid ? id % cpr : 0, valid, q, s);
+}
+
+// grouped_masked buffers: workgroup (e, slice) walks rows slice, slice +
+// slices, ... below expert e's count (clamped to [0, max_m]); rows past
+// it are not read.  Loop bounds are uniform over the workgroup.
+__global__ __launch_bounds__(256) void quant_mxfp4_masked_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                 int64_t k, const int32_t* __restrict__ counts,
+                                                                 int64_t max_m, int slices,
+                                                                 uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int64_t e = blockIdx.x / slices;
+  const int slice = (int)(blockIdx.x % slices);
+  int64_t c = counts[e];
+  c = c < 0 ? 0 : (c > max_m ? max_m : c);
+  const int64_t cpr = k / 8;
+  for (int64_t i = slice; i < c; i += slices)
+    for (int64_t base = 0; base < cpr; base += 256) {
+      const int64_t c8 = base + threadIdx.x;
+      mxfp4_chunk(x, ldx, k, e * max_m + i, c8 < cpr ? c8 : 0, c8 < cpr, q, s);
+    }
+}
+
 hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
-                              uint8_t* s, void* stream) {
+                              uint8_t* s, void* stream, const int32_t* counts, int64_t max_m) {
   if (m == 0) return HUM_OK;
-  const int64_t chunks = m * (k / 8);
-  quant_mxfp4_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (counts) {
+    // m = E * max_m rows; about 2048 workgroups over the experts
+    const int64_t e = m / max_m;
+    const int slices = (int)(e >= 2048 ? 1 : (2048 + e - 1) / e);
+    quant_mxfp4_masked_kernel<<<(unsigned)(e * slices), 256, 0, st>>>(
+        static_cast<const uint16_t*>(x), ldx, k, counts, max_m, slices, static_cast<uint8_t*>(q), s);
+  } else {
+    const int64_t chunks = m * (k / 8);
+    quant_mxfp4_kernel<<<cdiv_u(chunks, 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), ldx, m, k,
+                                                              static_cast<uint8_t*>(q), s);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp4 launch: %s", hipGetErrorString(err));
   return HUM_OK;

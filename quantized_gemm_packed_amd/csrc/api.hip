@@ -780,10 +780,12 @@ static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelK
 
 // The rows of one expert layer call, as the two GEMMs see them.
 struct MoeRows {
-  int64_t x_rows;      // rows of x (activations quantized before gate_up)
-  int32_t topk;        // a sorted slot f reads x row f / topk
-  int32_t sentinel;    // slots >= sentinel are padding
-  int32_t stream_rows; // upper bound of the valid rows of one expert block
+  int64_t x_rows;         // rows of x (activations quantized before gate_up)
+  int32_t topk;           // a sorted slot f reads x row f / topk
+  int32_t sentinel;       // slots >= sentinel are padding
+  int32_t stream_rows;    // upper bound of the valid rows of one expert block
+  const int32_t* counts;  // grouped_masked: live rows per expert buffer (else NULL)
+  int64_t max_m;          // grouped_masked: rows per expert buffer
 };
 
 // gate_up (+ SwiGLU, + requantization) into the workspace, then down with
@@ -808,8 +810,8 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const void* x_use = x_bf16;
   hum_status st = HUM_OK;
   if (mx) {
-    st = mx4 ? launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream)
-             : launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
+    st = mx4 ? launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m)
+             : launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
     if (st != HUM_OK) return st;
     x_use = ws + w.xq;
   }
@@ -892,7 +894,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
                     reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream);
   if (st != HUM_OK) return st;
   const int64_t slots = t * topk;
-  const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16)};
+  const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16), nullptr, 0};
   st = moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, rows, x_bf16, ws + w.y, stream);
   if (st != HUM_OK) return st;
   return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
@@ -909,15 +911,19 @@ static hum_status check_masked(const hum_weight_desc* w13, const hum_weight_desc
   return check_moe(w13, w2, (int64_t)w13->num_experts * max_m, 1);
 }
 
-// Tile choice from the expected rows per expert; the expert block must
-// divide max_m, so a larger tile steps down to one that does.
+// Tile choice for the masked layout.  The grids must cover every expert
+// buffer whole (E * max_m / block_m blocks times the N-tiles), however few
+// rows are live, and a workgroup that finds its block dead still costs a
+// dispatch: so the tile kernel with the largest block up to 64 rows that
+// divides max_m, at every expected_m (measured on MI355X, 128 experts,
+// max_m = 256, T = 16: the decode kernel's 16-row blocks made the layer
+// several times slower than its live work).  expected_m is kept for the
+// interface (the tile choice does not depend on it).
 static MoeCfg select_masked(const hum_weight_desc* w13, int64_t max_m, int64_t expected_m) {
-  MoeCfg mc = select_moe(w13, (expected_m < 1 ? 1 : expected_m) * w13->num_experts, 1);
-  while (max_m % tile_rows(mc.up) && mc.up.wave_m > 1) {
-    const int wm = mc.up.wave_m / 2;
-    mc = MoeCfg{moe_tile_cfg(wm), moe_tile_cfg(wm)};
-  }
-  return mc;
+  (void)w13;
+  (void)expected_m;
+  const int wm = max_m % 64 == 0 ? 4 : (max_m % 32 == 0 ? 2 : 1);
+  return MoeCfg{moe_tile_cfg(wm), moe_tile_cfg(wm)};
 }
 
 size_t hum_moe_masked_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t max_m,
@@ -954,7 +960,7 @@ hum_status hum_moe_gemm_masked(const hum_weight_desc* w13, const void* packed_w1
   st = launch_masked_align(expert_num_tokens, w13->num_experts, max_m, bm, reinterpret_cast<int32_t*>(ws + w.sorted),
                            reinterpret_cast<int32_t*>(ws + w.bexp), stream);
   if (st != HUM_OK) return st;
-  const MoeRows r{rows, 1, (int32_t)rows, (int32_t)(max_m < 16 ? max_m : 16)};
+  const MoeRows r{rows, 1, (int32_t)rows, (int32_t)(max_m < 16 ? max_m : 16), expert_num_tokens, max_m};
   return moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, r, x_bf16, out_bf16, stream);
 }
 

@@ -85,10 +85,12 @@ hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void*
                           float* out, void* stream);
 hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t ldx,
                                   void* q, float* s, void* stream);
+// counts / max_m (optional): quantize only the live rows of a grouped_masked
+// buffer (row r is live when r % max_m < counts[r / max_m]).
 hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
-                              uint8_t* s, void* stream);
+                              uint8_t* s, void* stream, const int32_t* counts = nullptr, int64_t max_m = 0);
 hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
-                              uint8_t* s, void* stream);
+                              uint8_t* s, void* stream, const int32_t* counts = nullptr, int64_t max_m = 0);
 hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
                                   void* stream);
 hum_status launch_zero(void* p, size_t bytes, void* stream);
