@@ -172,6 +172,9 @@ def decode_scale(scales, dtype: str):
         return decode_f32(scales)
     if dtype == "e8m0":
         return decode_e8m0(scales)
+    if dtype == "e4m3":
+        # NVFP4's group scales are E4M3 codes
+        return decode_e4m3(scales)
     raise ValueError(f"unknown scale dtype {dtype}")
 
 

@@ -36,7 +36,7 @@ class WeightDesc:
     weight_dtype: str          # "int4" | "uint4" | "int8" | "e2m1" | "e4m3"
     scale_gran: str            # "tensor" | "channel" | "group"
     group_size: int            # along K (ignored unless scale_gran == "group")
-    scale_dtype: str           # "bf16" | "f32" | "e8m0"
+    scale_dtype: str           # "bf16" | "f32" | "e8m0" | "e4m3" (NVFP4: E2M1 codes, G = 16)
     has_zero: bool
     has_global: bool
     num_experts: int

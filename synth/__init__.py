@@ -109,11 +109,13 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
                   scale_dtype: str, num_experts: int, n: int, k: int,
                   zero: bool = False, global_scale: bool = False,
                   scale_lo: float = 0.005, scale_hi: float = 0.02,
-                  e8m0_lo: int = 119, e8m0_hi: int = 123):
+                  e8m0_lo: int = 119, e8m0_hi: int = 123,
+                  e4m3_lo: int = 0x18, e4m3_hi: int = 0x38):
     """Random canonical weights of any supported description: codes uniform
     over the format's codes (E4M3 without its NaN codes; INT8 one byte per
     code, all 256), scales uniform in
     [scale_lo, scale_hi] (bf16 / f32) or E8M0 codes in [e8m0_lo, e8m0_hi],
+    E4M3 scale codes (NVFP4) uniform in [e4m3_lo, e4m3_hi] (positive, finite),
     zero points uniform in [0, 15], global scales uniform in [0.5, 2]."""
     g = rng(seed)
     e = num_experts
@@ -136,6 +138,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
         scales = _uniform_bf16(g, scale_lo, scale_hi, (e, sn, sg))
     elif scale_dtype == "f32":
         scales = g.uniform(scale_lo, scale_hi, size=(e, sn, sg)).astype(np.float32)
+    elif scale_dtype == "e4m3":
+        scales = g.integers(e4m3_lo, e4m3_hi + 1, size=(e, sn, sg), dtype=np.uint8)
     else:
         scales = g.integers(e8m0_lo, e8m0_hi + 1, size=(e, sn, sg), dtype=np.uint8)
     zeros = g.integers(0, 16, size=(e, sn, sg), dtype=np.uint8) if zero else None

@@ -43,6 +43,8 @@ def s_scale(v, dtype):
         return Fraction(s_bf16(v))
     if dtype == "f32":
         return Fraction(float(np.float32(v)))
+    if dtype == "e4m3":
+        return Fraction(s_e4m3(int(v)))
     return Fraction(2) ** (int(v) - 127)
 
 
@@ -86,6 +88,7 @@ CASES = [
     ("e4m3", "channel", 0, "f32", False, False),
     ("e4m3", "block", 16, "f32", False, False),
     ("int8", "channel", 0, "f32", False, False),
+    ("e2m1", "group", 16, "e4m3", False, True),
     ("int8", "tensor", 0, "f32", False, True),
 ]
 
@@ -111,6 +114,8 @@ def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
         sc = bf16_bits(g.uniform(0.005, 0.02, size=(sn, ng)).astype(np.float32))
     elif sd == "f32":
         sc = g.uniform(0.01, 0.1, size=(sn, ng)).astype(np.float32)
+    elif sd == "e4m3":
+        sc = g.integers(0x08, 0x7F, size=(sn, ng)).astype(np.uint8)   # positive finite, subnormals included
     else:
         sc = g.integers(119, 124, size=(sn, ng)).astype(np.uint8)
     zeros = g.integers(0, 16, size=(sn, ng)).astype(np.uint8) if zp else None
@@ -222,3 +227,18 @@ def test_int8_per_channel_equals_integer_matmul():
     got = G.linear(desc, x.astype(np.float64), cu[None], sc[None])
     ref = (x @ q.T).astype(np.float64) * sc[:, 0].astype(np.float64)[None, :]
     assert np.array_equal(got, ref)
+
+
+def test_nvfp4_group_scales_per_16():
+    """NVFP4: each 16-element group of a row takes its own E4M3 scale; a
+    single nonzero code in group g picks up exactly scale g (times the
+    global scale)."""
+    n, k = 2, 64
+    desc = G.WeightDesc("e2m1", "group", 16, "e4m3", False, True, 1, n, k)
+    cu = np.zeros((n, k), np.uint8)
+    cu[0, 17] = 0x2   # +1.0 in group 1
+    cu[1, 63] = 0xF   # -6.0 in group 3
+    sc = np.array([[0x38, 0x30, 0x40, 0x48], [0x38, 0x39, 0x3A, 0x3C]], np.uint8)   # 1, .5, 2, 4 / 1, 1.125, 1.25, 1.5
+    w = G.dequant_weight(desc, pack_nibbles(cu)[None], sc[None], global_scale=np.array([0.5], np.float32))[0]
+    assert w[0, 17] == 0.5 * 0.5 and np.count_nonzero(w[0]) == 1
+    assert w[1, 63] == -6.0 * 1.5 * 0.5 and np.count_nonzero(w[1]) == 1
