@@ -145,6 +145,40 @@ def dense_w4a16_sweep(hum, timer, iters):
             "step": step, "flops_step": flops_step, "wbytes": wbytes, "case": case}
 
 
+def dense_w4a16_fp4(hum, timer, iters, scale):
+    """FP4 weights x bf16 at N = K = 8192, the W4A16 sweep's shape: MXFP4
+    (E8M0 per 32) or NVFP4 (E4M3 per 16 + an f32 tensor scale)."""
+    import synth
+    import torch
+    n = k = 8192
+    if scale == "e8m0":
+        w = synth.quant_weights(synth.seed_for(11), "e2m1", "group", 32, "e8m0", 1, n, k)
+        desc = hum.make_desc("e2m1", "group", 32, "e8m0", n, k)
+        packed = hum.prepare_weight(desc, _dev(w["codes"]), _dev(w["scales"]))
+        wbytes = n * k // 2 + n * (k // 32)
+    else:
+        w = synth.quant_weights(synth.seed_for(11, 1), "e2m1", "group", 16, "e4m3", 1, n, k, global_scale=True)
+        desc = hum.make_desc("e2m1", "group", 16, "e4m3", n, k, has_global=True)
+        packed = hum.prepare_weight(desc, _dev(w["codes"]), _dev(w["scales"]), None, _dev(w["global_scale"]))
+        wbytes = n * k // 2 + n * (k // 16)
+    copies = rotate_copies(packed)
+    g = synth.rng(synth.seed_for(11, 2))
+    out = []
+    for m in synth.DENSE_SWEEP_M:
+        x = _dev(synth.bf16_normal(g, (m, k)))
+        o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        ws = hum.Workspace("cuda").get(hum.linear_workspace_bytes(desc, m))
+        fn = lambda i: hum.linear(desc, copies[i % len(copies)], x, out=o, workspace=ws)
+        timer.run(fn, 3)
+        t = timer.run(fn, iters)
+        flops = 2.0 * m * n * k
+        bound = "hbm" if m <= 64 else "mfma"
+        out.append({"m": m, "us": t * 1e6, "tflops": flops / t / 1e12, "weight_gbs": wbytes / t / 1e9,
+                    "bound": bound, "frac": (wbytes / t / HBM_PEAK) if bound == "hbm" else flops / t / BF16_PEAK,
+                    "tile": list(hum.select_config(desc, m).as_tuple())})
+    return out
+
+
 def dense_tiny(hum, timer, iters):
     import synth
     case = synth.dense_w4a16(synth.seed_for(1), 16, 512, 1024, group=128)
@@ -450,6 +484,8 @@ def main():
         sweep["dense_w8a8_fp8_block128_n7168_k2048"] = dense_w8a8_block(hum, timer, iters)
         sweep["dense_w8a16_fp8_n7168_k2048"] = dense_w8a16(hum, timer, iters, "e4m3")
         sweep["dense_w8a16_int8_n7168_k2048"] = dense_w8a16(hum, timer, iters, "int8")
+        sweep["dense_w4a16_mxfp4_n8192_k8192"] = dense_w4a16_fp4(hum, timer, iters, "e8m0")
+        sweep["dense_w4a16_nvfp4_n8192_k8192"] = dense_w4a16_fp4(hum, timer, iters, "e4m3")
         sweep["dense_w4a4_mxfp4_n7168_k2048"] = dense_w4a4(hum, timer, iters)
         del d["copies"]
         torch.cuda.empty_cache()

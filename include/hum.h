@@ -49,7 +49,9 @@ typedef enum hum_dtype {
   HUM_INT4 = 2,   /* signed two's-complement nibble, -8..7 */
   HUM_UINT4 = 3,  /* unsigned nibble 0..15, optional zero point */
   HUM_E2M1 = 4,   /* FP4 (MXFP4 element) */
-  HUM_E4M3 = 5,   /* FP8 E4M3 "FN": max 448, NaN = 0x7F/0xFF, no Inf */
+  HUM_E4M3 = 5,   /* FP8 E4M3 "FN": max 448, NaN = 0x7F/0xFF, no Inf; as a
+                     scale dtype: NVFP4's group scale (E2M1 weights, G = 16,
+                     finite codes) */
   HUM_E8M0 = 6,   /* power-of-two scale 2^(c-127) */
   HUM_INT8 = 7    /* signed two's-complement byte, -128..127 (W8A16: bf16
                      activations, per-channel or per-tensor f32 scales) */

@@ -154,7 +154,7 @@ def _gpu(t, name):
 
 _DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3, "int8": INT8}
 _GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP, "block": SCALE_BLOCK}
-_SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0}
+_SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0, "e4m3": E4M3}
 _AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4,
        "fp8_group": ACT_FP8_GROUP}
 

@@ -59,6 +59,14 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->has_zero_point && d->weight_dtype != HUM_UINT4) return set_error(HUM_ERR_UNSUPPORTED, "zero points need UINT4 codes");
       return HUM_OK;
     case HUM_E2M1:
+      if (d->scale_dtype == HUM_E4M3) {
+        // NVFP4: an E4M3 scale per 16 along K (+ the f32 tensor scale)
+        if (d->scale_gran != HUM_SCALE_GROUP || d->group_size != 16)
+          return set_error(HUM_ERR_UNSUPPORTED, "E2M1 weights with E4M3 scales take one scale per 16 along K (NVFP4)");
+        if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E2M1 takes no zero point");
+        if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "NVFP4 weights run with bf16 activations");
+        return HUM_OK;
+      }
       if (d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32 || d->scale_dtype != HUM_E8M0)
         return set_error(HUM_ERR_UNSUPPORTED, "E2M1 weights need E8M0 scales per 32 along K (MXFP4)");
       if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "E2M1 takes no zero point");
@@ -89,6 +97,7 @@ int fmt_of(const hum_weight_desc* d) {
   if (d->weight_dtype == HUM_INT8) return F_INT8_BF16;
   if (d->weight_dtype == HUM_E4M3)
     return d->scale_gran == HUM_SCALE_BLOCK ? F_FP8_BLOCK : (d->act_fmt == HUM_ACT_BF16 ? F_FP8_BF16 : F_FP8);
+  if (d->scale_dtype == HUM_E4M3) return F_NVFP4_BF16;
   if (d->act_fmt == HUM_ACT_MXFP8) return F_MXFP4_MXFP8;
   return d->act_fmt == HUM_ACT_MXFP4 ? F_MXFP4_MXFP4 : F_MXFP4_BF16;
 }
@@ -120,6 +129,12 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
     // 128-row block)
     L->ng = L->kb;
     L->scales_per_expert = align256(L->nt * L->kb * 4);
+  } else if (f == F_NVFP4_BF16) {
+    // a dword per lane and pair of K-blocks: the lane's two E4M3 group
+    // scales (16 along K each) of either K-block
+    L->ng = L->kb * 8;
+    L->kb4 = cdiv(L->kb, 2);
+    L->scales_per_expert = L->nt * L->kb4 * 64 * 4;
   } else {
     L->ng = L->kb * 4;
     L->scales_per_expert = L->nt * L->kb4 * 64 * 4;
@@ -179,7 +194,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
-  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK) {
+  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK && fmt_of(d) != F_NVFP4_BF16) {
     // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
     // wave: the fewest that keep the activation bytes each workgroup reads
     // (from L2) at or below its weight bytes.  Four K-waves when their K
@@ -703,7 +718,8 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   st = check_desc(w2);
   if (st != HUM_OK) return st;
   if (w13->num_experts != w2->num_experts) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 expert counts differ");
-  if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1)
+  if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1 || w13->scale_dtype != HUM_E8M0 ||
+      w2->scale_dtype != HUM_E8M0)
     return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs MXFP4 (E2M1 + E8M0) expert weights");
   if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
   if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");

@@ -41,6 +41,9 @@
 //                  scales in the epilogue.
 //   F_INT8_BF16    INT8 weights x bf16 activations (W8A16): bytes widened
 //                  through f32 (exact), the FP8 path's layout and epilogue.
+//   F_NVFP4_BF16   NVFP4: E2M1 -> f32, times its E4M3 scale per 16 (exact: at
+//                  most 6 significant bits) -> bf16; prefill-tile kernel
+//                  only.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
@@ -144,7 +147,7 @@ __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs&
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
     const int64_t zb = (int64_t)p.ng * 8;
     s.zero = make_rsrc(w.zero + ntc * zb, (valid && p.has_zero) ? zb : 0);
-  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
+  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
     const int64_t sb = (int64_t)p.kb4 * 256;
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
   }
@@ -246,11 +249,37 @@ __device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
+// A finite E4M3 code (OCP FP8: bias 7, subnormal quantum 2^-9) as f32.
+__device__ __forceinline__ float e4m3_scale_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
 // Byte i of w as a signed integer, in f32.
 __device__ __forceinline__ float i8_to_f32(uint32_t w, int i) { return (float)(int)(int8_t)(w >> (8 * i)); }
 // bf16 bits of lo in the low half, of hi in the high half, by truncation.
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Eight E2M1 codes (low nibble first) times an E4M3 group scale -> bf16.
+// The hardware's scaled FP4 conversion applies only a power-of-two scale, so
+// the codes are widened to f32 unscaled and multiplied by the full scale:
+// exact (at most 6 significant bits), hence also exact when packed to bf16
+// by taking each f32's upper half.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8_t nv_dequant(uint32_t w, float scale) {
+  const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  u32x4_t o;
+  o[0] = pack_hi16(r0[0] * scale, r0[1] * scale);
+  o[1] = pack_hi16(r1[0] * scale, r1[1] * scale);
+  o[2] = pack_hi16(r2[0] * scale, r2[1] * scale);
+  o[3] = pack_hi16(r3[0] * scale, r3[1] * scale);
+  return __builtin_bit_cast(bf16x8_t, o);
 }
 
 // bf16 B operand of the 4 k-steps of a K-block.
@@ -273,6 +302,15 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
+  } else if (FMT == F_NVFP4_BF16) {
+    // k-steps 2h and 2h + 1 (k = 32 lg + 16 h + [0, 16)) share the E4M3
+    // scale in byte 2 (kb & 1) + h of the lane's word
+    const uint32_t half = meta >> (16 * (kb & 1));
+    const float f0 = e4m3_scale_to_f32(half & 0xFF), f1 = e4m3_scale_to_f32((half >> 8) & 0xFF);
+    d[0] = nv_dequant(f.w[0][0], f0);
+    d[1] = nv_dequant(f.w[0][1], f0);
+    d[2] = nv_dequant(f.w[0][2], f1);
+    d[3] = nv_dequant(f.w[0][3], f1);
   } else if (FMT == F_INT8_BF16) {
     // INT8 -> bf16 is exact (|q| <= 128): each byte sign-extended to f32,
     // and two f32 packed by their upper halves (whose lower halves are zero
@@ -938,7 +976,8 @@ struct TileCfg {
   static constexpr bool kTracked = (kS == 3);
   static constexpr int kMI = (FMT == F_INT || FMT == F_FP8_BLOCK)
                                  ? 1
-                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) ? WN : 0);
+                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+                                     FMT == F_NVFP4_BF16) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
@@ -1114,7 +1153,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
     mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
     mi_gmul = 16u * (2u << sf);
-  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
+  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+                       FMT == F_NVFP4_BF16) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
   } else if constexpr (FMT == F_FP8_BLOCK) {
@@ -1176,10 +1216,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_FP8_BLOCK) {
       dma4(rms, rmsr, mw, mi_off + (uint32_t)kb * 4u);
-    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4) {
+    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+                         FMT == F_NVFP4_BF16) {
+      // a metadata row covers 4 K-blocks (E8M0 per 32) or 2 (NVFP4: two
+      // E4M3 per 32 of a lane)
+      constexpr int kRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
-        dma4(rms, rmsr, mw + ns * 256, ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> 2)) * 64 + lane) * 4);
+        dma4(rms, rmsr, mw + ns * 256,
+             ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> kRowShift)) * 64 + lane) * 4);
       }
     }
     // keep the issue ahead of the compute (the waits count on it)
@@ -1231,7 +1276,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
                                : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
       mw[ns] = 0;
-      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4)
+      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
     }
     if constexpr (FMT == F_FP8_BLOCK) {
@@ -1675,6 +1720,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_TILE_SET(F_FP8_BLOCK),
     HUM_DENSE_SET(F_FP8_BF16),
     HUM_DENSE_SET(F_INT8_BF16),
+    HUM_DENSE_TILE_SET(F_NVFP4_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1700,6 +1746,7 @@ static const ReduceInstance kReduces[] = {
     {F_FP8_BLOCK, EPI_BF16, splitk_reduce_kernel<F_FP8_BLOCK, EPI_BF16>},
     {F_FP8_BF16, EPI_BF16, splitk_reduce_kernel<F_FP8_BF16, EPI_BF16>},
     {F_INT8_BF16, EPI_BF16, splitk_reduce_kernel<F_INT8_BF16, EPI_BF16>},
+    {F_NVFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_NVFP4_BF16, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

@@ -57,12 +57,12 @@ struct Layout {
 
 enum Fmt : int {
   F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6,
-  F_INT8_BF16 = 7
+  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8
 };
 
 // Formats whose activations stay bf16 (bf16 MFMA on widened weights).
 constexpr bool fmt_bf16_act(int f) {
-  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16;
+  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16;
 }
 // 8-bit weight codes laid out for the bf16 MFMA: a lane's 32 codes of a
 // K-block contiguous (k = 32 * (lane / 16) + j), per-channel f32 scales.

@@ -191,6 +191,34 @@ __global__ void repack_mx_meta_kernel(RepackArgs a) {
   *reinterpret_cast<uint32_t*>(a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb4) * 64 + lane) * 4) = word;
 }
 
+// NVFP4 meta: one dword per (e, nt, K-block pair, lane), bytes 2 h + q =
+// the E4M3 scale of group 8 kb + 2 lg + q for K-block kb = 2 kb2 + h (the
+// lane's 32 codes of a K-block span groups 2 lg and 2 lg + 1).  Codes of
+// columns past N are zero, so their scale is too.
+__global__ void repack_nv_meta_kernel(RepackArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)a.num_experts * a.nt * a.kb4 * 64;
+  if (tid >= total) return;
+  const int lane = (int)(tid & 63);
+  int64_t rest = tid >> 6;
+  const int64_t kb2 = rest % a.kb4;
+  rest /= a.kb4;
+  const int64_t nt = rest % a.nt;
+  const int64_t e = rest / a.nt;
+  const int c = lane & 15, lg = lane >> 4;
+  const int64_t n = nt * kNSub + c;
+  uint32_t word = 0;
+  for (int h = 0; h < 2; ++h) {
+    const int64_t kb = 2 * kb2 + h;
+    if (kb >= a.kb || n >= a.n) continue;
+    for (int q = 0; q < 2; ++q) {
+      const int64_t g = kb * 8 + 2 * lg + q;
+      word |= (uint32_t)a.scales[(e * a.src_n + n) * a.src_ng + g] << (8 * (2 * h + q));
+    }
+  }
+  *reinterpret_cast<uint32_t*>(a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb2) * 64 + lane) * 4) = word;
+}
+
 // FP8 per-channel meta: f32 [NT*16] per expert.
 __global__ void repack_fp8_meta_kernel(RepackArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -273,6 +301,8 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   if (f == F_INT) {
     repack_int_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.ng, B), B, 0, s>>>(a);
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
+  } else if (f == F_NVFP4_BF16) {
+    repack_nv_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else if (f == F_FP8_BLOCK) {
@@ -298,6 +328,7 @@ struct DequantArgs {
   int num_experts, wdt, scale_f32, has_zero;
   int block;     // E4M3 with 2-D block scales
   int bf16_order;  // 8-bit codes in the bf16 MFMA order
+  int nvfp4;       // E2M1 with E4M3 scales per 16
 };
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -341,6 +372,16 @@ __global__ void dequant_kernel(DequantArgs a) {
     return;
   }
   const u32x4_t w = *reinterpret_cast<const u32x4_t*>(base + ((nt * a.kb + kb) * 64 + lane) * 16);
+  if (a.wdt == HUM_E2M1 && a.nvfp4) {
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(
+        a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb / 2) * 64 + lane) * 4);
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t code = (w[j / 8] >> (4 * (j % 8))) & 0xF;
+      const float s = e4m3_value((word >> (8 * (2 * (kb % 2) + j / 16))) & 0xFF);
+      orow[32 * lg + j] = e2m1_value(code) * s;
+    }
+    return;
+  }
   if (a.wdt == HUM_E2M1) {
     const uint32_t word = *reinterpret_cast<const uint32_t*>(
         a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb / 4) * 64 + lane) * 4);
@@ -393,6 +434,7 @@ hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void*
   a.has_zero = d->has_zero_point;
   a.block = d->scale_gran == HUM_SCALE_BLOCK;
   a.bf16_order = fmt_w8_bf16(fmt_of(d));
+  a.nvfp4 = fmt_of(d) == F_NVFP4_BF16;
   const int64_t total = (int64_t)d->num_experts * L.nt * L.kb * 64;
   dequant_kernel<<<grid_for(total, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(a);
   hipError_t err = hipGetLastError();

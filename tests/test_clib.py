@@ -47,6 +47,8 @@ def test_packed_size_ragged_n_pads_to_16(lib):
     dict(weight_dtype="e4m3", scale_gran="channel", group_size=0, scale_dtype="f32", act_fmt="mxfp8"),
     dict(weight_dtype="e4m3", scale_gran="group", group_size=128, scale_dtype="f32", act_fmt="fp8_token"),
     dict(weight_dtype="int8", scale_gran="group", group_size=128, scale_dtype="f32"),
+    dict(weight_dtype="e2m1", scale_gran="group", group_size=32, scale_dtype="e4m3"),
+    dict(weight_dtype="e2m1", scale_gran="group", group_size=16, scale_dtype="e4m3", act_fmt="mxfp8"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="bf16"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="f32", act_fmt="fp8_token"),
 ])
@@ -128,6 +130,13 @@ def test_autotune_argument_errors(lib):
     assert b"flags" in lib.hum_last_error()
     assert f(ctypes.byref(d), p, 0, p, None, None, p, None, 0, 10, 0, ctypes.byref(best), None, None) == 1
     assert f(ctypes.byref(d), p, 4, p, None, None, p, None, 0, 10, 0, None, None, None) == 1
+
+
+def test_moe_rejects_nvfp4_experts(lib):
+    w13 = hum.make_desc("e2m1", "group", 16, "e4m3", 512, 256, num_experts=4)
+    w2 = hum.make_desc("e2m1", "group", 16, "e4m3", 256, 256, num_experts=4)
+    assert lib.hum_moe_workspace_bytes(ctypes.byref(w13), ctypes.byref(w2), 8, 2) == 0
+    assert b"MXFP4" in lib.hum_last_error()
 
 
 def test_moe_batch_invariant_selection(lib):

@@ -25,6 +25,7 @@ FORMATS = {
     "int8_bf16": ("int8", "channel", 0, "f32", False, "bf16"),
     "e4m3_block128": ("e4m3", "block", 128, "f32", False, "fp8_group"),
     "mxfp4_bf16": ("e2m1", "group", 32, "e8m0", False, "bf16"),
+    "nvfp4_bf16": ("e2m1", "group", 16, "e4m3", False, "bf16"),
     "mxfp4_mxfp8": ("e2m1", "group", 32, "e8m0", False, "mxfp8"),
     "mxfp4_mxfp4": ("e2m1", "group", 32, "e8m0", False, "mxfp4"),
 }

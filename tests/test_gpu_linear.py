@@ -290,6 +290,47 @@ def test_int8_weights_random_vs_oracle(m, gran):
     assert_tol(out, ref, f"w8a16 int8 m={m} {gran}")
 
 
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_nvfp4_exact_every_tile(tile):
+    """NVFP4 x bf16: every E2M1 code, power-of-two E4M3 group scales (one per
+    16 along K), a power-of-two tensor scale and integer activations in
+    [-8, 8]: all sums exact in fp32, so bitwise equal to the oracle.  NVFP4
+    has no decode-kernel instances."""
+    m, n, k = rows_for(tile, 23), 272, 1024
+    g = synth.rng(43)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    w = synth.quant_weights(43, "e2m1", "group", 16, "e4m3", 1, n, k, global_scale=True)
+    w["scales"] = (g.integers(5, 10, size=w["scales"].shape) << 3).astype(np.uint8)   # 2^-2 .. 2^2
+    w["global_scale"] = np.array([0.5], np.float32)
+    hd, od = descs("e2m1", "group", 16, "e4m3", 1, n, k, glob=True)
+    packed = prepare(hd, w, "e4m3")
+    print(f"case nvfp4 exact tile={tile}", flush=True)
+    if tile[0] == 1:
+        with pytest.raises(hum.HumError, match="tile config not available"):
+            hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+        return
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], None, w["global_scale"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
+def test_nvfp4_random_vs_oracle(m):
+    """NVFP4 x bf16 at the selector's config: random E4M3 group scales
+    (subnormal to 1) and a tensor scale."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_for(10, m), "e2m1", "group", 16, "e4m3", 1, n, k, global_scale=True,
+                            e4m3_lo=0x04, e4m3_hi=0x38)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(10, 100 + m)), (m, k))
+    hd, od = descs("e2m1", "group", 16, "e4m3", 1, n, k, glob=True)
+    packed = prepare(hd, w, "e4m3")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], None, w["global_scale"])
+    assert_tol(out, ref, f"nvfp4 m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -431,7 +472,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "int8", "e2m1_mxfp8", "e2m1_mxfp4"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "int8", "nvfp4", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -443,6 +484,10 @@ def test_empty_m_is_a_no_op(fmt):
         w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
         hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
         packed = prepare(hd, w, "f32")
+    elif fmt == "nvfp4":
+        w = synth.quant_weights(synth.seed_for(3, 55), "e2m1", "group", 16, "e4m3", 1, n, k)
+        hd, _ = descs("e2m1", "group", 16, "e4m3", 1, n, k)
+        packed = prepare(hd, w, "e4m3")
     elif fmt == "int8":
         w = synth.quant_weights(synth.seed_for(3, 54), "int8", "channel", 0, "f32", 1, n, k)
         hd, _ = descs("int8", "channel", 0, "f32", 1, n, k)

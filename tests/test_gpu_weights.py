@@ -82,6 +82,22 @@ def test_dequant_bit_exact_int8(shape, gran):
     assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dequant_bit_exact_nvfp4(shape):
+    """NVFP4: E2M1 x its E4M3 group scale (16 along K), every scale code
+    from subnormal to 448 (exact in f32)."""
+    e, n, k = shape
+    hd, od = descs("e2m1", "group", 16, "e4m3", e, n, k)
+    w = synth.quant_weights(hash(("nvfp4", shape)) & 0xFFFF, "e2m1", "group", 16, "e4m3", e, n, k,
+                            e4m3_lo=0x01, e4m3_hi=0x7E)
+    packed = prepare(hd, w, "e4m3")
+    got = hum.dequant_weight(hd, packed)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.dequant_weight(od, w["codes"], w["scales"], include_global=False).astype(np.float32)
+    g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def test_group_k_equals_channel_bitwise():
     e, n, k = 1, 96, 512
     w = synth.quant_weights(5, "uint4", "group", k, "bf16", e, n, k, zero=True)
