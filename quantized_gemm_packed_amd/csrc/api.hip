@@ -194,7 +194,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
-  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK && fmt_of(d) != F_NVFP4_BF16) {
+  if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK) {
     // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
     // wave: the fewest that keep the activation bytes each workgroup reads
     // (from L2) at or below its weight bytes.  Four K-waves when their K

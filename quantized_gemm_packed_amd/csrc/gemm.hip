@@ -42,8 +42,7 @@
 //   F_INT8_BF16    INT8 weights x bf16 activations (W8A16): bytes widened
 //                  through f32 (exact), the FP8 path's layout and epilogue.
 //   F_NVFP4_BF16   NVFP4: E2M1 -> f32, times its E4M3 scale per 16 (exact: at
-//                  most 6 significant bits) -> bf16; prefill-tile kernel
-//                  only.
+//                  most 6 significant bits) -> bf16.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
@@ -69,6 +68,9 @@ struct Tr {
   static constexpr int kBWords =
       (FMT == F_FP8 || FMT == F_FP8_BLOCK || fmt_w8_bf16(FMT)) ? 2 : 1;  // 16-B words / lane / K-block
   static constexpr bool kBf16 = fmt_bf16_act(FMT);
+  // MX / NVFP4 weight scales: a metadata row (a dword per lane) covers
+  // 1 << kMetaRowShift K-blocks (E8M0 per 32: 4; NVFP4's two E4M3 per 32: 2)
+  static constexpr int kMetaRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
   // bytes of an activation row of `ld` elements
   static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
 };
@@ -178,8 +180,8 @@ __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe&
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
     const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
     f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
-  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8)) {
-    const uint32_t mo = ok ? (uint32_t)((kb >> 2) * 64 + lane) * 4 : kOob;
+  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16)) {
+    const uint32_t mo = ok ? (uint32_t)((kb >> Tr<FMT>::kMetaRowShift) * 64 + lane) * 4 : kOob;
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
   }
   return f;
@@ -586,7 +588,8 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   // first scale group / first 4-K-block E8M0 row of the K range (the LDS
   // metadata starts there)
   const int g0 = (FMT == F_INT) ? kb_begin / p.kb_per_group : 0;
-  const int r0 = kb_begin >> 2;
+  constexpr int kRS = T::kMetaRowShift;
+  const int r0 = kb_begin >> kRS;
   auto stage = [&]() {
     // source row of tile row `lane` (lanes 0..15; -1: padding / past the end)
     int src = -1;
@@ -678,8 +681,8 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
           }
         }
       }
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) && nkb > 0) {
-      const int n16 = (((kb_end + 3) >> 2) - r0) * 16;  // 16-byte slots of E8M0 rows
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nkb > 0) {
+      const int n16 = (((kb_end + (1 << kRS) - 1) >> kRS) - r0) * 16;  // 16-byte slots of scale rows
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
         if (!ntv[ns]) continue;
@@ -736,7 +739,8 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     }
     // weight metadata of the wave's K-blocks (INT: scales and zero points of
     // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
-    constexpr int kML = (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) ? 2 : 0);
+    constexpr int kML =
+        (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
     u32x4_t mbuf[WN][kML > 0 ? kML : 1];
     uint32_t zbuf[WN];
     int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
@@ -749,8 +753,8 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       zb0 = g0w * 8;
       zbytes = p.has_zero ? (g1w - g0w) * 8 : 0;  // <= 256 B
       zdst = p.lds_zero_off + (g0w - g0) * 8;
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) && nj > 0) {
-      const int rw0 = kw0 >> 2, rw1 = (kw0 + nj + 3) >> 2;
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nj > 0) {
+      const int rw0 = kw0 >> kRS, rw1 = (kw0 + nj + (1 << kRS) - 1) >> kRS;
       mb0 = rw0 * 256;
       mbytes = (rw1 - rw0) * 256;  // <= 2 KB
       mdst = (rw0 - r0) * 256;
@@ -813,8 +817,8 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
       const uint32_t zr = *reinterpret_cast<const uint32_t*>(mb + p.lds_zero_off + gl * 8 + ((c16 >> 3) << 2));
       z = p.has_zero ? zr : 0u;
-    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8) {
-      m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> 2) - r0) * 64 + lane) * 4);
+    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
+      m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> kRS) - r0) * 64 + lane) * 4);
     }
   };
 
@@ -1720,7 +1724,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_TILE_SET(F_FP8_BLOCK),
     HUM_DENSE_SET(F_FP8_BF16),
     HUM_DENSE_SET(F_INT8_BF16),
-    HUM_DENSE_TILE_SET(F_NVFP4_BF16),
+    HUM_DENSE_SET(F_NVFP4_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),

@@ -200,8 +200,9 @@ constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, i
     const int64_t zr = ((groups * 8 + 255) / 256) * 256;
     L.zero_off = sc;
     L.meta_stride = sc + zr;
-  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8) {
-    int64_t r = kb / 4 + 2;  // 4-K-block rows a range of kb blocks touches
+  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8 || fmt == F_NVFP4_BF16) {
+    // scale rows a range of kb blocks touches (a row: 4 K-blocks, NVFP4 2)
+    int64_t r = (fmt == F_NVFP4_BF16 ? kb / 2 : kb / 4) + 2;
     if (r > kb4) r = kb4;
     L.meta_stride = ((r * 256 + 1023) / 1024) * 1024;
   }
@@ -222,6 +223,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
     return groups * 16 * (scale_f32 ? 4 : 2) <= 1024 && groups * 8 <= 256;
   }
   if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8) return (per / 4 + 2) * 256 <= 2048;
+  if (fmt == F_NVFP4_BF16) return (per / 2 + 2) * 256 <= 2048;
   return true;
 }
 

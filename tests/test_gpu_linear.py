@@ -294,8 +294,8 @@ def test_int8_weights_random_vs_oracle(m, gran):
 def test_nvfp4_exact_every_tile(tile):
     """NVFP4 x bf16: every E2M1 code, power-of-two E4M3 group scales (one per
     16 along K), a power-of-two tensor scale and integer activations in
-    [-8, 8]: all sums exact in fp32, so bitwise equal to the oracle.  NVFP4
-    has no decode-kernel instances."""
+    [-8, 8]: all sums exact in fp32, so bitwise equal to the oracle (decode
+    and tile kernels)."""
     m, n, k = rows_for(tile, 23), 272, 1024
     g = synth.rng(43)
     xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
@@ -305,8 +305,8 @@ def test_nvfp4_exact_every_tile(tile):
     hd, od = descs("e2m1", "group", 16, "e4m3", 1, n, k, glob=True)
     packed = prepare(hd, w, "e4m3")
     print(f"case nvfp4 exact tile={tile}", flush=True)
-    if tile[0] == 1:
-        with pytest.raises(hum.HumError, match="tile config not available"):
+    if not stream_fits(tile, m, k, 2):
+        with pytest.raises(hum.HumError, match="raise split_k"):
             hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
         return
     out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
