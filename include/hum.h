@@ -269,6 +269,21 @@ hum_status hum_moe_select_config(const hum_weight_desc* w13, const hum_weight_de
                                  int64_t num_tokens, int32_t topk, uint32_t flags,
                                  hum_tile_config* cfg_out);
 
+/* On-device autotune of the MoE layer, as hum_autotune_linear does for dense
+ * ones: every compiled configuration (both GEMMs share it, no split-K; with
+ * HUM_SELECT_BATCH_INVARIANT tile kernels only) whose workspace fits
+ * `ws_bytes` is run once untimed and `iters` times between HIP events on the
+ * caller's buffers; the fastest is returned with its mean µs per layer call,
+ * and `out_bf16` ends holding its result.  The arguments are those of
+ * hum_moe_gemm_ex.  Blocks the host; not for graph capture. */
+hum_status hum_autotune_moe(const hum_weight_desc* w13, const void* packed_w13,
+                            const hum_weight_desc* w2, const void* packed_w2,
+                            int64_t num_tokens, int32_t topk, const void* x_bf16,
+                            const int32_t* topk_ids, const float* topk_weights,
+                            void* out_bf16, void* workspace, size_t ws_bytes, int32_t iters,
+                            uint32_t flags, hum_tile_config* best_out, float* best_us_out,
+                            void* stream);
+
 /* Workspace bytes hum_moe_gemm_ex needs with configuration `cfg`. */
 size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_desc* w2,
                                   int64_t num_tokens, int32_t topk,

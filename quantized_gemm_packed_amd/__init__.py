@@ -81,6 +81,8 @@ _SIGS = {
     "hum_last_error": (ctypes.c_char_p, []),
     "hum_packed_weight_bytes": (_SZ, [_DP]),
     "hum_select_config_ex": (_I32, [_DP, _I64, ctypes.c_uint32, _CP]),
+    "hum_autotune_moe": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _I32, ctypes.c_uint32, _CP,
+                                ctypes.POINTER(ctypes.c_float), _P]),
     "hum_moe_gemm_masked": (_I32, [_DP, _P, _DP, _P, _I64, _I64, _P, _P, _P, _P, _SZ, _CP, _P]),
     "hum_moe_masked_workspace_bytes": (_SZ, [_DP, _DP, _I64, _I64, _CP]),
     "hum_autotune_linear": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _I32, ctypes.c_uint32, _CP,
@@ -358,6 +360,33 @@ def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids
                                           _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg),
                                           _stream(x.device)))
     return out
+
+
+def autotune_moe(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids, topk_weights, out=None,
+                 workspace=None, iters: int = 5, batch_invariant: bool = False):
+    """Time every compiled MoE configuration on these buffers (on the device)
+    -> (fastest TileConfig, its µs per layer call).  `out`, if given, ends
+    holding the winner's result.  The workspace defaults to what the largest
+    expert block (128 rows) needs."""
+    import torch
+    for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"), (topk_ids, "topk_ids"),
+                  (topk_weights, "topk_weights")):
+        _gpu(t, nm)
+    t_count, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((t_count, w13.k), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        big = TileConfig()
+        big.kind, big.wave_m, big.wave_n, big.waves_n, big.waves_k, big.split_k, big.block_m = 0, 8, 4, 4, 1, 1, 128
+        workspace = _workspace(x.device).get(moe_workspace_bytes(w13, w2, t_count, topk, big))
+    best = TileConfig()
+    us = ctypes.c_float()
+    _check(load_library().hum_autotune_moe(ctypes.byref(w13), _ptr(packed_w13), ctypes.byref(w2), _ptr(packed_w2),
+                                           t_count, topk, _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(out),
+                                           _ptr(workspace), workspace.numel(), int(iters),
+                                           SELECT_BATCH_INVARIANT if batch_invariant else 0, ctypes.byref(best),
+                                           ctypes.byref(us), _stream(x.device)))
+    return best, us.value
 
 
 def moe_masked_workspace_bytes(w13: WeightDesc, w2: WeightDesc, max_m: int, expected_m: int,

@@ -916,6 +916,92 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
 }
 
+// ---- on-device autotune of the MoE layer ---------------------------------------
+
+static void moe_candidates(const hum_weight_desc* w13, uint32_t flags, std::vector<hum_tile_config>& out) {
+  const bool inv = (flags & HUM_SELECT_BATCH_INVARIANT) != 0;
+  for (int kind = HUM_KERNEL_TILE; kind <= HUM_KERNEL_STREAM; ++kind) {
+    if (inv && kind == HUM_KERNEL_STREAM) continue;
+    for (int wm = 1; wm <= (kind == HUM_KERNEL_TILE ? 8 : 1); wm *= 2)
+      for (int wn = 1; wn <= 8; wn *= 2)
+        for (int wk = 1; wk <= (kind == HUM_KERNEL_TILE ? 1 : 15); ++wk)
+          for (int st = 0; st <= (kind == HUM_KERNEL_TILE ? 3 : 0); st += 3) {
+            hum_tile_config c{};
+            c.kind = kind;
+            c.wave_m = wm;
+            c.wave_n = wn;
+            c.waves_n = kind == HUM_KERNEL_TILE ? 4 : 1;
+            c.waves_k = wk;
+            c.split_k = 1;
+            c.stages = st;
+            c.block_m = (int32_t)tile_rows(c);
+            KernelKey kup, kdn;
+            if (cfg_sane(c) && moe_keys(w13, MoeCfg{c, c}, &kup, &kdn) == HUM_OK) out.push_back(c);
+          }
+  }
+  clear_error();
+}
+
+hum_status hum_autotune_moe(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
+                            const void* packed_w2, int64_t t, int32_t topk, const void* x_bf16,
+                            const int32_t* topk_ids, const float* topk_weights, void* out_bf16, void* workspace,
+                            size_t ws_bytes, int32_t iters, uint32_t flags, hum_tile_config* best_out,
+                            float* best_us_out, void* stream) {
+  clear_error();
+  hum_status st = check_moe(w13, w2, t, topk);
+  if (st != HUM_OK) return st;
+  if (t < 1 || iters < 1 || iters > 10000 || !best_out) return set_error(HUM_ERR_INVALID_ARG, "bad t / iters / best_out");
+  if (flags & ~(uint32_t)HUM_SELECT_BATCH_INVARIANT) return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
+  if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
+    return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  std::vector<hum_tile_config> cands;
+  moe_candidates(w13, flags, cands);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return set_error(HUM_ERR_HIP, "hipEventCreate failed");
+  }
+  float best_us = 0.0f;
+  hum_tile_config best{};
+  bool found = false;
+  for (const hum_tile_config& c : cands) {
+    if (moe_ws(w13, w2, t, topk, MoeCfg{c, c}).total > (int64_t)ws_bytes) continue;
+    st = hum_moe_gemm_ex(w13, packed_w13, w2, packed_w2, t, topk, x_bf16, topk_ids, topk_weights, out_bf16,
+                         workspace, ws_bytes, &c, stream);
+    if (st == HUM_ERR_UNSUPPORTED) continue;
+    if (st == HUM_OK && hipEventRecord(e0, s) != hipSuccess) st = set_error(HUM_ERR_HIP, "hipEventRecord failed");
+    for (int i = 0; i < iters && st == HUM_OK; ++i)
+      st = hum_moe_gemm_ex(w13, packed_w13, w2, packed_w2, t, topk, x_bf16, topk_ids, topk_weights, out_bf16,
+                           workspace, ws_bytes, &c, stream);
+    float ms = 0.0f;
+    if (st == HUM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                         hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+      st = set_error(HUM_ERR_HIP, "timing events failed");
+    if (st != HUM_OK) {
+      (void)hipEventDestroy(e0);
+      (void)hipEventDestroy(e1);
+      return st;
+    }
+    const float us = ms * 1000.0f / (float)iters;
+    if (!found || us < best_us) {
+      best_us = us;
+      best = c;
+      found = true;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (!found) return set_error(HUM_ERR_UNSUPPORTED, "no compiled configuration fits this shape and workspace");
+  st = hum_moe_gemm_ex(w13, packed_w13, w2, packed_w2, t, topk, x_bf16, topk_ids, topk_weights, out_bf16, workspace,
+                       ws_bytes, &best, stream);
+  if (st != HUM_OK) return st;
+  *best_out = best;
+  if (best_us_out) *best_us_out = best_us;
+  clear_error();
+  return HUM_OK;
+}
+
 // ---- the grouped_masked layout ---------------------------------------------
 
 // Validation shared by the masked entry points.

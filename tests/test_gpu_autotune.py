@@ -64,3 +64,27 @@ def test_autotune_respects_workspace():
     _, hdi, _, pi = _int_layer(256, 1024)
     with pytest.raises(hum.HumError, match="no compiled configuration"):
         hum.autotune_linear(hdi, pi, dev(xb), workspace=empty, iters=1)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_autotune_moe(act):
+    """The MoE autotune's winner reproduces `out` bitwise and meets the
+    oracle's tolerance; the invariant flag keeps it on tile kernels."""
+    e, h, inter, t, topk = 8, 256, 128, 20, 2
+    w13 = synth.moe_weights_mxfp4(synth.seed_for(14), e, 2 * inter, h)
+    w2 = synth.moe_weights_mxfp4(synth.seed_for(14, 1), e, h, inter)
+    d13, o13 = descs("e2m1", "group", 32, "e8m0", e, 2 * inter, h, act=act)
+    d2, o2 = descs("e2m1", "group", 32, "e8m0", e, h, inter, act=act)
+    p13, p2 = prepare(d13, w13, "e8m0"), prepare(d2, w2, "e8m0")
+    ids, wts = synth.routing(synth.seed_for(14, 2), t, e, topk)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(14, 3)), (t, h))
+    out = torch.empty((t, h), dtype=torch.bfloat16, device="cuda")
+    print(f"case autotune moe act={act}", flush=True)
+    best, us = hum.autotune_moe(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), out=out, iters=2)
+    assert us > 0
+    again = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=best)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), best
+    assert_tol(out, oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act), f"autotune moe {act} {best}")
+    inv, _ = hum.autotune_moe(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), iters=1, batch_invariant=True)
+    assert inv.kind == hum.KERNEL_TILE
