@@ -89,6 +89,7 @@ CASES = [
     ("e4m3", "block", 16, "f32", False, False),
     ("int8", "channel", 0, "f32", False, False),
     ("e2m1", "group", 16, "e4m3", False, True),
+    ("int4", "group", 32, "e8m0", False, False),
     ("int8", "tensor", 0, "f32", False, True),
 ]
 
