@@ -146,14 +146,16 @@ def dense_w4a16_sweep(hum, timer, iters):
 
 
 def dense_w4a16_fp4(hum, timer, iters, scale):
-    """FP4 weights x bf16 at N = K = 8192, the W4A16 sweep's shape: MXFP4
-    (E8M0 per 32) or NVFP4 (E4M3 per 16 + an f32 tensor scale)."""
+    """4-bit weights x bf16 at N = K = 8192, the W4A16 sweep's shape: MXFP4
+    (E8M0 per 32), NVFP4 (E4M3 per 16 + an f32 tensor scale) or MXINT4 (INT4
+    codes, E8M0 per 32)."""
     import synth
     import torch
     n = k = 8192
-    if scale == "e8m0":
-        w = synth.quant_weights(synth.seed_for(11), "e2m1", "group", 32, "e8m0", 1, n, k)
-        desc = hum.make_desc("e2m1", "group", 32, "e8m0", n, k)
+    if scale in ("e8m0", "mxint4"):
+        wd = "e2m1" if scale == "e8m0" else "int4"
+        w = synth.quant_weights(synth.seed_for(11, 3 if scale == "mxint4" else 0), wd, "group", 32, "e8m0", 1, n, k)
+        desc = hum.make_desc(wd, "group", 32, "e8m0", n, k)
         packed = hum.prepare_weight(desc, _dev(w["codes"]), _dev(w["scales"]))
         wbytes = n * k // 2 + n * (k // 32)
     else:
@@ -486,6 +488,7 @@ def main():
         sweep["dense_w8a16_int8_n7168_k2048"] = dense_w8a16(hum, timer, iters, "int8")
         sweep["dense_w4a16_mxfp4_n8192_k8192"] = dense_w4a16_fp4(hum, timer, iters, "e8m0")
         sweep["dense_w4a16_nvfp4_n8192_k8192"] = dense_w4a16_fp4(hum, timer, iters, "e4m3")
+        sweep["dense_w4a16_mxint4_n8192_k8192"] = dense_w4a16_fp4(hum, timer, iters, "mxint4")
         sweep["dense_w4a4_mxfp4_n7168_k2048"] = dense_w4a4(hum, timer, iters)
         del d["copies"]
         torch.cuda.empty_cache()

@@ -46,7 +46,8 @@ typedef enum hum_status {
 typedef enum hum_dtype {
   HUM_BF16 = 0,
   HUM_F32 = 1,
-  HUM_INT4 = 2,   /* signed two's-complement nibble, -8..7 */
+  HUM_INT4 = 2,   /* signed two's-complement nibble, -8..7; with HUM_E8M0
+                     scales per 32 along K: MXINT4 (bf16 activations) */
   HUM_UINT4 = 3,  /* unsigned nibble 0..15, optional zero point */
   HUM_E2M1 = 4,   /* FP4 (MXFP4 element) */
   HUM_E4M3 = 5,   /* FP8 E4M3 "FN": max 448, NaN = 0x7F/0xFF, no Inf; as a

@@ -53,6 +53,14 @@ hum_status check_desc(const hum_weight_desc* d) {
   switch (d->weight_dtype) {
     case HUM_INT4:
     case HUM_UINT4:
+      if (d->scale_dtype == HUM_E8M0) {
+        // MXINT4: signed INT4 codes with an E8M0 scale per 32 along K
+        if (d->weight_dtype != HUM_INT4 || d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32)
+          return set_error(HUM_ERR_UNSUPPORTED, "integer weights with E8M0 scales are INT4 with one scale per 32 (MXINT4)");
+        if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "MXINT4 takes no zero point");
+        if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "MXINT4 weights run with bf16 activations");
+        return HUM_OK;
+      }
       if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "integer weights run with bf16 activations");
       if (d->scale_dtype != HUM_BF16 && d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "integer weights take bf16 or f32 scales");
       if (d->scale_gran == HUM_SCALE_GROUP && d->group_size % 128) return set_error(HUM_ERR_UNSUPPORTED, "integer group_size must be a multiple of 128");
@@ -93,6 +101,7 @@ hum_status check_desc(const hum_weight_desc* d) {
 }
 
 int fmt_of(const hum_weight_desc* d) {
+  if (d->weight_dtype == HUM_INT4 && d->scale_dtype == HUM_E8M0) return F_MXINT4_BF16;
   if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
   if (d->weight_dtype == HUM_INT8) return F_INT8_BF16;
   if (d->weight_dtype == HUM_E4M3)

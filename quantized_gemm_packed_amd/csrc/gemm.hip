@@ -43,6 +43,8 @@
 //                  through f32 (exact), the FP8 path's layout and epilogue.
 //   F_NVFP4_BF16   NVFP4: E2M1 -> f32, times its E4M3 scale per 16 (exact: at
 //                  most 6 significant bits) -> bf16.
+//   F_MXINT4_BF16  MXINT4: INT4 with an E8M0 scale per 32 -> f32 -> bf16
+//                  (exact), the MX path's scale staging.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
@@ -149,7 +151,7 @@ __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs&
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
     const int64_t zb = (int64_t)p.ng * 8;
     s.zero = make_rsrc(w.zero + ntc * zb, (valid && p.has_zero) ? zb : 0);
-  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
+  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
     const int64_t sb = (int64_t)p.kb4 * 256;
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
   }
@@ -180,7 +182,7 @@ __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe&
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
     const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
     f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
-  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16)) {
+  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16)) {
     const uint32_t mo = ok ? (uint32_t)((kb >> Tr<FMT>::kMetaRowShift) * 64 + lane) * 4 : kOob;
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
   }
@@ -302,6 +304,25 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
       o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+      d[s] = __builtin_bit_cast(bf16x8_t, o);
+    }
+  } else if (FMT == F_MXINT4_BF16) {
+    // MXINT4: the integer path's nibble order (k-step s in dword s, element
+    // j at bit (j & 1) * 16 + (j >> 1) * 4) holding q + 8; (u - 8) * 2^E is
+    // one exact FMA in f32, packed to bf16 by its upper half (at most 4
+    // significant bits)
+    const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
+    const float off = -8.0f * fs;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t w = f.w[0][s];
+      u32x4_t o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_fmaf((float)((w >> (4 * i)) & 15u), fs, off);
+        const float hi = __builtin_fmaf((float)((w >> (16 + 4 * i)) & 15u), fs, off);
+        o[i] = pack_hi16(lo, hi);
+      }
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
   } else if (FMT == F_NVFP4_BF16) {
@@ -681,7 +702,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
           }
         }
       }
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nkb > 0) {
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nkb > 0) {
       const int n16 = (((kb_end + (1 << kRS) - 1) >> kRS) - r0) * 16;  // 16-byte slots of scale rows
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
@@ -740,7 +761,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     // weight metadata of the wave's K-blocks (INT: scales and zero points of
     // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
     constexpr int kML =
-        (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
+        (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
     u32x4_t mbuf[WN][kML > 0 ? kML : 1];
     uint32_t zbuf[WN];
     int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
@@ -753,7 +774,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       zb0 = g0w * 8;
       zbytes = p.has_zero ? (g1w - g0w) * 8 : 0;  // <= 256 B
       zdst = p.lds_zero_off + (g0w - g0) * 8;
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nj > 0) {
+    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nj > 0) {
       const int rw0 = kw0 >> kRS, rw1 = (kw0 + nj + (1 << kRS) - 1) >> kRS;
       mb0 = rw0 * 256;
       mbytes = (rw1 - rw0) * 256;  // <= 2 KB
@@ -817,7 +838,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
       const uint32_t zr = *reinterpret_cast<const uint32_t*>(mb + p.lds_zero_off + gl * 8 + ((c16 >> 3) << 2));
       z = p.has_zero ? zr : 0u;
-    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
+    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
       m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> kRS) - r0) * 64 + lane) * 4);
     }
   };
@@ -980,7 +1001,7 @@ struct TileCfg {
   static constexpr bool kTracked = (kS == 3);
   static constexpr int kMI = (FMT == F_INT || FMT == F_FP8_BLOCK)
                                  ? 1
-                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
                                      FMT == F_NVFP4_BF16) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
@@ -1157,7 +1178,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
     mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
     mi_gmul = 16u * (2u << sf);
-  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
                        FMT == F_NVFP4_BF16) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
@@ -1220,7 +1241,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_FP8_BLOCK) {
       dma4(rms, rmsr, mw, mi_off + (uint32_t)kb * 4u);
-    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
+    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
                          FMT == F_NVFP4_BF16) {
       // a metadata row covers 4 K-blocks (E8M0 per 32) or 2 (NVFP4: two
       // E4M3 per 32 of a lane)
@@ -1280,7 +1301,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
                                : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
       mw[ns] = 0;
-      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
+      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
     }
     if constexpr (FMT == F_FP8_BLOCK) {
@@ -1725,6 +1746,7 @@ static const Instance kInstances[] = {
     HUM_DENSE_SET(F_FP8_BF16),
     HUM_DENSE_SET(F_INT8_BF16),
     HUM_DENSE_SET(F_NVFP4_BF16),
+    HUM_DENSE_SET(F_MXINT4_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
     HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
     HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
@@ -1751,6 +1773,7 @@ static const ReduceInstance kReduces[] = {
     {F_FP8_BF16, EPI_BF16, splitk_reduce_kernel<F_FP8_BF16, EPI_BF16>},
     {F_INT8_BF16, EPI_BF16, splitk_reduce_kernel<F_INT8_BF16, EPI_BF16>},
     {F_NVFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_NVFP4_BF16, EPI_BF16>},
+    {F_MXINT4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXINT4_BF16, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
 };

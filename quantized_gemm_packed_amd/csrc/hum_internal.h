@@ -57,12 +57,13 @@ struct Layout {
 
 enum Fmt : int {
   F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6,
-  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8
+  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8, F_MXINT4_BF16 = 9
 };
 
 // Formats whose activations stay bf16 (bf16 MFMA on widened weights).
 constexpr bool fmt_bf16_act(int f) {
-  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16;
+  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16 ||
+         f == F_MXINT4_BF16;
 }
 // 8-bit weight codes laid out for the bf16 MFMA: a lane's 32 codes of a
 // K-block contiguous (k = 32 * (lane / 16) + j), per-channel f32 scales.
@@ -200,7 +201,7 @@ constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, i
     const int64_t zr = ((groups * 8 + 255) / 256) * 256;
     L.zero_off = sc;
     L.meta_stride = sc + zr;
-  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8 || fmt == F_NVFP4_BF16) {
+  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXINT4_BF16 || fmt == F_MXFP4_MXFP8 || fmt == F_NVFP4_BF16) {
     // scale rows a range of kb blocks touches (a row: 4 K-blocks, NVFP4 2)
     int64_t r = (fmt == F_NVFP4_BF16 ? kb / 2 : kb / 4) + 2;
     if (r > kb4) r = kb4;
@@ -222,7 +223,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
     const int64_t groups = (per + kb_per_group - 1) / kb_per_group + 1;
     return groups * 16 * (scale_f32 ? 4 : 2) <= 1024 && groups * 8 <= 256;
   }
-  if (fmt == F_MXFP4_BF16 || fmt == F_MXFP4_MXFP8) return (per / 4 + 2) * 256 <= 2048;
+  if (fmt == F_MXFP4_BF16 || fmt == F_MXINT4_BF16 || fmt == F_MXFP4_MXFP8) return (per / 4 + 2) * 256 <= 2048;
   if (fmt == F_NVFP4_BF16) return (per / 2 + 2) * 256 <= 2048;
   return true;
 }

@@ -303,7 +303,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
   } else if (f == F_NVFP4_BF16) {
     repack_nv_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
-  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4) {
+  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4 || f == F_MXINT4_BF16) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else if (f == F_FP8_BLOCK) {
     repack_fp8_block_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb, B), B, 0, s>>>(a);
@@ -329,6 +329,7 @@ struct DequantArgs {
   int block;     // E4M3 with 2-D block scales
   int bf16_order;  // 8-bit codes in the bf16 MFMA order
   int nvfp4;       // E2M1 with E4M3 scales per 16
+  int mxint4;      // INT4 with E8M0 scales per 32
 };
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -392,6 +393,18 @@ __global__ void dequant_kernel(DequantArgs a) {
     }
     return;
   }
+  if (a.mxint4) {
+    // INT4 codes in the integer nibble order (stored q + 8), E8M0 per 32
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(
+        a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb / 4) * 64 + lane) * 4);
+    const float s = e8m0_to_f32((word >> (8 * (kb % 4))) & 0xFF);
+    for (int st = 0; st < 4; ++st)
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t u = (w[st] >> ((j & 1) * 16 + (j >> 1) * 4)) & 0xF;
+        orow[32 * lg + 8 * st + j] = (float)((int)u - 8) * s;
+      }
+    return;
+  }
   // INT4 / UINT4
   const int64_t g = kb / a.kb_per_group;
   const uint8_t* sb = a.packed + a.scales_off + e * a.scales_pe;
@@ -435,6 +448,7 @@ hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void*
   a.block = d->scale_gran == HUM_SCALE_BLOCK;
   a.bf16_order = fmt_w8_bf16(fmt_of(d));
   a.nvfp4 = fmt_of(d) == F_NVFP4_BF16;
+  a.mxint4 = fmt_of(d) == F_MXINT4_BF16;
   const int64_t total = (int64_t)d->num_experts * L.nt * L.kb * 64;
   dequant_kernel<<<grid_for(total, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(a);
   hipError_t err = hipGetLastError();

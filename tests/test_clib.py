@@ -48,6 +48,8 @@ def test_packed_size_ragged_n_pads_to_16(lib):
     dict(weight_dtype="e4m3", scale_gran="group", group_size=128, scale_dtype="f32", act_fmt="fp8_token"),
     dict(weight_dtype="int8", scale_gran="group", group_size=128, scale_dtype="f32"),
     dict(weight_dtype="e2m1", scale_gran="group", group_size=32, scale_dtype="e4m3"),
+    dict(weight_dtype="int4", scale_gran="group", group_size=128, scale_dtype="e8m0"),
+    dict(weight_dtype="uint4", scale_gran="group", group_size=32, scale_dtype="e8m0"),
     dict(weight_dtype="e2m1", scale_gran="group", group_size=16, scale_dtype="e4m3", act_fmt="mxfp8"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="bf16"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="f32", act_fmt="fp8_token"),

@@ -26,6 +26,7 @@ FORMATS = {
     "e4m3_block128": ("e4m3", "block", 128, "f32", False, "fp8_group"),
     "mxfp4_bf16": ("e2m1", "group", 32, "e8m0", False, "bf16"),
     "nvfp4_bf16": ("e2m1", "group", 16, "e4m3", False, "bf16"),
+    "mxint4_bf16": ("int4", "group", 32, "e8m0", False, "bf16"),
     "mxfp4_mxfp8": ("e2m1", "group", 32, "e8m0", False, "mxfp8"),
     "mxfp4_mxfp4": ("e2m1", "group", 32, "e8m0", False, "mxfp4"),
 }

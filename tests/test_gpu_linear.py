@@ -331,6 +331,42 @@ def test_nvfp4_random_vs_oracle(m):
     assert_tol(out, ref, f"nvfp4 m={m}")
 
 
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_mxint4_exact_every_tile(tile):
+    """MXINT4 x bf16: every INT4 code, E8M0 scales 2^-3 .. 2^1 per 32 along
+    K, integer activations in [-8, 8]: all sums exact in fp32, so bitwise
+    equal to the oracle (decode and tile kernels)."""
+    m, n, k = rows_for(tile, 23), 272, 1024
+    g = synth.rng(47)
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    w = synth.quant_weights(47, "int4", "group", 32, "e8m0", 1, n, k, e8m0_lo=124, e8m0_hi=128)
+    hd, od = descs("int4", "group", 32, "e8m0", 1, n, k)
+    packed = prepare(hd, w, "e8m0")
+    print(f"case mxint4 exact tile={tile}", flush=True)
+    if not stream_fits(tile, m, k, 2):
+        with pytest.raises(hum.HumError, match="raise split_k"):
+            hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+        return
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 2))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
+def test_mxint4_random_vs_oracle(m):
+    """MXINT4 x bf16 at the selector's config."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_for(12, m), "int4", "group", 32, "e8m0", 1, n, k)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(12, 100 + m)), (m, k))
+    hd, od = descs("int4", "group", 32, "e8m0", 1, n, k)
+    packed = prepare(hd, w, "e8m0")
+    out = hum.linear(hd, packed, dev(xb))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_tol(out, ref, f"mxint4 m={m}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a8_dense_random_vs_oracle(m):
     """Dense W4A8 (MXFP4 weights x MXFP8 activations) at the selector's config."""
@@ -472,7 +508,7 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(o1, o2)
 
 
-@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "int8", "nvfp4", "e2m1_mxfp8", "e2m1_mxfp4"])
+@pytest.mark.parametrize("fmt", ["uint4", "e4m3", "e4m3_block", "e4m3_bf16", "int8", "nvfp4", "mxint4", "e2m1_mxfp8", "e2m1_mxfp4"])
 def test_empty_m_is_a_no_op(fmt):
     """M = 0: a valid call that writes nothing (every format's path)."""
     n, k = 256, 512
@@ -484,6 +520,10 @@ def test_empty_m_is_a_no_op(fmt):
         w = synth.dense_w8a8(synth.seed_for(3, 50), 1, n, k)
         hd, _ = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
         packed = prepare(hd, w, "f32")
+    elif fmt == "mxint4":
+        w = synth.quant_weights(synth.seed_for(3, 56), "int4", "group", 32, "e8m0", 1, n, k)
+        hd, _ = descs("int4", "group", 32, "e8m0", 1, n, k)
+        packed = prepare(hd, w, "e8m0")
     elif fmt == "nvfp4":
         w = synth.quant_weights(synth.seed_for(3, 55), "e2m1", "group", 16, "e4m3", 1, n, k)
         hd, _ = descs("e2m1", "group", 16, "e4m3", 1, n, k)

@@ -98,6 +98,20 @@ def test_dequant_bit_exact_nvfp4(shape):
     assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_dequant_bit_exact_mxint4(shape):
+    """MXINT4: every INT4 code times its E8M0 scale per 32."""
+    e, n, k = shape
+    hd, od = descs("int4", "group", 32, "e8m0", e, n, k)
+    w = synth.quant_weights(hash(("mxint4", shape)) & 0xFFFF, "int4", "group", 32, "e8m0", e, n, k)
+    packed = prepare(hd, w, "e8m0")
+    got = hum.dequant_weight(hd, packed)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.dequant_weight(od, w["codes"], w["scales"], include_global=False).astype(np.float32)
+    g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def test_group_k_equals_channel_bitwise():
     e, n, k = 1, 96, 512
     w = synth.quant_weights(5, "uint4", "group", k, "bf16", e, n, k, zero=True)
