@@ -165,8 +165,10 @@ size_t hum_linear_workspace_bytes(const hum_weight_desc* desc, int64_t m);
 /* C[m][n] = A[m][:] . W[n][:] (+ bias[n]) -> bf16, fp32 accumulation
  * ("WnA16" and "W8A8 / W4A8 / W4A4" sections of the Humming announcement).
  *   a        : bf16 [m][k]; or, when act_fmt != BF16 and a_scales != NULL,
- *              already-quantized E4M3 codes [m][k] with their scales
- *              (f32 [m] for FP8_TOKEN, u8 [m][k/32] for MXFP8)
+ *              already-quantized codes with their scales, as hum_quant_act
+ *              writes them: E4M3 [m][k] + f32 [m] (FP8_TOKEN), E4M3 [m][k] +
+ *              E8M0 u8 [m][k/32] (MXFP8), E2M1 pairs u8 [m][k/2] + E8M0 u8
+ *              [m][k/32] (MXFP4), E4M3 [m][k] + f32 [m][k/128] (FP8_GROUP)
  *   bias     : bf16 [n] or NULL
  *   out      : bf16 [m][n] (row stride n)
  *   workspace: device buffer of hum_linear_workspace_bytes(desc, m) bytes
