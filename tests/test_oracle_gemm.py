@@ -243,3 +243,63 @@ def test_nvfp4_group_scales_per_16():
     w = G.dequant_weight(desc, pack_nibbles(cu)[None], sc[None], global_scale=np.array([0.5], np.float32))[0]
     assert w[0, 17] == 0.5 * 0.5 and np.count_nonzero(w[0]) == 1
     assert w[1, 63] == -6.0 * 1.5 * 0.5 and np.count_nonzero(w[1]) == 1
+
+
+def _e4m3_frac(c):
+    """E4M3 "FN" code -> exact rational, from its bit fields (sign, 4-bit
+    exponent with bias 7, 3-bit mantissa; exponent 0 is subnormal with
+    quantum 2^-9).  NaN codes are never passed."""
+    c = int(c)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    assert not (e == 15 and m == 7)
+    v = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -v if s else v
+
+
+def _f32_frac(x):
+    """The exact value of a float32, through its IEEE bit pattern."""
+    b = struct.unpack("<I", struct.pack("<f", float(np.float32(x))))[0]
+    s, e, f = b >> 31, (b >> 23) & 0xFF, b & 0x7FFFFF
+    v = Fraction(f, 1 << 23) * Fraction(2) ** -126 if e == 0 else (1 + Fraction(f, 1 << 23)) * Fraction(2) ** (e - 127)
+    return -v if s else v
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 5, 64), (64, 3, 64), (4, 4, 128)])
+def test_fp8_token_x_fp8_channel_vs_fraction_brute_force(m, n, k):
+    """The per-token FP8 x per-channel E4M3 (W8A8) reference as the tests
+    compose it -- the quantizer's codes and f32 row scales, dequantized by
+    activations("fp8_token") / dequant_fp8_per_token, times the weight through
+    linear_fp8_e4m3 and through linear() -- against a Fraction sum of
+    v(qa[m,k]) * s_a[m] * v(qw[n,k]) * s_w[n] with bit-field decoders of its
+    own.  Row scales differ per row and the shapes include M == K and M == N,
+    so a scale broadcast along the wrong axis changes the result; scales are
+    not powers of two, so a dequantized operand rounded to f32 (instead of
+    the exact product) moves every sum by about 2^-24 relative."""
+    from oracle import quant as Q
+    g = np.random.default_rng(300 + m + n + k)
+    xf = np.clip(g.standard_normal((m, k)), -1.9, 1.9).astype(np.float32)
+    for i in range(m):                       # a distinct amax (hence scale) per row
+        xf[i, (5 * i) % k] = (2.0 + i / 16.0) * (-1.0 if i & 1 else 1.0)
+    x = bf16_bits(xf)
+    qa, sa = Q.quant_fp8_per_token(decode_bf16(x).astype(np.float32))
+    assert len(set(sa.tolist())) == m        # distinct row scales
+    cw = g.integers(0, 256, size=(n, k))
+    cw = np.where((cw & 0x7F) == 0x7F, 0x7E, cw).astype(np.uint8)
+    sw = g.uniform(1e-3, 4e-3, size=n).astype(np.float32)
+    a = G.activations("fp8_token", q=qa, scales=sa)
+    # the dequantized activations: exactly v(q) * fl32(s)
+    for i in range(m):
+        for kk in range(0, k, 7):
+            assert Fraction(float(a[i, kk])) == _e4m3_frac(qa[i, kk]) * _f32_frac(sa[i])
+    assert np.array_equal(a, Q.dequant_fp8_per_token(qa, sa))
+    got1 = G.linear_fp8_e4m3(a, cw, sw)
+    od = G.WeightDesc("e4m3", "channel", 0, "f32", False, False, 1, n, k)
+    got2 = G.linear(od, a, cw[None], sw.reshape(1, n, 1))
+    for i in range(m):
+        for j in range(n):
+            terms = [_e4m3_frac(qa[i, kk]) * _f32_frac(sa[i]) * _e4m3_frac(cw[j, kk]) * _f32_frac(sw[j])
+                     for kk in range(k)]
+            ref = sum(terms, Fraction(0))
+            bound = 1e-13 * float(sum(abs(t) for t in terms))
+            assert abs(got1[i, j] - float(ref)) <= bound, (i, j, got1[i, j], float(ref))
+            assert abs(got2[i, j] - float(ref)) <= bound, (i, j, got2[i, j], float(ref))
