@@ -205,6 +205,9 @@ hum_status hum_select_config(const hum_weight_desc* desc, int64_t m,
 /* Selection flags. */
 #define HUM_SELECT_BATCH_INVARIANT 1u  /* every output row independent of m and
                                           of the other rows of the call */
+#define HUM_SELECT_MOE_GATE_UP 2u      /* hum_moe_select_config: the gate_up
+                                          GEMM's configuration (default: the
+                                          down GEMM's) */
 
 /* hum_select_config with flags ("batch invariance" among the compute options
  * in the Humming announcement's feature list).  HUM_SELECT_BATCH_INVARIANT
@@ -245,7 +248,9 @@ size_t hum_moe_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc
  *   w13 : [E][2I][H] description + packed buffer; w2 : [E][H][I]
  *   x   : bf16 [T][H]; topk_ids i32 [T][topk]; topk_weights f32 [T][topk]
  *   out : bf16 [T][H]
- * topk_ids must lie in [0, E).  At most 512 experts.
+ * A slot whose id lies outside [0, E) (for example -1 for an expert held
+ * on another device) is skipped: it adds nothing to out.  At most 512
+ * experts.
  * No device->host synchronization: grids are sized from T, topk and E. */
 hum_status hum_moe_gemm(const hum_weight_desc* w13, const void* packed_w13,
                         const hum_weight_desc* w2, const void* packed_w2,
@@ -265,9 +270,10 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13,
 
 /* The configuration for hum_moe_gemm_ex (both GEMMs) at T tokens.  flags = 0:
  * the selector's down-GEMM configuration (hum_moe_gemm itself may run a small
- * batch's gate_up GEMM on the decode kernel).  HUM_SELECT_BATCH_INVARIANT: a
- * tile-kernel configuration, with which every token's output row is bitwise
- * independent of T and of the other tokens' routing. */
+ * batch's gate_up GEMM on the decode kernel); HUM_SELECT_MOE_GATE_UP: the
+ * gate_up GEMM's.  HUM_SELECT_BATCH_INVARIANT: a tile-kernel configuration,
+ * with which every token's output row is bitwise independent of T and of the
+ * other tokens' routing. */
 hum_status hum_moe_select_config(const hum_weight_desc* w13, const hum_weight_desc* w2,
                                  int64_t num_tokens, int32_t topk, uint32_t flags,
                                  hum_tile_config* cfg_out);

@@ -154,6 +154,60 @@ def _gpu(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _want(t, name, dtype, shape=None, numel=None):
+    """Checks a tensor argument's dtype and shape (or element count) before
+    anything is handed to the library: the kernels size their reads and
+    writes from the description, not from the tensor."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != int(numel):
+        raise ValueError(f"{name} must hold {int(numel)} elements, got {t.numel()}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _act_shapes(desc, m):
+    """(codes dtype, codes shape, scales dtype, scales shape) of pre-quantized
+    activations of `m` rows in desc's activation format."""
+    import torch
+    k = desc.k
+    fmt = desc.act_fmt
+    if fmt == ACT_FP8_TOKEN:
+        return torch.uint8, (m, k), torch.float32, (m,)
+    if fmt == ACT_MXFP8:
+        return torch.uint8, (m, k), torch.uint8, (m, k // 32)
+    if fmt == ACT_MXFP4:
+        return torch.uint8, (m, k // 2), torch.uint8, (m, k // 32)
+    if fmt == ACT_FP8_GROUP:
+        return torch.uint8, (m, k), torch.float32, (m, k // 128)
+    raise ValueError("bf16 activations take no a_scales")
+
+
+def _check_linear_args(desc, packed, a, a_scales, bias, out):
+    import torch
+    if a is None or a.dim() != 2:
+        raise ValueError("a must be a 2-D tensor [m, k]")
+    m = a.shape[0]
+    _want(packed, "packed", torch.uint8)
+    if a_scales is None:
+        _want(a, "a", torch.bfloat16, (m, desc.k))
+    else:
+        cd, cs, sd, ss = _act_shapes(desc, m)
+        _want(a, "a (pre-quantized codes)", cd, cs)
+        _want(a_scales, "a_scales", sd, ss)
+    _want(bias, "bias", torch.bfloat16, (desc.n,))
+    _want(out, "out", torch.bfloat16, (m, desc.n))
+    _same_device(packed, a, a_scales, bias, out)
+
+
 _DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3, "int8": INT8}
 _GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP, "block": SCALE_BLOCK}
 _SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0, "e4m3": E4M3}
@@ -191,11 +245,35 @@ def packed_weight_bytes(desc: WeightDesc) -> int:
 def prepare_weight(desc: WeightDesc, codes, scales, zeros=None, global_scale=None, packed=None):
     """Canonical device tensors -> packed uint8 device tensor."""
     import torch
+    e, n, k = desc.num_experts, desc.n, desc.k
+    four_bit = desc.weight_dtype in (INT4, UINT4, E2M1)
+    _want(codes, "codes", torch.uint8, numel=e * n * (k // 2 if four_bit else k))
+    if desc.scale_gran == SCALE_TENSOR:
+        nsc = e
+    elif desc.scale_gran == SCALE_CHANNEL:
+        nsc = e * n
+    elif desc.scale_gran == SCALE_BLOCK:
+        g = max(desc.group_size, 1)
+        nsc = e * (-(-n // g)) * (k // g)
+    else:
+        nsc = e * n * (k // max(desc.group_size, 1))
+    sdt = {BF16: (torch.int16, torch.bfloat16, torch.uint16), F32: (torch.float32,),
+           E8M0: (torch.uint8,), E4M3: (torch.uint8,)}.get(desc.scale_dtype, ())
+    if scales is None or scales.dtype not in sdt:
+        raise ValueError(f"scales must be one of {sdt} for scale dtype {desc.scale_dtype}")
+    _want(scales, "scales", scales.dtype, numel=nsc)
+    if desc.has_zero_point:
+        _want(zeros, "zeros", torch.uint8, numel=nsc)
+    if desc.has_global_scale:
+        _want(global_scale, "global_scale", torch.float32, numel=e)
+    _same_device(codes, scales, zeros, global_scale)
     for t, nm in ((codes, "codes"), (scales, "scales"), (zeros, "zeros"), (global_scale, "global_scale")):
         _gpu(t, nm)
     nb = packed_weight_bytes(desc)
     if packed is None:
         packed = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    _want(packed, "packed", torch.uint8)
+    _gpu(packed, "packed")
     _check(load_library().hum_prepare_weight(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
                                              _ptr(global_scale), _ptr(packed), packed.numel(),
                                              _stream(codes.device)))
@@ -214,6 +292,9 @@ def quant_act(act_fmt, x):
     """bf16 x [m, k] -> (codes, scales): E4M3 codes uint8 [m, k], or for
     MXFP4 E2M1 codes two per byte uint8 [m, k/2] (even k in the low nibble)."""
     import torch
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [m, k]")
+    _want(x, "x", torch.bfloat16)
     _gpu(x, "x")
     fmt = _AF.get(act_fmt, act_fmt)
     m, k = x.shape
@@ -241,10 +322,17 @@ def select_config(desc: WeightDesc, m: int, batch_invariant: bool = False) -> Ti
     return c
 
 
-def moe_select_config(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, batch_invariant: bool = False) -> TileConfig:
+SELECT_MOE_GATE_UP = 2
+
+
+def moe_select_config(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, batch_invariant: bool = False,
+                      gate_up: bool = False) -> TileConfig:
+    """The MoE selector's configuration: the down GEMM's, or with gate_up the
+    gate_up GEMM's."""
     c = TileConfig()
+    flags = (SELECT_BATCH_INVARIANT if batch_invariant else 0) | (SELECT_MOE_GATE_UP if gate_up else 0)
     _check(load_library().hum_moe_select_config(ctypes.byref(w13), ctypes.byref(w2), int(t), int(topk),
-                                                SELECT_BATCH_INVARIANT if batch_invariant else 0, ctypes.byref(c)))
+                                                flags, ctypes.byref(c)))
     return c
 
 
@@ -257,7 +345,9 @@ def linear_workspace_bytes(desc: WeightDesc, m: int, cfg: TileConfig | None = No
 
 class Workspace:
     """A device buffer that grows on demand (its contents need no
-    initialisation); one buffer serves any sequence of calls on one stream."""
+    initialisation).  One buffer serves any sequence of calls on one stream;
+    calls that may overlap in time (on different streams) need different
+    workspaces."""
 
     def __init__(self, device):
         self.device = device
@@ -268,6 +358,10 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
+            if self.buf is not None:
+                # the old buffer may still be read by work queued on the
+                # current stream: keep the allocator from reusing it early
+                self.buf.record_stream(torch.cuda.current_stream(self.device))
             self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
         return self.buf
 
@@ -276,10 +370,14 @@ _WS: dict = {}
 
 
 def _workspace(device):
+    """The binding's own workspace for calls on `device`'s current stream:
+    one per (device, stream), so calls on two streams never share scratch."""
     import torch
-    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    d = torch.device(device)
+    idx = d.index if d.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
     if key not in _WS:
-        _WS[key] = Workspace(torch.device("cuda", key))
+        _WS[key] = Workspace(torch.device("cuda", idx))
     return _WS[key]
 
 
@@ -288,7 +386,8 @@ def linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, cfg:
     """bf16 out [m, n] = A @ W^T (+ bias).  batch_invariant: every row's
     result independent of m (the library's invariant configuration)."""
     import torch
-    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias")):
+    _check_linear_args(desc, packed, a, a_scales, bias, out)
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias"), (out, "out")):
         _gpu(t, nm)
     m = a.shape[0]
     if batch_invariant and cfg is None:
@@ -311,7 +410,8 @@ def autotune_linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=N
     the winner's result.  The workspace defaults to the largest any
     candidate needs (a tile configuration with split-K 16)."""
     import torch
-    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias")):
+    _check_linear_args(desc, packed, a, a_scales, bias, out)
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias"), (out, "out")):
         _gpu(t, nm)
     m = a.shape[0]
     if out is None:
@@ -330,6 +430,20 @@ def autotune_linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=N
     return best, us.value
 
 
+def _check_moe_args(w13, packed_w13, packed_w2, x, topk_ids, topk_weights, out):
+    import torch
+    if topk_ids is None or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be a 2-D tensor [T, topk]")
+    t, k = topk_ids.shape
+    _want(topk_ids, "topk_ids", torch.int32)
+    _want(topk_weights, "topk_weights", torch.float32, (t, k))
+    _want(x, "x", torch.bfloat16, (t, w13.k))
+    _want(out, "out", torch.bfloat16, (t, w13.k))
+    _want(packed_w13, "packed_w13", torch.uint8)
+    _want(packed_w2, "packed_w2", torch.uint8)
+    _same_device(packed_w13, packed_w2, x, topk_ids, topk_weights, out)
+
+
 def moe_workspace_bytes(w13: WeightDesc, w2: WeightDesc, t: int, topk: int, cfg: TileConfig | None = None) -> int:
     lib = load_library()
     if cfg is None:
@@ -342,8 +456,9 @@ def moe_gemm(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk_ids
     """bf16 out [T, H] of the MoE expert layer.  batch_invariant: every
     token's result independent of the other tokens of the call."""
     import torch
+    _check_moe_args(w13, packed_w13, packed_w2, x, topk_ids, topk_weights, out)
     for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"), (topk_ids, "topk_ids"),
-                  (topk_weights, "topk_weights")):
+                  (topk_weights, "topk_weights"), (out, "out")):
         _gpu(t, nm)
     t_count, topk = topk_ids.shape
     if batch_invariant and cfg is None:
@@ -369,8 +484,9 @@ def autotune_moe(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, topk
     holding the winner's result.  The workspace defaults to what the largest
     expert block (128 rows) needs."""
     import torch
+    _check_moe_args(w13, packed_w13, packed_w2, x, topk_ids, topk_weights, out)
     for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"), (topk_ids, "topk_ids"),
-                  (topk_weights, "topk_weights")):
+                  (topk_weights, "topk_weights"), (out, "out")):
         _gpu(t, nm)
     t_count, topk = topk_ids.shape
     if out is None:
@@ -405,10 +521,18 @@ def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, e
     [E] (device) -> bf16 [E, max_m, H]; rows past an expert's count are left
     as they were in `out`."""
     import torch
-    for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"),
-                  (expert_num_tokens, "expert_num_tokens")):
-        _gpu(t, nm)
+    if x is None or x.dim() != 3:
+        raise ValueError("x must be a 3-D tensor [E, max_m, H]")
     e, max_m, h = x.shape
+    _want(x, "x", torch.bfloat16, (w13.num_experts, max_m, w13.k))
+    _want(expert_num_tokens, "expert_num_tokens", torch.int32, (w13.num_experts,))
+    _want(out, "out", torch.bfloat16, (w13.num_experts, max_m, w13.k))
+    _want(packed_w13, "packed_w13", torch.uint8)
+    _want(packed_w2, "packed_w2", torch.uint8)
+    _same_device(packed_w13, packed_w2, x, expert_num_tokens, out)
+    for t, nm in ((packed_w13, "packed_w13"), (packed_w2, "packed_w2"), (x, "x"),
+                  (expert_num_tokens, "expert_num_tokens"), (out, "out")):
+        _gpu(t, nm)
     if out is None:
         out = torch.zeros((e, max_m, h), dtype=torch.bfloat16, device=x.device)
     lib = load_library()
@@ -424,6 +548,9 @@ def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, e
 def moe_align(topk_ids, num_experts: int, block_m: int):
     """-> (sorted int32 [T*topk + E*(block_m-1)], offsets int32 [E+1], counts int32 [E])."""
     import torch
+    if topk_ids is None or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be a 2-D tensor [T, topk]")
+    _want(topk_ids, "topk_ids", torch.int32)
     _gpu(topk_ids, "topk_ids")
     t, k = topk_ids.shape
     cap = t * k + num_experts * (block_m - 1)
@@ -439,10 +566,15 @@ def moe_align(topk_ids, num_experts: int, block_m: int):
 def moe_reduce(y, topk_weights):
     """y bf16 [T*topk, H], w f32 [T, topk] -> bf16 [T, H]."""
     import torch
-    _gpu(y, "y")
-    _gpu(topk_weights, "topk_weights")
+    if topk_weights is None or topk_weights.dim() != 2 or y is None or y.dim() != 2:
+        raise ValueError("y must be [T*topk, H] and topk_weights [T, topk]")
     t, k = topk_weights.shape
     h = y.shape[1]
+    _want(topk_weights, "topk_weights", torch.float32)
+    _want(y, "y", torch.bfloat16, (t * k, h))
+    _same_device(y, topk_weights)
+    _gpu(y, "y")
+    _gpu(topk_weights, "topk_weights")
     out = torch.empty((t, h), dtype=torch.bfloat16, device=y.device)
     _check(load_library().hum_moe_reduce(_ptr(y), _ptr(topk_weights), t, k, h, _ptr(out), _stream(y.device)))
     return out

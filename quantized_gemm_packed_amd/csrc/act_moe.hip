@@ -430,6 +430,7 @@ hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e, 
 // Reduce: out[t][:] = bf16(sum_j w[t][j] * y[t*topk + j][:]), fp32, j order.
 
 __global__ __launch_bounds__(256) void moe_reduce_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
+                                                         const int32_t* __restrict__ ids, int32_t num_experts,
                                                          int64_t t_count, int32_t topk, int64_t h,
                                                          uint16_t* __restrict__ out) {
   const int64_t cpr = h / 8;
@@ -440,6 +441,12 @@ __global__ __launch_bounds__(256) void moe_reduce_kernel(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   for (int j = 0; j < topk; ++j) {
+    // a slot routed outside [0, E) (an expert held elsewhere) was never
+    // computed: it contributes nothing
+    if (ids) {
+      const int32_t e = ids[t * topk + j];
+      if (e < 0 || e >= num_experts) continue;
+    }
     const float wj = w[t * topk + j];
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + (t * topk + j) * h + c8 * 8);
 #pragma unroll
@@ -455,10 +462,10 @@ __global__ __launch_bounds__(256) void moe_reduce_kernel(const uint16_t* __restr
 }
 
 hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t topk, int64_t h,
-                             void* out, void* stream) {
+                             void* out, void* stream, const int32_t* ids, int32_t num_experts) {
   if (t == 0) return HUM_OK;
   moe_reduce_kernel<<<cdiv_u(t * (h / 8), 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(y), w, t, topk, h, static_cast<uint16_t*>(out));
+      static_cast<const uint16_t*>(y), w, ids, num_experts, t, topk, h, static_cast<uint16_t*>(out));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "moe_reduce launch: %s", hipGetErrorString(err));
   return HUM_OK;

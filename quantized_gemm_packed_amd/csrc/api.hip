@@ -310,11 +310,48 @@ static hum_tile_config moe_tile_cfg(int wm) {
   return c;
 }
 
+// A gathered decode-kernel configuration stages the activation rows of its
+// whole K range (and the weight metadata) in LDS: it fits when that plan and
+// the in-workgroup reduction stay within kStreamLdsMax.
+static bool moe_stream_fits(const hum_weight_desc* w, const hum_tile_config& c, int rows) {
+  if (c.kind != HUM_KERNEL_STREAM) return true;
+  Layout L;
+  if (compute_layout(w, &L) != HUM_OK) return false;
+  const StreamLdsPlan P =
+      stream_lds_plan(fmt_of(w), rows, kb_per_split(L.kb, c), c.wave_n, L.kb_per_group, L.scale_f32, L.ng, L.kb4);
+  const int64_t red = (int64_t)(c.waves_k - 1) * c.wave_n * 64 * 16;
+  return P.total <= kStreamLdsMax && red <= kStreamLdsMax;
+}
+
+// Makes a decode-kernel GEMM of the layer fit its LDS plan: more split-K
+// (where a reduce exists) while the K range is too long, else the 16-row
+// tile kernel for both GEMMs.
+static void moe_fit(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk, MoeCfg& mc) {
+  const int rows = (int)(t * topk < 16 ? t * topk : 16);
+  const int f = fmt_of(w13);
+  const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
+  auto fix = [&](const hum_weight_desc* w, hum_tile_config& c, int epi) -> bool {
+    while (!moe_stream_fits(w, c, rows)) {
+      if (c.split_k >= 8 || !reduce_instance_exists(f, epi)) return false;
+      c.split_k *= 2;
+    }
+    return true;
+  };
+  if (!fix(w13, mc.up, epi_up) || !fix(w2, mc.dn, EPI_SCATTER)) mc = MoeCfg{moe_tile_cfg(1), moe_tile_cfg(1)};
+}
+
 // Measured on MI355X (E = 128, top-8, H = 4096, I = 1024) over the mean
 // rows per expert: the decode kernel only while most experts see at most a
 // row or two (it reads each weight once, but its bf16 path is VALU heavy);
 // 16-row tiles up to ~100 rows, larger tiles beyond.
-static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk) {
+static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk);
+static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk, const hum_weight_desc* w2 = nullptr) {
+  MoeCfg mc = select_moe_shape(w13, t, topk);
+  if (w2) moe_fit(w13, w2, t, topk, mc);
+  return mc;
+}
+
+static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   const double rows = (double)t * topk / w13->num_experts;
   if (fmt_of(w13) == F_MXFP4_MXFP4) {
     // W4A4: tile kernels only (no decode-kernel path)
@@ -521,7 +558,8 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   if (m == 0) return HUM_OK;
   if (!packed || !a || !out) return set_error(HUM_ERR_INVALID_ARG, "packed, a and out must be non-NULL");
   hum_tile_config c = cfg ? *cfg : select_dense(desc, m);
-  if (!cfg_sane(c) || !gemm_instance_exists(dense_key(desc, c)))
+  if (!cfg_sane(c) || !gemm_instance_exists(dense_key(desc, c)) ||
+      (c.split_k > 1 && !reduce_instance_exists(fmt_of(desc), EPI_BF16)))
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   if (c.kind == HUM_KERNEL_STREAM && m > 16) return set_error(HUM_ERR_UNSUPPORTED, "the stream kernel takes m <= 16");
   const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
@@ -749,8 +787,10 @@ hum_status hum_moe_select_config(const hum_weight_desc* w13, const hum_weight_de
   hum_status st = check_moe(w13, w2, t, topk);
   if (st != HUM_OK) return st;
   if (!cfg_out) return set_error(HUM_ERR_INVALID_ARG, "cfg_out is NULL");
-  if (flags & ~(uint32_t)HUM_SELECT_BATCH_INVARIANT) return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
-  hum_tile_config c = select_moe(w13, t < 1 ? 1 : t, topk).dn;
+  if (flags & ~(uint32_t)(HUM_SELECT_BATCH_INVARIANT | HUM_SELECT_MOE_GATE_UP))
+    return set_error(HUM_ERR_INVALID_ARG, "unknown selection flags 0x%x", flags);
+  const MoeCfg mc = select_moe(w13, t < 1 ? 1 : t, topk, w2);
+  hum_tile_config c = (flags & HUM_SELECT_MOE_GATE_UP) ? mc.up : mc.dn;
   // the grouped tile kernel sums each slot's row in a fixed order (no split-K);
   // the decode kernel splits K inside the workgroup
   if ((flags & HUM_SELECT_BATCH_INVARIANT) && c.kind != HUM_KERNEL_TILE) c = moe_tile_cfg(1);
@@ -762,7 +802,7 @@ size_t hum_moe_workspace_bytes_ex(const hum_weight_desc* w13, const hum_weight_d
                                   const hum_tile_config* cfg) {
   clear_error();
   if (check_moe(w13, w2, t, topk) != HUM_OK) return 0;
-  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk, w2);
   return (size_t)moe_ws(w13, w2, t, topk, mc).total;
 }
 
@@ -800,6 +840,8 @@ static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelK
   *kup = KernelKey{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
   *kdn = KernelKey{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
   if (!gemm_instance_exists(*kup) || !gemm_instance_exists(*kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  if ((cu.split_k > 1 && !reduce_instance_exists(f, epi_up)) || (cd.split_k > 1 && !reduce_instance_exists(f, EPI_SCATTER)))
+    return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for this MoE format");
   return HUM_OK;
 }
 
@@ -903,7 +945,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   if (t == 0) return HUM_OK;
   if (!packed_w13 || !packed_w2 || !x_bf16 || !topk_ids || !topk_weights || !out_bf16)
     return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
-  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk);
+  const MoeCfg mc = cfg ? MoeCfg{*cfg, *cfg} : select_moe(w13, t, topk, w2);
   KernelKey kup, kdn;
   st = moe_keys(w13, mc, &kup, &kdn);
   if (st != HUM_OK) return st;
@@ -922,7 +964,7 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16), nullptr, 0};
   st = moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, rows, x_bf16, ws + w.y, stream);
   if (st != HUM_OK) return st;
-  return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream);
+  return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream, topk_ids, (int32_t)E);
 }
 
 // ---- on-device autotune of the MoE layer ---------------------------------------

@@ -1792,6 +1792,12 @@ static const Instance* find_instance(const KernelKey& k) {
 
 bool gemm_instance_exists(const KernelKey& key) { return find_instance(key) != nullptr; }
 
+bool reduce_instance_exists(int fmt, int epi) {
+  for (const ReduceInstance& q : kReduces)
+    if (q.fmt == fmt && q.epi == epi) return true;
+  return false;
+}
+
 hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_tiles, int block_m, void* stream) {
   GemmParams p = p_in;
   if (p.group_m < 1) p.group_m = 1;
@@ -1810,6 +1816,14 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
   if (p.scales_per_expert >= kRsrcMax ||
       (p.wzero && (int64_t)(p.wzero - p.wscale) + p.zeros_per_expert >= kRsrcMax))
     return set_error(HUM_ERR_UNSUPPORTED, "weight metadata above 2 GiB");
+  // the split-K reduce is resolved before anything is enqueued, so that a
+  // configuration without one is refused with nothing launched
+  const ReduceInstance* red_in = nullptr;
+  if (p.split_k > 1) {
+    for (const ReduceInstance& q : kReduces)
+      if (q.fmt == key.fmt && q.epi == key.epi) red_in = &q;
+    if (!red_in) return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for fmt=%d epi=%d", key.fmt, key.epi);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   size_t dyn = 0;
   if (key.kind == KIND_STREAM) {
@@ -1843,10 +1857,7 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "gemm launch: %s", hipGetErrorString(err));
   if (p.split_k > 1) {
-    const ReduceInstance* r = nullptr;
-    for (const ReduceInstance& q : kReduces)
-      if (q.fmt == key.fmt && q.epi == key.epi) r = &q;
-    if (!r) return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for fmt=%d epi=%d", key.fmt, key.epi);
+    const ReduceInstance* r = red_in;
     const int64_t cols = (key.epi == EPI_SWIGLU_MXFP8) ? 32 : 8;
     const int64_t threads = p.m * ((p.n + cols - 1) / cols);
     if (threads > 0) {

@@ -104,8 +104,11 @@ hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
 // rows are padding.
 hum_status launch_masked_align(const int32_t* counts, int32_t e, int64_t max_m, int32_t block_m,
                                int32_t* sorted, int32_t* block_expert, void* stream);
+// ids (optional): slots whose expert id lies outside [0, num_experts) are
+// skipped (they were never computed).
 hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t topk,
-                             int64_t h, void* out, void* stream);
+                             int64_t h, void* out, void* stream, const int32_t* ids = nullptr,
+                             int32_t num_experts = 0);
 
 // GEMM epilogues / A-row modes
 enum Epi : int { EPI_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_SWIGLU_MXFP8 = 2, EPI_SCATTER = 3, EPI_SWIGLU_MXFP4 = 4 };
@@ -239,6 +242,8 @@ struct KernelKey {
 hum_status launch_gemm(const KernelKey& key, const GemmParams& p, int64_t m_tiles, int block_m,
                        void* stream);
 bool gemm_instance_exists(const KernelKey& key);
+// A split-K reduce kernel is compiled for this format and epilogue.
+bool reduce_instance_exists(int fmt, int epi);
 hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, int kbc, uint8_t* out,
                          void* stream);
 

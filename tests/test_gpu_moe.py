@@ -275,3 +275,45 @@ def test_moe_masked_edges():
     hum.moe_gemm_masked(d13, p13, d2, p2, dev(xb), dev(c0), 4, out=out)
     torch.cuda.synchronize()
     assert np.all(out.view(torch.int16).cpu().numpy() == _UNTOUCHED)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+def test_moe_invalid_expert_ids_contribute_nothing(act):
+    """Slots routed to an id outside [0, E) (-1: an expert held elsewhere, or
+    E itself) add nothing: the same as a valid id with weight 0."""
+    e, h, inter, k, t = 8, 256, 128, 3, 40
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(760, e, h, inter, act)
+    ids, wts = synth.routing(761, t, e, k)
+    bad = np.zeros_like(ids, dtype=bool)
+    bad[::3, 0] = True
+    bad[1::5, 2] = True
+    ids_bad = ids.copy()
+    ids_bad[bad] = -1
+    ids_bad[7, 1] = e
+    bad[7, 1] = True
+    xb = synth.bf16_normal(synth.rng(762), (t, h))
+    # a first call leaves other rows in the workspace's slot buffer
+    hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids_bad), dev(wts))
+    torch.cuda.synchronize()
+    ids_ref = np.where(bad, 0, ids).astype(np.int32)
+    wts_ref = np.where(bad, 0.0, wts).astype(np.float32)
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids_ref, wts_ref, act)
+    assert_tol(out, ref, f"invalid ids act={act}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("t", [1, 2, 5])
+def test_moe_wide_hidden_decode(act, t):
+    """H = 5120 (40 K-blocks): the gate_up decode kernel's K range would
+    overflow LDS at 16 rows without more split-K; the selector must pick a
+    configuration that runs."""
+    e, h, inter, k = 16, 5120, 256, 8
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(770, e, h, inter, act)
+    ids, wts = synth.routing(771 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(772 + t), (t, h))
+    print(f"case moe wide act={act} t={t} up={hum.moe_select_config(d13, d2, t, k, gate_up=True)}", flush=True)
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"wide act={act} t={t}")
