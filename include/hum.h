@@ -180,6 +180,22 @@ hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m
                       const void* a, const void* a_scales, const void* bias,
                       void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): hum_linear with no
+ * workspace argument.  The workspace (split-K partials, activations
+ * quantized in the call, row sums) lives in a static device array of
+ * HUM_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends; no entry point allocates.  The selector's configuration
+ * is used; a call whose workspace would exceed the array is refused with
+ * HUM_ERR_WORKSPACE before anything is launched.  The array's contents need
+ * no initialisation and are left as the last call wrote them.  Calls on one
+ * GPU share the array: calls that overlap in time (different streams) race,
+ * so one stream (or ordered streams) per GPU.  Arguments as hum_linear. */
+#define HUM_NOALLOC_SCRATCH_BYTES (32u << 20)
+hum_status hum_linear_noalloc(const hum_weight_desc* desc, const void* packed, int64_t m,
+                              const void* a, const void* a_scales, const void* bias,
+                              void* out, void* stream);
+
 /* hum_linear with an explicit tile configuration (NULL = selector). */
 hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m,
                          const void* a, const void* a_scales, const void* bias,

@@ -95,6 +95,7 @@ _SIGS = {
     "hum_linear_workspace_bytes_ex": (_SZ, [_DP, _I64, _CP]),
     "hum_linear": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "hum_linear_ex": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
+    "hum_linear_noalloc": (_I32, [_DP, _P, _I64, _P, _P, _P, _P, _P]),
     "hum_prepare_workspace": (_I32, [_P, _SZ, _P]),
     "hum_select_config": (_I32, [_DP, _I64, _CP]),
     "hum_moe_workspace_bytes": (_SZ, [_DP, _DP, _I64, _I32]),
@@ -400,6 +401,19 @@ def linear(desc: WeightDesc, packed, a, a_scales=None, bias=None, out=None, cfg:
     lib = load_library()
     _check(lib.hum_linear_ex(ctypes.byref(desc), _ptr(packed), m, _ptr(a), _ptr(a_scales), _ptr(bias), _ptr(out),
                              _ptr(ws), wsb, None if cfg is None else ctypes.byref(cfg), _stream(a.device)))
+    return out
+
+
+def linear_noalloc(desc: WeightDesc, packed, a, out, a_scales=None, bias=None):
+    """hum_linear_noalloc: the library's static scratch array instead of a
+    workspace; `out` (bf16 [m, n]) must be given, so nothing is allocated."""
+    _check_linear_args(desc, packed, a, a_scales, bias, out)
+    if out is None:
+        raise ValueError("out must be given (the no-allocation call allocates nothing)")
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (bias, "bias"), (out, "out")):
+        _gpu(t, nm)
+    _check(load_library().hum_linear_noalloc(ctypes.byref(desc), _ptr(packed), a.shape[0], _ptr(a), _ptr(a_scales),
+                                             _ptr(bias), _ptr(out), _stream(a.device)))
     return out
 
 

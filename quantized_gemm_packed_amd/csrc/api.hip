@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "hum_internal.h"
@@ -614,6 +615,63 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
 hum_status hum_linear(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a, const void* a_scales,
                       const void* bias, void* out, void* workspace, size_t ws_bytes, void* stream) {
   return hum_linear_ex(desc, packed, m, a, a_scales, bias, out, workspace, ws_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// No-allocation variant of hum_linear: its workspace (split-K partials,
+// quantized activations, row sums) lives in this fixed static device array.
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code the array's name is only a stand-in: its device address is
+// looked up once per device (with that device current) and kept.
+
+namespace hum {
+static __device__ __align__(256) uint8_t scratch[HUM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_dev[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (looked up on first use).
+static hum_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return set_error(HUM_ERR_HIP, "hipGetDevice failed");
+  if (dev >= kMaxDevices) return set_error(HUM_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(HUM_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return HUM_OK;
+}
+}  // namespace hum
+
+extern "C" {
+
+hum_status hum_linear_noalloc(const hum_weight_desc* desc, const void* packed, int64_t m, const void* a,
+                              const void* a_scales, const void* bias, void* out, void* stream) {
+  clear_error();
+  hum_status st = check_desc(desc);
+  if (st != HUM_OK) return st;
+  if (m < 0) return set_error(HUM_ERR_INVALID_ARG, "m < 0");
+  if (m == 0) return HUM_OK;
+  const hum_tile_config c = select_dense(desc, m);
+  const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  const int64_t need = dense_ws(desc, m, c, quant_a).total;
+  if (need > (int64_t)HUM_NOALLOC_SCRATCH_BYTES)
+    return set_error(HUM_ERR_WORKSPACE,
+                     "hum_linear_noalloc: this call needs %lld bytes of scratch; the static array holds %lld "
+                     "(use hum_linear with a workspace)",
+                     (long long)need, (long long)HUM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != HUM_OK) return st;
+  return hum_linear_ex(desc, packed, m, a, a_scales, bias, out, ws, (size_t)HUM_NOALLOC_SCRATCH_BYTES, &c, stream);
 }
 
 // ---------------------------------------------------------------------------
