@@ -16,7 +16,12 @@ Readings where the pages are silent:
   routed scaling factor of 1.
 * precision at the stage boundary follows the activation format: bf16 (RNE)
   for W4A16, MXFP8 of the float value for W4A8, MXFP4 of it for W4A4; the
-  token activations are MXFP8- (W4A8) or MXFP4- (W4A4) quantized.
+  token activations are MXFP8- (W4A8) or MXFP4- (W4A4) quantized.  With FP8
+  activations (per token, or per token and 128 along K for block-scaled
+  experts -- the W8A8 of section "W8A8 / W4A8 / W4A4") the layer input is
+  quantized with that rule, and the SwiGLU output is rounded to bf16 and
+  then quantized with the same rule (a per-row amax spans the whole
+  intermediate row, so the rule applies to the stored bf16 row).
 * align: flat index f = t*topk + j; experts' segments in expert order, each
   padded to a multiple of block_m; inside a segment ascending f (stable);
   padding slots hold the sentinel T*topk.
@@ -28,7 +33,8 @@ import numpy as np
 
 from .formats import decode_bf16, encode_bf16
 from .gemm import WeightDesc, dequant_weight
-from .quant import dequant_mxfp4, dequant_mxfp8, quant_mxfp4, quant_mxfp8
+from .quant import (dequant_fp8_group, dequant_fp8_per_token, dequant_mxfp4, dequant_mxfp8, quant_fp8_group,
+                    quant_fp8_per_token, quant_mxfp4, quant_mxfp8)
 
 
 def align_capacity(num_tokens: int, topk: int, num_experts: int, block_m: int) -> int:
@@ -82,6 +88,33 @@ def qdq_mxfp4(a):
     return dequant_mxfp4(q, e)
 
 
+def qdq_fp8_token(a):
+    """Per-token FP8 quantize-dequantize of float32-representable rows
+    (bf16 values)."""
+    q, s = quant_fp8_per_token(np.asarray(a, np.float64).astype(np.float32))
+    return dequant_fp8_per_token(q, s)
+
+
+def qdq_fp8_group(a):
+    q, s = quant_fp8_group(np.asarray(a, np.float64).astype(np.float32))
+    return dequant_fp8_group(q, s)
+
+
+def stage_precision(a, act_fmt: str):
+    """The SwiGLU output as the down GEMM sees it."""
+    if act_fmt == "bf16":
+        return round_bf16(a)
+    if act_fmt == "mxfp8":
+        return qdq_mxfp8(a)
+    if act_fmt == "mxfp4":
+        return qdq_mxfp4(a)
+    if act_fmt == "fp8_token":
+        return qdq_fp8_token(round_bf16(a))
+    if act_fmt == "fp8_group":
+        return qdq_fp8_group(round_bf16(a))
+    raise ValueError(act_fmt)
+
+
 def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
                 x_bits, ids, weights, act_fmt: str, experts=None,
                 return_y: bool = False):
@@ -125,6 +158,10 @@ def quant_input(x, act_fmt: str):
         return qdq_mxfp8(x)
     if act_fmt == "mxfp4":
         return qdq_mxfp4(x)
+    if act_fmt == "fp8_token":
+        return qdq_fp8_token(x)
+    if act_fmt == "fp8_group":
+        return qdq_fp8_group(x)
     if act_fmt == "bf16":
         return x
     raise ValueError(act_fmt)
@@ -139,8 +176,7 @@ def expert_mlp(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict, a_in,
                           w13.get("global_scale"), experts=[e])[0]
     h = np.asarray(a_in, dtype=np.float64) @ w_gu.T
     del w_gu
-    a = swiglu(h, inter)
-    a = round_bf16(a) if act_fmt == "bf16" else (qdq_mxfp8(a) if act_fmt == "mxfp8" else qdq_mxfp4(a))
+    a = stage_precision(swiglu(h, inter), act_fmt)
     w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
                           w2.get("global_scale"), experts=[e])[0]
     return a @ w_dn.T

@@ -57,23 +57,52 @@ def _small_layer(seed, e, hdim, inter):
     return d13, w13, d2, w2
 
 
-@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+def _fp8_layer(seed, e, hdim, inter, gran):
+    from synth import quant_weights
+    gs = 128 if gran == "block" else 0
+    w13 = quant_weights(seed, "e4m3", gran, gs, "f32", e, 2 * inter, hdim, scale_lo=0.0005, scale_hi=0.002)
+    w2 = quant_weights(seed + 1, "e4m3", gran, gs, "f32", e, hdim, inter, scale_lo=0.0005, scale_hi=0.002)
+    d13 = G.WeightDesc("e4m3", gran, gs, "f32", False, False, e, 2 * inter, hdim)
+    d2 = G.WeightDesc("e4m3", gran, gs, "f32", False, False, e, hdim, inter)
+    return d13, w13, d2, w2
+
+
+def _fp8_qdq_ref(act):
+    """Independent restatement of the FP8 stage rules for the loop below:
+    the input row quantized by its own rule, the SwiGLU output rounded to
+    bf16 first."""
+    from oracle import quant as Q
+    if act == "fp8_token":
+        q = lambda a: Q.dequant_fp8_per_token(*Q.quant_fp8_per_token(np.asarray(a, np.float32)))
+    else:
+        q = lambda a: Q.dequant_fp8_group(*Q.quant_fp8_group(np.asarray(a, np.float32)))
+    return q, (lambda a: q(decode_bf16(encode_bf16(a))))
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4", "fp8_token", "fp8_group"])
 def test_moe_equals_loop_of_dense(act):
     e, hdim, inter, t, k = 6, 64, 32, 9, 3
-    d13, w13, d2, w2 = _small_layer(30, e, hdim, inter)
+    if act.startswith("fp8"):
+        hdim, inter = 256, 128
+        d13, w13, d2, w2 = _fp8_layer(30, e, hdim, inter, "block" if act == "fp8_group" else "channel")
+        q_in, q_mid = _fp8_qdq_ref(act)
+    else:
+        d13, w13, d2, w2 = _small_layer(30, e, hdim, inter)
+        qdq = {"mxfp8": M.qdq_mxfp8, "mxfp4": M.qdq_mxfp4}.get(act)
+        q_in = (lambda a: a) if act == "bf16" else qdq
+        q_mid = (lambda a: decode_bf16(encode_bf16(a))) if act == "bf16" else qdq
     g = np.random.default_rng(31)
     x = bf16_bits(g.standard_normal((t, hdim)).astype(np.float32))
     ids, wts = routing(32, t, e, k)
     out = M.moe_forward(d13, w13, d2, w2, x, ids, wts, act)
-    qdq = {"mxfp8": M.qdq_mxfp8, "mxfp4": M.qdq_mxfp4}.get(act)
-    a_in = decode_bf16(x) if act == "bf16" else qdq(decode_bf16(x))
+    a_in = q_in(decode_bf16(x))
     ref = np.zeros_like(out)
     for tt in range(t):
         for j in range(k):
             ex = int(ids[tt, j])
             h = G.linear(d13, a_in[tt:tt + 1], w13["codes"], w13["scales"], expert=ex)
             a = M.silu(h[:, :inter]) * h[:, inter:]
-            a = decode_bf16(encode_bf16(a)) if act == "bf16" else qdq(a)
+            a = q_mid(a)
             y = G.linear(d2, a, w2["codes"], w2["scales"], expert=ex)
             ref[tt] += float(wts[tt, j]) * y[0]
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
