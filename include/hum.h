@@ -257,7 +257,12 @@ size_t hum_moe_workspace_bytes(const hum_weight_desc* w13, const hum_weight_desc
                                int64_t num_tokens, int32_t topk);
 
 /* Full MoE expert layer ("indexed" grouping: rows gathered through the
- * sorted routing ids; SGLang PR #23754 summary, "Key source snippets"):
+ * sorted routing ids; SGLang PR #23754 summary, "Key source snippets").
+ * Expert formats: MXFP4 (bf16, MXFP8 or MXFP4 activations), MXINT4 and
+ * NVFP4 (bf16), E4M3 per-channel / per-tensor (bf16 or per-token FP8
+ * activations), E4M3 with 128 x 128 block scales (per-group FP8) and INT8
+ * (bf16); w13 and w2 share one format.  FP8 activation formats quantize
+ * the bf16 SwiGLU output with the same rule before the down GEMM:
  *   align (sort token slots by expert) -> gate_up grouped GEMM with a fused
  *   SwiGLU (a = silu(h[:I]) * h[I:], requantized to MXFP8 for W4A8) -> down
  *   grouped GEMM -> top-k weighted reduce.
@@ -358,6 +363,58 @@ hum_status hum_moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t to
 hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights,
                           int64_t num_tokens, int32_t topk, int64_t h,
                           void* out_bf16, void* stream);
+
+/* Stage export: one grouped GEMM of a MoE layer over rows sorted by expert
+ * (the per-gemm_type runner paths of the SGLang PR #23754 summary, "Key
+ * source snippets"; the "Gateup" and "Down" GEMMs of the Humming
+ * announcement's "Performance" section), with the sorted order and padded
+ * offsets that hum_moe_align returns.
+ *   w, packed   : expert weights [E][N][K] (the formats hum_moe_gemm runs)
+ *   a_mode      : HUM_MOE_A_GATHER : sorted row r reads a[sorted[r] / topk]
+ *                                    (a: [num_tokens][K], the layer input)
+ *                 HUM_MOE_A_SORTED : sorted row r reads a[r]
+ *                                    (a: [sorted_len][K], e.g. the SwiGLU
+ *                                    output of the gate_up stage)
+ *   a, a_scales : activations in w's activation format: bf16, or codes and
+ *                 scales as hum_quant_act writes them (this call quantizes
+ *                 nothing)
+ *   sorted      : i32 [sorted_len], sentinel num_tokens * topk for padding
+ *   offsets     : i32 [E + 1], padded to block_m (block_m = 16, 32, 64, 128)
+ *   epilogue    : HUM_MOE_EPI_NONE         bf16 out [sorted_len][N]
+ *                 HUM_MOE_EPI_SCATTER      bf16 out [num_tokens*topk][N] at
+ *                                          row sorted[r] (flat slot order)
+ *                 HUM_MOE_EPI_SWIGLU_BF16  bf16 out [sorted_len][N/2] of
+ *                                          silu(h[:N/2]) * h[N/2:]
+ *                 HUM_MOE_EPI_SWIGLU_MXFP8 E4M3 out [sorted_len][N/2] + E8M0
+ *                                          out_scales [sorted_len][N/64]
+ *                 HUM_MOE_EPI_SWIGLU_MXFP4 E2M1 pairs out [sorted_len][N/4] +
+ *                                          E8M0 out_scales [sorted_len][N/64]
+ *                 (the SwiGLU epilogue must be the activation format's: MX
+ *                 requantization for MXFP8 / MXFP4, bf16 otherwise)
+ *   out_swiglu_f32 : optional f32 [sorted_len][N/2]: the SwiGLU values the
+ *                 epilogue rounded or requantized
+ *   cfg         : NULL = a configuration with block_m-row tiles
+ *   workspace   : hum_moe_grouped_gemm_workspace_bytes(...) bytes
+ * Padding rows (sorted[r] >= num_tokens * topk) are never stored. */
+typedef enum hum_moe_a_mode { HUM_MOE_A_GATHER = 0, HUM_MOE_A_SORTED = 1 } hum_moe_a_mode;
+typedef enum hum_moe_epilogue {
+  HUM_MOE_EPI_NONE = 0,
+  HUM_MOE_EPI_SCATTER = 1,
+  HUM_MOE_EPI_SWIGLU_BF16 = 2,
+  HUM_MOE_EPI_SWIGLU_MXFP8 = 3,
+  HUM_MOE_EPI_SWIGLU_MXFP4 = 4
+} hum_moe_epilogue;
+
+size_t hum_moe_grouped_gemm_workspace_bytes(const hum_weight_desc* w, int32_t a_mode, int32_t epilogue,
+                                            int64_t num_tokens, int32_t topk, int64_t sorted_len,
+                                            int32_t block_m, const hum_tile_config* cfg);
+
+hum_status hum_moe_grouped_gemm(const hum_weight_desc* w, const void* packed, int32_t a_mode,
+                                int32_t epilogue, int64_t num_tokens, int32_t topk, const void* a,
+                                const void* a_scales, const int32_t* sorted, int64_t sorted_len,
+                                const int32_t* offsets, int32_t block_m, void* out, void* out_scales,
+                                float* out_swiglu_f32, const hum_tile_config* cfg, void* workspace,
+                                size_t ws_bytes, void* stream);
 
 /* Thread-local description of the last error (empty string if none). */
 const char* hum_last_error(void);

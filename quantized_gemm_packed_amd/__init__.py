@@ -104,6 +104,9 @@ _SIGS = {
     "hum_moe_gemm_ex": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
     "hum_moe_align": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "hum_moe_reduce": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+    "hum_moe_grouped_gemm_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I64, _I32, _I64, _I32, _CP]),
+    "hum_moe_grouped_gemm": (_I32, [_DP, _P, _I32, _I32, _I64, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P, _P, _CP,
+                                    _P, _SZ, _P]),
 }
 
 
@@ -592,6 +595,69 @@ def moe_reduce(y, topk_weights):
     out = torch.empty((t, h), dtype=torch.bfloat16, device=y.device)
     _check(load_library().hum_moe_reduce(_ptr(y), _ptr(topk_weights), t, k, h, _ptr(out), _stream(y.device)))
     return out
+
+
+MOE_A_GATHER, MOE_A_SORTED = range(2)
+MOE_EPI_NONE, MOE_EPI_SCATTER, MOE_EPI_SWIGLU_BF16, MOE_EPI_SWIGLU_MXFP8, MOE_EPI_SWIGLU_MXFP4 = range(5)
+_MOE_EPI = {"none": MOE_EPI_NONE, "scatter": MOE_EPI_SCATTER, "swiglu_bf16": MOE_EPI_SWIGLU_BF16,
+            "swiglu_mxfp8": MOE_EPI_SWIGLU_MXFP8, "swiglu_mxfp4": MOE_EPI_SWIGLU_MXFP4}
+
+
+def moe_grouped_gemm(w: WeightDesc, packed, a, sorted_ids, offsets, block_m: int, num_tokens: int, topk: int,
+                     a_mode: str = "gather", epilogue: str = "none", a_scales=None, cfg: TileConfig | None = None,
+                     keep_swiglu_f32: bool = False, workspace=None):
+    """One grouped GEMM stage over rows sorted by expert (hum_moe_grouped_gemm).
+    Returns out, or (out, out_scales) for the MX SwiGLU epilogues, plus the
+    fp32 SwiGLU values last when keep_swiglu_f32."""
+    import torch
+    if sorted_ids is None or sorted_ids.dim() != 1:
+        raise ValueError("sorted_ids must be a 1-D int32 tensor")
+    _want(sorted_ids, "sorted_ids", torch.int32)
+    _want(offsets, "offsets", torch.int32, (w.num_experts + 1,))
+    _want(packed, "packed", torch.uint8)
+    mode = {"gather": MOE_A_GATHER, "sorted": MOE_A_SORTED}[a_mode]
+    epi = _MOE_EPI[epilogue]
+    slen = sorted_ids.shape[0]
+    rows = num_tokens if mode == MOE_A_GATHER else slen
+    if w.act_fmt == ACT_BF16:
+        _want(a, "a", torch.bfloat16, (rows, w.k))
+    else:
+        cd, cs, sd, ss = _act_shapes(w, rows)
+        _want(a, "a", cd, cs)
+        _want(a_scales, "a_scales", sd, ss)
+    _same_device(packed, a, a_scales, sorted_ids, offsets)
+    for t, nm in ((packed, "packed"), (a, "a"), (a_scales, "a_scales"), (sorted_ids, "sorted_ids"),
+                  (offsets, "offsets")):
+        _gpu(t, nm)
+    dev = a.device
+    n = w.n
+    out_s = None
+    if epi == MOE_EPI_NONE:
+        out = torch.empty((slen, n), dtype=torch.bfloat16, device=dev)
+    elif epi == MOE_EPI_SCATTER:
+        out = torch.empty((num_tokens * topk, n), dtype=torch.bfloat16, device=dev)
+    elif epi == MOE_EPI_SWIGLU_BF16:
+        out = torch.empty((slen, n // 2), dtype=torch.bfloat16, device=dev)
+    elif epi == MOE_EPI_SWIGLU_MXFP8:
+        out = torch.empty((slen, n // 2), dtype=torch.uint8, device=dev)
+        out_s = torch.empty((slen, n // 64), dtype=torch.uint8, device=dev)
+    else:
+        out = torch.empty((slen, n // 4), dtype=torch.uint8, device=dev)
+        out_s = torch.empty((slen, n // 64), dtype=torch.uint8, device=dev)
+    f32 = torch.empty((slen, n // 2), dtype=torch.float32, device=dev) if keep_swiglu_f32 else None
+    lib = load_library()
+    cp = None if cfg is None else ctypes.byref(cfg)
+    need = lib.hum_moe_grouped_gemm_workspace_bytes(ctypes.byref(w), mode, epi, num_tokens, topk, slen, block_m, cp)
+    if need == 0:
+        raise HumError(2, lib.hum_last_error().decode())
+    ws = workspace if workspace is not None else _workspace(dev).get(need)
+    _check(lib.hum_moe_grouped_gemm(ctypes.byref(w), _ptr(packed), mode, epi, num_tokens, topk, _ptr(a),
+                                    _ptr(a_scales), _ptr(sorted_ids), slen, _ptr(offsets), block_m, _ptr(out),
+                                    _ptr(out_s), _ptr(f32), cp, _ptr(ws), ws.numel(), _stream(dev)))
+    res = (out,) if out_s is None else (out, out_s)
+    if keep_swiglu_f32:
+        res = res + (f32,)
+    return res[0] if len(res) == 1 else res
 
 
 @dataclass

@@ -16,7 +16,11 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhum.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "repack.hip", "act_moe.hip", "gemm.hip"]
+# The GEMM kernel instances are spread over several translation units so
+# that they compile in parallel.
+GEMM_SOURCES = ["gemm.hip", "inst_dense_a.hip", "inst_dense_b.hip", "inst_moe_a.hip", "inst_moe_b.hip",
+                "inst_moe_c.hip"]
+SOURCES = ["api.hip", "repack.hip", "act_moe.hip", *GEMM_SOURCES]
 ARCH = os.environ.get("HUM_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -36,7 +40,7 @@ def _hipcc() -> str:
 # Per-source flags.  The GEMM kernels keep MFMA results in ordinary VGPRs:
 # the INT path scales every K-block's MFMA result on the VALU, which reads
 # VGPRs only (AGPR results would cost one v_accvgpr_read per element).
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in GEMM_SOURCES}
 
 
 def _compile(src: str) -> str:

@@ -20,8 +20,10 @@ static inline unsigned cdiv_u(int64_t a, int64_t b) { return (unsigned)((a + b -
 
 __global__ __launch_bounds__(256) void quant_fp8_token_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                               int64_t k, uint8_t* __restrict__ q,
-                                                              float* __restrict__ s) {
+                                                              float* __restrict__ s,
+                                                              const int32_t* __restrict__ sorted, int32_t sentinel) {
   const int64_t row = blockIdx.x;
+  if (sorted && sorted[row] >= sentinel) return;  // a padding slot of grouped rows
   const uint16_t* xr = x + row * ldx;
   const int tid = threadIdx.x;
   __shared__ float red[4];
@@ -62,10 +64,10 @@ __global__ __launch_bounds__(256) void quant_fp8_token_kernel(const uint16_t* __
 }
 
 hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
-                                  float* s, void* stream) {
+                                  float* s, void* stream, const int32_t* sorted, int32_t sentinel) {
   if (m == 0) return HUM_OK;
   quant_fp8_token_kernel<<<(unsigned)m, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(x), ldx, k, static_cast<uint8_t*>(q), s);
+      static_cast<const uint16_t*>(x), ldx, k, static_cast<uint8_t*>(q), s, sorted, sentinel);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_fp8_token launch: %s", hipGetErrorString(err));
   return HUM_OK;
@@ -79,10 +81,13 @@ hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t l
 
 __global__ __launch_bounds__(256) void quant_fp8_group_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                               int64_t m, int64_t k, uint8_t* __restrict__ q,
-                                                              float* __restrict__ s) {
+                                                              float* __restrict__ s,
+                                                              const int32_t* __restrict__ sorted, int32_t sentinel) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t cpr = k / 8;  // chunks per row
-  const bool valid = id < m * cpr;
+  // (a padding slot of grouped rows is skipped: its 16-lane groups all
+  // belong to the one row, so they drop out together)
+  const bool valid = id < m * cpr && !(sorted && sorted[id / cpr] >= sentinel);
   const int64_t row = valid ? id / cpr : 0;
   const int64_t c8 = valid ? id % cpr : 0;
   u32x4_t v = {0, 0, 0, 0};
@@ -107,11 +112,11 @@ __global__ __launch_bounds__(256) void quant_fp8_group_kernel(const uint16_t* __
 }
 
 hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
-                                  void* stream) {
+                                  void* stream, const int32_t* sorted, int32_t sentinel) {
   if (m == 0) return HUM_OK;
   const int64_t chunks = m * (k / 8);
   quant_fp8_group_kernel<<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s, sorted, sentinel);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_fp8_group launch: %s", hipGetErrorString(err));
   return HUM_OK;
@@ -468,6 +473,39 @@ hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t t
       static_cast<const uint16_t*>(y), w, ids, num_experts, t, topk, h, static_cast<uint16_t*>(out));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "moe_reduce launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Block -> expert map of grouped rows from align's padded offsets: block b
+// (rows b*block_m ..) belongs to the largest e with offsets[e] <= b*block_m,
+// or to none (-1) past offsets[E].
+
+__global__ void block_expert_kernel(const int32_t* __restrict__ offsets, int32_t num_experts, int32_t block_m,
+                                    int64_t nblocks, int32_t* __restrict__ block_expert) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const int64_t pos = b * block_m;
+  int32_t ex = -1;
+  if (pos < offsets[num_experts]) {
+    int lo = 0, hi = num_experts - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offsets[mid] <= pos) lo = mid;
+      else hi = mid - 1;
+    }
+    ex = lo;
+  }
+  block_expert[b] = ex;
+}
+
+hum_status launch_block_expert(const int32_t* offsets, int32_t e, int32_t block_m, int64_t nblocks,
+                               int32_t* block_expert, void* stream) {
+  if (nblocks == 0) return HUM_OK;
+  block_expert_kernel<<<cdiv_u(nblocks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(offsets, e, block_m,
+                                                                                           nblocks, block_expert);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "block_expert launch: %s", hipGetErrorString(err));
   return HUM_OK;
 }
 

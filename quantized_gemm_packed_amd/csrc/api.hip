@@ -311,6 +311,17 @@ static hum_tile_config moe_tile_cfg(int wm) {
   return c;
 }
 
+// Expert weight formats the MoE layers run (per activation format).
+static bool moe_fmt_ok(int f) {
+  return f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4 || f == F_MXINT4_BF16 || f == F_NVFP4_BF16 ||
+         f == F_FP8 || f == F_FP8_BLOCK || f == F_FP8_BF16 || f == F_INT8_BF16;
+}
+
+// The gate_up GEMM's epilogue for a format.
+static int moe_up_epi(int f) {
+  return f == F_MXFP4_MXFP8 ? EPI_SWIGLU_MXFP8 : (f == F_MXFP4_MXFP4 ? EPI_SWIGLU_MXFP4 : EPI_SWIGLU_BF16);
+}
+
 // A gathered decode-kernel configuration stages the activation rows of its
 // whole K range (and the weight metadata) in LDS: it fits when that plan and
 // the in-workgroup reduction stay within kStreamLdsMax.
@@ -330,7 +341,7 @@ static bool moe_stream_fits(const hum_weight_desc* w, const hum_tile_config& c, 
 static void moe_fit(const hum_weight_desc* w13, const hum_weight_desc* w2, int64_t t, int32_t topk, MoeCfg& mc) {
   const int rows = (int)(t * topk < 16 ? t * topk : 16);
   const int f = fmt_of(w13);
-  const int epi_up = (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : EPI_SWIGLU_BF16;
+  const int epi_up = moe_up_epi(f);
   auto fix = [&](const hum_weight_desc* w, hum_tile_config& c, int epi) -> bool {
     while (!moe_stream_fits(w, c, rows)) {
       if (c.split_k >= 8 || !reduce_instance_exists(f, epi)) return false;
@@ -354,12 +365,12 @@ static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk, co
 
 static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   const double rows = (double)t * topk / w13->num_experts;
-  if (fmt_of(w13) == F_MXFP4_MXFP4) {
-    // W4A4: tile kernels only (no decode-kernel path)
+  if (fmt_of(w13) == F_MXFP4_MXFP4 || fmt_of(w13) == F_FP8_BLOCK) {
+    // W4A4 and block-scaled FP8: tile kernels only (no decode-kernel path)
     const int wm = rows <= 16 ? 1 : (rows <= 256 ? 2 : 4);
     return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
   }
-  if (fmt_of(w13) != F_MXFP4_MXFP8) {
+  if (fmt_of(w13) != F_MXFP4_MXFP8 && fmt_of(w13) != F_FP8) {
     if (rows < 0.5) return {moe_stream_cfg(), moe_stream_cfg()};
     const int wm = rows <= 96 ? 1 : (rows <= 192 ? 2 : 4);
     return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
@@ -769,9 +780,34 @@ hum_status hum_autotune_linear(const hum_weight_desc* desc, const void* packed, 
 // ---------------------------------------------------------------------------
 // MoE.
 
+// Bytes of `rows` activation rows of length k in activation format `fmt`:
+// codes, and scales (MX: E8M0 per 32; FP8 per token: f32 per row; FP8 per
+// group: f32 per 128).
+struct ActBytes {
+  int64_t codes, scales;
+};
+static ActBytes act_bytes(int fmt, int64_t rows, int64_t k) {
+  switch (fmt) {
+    case HUM_ACT_FP8_TOKEN: return {rows * k, rows * 4};
+    case HUM_ACT_MXFP8: return {rows * k, rows * (k / 32)};
+    case HUM_ACT_MXFP4: return {rows * (k / 2), rows * (k / 32)};
+    case HUM_ACT_FP8_GROUP: return {rows * k, rows * (k / 128) * 4};
+    default: return {rows * k * 2, 0};
+  }
+}
+// Bytes per row of the activation scales the GEMM kernels stage per row.
+static int64_t act_scale_ld(int fmt, int64_t k) {
+  return fmt == HUM_ACT_FP8_GROUP ? (k / 128) * 4 : (fmt == HUM_ACT_FP8_TOKEN ? 4 : k / 32);
+}
+// The gate_up epilogue requantizes the SwiGLU output itself (MX formats) or
+// writes it in bf16, to be quantized by a kernel between the GEMMs (FP8 per
+// token / per group) or used as is (bf16).
+static bool act_fused_requant(int fmt) { return fmt == HUM_ACT_MXFP8 || fmt == HUM_ACT_MXFP4; }
+static bool act_separate_quant(int fmt) { return fmt == HUM_ACT_FP8_TOKEN || fmt == HUM_ACT_FP8_GROUP; }
+
 struct MoeWs {
   int64_t partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0;
-  int64_t xq = 0, xs = 0, inter = 0, inter_s = 0, y = 0, total = 0;
+  int64_t xq = 0, xs = 0, inter = 0, inter_s = 0, interq = 0, interq_s = 0, y = 0, total = 0;
   int64_t cap = 0, nblocks = 0;
 };
 
@@ -785,10 +821,9 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   const int split = mc.up.split_k > mc.dn.split_k ? mc.up.split_k : mc.dn.split_k;
   const int64_t inter = w2->k;
   const int64_t h = w13->k;
+  const int act = w13->act_fmt;
   w.cap = masked ? t : t * topk + E * (bm - 1);
   w.nblocks = cdiv(w.cap, bm);
-  const bool mx = w13->act_fmt == HUM_ACT_MXFP8 || w13->act_fmt == HUM_ACT_MXFP4;
-  const bool mx4 = w13->act_fmt == HUM_ACT_MXFP4;  // E2M1 codes, two per byte
   const int64_t pcols = (2 * inter > cdiv(h, kNSub) * kNSub) ? 2 * inter : cdiv(h, kNSub) * kNSub;
   int64_t off = 0;
   w.partials = off;
@@ -802,15 +837,27 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   w.bexp = off;
   off = align256(off + w.nblocks * 4);
   w.xq = off;
-  if (mx) {
-    off = align256(off + (mx4 ? t * (h / 2) : t * h));
+  if (act != HUM_ACT_BF16) {
+    const ActBytes ab = act_bytes(act, t, h);
+    off = align256(off + ab.codes);
     w.xs = off;
-    off = align256(off + t * (h / 32));
+    off = align256(off + ab.scales);
   }
+  // gate_up output: MX codes (+ scales) when requantized in the epilogue,
+  // else bf16
   w.inter = off;
-  off = align256(off + (mx4 ? w.cap * (inter / 2) : w.cap * inter * (mx ? 1 : 2)));
+  const ActBytes ib = act_bytes(act_fused_requant(act) ? act : HUM_ACT_BF16, w.cap, inter);
+  off = align256(off + ib.codes);
   w.inter_s = off;
-  if (mx) off = align256(off + w.cap * (inter / 32));
+  off = align256(off + ib.scales);
+  // FP8 per token / per group: the intermediate quantized between the GEMMs
+  w.interq = off;
+  if (act_separate_quant(act)) {
+    const ActBytes qb = act_bytes(act, w.cap, inter);
+    off = align256(off + qb.codes);
+    w.interq_s = off;
+    off = align256(off + qb.scales);
+  }
   w.y = off;
   if (!masked) off = align256(off + t * topk * h * 2);
   w.total = off;
@@ -823,10 +870,12 @@ static hum_status check_moe(const hum_weight_desc* w13, const hum_weight_desc* w
   st = check_desc(w2);
   if (st != HUM_OK) return st;
   if (w13->num_experts != w2->num_experts) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 expert counts differ");
-  if (w13->weight_dtype != HUM_E2M1 || w2->weight_dtype != HUM_E2M1 || w13->scale_dtype != HUM_E8M0 ||
-      w2->scale_dtype != HUM_E8M0)
-    return set_error(HUM_ERR_UNSUPPORTED, "the MoE path runs MXFP4 (E2M1 + E8M0) expert weights");
   if (w13->act_fmt != w2->act_fmt) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 activation formats differ");
+  if (fmt_of(w13) != fmt_of(w2)) return set_error(HUM_ERR_INVALID_ARG, "w13 and w2 weight formats differ");
+  if (!moe_fmt_ok(fmt_of(w13)))
+    return set_error(HUM_ERR_UNSUPPORTED,
+                     "the MoE path runs MXFP4, MXINT4, NVFP4, FP8 (per-channel / per-tensor / 128-block) and INT8 "
+                     "expert weights; not INT4 / UINT4 with group scales");
   if (w13->n != 2 * w2->k) return set_error(HUM_ERR_INVALID_ARG, "w13 n must be 2 * intermediate (w2 k)");
   if (w2->n != w13->k) return set_error(HUM_ERR_INVALID_ARG, "w2 n must equal the hidden size (w13 k)");
   if (w2->k % 128) return set_error(HUM_ERR_UNSUPPORTED, "intermediate size must be a multiple of 128");
@@ -886,6 +935,143 @@ hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights, int64_t
   return launch_moe_reduce(y_bf16, topk_weights, t, topk, h, out_bf16, stream);
 }
 
+// ---- one grouped GEMM (stage export) -------------------------------------
+
+struct StageSetup {
+  hum_tile_config c;
+  KernelKey key;
+  int64_t nblocks = 0, bexp = 0, partials = 0, total = 0;
+};
+
+static int stage_epi(int32_t e) {
+  switch (e) {
+    case HUM_MOE_EPI_NONE: return EPI_BF16;
+    case HUM_MOE_EPI_SCATTER: return EPI_SCATTER;
+    case HUM_MOE_EPI_SWIGLU_BF16: return EPI_SWIGLU_BF16;
+    case HUM_MOE_EPI_SWIGLU_MXFP8: return EPI_SWIGLU_MXFP8;
+    case HUM_MOE_EPI_SWIGLU_MXFP4: return EPI_SWIGLU_MXFP4;
+  }
+  return -1;
+}
+
+// Validation, configuration and workspace plan of hum_moe_grouped_gemm.
+static hum_status stage_setup(const hum_weight_desc* w, int32_t a_mode, int32_t epilogue, int64_t t, int32_t topk,
+                              int64_t sorted_len, int32_t block_m, const hum_tile_config* cfg, StageSetup* out) {
+  hum_status st = check_desc(w);
+  if (st != HUM_OK) return st;
+  const int f = fmt_of(w);
+  if (!moe_fmt_ok(f)) return set_error(HUM_ERR_UNSUPPORTED, "no grouped GEMM for this weight format");
+  if (w->num_experts > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
+  if (t < 0 || topk < 1 || topk > 64 || sorted_len < 0) return set_error(HUM_ERR_INVALID_ARG, "bad num_tokens / topk / sorted_len");
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128)
+    return set_error(HUM_ERR_INVALID_ARG, "block_m must be 16, 32, 64 or 128");
+  if (a_mode != HUM_MOE_A_GATHER && a_mode != HUM_MOE_A_SORTED) return set_error(HUM_ERR_INVALID_ARG, "bad a_mode");
+  const int epi = stage_epi(epilogue);
+  if (epi < 0) return set_error(HUM_ERR_INVALID_ARG, "bad epilogue");
+  const bool swiglu = epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_MXFP8 || epi == EPI_SWIGLU_MXFP4;
+  if (swiglu && w->n % 64) return set_error(HUM_ERR_INVALID_ARG, "SwiGLU epilogues need n = 2 * I with I % 32 == 0");
+  if (swiglu && epi != moe_up_epi(f))
+    return set_error(HUM_ERR_UNSUPPORTED, "this activation format's SwiGLU epilogue is %s",
+                     moe_up_epi(f) == EPI_SWIGLU_MXFP8 ? "SWIGLU_MXFP8"
+                                                      : (moe_up_epi(f) == EPI_SWIGLU_MXFP4 ? "SWIGLU_MXFP4" : "SWIGLU_BF16"));
+  if (t * topk + (int64_t)w->num_experts * 127 >= ((int64_t)1 << 31) || sorted_len >= ((int64_t)1 << 31))
+    return set_error(HUM_ERR_UNSUPPORTED, "too many rows");
+  StageSetup S;
+  if (cfg) {
+    S.c = *cfg;
+  } else {
+    const MoeCfg mc = select_moe_shape(w, t < 1 ? 1 : t, topk);
+    S.c = (tile_rows(mc.dn) == block_m) ? mc.dn : moe_tile_cfg(block_m / 16);
+  }
+  if (!cfg_sane(S.c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  if (tile_rows(S.c) != block_m) return set_error(HUM_ERR_INVALID_ARG, "the configuration's block (%d rows) differs from block_m", (int)tile_rows(S.c));
+  S.key = KernelKey{f, S.c.kind, S.c.wave_m, S.c.wave_n, S.c.waves_n, S.c.waves_k,
+                    a_mode == HUM_MOE_A_GATHER ? A_GATHER : A_DIRECT, epi, key_stages(S.c)};
+  if (!gemm_instance_exists(S.key)) return set_error(HUM_ERR_UNSUPPORTED, "no grouped GEMM instance for this mode, epilogue and tile");
+  if (S.c.split_k > 1 && !reduce_instance_exists(f, epi)) return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for this format and epilogue");
+  if (S.c.kind == HUM_KERNEL_STREAM && !moe_stream_fits(w, S.c, (int)(t * topk < 16 ? t * topk : 16)))
+    return set_error(HUM_ERR_UNSUPPORTED, "decode kernel: K range per split too long for LDS (raise split_k)");
+  S.nblocks = cdiv(sorted_len, block_m);
+  int64_t off = 0;
+  S.bexp = off;
+  off = align256(off + S.nblocks * 4);
+  S.partials = off;
+  const int64_t ncols = swiglu ? w->n : cdiv(w->n, kNSub) * kNSub;
+  if (S.c.split_k > 1) off = align256(off + (int64_t)S.c.split_k * sorted_len * ncols * 4);
+  S.total = off;
+  *out = S;
+  return HUM_OK;
+}
+
+size_t hum_moe_grouped_gemm_workspace_bytes(const hum_weight_desc* w, int32_t a_mode, int32_t epilogue,
+                                            int64_t num_tokens, int32_t topk, int64_t sorted_len, int32_t block_m,
+                                            const hum_tile_config* cfg) {
+  clear_error();
+  StageSetup S;
+  if (stage_setup(w, a_mode, epilogue, num_tokens, topk, sorted_len, block_m, cfg, &S) != HUM_OK) return 0;
+  return (size_t)(S.total > 0 ? S.total : 256);
+}
+
+hum_status hum_moe_grouped_gemm(const hum_weight_desc* w, const void* packed, int32_t a_mode, int32_t epilogue,
+                                int64_t num_tokens, int32_t topk, const void* a, const void* a_scales,
+                                const int32_t* sorted, int64_t sorted_len, const int32_t* offsets, int32_t block_m,
+                                void* out, void* out_scales, float* out_swiglu_f32, const hum_tile_config* cfg,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  StageSetup S;
+  hum_status st = stage_setup(w, a_mode, epilogue, num_tokens, topk, sorted_len, block_m, cfg, &S);
+  if (st != HUM_OK) return st;
+  if (sorted_len == 0 || num_tokens == 0) return HUM_OK;
+  const int act = w->act_fmt;
+  const int epi = stage_epi(epilogue);
+  const bool swiglu = epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_MXFP8 || epi == EPI_SWIGLU_MXFP4;
+  if (!packed || !a || !sorted || !offsets || !out) return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  if (act != HUM_ACT_BF16 && !a_scales) return set_error(HUM_ERR_INVALID_ARG, "quantized activations need a_scales");
+  if ((epi == EPI_SWIGLU_MXFP8 || epi == EPI_SWIGLU_MXFP4) && !out_scales)
+    return set_error(HUM_ERR_INVALID_ARG, "MX epilogues need out_scales");
+  if (!workspace || ws_bytes < (size_t)S.total)
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)S.total);
+  const int64_t a_rows = a_mode == HUM_MOE_A_GATHER ? num_tokens : sorted_len;
+  const ActBytes ab = act_bytes(act, a_rows, w->k);
+  if (ab.codes >= ((int64_t)1 << 31) || ab.scales >= ((int64_t)1 << 31))
+    return set_error(HUM_ERR_UNSUPPORTED, "activations above 2 GiB");
+  Layout L;
+  compute_layout(w, &L);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + S.bexp);
+  st = launch_block_expert(offsets, w->num_experts, block_m, S.nblocks, bexp, stream);
+  if (st != HUM_OK) return st;
+  GemmParams p{};
+  fill_weight_params(p, w, L, packed);
+  const int64_t nout = swiglu ? w->n / 2 : w->n;
+  p.n = nout;
+  p.swiglu_nt_off = swiglu ? (int)(nout / kNSub) : 0;
+  p.a = a;
+  p.lda = w->k;
+  p.a_scale = a_scales;
+  p.a_scale_ld = act_scale_ld(act, w->k);
+  p.m = sorted_len;
+  p.sorted = sorted;
+  p.block_expert = bexp;
+  p.topk = topk;
+  p.sentinel = (int)(num_tokens * topk);
+  p.out = out;
+  p.ldo = nout;
+  p.out_scale = out_scales;
+  p.swiglu_f32 = swiglu ? out_swiglu_f32 : nullptr;
+  p.bias = nullptr;
+  p.n_tiles = (int)(swiglu ? cdiv(cdiv(nout, kNSub), tile_subtiles(S.c) / 2) : cdiv(L.nt, tile_subtiles(S.c)));
+  p.group_m = 1;  // M-tiles are different experts
+  p.split_k = S.c.split_k;
+  p.kb_per_split = kb_per_split(L.kb, S.c);
+  p.partials = reinterpret_cast<float*>(ws + S.partials);
+  p.stream_rows = (int)(num_tokens * topk < 16 ? num_tokens * topk : 16);
+  p.a_bytes = ab.codes;
+  p.a_scale_bytes = ab.scales;
+  log_cfg("moe grouped gemm", S.c, sorted_len);
+  return launch_gemm(S.key, p, S.nblocks, block_m, stream);
+}
+
 // Kernel keys of a layer's two GEMMs; HUM_OK when both are compiled.
 static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelKey* kup, KernelKey* kdn) {
   const hum_tile_config& cu = mc.up;
@@ -893,8 +1079,7 @@ static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelK
   if (!cfg_sane(cu) || !cfg_sane(cd) || tile_rows(cu) != tile_rows(cd))
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
-  const int epi_up =
-      (f == F_MXFP4_MXFP8) ? EPI_SWIGLU_MXFP8 : (f == F_MXFP4_MXFP4 ? EPI_SWIGLU_MXFP4 : EPI_SWIGLU_BF16);
+  const int epi_up = moe_up_epi(f);
   *kup = KernelKey{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
   *kdn = KernelKey{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
   if (!gemm_instance_exists(*kup) || !gemm_instance_exists(*kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
@@ -915,7 +1100,9 @@ struct MoeRows {
 
 // gate_up (+ SwiGLU, + requantization) into the workspace, then down with
 // its rows scattered to y[slot] (row stride h), over the expert blocks that
-// ws.sorted / ws.bexp describe.
+// ws.sorted / ws.bexp describe.  The layer input is quantized first where
+// the activation format asks for it; FP8 per-token / per-group layers also
+// quantize the bf16 SwiGLU output (its live rows) before the down GEMM.
 static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
                             const void* packed_w2, const MoeCfg& mc, const KernelKey& kup, const KernelKey& kdn,
                             const MoeWs& w, uint8_t* ws, const MoeRows& r, const void* x_bf16, void* y,
@@ -929,17 +1116,22 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const int32_t bm = (int32_t)tile_rows(cu);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
-  const int f = fmt_of(w13);
-  const bool mx4 = f == F_MXFP4_MXFP4;
-  const bool mx = f == F_MXFP4_MXFP8 || mx4;
+  const int act = w13->act_fmt;
+  const bool fused_q = act_fused_requant(act);
+  const bool sep_q = act_separate_quant(act);
   const void* x_use = x_bf16;
   hum_status st = HUM_OK;
-  if (mx) {
-    st = mx4 ? launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m)
-             : launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
-    if (st != HUM_OK) return st;
-    x_use = ws + w.xq;
+  if (act == HUM_ACT_MXFP4) {
+    st = launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
+  } else if (act == HUM_ACT_MXFP8) {
+    st = launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
+  } else if (act == HUM_ACT_FP8_TOKEN) {
+    st = launch_quant_fp8_token(t, h, x_bf16, h, ws + w.xq, reinterpret_cast<float*>(ws + w.xs), stream);
+  } else if (act == HUM_ACT_FP8_GROUP) {
+    st = launch_quant_fp8_group(t, h, x_bf16, h, ws + w.xq, reinterpret_cast<float*>(ws + w.xs), stream);
   }
+  if (st != HUM_OK) return st;
+  if (act != HUM_ACT_BF16) x_use = ws + w.xq;
   // gate_up (+ SwiGLU)
   GemmParams p{};
   fill_weight_params(p, w13, L13, packed_w13);
@@ -947,8 +1139,8 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   p.swiglu_nt_off = (int)(inter / kNSub);
   p.a = x_use;
   p.lda = h;
-  p.a_scale = mx ? ws + w.xs : nullptr;
-  p.a_scale_ld = h / 32;
+  p.a_scale = act != HUM_ACT_BF16 ? ws + w.xs : nullptr;
+  p.a_scale_ld = act_scale_ld(act, h);
   p.m = w.cap;
   p.sorted = sorted;
   p.block_expert = bexp;
@@ -956,24 +1148,38 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   p.sentinel = r.sentinel;
   p.out = ws + w.inter;
   p.ldo = inter;
-  p.out_scale = mx ? ws + w.inter_s : nullptr;
+  p.out_scale = fused_q ? ws + w.inter_s : nullptr;
   p.bias = nullptr;
   p.n_tiles = (int)cdiv(cdiv(inter, kNSub), tile_subtiles(cu) / 2);
   p.split_k = cu.split_k;
   p.kb_per_split = kb_per_split(L13.kb, cu);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
   p.stream_rows = r.stream_rows;
-  p.a_bytes = mx4 ? t * (h / 2) : t * h * (mx ? 1 : 2);
-  p.a_scale_bytes = mx ? t * (h / 32) : 0;
+  const ActBytes xb = act_bytes(act, t, h);
+  p.a_bytes = xb.codes;
+  p.a_scale_bytes = xb.scales;
   st = launch_gemm(kup, p, w.nblocks, bm, stream);
   if (st != HUM_OK) return st;
+  // FP8 per token / per group: quantize the live rows of the intermediate
+  const void* a2 = ws + w.inter;
+  const void* s2 = fused_q ? ws + w.inter_s : nullptr;
+  if (sep_q) {
+    st = act == HUM_ACT_FP8_TOKEN
+             ? launch_quant_fp8_token(w.cap, inter, ws + w.inter, inter, ws + w.interq,
+                                      reinterpret_cast<float*>(ws + w.interq_s), stream, sorted, r.sentinel)
+             : launch_quant_fp8_group(w.cap, inter, ws + w.inter, inter, ws + w.interq,
+                                      reinterpret_cast<float*>(ws + w.interq_s), stream, sorted, r.sentinel);
+    if (st != HUM_OK) return st;
+    a2 = ws + w.interq;
+    s2 = ws + w.interq_s;
+  }
   // down (rows scattered back to flat slots)
   GemmParams q{};
   fill_weight_params(q, w2, L2, packed_w2);
-  q.a = ws + w.inter;
+  q.a = a2;
   q.lda = inter;
-  q.a_scale = mx ? ws + w.inter_s : nullptr;
-  q.a_scale_ld = inter / 32;
+  q.a_scale = s2;
+  q.a_scale_ld = act_scale_ld(act, inter);
   q.m = w.cap;
   q.sorted = sorted;
   q.block_expert = bexp;
@@ -988,8 +1194,9 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   q.kb_per_split = kb_per_split(L2.kb, cd);
   q.partials = reinterpret_cast<float*>(ws + w.partials);
   q.stream_rows = r.stream_rows;  // valid (non-padding) rows of a block
-  q.a_bytes = mx4 ? w.cap * (inter / 2) : w.cap * inter * (mx ? 1 : 2);
-  q.a_scale_bytes = mx ? w.cap * (inter / 32) : 0;
+  const ActBytes ab = act_bytes(act, w.cap, inter);
+  q.a_bytes = ab.codes;
+  q.a_scale_bytes = ab.scales;
   return launch_gemm(kdn, q, w.nblocks, bm, stream);
 }
 

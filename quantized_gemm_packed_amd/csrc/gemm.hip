@@ -1,1615 +1,13 @@
-// Quantized GEMM for gfx950: dense layers and grouped (MoE) expert layers.
-//
-// What is computed is the WnA16 / W8A8 / W4A8 GEMM of "Announcing Humming:
-// Fast, Flexible Kernels for Quantized Inference" (sections "WnA16" and
-// "W8A8 / W4A8 / W4A4"): dequantization and scaling fused into the GEMM
-// (section "Shared CUDA components"), a task mapping per GEMM type for dense
-// and MoE work, scale / bias epilogues.  The design is gfx950's own.
-//
-// Two kernel families share the fragment, MFMA and epilogue code below:
-//
-// * stream_kernel (decode, one 16-row tile): KW wave64s of a workgroup split
-//   the K range of the same WN 16-column sub-tiles.  Weights stream from HBM
-//   straight into a register ring PF K-blocks deep (one 16-byte load per
-//   lane per sub-tile and K-block -- the packed layout puts exactly each
-//   lane's MFMA operand there); the activation rows and the weight metadata
-//   of the K range are staged in LDS once.  No barrier until the final
-//   in-workgroup reduction through LDS.
-// * tile_kernel (prefill): 4 waves side by side along N share a 16*WM-row
-//   activation tile.  Each K-block's activation tile (XOR swizzled so the
-//   operand reads are conflict free) and metadata are copied global -> LDS
-//   by buffer-load-to-LDS DMA, one or two K-blocks ahead; each wave loads
-//   its own weight fragments straight into registers and dequantizes them
-//   there.  Workgroups are ordered so that the tiles one XCD runs at a time
-//   share activation rows and weight columns in its L2.
-//
-// Formats:
-//   F_INT          INT4/UINT4 -> bf16 (128 + u) with one AND-OR per two
-//                  codes; a K-block accumulates in fp32 and
-//                  s * (P - (128 + z) * sum(a)) applies scale, zero point and
-//                  the offset (exact for integer codes).
-//   F_MXFP4_BF16   E2M1 with its E8M0 scale -> bf16 through
-//                  v_cvt_scalef32_pk_bf16_fp4 (exact), bf16 MFMA.
-//   F_FP8          E4M3 x E4M3 on the 16x16x128 f8f6f4 MFMA; per-token and
-//                  per-channel scales in the epilogue.
-//   F_MXFP4_MXFP8  E4M3 activations x E2M1 weights on the block-scaled
-//                  16x16x128 MFMA, both E8M0 scales as operands.
-//   F_MXFP4_MXFP4  E2M1 activations x E2M1 weights (W4A4) on the same
-//                  MFMA; prefill-tile kernel only.
-//   F_FP8_BF16     E4M3 weights x bf16 activations (W8A16): the hardware
-//                  FP8 -> bf16 conversion (exact), bf16 MFMA, per-channel
-//                  scales in the epilogue.
-//   F_INT8_BF16    INT8 weights x bf16 activations (W8A16): bytes widened
-//                  through f32 (exact), the FP8 path's layout and epilogue.
-//   F_NVFP4_BF16   NVFP4: E2M1 -> f32, times its E4M3 scale per 16 (exact: at
-//                  most 6 significant bits) -> bf16.
-//   F_MXINT4_BF16  MXINT4: INT4 with an E8M0 scale per 32 -> f32 -> bf16
-//                  (exact), the MX path's scale staging.
-//   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
-//                  K-block (128) at a time, each K-block's result scaled by
-//                  the row's group scale times the 128 x 128 weight-block
-//                  scale (acc += sa * sw * P); prefill-tile kernel only.
-//
-// Split-K across workgroups writes fp32 partials; a separate reduce kernel
-// sums them in split order (deterministic) and applies the epilogue.
-// Partial sums are never rounded below fp32 (the accuracy loss through a bf16
-// Stream-K reduction, issue #31 in the senn-tech.com review, is what this
-// avoids).
-#include "dev_common.h"
-#include "hum_internal.h"
+// Quantized GEMM launch: kernel instance lookup, split-K reduce instances,
+// and the INT row-sum pre-pass.  The kernels (stream_kernel, tile_kernel,
+// splitk_reduce_kernel) are templates in gemm_kernels.h; their compiled
+// instances are listed in the inst_*.hip translation units.
+#include "gemm_kernels.h"
 
-#include <type_traits>
+#include <mutex>
+#include <vector>
 
 namespace hum {
-
-template <int FMT>
-struct Tr {
-  static constexpr int kAElem = fmt_bf16_act(FMT) ? 2 : 1;  // activation bytes (FP4: 1/2)
-  static constexpr bool kA4 = (FMT == F_MXFP4_MXFP4);                           // 4-bit activations
-  static constexpr int kARowB = kA4 ? 64 : 128 * kAElem;                        // activation bytes per row per K-block
-  static constexpr int kBWords =
-      (FMT == F_FP8 || FMT == F_FP8_BLOCK || fmt_w8_bf16(FMT)) ? 2 : 1;  // 16-B words / lane / K-block
-  static constexpr bool kBf16 = fmt_bf16_act(FMT);
-  // MX / NVFP4 weight scales: a metadata row (a dword per lane) covers
-  // 1 << kMetaRowShift K-blocks (E8M0 per 32: 4; NVFP4's two E4M3 per 32: 2)
-  static constexpr int kMetaRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
-  // bytes of an activation row of `ld` elements
-  static __device__ __forceinline__ int64_t row_bytes(int64_t ld) { return kA4 ? ld / 2 : ld * kAElem; }
-};
-
-// ---------------------------------------------------------------------------
-// Weight fragments
-
-template <int FMT>
-struct BFrag {
-  u32x4_t w[Tr<FMT>::kBWords];
-  // raw metadata words as loaded (decoded where the fragment is used, so
-  // that no arithmetic waits on a load where it is issued)
-  uint32_t meta;  // INT: dword holding the column's scale; MX: E8M0 codes of 4 K-blocks
-  uint32_t zero;  // INT: dword holding the column's zero-point nibble
-};
-
-struct WPtrs {
-  const uint8_t* codes;
-  const uint8_t* meta;
-  const uint8_t* zero;
-};
-
-// Buffer resources over the weight stripe of one 16-column sub-tile (its
-// codes and metadata for the whole K).  A fragment outside the stripe -- a
-// K-block past the end of the wave's range, or a sub-tile past N (range 0)
-// -- is read at an offset beyond the range: the hardware returns zeros and
-// touches no memory.  So every weight load is unconditional (a load inside a
-// branch makes the compiler wait for all outstanding loads where the branch
-// rejoins, which would serialize the prefetch ring) and costs nothing when
-// unused.
-struct WStripe {
-  __amdgpu_buffer_rsrc_t codes, meta, zero;
-};
-
-constexpr uint32_t kOob = 0x80000000u;  // beyond every stripe (stripes are < 2 GiB)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// The same descriptor as four words, for LDS DMA issued from inline assembly.
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
-}
-
-// LDS DMA (buffer_load ... lds): lane l's 16 (4) bytes at byte offset voff of
-// the buffer land at lds + 16 l (4 l).  Issued from inline assembly so that
-// the compiler keeps no count of it and adds no waits of its own for the
-// LDS it writes: the kernel waits itself (s_waitcnt vmcnt), knowing which
-// copies it needs.  The instruction has no register result, so nothing of
-// the asm statement is left in flight but the copy itself.
-__device__ __forceinline__ uint32_t lds_addr(const void* lds) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
-}
-__device__ __forceinline__ void dma_b128(u32x4_t r, const void* lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(r) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_b32(u32x4_t r, const void* lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds_addr(lds)), "v"(voff), "s"(r) : "memory", "m0");
-}
-
-template <int FMT>
-__device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs& w, int nt, bool valid) {
-  constexpr int kCB = 16 * Tr<FMT>::kBWords;  // code bytes per lane per K-block
-  const int64_t ntc = valid ? nt : 0;
-  WStripe s;
-  const int64_t cb = (int64_t)p.kb_count * 64 * kCB;
-  s.codes = make_rsrc(w.codes + ntc * cb, valid ? cb : 0);
-  s.meta = s.codes;
-  s.zero = s.codes;
-  if (FMT == F_INT) {
-    const int64_t sb = (int64_t)p.ng * 16 * (p.scale_f32 ? 4 : 2);
-    s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
-    const int64_t zb = (int64_t)p.ng * 8;
-    s.zero = make_rsrc(w.zero + ntc * zb, (valid && p.has_zero) ? zb : 0);
-  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
-    const int64_t sb = (int64_t)p.kb4 * 256;
-    s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
-  }
-  return s;
-}
-
-// Loads of one weight fragment (K-block kb of the stripe; zeros when !ok).
-// META = false loads the codes only (the caller holds the metadata).
-template <int FMT, bool META = true>
-__device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe& s, bool ok, int kb, int lane) {
-  constexpr int kCB = 16 * Tr<FMT>::kBWords;
-  BFrag<FMT> f;
-  const uint32_t co = ok ? (uint32_t)(kb * 64 + lane) * kCB : kOob;
-#pragma unroll
-  for (int i = 0; i < Tr<FMT>::kBWords; ++i) f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(s.codes, co + 16 * i, 0, 0);
-  f.meta = 0;
-  f.zero = 0;
-  if (META && FMT == F_INT) {
-    const int c16 = lane & 15;
-    // floor(kb / kb_per_group), exact in fp32: kb < 2^14, and the quotient
-    // of (kb + 1/2) sits at least 1/(2 kb_per_group) from an integer
-    const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-    // bf16 scales: the dword holding the pair of column c16; f32: its dword
-    // (arithmetic rather than a select on the uniform format flag, which
-    // the compiler would turn into a branch around the load)
-    const int sf = p.scale_f32;
-    const uint32_t so = ok ? (uint32_t)(gi * 16 + (c16 & (14 | sf))) << (1 + sf) : kOob;
-    f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
-    const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
-    f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
-  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16)) {
-    const uint32_t mo = ok ? (uint32_t)((kb >> Tr<FMT>::kMetaRowShift) * 64 + lane) * 4 : kOob;
-    f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
-  }
-  return f;
-}
-
-// INT metadata words of one K-block of a stripe (zeros when !ok): the
-// scale dword and zero-point dword of column lane & 15.
-__device__ __forceinline__ BFrag<F_INT> load_b_meta_int(const GemmParams& p, const WStripe& s, bool ok, int kb,
-                                                        int lane) {
-  BFrag<F_INT> f;
-  const int c16 = lane & 15;
-  const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-  const int sf = p.scale_f32;
-  const uint32_t so = ok ? (uint32_t)(gi * 16 + (c16 & (14 | sf))) << (1 + sf) : kOob;
-  f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
-  const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
-  f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
-  return f;
-}
-
-// Decoders of a fragment's metadata words.  The INT scale of column c16 is
-// (raw << sh) & mk: f32 scales sh = 0, mk = ~0; bf16 pairs take the low
-// half (sh = 16) for even columns and the high half (mk = 0xFFFF0000) for
-// odd ones.
-struct IntScaleSel {
-  uint32_t sh, mk;
-};
-__device__ __forceinline__ IntScaleSel int_scale_sel(const GemmParams& p, int c16) {
-  const bool half = p.scale_f32 == 0;
-  return IntScaleSel{(half && !(c16 & 1)) ? 16u : 0u, (half && (c16 & 1)) ? 0xFFFF0000u : 0xFFFFFFFFu};
-}
-__device__ __forceinline__ float frag_int_scale(uint32_t raw, const IntScaleSel& sel) {
-  return __uint_as_float((raw << sel.sh) & sel.mk);
-}
-__device__ __forceinline__ int frag_int_zero(uint32_t raw, int c16) { return (int)((raw >> (4 * (c16 & 7))) & 0xF); }
-__device__ __forceinline__ uint32_t frag_mx_code(uint32_t raw, int kb) { return (raw >> (8 * (kb & 3))) & 0xFF; }
-
-// (x & mask) | magic in one instruction.  gfx9 encodes no literal in the
-// three-operand form, so with the constants in sight the compiler would
-// split it into two literal-carrying ones.  The empty asm statements (they
-// emit nothing) hide the constants: the mask then rides in an SGPR and the
-// magic in a VGPR, and the operation stays ordinary compiler-scheduled code,
-// whose hazards against matrix instructions in flight the compiler tracks
-// (a VALU instruction written in asm is outside that tracking).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  asm("" : "+s"(mask));
-  asm("" : "+v"(magic));
-  return (x & mask) | magic;
-}
-
-__device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, g = 0x43004300u;
-  u32x4_t o;
-  o[0] = and_or(w, m, g);
-  o[1] = and_or(w >> 4, m, g);
-  o[2] = and_or(w >> 8, m, g);
-  o[3] = and_or(w >> 12, m, g);
-  return __builtin_bit_cast(bf16x8_t, o);
-}
-
-__device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
-  u32x4_t o;
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-  return __builtin_bit_cast(bf16x8_t, o);
-}
-
-// A finite E4M3 code (OCP FP8: bias 7, subnormal quantum 2^-9) as f32.
-__device__ __forceinline__ float e4m3_scale_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return (c & 0x80u) ? -mag : mag;
-}
-
-// Byte i of w as a signed integer, in f32.
-__device__ __forceinline__ float i8_to_f32(uint32_t w, int i) { return (float)(int)(int8_t)(w >> (8 * i)); }
-// bf16 bits of lo in the low half, of hi in the high half, by truncation.
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// Eight E2M1 codes (low nibble first) times an E4M3 group scale -> bf16.
-// The hardware's scaled FP4 conversion applies only a power-of-two scale, so
-// the codes are widened to f32 unscaled and multiplied by the full scale:
-// exact (at most 6 significant bits), hence also exact when packed to bf16
-// by taking each f32's upper half.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16x8_t nv_dequant(uint32_t w, float scale) {
-  const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  u32x4_t o;
-  o[0] = pack_hi16(r0[0] * scale, r0[1] * scale);
-  o[1] = pack_hi16(r1[0] * scale, r1[1] * scale);
-  o[2] = pack_hi16(r2[0] * scale, r2[1] * scale);
-  o[3] = pack_hi16(r3[0] * scale, r3[1] * scale);
-  return __builtin_bit_cast(bf16x8_t, o);
-}
-
-// bf16 B operand of the 4 k-steps of a K-block.
-template <int FMT>
-__device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, int kb, bf16x8_t (&d)[4]) {
-  if (FMT == F_INT) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) d[s] = int_dequant(f.w[0][s]);
-  } else if (FMT == F_FP8_BF16) {
-    // E4M3 -> bf16 is exact (3 mantissa bits, exponents within bf16's
-    // range): the hardware conversion with a unit scale, two codes per
-    // instruction; k-step s takes bytes 8s .. 8s+7 of the lane's 32
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t w0 = f.w[s >> 1][2 * (s & 1)], w1 = f.w[s >> 1][2 * (s & 1) + 1];
-      u32x4_t o;
-      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-      d[s] = __builtin_bit_cast(bf16x8_t, o);
-    }
-  } else if (FMT == F_MXINT4_BF16) {
-    // MXINT4: the integer path's nibble order (k-step s in dword s, element
-    // j at bit (j & 1) * 16 + (j >> 1) * 4) holding q + 8; (u - 8) * 2^E is
-    // one exact FMA in f32, packed to bf16 by its upper half (at most 4
-    // significant bits)
-    const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
-    const float off = -8.0f * fs;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t w = f.w[0][s];
-      u32x4_t o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lo = __builtin_fmaf((float)((w >> (4 * i)) & 15u), fs, off);
-        const float hi = __builtin_fmaf((float)((w >> (16 + 4 * i)) & 15u), fs, off);
-        o[i] = pack_hi16(lo, hi);
-      }
-      d[s] = __builtin_bit_cast(bf16x8_t, o);
-    }
-  } else if (FMT == F_NVFP4_BF16) {
-    // k-steps 2h and 2h + 1 (k = 32 lg + 16 h + [0, 16)) share the E4M3
-    // scale in byte 2 (kb & 1) + h of the lane's word
-    const uint32_t half = meta >> (16 * (kb & 1));
-    const float f0 = e4m3_scale_to_f32(half & 0xFF), f1 = e4m3_scale_to_f32((half >> 8) & 0xFF);
-    d[0] = nv_dequant(f.w[0][0], f0);
-    d[1] = nv_dequant(f.w[0][1], f0);
-    d[2] = nv_dequant(f.w[0][2], f1);
-    d[3] = nv_dequant(f.w[0][3], f1);
-  } else if (FMT == F_INT8_BF16) {
-    // INT8 -> bf16 is exact (|q| <= 128): each byte sign-extended to f32,
-    // and two f32 packed by their upper halves (whose lower halves are zero
-    // for integers this small); same byte order as the FP8 branch
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t w0 = f.w[s >> 1][2 * (s & 1)], w1 = f.w[s >> 1][2 * (s & 1) + 1];
-      u32x4_t o;
-      o[0] = pack_hi16(i8_to_f32(w0, 0), i8_to_f32(w0, 1));
-      o[1] = pack_hi16(i8_to_f32(w0, 2), i8_to_f32(w0, 3));
-      o[2] = pack_hi16(i8_to_f32(w1, 0), i8_to_f32(w1, 1));
-      o[3] = pack_hi16(i8_to_f32(w1, 2), i8_to_f32(w1, 3));
-      d[s] = __builtin_bit_cast(bf16x8_t, o);
-    }
-  } else {
-    const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
-#pragma unroll
-    for (int s = 0; s < 4; ++s) d[s] = mx_dequant(f.w[0][s], fs);
-  }
-}
-
-__device__ __forceinline__ f32x4_t mfma_bf16_kblock(const bf16x8_t (&a)[4], const bf16x8_t (&b)[4], f32x4_t c) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b[s], c, 0, 0, 0);
-  return c;
-}
-
-template <int FMT>
-__device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, const BFrag<FMT>& f, uint32_t meta, int kb,
-                                                  f32x4_t c) {
-  i32x8_t b8;
-  b8[0] = f.w[0][0]; b8[1] = f.w[0][1]; b8[2] = f.w[0][2]; b8[3] = f.w[0][3];
-  if (FMT == F_FP8 || FMT == F_FP8_BLOCK) {
-    b8[4] = f.w[Tr<FMT>::kBWords - 1][0]; b8[5] = f.w[Tr<FMT>::kBWords - 1][1];
-    b8[6] = f.w[Tr<FMT>::kBWords - 1][2]; b8[7] = f.w[Tr<FMT>::kBWords - 1][3];
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 0, 0, 0, 127, 0, 127);
-  } else {
-    b8[4] = 0; b8[5] = 0; b8[6] = 0; b8[7] = 0;
-    // A format: E4M3 (0) or E2M1 (4, only the low 4 dwords of a8 are read)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, FMT == F_MXFP4_MXFP4 ? 4 : 0, 4, 0, sa, 0,
-                                                            (int)frag_mx_code(meta, kb));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Epilogue pieces
-
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
-
-// Column scale of the plain / scatter epilogues (per-channel FP8 scale and
-// the second-level scale); the per-token FP8 row scale is applied apart.
-template <int FMT>
-__device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, float gs) {
-  if (FMT == F_FP8 || fmt_w8_bf16(FMT)) return gs * reinterpret_cast<const float*>(wmeta)[col];
-  return gs;
-}
-
-// Stores of one 16x16 accumulator tile held in the MFMA C layout (lane holds
-// rows 4*lg + i of column c16) for the plain and scatter epilogues.
-template <int FMT, int EPI>
-__device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* wmeta, float gs, int64_t row_base,
-                                           int64_t col, const f32x4_t& v, int lg) {
-  if (col >= p.n) return;
-  uint16_t* out = static_cast<uint16_t*>(p.out);
-  const float cs = col_scale<FMT>(wmeta, col, gs);
-  const float bias = (EPI == EPI_BF16 && p.bias) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row_base + 4 * lg + i;
-    if (row >= p.m) continue;
-    float x = v[i] * cs;
-    if (FMT == F_FP8) x *= reinterpret_cast<const float*>(p.a_scale)[row];
-    x += bias;
-    if (EPI == EPI_SCATTER) {
-      const int32_t f = p.sorted[row];
-      if (f >= p.sentinel) continue;
-      out[(int64_t)f * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
-    } else {
-      out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
-    }
-  }
-}
-
-// SwiGLU epilogue of a gate / up tile pair in the C layout.
-__device__ __forceinline__ void store_swiglu_bf16(const GemmParams& p, float gs, int64_t row_base, int64_t col,
-                                                  const f32x4_t& g, const f32x4_t& u, int lg) {
-  if (col >= p.n) return;
-  uint16_t* out = static_cast<uint16_t*>(p.out);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row_base + 4 * lg + i;
-    if (row >= p.m) continue;
-    out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(silu_f32(g[i] * gs) * (u[i] * gs));
-  }
-}
-
-// SwiGLU + MXFP8 requantization of 32 columns: two gate / up tile pairs.
-// The 16 lanes of a DPP row hold the 16 columns of the same 4 rows, so the
-// block absolute maximum is a row reduction.
-__device__ __forceinline__ void store_swiglu_mxfp8(const GemmParams& p, float gs, int64_t row_base, int64_t col0,
-                                                   const f32x4_t& g0, const f32x4_t& u0, const f32x4_t& g1,
-                                                   const f32x4_t& u1, int lg, int c16) {
-  uint8_t* outq = static_cast<uint8_t*>(p.out);
-  uint8_t* outs = static_cast<uint8_t*>(p.out_scale);
-  const bool ok = (col0 - c16) < p.n;  // whole 32-column block valid (I % 32 == 0)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row_base + 4 * lg + i;
-    const float a0 = silu_f32(g0[i] * gs) * (u0[i] * gs);
-    const float a1 = silu_f32(g1[i] * gs) * (u1[i] * gs);
-    const float amax = row16_max(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
-    const int e = mx_scale_code(amax);
-    const float inv = mx_inv_scale(e);
-    const uint32_t q = f32x2_to_e4m3x2(a0 * inv, a1 * inv);
-    if (ok && row < p.m) {
-      outq[row * p.ldo + col0] = (uint8_t)(q & 0xFF);
-      outq[row * p.ldo + col0 + 16] = (uint8_t)(q >> 8);
-      if (c16 == 0) outs[row * (p.ldo / 32) + (col0 - c16) / 32] = (uint8_t)e;
-    }
-  }
-}
-
-// SwiGLU + MXFP4 requantization of 32 columns (W4A4): as the MXFP8 one,
-// with E2M1 codes two per byte (even column in the low nibble): the lane of
-// an even column takes its odd neighbour's code across the DPP quad and
-// stores the byte.
-__device__ __forceinline__ void store_swiglu_mxfp4(const GemmParams& p, float gs, int64_t row_base, int64_t col0,
-                                                   const f32x4_t& g0, const f32x4_t& u0, const f32x4_t& g1,
-                                                   const f32x4_t& u1, int lg, int c16) {
-  uint8_t* outq = static_cast<uint8_t*>(p.out);
-  uint8_t* outs = static_cast<uint8_t*>(p.out_scale);
-  const bool ok = (col0 - c16) < p.n;  // whole 32-column block valid (I % 32 == 0)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row_base + 4 * lg + i;
-    const float a0 = silu_f32(g0[i] * gs) * (u0[i] * gs);
-    const float a1 = silu_f32(g1[i] * gs) * (u1[i] * gs);
-    const float amax = row16_max(__builtin_fmaxf(__builtin_fabsf(a0), __builtin_fabsf(a1)));
-    const int e = mx_scale_code_emax(amax, 2);
-    const float inv = mx_inv_scale(e);
-    const uint32_t q0 = f32_to_e2m1(a0 * inv), q1 = f32_to_e2m1(a1 * inv);
-    const uint32_t n0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q0, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    const uint32_t n1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q1, 0xB1, 0xF, 0xF, false);
-    if (ok && row < p.m && (c16 & 1) == 0) {
-      uint8_t* rq = outq + row * (p.ldo / 2);
-      rq[col0 / 2] = (uint8_t)(q0 | (n0 << 4));
-      rq[(col0 + 16) / 2] = (uint8_t)(q1 | (n1 << 4));
-      if (c16 == 0) outs[row * (p.ldo / 32) + (col0 - c16) / 32] = (uint8_t)e;
-    }
-  }
-}
-
-// Partial tile (fp32, natural [split][row][col] layout) of one 16x16 C tile.
-__device__ __forceinline__ void store_partial(const GemmParams& p, int split, int64_t row_base, int64_t col,
-                                              int64_t ncols, const f32x4_t& v, int lg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row_base + 4 * lg + i;
-    if (row >= p.m) continue;
-    if (p.sorted && p.sorted[row] >= p.sentinel) continue;
-    p.partials[((int64_t)split * p.m + row) * ncols + col] = v[i];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Decode kernel: one 16-row tile (at most 16 valid rows) of WN 16-column
-// sub-tiles, KW compute waves splitting the workgroup's K range.
-//
-// The activation rows of the K range and the weight metadata (scales, zero
-// points, E8M0 rows) are staged in LDS; each wave's only other loads are
-// its weight ring, PF K-blocks deep, whose slots it consumes as they land
-// (vector-memory loads complete in order).  Dense workgroups stage wave by
-// wave (each wave copies its own contiguous K-blocks with plain loads issued
-// ahead of its ring); MoE workgroups gather their rows through a loader wave
-// with LDS-DMA.  Rows >= the valid count are never stored; their fragments
-// repeat row 0 (an output row depends on its own A row alone).  LDS row
-// layout per K-block: 16-byte chunks XOR-swizzled with the row, so the 16
-// rows of one fragment read hit 16 different bank groups.  The KW partial
-// sums are added in a fixed order through LDS at the end.
-
-template <int FMT>
-struct StreamLds {
-  static constexpr int kRowB = 128 * Tr<FMT>::kAElem;  // bytes per row per K-block
-};
-
-// Waves of a stream workgroup: KW compute waves, plus a loader wave where
-// the activation rows are gathered (MoE).  Dense workgroups stage their
-// activations wave by wave and need none.
-// (MXFP8 activations carry per-32 scales, which the loader wave stages.)
-constexpr bool stream_self_staged(int fmt, int amode, int epi) {
-  return amode == A_DIRECT && epi == EPI_BF16 && fmt != F_MXFP4_MXFP8;
-}
-constexpr int stream_waves(int fmt, int kw, int amode, int epi) {
-  return kw + (stream_self_staged(fmt, amode, epi) ? 0 : 1);
-}
-
-template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
-__global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
-  using T = Tr<FMT>;
-  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
-  static_assert(EPI != EPI_SWIGLU_MXFP4 && FMT != F_MXFP4_MXFP4, "W4A4 runs on the tile kernel only");
-  static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
-  static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
-  constexpr int kRowB = StreamLds<FMT>::kRowB;
-  constexpr int kCPR = kRowB / 16;
-  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-  __shared__ int s_nrows;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, lg = lane >> 4;
-
-  // grid (n-tile, m-tile, split): no index arithmetic
-  const int tn = (int)blockIdx.x;
-  const int tm = (int)blockIdx.y;
-  const int split = (int)blockIdx.z;
-
-  int expert = 0;
-  if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
-    expert = p.block_expert[tm];
-    if (expert < 0) return;
-  }
-  const int64_t row0 = tm * 16;
-  WPtrs wp;
-  wp.codes = p.codes + (int64_t)expert * p.codes_per_expert;
-  wp.meta = p.wscale + (int64_t)expert * p.scales_per_expert;
-  // without zero points the (unused) zero loads read the scale array
-  wp.zero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : wp.meta;
-  const float gs = p.gscale[expert];
-
-  int nts[WN];
-  bool ntv[WN];
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) {
-    if constexpr (kSwiglu) {
-      const int ntg = tn * (WN / 2) + ns % (WN / 2);
-      ntv[ns] = ntg * 16 < p.n;
-      nts[ns] = ntg + (ns >= WN / 2 ? p.swiglu_nt_off : 0);
-    } else {
-      nts[ns] = tn * WN + ns;
-      ntv[ns] = nts[ns] < p.nt_count;
-    }
-  }
-
-  const int kb_begin = split * p.kb_per_split;
-  int kb_end = kb_begin + p.kb_per_split;
-  if (kb_end > p.kb_count) kb_end = p.kb_count;
-  const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
-  constexpr bool kSelf = stream_self_staged(FMT, AMODE, EPI);
-  // Self-staged (dense) workgroups give compute wave w the contiguous
-  // K-blocks [kw0, kw0 + nj); otherwise wave w takes kb_begin + w, + KW, ...
-  // (wave KW, the loader, takes none).
-  int kw0, nj;
-  if constexpr (kSelf) {
-    const int per = (nkb + KW - 1) / KW;
-    kw0 = kb_begin + wave * per;
-    const int kw1 = kw0 + per < kb_end ? kw0 + per : kb_end;
-    nj = kw1 > kw0 ? kw1 - kw0 : 0;
-  } else {
-    kw0 = kb_begin + wave;
-    nj = (wave < KW && kw0 < kb_end) ? (kb_end - kw0 + KW - 1) / KW : 0;
-  }
-  // the wave's j-th K-block (j < nj + PF; it matters only for j < nj)
-  auto kb_at = [&](int j) { return kSelf ? kw0 + j : kw0 + j * KW; };
-
-  // The loader wave finds the source row of each tile row (-1: padding /
-  // past the end) and stages the activation rows of the K range into LDS
-  // with LDS-DMA loads; the compute waves issue their weight rings (the
-  // loader's range is empty, so its ring loads return zeros at once).
-  WStripe st[WN];
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) st[ns] = make_stripe<FMT>(p, wp, nts[ns], ntv[ns]);
-  // first scale group / first 4-K-block E8M0 row of the K range (the LDS
-  // metadata starts there)
-  const int g0 = (FMT == F_INT) ? kb_begin / p.kb_per_group : 0;
-  constexpr int kRS = T::kMetaRowShift;
-  const int r0 = kb_begin >> kRS;
-  auto stage = [&]() {
-    // source row of tile row `lane` (lanes 0..15; -1: padding / past the end)
-    int src = -1;
-    if (lane < 16) {
-      const int64_t row = row0 + lane;
-      if (AMODE == A_GATHER) {
-        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-        if (f < p.sentinel) src = f / p.topk;
-      } else if (row < p.m) {
-        // grouped rows in sorted order: padding slots (sentinel) are skipped
-        src = (p.sorted && p.sorted[row] >= p.sentinel) ? -1 : (int)row;
-      }
-    }
-    // rows [0, nr) are stored (dense: rows < m are a prefix; MoE: the valid
-    // rows of a block are a prefix).  Direct rows are row0 + r; gathered
-    // ones are read from lane r.
-    const int nr = __builtin_popcountll(__builtin_amdgcn_ballot_w64(src >= 0));
-    if (lane == 0) s_nrows = nr;
-    if (nr == 0) return;
-    auto src_row = [&](int r) -> int64_t {
-      if constexpr (AMODE == A_GATHER) return __builtin_amdgcn_ds_bpermute(r << 2, src);
-      return row0 + r;
-    };
-    // x / nr for x < 2^14 (nr <= 16) as a multiply-shift: exact while
-    // x * nr < 2^20
-    const uint32_t mnr = ((1u << 20) + nr - 1) / nr;
-    // LDS: activation slots (rounded up to whole 64-lane DMA instructions),
-    // then the MX scale dwords (likewise rounded).  Each DMA instruction
-    // fills 64 consecutive 16-byte slots; slot s of the layout
-    // [K-block][row][swizzled chunk] holds logical chunk phys ^ swizzle(row).
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a, p.a_bytes);
-    const int slots = nr * kCPR * nkb;
-#pragma unroll 1
-    for (int base = 0; base < slots; base += 64) {
-      const int sidx = base + lane;
-      const int phys = sidx & (kCPR - 1);
-      const uint32_t rowkb = (uint32_t)sidx / kCPR;
-      const int kbl = (int)((rowkb * mnr) >> 20);
-      const int r = (int)rowkb - kbl * nr;
-      const int c = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
-      const int64_t sr = src_row(r < nr ? r : 0);
-      // lanes past `slots` fill unused slots of the footprint from offset 0
-      // (always a valid address): no reliance on range checking
-      const uint32_t voff = sidx < slots
-                                ? (uint32_t)((sr * p.lda + (int64_t)(kb_begin + kbl) * 128) * T::kAElem + c * 16)
-                                : 0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dsm + base * 16, 16, voff, 0, 0, 0);
-    }
-    if (FMT == F_MXFP4_MXFP8) {
-      const int scale_off = ((slots + 63) & ~63) * 16;
-      const __amdgpu_buffer_rsrc_t rsc = make_rsrc(p.a_scale, p.a_scale_bytes);
-      const int n4 = nr * nkb;
-#pragma unroll 1
-      for (int base = 0; base < n4; base += 64) {
-        const int sidx = base + lane;
-        const int kbl = (int)(((uint32_t)sidx * mnr) >> 20);
-        const int r = sidx - kbl * nr;
-        const int64_t sr = src_row(r < nr ? r : 0);
-        const uint32_t voff = sidx < n4 ? (uint32_t)(sr * p.a_scale_ld + (int64_t)(kb_begin + kbl) * 4) : 0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, dsm + scale_off + base * 4, 4, voff, 0, 0, 0);
-      }
-    }
-    // weight metadata of the K range, per valid sub-tile (filler lanes read
-    // the stripe's first bytes, which always exist)
-    if (FMT == F_INT && nkb > 0) {
-      const int g1 = (kb_end - 1) / p.kb_per_group + 1;
-      const int ss = p.scale_f32 ? 4 : 2;
-      const int n16 = (g1 - g0) * ss;  // 16-byte slots of scales
-      const int n4 = (g1 - g0) * 2;    // 4-byte slots of zero points
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        if (!ntv[ns]) continue;
-        uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
-        // (resources copied to locals: a captured array member passed to
-        // the LDS-DMA builtin makes the host pass drop the kernel's stub)
-        const __amdgpu_buffer_rsrc_t rm = st[ns].meta, rz = st[ns].zero;
-#pragma unroll 1
-        for (int base = 0; base < n16; base += 64) {
-          const int sl = base + lane;
-          const uint32_t voff = sl < n16 ? (uint32_t)(g0 * 16 * ss + sl * 16) : 0u;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, mb + base * 16, 16, voff, 0, 0, 0);
-        }
-        if (p.has_zero) {
-#pragma unroll 1
-          for (int base = 0; base < n4; base += 64) {
-            const int sl = base + lane;
-            const uint32_t voff = sl < n4 ? (uint32_t)(g0 * 8 + sl * 4) : 0u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, mb + p.lds_zero_off + base * 4, 4, voff, 0, 0, 0);
-          }
-        }
-      }
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nkb > 0) {
-      const int n16 = (((kb_end + (1 << kRS) - 1) >> kRS) - r0) * 16;  // 16-byte slots of scale rows
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        if (!ntv[ns]) continue;
-        uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
-        const __amdgpu_buffer_rsrc_t rm = st[ns].meta;
-#pragma unroll 1
-        for (int base = 0; base < n16; base += 64) {
-          const int sl = base + lane;
-          const uint32_t voff = sl < n16 ? (uint32_t)(r0 * 256 + sl * 16) : 0u;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, mb + base * 16, 16, voff, 0, 0, 0);
-        }
-      }
-    }
-  };
-  BFrag<FMT> ring[PF][WN];
-  auto issue_ring = [&]() {
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT, false>(p, st[ns], q < nj, kb_at(q), lane);
-      // issue slot by slot, in the order of use (they land in issue order)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Loader path (gathered rows): the rings go out first, the loader wave
-  // looks the rows up and DMAs them, and waits for its DMA inside its own
-  // branch (the compiler waits for every outstanding vector-memory load
-  // before an LDS read that follows an LDS-DMA it cannot prove finished, so
-  // the wait must close the branch).
-  auto stage_via_loader = [&]() {
-    issue_ring();
-    if (wave == KW) {
-      stage();
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
-  };
-  auto self_stage = [&](int nr) {
-    const int nch = nj * nr * kCPR;                  // 16-byte activation chunks (<= 512)
-    const int slot0 = (kw0 - kb_begin) * nr * kCPR;  // first LDS slot of the wave's K-blocks
-    const uint32_t mnr = ((1u << 20) + nr - 1) / nr; // x / nr as a multiply-shift (x * nr < 2^20)
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-    u32x4_t abuf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = i * 64 + lane;
-      const uint32_t rowkb = (uint32_t)c / kCPR;
-      const int kbl = (int)((rowkb * mnr) >> 20);
-      const int r = (int)rowkb - kbl * nr;
-      const int phys = c & (kCPR - 1);
-      const int lc = T::kBf16 ? (phys ^ r) : (phys ^ ((r >> 1) & 7));
-      const uint32_t off = (uint32_t)(((row0 + r) * p.lda + (int64_t)(kw0 + kbl) * 128) * T::kAElem + lc * 16);
-      abuf[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off : kOob, 0, 0);
-    }
-    // weight metadata of the wave's K-blocks (INT: scales and zero points of
-    // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
-    constexpr int kML =
-        (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
-    u32x4_t mbuf[WN][kML > 0 ? kML : 1];
-    uint32_t zbuf[WN];
-    int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
-    if (FMT == F_INT && nj > 0) {
-      const int g0w = kw0 / p.kb_per_group, g1w = (kw0 + nj - 1) / p.kb_per_group + 1;
-      const int ss = p.scale_f32 ? 4 : 2;
-      mb0 = g0w * 16 * ss;
-      mbytes = (g1w - g0w) * 16 * ss;  // <= 1 KB
-      mdst = (g0w - g0) * 16 * ss;
-      zb0 = g0w * 8;
-      zbytes = p.has_zero ? (g1w - g0w) * 8 : 0;  // <= 256 B
-      zdst = p.lds_zero_off + (g0w - g0) * 8;
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nj > 0) {
-      const int rw0 = kw0 >> kRS, rw1 = (kw0 + nj + (1 << kRS) - 1) >> kRS;
-      mb0 = rw0 * 256;
-      mbytes = (rw1 - rw0) * 256;  // <= 2 KB
-      mdst = (rw0 - r0) * 256;
-    }
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-#pragma unroll
-      for (int i = 0; i < kML; ++i) {
-        const int b = (i * 64 + lane) * 16;
-        mbuf[ns][i] = __builtin_amdgcn_raw_buffer_load_b128(st[ns].meta, b < mbytes ? (uint32_t)(mb0 + b) : kOob, 0, 0);
-      }
-      if (FMT == F_INT)
-        zbuf[ns] = __builtin_amdgcn_raw_buffer_load_b32(st[ns].zero,
-                                                        lane * 4 < zbytes ? (uint32_t)(zb0 + lane * 4) : kOob, 0, 0);
-    }
-    issue_ring();
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i * 64 + lane < nch) *reinterpret_cast<u32x4_t*>(dsm + (slot0 + i * 64 + lane) * 16) = abuf[i];
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-      uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
-#pragma unroll
-      for (int i = 0; i < kML; ++i)
-        if ((i * 64 + lane) * 16 < mbytes) *reinterpret_cast<u32x4_t*>(mb + mdst + (i * 64 + lane) * 16) = mbuf[ns][i];
-      if (FMT == F_INT && lane * 4 < zbytes) *reinterpret_cast<uint32_t*>(mb + zdst + lane * 4) = zbuf[ns];
-    }
-  };
-
-  int nrows = 0;
-  if constexpr (kSelf) {
-    // Each wave copies the activation rows and weight metadata of its own
-    // K-blocks into their places of the workgroup's LDS layout with plain
-    // loads issued ahead of its ring (vector-memory loads land in issue
-    // order, so the copy waits for them alone), then reads only what it
-    // wrote: no barrier, no loader.  Rows < m of the tile are a prefix.
-    nrows = p.m - row0 < 16 ? (int)(p.m - row0) : 16;
-    self_stage(nrows);
-  } else {
-    stage_via_loader();
-    nrows = s_nrows;
-  }
-
-  const int scale_off = ((nrows * kCPR * nkb + 63) & ~63) * 16;
-
-  f32x4_t acc[WN];
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) acc[ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const bool arow_ok = c16 < nrows;
-  const int rr = arow_ok ? c16 : 0;  // LDS row read (row 0 stands in for empty rows)
-  const IntScaleSel ssel = int_scale_sel(p, c16);
-  // raw metadata words of sub-tile ns at K-block kb, from the LDS copy
-  auto lds_meta = [&](int ns, int kb, uint32_t& m, uint32_t& z) {
-    const uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
-    m = 0;
-    z = 0;
-    if (FMT == F_INT) {
-      const int gl = (int)(((float)kb + 0.5f) * p.inv_kbg) - g0;
-      const int sf = p.scale_f32;
-      m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
-      const uint32_t zr = *reinterpret_cast<const uint32_t*>(mb + p.lds_zero_off + gl * 8 + ((c16 >> 3) << 2));
-      z = p.has_zero ? zr : 0u;
-    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
-      m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> kRS) - r0) * 64 + lane) * 4);
-    }
-  };
-
-  for (int j0 = 0; j0 < nj; j0 += PF) {
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int j = j0 + q;
-      if (j < nj) {
-        const int kb = kb_at(j);
-        const uint8_t* ab = dsm + ((kb - kb_begin) * nrows + rr) * kRowB;
-        if constexpr (T::kBf16) {
-          // (rows >= nrows read row 0: an output row depends on its own A
-          // row alone, and those rows are never stored)
-          bf16x8_t af[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            af[s] = *reinterpret_cast<const bf16x8_t*>(ab + (((4 * lg + s) ^ rr) * 16));
-          f32x4_t rs = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (FMT == F_INT) {
-            // row sums of the K-block in the C layout: A x ones
-            const u32x4_t o = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-            const bf16x8_t one = __builtin_bit_cast(bf16x8_t, o);
-            const bf16x8_t on[4] = {one, one, one, one};
-            rs = mfma_bf16_kblock(af, on, rs);
-          }
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns) {
-            bf16x8_t d[4];
-            uint32_t mw, zw;
-            lds_meta(ns, kb, mw, zw);
-            dequant_b<FMT>(ring[q][ns], mw, kb, d);
-            if (FMT == F_INT) {
-              const f32x4_t t = mfma_bf16_kblock(af, d, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-              const float sc = frag_int_scale(mw, ssel);
-              const float off = (float)(p.int_offset + frag_int_zero(zw, c16));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(sc, __builtin_fmaf(-off, rs[i], t[i]), acc[ns][i]);
-            } else {
-              acc[ns] = mfma_bf16_kblock(af, d, acc[ns]);
-            }
-          }
-        } else {
-          const int sw = (rr >> 1) & 7;
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(ab + ((lg ^ sw) * 16));
-          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(ab + (((4 + lg) ^ sw) * 16));
-          int sa = 127;
-          if (FMT == F_MXFP4_MXFP8) {
-            const uint32_t sw4 = reinterpret_cast<const uint32_t*>(dsm + scale_off)[(kb - kb_begin) * nrows + rr];
-            sa = arow_ok ? (int)((sw4 >> (8 * lg)) & 0xFF) : 127;
-          }
-          i32x8_t a8;
-          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
-          a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns) {
-            uint32_t mw, zw;
-            lds_meta(ns, kb, mw, zw);
-            acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], mw, kb, acc[ns]);
-          }
-        }
-      }
-      // refill (past the end of the range the load returns zeros without
-      // touching memory)
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) ring[q][ns] = load_b<FMT, false>(p, st[ns], j + PF < nj, kb_at(j + PF), lane);
-    }
-  }
-
-  // in-workgroup reduction over the KW waves (fixed order), through the LDS
-  // that held the activations
-  if constexpr (KW > 1) {
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(dsm);
-    __syncthreads();
-    if (wave > 0 && wave < KW) {
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) red[((wave - 1) * WN + ns) * 64 + lane] = acc[ns];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 1; w < KW; ++w)
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        const f32x4_t v = red[((w - 1) * WN + ns) * 64 + lane];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[ns][i] += v[i];
-      }
-  }
-
-  if (p.split_k > 1) {
-    const int64_t ncols = kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-      if (!ntv[ns]) continue;
-      store_partial(p, split, row0, (int64_t)nts[ns] * 16 + c16, ncols, acc[ns], lg);
-    }
-    return;
-  }
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg);
-  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-#pragma unroll
-    for (int j = 0; j < WN / 2; ++j)
-      store_swiglu_bf16(p, gs, row0, (int64_t)nts[j] * 16 + c16, acc[j], acc[j + WN / 2], lg);
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < WN / 4; ++jj)
-      store_swiglu_mxfp8(p, gs, row0, (int64_t)nts[2 * jj] * 16 + c16, acc[2 * jj], acc[2 * jj + WN / 2],
-                         acc[2 * jj + 1], acc[2 * jj + 1 + WN / 2], lg, c16);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Prefill kernel: a (16 WM) x (64 WN) output tile per workgroup of 4 waves;
-// wave w owns columns [16 WN w, 16 WN (w + 1)) of the tile for all its rows.
-//
-// Every K-block's activation tile (16 WM rows, 16-byte chunks XOR-swizzled
-// with the row), with the MXFP8 scale words of its rows and each wave's
-// metadata words (INT scale dwords or E8M0 rows), goes from global memory
-// straight into LDS by LDS-DMA, kS - 1 K-blocks ahead of its use.  Each
-// wave's weight-code fragments (private to the wave) go straight into
-// registers, one register set per stage.  A K-block step is: issue the
-// copies of K-block j + kS - 1, compute K-block j, wait until this wave's
-// copies of K-block j + 1 have landed (with three stages the copies of
-// K-block j + 2 stay in flight), barrier.  With two stages the LDS copies
-// are issued from inline assembly, which the compiler does not track, and
-// every step ends with a full wait; with three they are issued through the
-// compiler's builtin into one LDS array per stage, so that the compiler's
-// own waits for the register fragments count them too.
-
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
-struct TileCfg {
-  using T = Tr<FMT>;
-  // pipeline stages (2 or 3): with two, a K-block's copy overlaps one
-  // K-block of compute; with three it has two K-blocks of compute to land
-  static constexpr int kS = S;
-  static constexpr int kTM = 16 * WM;
-  static constexpr int kTNS = 4 * WN;                            // weight sub-tiles per workgroup
-  static constexpr int kRowB = T::kARowB;                        // activation bytes per row per K-block
-  static constexpr int kCPR = kRowB / 16;                        // 16-byte chunks per row
-  static constexpr int kA = kTM * kRowB;                         // activation tile (whole KB)
-  static constexpr int kAI = kA / 1024;                          // its 1-KB DMA instructions
-  static constexpr int kAIW = (kAI + 3) / 4;                     // ... per wave
-  // a dword per row and K-block: MX scales (E8M0 per 32) or the f32 scale of
-  // a per-group FP8 row
-  static constexpr bool kX = (FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_FP8_BLOCK);
-  static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
-  static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
-  // Each wave loads its own weight fragments straight into registers,
-  // kS - 1 K-blocks ahead, one register set per stage (they are private to
-  // the wave: staging them through LDS would only add LDS traffic).
-  static constexpr bool kBReg = true;
-  static constexpr int kB = 0;
-  // Three stages issue their LDS copies through the compiler's builtin, so
-  // that its count of loads in flight includes them and its waits for the
-  // register fragments (two stages deep) are exact; two stages issue them
-  // from inline assembly and wait for everything at the end of each step.
-  static constexpr bool kTracked = (kS == 3);
-  static constexpr int kMI = (FMT == F_INT || FMT == F_FP8_BLOCK)
-                                 ? 1
-                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                                     FMT == F_NVFP4_BF16) ? WN : 0);
-  static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
-  static constexpr int kStage = kA + kXI * 256 + kB + kM;
-  static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
-  static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
-  static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
-  static_assert(kA % 1024 == 0, "whole 1-KB activation DMA instructions");
-  static_assert(kS * kStage <= 160 * 1024, "LDS budget");
-  static_assert(FMT != F_INT || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
-};
-
-// Physical 16-byte chunk of logical chunk c of LDS tile row r, for rows of
-// cpr chunks (16: bf16, 8: FP8, 4: FP4): the 16 rows of one fragment read
-// land on different banks.
-__device__ __forceinline__ int swz(int r, int c, int cpr) {
-  return cpr == 16 ? (c ^ (r & 15)) : (cpr == 8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3)));
-}
-
-// LDS of the pipeline: kS stages of kStage bytes, each holding the
-// activation tile, the per-row words, the code fragments and the metadata
-// words at fixed offsets.
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
-struct TileLds {
-  using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
-  // (three stages: one array each, so that the compiler can tell a copy
-  // into one stage from a read of another and adds no wait between them;
-  // the stage is a constant wherever this is called)
-  static __device__ __forceinline__ uint8_t* stage(int st) {
-    if constexpr (C::kTracked) {
-      __shared__ __attribute__((aligned(16))) uint8_t s0[C::kStage];
-      __shared__ __attribute__((aligned(16))) uint8_t s1[C::kStage];
-      __shared__ __attribute__((aligned(16))) uint8_t s2[C::kStage];
-      return st == 0 ? s0 : (st == 1 ? s1 : s2);
-    } else {
-      __shared__ __attribute__((aligned(16))) uint8_t v[C::kS * C::kStage];
-      return v + st * C::kStage;
-    }
-  }
-  static __device__ __forceinline__ uint8_t* m(int st) { return stage(st); }
-  static __device__ __forceinline__ uint8_t* a(int st) { return m(st) + C::kM; }
-  static __device__ __forceinline__ uint8_t* x(int st) { return a(st) + C::kA; }
-  static __device__ __forceinline__ uint8_t* b(int st) { return a(st) + C::kA + C::kXI * 256; }
-};
-
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
-__global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
-  using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
-  using T = typename C::T;
-  constexpr int kAE = T::kAElem;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, lg = lane >> 4;
-
-  // XCD-aware order: consecutive workgroup ids go round-robin over the 8
-  // XCDs; remap them so that each XCD walks a contiguous range of tiles.
-  // Within it, tiles go in groups of group_m M-tiles by all N-tiles, M
-  // fastest: the workgroups one XCD runs at a time then share both their
-  // activation rows and their weight columns through that XCD's L2.  (MoE
-  // M-tiles belong to different experts and take group_m = 1.)
-  const uint32_t nwg = gridDim.x;
-  uint32_t bid = blockIdx.x;
-  if (nwg % 8 == 0) bid = (bid % 8) * (nwg / 8) + bid / 8;
-  const int split = (int)(bid % (uint32_t)p.split_k);
-  bid /= (uint32_t)p.split_k;
-  int tn;
-  int64_t tm;
-  {
-    const uint32_t m_tiles = nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
-    const uint32_t per_group = (uint32_t)p.group_m * (uint32_t)p.n_tiles;
-    const uint32_t g = bid / per_group, r = bid % per_group;
-    const uint32_t m0 = g * (uint32_t)p.group_m;
-    const uint32_t gm = m_tiles - m0 < (uint32_t)p.group_m ? m_tiles - m0 : (uint32_t)p.group_m;
-    tm = m0 + r % gm;
-    tn = (int)(r / gm);
-  }
-
-  int expert = 0;
-  if (AMODE == A_GATHER || EPI == EPI_SCATTER) {
-    expert = p.block_expert[tm];
-    if (expert < 0) return;
-  }
-  const int64_t row0 = tm * C::kTM;
-  WPtrs wp;
-  wp.codes = p.codes + (int64_t)expert * p.codes_per_expert;
-  wp.meta = p.wscale + (int64_t)expert * p.scales_per_expert;
-  // without zero points the (unused) zero words come from the scale array
-  wp.zero = p.wzero ? p.wzero + (int64_t)expert * p.zeros_per_expert : wp.meta;
-  const float gs = p.gscale[expert];
-
-  int nts[WN];
-  bool ntv[WN];
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) {
-    if constexpr (C::kSwiglu) {
-      const int ntg = tn * (C::kTNS / 2) + wn * (WN / 2) + ns % (WN / 2);
-      ntv[ns] = ntg * 16 < p.n;
-      nts[ns] = ntg + (ns >= WN / 2 ? p.swiglu_nt_off : 0);
-    } else {
-      nts[ns] = tn * C::kTNS + wn * WN + ns;
-      ntv[ns] = nts[ns] < p.nt_count;
-    }
-  }
-
-  const int kb_begin = split * p.kb_per_split;
-  int kb_end = kb_begin + p.kb_per_split;
-  if (kb_end > p.kb_count) kb_end = p.kb_count;
-  const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
-
-  // --- DMA sources (every lane always gets a valid address: rows past the
-  // end or padding read row 0 / slot 0, whose outputs are never stored) ---
-  auto src_row = [&](int r) -> int64_t {
-    const int64_t row = row0 + r;
-    if (AMODE == A_GATHER) {
-      const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-      return f < p.sentinel ? (int64_t)(f / p.topk) : 0;
-    }
-    return row < p.m ? row : 0;
-  };
-  // each buffer resource twice: as words for the inline-assembly copies and
-  // as the builtin's type for the tracked ones
-  const u32x4_t ra = rsrc_words(p.a, p.a_bytes);
-  const __amdgpu_buffer_rsrc_t rar = make_rsrc(p.a, p.a_bytes);
-  uint32_t a_off[C::kAIW];  // activation chunk of this lane in each of the wave's instructions (K-block 0)
-  // (every wave issues kAIW instructions; with fewer than 4 in the tile,
-  // waves repeat one -- same bytes to the same place -- so that the count of
-  // DMAs in flight is the same on every path, which the compiler's waits
-  // rely on)
-#pragma unroll
-  for (int i = 0; i < C::kAIW; ++i) {
-    const int ins = (wn + 4 * i) % C::kAI;
-    const int slot = ins * 64 + lane;
-    const int r = slot / C::kCPR;
-    const int lc = swz(r, slot % C::kCPR, C::kCPR);
-    a_off[i] = (uint32_t)(src_row(r) * T::row_bytes(p.lda) + lc * 16);
-  }
-  u32x4_t rx = ra;
-  __amdgpu_buffer_rsrc_t rxr = rar;
-  uint32_t x_off[C::kXI > 0 ? C::kXI : 1];
-  if constexpr (C::kX) {
-    rx = rsrc_words(p.a_scale, p.a_scale_bytes);
-    rxr = make_rsrc(p.a_scale, p.a_scale_bytes);
-#pragma unroll
-    for (int i = 0; i < C::kXI; ++i) {
-      const int r = i * 64 + lane < C::kTM ? i * 64 + lane : 0;
-      const int64_t sr = src_row(r);
-      x_off[i] = (uint32_t)(sr * p.a_scale_ld);
-    }
-  }
-  __amdgpu_buffer_rsrc_t rbr[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
-#pragma unroll
-  for (int ns = 0; ns < WN; ++ns) {
-    const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
-    const uint8_t* base = wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb;
-    rbr[ns] = make_rsrc(base, cb);
-  }
-  // register-loaded fragments, one set per stage
-  BFrag<FMT> bA[WN], bB[WN], bC[WN];
-  // metadata words of the wave's sub-tiles.  INT: one copy per K-block, lane
-  // l takes scale dword l / WN (of 8 for bf16 scales, 16 for f32) of
-  // sub-tile l % WN, so that a lane finds its word of every sub-tile side by
-  // side (one vector read).  (Zero points enter through the offset terms
-  // after the K loop.)  MX: lane l its E8M0 word of each sub-tile.
-  u32x4_t rms = ra;
-  __amdgpu_buffer_rsrc_t rmsr = rar;
-  const int sf = p.scale_f32;
-  uint32_t mi_off = 0, mi_gmul = 0;
-  if constexpr (FMT == F_INT) {
-    rms = rsrc_words(wp.meta, p.scales_per_expert);
-    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
-    const int nsw = (8 << sf) * WN;  // scale words (<= 64)
-    const int ww = lane < nsw ? lane : 0;
-    const int sub = ww % WN, d = ww / WN;
-    const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
-    mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
-    mi_gmul = 16u * (2u << sf);
-  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                       FMT == F_NVFP4_BF16) {
-    rms = rsrc_words(wp.meta, p.scales_per_expert);
-    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
-  } else if constexpr (FMT == F_FP8_BLOCK) {
-    // lane l < WN copies the f32 block scale of sub-tile l (per K-block)
-    rms = rsrc_words(wp.meta, p.scales_per_expert);
-    rmsr = make_rsrc(wp.meta, p.scales_per_expert);
-    uint32_t ntl = 0;
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns)
-      if (lane == ns && ntv[ns]) ntl = (uint32_t)nts[ns];
-    mi_off = ntl * (uint32_t)p.kb_count * 4u;
-  }
-
-  // copies of K-block kb into stage st (this wave's share) and its weight
-  // fragments into registers bdst
-  using St = TileLds<FMT, WM, WN, AMODE, EPI, S>;
-  // LDS DMA: inline assembly (untracked) or the builtin (tracked)
-  using LdsPtr = __attribute__((address_space(3))) void*;
-  auto dma16 = [&](const u32x4_t& rw, __amdgpu_buffer_rsrc_t rr, uint8_t* lds, uint32_t voff) -> void {
-    if constexpr (C::kTracked)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)lds, 16, voff, 0, 0, 0);
-    else
-      dma_b128(rw, lds, voff);
-  };
-  auto dma4 = [&](const u32x4_t& rw, __amdgpu_buffer_rsrc_t rr, uint8_t* lds, uint32_t voff) -> void {
-    if constexpr (C::kTracked)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (LdsPtr)lds, 4, voff, 0, 0, 0);
-    else
-      dma_b32(rw, lds, voff);
-  };
-  auto issue = [&](int kb, int st, BFrag<FMT>* bdst) -> void {
-#pragma unroll
-    for (int i = 0; i < C::kAIW; ++i) {
-      const int ins = (wn + 4 * i) % C::kAI;
-      dma16(ra, rar, St::a(st) + ins * 1024, a_off[i] + (uint32_t)kb * C::kRowB);
-    }
-    // per-row words: every wave copies them all (same bytes, same place)
-    if constexpr (C::kX) {
-#pragma unroll
-      for (int i = 0; i < C::kXI; ++i)
-        dma4(rx, rxr, St::x(st) + i * 256, x_off[i] + (uint32_t)kb * 4);
-    }
-    {
-      // (compiler-tracked loads.  A lane's kBWords 16-byte words sit side
-      // by side in the packed layout.)
-      const uint32_t boff = (uint32_t)kb * C::kCB + lane * 16 * T::kBWords;
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns)
-#pragma unroll
-        for (int h = 0; h < T::kBWords; ++h)
-          bdst[ns].w[h] = __builtin_amdgcn_raw_buffer_load_b128(rbr[ns], boff + h * 16, 0, 0);
-      // (the offset stays live past the loads: no load's destination
-      // reuses the register another load reads its address from)
-      asm volatile("" ::"v"(boff));
-    }
-    uint8_t* mw = St::m(st) + wn * C::kMI * 256;
-    if constexpr (FMT == F_INT) {
-      const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-      dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
-    } else if constexpr (FMT == F_FP8_BLOCK) {
-      dma4(rms, rmsr, mw, mi_off + (uint32_t)kb * 4u);
-    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                         FMT == F_NVFP4_BF16) {
-      // a metadata row covers 4 K-blocks (E8M0 per 32) or 2 (NVFP4: two
-      // E4M3 per 32 of a lane)
-      constexpr int kRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) {
-        dma4(rms, rmsr, mw + ns * 256,
-             ((uint32_t)((ntv[ns] ? nts[ns] : 0) * p.kb4 + (kb >> kRowShift)) * 64 + lane) * 4);
-      }
-    }
-    // keep the issue ahead of the compute (the waits count on it)
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // this wave's copies into the next stage have landed, so that after the
-  // barrier every wave may read them.  Vector-memory loads complete in
-  // order; with three stages the wave has issued since then only the kIss
-  // loads of the stage after (the loop holds no other vector-memory
-  // access), which stay in flight; with two, everything is waited for.
-  // The compiler's own waits cover only this wave's reads of its own
-  // copies, hence this one.
-  constexpr int kIss = C::kAIW + C::kXI + WN * T::kBWords + C::kMI;
-  static_assert(kIss < 64, "vmcnt range");
-  constexpr int kAhead = C::kS == 3 ? kIss : 0;  // loads left in flight after the wait
-  auto wait_own = [&]() -> void {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((kAhead & 15) | ((kAhead >> 4) << 14) | (7 << 4) | (15 << 8));
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // workgroup barrier without a memory fence (the fence of __syncthreads()
-  // would wait for every DMA in flight, prefetches included); the empty asm
-  // keeps the compiler from moving memory accesses across it
-  auto barrier = [&]() -> void {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-  };
-
-  f32x4_t acc[WM][WN];
-#pragma unroll
-  for (int ms = 0; ms < WM; ++ms)
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const IntScaleSel ssel = int_scale_sel(p, c16);
-  auto compute = [&](int kb, int st, const BFrag<FMT>* bsrc) -> void {
-    const uint8_t* abase = St::a(st);
-    const uint8_t* bbase = St::b(st) + wn * WN * C::kCB;
-    const uint8_t* mbase = St::m(st) + wn * C::kMI * 256;
-    BFrag<FMT> bf[WN];
-    uint32_t mw[WN];
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-#pragma unroll
-      for (int h = 0; h < T::kBWords; ++h)
-        bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
-                               : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
-      mw[ns] = 0;
-      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
-        mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
-    }
-    if constexpr (FMT == F_FP8_BLOCK) {
-      // the WN block scales of this K-block, side by side
-      struct alignas(4 * WN) Words { float w[WN]; };
-      const Words sw = *reinterpret_cast<const Words*>(mbase);
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms) {
-        const int r = ms * 16 + c16;
-        const int swr = (r >> 1) & 7;
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + ((lg ^ swr) * 16));
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (((4 + lg) ^ swr) * 16));
-        i32x8_t a8;
-        a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
-        a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
-        // the f32 group scales of this lane's 4 output rows (C layout)
-        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(St::x(st) + (ms * 16 + 4 * lg) * 4);
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns) {
-          const f32x4_t t = mfma_f8_kblock<FMT>(a8, 127, bf[ns], 0u, kb, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[ms][ns][i] = __builtin_fmaf(sa[i] * sw.w[ns], t[i], acc[ms][ns][i]);
-        }
-      }
-      return;
-    }
-    if constexpr (FMT == F_INT) {
-      // this lane's scale words of the WN sub-tiles, side by side (one
-      // aligned vector read)
-      struct alignas(4 * WN) Words { uint32_t w[WN]; };
-      const Words sw = *reinterpret_cast<const Words*>(mbase + (sf ? c16 : (c16 >> 1)) * WN * 4);
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) mw[ns] = sw.w[ns];
-    }
-    if constexpr (T::kBf16) {
-      bf16x8_t d[WN][4];
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bf[ns], mw[ns], kb, d[ns]);
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms) {
-        const int r = ms * 16 + c16;
-        bf16x8_t af[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          af[s] = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + (((4 * lg + s) ^ c16) * 16));
-        if constexpr (FMT == F_INT) {
-          // one K-block of (128 + u) codes, scaled; the offset it carries
-          // is taken off after the K loop
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns) {
-            const f32x4_t t = mfma_bf16_kblock(af, d[ns], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
-            const float sc = frag_int_scale(mw[ns], ssel);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[ms][ns][i] = __builtin_fmaf(sc, t[i], acc[ms][ns][i]);
-          }
-        } else {
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_bf16_kblock(af, d[ns], acc[ms][ns]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms) {
-        const int r = ms * 16 + c16;
-        i32x8_t a8;
-        if constexpr (T::kA4) {
-          // 32 E2M1 codes of k = 32 lg + j: one 16-byte chunk
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (swz(r, lg, 4) * 16));
-          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
-          a8[4] = 0; a8[5] = 0; a8[6] = 0; a8[7] = 0;
-        } else {
-          const int sw = (r >> 1) & 7;
-          const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + ((lg ^ sw) * 16));
-          const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(abase + r * C::kRowB + (((4 + lg) ^ sw) * 16));
-          a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
-          a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
-        }
-        int sa = 127;
-        if (C::kX) sa = (int)((reinterpret_cast<const uint32_t*>(St::x(st))[r] >> (8 * lg)) & 0xFF);
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = mfma_f8_kblock<FMT>(a8, sa, bf[ns], mw[ns], kb, acc[ms][ns]);
-      }
-    }
-  };
-
-  if (nkb > 0) {
-    // K-block j uses stage j % kS and register set j % kS.  In the loop the
-    // copies are issued unconditionally (past the last K-block they re-read
-    // that block into a stage that is never consumed): the count of loads in
-    // flight is then the same on every path, which the explicit waits rely
-    // on.  The loop is unrolled kS times, so that every stage and register
-    // set is a constant and the accumulators stay in the same registers.
-    const int kb_last = kb_begin + nkb - 1;
-    auto kb_at = [&](int j) -> int { return kb_begin + j <= kb_last ? kb_begin + j : kb_last; };
-    if constexpr (C::kS == 2) {
-      issue(kb_at(0), 0, bA);
-      wait_own();
-      barrier();
-      int j = 0;
-      for (; j + 1 < nkb; j += 2) {
-        issue(kb_at(j + 1), 1, bB);
-        compute(kb_begin + j, 0, bA);
-        wait_own();
-        barrier();
-        issue(kb_at(j + 2), 0, bA);
-        compute(kb_begin + j + 1, 1, bB);
-        wait_own();
-        barrier();
-      }
-      if (j < nkb) compute(kb_begin + j, 0, bA);
-    } else {
-      issue(kb_at(0), 0, bA);
-      issue(kb_at(1), 1, bB);
-      wait_own();
-      barrier();
-      int j = 0;
-      for (; j + 2 < nkb; j += 3) {
-        issue(kb_at(j + 2), 2, bC);
-        compute(kb_begin + j, 0, bA);
-        wait_own();
-        barrier();
-        issue(kb_at(j + 3), 0, bA);
-        compute(kb_begin + j + 1, 1, bB);
-        wait_own();
-        barrier();
-        issue(kb_at(j + 4), 1, bB);
-        compute(kb_begin + j + 2, 2, bC);
-        wait_own();
-        barrier();
-      }
-      // one or two K-blocks left, their copies issued: nothing more to
-      // issue, so wait for everything
-      if (j < nkb) {
-        compute(kb_begin + j, 0, bA);
-        if (j + 1 < nkb) {
-          __builtin_amdgcn_s_waitcnt(0);
-          barrier();
-          compute(kb_begin + j + 1, 1, bB);
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
-
-  if constexpr (FMT == F_INT) {
-    // The K loop summed s * (128 + u) a per K-block; the offset part,
-    // sum over K-blocks of s (offset + z) * (sum of the block's a), is one
-    // more small product, taken here on the MFMA: row sums (A) times the
-    // weight's offset terms (B, stored negated) with K running over
-    // K-blocks, each operand as a bf16 hi / lo pair (hi*hi + hi*lo + lo*hi).
-    // The first split adds the whole of it.
-    if (split == 0) {
-      const int64_t mt16 = (p.m + 15) / 16;
-      const int64_t rs_half = mt16 * p.kbc * 1024;
-      const int64_t co_half = (int64_t)p.nt_count * p.kbc * 1024;
-      const uint8_t* cob = p.wco + (int64_t)expert * p.co_per_expert;
-      for (int cc = 0; cc < p.kbc; ++cc) {
-        bf16x8_t ch[WN], cl[WN];
-#pragma unroll
-        for (int ns = 0; ns < WN; ++ns) {
-          const int64_t o = (((int64_t)(ntv[ns] ? nts[ns] : 0) * p.kbc + cc) * 64 + lane) * 16;
-          ch[ns] = *reinterpret_cast<const bf16x8_t*>(cob + o);
-          cl[ns] = *reinterpret_cast<const bf16x8_t*>(cob + co_half + o);
-        }
-#pragma unroll
-        for (int ms = 0; ms < WM; ++ms) {
-          const int64_t mt = row0 / 16 + ms;
-          if (mt >= mt16) break;  // rows past m: never stored
-          const int64_t o = ((mt * p.kbc + cc) * 64 + lane) * 16;
-          const bf16x8_t rh = *reinterpret_cast<const bf16x8_t*>(p.a_rowsum + o);
-          const bf16x8_t rl = *reinterpret_cast<const bf16x8_t*>(p.a_rowsum + rs_half + o);
-#pragma unroll
-          for (int ns = 0; ns < WN; ++ns) {
-            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, ch[ns], acc[ms][ns], 0, 0, 0);
-            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, cl[ns], acc[ms][ns], 0, 0, 0);
-            acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, ch[ns], acc[ms][ns], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  if (p.split_k > 1) {
-    const int64_t ncols = C::kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
-#pragma unroll
-    for (int ns = 0; ns < WN; ++ns) {
-      if (!ntv[ns]) continue;
-#pragma unroll
-      for (int ms = 0; ms < WM; ++ms)
-        store_partial(p, split, row0 + ms * 16, (int64_t)nts[ns] * 16 + c16, ncols, acc[ms][ns], lg);
-    }
-    return;
-  }
-#pragma unroll
-  for (int ms = 0; ms < WM; ++ms) {
-    const int64_t rb = row0 + ms * 16;
-    if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
-#pragma unroll
-      for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, rb, (int64_t)nts[ns] * 16 + c16, acc[ms][ns], lg);
-    } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-#pragma unroll
-      for (int j = 0; j < WN / 2; ++j)
-        store_swiglu_bf16(p, gs, rb, (int64_t)nts[j] * 16 + c16, acc[ms][j], acc[ms][j + WN / 2], lg);
-    } else if constexpr (EPI == EPI_SWIGLU_MXFP4) {
-#pragma unroll
-      for (int jj = 0; jj < WN / 4; ++jj)
-        store_swiglu_mxfp4(p, gs, rb, (int64_t)nts[2 * jj] * 16 + c16, acc[ms][2 * jj], acc[ms][2 * jj + WN / 2],
-                           acc[ms][2 * jj + 1], acc[ms][2 * jj + 1 + WN / 2], lg, c16);
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < WN / 4; ++jj)
-        store_swiglu_mxfp8(p, gs, rb, (int64_t)nts[2 * jj] * 16 + c16, acc[ms][2 * jj], acc[ms][2 * jj + WN / 2],
-                           acc[ms][2 * jj + 1], acc[ms][2 * jj + 1 + WN / 2], lg, c16);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Split-K reduce + epilogue: one thread per (row, 32-column block) for the
-// MXFP8 epilogue, per (row, 8 columns) otherwise.  Partials are summed in
-// split order.
-
-template <int FMT, int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p, int block_m) {
-  static_assert(EPI != EPI_SWIGLU_MXFP4, "no split-K for the MXFP4 SwiGLU epilogue");
-  constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
-  constexpr int kCols = (EPI == EPI_SWIGLU_MXFP8) ? 32 : 8;
-  const int64_t ncols = kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
-  const int64_t outc = p.n;
-  const int64_t cpr = (outc + kCols - 1) / kCols;
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= p.m * cpr) return;
-  const int64_t row = id / cpr;
-  const int64_t c0 = (id % cpr) * kCols;
-  int expert = 0;
-  if (p.sorted) {
-    if (p.sorted[row] >= p.sentinel) return;
-    expert = p.block_expert[row / block_m];
-  }
-  const float gs = p.gscale[expert];
-  const uint8_t* wmeta = p.wscale + (int64_t)expert * p.scales_per_expert;
-  float v[kCols], u[kCols];
-#pragma unroll
-  for (int i = 0; i < kCols; ++i) v[i] = u[i] = 0.0f;
-  // The loads are unconditional (columns past the end re-read the last
-  // column, whose sums are never stored): a branch around each load would
-  // make the compiler wait for it before the next one.  Four splits' loads
-  // go out together.
-  int cc[kCols];
-#pragma unroll
-  for (int i = 0; i < kCols; ++i) cc[i] = (int)(c0 + i < outc ? c0 + i : outc - 1);
-#pragma unroll 4
-  for (int s = 0; s < p.split_k; ++s) {
-    const float* src = p.partials + ((int64_t)s * p.m + row) * ncols;
-#pragma unroll
-    for (int i = 0; i < kCols; ++i) {
-      v[i] += src[cc[i]];
-      if (kSwiglu) u[i] += src[cc[i] + p.n];
-    }
-  }
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-    const int64_t orow = (EPI == EPI_SCATTER) ? (int64_t)p.sorted[row] : row;
-    const float rsc = (FMT == F_FP8) ? reinterpret_cast<const float*>(p.a_scale)[row] : 1.0f;
-    uint32_t h[kCols];
-#pragma unroll
-    for (int i = 0; i < kCols; ++i) {
-      float x = v[i] * col_scale<FMT>(wmeta, cc[i], gs) * rsc;
-      if (EPI == EPI_BF16 && p.bias) x += bf16_bits_to_f32(p.bias[cc[i]]);
-      h[i] = f32_to_bf16_bits(x);
-    }
-    uint16_t* dst = out + orow * p.ldo + c0;
-    if (c0 + kCols <= outc && ((uintptr_t)dst & 15) == 0) {
-      // a whole 16-byte group: one store
-      u32x4_t w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = h[2 * i] | (h[2 * i + 1] << 16);
-      *reinterpret_cast<u32x4_t*>(dst) = w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < kCols; ++i)
-        if (c0 + i < outc) dst[i] = (uint16_t)h[i];
-    }
-  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-#pragma unroll
-    for (int i = 0; i < kCols; ++i)
-      if (c0 + i < outc) out[row * p.ldo + c0 + i] = (uint16_t)f32_to_bf16_bits(silu_f32(v[i] * gs) * (u[i] * gs));
-  } else {
-    float a[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      a[i] = silu_f32(v[i] * gs) * (u[i] * gs);
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(a[i]));
-    }
-    const int e = mx_scale_code(amax);
-    const float inv = mx_inv_scale(e);
-    uint8_t* outq = static_cast<uint8_t*>(p.out) + row * p.ldo + c0;
-#pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      const uint32_t q = f32x2_to_e4m3x2(a[i] * inv, a[i + 1] * inv);
-      outq[i] = (uint8_t)(q & 0xFF);
-      outq[i + 1] = (uint8_t)(q >> 8);
-    }
-    static_cast<uint8_t*>(p.out_scale)[row * (p.ldo / 32) + c0 / 32] = (uint8_t)e;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Row sums of bf16 activations per K-block (the INT prefill offset term), as
@@ -1655,106 +53,7 @@ hum_status launch_rowsum(const void* a, int64_t lda, int64_t m, int kb_count, in
 }
 
 // ---------------------------------------------------------------------------
-// Instances.
-
-typedef void (*gemm_fn)(const GemmParams);
-typedef void (*reduce_fn)(const GemmParams, int);
-
-struct Instance {
-  KernelKey key;
-  gemm_fn fn;
-  int threads;
-};
-
-#define HUM_STREAM(F, WN, KW, PF, AM, EP) \
-  {{F, KIND_STREAM, 1, WN, 1, KW, AM, EP, 0}, stream_kernel<F, WN, KW, PF, AM, EP>, 64 * stream_waves(F, KW, AM, EP)}
-#define HUM_TILE_S(F, WM, WN, AM, EP, S) \
-  {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
-#define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
-
-// Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
-// half as many).  A CU keeps about 64-128 KB of weights in flight.
-#define HUM_PF(F, n) (((F) == F_FP8 || fmt_w8_bf16(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
-#define HUM_DENSE_SET(F)                                   \
-  HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
-  HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \
-  HUM_STREAM(F, 2, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
-  HUM_STREAM(F, 2, 15, HUM_PF(F, 4), A_DIRECT, EPI_BF16),  \
-  HUM_STREAM(F, 4, 8, HUM_PF(F, 4), A_DIRECT, EPI_BF16),   \
-  HUM_STREAM(F, 4, 15, HUM_PF(F, 2), A_DIRECT, EPI_BF16),  \
-  HUM_STREAM(F, 1, 4, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
-  HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 2, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 4, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 4, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 8, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE_S(F, 2, 2, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 2, 4, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 4, 2, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
-
-// Tile instances only (formats without a decode-kernel path)
-#define HUM_DENSE_TILE_SET(F)                              \
-  HUM_TILE(F, 1, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 2, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 2, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 4, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 4, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 8, 2, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE(F, 8, 4, A_DIRECT, EPI_BF16),                   \
-  HUM_TILE_S(F, 2, 2, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 2, 4, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 4, 2, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 4, 4, A_DIRECT, EPI_BF16, 3),              \
-  HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
-
-// Tile-only MoE instances (W4A4)
-#define HUM_MOE_TILE_SET(F, EPI_UP)                        \
-  HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 8, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 1, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 2, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 4, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 8, 4, A_DIRECT, EPI_SCATTER)
-
-#define HUM_MOE_SET(F, EPI_UP)                             \
-  HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
-  HUM_STREAM(F, 4, 8, 4, A_DIRECT, EPI_SCATTER),           \
-  HUM_STREAM(F, 4, 15, 2, A_GATHER, EPI_UP),               \
-  HUM_STREAM(F, 4, 15, 2, A_DIRECT, EPI_SCATTER),          \
-  HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 4, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 8, 4, A_GATHER, EPI_UP),                     \
-  HUM_TILE(F, 1, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 2, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 4, 4, A_DIRECT, EPI_SCATTER),                \
-  HUM_TILE(F, 8, 4, A_DIRECT, EPI_SCATTER)
-
-static const Instance kInstances[] = {
-    HUM_DENSE_SET(F_INT),
-    HUM_DENSE_SET(F_FP8),
-    HUM_DENSE_SET(F_MXFP4_BF16),
-    HUM_DENSE_SET(F_MXFP4_MXFP8),
-    HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
-    HUM_DENSE_TILE_SET(F_FP8_BLOCK),
-    HUM_DENSE_SET(F_FP8_BF16),
-    HUM_DENSE_SET(F_INT8_BF16),
-    HUM_DENSE_SET(F_NVFP4_BF16),
-    HUM_DENSE_SET(F_MXINT4_BF16),
-    HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_GATHER, EPI_SWIGLU_BF16),
-    HUM_STREAM(F_MXFP4_BF16, 2, 8, 4, A_DIRECT, EPI_SCATTER),
-    HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_GATHER, EPI_SWIGLU_BF16),
-    HUM_STREAM(F_MXFP4_BF16, 2, 15, 4, A_DIRECT, EPI_SCATTER),
-    HUM_MOE_SET(F_MXFP4_BF16, EPI_SWIGLU_BF16),
-    HUM_MOE_SET(F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8),
-    HUM_MOE_TILE_SET(F_MXFP4_MXFP4, EPI_SWIGLU_MXFP4),
-};
+// Split-K reduce instances and the launcher.
 
 struct ReduceInstance {
   int fmt, epi;
@@ -1776,19 +75,33 @@ static const ReduceInstance kReduces[] = {
     {F_MXINT4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXINT4_BF16, EPI_BF16>},
     {F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SWIGLU_MXFP8>},
     {F_MXFP4_MXFP8, EPI_SCATTER, splitk_reduce_kernel<F_MXFP4_MXFP8, EPI_SCATTER>},
+#define HUM_MOE_REDUCES(F) {F, EPI_SWIGLU_BF16, splitk_reduce_kernel<F, EPI_SWIGLU_BF16>}, \
+                           {F, EPI_SCATTER, splitk_reduce_kernel<F, EPI_SCATTER>}
+    HUM_MOE_REDUCES(F_FP8),
+    HUM_MOE_REDUCES(F_FP8_BLOCK),
+    HUM_MOE_REDUCES(F_FP8_BF16),
+    HUM_MOE_REDUCES(F_INT8_BF16),
+    HUM_MOE_REDUCES(F_NVFP4_BF16),
+    HUM_MOE_REDUCES(F_MXINT4_BF16),
+#undef HUM_MOE_REDUCES
 };
 
-static bool g_big_lds[sizeof(kInstances) / sizeof(kInstances[0])];
-
 static const Instance* find_instance(const KernelKey& k) {
-  for (const Instance& in : kInstances) {
-    const KernelKey& q = in.key;
-    if (q.fmt == k.fmt && q.kind == k.kind && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n &&
-        q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi && q.stages == k.stages)
-      return &in;
-  }
+  static const InstanceTable tables[] = {instances_dense_a(), instances_dense_b(), instances_moe_a(),
+                                         instances_moe_b(), instances_moe_c()};
+  for (const InstanceTable& t : tables)
+    for (int i = 0; i < t.n; ++i) {
+      const KernelKey& q = t.p[i].key;
+      if (q.fmt == k.fmt && q.kind == k.kind && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n &&
+          q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi && q.stages == k.stages)
+        return &t.p[i];
+    }
   return nullptr;
 }
+
+// Stream kernels whose dynamic-LDS limit was raised (once per kernel).
+static std::mutex g_lds_mu;
+static std::vector<const void*> g_big_lds;
 
 bool gemm_instance_exists(const KernelKey& key) { return find_instance(key) != nullptr; }
 
@@ -1801,6 +114,7 @@ bool reduce_instance_exists(int fmt, int epi) {
 hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_tiles, int block_m, void* stream) {
   GemmParams p = p_in;
   if (p.group_m < 1) p.group_m = 1;
+  p.a_gather = key.amode == A_GATHER;
   const Instance* in = find_instance(key);
   if (!in)
     return set_error(HUM_ERR_UNSUPPORTED,
@@ -1839,12 +153,14 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
     dyn = (size_t)(L.total > red ? L.total : red);
     if ((int64_t)dyn > kStreamLdsMax) return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per split too long for LDS");
     if (dyn > 64 * 1024) {
-      const int idx = (int)(in - kInstances);
-      if (!g_big_lds[idx]) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(in->fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)kStreamLdsMax) != hipSuccess)
+      const void* fn = reinterpret_cast<const void*>(in->fn);
+      std::lock_guard<std::mutex> lock(g_lds_mu);
+      bool raised = false;
+      for (const void* q : g_big_lds) raised = raised || q == fn;
+      if (!raised) {
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax) != hipSuccess)
           return set_error(HUM_ERR_HIP, "cannot raise the LDS limit of the stream kernel");
-        g_big_lds[idx] = true;
+        g_big_lds.push_back(fn);
       }
     }
   }

@@ -84,8 +84,11 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
                          void* packed, void* stream);
 hum_status launch_dequant(const hum_weight_desc* d, const Layout& L, const void* packed,
                           float* out, void* stream);
+// sorted / sentinel (optional): rows r with sorted[r] >= sentinel (padding
+// slots of grouped rows) are skipped.
 hum_status launch_quant_fp8_token(int64_t m, int64_t k, const void* x, int64_t ldx,
-                                  void* q, float* s, void* stream);
+                                  void* q, float* s, void* stream, const int32_t* sorted = nullptr,
+                                  int32_t sentinel = 0);
 // counts / max_m (optional): quantize only the live rows of a grouped_masked
 // buffer (row r is live when r % max_m < counts[r / max_m]).
 hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
@@ -93,11 +96,15 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
 hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
                               uint8_t* s, void* stream, const int32_t* counts = nullptr, int64_t max_m = 0);
 hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
-                                  void* stream);
+                                  void* stream, const int32_t* sorted = nullptr, int32_t sentinel = 0);
 hum_status launch_zero(void* p, size_t bytes, void* stream);
 hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
                         int32_t block_m, int32_t* sorted, int32_t* offsets, int32_t* counts,
                         int32_t* block_expert, int64_t nblocks, void* stream);
+// block_expert[b] = the expert whose padded segment (align's offsets[E+1])
+// holds rows b*block_m.., or -1 past the last segment.
+hum_status launch_block_expert(const int32_t* offsets, int32_t e, int32_t block_m, int64_t nblocks,
+                               int32_t* block_expert, void* stream);
 // grouped_masked layout: sorted[e * max_m + i] = that position when
 // i < clamp(counts[e], 0, max_m), else the sentinel E * max_m; block b of
 // block_m rows belongs to expert b * block_m / max_m, or -1 when all its
@@ -148,10 +155,12 @@ struct GemmParams {
   const int32_t* block_expert;
   int topk;
   int sentinel;
+  int a_gather;       // rows gathered through sorted (set from the kernel key by launch_gemm)
   // outputs
   void* out;
   int64_t ldo;        // elements
   void* out_scale;    // MXFP8 epilogue scales, [rows][ldo/32]
+  float* swiglu_f32;  // SwiGLU epilogues (optional): the fp32 values stored / requantized, [rows][n]
   const uint16_t* bias;
   float* partials;    // split-K partials, [split][m][columns] fp32
   int split_k;

@@ -59,10 +59,22 @@ def tol_stats(gpu, ref):
     return rel, mx
 
 
-def assert_tol(gpu, ref, what=""):
+def assert_tol(gpu, ref, what="", max_rel=MAX_REL):
     rel, mx = tol_stats(gpu, ref)
-    assert rel <= REL_FRO and mx <= MAX_REL, f"{what}: relFro={rel:.3e} maxrel={mx:.3e}"
+    assert rel <= REL_FRO and mx <= max_rel, f"{what}: relFro={rel:.3e} maxrel={mx:.3e}"
     return rel, mx
+
+
+# Elementwise bound for MoE layers whose SwiGLU output is requantized to
+# per-token / per-group FP8 (a layer of two GEMMs, not one): the FP8 x FP8
+# matrix instruction accumulates a 128-deep dot product below fp32
+# precision (measured: at most 2.2e-4 of the row's largest value, checked by
+# test_fp8_mfma_accumulation_error), and where that moves a SwiGLU value
+# across an E4M3 rounding boundary the requantized element changes by one
+# E4M3 step (up to 1/8 of itself).  Each GEMM stage alone, fed identical
+# inputs, meets the 1e-2 bound; the layer's relative Frobenius bound stays
+# 5e-3.
+MAX_REL_FP8_REQUANT_LAYER = 2.5e-2
 
 
 def assert_bf16_exact(gpu, ref, what=""):

@@ -72,7 +72,7 @@ def _layer(seed, e, h, inter, act):
 @pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 @pytest.mark.parametrize("t", [1, 9, 70])
 def test_moe_layer_every_tile(act, tile, t):
-    e, h, inter, k = 8, 256, 128, 2
+    e, h, inter, k = 8, 1024, 512, 2
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(700, e, h, inter, act)
     ids, wts = synth.routing(701 + t, t, e, k)
     xb = synth.bf16_normal(synth.rng(702 + t), (t, h))
@@ -114,7 +114,7 @@ def test_moe_stream_wave_n2_bf16():
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
 def test_moe_skewed_and_empty_experts(act):
-    e, h, inter, k, t = 16, 256, 128, 4, 200
+    e, h, inter, k, t = 16, 1024, 512, 4, 200
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(720, e, h, inter, act)
     ids, wts = synth.routing(721, t, e, k, zipf_s=1.5)
     ids[:, 0] = 3                                  # one expert gets every token
@@ -152,7 +152,7 @@ def test_moe_single_expert_equals_dense_chain():
 def test_moe_default_selection_every_regime(act, t):
     """The selector's choices over the rows-per-expert range (decode kernel,
     16-row tiles, decode gate_up with a tiled down GEMM, larger tiles)."""
-    e, h, inter, k = 8, 256, 128, 2
+    e, h, inter, k = 8, 1024, 512, 2
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(740, e, h, inter, act)
     ids, wts = synth.routing(741 + t, t, e, k)
     xb = synth.bf16_normal(synth.rng(742 + t), (t, h))
@@ -197,7 +197,7 @@ def _check_masked(out, ref, valid, what):
 @pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_moe_masked_every_tile(act, tile):
-    e, h, inter, max_m = 8, 256, 128, 128
+    e, h, inter, max_m = 8, 1024, 512, 128
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(720, e, h, inter, act)
     xb, cnt, out = _masked_case(721, e, max_m, h, [128, 0, 1, 17, 33, 140, 5, 100])
     print(f"case moe masked act={act} tile={tile}", flush=True)
@@ -215,7 +215,7 @@ def test_moe_masked_every_tile(act, tile):
 @pytest.mark.parametrize("expected_m", [1, 20, 200])
 def test_moe_masked_selector(act, expected_m):
     """Default tiles from expected_m; max_m = 48 makes 64-row tiles step down."""
-    e, h, inter, max_m = 8, 256, 128, 48
+    e, h, inter, max_m = 8, 1024, 512, 48
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(730, e, h, inter, act)
     g = synth.rng(731 + expected_m)
     xb, cnt, out = _masked_case(732 + expected_m, e, max_m, h, g.integers(0, max_m + 1, size=e))

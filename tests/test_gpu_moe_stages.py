@@ -1,0 +1,193 @@
+"""GPU: the two grouped GEMMs of a MoE layer as stages (hum_moe_grouped_gemm)
+over hum_moe_align's sorted order, against the oracle.
+
+* Exact-integer cases: integer activations, E2M1 codes with E8M0 scales of
+  1 and 1/2, so every product and partial sum is a multiple of 1/4 far
+  below 2^24 -- fp32 accumulation is exact in any order, and the bf16
+  outputs must equal bf16(oracle) bit for bit.  Gate_up (gathered rows) and
+  down (rows in sorted order) with the plain and scatter epilogues, on every
+  compiled MoE tile, and each expert's rows also against hum_linear on that
+  expert alone.
+* The SwiGLU epilogues' rounding / MX requantization bit for bit: gate
+  columns whose fp32 SwiGLU is exactly gate * up (gate >= 17, where
+  1 + exp(-gate) rounds to 1 in fp32, and gate * up exact in fp32), so the
+  expected codes are the oracle's quantizer applied to the oracle's exact
+  gate * up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_packed_amd as hum
+import synth
+from gpu_util import bf16_bits_of, dev, descs, prepare
+
+pytestmark = pytest.mark.gpu
+
+# (kind, wave_m, wave_n, waves_n, waves_k): every compiled MoE instance
+MOE_TILES = [(1, 1, 4, 1, 8), (1, 1, 4, 1, 15), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 4, 4, 4, 1), (0, 8, 4, 4, 1)]
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def cfg(t):
+    c = hum.TileConfig()
+    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = t
+    c.split_k = 1
+    c.block_m = 16 * t[1]
+    return c
+
+
+def exact_weights(seed, e, n, k):
+    """MXFP4 weights whose values are multiples of 1/4: random E2M1 codes,
+    E8M0 exponents 127 (x1) or 126 (x1/2)."""
+    g = synth.rng(seed)
+    codes = synth.pack_nibbles(g.integers(0, 16, size=(e, n, k), dtype=np.uint8))
+    scales = g.integers(126, 128, size=(e, n, k // 32)).astype(np.uint8)
+    return {"codes": codes, "scales": scales}
+
+
+def exact_acts(seed, rows, k, act):
+    """Integer activations the activation format represents exactly, as
+    (bf16 bits, codes, scales, exact float64 values)."""
+    g = synth.rng(seed)
+    if act == "mxfp4":
+        mags = np.array([0, 1, 2, 3, 4, 6], np.float64)
+        v = mags[g.integers(0, 6, size=(rows, k))] * np.where(g.integers(0, 2, size=(rows, k)) == 1, -1.0, 1.0)
+        v[:, ::32] = 6.0           # every 32-block's amax is 6: scale 2^0, all values exact
+    else:
+        v = g.integers(-8, 9, size=(rows, k)).astype(np.float64)
+    bits = synth.bf16_bits(v.astype(np.float32))
+    if act == "bf16":
+        return bits, None, None, v
+    q, s = (oracle.quant.quant_mxfp8 if act == "mxfp8" else oracle.quant.quant_mxfp4)(v)
+    assert np.array_equal(oracle.gemm.activations(act, q=q, scales=s), v)   # exact in the format
+    return bits, q, s, v
+
+
+def stage_inputs(bits, q, s, act):
+    if act == "bf16":
+        return dev(bits), None
+    return dev(q), dev(s)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_gate_up_and_down_exact_integer_every_tile(act, tile):
+    if act == "mxfp4" and tile[0] == 1:
+        pytest.skip("W4A4 runs on the tile kernel only")
+    e, h, inter, k, t = 8, 1024, 512, 2, 40
+    bm = 16 * tile[1]
+    w13 = exact_weights(900, e, 2 * inter, h)
+    w2 = exact_weights(901, e, h, inter)
+    d13, o13 = descs("e2m1", "group", 32, "e8m0", e, 2 * inter, h, act=act)
+    d2, o2 = descs("e2m1", "group", 32, "e8m0", e, h, inter, act=act)
+    p13, p2 = prepare(d13, w13, "e8m0"), prepare(d2, w2, "e8m0")
+    ids, _ = synth.routing(902, t, e, k, zipf_s=1.3)
+    srt, off, cnt = oracle.moe.align(ids, e, bm)
+    xbits, xq, xs, xv = exact_acts(903, t, h, act)
+    print(f"case stage exact act={act} tile={tile}", flush=True)
+    a, a_s = stage_inputs(xbits, xq, xs, act)
+    h_gpu = hum.moe_grouped_gemm(d13, p13, a, dev(srt), dev(off), bm, t, k, a_mode="gather", epilogue="none",
+                                 a_scales=a_s, cfg=cfg(tile))
+    # down: integer intermediate rows in sorted order
+    ibits, iq, isc, iv = exact_acts(904, len(srt), inter, act)
+    a2, a2_s = stage_inputs(ibits, iq, isc, act)
+    y_sorted = hum.moe_grouped_gemm(d2, p2, a2, dev(srt), dev(off), bm, t, k, a_mode="sorted", epilogue="none",
+                                    a_scales=a2_s, cfg=cfg(tile))
+    y_flat = hum.moe_grouped_gemm(d2, p2, a2, dev(srt), dev(off), bm, t, k, a_mode="sorted", epilogue="scatter",
+                                  a_scales=a2_s, cfg=cfg(tile))
+    torch.cuda.synchronize()
+    hb, ysb, yfb = bf16_bits_of(h_gpu), bf16_bits_of(y_sorted), bf16_bits_of(y_flat)
+    for ex in range(e):
+        seg = srt[off[ex]:off[ex] + cnt[ex]]
+        if len(seg) == 0:
+            continue
+        rows = np.arange(off[ex], off[ex] + cnt[ex])
+        href = oracle.gemm.linear(o13, xv[seg // k], w13["codes"], w13["scales"], expert=ex)
+        yref = oracle.gemm.linear(o2, iv[rows], w2["codes"], w2["scales"], expert=ex)
+        assert np.array_equal(hb[rows], oracle.formats.encode_bf16(href)), f"gate_up expert {ex}"
+        assert np.array_equal(ysb[rows], oracle.formats.encode_bf16(yref)), f"down expert {ex}"
+        assert np.array_equal(yfb[seg], oracle.formats.encode_bf16(yref)), f"down scatter expert {ex}"
+        # the same rows through the dense layer on this expert alone
+        e13, _ = descs("e2m1", "group", 32, "e8m0", 1, 2 * inter, h, act=act)
+        pe = prepare(e13, {"codes": w13["codes"][ex:ex + 1], "scales": w13["scales"][ex:ex + 1]}, "e8m0")
+        xa, xa_s = stage_inputs(xbits[seg // k], None if xq is None else xq[seg // k],
+                                None if xs is None else xs[seg // k], act)
+        dense = hum.linear(e13, pe, xa, a_scales=xa_s)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits_of(dense), hb[rows]), f"gate_up vs hum_linear expert {ex}"
+
+
+def swiglu_exact_case(seed, e, h, inter, t, k, act):
+    """Gate weights in (0, 2] and activations in {1, 2}: every gate output is
+    at least 0.5 * h >= 17; up weights in [-1, 1].  All values are multiples
+    of 1/2, sums far below 2^12, so gate * up is exact in fp32."""
+    g = synth.rng(seed)
+    codes = np.zeros((e, 2 * inter, h), np.uint8)
+    codes[:, :inter] = g.integers(1, 5, size=(e, inter, h))                 # +0.5 .. +2
+    up = g.integers(0, 5, size=(e, inter, h))                                # -1 .. 1
+    codes[:, inter:] = np.array([0xA, 0x9, 0x0, 0x1, 0x2], np.uint8)[up]
+    w13 = {"codes": synth.pack_nibbles(codes), "scales": np.full((e, 2 * inter, h // 32), 127, np.uint8)}
+    x = g.integers(1, 3, size=(t, h)).astype(np.float64)
+    bits = synth.bf16_bits(x.astype(np.float32))
+    q = s = None
+    if act != "bf16":
+        q, s = (oracle.quant.quant_mxfp8 if act == "mxfp8" else oracle.quant.quant_mxfp4)(x)
+        assert np.array_equal(oracle.gemm.activations(act, q=q, scales=s), x)
+    return w13, bits, q, s, x
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("tile", [(1, 1, 4, 1, 8), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 8, 4, 4, 1)],
+                         ids=lambda t: "t" + "".join(map(str, t)))
+def test_swiglu_epilogue_codes_bit_exact(act, tile):
+    if act == "mxfp4" and tile[0] == 1:
+        pytest.skip("W4A4 runs on the tile kernel only")
+    e, h, inter, k, t = 4, 256, 256, 2, 50
+    bm = 16 * tile[1]
+    w13, xbits, xq, xs, xv = swiglu_exact_case(910, e, h, inter, t, k, act)
+    d13, o13 = descs("e2m1", "group", 32, "e8m0", e, 2 * inter, h, act=act)
+    p13 = prepare(d13, w13, "e8m0")
+    ids, _ = synth.routing(911, t, e, k)
+    srt, off, cnt = oracle.moe.align(ids, e, bm)
+    a, a_s = stage_inputs(xbits, xq, xs, act)
+    epi = {"bf16": "swiglu_bf16", "mxfp8": "swiglu_mxfp8", "mxfp4": "swiglu_mxfp4"}[act]
+    print(f"case swiglu act={act} tile={tile}", flush=True)
+    res = hum.moe_grouped_gemm(d13, p13, a, dev(srt), dev(off), bm, t, k, a_mode="gather", epilogue=epi,
+                               a_scales=a_s, cfg=cfg(tile), keep_swiglu_f32=True)
+    torch.cuda.synchronize()
+    out, f32 = res[0], res[-1].cpu().numpy()
+    for ex in range(e):
+        seg = srt[off[ex]:off[ex] + cnt[ex]]
+        if len(seg) == 0:
+            continue
+        rows = np.arange(off[ex], off[ex] + cnt[ex])
+        hh = oracle.gemm.linear(o13, xv[seg // k], w13["codes"], w13["scales"], expert=ex)
+        gate, up = hh[:, :inter], hh[:, inter:]
+        assert gate.min() >= 17.0
+        a_exact = gate * up                           # the fp32 SwiGLU for gate >= 17, exactly
+        assert np.array_equal(f32[rows].astype(np.float64), a_exact), f"SwiGLU values expert {ex}"
+        if act == "bf16":
+            assert np.array_equal(bf16_bits_of(out)[rows], oracle.formats.encode_bf16(a_exact)), f"bf16 expert {ex}"
+        elif act == "mxfp8":
+            q, s = oracle.quant.quant_mxfp8(a_exact)
+            assert np.array_equal(res[1].cpu().numpy()[rows], s), f"E8M0 expert {ex}"
+            assert np.array_equal(out.cpu().numpy()[rows], q), f"E4M3 codes expert {ex}"
+        else:
+            q, s = oracle.quant.quant_mxfp4(a_exact)
+            assert np.array_equal(res[1].cpu().numpy()[rows], s), f"E8M0 expert {ex}"
+            assert np.array_equal(out.cpu().numpy()[rows], q), f"E2M1 codes expert {ex}"
+
+
+def test_stage_argument_errors():
+    e, h, inter = 4, 256, 128
+    d13, _ = descs("e2m1", "group", 32, "e8m0", e, 2 * inter, h, act="mxfp8")
+    srt, off, _ = oracle.moe.align(np.zeros((3, 1), np.int32), e, 16)
+    q = torch.zeros((3, h), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((3, h // 32), dtype=torch.uint8, device="cuda")
+    pk = torch.zeros(hum.packed_weight_bytes(d13), dtype=torch.uint8, device="cuda")
+    with pytest.raises(hum.HumError, match="SWIGLU_MXFP8"):
+        hum.moe_grouped_gemm(d13, pk, q, dev(srt), dev(off), 16, 3, 1, epilogue="swiglu_bf16", a_scales=s)
+    with pytest.raises(hum.HumError, match="block_m"):
+        hum.moe_grouped_gemm(d13, pk, q, dev(srt), dev(off), 24, 3, 1, epilogue="none", a_scales=s)
