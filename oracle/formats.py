@@ -41,7 +41,7 @@ def decode_uint4(c):
     return (np.asarray(c, dtype=np.int64) & 0xF).astype(np.float64)
 
 
-def decode_e2m1(c):
+def _e2m1_closed_form(c):
     c = np.asarray(c, dtype=np.int64) & 0xF
     s = (c >> 3) & 1
     e = (c >> 1) & 3
@@ -50,7 +50,7 @@ def decode_e2m1(c):
     return np.where(s == 1, -mag, mag).astype(np.float64)
 
 
-def decode_e4m3(c):
+def _e4m3_closed_form(c):
     c = np.asarray(c, dtype=np.int64) & 0xFF
     s = (c >> 7) & 1
     e = (c >> 3) & 0xF
@@ -59,6 +59,26 @@ def decode_e4m3(c):
                    np.ldexp(1.0 + m / 8.0, e - 7))
     mag = np.where((e == 15) & (m == 7), np.nan, mag)
     return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+# The closed forms above evaluated once per code; decoding a tensor looks
+# its codes up (the same values, without re-evaluating the closed form per
+# element).
+_E2M1_VALUES = _e2m1_closed_form(np.arange(16))
+_E4M3_VALUES = _e4m3_closed_form(np.arange(256))
+
+
+def _code_index(c, mask):
+    c = np.asarray(c)
+    return (c & mask) if c.dtype == np.uint8 else (c.astype(np.int64) & mask)
+
+
+def decode_e2m1(c):
+    return np.take(_E2M1_VALUES, _code_index(c, 0xF))
+
+
+def decode_e4m3(c):
+    return np.take(_E4M3_VALUES, _code_index(c, 0xFF))
 
 
 def decode_e8m0(c):

@@ -117,7 +117,7 @@ def stage_precision(a, act_fmt: str):
 
 def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
                 x_bits, ids, weights, act_fmt: str, experts=None,
-                return_y: bool = False):
+                return_y: bool = False, dequant=None):
     """Full MoE layer in float64.  Returns out (float64 [T, H]) before the
     final bf16 rounding, and optionally y (float64 [T*topk, H]) indexed by
     flat routing index.
@@ -126,6 +126,8 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
     ``zeros`` / ``global_scale``.  ``act_fmt``: "bf16" (W4A16), "mxfp8"
     (W4A8) or "mxfp4" (W4A4: the layer input and the SwiGLU output are
     quantized to MXFP4 the way MXFP8 is for W4A8).  ``experts``: restrict to these experts (bounded samples).
+    ``dequant``: optional e -> (W13[e], W2[e]) giving the dequantized weights
+    (a caller's cache of dequant_weight results, for repeated calls).
     """
     ids = np.asarray(ids, dtype=np.int64)
     wts = np.asarray(weights, dtype=np.float32).astype(np.float64)
@@ -144,7 +146,7 @@ def moe_forward(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict,
         if f.size == 0:
             continue
         tok = f // k
-        y = expert_mlp(desc13, w13, desc2, w2, a_in[tok], e, act_fmt)
+        y = expert_mlp(desc13, w13, desc2, w2, a_in[tok], e, act_fmt, dequant)
         if return_y:
             y_all[f] = y
         np.add.at(out, tok, wts.reshape(-1)[f][:, None] * y)
@@ -167,18 +169,26 @@ def quant_input(x, act_fmt: str):
     raise ValueError(act_fmt)
 
 
-def expert_mlp(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict, a_in, e: int, act_fmt: str):
+def expert_mlp(desc13: WeightDesc, w13: dict, desc2: WeightDesc, w2: dict, a_in, e: int, act_fmt: str,
+               dequant=None):
     """One expert on its rows a_in (float64 [R, H], already in the input
     format): h = a_in W13[e]^T, a = SwiGLU(h) at the stage precision,
     y = a W2[e]^T (float64 [R, H])."""
     inter = desc2.k
-    w_gu = dequant_weight(desc13, w13["codes"], w13["scales"], w13.get("zeros"),
-                          w13.get("global_scale"), experts=[e])[0]
+    if dequant is not None:
+        w_gu, w_dn = dequant(e)
+        w_gu = np.asarray(w_gu, dtype=np.float64)
+        w_dn = np.asarray(w_dn, dtype=np.float64)
+    else:
+        w_gu = dequant_weight(desc13, w13["codes"], w13["scales"], w13.get("zeros"),
+                              w13.get("global_scale"), experts=[e])[0]
+        w_dn = None
     h = np.asarray(a_in, dtype=np.float64) @ w_gu.T
     del w_gu
     a = stage_precision(swiglu(h, inter), act_fmt)
-    w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
-                          w2.get("global_scale"), experts=[e])[0]
+    if w_dn is None:
+        w_dn = dequant_weight(desc2, w2["codes"], w2["scales"], w2.get("zeros"),
+                              w2.get("global_scale"), experts=[e])[0]
     return a @ w_dn.T
 
 

@@ -985,8 +985,10 @@ static hum_status stage_setup(const hum_weight_desc* w, int32_t a_mode, int32_t 
   }
   if (!cfg_sane(S.c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   if (tile_rows(S.c) != block_m) return set_error(HUM_ERR_INVALID_ARG, "the configuration's block (%d rows) differs from block_m", (int)tile_rows(S.c));
-  S.key = KernelKey{f, S.c.kind, S.c.wave_m, S.c.wave_n, S.c.waves_n, S.c.waves_k,
-                    a_mode == HUM_MOE_A_GATHER ? A_GATHER : A_DIRECT, epi, key_stages(S.c)};
+  // sorted rows: the scatter epilogue's instances read them directly (that
+  // epilogue implies grouped rows); the others take the grouped-row mode
+  const int amode = a_mode == HUM_MOE_A_GATHER ? A_GATHER : (epi == EPI_SCATTER ? A_DIRECT : A_SORTED);
+  S.key = KernelKey{f, S.c.kind, S.c.wave_m, S.c.wave_n, S.c.waves_n, S.c.waves_k, amode, epi, key_stages(S.c)};
   if (!gemm_instance_exists(S.key)) return set_error(HUM_ERR_UNSUPPORTED, "no grouped GEMM instance for this mode, epilogue and tile");
   if (S.c.split_k > 1 && !reduce_instance_exists(f, epi)) return set_error(HUM_ERR_UNSUPPORTED, "no split-K reduce for this format and epilogue");
   if (S.c.kind == HUM_KERNEL_STREAM && !moe_stream_fits(w, S.c, (int)(t * topk < 16 ? t * topk : 16)))

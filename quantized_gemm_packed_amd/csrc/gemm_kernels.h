@@ -395,10 +395,13 @@ __device__ __forceinline__ float gathered_row_scale(const GemmParams& p, int64_t
 
 // The per-token FP8 activation scale of output row `row` (1 for other
 // formats): the row's own, or for gathered rows the gathered token's.
-template <int FMT>
+// AM: the row mode when known at compile time, -1 for the run-time flag
+// (split-K reduce).
+template <int FMT, int AM = -1>
 __device__ __forceinline__ float row_act_scale(const GemmParams& p, int64_t row) {
   if (FMT != F_FP8) return 1.0f;
-  return p.a_gather ? gathered_row_scale(p, row) : reinterpret_cast<const float*>(p.a_scale)[row];
+  const bool gathered = AM < 0 ? p.a_gather != 0 : AM == A_GATHER;
+  return gathered ? gathered_row_scale(p, row) : reinterpret_cast<const float*>(p.a_scale)[row];
 }
 
 // Column scale of the plain / scatter epilogues (per-channel FP8 scale and
@@ -411,7 +414,7 @@ __device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, fl
 
 // Stores of one 16x16 accumulator tile held in the MFMA C layout (lane holds
 // rows 4*lg + i of column c16) for the plain and scatter epilogues.
-template <int FMT, int EPI>
+template <int FMT, int EPI, int AMODE>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* wmeta, float gs, int64_t row_base,
                                            int64_t col, const f32x4_t& v, int lg) {
   if (col >= p.n) return;
@@ -423,7 +426,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* w
     const int64_t row = row_base + 4 * lg + i;
     if (row >= p.m) continue;
     float x = v[i] * cs;
-    if (FMT == F_FP8) x *= row_act_scale<FMT>(p, row);
+    if (FMT == F_FP8) x *= row_act_scale<FMT, AMODE>(p, row);
     x += bias;
     if (EPI == EPI_SCATTER) {
       const int32_t f = p.sorted[row];
@@ -431,7 +434,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* w
       out[(int64_t)f * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
     } else {
       // grouped rows in sorted order: padding slots are not stored
-      if (p.sorted && p.sorted[row] >= p.sentinel) continue;
+      if (AMODE != A_DIRECT && p.sorted[row] >= p.sentinel) continue;
       out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(x);
     }
   }
@@ -455,7 +458,7 @@ __device__ __forceinline__ void keep_swiglu_f32(const GemmParams& p, int64_t row
 }
 
 // SwiGLU epilogue of a gate / up tile pair in the C layout.
-template <int FMT>
+template <int FMT, int AMODE>
 __device__ __forceinline__ void store_swiglu_bf16(const GemmParams& p, const uint8_t* wmeta, float gs, int64_t row_base,
                                                   int64_t col, const f32x4_t& g, const f32x4_t& u, int lg) {
   if (col >= p.n) return;
@@ -464,7 +467,7 @@ __device__ __forceinline__ void store_swiglu_bf16(const GemmParams& p, const uin
   for (int i = 0; i < 4; ++i) {
     const int64_t row = row_base + 4 * lg + i;
     if (row >= p.m) continue;
-    const float a = swiglu_val<FMT>(p, wmeta, gs, row_act_scale<FMT>(p, row), col, g[i], u[i]);
+    const float a = swiglu_val<FMT>(p, wmeta, gs, row_act_scale<FMT, AMODE>(p, row), col, g[i], u[i]);
     keep_swiglu_f32(p, row, col, a);
     out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(a);
   }
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   const int split = (int)blockIdx.z;
 
   int expert = 0;
-  if (p.block_expert) {  // grouped rows: the block's expert (-1: all padding)
+  if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {  // grouped rows: the block's expert (-1: all padding)
     expert = p.block_expert[tm];
     if (expert < 0) return;
   }
@@ -992,11 +995,11 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   }
   if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
 #pragma unroll
-    for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg);
+    for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg);
   } else if constexpr (EPI == EPI_SWIGLU_BF16) {
 #pragma unroll
     for (int j = 0; j < WN / 2; ++j)
-      store_swiglu_bf16<FMT>(p, wp.meta, gs, row0, (int64_t)nts[j] * 16 + c16, acc[j], acc[j + WN / 2], lg);
+      store_swiglu_bf16<FMT, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[j] * 16 + c16, acc[j], acc[j + WN / 2], lg);
   } else {
 #pragma unroll
     for (int jj = 0; jj < WN / 4; ++jj)
@@ -1132,7 +1135,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   }
 
   int expert = 0;
-  if (p.block_expert) {  // grouped rows: the block's expert (-1: all padding)
+  if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {  // grouped rows: the block's expert (-1: all padding)
     expert = p.block_expert[tm];
     if (expert < 0) return;
   }
@@ -1552,11 +1555,11 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     const int64_t rb = row0 + ms * 16;
     if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
 #pragma unroll
-      for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI>(p, wp.meta, gs, rb, (int64_t)nts[ns] * 16 + c16, acc[ms][ns], lg);
+      for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI, AMODE>(p, wp.meta, gs, rb, (int64_t)nts[ns] * 16 + c16, acc[ms][ns], lg);
     } else if constexpr (EPI == EPI_SWIGLU_BF16) {
 #pragma unroll
       for (int j = 0; j < WN / 2; ++j)
-        store_swiglu_bf16<FMT>(p, wp.meta, gs, rb, (int64_t)nts[j] * 16 + c16, acc[ms][j], acc[ms][j + WN / 2], lg);
+        store_swiglu_bf16<FMT, AMODE>(p, wp.meta, gs, rb, (int64_t)nts[j] * 16 + c16, acc[ms][j], acc[ms][j + WN / 2], lg);
     } else if constexpr (EPI == EPI_SWIGLU_MXFP4) {
 #pragma unroll
       for (int jj = 0; jj < WN / 4; ++jj)
@@ -1735,8 +1738,8 @@ InstanceTable instances_moe_c();
   HUM_TILE_S(F, 8, 2, A_DIRECT, EPI_BF16, 3)
 
 // MoE tile instances: gate_up (gathered rows, EPI_UP) and down (rows in
-// sorted order, scattered to flat slots); gathered rows with the plain
-// epilogue (per sorted row) serve the stage export.
+// sorted order, scattered to flat slots); gathered and sorted rows with the
+// plain epilogue (per sorted row) serve the stage export.
 #define HUM_MOE_TILE_SET(F, EPI_UP)                        \
   HUM_TILE(F, 1, 4, A_GATHER, EPI_UP),                     \
   HUM_TILE(F, 2, 4, A_GATHER, EPI_UP),                     \
@@ -1749,7 +1752,11 @@ InstanceTable instances_moe_c();
   HUM_TILE(F, 1, 4, A_GATHER, EPI_BF16),                   \
   HUM_TILE(F, 2, 4, A_GATHER, EPI_BF16),                   \
   HUM_TILE(F, 4, 4, A_GATHER, EPI_BF16),                   \
-  HUM_TILE(F, 8, 4, A_GATHER, EPI_BF16)
+  HUM_TILE(F, 8, 4, A_GATHER, EPI_BF16),                   \
+  HUM_TILE(F, 1, 4, A_SORTED, EPI_BF16),                   \
+  HUM_TILE(F, 2, 4, A_SORTED, EPI_BF16),                   \
+  HUM_TILE(F, 4, 4, A_SORTED, EPI_BF16),                   \
+  HUM_TILE(F, 8, 4, A_SORTED, EPI_BF16)
 
 #define HUM_MOE_SET(F, EPI_UP)                             \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_UP),                \
@@ -1758,6 +1765,8 @@ InstanceTable instances_moe_c();
   HUM_STREAM(F, 4, 15, 2, A_DIRECT, EPI_SCATTER),          \
   HUM_STREAM(F, 4, 8, 4, A_GATHER, EPI_BF16),              \
   HUM_STREAM(F, 4, 15, 2, A_GATHER, EPI_BF16),             \
+  HUM_STREAM(F, 4, 8, 4, A_SORTED, EPI_BF16),              \
+  HUM_STREAM(F, 4, 15, 2, A_SORTED, EPI_BF16),             \
   HUM_MOE_TILE_SET(F, EPI_UP)
 
 }  // namespace hum

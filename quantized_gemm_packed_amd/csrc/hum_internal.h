@@ -119,7 +119,10 @@ hum_status launch_moe_reduce(const void* y, const float* w, int64_t t, int32_t t
 
 // GEMM epilogues / A-row modes
 enum Epi : int { EPI_BF16 = 0, EPI_SWIGLU_BF16 = 1, EPI_SWIGLU_MXFP8 = 2, EPI_SCATTER = 3, EPI_SWIGLU_MXFP4 = 4 };
-enum AMode : int { A_DIRECT = 0, A_GATHER = 1 };
+// A-row modes: dense rows; grouped rows gathered through sorted (row r
+// reads a[sorted[r] / topk]); grouped rows read in sorted order (row r reads
+// a[r], padding slots skipped).  The scatter epilogue implies grouped rows.
+enum AMode : int { A_DIRECT = 0, A_GATHER = 1, A_SORTED = 2 };
 
 struct GemmParams {
   // weights
