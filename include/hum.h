@@ -416,6 +416,35 @@ hum_status hum_moe_grouped_gemm(const hum_weight_desc* w, const void* packed, in
                                 float* out_swiglu_f32, const hum_tile_config* cfg, void* workspace,
                                 size_t ws_bytes, void* stream);
 
+/* ---- measurement -------------------------------------------------------- */
+
+/* Device peak probes (measurement only; the GEMM path never calls them).
+ * Enqueue on `stream` one launch of a probe kernel and report its work in
+ * *work_out (bytes read, or flops), to be timed by the caller:
+ *   HUM_PEAK_HBM_READ     : stream-read n bytes of the device buffer buf
+ *                           (n a multiple of 16)
+ *   HUM_PEAK_MFMA_*       : n iterations of eight independent matrix
+ *                           instructions per wave on every CU (bf16
+ *                           16x16x32; E4M3 x E4M3, E2M1 x E2M1 and E4M3 x
+ *                           E2M1 16x16x128)
+ *   HUM_PEAK_MFMA32_*     : the same rates with the 32x32 shapes (four
+ *                           independent instructions per wave)
+ *   sink : device buffer of at least 2048 * 256 * 4 bytes (probe results
+ *          land there so that no work is dead).
+ * The rooflines the bench reports against are the published MI355X peaks;
+ * these re-measure what the box sustains. */
+#define HUM_PEAK_HBM_READ 0
+#define HUM_PEAK_MFMA_BF16 1
+#define HUM_PEAK_MFMA_FP8 2
+#define HUM_PEAK_MFMA_FP4 3
+#define HUM_PEAK_MFMA_FP8_FP4 4
+#define HUM_PEAK_MFMA32_BF16 5     /* the 32x32 shapes: bf16 32x32x16, f8f6f4 32x32x64 */
+#define HUM_PEAK_MFMA32_FP8 6
+#define HUM_PEAK_MFMA32_FP4 7
+#define HUM_PEAK_MFMA32_FP8_FP4 8
+hum_status hum_peak_probe(int32_t kind, int64_t n, const void* buf, void* sink, double* work_out,
+                          void* stream);
+
 /* Thread-local description of the last error (empty string if none). */
 const char* hum_last_error(void);
 

@@ -104,6 +104,7 @@ _SIGS = {
     "hum_moe_gemm_ex": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
     "hum_moe_align": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
     "hum_moe_reduce": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+    "hum_peak_probe": (_I32, [_I32, _I64, _P, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "hum_moe_grouped_gemm_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I64, _I32, _I64, _I32, _CP]),
     "hum_moe_grouped_gemm": (_I32, [_DP, _P, _I32, _I32, _I64, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P, _P, _CP,
                                     _P, _SZ, _P]),
@@ -658,6 +659,22 @@ def moe_grouped_gemm(w: WeightDesc, packed, a, sorted_ids, offsets, block_m: int
     if keep_swiglu_f32:
         res = res + (f32,)
     return res[0] if len(res) == 1 else res
+
+
+(PEAK_HBM_READ, PEAK_MFMA_BF16, PEAK_MFMA_FP8, PEAK_MFMA_FP4, PEAK_MFMA_FP8_FP4, PEAK_MFMA32_BF16, PEAK_MFMA32_FP8,
+ PEAK_MFMA32_FP4, PEAK_MFMA32_FP8_FP4) = range(9)
+
+
+def peak_probe(kind: int, n: int, buf=None, sink=None):
+    """Enqueue one device peak probe (measurement only) -> (sink, work):
+    bytes read for PEAK_HBM_READ, flops for the matrix-instruction loops."""
+    import torch
+    if sink is None:
+        sink = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    work = ctypes.c_double()
+    _check(load_library().hum_peak_probe(int(kind), int(n), _ptr(buf), _ptr(sink), ctypes.byref(work),
+                                         _stream(sink.device)))
+    return sink, work.value
 
 
 @dataclass
