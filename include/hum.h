@@ -93,7 +93,9 @@ typedef struct hum_weight_desc {
 
 typedef enum hum_kernel_kind {
   HUM_KERNEL_TILE = 0,    /* prefill: 4 waves along N share an LDS activation tile */
-  HUM_KERNEL_STREAM = 1   /* decode: one 16-row tile, waves_k waves stream K */
+  HUM_KERNEL_STREAM = 1,  /* decode: one 16-row tile, waves_k waves stream K */
+  HUM_KERNEL_TILE32 = 2   /* prefill with 32 x 32 MFMA blocks (bf16 activations,
+                             INT / MXFP4 weights; wave_m, wave_n even) */
 } hum_kernel_kind;
 
 /* Tile / split-K configuration (output of the selector, or forced). */

@@ -23,7 +23,7 @@ __all__ = [
 ]
 
 BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0, INT8 = range(8)
-KERNEL_TILE, KERNEL_STREAM = range(2)
+KERNEL_TILE, KERNEL_STREAM, KERNEL_TILE32 = range(3)
 SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP, SCALE_BLOCK = range(4)
 ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4, ACT_FP8_GROUP = range(5)
 

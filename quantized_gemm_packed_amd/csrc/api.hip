@@ -165,7 +165,7 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
 static const int kCUs = 256;
 
 static int key_stages(const hum_tile_config& c) {
-  return c.kind == HUM_KERNEL_TILE ? (c.stages == 0 ? 2 : c.stages) : 0;
+  return c.kind != HUM_KERNEL_STREAM ? (c.stages == 0 ? 2 : c.stages) : 0;
 }
 
 static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
@@ -176,6 +176,9 @@ static bool cfg_sane(const hum_tile_config& c) {
   if (c.split_k < 1 || c.split_k > 64 || c.wave_m < 1 || c.wave_n < 1) return false;
   if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 15;
   if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1 && (c.stages == 0 || c.stages == 2 || c.stages == 3);
+  if (c.kind == HUM_KERNEL_TILE32)
+    return c.waves_n == 4 && c.waves_k == 1 && (c.stages == 0 || c.stages == 2 || c.stages == 3) && c.wave_m % 2 == 0 &&
+           c.wave_n % 2 == 0;
   return false;
 }
 
@@ -183,7 +186,7 @@ static int64_t tile_rows(const hum_tile_config& c) { return 16 * (int64_t)c.wave
 
 // Columns (16-wide sub-tiles) one workgroup covers.
 static int64_t tile_subtiles(const hum_tile_config& c) {
-  return (int64_t)c.wave_n * (c.kind == HUM_KERNEL_TILE ? 4 : 1);
+  return (int64_t)c.wave_n * (c.kind != HUM_KERNEL_STREAM ? 4 : 1);
 }
 
 // Grid split so that the launch reaches `target` waves, each split keeping
@@ -273,6 +276,20 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
         c.wave_n = 2;
         c.stages = 3;
       }
+      c.split_k = 1;
+    }
+    if ((fmt_of(d) == F_INT && m >= 256) || (fmt_of(d) == F_MXFP4_BF16 && m >= 512)) {
+      // INT / MXFP4 weights with bf16 activations: 32 x 32 MFMA blocks (the
+      // bf16 16x16x32 shape issues at about half the 32x32x16 rate).
+      // Measured on MI355X at N = K = 8192: INT 64 x 128 tiles with three
+      // stages at M = 256, 64 x 256 with three stages to M = 1024 and two
+      // above; MXFP4 64 x 256 with three stages to M = 1024, 128 x 256 with
+      // two above
+      c.kind = HUM_KERNEL_TILE32;
+      c.wave_m = 4;
+      c.wave_n = (fmt_of(d) == F_INT && m < 512) ? 2 : 4;
+      c.stages = m <= 1024 ? 3 : 2;
+      if (fmt_of(d) == F_MXFP4_BF16 && m > 1024) c.wave_m = 8;
       c.split_k = 1;
     }
     if (fmt_of(d) == F_MXFP4_MXFP4) {
@@ -414,7 +431,7 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
                               : (d->act_fmt == HUM_ACT_FP8_GROUP ? m * (d->k / 128) * 4 : m * 4)));
   }
   w.rowsum = off;
-  if (fmt_of(d) == F_INT && c.kind == HUM_KERNEL_TILE) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
+  if (fmt_of(d) == F_INT && c.kind != HUM_KERNEL_STREAM) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
   w.total = off;
   return w;
 }
@@ -497,6 +514,9 @@ hum_status hum_select_config(const hum_weight_desc* desc, int64_t m, hum_tile_co
 static hum_tile_config select_dense_invariant(const hum_weight_desc* d, int64_t m) {
   hum_tile_config c = select_dense(d, m);
   if (c.kind == HUM_KERNEL_STREAM) c = select_dense(d, 17);
+  // 32x32 blocks sum each dot product in another order than 16x16 ones:
+  // one block shape for every m
+  if (c.kind == HUM_KERNEL_TILE32) c.kind = HUM_KERNEL_TILE;
   c.split_k = 1;
   c.block_m = (int32_t)tile_rows(c);
   return c;
@@ -590,7 +610,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   }
   GemmParams p{};
   fill_weight_params(p, desc, L, packed);
-  if (fmt_of(desc) == F_INT && c.kind == HUM_KERNEL_TILE) {
+  if (fmt_of(desc) == F_INT && c.kind != HUM_KERNEL_STREAM) {
     st = launch_rowsum(a_use, desc->k, m, (int)L.kb, (int)L.kbc, ws + w.rowsum, stream);
     if (st != HUM_OK) return st;
     p.a_rowsum = ws + w.rowsum;
@@ -694,17 +714,19 @@ static void dense_candidates(const hum_weight_desc* d, int64_t m, uint32_t flags
   const bool inv = (flags & HUM_SELECT_BATCH_INVARIANT) != 0;
   for (int split = 1; split <= 16; split *= 2) {
     if (inv && split > 1) break;
-    for (int kind = HUM_KERNEL_TILE; kind <= HUM_KERNEL_STREAM; ++kind) {
+    for (int kind = HUM_KERNEL_TILE; kind <= HUM_KERNEL_TILE32; ++kind) {
       if (kind == HUM_KERNEL_STREAM && (inv || m > 16)) continue;
-      for (int wm = 1; wm <= (kind == HUM_KERNEL_TILE ? 8 : 1); wm *= 2)
+      if (kind == HUM_KERNEL_TILE32 && inv) continue;
+      const bool tile = kind != HUM_KERNEL_STREAM;
+      for (int wm = 1; wm <= (tile ? 8 : 1); wm *= 2)
         for (int wn = 1; wn <= 8; wn *= 2)
-          for (int wk = 1; wk <= (kind == HUM_KERNEL_TILE ? 1 : 15); ++wk)
-            for (int st = 0; st <= (kind == HUM_KERNEL_TILE ? 3 : 0); st += 3) {
+          for (int wk = 1; wk <= (tile ? 1 : 15); ++wk)
+            for (int st = 0; st <= (tile ? 3 : 0); st += 3) {
               hum_tile_config c{};
               c.kind = kind;
               c.wave_m = wm;
               c.wave_n = wn;
-              c.waves_n = kind == HUM_KERNEL_TILE ? 4 : 1;
+              c.waves_n = tile ? 4 : 1;
               c.waves_k = wk;
               c.split_k = split;
               c.stages = st;

@@ -275,6 +275,7 @@ __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
 // exact (at most 6 significant bits), hence also exact when packed to bf16
 // by taking each f32's upper half.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ bf16x8_t nv_dequant(uint32_t w, float scale) {
   const f32x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
   const f32x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
@@ -1101,11 +1102,25 @@ struct TileLds {
   static __device__ __forceinline__ uint8_t* b(int st) { return a(st) + C::kA + C::kXI * 256; }
 };
 
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S>
+// MS = 32: the bf16 contraction runs on the 32x32x16 MFMA (on gfx950 the
+// 16x16x32 bf16 shape issues at about half the rate of the 32x32 one).  A
+// 32 x 32 block is a pair of 16-row sub-tiles by a pair of 16-column
+// sub-tiles.  The packed fragments hold, for lane c + 16q of a sub-tile,
+// column c and k = 32q .. 32q + 31; one permlane16 swap per code dword of a
+// sub-tile pair hands each lane column c (lane bit 4 clear) or c + 16 (set)
+// of the pair with k = 64h + 32R + 8s + (0..7) (h = lane / 32) in the
+// swap's result R, dword s: the B operand of instruction (R, s).  The A
+// operand reads the same k from the LDS tile.  Dense layers, bf16
+// activations, INT and MXFP4 weights.
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S, int MS = 16>
 __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
   using T = typename C::T;
   constexpr int kAE = T::kAElem;
+  static_assert(MS == 16 || (MS == 32 && (FMT == F_INT || FMT == F_MXFP4_BF16) && WM % 2 == 0 && WN % 2 == 0 &&
+                             AMODE == A_DIRECT && EPI == EPI_BF16),
+                "32x32 blocks: dense bf16-activation INT / MXFP4 tiles of even sub-tile counts");
+  constexpr int MP = MS == 32 ? WM / 2 : 1, NP = MS == 32 ? WN / 2 : 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wn = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1341,6 +1356,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   for (int ms = 0; ms < WM; ++ms)
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) acc[ms][ns] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // (MS = 32) 32 x 32 accumulators in the MFMA's C layout: register i of
+  // lane l holds row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+  f32x16_t acc32[MP][NP];
+#pragma unroll
+  for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+    for (int np = 0; np < NP; ++np)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc32[mp][np][i] = 0.0f;
 
   const IntScaleSel ssel = int_scale_sel(p, c16);
   auto compute = [&](int kb, int st, const BFrag<FMT>* bsrc) -> void {
@@ -1391,7 +1415,79 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) mw[ns] = sw.w[ns];
     }
-    if constexpr (T::kBf16) {
+    if constexpr (T::kBf16 && MS == 32) {
+      const int h = lane >> 5;
+      const bool hi = (lane & 16) != 0;  // the lane's column is in the pair's second sub-tile
+      uint32_t cw[NP][2][4];  // code dwords after the swap, [pair][R][s]
+      uint32_t mp2[NP][2];    // MXFP4: E8M0 words after the same swap
+#pragma unroll
+      for (int np = 0; np < NP; ++np) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const auto r = __builtin_amdgcn_permlane16_swap(bf[2 * np].w[0][s], bf[2 * np + 1].w[0][s], false, false);
+          cw[np][0][s] = r[0];
+          cw[np][1][s] = r[1];
+        }
+        if constexpr (FMT == F_MXFP4_BF16) {
+          const auto r = __builtin_amdgcn_permlane16_swap(mw[2 * np], mw[2 * np + 1], false, false);
+          mp2[np][0] = r[0];
+          mp2[np][1] = r[1];
+        }
+      }
+      // INT: one K-block of (128 + u) codes into fresh accumulators, then
+      // scaled by the lane's column scale (the offset is taken off after the
+      // K loop); MXFP4: scaled in the widening, accumulated in place
+      f32x16_t tk[MP][NP];
+      if constexpr (FMT == F_INT) {
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+          for (int np = 0; np < NP; ++np)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tk[mp][np][i] = 0.0f;
+      }
+#pragma unroll
+      for (int R = 0; R < 2; ++R)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8_t dd[NP];
+#pragma unroll
+          for (int np = 0; np < NP; ++np) {
+            if constexpr (FMT == F_INT)
+              dd[np] = int_dequant(cw[np][R][s]);
+            else
+              dd[np] = mx_dequant(cw[np][R][s], e8m0_to_f32(frag_mx_code(mp2[np][R], kb)));
+          }
+#pragma unroll
+          for (int mp = 0; mp < MP; ++mp) {
+            const int r = mp * 32 + (lane & 31);
+            const int chunk = 8 * h + 4 * R + s;
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + ((chunk ^ (r & 15)) * 16));
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+              if constexpr (FMT == F_INT)
+                tk[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dd[np], tk[mp][np], 0, 0, 0);
+              else
+                acc32[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dd[np], acc32[mp][np], 0, 0, 0);
+            }
+          }
+        }
+      if constexpr (FMT == F_INT) {
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+          // the scale word of the lane's column (sub-tile 2 np + hi), read
+          // from LDS by address (a per-lane choice between two elements of
+          // a register array would be turned into an indexed array access)
+          const uint32_t mwl = *reinterpret_cast<const uint32_t*>(mbase + (sf ? c16 : (c16 >> 1)) * WN * 4 +
+                                                                   (2 * np + (hi ? 1 : 0)) * 4);
+          const float sc = frag_int_scale(mwl, ssel);
+#pragma unroll
+          for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc32[mp][np][i] = __builtin_fmaf(sc, tk[mp][np][i], acc32[mp][np][i]);
+        }
+      }
+    } else if constexpr (T::kBf16) {
       bf16x8_t d[WN][4];
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) dequant_b<FMT>(bf[ns], mw[ns], kb, d[ns]);
@@ -1508,7 +1604,67 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     // weight's offset terms (B, stored negated) with K running over
     // K-blocks, each operand as a bf16 hi / lo pair (hi*hi + hi*lo + lo*hi).
     // The first split adds the whole of it.
-    if (split == 0) {
+    if (split == 0 && MS == 32) {
+      // the same product on the 32x32x16 MFMA: row sums of a pair of 16-row
+      // tiles and offset terms of a pair of sub-tiles, each swapped into the
+      // 32-wide operand layout as the weight codes are (K-block slots
+      // 8 lg + (0..7) of the 16-wide layouts: lane groups 0 / 2 in the
+      // swap's result 0, 1 / 3 in result 1)
+      const int64_t mt16 = (p.m + 15) / 16;
+      const int64_t rs_half = mt16 * p.kbc * 1024;
+      const int64_t co_half = (int64_t)p.nt_count * p.kbc * 1024;
+      const uint8_t* cob = p.wco + (int64_t)expert * p.co_per_expert;
+      auto swap4 = [](const u32x4_t& x, const u32x4_t& y, u32x4_t& r0, u32x4_t& r1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const auto r = __builtin_amdgcn_permlane16_swap(x[j], y[j], false, false);
+          r0[j] = r[0];
+          r1[j] = r[1];
+        }
+      };
+      for (int cc = 0; cc < p.kbc; ++cc) {
+        u32x4_t ch[NP][2], cl[NP][2];
+#pragma unroll
+        for (int np = 0; np < NP; ++np) {
+          u32x4_t xh[2], xl[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int ns = 2 * np + q;
+            const int64_t o = (((int64_t)(ntv[ns] ? nts[ns] : 0) * p.kbc + cc) * 64 + lane) * 16;
+            xh[q] = *reinterpret_cast<const u32x4_t*>(cob + o);
+            xl[q] = *reinterpret_cast<const u32x4_t*>(cob + co_half + o);
+          }
+          swap4(xh[0], xh[1], ch[np][0], ch[np][1]);
+          swap4(xl[0], xl[1], cl[np][0], cl[np][1]);
+        }
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) {
+          u32x4_t yh[2], yl[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int64_t mt = row0 / 16 + 2 * mp + q;
+            // (16-row tiles past m have no row sums: zero, their rows are never stored)
+            const int64_t o = ((mt * p.kbc + cc) * 64 + lane) * 16;
+            yh[q] = mt < mt16 ? *reinterpret_cast<const u32x4_t*>(p.a_rowsum + o) : u32x4_t{0, 0, 0, 0};
+            yl[q] = mt < mt16 ? *reinterpret_cast<const u32x4_t*>(p.a_rowsum + rs_half + o) : u32x4_t{0, 0, 0, 0};
+          }
+          u32x4_t rh[2], rl[2];
+          swap4(yh[0], yh[1], rh[0], rh[1]);
+          swap4(yl[0], yl[1], rl[0], rl[1]);
+#pragma unroll
+          for (int R = 0; R < 2; ++R) {
+            const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, rh[R]), al = __builtin_bit_cast(bf16x8_t, rl[R]);
+#pragma unroll
+            for (int np = 0; np < NP; ++np) {
+              const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, ch[np][R]), bl = __builtin_bit_cast(bf16x8_t, cl[np][R]);
+              acc32[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc32[mp][np], 0, 0, 0);
+              acc32[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc32[mp][np], 0, 0, 0);
+              acc32[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc32[mp][np], 0, 0, 0);
+            }
+          }
+        }
+      }
+    } else if (split == 0) {
       const int64_t mt16 = (p.m + 15) / 16;
       const int64_t rs_half = mt16 * p.kbc * 1024;
       const int64_t co_half = (int64_t)p.nt_count * p.kbc * 1024;
@@ -1539,6 +1695,36 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     }
   }
 
+  if constexpr (MS == 32) {
+    // 32 x 32 blocks: lane l holds column l % 32 of its pair and rows
+    // 8 (i / 4) + 4 (l / 32) + i % 4
+    const int64_t ncols = (int64_t)p.nt_count * 16;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+      // the pair's sub-tiles are consecutive: column nts[2 np] * 16 + l % 32
+      // (past N: never stored)
+      const int64_t col = (int64_t)nts[2 * np] * 16 + (lane & 31);
+      if (col >= p.n) continue;
+      const float cs = col_scale<FMT>(wp.meta, col, gs);
+      const float bias = p.bias ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
+#pragma unroll
+      for (int mp = 0; mp < MP; ++mp) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int64_t row = row0 + 32 * mp + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (row >= p.m) continue;
+          if (p.split_k > 1) {
+            p.partials[((int64_t)split * p.m + row) * ncols + col] = acc32[mp][np][i];
+          } else {
+            uint16_t* out = static_cast<uint16_t*>(p.out);
+            out[row * p.ldo + col] = (uint16_t)f32_to_bf16_bits(acc32[mp][np][i] * cs + bias);
+          }
+        }
+      }
+    }
+    return;
+  }
   if (p.split_k > 1) {
     const int64_t ncols = C::kSwiglu ? 2 * p.n : (int64_t)p.nt_count * 16;
 #pragma unroll
@@ -1708,6 +1894,20 @@ InstanceTable instances_moe_c();
 #define HUM_TILE_S(F, WM, WN, AM, EP, S) \
   {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
 #define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
+#define HUM_TILE32_S(F, WM, WN, S) \
+  {{F, KIND_TILE32, WM, WN, 4, 1, A_DIRECT, EPI_BF16, S}, tile_kernel<F, WM, WN, A_DIRECT, EPI_BF16, S, 32>, 256}
+// 32x32-block tiles (bf16 activations: INT and MXFP4 weights; INT's 128 x
+// 256 tile would spill its per-K-block accumulators)
+#define HUM_DENSE_TILE32_SET(F)                            \
+  HUM_TILE32_S(F, 2, 2, 2),                                \
+  HUM_TILE32_S(F, 2, 4, 2),                                \
+  HUM_TILE32_S(F, 4, 2, 2),                                \
+  HUM_TILE32_S(F, 4, 4, 2),                                \
+  HUM_TILE32_S(F, 8, 2, 2),                                \
+  HUM_TILE32_S(F, 2, 2, 3),                                \
+  HUM_TILE32_S(F, 2, 4, 3),                                \
+  HUM_TILE32_S(F, 4, 2, 3),                                \
+  HUM_TILE32_S(F, 4, 4, 3)
 
 // Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.

@@ -177,7 +177,7 @@ struct GemmParams {
   int lds_meta_off, lds_meta_stride, lds_zero_off;
 };
 
-enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1 };
+enum Kind : int { KIND_TILE = 0, KIND_STREAM = 1, KIND_TILE32 = 2 };
 
 // The decode (stream) kernel stages the activation rows of its K range in
 // LDS (rows x K-blocks x 256 B for bf16, 128 B (+4 B of MX scales) for

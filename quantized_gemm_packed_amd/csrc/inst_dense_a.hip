@@ -12,6 +12,9 @@ static const Instance kDenseA[] = {
     HUM_DENSE_SET(F_MXFP4_MXFP8),
     HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
     HUM_DENSE_TILE_SET(F_FP8_BLOCK),
+    HUM_DENSE_TILE32_SET(F_INT),
+    HUM_DENSE_TILE32_SET(F_MXFP4_BF16),
+    HUM_TILE32_S(F_MXFP4_BF16, 8, 4, 2),
 };
 
 HUM_TABLE(instances_dense_a, kDenseA)

@@ -37,7 +37,7 @@ def test_autotune_result_matches_its_config(m):
     ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w["zeros"])
     assert_tol(out, ref, f"autotune m={m} cfg={best}")
     if m > 16:
-        assert best.kind == hum.KERNEL_TILE
+        assert best.kind in (hum.KERNEL_TILE, hum.KERNEL_TILE32)   # the decode kernel takes at most 16 rows
 
 
 def test_autotune_batch_invariant_candidates_only():

@@ -24,6 +24,9 @@ TILE_TILES = [(0, 1, 4, 4, 1), (0, 2, 2, 4, 1), (0, 2, 4, 4, 1), (0, 4, 2, 4, 1)
               (0, 8, 2, 4, 1), (0, 8, 4, 4, 1),
               (0, 2, 2, 4, 1, 3), (0, 2, 4, 4, 1, 3), (0, 4, 2, 4, 1, 3), (0, 4, 4, 4, 1, 3), (0, 8, 2, 4, 1, 3)]
 DENSE_TILES = STREAM_TILES + TILE_TILES
+# 32x32-block tiles (INT and MXFP4 weights with bf16 activations)
+TILE32_TILES = [(2, 2, 2, 4, 1), (2, 2, 4, 4, 1), (2, 4, 2, 4, 1), (2, 4, 4, 4, 1), (2, 8, 2, 4, 1),
+                (2, 2, 2, 4, 1, 3), (2, 2, 4, 4, 1, 3), (2, 4, 2, 4, 1, 3), (2, 4, 4, 4, 1, 3)]
 
 
 def cfg(t, split):
@@ -60,7 +63,7 @@ def _int_exact_case(seed, wd, m, n, k, gs, zero):
     return w, xb
 
 
-@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 @pytest.mark.parametrize("split", [1, 2, 4])
 def test_int_exact_every_tile(tile, split):
     m, n, k, gs = rows_for(tile, 37), 640, 2048, 128
@@ -78,7 +81,7 @@ def test_int_exact_every_tile(tile, split):
     assert_bf16_exact(out, ref, f"tile={tile} split={split}")
 
 
-@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_int4_sym_exact_every_tile(tile):
     m, n, k, gs = 5, 200, 1024, 256
     w, xb = _int_exact_case(32, "int4", m, n, k, gs, False)
@@ -90,7 +93,7 @@ def test_int4_sym_exact_every_tile(tile):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
-@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_mxfp4_bf16_exact_every_tile(tile):
     m, n, k = 9, 96, 1024
     g = synth.rng(33)
@@ -548,3 +551,29 @@ def test_empty_m_is_a_no_op(fmt):
     out = hum.linear(hd, packed, x)
     torch.cuda.synchronize()
     assert tuple(out.shape) == (0, n)
+
+
+@pytest.mark.parametrize("wd", ["uint4", "e2m1"])
+@pytest.mark.parametrize("tile", TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("m", [33, 300])
+def test_tile32_random_vs_oracle(wd, tile, m):
+    """32x32-block tiles on random data, ragged M and N, bias (MXFP4 also
+    with a global scale), against the oracle at the bf16-output bound."""
+    n, k = 592, 1024
+    if wd == "uint4":
+        w = synth.quant_weights(950 + m, "uint4", "group", 128, "bf16", 1, n, k, zero=True)
+        hd, od = descs("uint4", "group", 128, "bf16", 1, n, k, zero=True)
+        sd = "bf16"
+    else:
+        w = synth.quant_weights(951 + m, "e2m1", "group", 32, "e8m0", 1, n, k, global_scale=True)
+        hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, glob=True)
+        sd = "e8m0"
+    xb = synth.bf16_normal(synth.rng(952 + m), (m, k))
+    bias = synth.bf16_normal(synth.rng(953), (n,))
+    packed = prepare(hd, w, sd)
+    for split in (1, 2):
+        out = hum.linear(hd, packed, dev(xb), bias=dev(bias), cfg=cfg(tile, split))
+        torch.cuda.synchronize()
+        ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w.get("zeros"),
+                                 w.get("global_scale"), bias_bits=bias)
+        assert_tol(out, ref, f"{wd} tile={tile} m={m} split={split}")
