@@ -6,6 +6,15 @@ for Quantized Inference", sections "Background" and "WnA16"; they never give
 bit layouts.  The readings below are the OCP definitions:
 
 * INT4: two's complement nibble, values -8..7.  UINT4: 0..15.
+* INTb / UINTb for b = 1, 2, 3 (section "WnA16" lists INT1, INT2 and INT3
+  among the shared dequantization path's widths; section "Quantization
+  support" of the aireiter.com review names GPTQ INT3 checkpoints): the
+  same two's complement / unsigned reading at b bits (INT3 -4..3, INT2
+  -2..1, INT1 -1..0; UINTb 0..2^b-1).  Canonical packing is an LSB-first
+  bit stream along K: code k of a row occupies bits b*k .. b*k+b-1 of the
+  row's bytes read as one little-endian integer (for b = 4 this is the
+  nibble packing, even k in the low nibble; for b = 3 it is the GPTQ
+  3-bit stream, whose 32-bit words, little-endian, hold the same bits).
 * INT8: two's complement byte, values -128..127 (one code per byte; the
   pages list INT8 among the weight widths without a layout).
 * E2M1 (OCP MX v1.0): sign, 2 exponent bits (bias 1), 1 mantissa bit;
@@ -207,8 +216,36 @@ def unpack_nibbles(packed):
     return out
 
 
+INT_BITS = {"int1": 1, "int2": 2, "int3": 3, "uint1": 1, "uint2": 2, "uint3": 3}
+
+
+def unpack_bits(packed, bits: int):
+    """uint8 [..., K*bits/8] LSB-first bit stream -> uint8 [..., K] codes.
+
+    Bit i of the row is bit (i % 8) of byte i // 8; code k is the bits
+    bits*k .. bits*k + bits - 1, least significant first."""
+    p = np.asarray(packed, dtype=np.uint8)
+    stream = np.unpackbits(p, axis=-1, bitorder="little")          # [..., 8 * bytes]
+    k = stream.shape[-1] // bits
+    b = stream[..., :k * bits].reshape(p.shape[:-1] + (k, bits)).astype(np.int64)
+    weights = np.left_shift(1, np.arange(bits, dtype=np.int64))
+    return (b * weights).sum(axis=-1).astype(np.uint8)
+
+
+def decode_intb(c, bits: int):
+    """b-bit two's complement code -> value in [-2^(b-1), 2^(b-1) - 1]."""
+    c = np.asarray(c, dtype=np.int64) & ((1 << bits) - 1)
+    return np.where(c >= (1 << (bits - 1)), c - (1 << bits), c).astype(np.float64)
+
+
 def decode_weight_codes(codes, weight_dtype: str):
     """Canonical code array -> float64 element values v(q)."""
+    if weight_dtype in INT_BITS:
+        b = INT_BITS[weight_dtype]
+        q = unpack_bits(codes, b)
+        if weight_dtype.startswith("u"):
+            return q.astype(np.float64)
+        return decode_intb(q, b)
     if weight_dtype in ("int4", "uint4", "e2m1"):
         q = unpack_nibbles(codes)
         return {"int4": decode_int4, "uint4": decode_uint4,

@@ -8,7 +8,8 @@ and a second-level scale are independent parameters, and the activations
 carry their own format.  Readings where the page is silent:
 
 * zero point: an integer z subtracted from the decoded code before scaling,
-  W = (v(q) - z) * S; only unsigned 4-bit codes carry one.
+  W = (v(q) - z) * S; only unsigned integer codes (UINT1..UINT4) carry one,
+  z in [0, 2^b).
 * group g of element k is floor(k / G); channel granularity is G = K;
   tensor granularity is one scale per expert.
 * the second-level scale is one float32 per expert, multiplied after the
@@ -33,7 +34,7 @@ from .quant import dequant_fp8_group, dequant_fp8_per_token, dequant_mxfp4, dequ
 
 @dataclass
 class WeightDesc:
-    weight_dtype: str          # "int4" | "uint4" | "int8" | "e2m1" | "e4m3"
+    weight_dtype: str          # "int1".."int4" | "uint1".."uint4" | "int8" | "e2m1" | "e4m3"
     scale_gran: str            # "tensor" | "channel" | "group"
     group_size: int            # along K (ignored unless scale_gran == "group")
     scale_dtype: str           # "bf16" | "f32" | "e8m0" | "e4m3" (NVFP4: E2M1 codes, G = 16)

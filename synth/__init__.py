@@ -30,7 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rng", "seed_for", "bf16_bits", "bf16_normal", "pack_nibbles",
+    "rng", "seed_for", "bf16_bits", "bf16_normal", "pack_nibbles", "pack_bits", "INT_BITS",
     "dense_w4a16", "dense_w8a8", "moe_weights_mxfp4", "routing", "quant_weights",
     "DENSE_SWEEP_M", "FP8_SWEEP_M", "MOE_W4A16_T", "MOE_W4A8_T",
 ]
@@ -67,6 +67,20 @@ def pack_nibbles(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8)
     assert c.shape[-1] % 2 == 0
     return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+INT_BITS = {"int1": 1, "int2": 2, "int3": 3, "uint1": 1, "uint2": 2, "uint3": 3}
+
+
+def pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
+    """uint8 codes (0 .. 2^bits - 1) [..., K] -> uint8 [..., K*bits/8]: an
+    LSB-first bit stream along K (code k at bits bits*k .. bits*k+bits-1 of
+    the row read as one little-endian integer)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert (c.shape[-1] * bits) % 8 == 0
+    planes = [(c >> i) & 1 for i in range(bits)]                   # bit i of every code
+    stream = np.stack(planes, axis=-1).reshape(c.shape[:-1] + (c.shape[-1] * bits,))
+    return np.packbits(stream, axis=-1, bitorder="little")
 
 
 def _uniform_bf16(g, lo, hi, shape):
@@ -116,7 +130,7 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
     code, all 256), scales uniform in
     [scale_lo, scale_hi] (bf16 / f32) or E8M0 codes in [e8m0_lo, e8m0_hi],
     E4M3 scale codes (NVFP4) uniform in [e4m3_lo, e4m3_hi] (positive, finite),
-    zero points uniform in [0, 15], global scales uniform in [0.5, 2]."""
+    zero points uniform over the codes (0..2^b-1), global scales uniform in [0.5, 2]."""
     g = rng(seed)
     e = num_experts
     if scale_gran == "group":
@@ -132,6 +146,9 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
         codes = np.where((c & 0x7F) == 0x7F, c & 0xFE, c).astype(np.uint8)
     elif weight_dtype == "int8":
         codes = g.integers(0, 256, size=(e, n, k), dtype=np.uint8)
+    elif weight_dtype in INT_BITS:
+        b = INT_BITS[weight_dtype]
+        codes = pack_bits(g.integers(0, 1 << b, size=(e, n, k), dtype=np.uint8), b)
     else:
         codes = pack_nibbles(g.integers(0, 16, size=(e, n, k), dtype=np.uint8))
     if scale_dtype == "bf16":
@@ -142,7 +159,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
         scales = g.integers(e4m3_lo, e4m3_hi + 1, size=(e, sn, sg), dtype=np.uint8)
     else:
         scales = g.integers(e8m0_lo, e8m0_hi + 1, size=(e, sn, sg), dtype=np.uint8)
-    zeros = g.integers(0, 16, size=(e, sn, sg), dtype=np.uint8) if zero else None
+    zmax = 1 << INT_BITS.get(weight_dtype, 4)
+    zeros = g.integers(0, zmax, size=(e, sn, sg), dtype=np.uint8) if zero else None
     gsc = g.uniform(0.5, 2.0, size=e).astype(np.float32) if global_scale else None
     return {"codes": codes, "scales": scales, "zeros": zeros, "global_scale": gsc}
 

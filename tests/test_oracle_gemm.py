@@ -12,7 +12,7 @@ import torch
 
 from oracle import gemm as G
 from oracle.formats import decode_bf16
-from synth import bf16_bits, pack_nibbles
+from synth import bf16_bits, pack_bits, pack_nibbles
 
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
 
@@ -23,6 +23,10 @@ def s_int4(c):
 
 def s_int8(c):
     return c - 256 if c >= 128 else c
+
+
+def s_intb(c, b):
+    return c - (1 << b) if c >= (1 << (b - 1)) else c
 
 
 def s_e2m1(c):
@@ -50,7 +54,9 @@ def s_scale(v, dtype):
 
 def brute_linear(desc, a_vals, codes_unpacked, scales, zeros, gscale):
     """C[m][n] with exact rationals, one scalar at a time."""
-    dec = {"int4": s_int4, "uint4": lambda c: c, "int8": s_int8, "e2m1": s_e2m1, "e4m3": s_e4m3}[desc.weight_dtype]
+    dec = {"int4": s_int4, "uint4": lambda c: c, "int8": s_int8, "e2m1": s_e2m1, "e4m3": s_e4m3,
+           "int3": lambda c: s_intb(c, 3), "int2": lambda c: s_intb(c, 2), "int1": lambda c: s_intb(c, 1),
+           "uint3": lambda c: c, "uint2": lambda c: c, "uint1": lambda c: c}[desc.weight_dtype]
     m, k = len(a_vals), desc.k
     out = []
     for i in range(m):
@@ -91,7 +97,14 @@ CASES = [
     ("e2m1", "group", 16, "e4m3", False, True),
     ("int4", "group", 32, "e8m0", False, False),
     ("int8", "tensor", 0, "f32", False, True),
+    ("int3", "group", 16, "bf16", False, False),
+    ("uint3", "group", 32, "bf16", True, False),
+    ("int2", "channel", 0, "f32", False, False),
+    ("uint2", "group", 16, "f32", True, True),
+    ("int1", "group", 32, "bf16", False, False),
+    ("uint1", "tensor", 0, "f32", True, False),
 ]
+BITS = {"int3": 3, "uint3": 3, "int2": 2, "uint2": 2, "int1": 1, "uint1": 1}
 
 
 @pytest.mark.parametrize("wd,gran,gs,sd,zp,gl", CASES)
@@ -108,6 +121,9 @@ def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
     elif wd == "int8":
         cu = g.integers(0, 256, size=(n, k)).astype(np.uint8)
         codes = cu[None]
+    elif wd in BITS:
+        cu = g.integers(0, 1 << BITS[wd], size=(n, k)).astype(np.uint8)
+        codes = pack_bits(cu, BITS[wd])[None]
     else:
         cu = g.integers(0, 16, size=(n, k)).astype(np.uint8)
         codes = pack_nibbles(cu)[None]
@@ -119,7 +135,7 @@ def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
         sc = g.integers(0x08, 0x7F, size=(sn, ng)).astype(np.uint8)   # positive finite, subnormals included
     else:
         sc = g.integers(119, 124, size=(sn, ng)).astype(np.uint8)
-    zeros = g.integers(0, 16, size=(sn, ng)).astype(np.uint8) if zp else None
+    zeros = g.integers(0, 1 << BITS.get(wd, 4), size=(sn, ng)).astype(np.uint8) if zp else None
     gsc = np.array([0.75], np.float32)
     a_bits = bf16_bits(g.standard_normal((m, k)).astype(np.float32))
     a = decode_bf16(a_bits)
@@ -303,3 +319,58 @@ def test_fp8_token_x_fp8_channel_vs_fraction_brute_force(m, n, k):
             bound = 1e-13 * float(sum(abs(t) for t in terms))
             assert abs(got1[i, j] - float(ref)) <= bound, (i, j, got1[i, j], float(ref))
             assert abs(got2[i, j] - float(ref)) <= bound, (i, j, got2[i, j], float(ref))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_bit_stream_unpacking_against_big_integer(bits):
+    """Code k of a canonical b-bit row is bits b*k .. b*k+b-1 of the row read
+    as one little-endian integer: checked through Python's arbitrary
+    precision integers, and for b = 4 against the nibble reading."""
+    from oracle.formats import unpack_bits, unpack_nibbles
+    g = np.random.default_rng(90 + bits)
+    rows = g.integers(0, 256, size=(3, 12 * bits)).astype(np.uint8)
+    got = unpack_bits(rows, bits)
+    assert got.shape == (3, 96)
+    for r in range(3):
+        big = int.from_bytes(bytes(rows[r].tolist()), "little")
+        want = [(big >> (bits * kk)) & ((1 << bits) - 1) for kk in range(96)]
+        assert got[r].tolist() == want
+    if bits == 4:
+        assert np.array_equal(got, unpack_nibbles(rows))
+
+
+def test_int3_stream_golden_bytes():
+    """Eight 3-bit codes 1..7, 0 written out by hand: 1 + 2*8 + 3*64 + 4*512
+    + 5*4096 + 6*32768 + 7*262144 = 0x1F58D1, little-endian bytes D1 58 1F;
+    as INT3 they read 1, 2, 3, -4, -3, -2, -1, 0."""
+    from oracle.formats import decode_weight_codes
+    row = np.array([[0xD1, 0x58, 0x1F]], np.uint8)
+    assert decode_weight_codes(row, "uint3")[0].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]
+    assert decode_weight_codes(row, "int3")[0].tolist() == [1, 2, 3, -4, -3, -2, -1, 0]
+    assert np.array_equal(pack_bits(np.array([[1, 2, 3, 4, 5, 6, 7, 0]], np.uint8), 3), row)
+
+
+@pytest.mark.parametrize("wd,vals", [("int1", [0, -1]), ("int2", [0, 1, -2, -1]),
+                                     ("int3", [0, 1, 2, 3, -4, -3, -2, -1]),
+                                     ("uint2", [0, 1, 2, 3]), ("uint1", [0, 1])])
+def test_low_bit_integer_value_sets(wd, vals):
+    """Every code of a b-bit integer format, one per element of an 8-code
+    row: the values are the two's complement (or unsigned) range."""
+    from oracle.formats import decode_weight_codes
+    b = BITS[wd]
+    codes = np.array([list(range(1 << b)) * (8 // (1 << b)) if (1 << b) <= 8 else list(range(8))], np.uint8)
+    got = decode_weight_codes(pack_bits(codes, b), wd)[0]
+    assert got.tolist() == (vals * (8 // len(vals)))
+
+
+@pytest.mark.parametrize("wd", ["uint1", "uint2", "uint3"])
+def test_low_bit_codes_equal_zero_point_give_zero(wd):
+    g = np.random.default_rng(24)
+    b = BITS[wd]
+    n, k, gs = 8, 256, 64
+    z = g.integers(0, 1 << b, size=(1, n, k // gs)).astype(np.uint8)
+    cu = np.repeat(z, gs, axis=2)
+    sc = bf16_bits(g.uniform(0.005, 0.02, size=(1, n, k // gs)).astype(np.float32))
+    a = decode_bf16(bf16_bits(g.standard_normal((3, k)).astype(np.float32)))
+    d = G.WeightDesc(wd, "group", gs, "bf16", True, False, 1, n, k)
+    assert np.all(G.linear(d, a, pack_bits(cu, b), sc, z) == 0)
