@@ -54,8 +54,21 @@ typedef enum hum_dtype {
                      scale dtype: NVFP4's group scale (E2M1 weights, G = 16,
                      finite codes) */
   HUM_E8M0 = 6,   /* power-of-two scale 2^(c-127) */
-  HUM_INT8 = 7    /* signed two's-complement byte, -128..127 (W8A16: bf16
+  HUM_INT8 = 7,   /* signed two's-complement byte, -128..127 (W8A16: bf16
                      activations, per-channel or per-tensor f32 scales) */
+  /* Low-bit integer weights ("Announcing Humming", section "WnA16": the
+     shared dequantization path covers INT1, INT2 and INT3 as well): b-bit
+     codes packed as an LSB-first bit stream along K (code k of a row at
+     bits b*k .. b*k+b-1 of the row's bytes read as one little-endian
+     integer; codes [E][N][K*b/8]).  Signed: two's complement; unsigned:
+     0..2^b-1 with an optional zero point.  bf16 activations, bf16 / f32
+     scales per tensor, channel or group (G a multiple of 128). */
+  HUM_INT3 = 8,   /* -4..3 */
+  HUM_UINT3 = 9,  /* 0..7 */
+  HUM_INT2 = 10,  /* -2..1 */
+  HUM_UINT2 = 11, /* 0..3 */
+  HUM_INT1 = 12,  /* -1..0 */
+  HUM_UINT1 = 13  /* 0..1 */
 } hum_dtype;
 
 typedef enum hum_scale_gran {
@@ -79,11 +92,13 @@ typedef enum hum_act_fmt {
 
 /* The quantization description of one weight tensor [E][N][K]. */
 typedef struct hum_weight_desc {
-  int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_INT8 | HUM_E2M1 | HUM_E4M3 */
+  int32_t weight_dtype;      /* HUM_INT4 | HUM_UINT4 | HUM_INT8 | HUM_E2M1 | HUM_E4M3 |
+                                HUM_INT3 .. HUM_UINT1 */
   int32_t scale_gran;        /* hum_scale_gran */
   int32_t group_size;        /* K elements per group (HUM_SCALE_GROUP), block edge (HUM_SCALE_BLOCK) */
   int32_t scale_dtype;       /* HUM_BF16 | HUM_F32 | HUM_E8M0 */
-  int32_t has_zero_point;    /* 0/1; UINT4 only; zeros u8 [E][N][K/G] (0..15) */
+  int32_t has_zero_point;    /* 0/1; unsigned integer codes only (UINT4 .. UINT1);
+                                zeros u8 [E][N][K/G] (0..2^b-1) */
   int32_t has_global_scale;  /* 0/1; second-level f32 scale per expert, [E] */
   int32_t act_fmt;           /* hum_act_fmt the layer runs with */
   int32_t num_experts;       /* E >= 1 (dense layers use 1) */
@@ -118,7 +133,8 @@ typedef struct hum_tile_config {
 size_t hum_packed_weight_bytes(const hum_weight_desc* desc);
 
 /* Canonical ("standard format") tensors -> packed kernel layout.
- *   codes  : u8 [E][N][K/2] (4-bit) or [E][N][K] (INT8, E4M3)
+ *   codes  : u8 [E][N][K/2] (4-bit), [E][N][K] (INT8, E4M3) or
+ *            [E][N][K*b/8] (b-bit integers, b = 1, 2, 3)
  *   scales : [E][N'][K/G'] in scale_dtype (N' = 1 for TENSOR, G' per gran)
  *   zeros  : u8 [E][N'][K/G'] or NULL when has_zero_point == 0
  *   global_scale : f32 [E] or NULL when has_global_scale == 0

@@ -54,6 +54,12 @@ hum_status check_desc(const hum_weight_desc* d) {
   switch (d->weight_dtype) {
     case HUM_INT4:
     case HUM_UINT4:
+    case HUM_INT3:
+    case HUM_UINT3:
+    case HUM_INT2:
+    case HUM_UINT2:
+    case HUM_INT1:
+    case HUM_UINT1:
       if (d->scale_dtype == HUM_E8M0) {
         // MXINT4: signed INT4 codes with an E8M0 scale per 32 along K
         if (d->weight_dtype != HUM_INT4 || d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32)
@@ -65,7 +71,8 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "integer weights run with bf16 activations");
       if (d->scale_dtype != HUM_BF16 && d->scale_dtype != HUM_F32) return set_error(HUM_ERR_UNSUPPORTED, "integer weights take bf16 or f32 scales");
       if (d->scale_gran == HUM_SCALE_GROUP && d->group_size % 128) return set_error(HUM_ERR_UNSUPPORTED, "integer group_size must be a multiple of 128");
-      if (d->has_zero_point && d->weight_dtype != HUM_UINT4) return set_error(HUM_ERR_UNSUPPORTED, "zero points need UINT4 codes");
+      if (d->has_zero_point && dtype_int_signed(d->weight_dtype))
+        return set_error(HUM_ERR_UNSUPPORTED, "zero points need unsigned integer codes");
       return HUM_OK;
     case HUM_E2M1:
       if (d->scale_dtype == HUM_E4M3) {
@@ -103,7 +110,13 @@ hum_status check_desc(const hum_weight_desc* d) {
 
 int fmt_of(const hum_weight_desc* d) {
   if (d->weight_dtype == HUM_INT4 && d->scale_dtype == HUM_E8M0) return F_MXINT4_BF16;
-  if (d->weight_dtype == HUM_INT4 || d->weight_dtype == HUM_UINT4) return F_INT;
+  switch (dtype_int_bits(d->weight_dtype)) {
+    case 4: return F_INT;
+    case 3: return F_INT3;
+    case 2: return F_INT2;
+    case 1: return F_INT1;
+    default: break;
+  }
   if (d->weight_dtype == HUM_INT8) return F_INT8_BF16;
   if (d->weight_dtype == HUM_E4M3)
     return d->scale_gran == HUM_SCALE_BLOCK ? F_FP8_BLOCK : (d->act_fmt == HUM_ACT_BF16 ? F_FP8_BF16 : F_FP8);
@@ -120,9 +133,9 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   L->kb = d->k / kKBlk;
   L->kb4 = cdiv(L->kb, 4);
   const int f = fmt_of(d);
-  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || fmt_w8_bf16(f)) ? 32 : 16;
+  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || fmt_w8_bf16(f)) ? 32 : (fmt_int(f) ? 4 * fmt_int_bits(f) : 16);
   L->codes_per_expert = L->nt * L->kb * 64 * L->code_bytes;
-  if (f == F_INT) {
+  if (fmt_int(f)) {
     const bool grp = d->scale_gran == HUM_SCALE_GROUP && d->group_size < d->k;
     L->ng = grp ? d->k / d->group_size : 1;
     L->kb_per_group = grp ? d->group_size / kKBlk : (int)L->kb;
@@ -218,7 +231,9 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     c.waves_n = 1;
     const bool bf16_act = fmt_bf16_act(fmt_of(d));
     const int64_t a_bytes = m * (bf16_act ? 2 : 1);            // per k
-    const int64_t w_bytes16 = (fmt_of(d) == F_FP8 || fmt_w8_bf16(fmt_of(d))) ? 16 : 8;      // per k of a 16-column sub-tile
+    const int64_t w_bytes16 = (fmt_of(d) == F_FP8 || fmt_w8_bf16(fmt_of(d)))
+                                  ? 16
+                                  : (fmt_int(fmt_of(d)) ? 2 * fmt_int_bits(fmt_of(d)) : 8);  // per k of a 16-column sub-tile
     const int64_t need = cdiv(a_bytes, w_bytes16);
     c.wave_n = need <= 1 ? 1 : (need <= 2 ? 2 : 4);
     const int64_t wgs = cdiv(nt, c.wave_n);
@@ -278,7 +293,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       }
       c.split_k = 1;
     }
-    if ((fmt_of(d) == F_INT && m >= 256) || (fmt_of(d) == F_MXFP4_BF16 && m >= 512)) {
+    if ((fmt_int(fmt_of(d)) && m >= 256) || (fmt_of(d) == F_MXFP4_BF16 && m >= 512)) {
       // INT / MXFP4 weights with bf16 activations: 32 x 32 MFMA blocks (the
       // bf16 16x16x32 shape issues at about half the 32x32x16 rate).
       // Measured on MI355X at N = K = 8192: INT 64 x 128 tiles with three
@@ -287,7 +302,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       // two above
       c.kind = HUM_KERNEL_TILE32;
       c.wave_m = 4;
-      c.wave_n = (fmt_of(d) == F_INT && m < 512) ? 2 : 4;
+      c.wave_n = (fmt_int(fmt_of(d)) && m < 512) ? 2 : 4;
       c.stages = m <= 1024 ? 3 : 2;
       if (fmt_of(d) == F_MXFP4_BF16 && m > 1024) c.wave_m = 8;
       c.split_k = 1;
@@ -431,7 +446,7 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
                               : (d->act_fmt == HUM_ACT_FP8_GROUP ? m * (d->k / 128) * 4 : m * 4)));
   }
   w.rowsum = off;
-  if (fmt_of(d) == F_INT && c.kind != HUM_KERNEL_STREAM) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
+  if (fmt_int(fmt_of(d)) && c.kind != HUM_KERNEL_STREAM) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
   w.total = off;
   return w;
 }
@@ -567,7 +582,7 @@ static void fill_weight_params(GemmParams& p, const hum_weight_desc* d, const La
   p.inv_kbg = 1.0f / (float)L.kb_per_group;
   p.kb4 = (int)L.kb4;
   p.scale_f32 = L.scale_f32;
-  p.int_offset = (d->weight_dtype == HUM_INT4) ? 136 : 128;
+  p.int_offset = dtype_int_signed(d->weight_dtype) ? 128 + (1 << (dtype_int_bits(d->weight_dtype) - 1)) : 128;
   p.has_zero = d->has_zero_point;
   p.n = d->n;
   p.swiglu_nt_off = 0;
@@ -610,7 +625,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   }
   GemmParams p{};
   fill_weight_params(p, desc, L, packed);
-  if (fmt_of(desc) == F_INT && c.kind != HUM_KERNEL_STREAM) {
+  if (fmt_int(fmt_of(desc)) && c.kind != HUM_KERNEL_STREAM) {
     st = launch_rowsum(a_use, desc->k, m, (int)L.kb, (int)L.kbc, ws + w.rowsum, stream);
     if (st != HUM_OK) return st;
     p.a_rowsum = ws + w.rowsum;

@@ -62,6 +62,9 @@ struct ReduceInstance {
 
 static const ReduceInstance kReduces[] = {
     {F_INT, EPI_BF16, splitk_reduce_kernel<F_INT, EPI_BF16>},
+    {F_INT3, EPI_BF16, splitk_reduce_kernel<F_INT3, EPI_BF16>},
+    {F_INT2, EPI_BF16, splitk_reduce_kernel<F_INT2, EPI_BF16>},
+    {F_INT1, EPI_BF16, splitk_reduce_kernel<F_INT1, EPI_BF16>},
     {F_FP8, EPI_BF16, splitk_reduce_kernel<F_FP8, EPI_BF16>},
     {F_MXFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_BF16>},
     {F_MXFP4_BF16, EPI_SWIGLU_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SWIGLU_BF16>},
@@ -87,8 +90,9 @@ static const ReduceInstance kReduces[] = {
 };
 
 static const Instance* find_instance(const KernelKey& k) {
-  static const InstanceTable tables[] = {instances_dense_a(), instances_dense_b(), instances_moe_a(),
-                                         instances_moe_b(), instances_moe_c()};
+  static const InstanceTable tables[] = {instances_dense_a(), instances_dense_b(), instances_dense_c(),
+                                         instances_dense_d(), instances_moe_a(), instances_moe_b(),
+                                         instances_moe_c()};
   for (const InstanceTable& t : tables)
     for (int i = 0; i < t.n; ++i) {
       const KernelKey& q = t.p[i].key;

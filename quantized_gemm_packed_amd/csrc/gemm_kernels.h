@@ -25,7 +25,8 @@
 //
 // Formats:
 //   F_INT          INT4/UINT4 -> bf16 (128 + u) with one AND-OR per two
-//                  codes; a K-block accumulates in fp32 and
+//                  codes (F_INT3 / F_INT2 / F_INT1: b-bit codes from bit
+//                  planes, one or two AND-ORs per two codes); a K-block accumulates in fp32 and
 //                  s * (P - (128 + z) * sum(a)) applies scale, zero point and
 //                  the offset (exact for integer codes).
 //   F_MXFP4_BF16   E2M1 with its E8M0 scale -> bf16 through
@@ -72,6 +73,10 @@ struct Tr {
   static constexpr int kBWords =
       (FMT == F_FP8 || FMT == F_FP8_BLOCK || fmt_w8_bf16(FMT)) ? 2 : 1;  // 16-B words / lane / K-block
   static constexpr bool kBf16 = fmt_bf16_act(FMT);
+  // integer family: bits per code; code bytes per lane per K-block (b-bit
+  // integers: 4b, else 16 per 16-byte word)
+  static constexpr int kIntBits = fmt_int_bits(FMT);
+  static constexpr int kCodeB = fmt_int(FMT) ? 4 * kIntBits : 16 * kBWords;
   // MX / NVFP4 weight scales: a metadata row (a dword per lane) covers
   // 1 << kMetaRowShift K-blocks (E8M0 per 32: 4; NVFP4's two E4M3 per 32: 2)
   static constexpr int kMetaRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
@@ -82,9 +87,37 @@ struct Tr {
 // ---------------------------------------------------------------------------
 // Weight fragments
 
+// A lane's code words of one K-block: 16-byte words, or for b-bit integers
+// (b < 4) b dwords.
+template <int B>
+struct CodeWord { using type = u32x4_t; };
+template <> struct CodeWord<12> { using type = u32x3_t; };
+template <> struct CodeWord<8> { using type = u32x2_t; };
+template <> struct CodeWord<4> { using type = u32x1_t; };
+
+template <int FMT>
+using CodeW = typename CodeWord<Tr<FMT>::kCodeB < 16 ? Tr<FMT>::kCodeB : 16>::type;
+
+// One buffer load of a lane's code word (16-byte words: one of them).
+template <int FMT>
+__device__ __forceinline__ CodeW<FMT> load_code_word(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  constexpr int B = Tr<FMT>::kCodeB;
+  if constexpr (B == 4) {
+    CodeW<FMT> w;
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return w;
+  } else if constexpr (B == 8) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  } else if constexpr (B == 12) {
+    return __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  }
+}
+
 template <int FMT>
 struct BFrag {
-  u32x4_t w[Tr<FMT>::kBWords];
+  CodeW<FMT> w[Tr<FMT>::kBWords];
   // raw metadata words as loaded (decoded where the fragment is used, so
   // that no arithmetic waits on a load where it is issued)
   uint32_t meta;  // INT: dword holding the column's scale; MX: E8M0 codes of 4 K-blocks
@@ -141,14 +174,14 @@ __device__ __forceinline__ void dma_b32(u32x4_t r, const void* lds, uint32_t vof
 
 template <int FMT>
 __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs& w, int nt, bool valid) {
-  constexpr int kCB = 16 * Tr<FMT>::kBWords;  // code bytes per lane per K-block
+  constexpr int kCB = Tr<FMT>::kCodeB;  // code bytes per lane per K-block
   const int64_t ntc = valid ? nt : 0;
   WStripe s;
   const int64_t cb = (int64_t)p.kb_count * 64 * kCB;
   s.codes = make_rsrc(w.codes + ntc * cb, valid ? cb : 0);
   s.meta = s.codes;
   s.zero = s.codes;
-  if (FMT == F_INT) {
+  if (fmt_int(FMT)) {
     const int64_t sb = (int64_t)p.ng * 16 * (p.scale_f32 ? 4 : 2);
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
     const int64_t zb = (int64_t)p.ng * 8;
@@ -164,14 +197,14 @@ __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs&
 // META = false loads the codes only (the caller holds the metadata).
 template <int FMT, bool META = true>
 __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe& s, bool ok, int kb, int lane) {
-  constexpr int kCB = 16 * Tr<FMT>::kBWords;
+  constexpr int kCB = Tr<FMT>::kCodeB;
   BFrag<FMT> f;
   const uint32_t co = ok ? (uint32_t)(kb * 64 + lane) * kCB : kOob;
 #pragma unroll
-  for (int i = 0; i < Tr<FMT>::kBWords; ++i) f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(s.codes, co + 16 * i, 0, 0);
+  for (int i = 0; i < Tr<FMT>::kBWords; ++i) f.w[i] = load_code_word<FMT>(s.codes, co + 16 * i);
   f.meta = 0;
   f.zero = 0;
-  if (META && FMT == F_INT) {
+  if (META && fmt_int(FMT)) {
     const int c16 = lane & 15;
     // floor(kb / kb_per_group), exact in fp32: kb < 2^14, and the quotient
     // of (kb + 1/2) sits at least 1/(2 kb_per_group) from an integer
@@ -188,21 +221,6 @@ __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe&
     const uint32_t mo = ok ? (uint32_t)((kb >> Tr<FMT>::kMetaRowShift) * 64 + lane) * 4 : kOob;
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
   }
-  return f;
-}
-
-// INT metadata words of one K-block of a stripe (zeros when !ok): the
-// scale dword and zero-point dword of column lane & 15.
-__device__ __forceinline__ BFrag<F_INT> load_b_meta_int(const GemmParams& p, const WStripe& s, bool ok, int kb,
-                                                        int lane) {
-  BFrag<F_INT> f;
-  const int c16 = lane & 15;
-  const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
-  const int sf = p.scale_f32;
-  const uint32_t so = ok ? (uint32_t)(gi * 16 + (c16 & (14 | sf))) << (1 + sf) : kOob;
-  f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
-  const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
-  f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
   return f;
 }
 
@@ -244,6 +262,38 @@ __device__ __forceinline__ bf16x8_t int_dequant(uint32_t w) {
   o[2] = and_or(w >> 8, m, g);
   o[3] = and_or(w >> 12, m, g);
   return __builtin_bit_cast(bf16x8_t, o);
+}
+
+// bf16 operand (128 + u pairs) of 8-k step s of a b-bit integer fragment:
+// the lane's code words of one K-block in the packed bit-plane order (4-bit:
+// step s in dword s; 2-bit plane: step s in dword s / 2, byte pair s & 1;
+// 1-bit plane: the last dword, nibble pair s).  s is a constant after
+// unrolling.
+template <int BITS, typename W>
+__device__ __forceinline__ bf16x8_t int_dequant_step(const W& w, int s) {
+  if constexpr (BITS == 4) {
+    return int_dequant(w[s]);
+  } else {
+    const uint32_t g = 0x43004300u;
+    u32x4_t o;
+    if constexpr (BITS == 1) {
+      const uint32_t x = w[0] >> (4 * s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = and_or(x >> i, 0x00010001u, g);
+    } else {
+      const uint32_t x = w[s >> 1] >> (8 * (s & 1));
+      if constexpr (BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = and_or(x >> (2 * i), 0x00030003u, g);
+      } else {
+        // bit 2 of each code from the 1-bit plane, moved to bit 2 of its half
+        const uint32_t z = (w[2] >> (4 * s)) << 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = and_or(z >> i, 0x00040004u, and_or(x >> (2 * i), 0x00030003u, g));
+      }
+    }
+    return __builtin_bit_cast(bf16x8_t, o);
+  }
 }
 
 __device__ __forceinline__ bf16x8_t mx_dequant(uint32_t w, float scale) {
@@ -292,10 +342,10 @@ __device__ __forceinline__ bf16x8_t nv_dequant(uint32_t w, float scale) {
 // bf16 B operand of the 4 k-steps of a K-block.
 template <int FMT>
 __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, int kb, bf16x8_t (&d)[4]) {
-  if (FMT == F_INT) {
+  if constexpr (fmt_int(FMT)) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) d[s] = int_dequant(f.w[0][s]);
-  } else if (FMT == F_FP8_BF16) {
+    for (int s = 0; s < 4; ++s) d[s] = int_dequant_step<Tr<FMT>::kIntBits>(f.w[0], s);
+  } else if constexpr (FMT == F_FP8_BF16) {
     // E4M3 -> bf16 is exact (3 mantissa bits, exponents within bf16's
     // range): the hardware conversion with a unit scale, two codes per
     // instruction; k-step s takes bytes 8s .. 8s+7 of the lane's 32
@@ -309,7 +359,7 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
-  } else if (FMT == F_MXINT4_BF16) {
+  } else if constexpr (FMT == F_MXINT4_BF16) {
     // MXINT4: the integer path's nibble order (k-step s in dword s, element
     // j at bit (j & 1) * 16 + (j >> 1) * 4) holding q + 8; (u - 8) * 2^E is
     // one exact FMA in f32, packed to bf16 by its upper half (at most 4
@@ -328,7 +378,7 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       }
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
-  } else if (FMT == F_NVFP4_BF16) {
+  } else if constexpr (FMT == F_NVFP4_BF16) {
     // k-steps 2h and 2h + 1 (k = 32 lg + 16 h + [0, 16)) share the E4M3
     // scale in byte 2 (kb & 1) + h of the lane's word
     const uint32_t half = meta >> (16 * (kb & 1));
@@ -337,7 +387,7 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
     d[1] = nv_dequant(f.w[0][1], f0);
     d[2] = nv_dequant(f.w[0][2], f1);
     d[3] = nv_dequant(f.w[0][3], f1);
-  } else if (FMT == F_INT8_BF16) {
+  } else if constexpr (FMT == F_INT8_BF16) {
     // INT8 -> bf16 is exact (|q| <= 128): each byte sign-extended to f32,
     // and two f32 packed by their upper halves (whose lower halves are zero
     // for integers this small); same byte order as the FP8 branch
@@ -664,7 +714,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   for (int ns = 0; ns < WN; ++ns) st[ns] = make_stripe<FMT>(p, wp, nts[ns], ntv[ns]);
   // first scale group / first 4-K-block E8M0 row of the K range (the LDS
   // metadata starts there)
-  const int g0 = (FMT == F_INT) ? kb_begin / p.kb_per_group : 0;
+  const int g0 = fmt_int(FMT) ? kb_begin / p.kb_per_group : 0;
   constexpr int kRS = T::kMetaRowShift;
   const int r0 = kb_begin >> kRS;
   auto stage = [&]() {
@@ -731,7 +781,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     }
     // weight metadata of the K range, per valid sub-tile (filler lanes read
     // the stripe's first bytes, which always exist)
-    if (FMT == F_INT && nkb > 0) {
+    if (fmt_int(FMT) && nkb > 0) {
       const int g1 = (kb_end - 1) / p.kb_per_group + 1;
       const int ss = p.scale_f32 ? 4 : 2;
       const int n16 = (g1 - g0) * ss;  // 16-byte slots of scales
@@ -817,11 +867,11 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     // weight metadata of the wave's K-blocks (INT: scales and zero points of
     // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
     constexpr int kML =
-        (FMT == F_INT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
+        fmt_int(FMT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
     u32x4_t mbuf[WN][kML > 0 ? kML : 1];
     uint32_t zbuf[WN];
     int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
-    if (FMT == F_INT && nj > 0) {
+    if (fmt_int(FMT) && nj > 0) {
       const int g0w = kw0 / p.kb_per_group, g1w = (kw0 + nj - 1) / p.kb_per_group + 1;
       const int ss = p.scale_f32 ? 4 : 2;
       mb0 = g0w * 16 * ss;
@@ -843,7 +893,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
         const int b = (i * 64 + lane) * 16;
         mbuf[ns][i] = __builtin_amdgcn_raw_buffer_load_b128(st[ns].meta, b < mbytes ? (uint32_t)(mb0 + b) : kOob, 0, 0);
       }
-      if (FMT == F_INT)
+      if (fmt_int(FMT))
         zbuf[ns] = __builtin_amdgcn_raw_buffer_load_b32(st[ns].zero,
                                                         lane * 4 < zbytes ? (uint32_t)(zb0 + lane * 4) : kOob, 0, 0);
     }
@@ -857,7 +907,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
 #pragma unroll
       for (int i = 0; i < kML; ++i)
         if ((i * 64 + lane) * 16 < mbytes) *reinterpret_cast<u32x4_t*>(mb + mdst + (i * 64 + lane) * 16) = mbuf[ns][i];
-      if (FMT == F_INT && lane * 4 < zbytes) *reinterpret_cast<uint32_t*>(mb + zdst + lane * 4) = zbuf[ns];
+      if (fmt_int(FMT) && lane * 4 < zbytes) *reinterpret_cast<uint32_t*>(mb + zdst + lane * 4) = zbuf[ns];
     }
   };
 
@@ -888,7 +938,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     const uint8_t* mb = dsm + p.lds_meta_off + ns * p.lds_meta_stride;
     m = 0;
     z = 0;
-    if (FMT == F_INT) {
+    if (fmt_int(FMT)) {
       const int gl = (int)(((float)kb + 0.5f) * p.inv_kbg) - g0;
       const int sf = p.scale_f32;
       m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
@@ -914,7 +964,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
           for (int s = 0; s < 4; ++s)
             af[s] = *reinterpret_cast<const bf16x8_t*>(ab + (((4 * lg + s) ^ rr) * 16));
           f32x4_t rs = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (FMT == F_INT) {
+          if (fmt_int(FMT)) {
             // row sums of the K-block in the C layout: A x ones
             const u32x4_t o = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
             const bf16x8_t one = __builtin_bit_cast(bf16x8_t, o);
@@ -927,7 +977,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
             uint32_t mw, zw;
             lds_meta(ns, kb, mw, zw);
             dequant_b<FMT>(ring[q][ns], mw, kb, d);
-            if (FMT == F_INT) {
+            if (fmt_int(FMT)) {
               const f32x4_t t = mfma_bf16_kblock(af, d, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
               const float sc = frag_int_scale(mw, ssel);
               const float off = (float)(p.int_offset + frag_int_zero(zw, c16));
@@ -1044,7 +1094,7 @@ struct TileCfg {
   // a per-group FP8 row
   static constexpr bool kX = (FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_FP8_BLOCK);
   static constexpr int kXI = kX ? (kTM + 63) / 64 : 0;           // its 256-B DMA instructions
-  static constexpr int kCB = 1024 * T::kBWords;                  // code bytes per sub-tile per K-block
+  static constexpr int kCB = 64 * T::kCodeB;                     // code bytes per sub-tile per K-block
   // Each wave loads its own weight fragments straight into registers,
   // kS - 1 K-blocks ahead, one register set per stage (they are private to
   // the wave: staging them through LDS would only add LDS traffic).
@@ -1055,7 +1105,7 @@ struct TileCfg {
   // register fragments (two stages deep) are exact; two stages issue them
   // from inline assembly and wait for everything at the end of each step.
   static constexpr bool kTracked = (kS == 3);
-  static constexpr int kMI = (FMT == F_INT || FMT == F_FP8_BLOCK)
+  static constexpr int kMI = (fmt_int(FMT) || FMT == F_FP8_BLOCK)
                                  ? 1
                                  : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
                                      FMT == F_NVFP4_BF16) ? WN : 0);
@@ -1066,7 +1116,7 @@ struct TileCfg {
   static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
   static_assert(kA % 1024 == 0, "whole 1-KB activation DMA instructions");
   static_assert(kS * kStage <= 160 * 1024, "LDS budget");
-  static_assert(FMT != F_INT || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
+  static_assert(!fmt_int(FMT) || WN * 16 <= 64, "INT scale words of a wave fit one DMA instruction");
 };
 
 // Physical 16-byte chunk of logical chunk c of LDS tile row r, for rows of
@@ -1117,7 +1167,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
   using T = typename C::T;
   constexpr int kAE = T::kAElem;
-  static_assert(MS == 16 || (MS == 32 && (FMT == F_INT || FMT == F_MXFP4_BF16) && WM % 2 == 0 && WN % 2 == 0 &&
+  static_assert(MS == 16 || (MS == 32 && (fmt_int(FMT) || FMT == F_MXFP4_BF16) && WM % 2 == 0 && WN % 2 == 0 &&
                              AMODE == A_DIRECT && EPI == EPI_BF16),
                 "32x32 blocks: dense bf16-activation INT / MXFP4 tiles of even sub-tile counts");
   constexpr int MP = MS == 32 ? WM / 2 : 1, NP = MS == 32 ? WN / 2 : 1;
@@ -1224,7 +1274,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   __amdgpu_buffer_rsrc_t rbr[WN];  // code stripes (invalid sub-tiles read sub-tile 0)
 #pragma unroll
   for (int ns = 0; ns < WN; ++ns) {
-    const int64_t cb = (int64_t)p.kb_count * 64 * 16 * T::kBWords;
+    const int64_t cb = (int64_t)p.kb_count * C::kCB;
     const uint8_t* base = wp.codes + (ntv[ns] ? (int64_t)nts[ns] : 0) * cb;
     rbr[ns] = make_rsrc(base, cb);
   }
@@ -1239,7 +1289,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   __amdgpu_buffer_rsrc_t rmsr = rar;
   const int sf = p.scale_f32;
   uint32_t mi_off = 0, mi_gmul = 0;
-  if constexpr (FMT == F_INT) {
+  if constexpr (fmt_int(FMT)) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
     const int nsw = (8 << sf) * WN;  // scale words (<= 64)
@@ -1295,18 +1345,18 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     {
       // (compiler-tracked loads.  A lane's kBWords 16-byte words sit side
       // by side in the packed layout.)
-      const uint32_t boff = (uint32_t)kb * C::kCB + lane * 16 * T::kBWords;
+      const uint32_t boff = (uint32_t)kb * C::kCB + lane * T::kCodeB;
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns)
 #pragma unroll
         for (int h = 0; h < T::kBWords; ++h)
-          bdst[ns].w[h] = __builtin_amdgcn_raw_buffer_load_b128(rbr[ns], boff + h * 16, 0, 0);
+          bdst[ns].w[h] = load_code_word<FMT>(rbr[ns], boff + h * 16);
       // (the offset stays live past the loads: no load's destination
       // reuses the register another load reads its address from)
       asm volatile("" ::"v"(boff));
     }
     uint8_t* mw = St::m(st) + wn * C::kMI * 256;
-    if constexpr (FMT == F_INT) {
+    if constexpr (fmt_int(FMT)) {
       const int gi = (int)(((float)kb + 0.5f) * p.inv_kbg);
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_FP8_BLOCK) {
@@ -1378,7 +1428,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
       for (int h = 0; h < T::kBWords; ++h)
         bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
-                               : *reinterpret_cast<const u32x4_t*>(bbase + ns * C::kCB + lane * 16 * T::kBWords + h * 16);
+                               : *reinterpret_cast<const CodeW<FMT>*>(bbase + ns * C::kCB + lane * T::kCodeB + h * 16);
       mw[ns] = 0;
       if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
@@ -1407,7 +1457,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       }
       return;
     }
-    if constexpr (FMT == F_INT) {
+    if constexpr (fmt_int(FMT)) {
       // this lane's scale words of the WN sub-tiles, side by side (one
       // aligned vector read)
       struct alignas(4 * WN) Words { uint32_t w[WN]; };
@@ -1418,12 +1468,15 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     if constexpr (T::kBf16 && MS == 32) {
       const int h = lane >> 5;
       const bool hi = (lane & 16) != 0;  // the lane's column is in the pair's second sub-tile
-      uint32_t cw[NP][2][4];  // code dwords after the swap, [pair][R][s]
+      // code dwords after the swap, [pair][R][dword] (a lane's 4-bit codes:
+      // dword s = step s; b-bit integers: their b bit-plane dwords)
+      constexpr int kND = T::kCodeB / 4;
+      CodeW<FMT> cw[NP][2];
       uint32_t mp2[NP][2];    // MXFP4: E8M0 words after the same swap
 #pragma unroll
       for (int np = 0; np < NP; ++np) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < kND; ++s) {
           const auto r = __builtin_amdgcn_permlane16_swap(bf[2 * np].w[0][s], bf[2 * np + 1].w[0][s], false, false);
           cw[np][0][s] = r[0];
           cw[np][1][s] = r[1];
@@ -1438,7 +1491,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
       // scaled by the lane's column scale (the offset is taken off after the
       // K loop); MXFP4: scaled in the widening, accumulated in place
       f32x16_t tk[MP][NP];
-      if constexpr (FMT == F_INT) {
+      if constexpr (fmt_int(FMT)) {
 #pragma unroll
         for (int mp = 0; mp < MP; ++mp)
 #pragma unroll
@@ -1453,8 +1506,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
           bf16x8_t dd[NP];
 #pragma unroll
           for (int np = 0; np < NP; ++np) {
-            if constexpr (FMT == F_INT)
-              dd[np] = int_dequant(cw[np][R][s]);
+            if constexpr (fmt_int(FMT))
+              dd[np] = int_dequant_step<T::kIntBits>(cw[np][R], s);
             else
               dd[np] = mx_dequant(cw[np][R][s], e8m0_to_f32(frag_mx_code(mp2[np][R], kb)));
           }
@@ -1465,14 +1518,14 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + ((chunk ^ (r & 15)) * 16));
 #pragma unroll
             for (int np = 0; np < NP; ++np) {
-              if constexpr (FMT == F_INT)
+              if constexpr (fmt_int(FMT))
                 tk[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dd[np], tk[mp][np], 0, 0, 0);
               else
                 acc32[mp][np] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dd[np], acc32[mp][np], 0, 0, 0);
             }
           }
         }
-      if constexpr (FMT == F_INT) {
+      if constexpr (fmt_int(FMT)) {
 #pragma unroll
         for (int np = 0; np < NP; ++np) {
           // the scale word of the lane's column (sub-tile 2 np + hi), read
@@ -1498,7 +1551,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           af[s] = *reinterpret_cast<const bf16x8_t*>(abase + r * C::kRowB + (((4 * lg + s) ^ c16) * 16));
-        if constexpr (FMT == F_INT) {
+        if constexpr (fmt_int(FMT)) {
           // one K-block of (128 + u) codes, scaled; the offset it carries
           // is taken off after the K loop
 #pragma unroll
@@ -1597,7 +1650,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA outlives the workgroup's LDS
 
-  if constexpr (FMT == F_INT) {
+  if constexpr (fmt_int(FMT)) {
     // The K loop summed s * (128 + u) a per K-block; the offset part,
     // sum over K-blocks of s (offset + z) * (sum of the block's a), is one
     // more small product, taken here on the MFMA: row sums (A) times the
@@ -1882,6 +1935,8 @@ struct InstanceTable {
 // One table per translation unit.
 InstanceTable instances_dense_a();
 InstanceTable instances_dense_b();
+InstanceTable instances_dense_c();
+InstanceTable instances_dense_d();
 InstanceTable instances_moe_a();
 InstanceTable instances_moe_b();
 InstanceTable instances_moe_c();

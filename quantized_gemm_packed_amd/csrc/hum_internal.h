@@ -16,15 +16,25 @@
 //           bf16 pair (128 + u_{2j}, 128 + u_{2j+1}).  INT4 is stored
 //           offset by 8 (u = v + 8).  E2M1 keeps the canonical order (even
 //           k in the low nibble).
-//   meta  : INT4/UINT4 : scales [NT][NG][16] (bf16 or f32), zeros
+//           b-bit integers (b = 3, 2, 1; B = 4b): the same 32 codes per lane
+//           in the same element order (element j of 8-k step s is k = 32*lg
+//           + 8*s + j), split into bit planes.  A 2-bit plane (b = 2, 3) is
+//           two dwords: step s in dword s/2, element j at bit (j & 1) * 16 +
+//           2 * (4 * (s & 1) + j / 2), so that (w >> 2i) & 0x00030003 |
+//           0x43004300 is a bf16 pair.  A 1-bit plane (b = 1, 3) is one dword
+//           after it: element j of step s at bit (j & 1) * 16 + 4 * s + j / 2.
+//           For b = 3 the 1-bit plane holds bit 2 of each code.  Signed codes
+//           are stored offset by 2^(b-1).
+//   meta  : INTb/UINTb : scales [NT][NG][16] (bf16 or f32), zeros
 //                        [NT][NG][8 bytes] (16 nibbles, column c at nibble c)
 //           E2M1/E8M0  : scales [NT][KB4][64 lanes][4 bytes], byte i of the
 //                        dword of lane l is the E8M0 code of column c and
 //                        32-block lg of K-block 4*kb4 + i
 //           E4M3       : scales f32 [NT*16]
-//   offset terms (INT4 / UINT4 only): -s * (offset + z) per column and
+//   offset terms (integer formats only): -s * (offset + z) per column and
 //           K-block, where offset + z is what the bf16 (128 + u) codes carry
-//           beyond the code's value (INT4: 136, UINT4: 128 + zero point).  As
+//           beyond the code's value (signed b-bit: 128 + 2^(b-1), unsigned:
+//           128 + zero point).  As
 //           bf16 hi / lo pairs, [NT][KBC][64 lanes][8] hi then the same for
 //           lo, KBC = ceil(KB / 32): lane l = c + 16*lg holds K-blocks
 //           32*kbc + 8*lg + (0..7) of column c -- the B operand of a 16x16x32
@@ -57,12 +67,29 @@ struct Layout {
 
 enum Fmt : int {
   F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6,
-  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8, F_MXINT4_BF16 = 9
+  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8, F_MXINT4_BF16 = 9, F_INT3 = 10, F_INT2 = 11, F_INT1 = 12
 };
+
+// The integer family (b-bit codes with bf16 / f32 group scales, optional
+// zero points, bf16 activations): one kernel path, b = 4, 3, 2, 1.
+constexpr bool fmt_int(int f) { return f == F_INT || f == F_INT3 || f == F_INT2 || f == F_INT1; }
+constexpr int fmt_int_bits(int f) { return f == F_INT3 ? 3 : (f == F_INT2 ? 2 : (f == F_INT1 ? 1 : 4)); }
+
+// Bits of an integer-family weight dtype (0 for the others), and whether
+// its codes are signed.
+constexpr int dtype_int_bits(int dt) {
+  return (dt == HUM_INT4 || dt == HUM_UINT4) ? 4
+         : (dt == HUM_INT3 || dt == HUM_UINT3) ? 3
+         : (dt == HUM_INT2 || dt == HUM_UINT2) ? 2
+         : (dt == HUM_INT1 || dt == HUM_UINT1) ? 1 : 0;
+}
+constexpr bool dtype_int_signed(int dt) {
+  return dt == HUM_INT4 || dt == HUM_INT3 || dt == HUM_INT2 || dt == HUM_INT1;
+}
 
 // Formats whose activations stay bf16 (bf16 MFMA on widened weights).
 constexpr bool fmt_bf16_act(int f) {
-  return f == F_INT || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16 ||
+  return fmt_int(f) || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16 ||
          f == F_MXINT4_BF16;
 }
 // 8-bit weight codes laid out for the bf16 MFMA: a lane's 32 codes of a
@@ -209,7 +236,7 @@ struct StreamLdsPlan {
 constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, int64_t kb_per_group, int scale_f32,
                                         int64_t ng, int64_t kb4) {
   StreamLdsPlan L{stream_lds_footprint(fmt, rows, kb), 0, 0, 0};
-  if (fmt == F_INT) {
+  if (fmt_int(fmt)) {
     int64_t groups = (kb + kb_per_group - 1) / kb_per_group + 1;  // groups a range of kb blocks touches
     if (groups > ng) groups = ng;
     const int64_t sc = ((groups * 16 * (scale_f32 ? 4 : 2) + 1023) / 1024) * 1024;
@@ -234,7 +261,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
   const int64_t per = (kb + kw - 1) / kw;
   const int64_t cpr = fmt_bf16_act(fmt) ? 16 : 8;
   if (rows * per * cpr > 512) return false;
-  if (fmt == F_INT) {
+  if (fmt_int(fmt)) {
     const int64_t groups = (per + kb_per_group - 1) / kb_per_group + 1;
     return groups * 16 * (scale_f32 ? 4 : 2) <= 1024 && groups * 8 <= 256;
   }

@@ -58,6 +58,35 @@ __device__ __forceinline__ u32x4_t pack_lane_4bit(const RepackArgs& a, int64_t e
   return r;
 }
 
+// 32 canonical b-bit codes (b = 1, 2, 3) of (row n, k0 .. k0+31) in the
+// packed bit planes of the integer path: the 2-bit plane (b = 2, 3) in dwords
+// 0, 1 -- element j of 8-k step s at dword s / 2, bit (j & 1) * 16 +
+// 2 * (4 * (s & 1) + j / 2) -- and the 1-bit plane (bit 2 of a 3-bit code,
+// the code itself for b = 1) in the next dword, element j of step s at bit
+// (j & 1) * 16 + 4 * s + j / 2.  Signed codes are stored offset by 2^(b-1);
+// padding rows hold the codes that decode to zero.
+__device__ __forceinline__ void pack_lane_bits(const RepackArgs& a, int bits, bool sgn, int64_t e, int64_t n,
+                                               int64_t k0, uint32_t (&out)[3]) {
+  const uint32_t flip = sgn ? (1u << (bits - 1)) : 0u;
+  uint32_t src[3] = {0, 0, 0};
+  if (n < a.n) {
+    // the row's 32 codes: 4b bytes from bit b * k0 of the row (dword aligned:
+    // K is a multiple of 128)
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(a.codes + ((e * a.n + n) * a.k + k0) * bits / 8);
+    for (int i = 0; i < bits; ++i) src[i] = w[i];
+  }
+  out[0] = out[1] = out[2] = 0;
+  for (int s = 0; s < 4; ++s)
+    for (int j = 0; j < 8; ++j) {
+      const int bit = bits * (8 * s + j);
+      const uint64_t win = (uint64_t)src[bit / 32] | ((bit / 32 + 1 < bits) ? (uint64_t)src[bit / 32 + 1] << 32 : 0);
+      uint32_t u = (uint32_t)(win >> (bit % 32)) & ((1u << bits) - 1);
+      u = (n < a.n) ? (u ^ flip) : flip;
+      if (bits >= 2) out[s >> 1] |= (u & 3u) << ((j & 1) * 16 + 2 * (4 * (s & 1) + (j >> 1)));
+      if (bits != 2) out[bits == 3 ? 2 : 0] |= ((bits == 3 ? (u >> 2) : u) & 1u) << ((j & 1) * 16 + 4 * s + (j >> 1));
+    }
+}
+
 __global__ void repack_codes_kernel(RepackArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.num_experts * a.nt * a.kb * 64;
@@ -84,6 +113,12 @@ __global__ void repack_codes_kernel(RepackArgs a) {
     u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 32);
     d[0] = lo;
     d[1] = hi;
+  } else if (dtype_int_bits(a.wdt) != 0 && dtype_int_bits(a.wdt) < 4) {
+    const int bits = dtype_int_bits(a.wdt);
+    uint32_t v[3];
+    pack_lane_bits(a, bits, dtype_int_signed(a.wdt), e, n, kb * kKBlk + 32 * lg, v);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 4 * bits);
+    for (int i = 0; i < bits; ++i) d[i] = v[i];
   } else {
     u32x4_t v = pack_lane_4bit(a, e, n, kb * kKBlk + 32 * lg);
     *reinterpret_cast<u32x4_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 16) = v;
@@ -136,7 +171,9 @@ __global__ void repack_int_co_kernel(RepackArgs a) {
   const int64_t e = rest / a.nt;
   const int c = lane & 15, lg = lane >> 4;
   const int64_t n = nt * kNSub + c;
-  const float offset = (a.wdt == HUM_INT4) ? 136.0f : 128.0f;
+  // what the bf16 (128 + u) codes carry beyond the value: 128 + 2^(b-1) for
+  // signed b-bit codes (stored offset by 2^(b-1)), 128 for unsigned ones
+  const float offset = dtype_int_signed(a.wdt) ? (float)(128 + (1 << (dtype_int_bits(a.wdt) - 1))) : 128.0f;
   u32x4_t hi, lo;
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
@@ -298,7 +335,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
   const int64_t ncode = (int64_t)d->num_experts * L.nt * L.kb * 64;
   repack_codes_kernel<<<grid_for(ncode, B), B, 0, s>>>(a);
   const int f = fmt_of(d);
-  if (f == F_INT) {
+  if (fmt_int(f)) {
     repack_int_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.ng, B), B, 0, s>>>(a);
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
   } else if (f == F_NVFP4_BF16) {
@@ -370,6 +407,31 @@ __global__ void dequant_kernel(DequantArgs a) {
       const int kk = a.bf16_order ? (32 * lg + j) : ((j < 16) ? (16 * lg + j) : (64 + 16 * lg + j - 16));
       orow[kk] = (a.wdt == HUM_INT8 ? (float)(int8_t)src[j] : e4m3_value(src[j])) * s;
     }
+    return;
+  }
+  const int bits = dtype_int_bits(a.wdt);
+  if (bits != 0 && bits < 4) {
+    // b-bit integers: the bit planes of the lane's 32 codes
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(base + ((nt * a.kb + kb) * 64 + lane) * 4 * bits);
+    const int64_t g = kb / a.kb_per_group;
+    const uint8_t* sb = a.packed + a.scales_off + e * a.scales_pe;
+    const float s = a.scale_f32 ? reinterpret_cast<const float*>(sb)[(nt * a.ng + g) * 16 + c]
+                                : bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sb)[(nt * a.ng + g) * 16 + c]);
+    int off = dtype_int_signed(a.wdt) ? (1 << (bits - 1)) : 0;
+    if (a.has_zero) {
+      const uint64_t zp = *reinterpret_cast<const uint64_t*>(a.packed + a.zeros_off + e * a.zeros_pe + (nt * a.ng + g) * 8);
+      off += (int)((zp >> (4 * c)) & 0xF);
+    }
+    for (int st = 0; st < 4; ++st)
+      for (int j = 0; j < 8; ++j) {
+        uint32_t u = 0;
+        if (bits >= 2) u = (w[st >> 1] >> ((j & 1) * 16 + 2 * (4 * (st & 1) + (j >> 1)))) & 3u;
+        if (bits != 2) {
+          const uint32_t b1 = (w[bits == 3 ? 2 : 0] >> ((j & 1) * 16 + 4 * st + (j >> 1))) & 1u;
+          u |= bits == 3 ? (b1 << 2) : b1;
+        }
+        orow[32 * lg + 8 * st + j] = (float)((int)u - off) * s;
+      }
     return;
   }
   const u32x4_t w = *reinterpret_cast<const u32x4_t*>(base + ((nt * a.kb + kb) * 64 + lane) * 16);

@@ -30,7 +30,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "rng", "seed_for", "bf16_bits", "bf16_normal", "pack_nibbles", "pack_bits", "INT_BITS",
+    "rng", "seed_for", "seed_of", "bf16_bits", "bf16_normal", "pack_nibbles", "pack_bits", "INT_BITS",
     "dense_w4a16", "dense_w8a8", "moe_weights_mxfp4", "routing", "quant_weights",
     "DENSE_SWEEP_M", "FP8_SWEEP_M", "MOE_W4A16_T", "MOE_W4A8_T",
 ]
@@ -39,6 +39,13 @@ DENSE_SWEEP_M = (1, 4, 16, 64, 256, 1024, 4096)
 FP8_SWEEP_M = (1, 16, 128, 1024, 4096)
 MOE_W4A16_T = (1, 16, 64, 512, 4096)
 MOE_W4A8_T = (1, 64, 1024, 8192)
+
+
+def seed_of(*parts) -> int:
+    """A stable 16-bit seed from any printable values (CRC-32 of their repr;
+    unlike hash(), the same in every process)."""
+    import zlib
+    return zlib.crc32(repr(parts).encode()) & 0xFFFF
 
 
 def seed_for(config: int, index: int = 0) -> int:

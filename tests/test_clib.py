@@ -35,6 +35,20 @@ def test_packed_size_dense_int4(lib):
     assert codes + scales + zeros + offsets <= nb <= codes + scales + zeros + offsets + 4096
 
 
+@pytest.mark.parametrize("wd,bits", [("int3", 3), ("uint3", 3), ("int2", 2), ("uint2", 2), ("int1", 1), ("uint1", 1)])
+def test_packed_size_low_bit_integers(lib, wd, bits):
+    """b-bit codes take 4b bytes per lane and K-block (N = K = 8192, G = 128,
+    bf16 scales, zero points for the unsigned codes)."""
+    zero = wd.startswith("u")
+    d = hum.make_desc(wd, "group", 128, "bf16", 8192, 8192, has_zero=zero)
+    nb = hum.packed_weight_bytes(d)
+    codes = 8192 * 8192 * bits // 8
+    scales = 8192 * 64 * 2
+    zeros = 8192 * 64 // 2 if zero else 0
+    offsets = 8192 * 64 * 4
+    assert codes + scales + zeros + offsets <= nb <= codes + scales + zeros + offsets + 4096
+
+
 def test_packed_size_ragged_n_pads_to_16(lib):
     d = hum.make_desc("int4", "group", 128, "bf16", 40, 256)
     assert hum.packed_weight_bytes(d) >= 48 * 256 // 2
@@ -53,6 +67,10 @@ def test_packed_size_ragged_n_pads_to_16(lib):
     dict(weight_dtype="e2m1", scale_gran="group", group_size=16, scale_dtype="e4m3", act_fmt="mxfp8"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="bf16"),
     dict(weight_dtype="int8", scale_gran="channel", group_size=0, scale_dtype="f32", act_fmt="fp8_token"),
+    dict(weight_dtype="int3", scale_gran="group", group_size=128, scale_dtype="bf16", has_zero=True),
+    dict(weight_dtype="int2", scale_gran="group", group_size=32, scale_dtype="e8m0"),
+    dict(weight_dtype="uint3", scale_gran="group", group_size=128, scale_dtype="bf16", act_fmt="mxfp8"),
+    dict(weight_dtype="int1", scale_gran="group", group_size=64, scale_dtype="bf16"),
 ])
 def test_unsupported_descriptions_rejected(lib, bad):
     kw = dict(n=256, k=1024)

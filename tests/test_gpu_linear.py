@@ -93,6 +93,51 @@ def test_int4_sym_exact_every_tile(tile):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
+LOWBIT = [("int3", False), ("uint3", True), ("int2", False), ("uint2", True), ("int1", False), ("uint1", True)]
+
+
+@pytest.mark.parametrize("wd,zero", LOWBIT, ids=lambda v: str(v))
+@pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_lowbit_int_exact_every_tile(wd, zero, tile):
+    """INT3 / INT2 / INT1 (signed and unsigned with zero points): exact-integer
+    cases bit for bit on every compiled tile, split 1 for the 3- and 2-bit
+    codes and 2 for all (the split-K partial path)."""
+    m, n, k, gs = rows_for(tile, 21), 336, 1024, 128
+    w, xb = _int_exact_case(synth.seed_of(wd, tile), wd, m, n, k, gs, zero)
+    hd, od = descs(wd, "group", gs, "bf16", 1, n, k, zero=zero)
+    packed = prepare(hd, w, "bf16")
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w.get("zeros"))
+    for split in ((1, 2) if wd[-1] in "32" else (2,)):
+        print(f"case {wd} exact tile={tile} split={split}", flush=True)
+        out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+        torch.cuda.synchronize()
+        assert_bf16_exact(out, ref, f"{wd} tile={tile} split={split}")
+
+
+@pytest.mark.parametrize("wd,gran,gs,sd,zero", [("int3", "group", 128, "bf16", False),
+                                                ("uint3", "group", 256, "bf16", True),
+                                                ("int2", "channel", 0, "f32", False),
+                                                ("uint2", "group", 128, "bf16", True),
+                                                ("int1", "group", 128, "f32", False),
+                                                ("uint1", "tensor", 0, "bf16", True)])
+@pytest.mark.parametrize("m", [1, 7, 16, 64, 300])
+def test_lowbit_random_vs_oracle(wd, gran, gs, sd, zero, m):
+    """Low-bit integer weights on random data with the selector's
+    configuration, ragged N, a bias and a global scale."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_of(wd, gran, m), wd, gran, gs, sd, 1, n, k, zero=zero, global_scale=True)
+    hd, od = descs(wd, gran, gs, sd, 1, n, k, zero=zero, glob=True)
+    xb = synth.bf16_normal(synth.rng(synth.seed_of("x", wd, m)), (m, k))
+    bias = synth.bf16_normal(synth.rng(synth.seed_of("b", wd)), (n,))
+    packed = prepare(hd, w, sd)
+    print(f"case {wd} random m={m}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), bias=dev(bias))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], w.get("zeros"),
+                             w.get("global_scale"), bias_bits=bias)
+    assert_tol(out, ref, f"{wd} {gran} m={m}")
+
+
 @pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_mxfp4_bf16_exact_every_tile(tile):
     m, n, k = 9, 96, 1024

@@ -24,6 +24,13 @@ FORMATS = [
     ("e4m3", "channel", 0, "f32", False, False),
     ("e4m3", "tensor", 0, "f32", False, True),
     ("e4m3", "block", 128, "f32", False, False),
+    ("int3", "group", 128, "bf16", False, False),
+    ("uint3", "group", 128, "bf16", True, False),
+    ("uint3", "channel", 0, "f32", True, True),
+    ("int2", "group", 256, "f32", False, False),
+    ("uint2", "group", 128, "bf16", True, False),
+    ("int1", "tensor", 0, "bf16", False, False),
+    ("uint1", "group", 128, "bf16", True, False),
 ]
 SHAPES = [(1, 40, 256), (3, 640, 1024), (2, 16, 128)]
 
@@ -39,7 +46,7 @@ def test_dequant_bit_exact(fmt, shape):
         pytest.skip("group does not divide k")
     act = {"e4m3": "fp8_group" if gran == "block" else "fp8_token"}.get(wd, "bf16")
     hd, od = descs(wd, gran, gs, sd, e, n, k, zero, glob, act)
-    w = synth.quant_weights(hash((fmt, shape)) & 0xFFFF, wd, gran, gs, sd, e, n, k, zero, glob,
+    w = synth.quant_weights(synth.seed_of(fmt, shape), wd, gran, gs, sd, e, n, k, zero, glob,
                             e8m0_lo=100, e8m0_hi=150)
     print(f"case {fmt} {shape}", flush=True)
     packed = prepare(hd, w, sd)
@@ -58,7 +65,7 @@ def test_dequant_bit_exact_fp8_weights_bf16_act(shape, gran):
     """E4M3 weights packed for bf16 activations (their own fragment order)."""
     e, n, k = shape
     hd, od = descs("e4m3", gran, 0, "f32", e, n, k, act="bf16")
-    w = synth.quant_weights(hash(("w8a16", shape, gran)) & 0xFFFF, "e4m3", gran, 0, "f32", e, n, k)
+    w = synth.quant_weights(synth.seed_of("w8a16", shape, gran), "e4m3", gran, 0, "f32", e, n, k)
     packed = prepare(hd, w, "f32")
     got = hum.dequant_weight(hd, packed)
     torch.cuda.synchronize()
@@ -73,7 +80,7 @@ def test_dequant_bit_exact_int8(shape, gran):
     """INT8 weights (the FP8-for-bf16 fragment order, every code)."""
     e, n, k = shape
     hd, od = descs("int8", gran, 0, "f32", e, n, k)
-    w = synth.quant_weights(hash(("int8", shape, gran)) & 0xFFFF, "int8", gran, 0, "f32", e, n, k)
+    w = synth.quant_weights(synth.seed_of("int8", shape, gran), "int8", gran, 0, "f32", e, n, k)
     packed = prepare(hd, w, "f32")
     got = hum.dequant_weight(hd, packed)
     torch.cuda.synchronize()
@@ -88,7 +95,7 @@ def test_dequant_bit_exact_nvfp4(shape):
     from subnormal to 448 (exact in f32)."""
     e, n, k = shape
     hd, od = descs("e2m1", "group", 16, "e4m3", e, n, k)
-    w = synth.quant_weights(hash(("nvfp4", shape)) & 0xFFFF, "e2m1", "group", 16, "e4m3", e, n, k,
+    w = synth.quant_weights(synth.seed_of("nvfp4", shape), "e2m1", "group", 16, "e4m3", e, n, k,
                             e4m3_lo=0x01, e4m3_hi=0x7E)
     packed = prepare(hd, w, "e4m3")
     got = hum.dequant_weight(hd, packed)
@@ -103,7 +110,7 @@ def test_dequant_bit_exact_mxint4(shape):
     """MXINT4: every INT4 code times its E8M0 scale per 32."""
     e, n, k = shape
     hd, od = descs("int4", "group", 32, "e8m0", e, n, k)
-    w = synth.quant_weights(hash(("mxint4", shape)) & 0xFFFF, "int4", "group", 32, "e8m0", e, n, k)
+    w = synth.quant_weights(synth.seed_of("mxint4", shape), "int4", "group", 32, "e8m0", e, n, k)
     packed = prepare(hd, w, "e8m0")
     got = hum.dequant_weight(hd, packed)
     torch.cuda.synchronize()

@@ -12,7 +12,7 @@ import torch
 
 from oracle import gemm as G
 from oracle.formats import decode_bf16
-from synth import bf16_bits, pack_bits, pack_nibbles
+from synth import bf16_bits, pack_bits, pack_nibbles, seed_of
 
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
 
@@ -109,7 +109,7 @@ BITS = {"int3": 3, "uint3": 3, "int2": 2, "uint2": 2, "int1": 1, "uint1": 1}
 
 @pytest.mark.parametrize("wd,gran,gs,sd,zp,gl", CASES)
 def test_linear_vs_fraction_brute_force(wd, gran, gs, sd, zp, gl):
-    g = np.random.default_rng(hash((wd, gran, gs, sd)) & 0xFFFF)
+    g = np.random.default_rng(seed_of(wd, gran, gs, sd))
     m, n, k = 3, (40 if gran == "block" else 5), 64
     desc = G.WeightDesc(wd, gran, gs, sd, zp, gl, 1, n, k)
     ng = desc.groups()
