@@ -124,6 +124,12 @@ typedef struct hum_tile_config {
   int32_t block_m;   /* rows per workgroup tile = MoE expert block (16*wave_m) */
   int32_t stages;    /* tile kernel: K-blocks of operands staged in LDS at once
                         (2 or 3; 0 = 2); ignored by the stream kernel */
+  int32_t stream_k;  /* dense tile kernels: 0 = off; G > 0 = Stream-K ("Device-
+                        specific tuning" in the Humming announcement lists it
+                        among the task mappings): G workgroups share the tiles'
+                        K-blocks evenly, a tile shared by several is summed by
+                        the last of them to finish, in a fixed order (fp32
+                        partials; split_k must be 1; at most 16384 tiles) */
 } hum_tile_config;
 
 /* ---- weight preparation ------------------------------------------------ */
@@ -226,7 +232,13 @@ size_t hum_linear_workspace_bytes_ex(const hum_weight_desc* desc, int64_t m,
                                      const hum_tile_config* cfg);
 
 /* Zero a device buffer (enqueued on `stream`; a fill kernel, so it can be
- * captured in a HIP graph).  Workspaces need no zeroing; this is a helper. */
+ * captured in a HIP graph).
+ * Workspaces: the first HUM_WS_HEADER_BYTES of every workspace hold the
+ * Stream-K tile counters, which must be zero before the workspace's first
+ * call (this call, once) and which every call leaves zero; the rest needs
+ * no initialisation.  Calls that may overlap in time need different
+ * workspaces. */
+#define HUM_WS_HEADER_BYTES (64u << 10)
 hum_status hum_prepare_workspace(void* workspace, size_t ws_bytes, void* stream);
 
 /* Selector: the tile / split-K configuration hum_linear would use for m

@@ -62,7 +62,7 @@ class TileConfig(ctypes.Structure):
         ("kind", ctypes.c_int32),
         ("wave_m", ctypes.c_int32), ("wave_n", ctypes.c_int32), ("waves_n", ctypes.c_int32),
         ("waves_k", ctypes.c_int32), ("split_k", ctypes.c_int32), ("block_m", ctypes.c_int32),
-        ("stages", ctypes.c_int32),
+        ("stages", ctypes.c_int32), ("stream_k", ctypes.c_int32),
     ]
 
     def as_tuple(self):

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 # The GEMM kernel instances are spread over several translation units so
 # that they compile in parallel.
 GEMM_SOURCES = ["gemm.hip", "inst_dense_a.hip", "inst_dense_b.hip", "inst_dense_c.hip", "inst_dense_d.hip",
-                "inst_moe_a.hip", "inst_moe_b.hip", "inst_moe_c.hip"]
+                "inst_dense_sk.hip", "inst_moe_a.hip", "inst_moe_b.hip", "inst_moe_c.hip"]
 SOURCES = ["api.hip", "repack.hip", "act_moe.hip", "peaks.hip", *GEMM_SOURCES]
 ARCH = os.environ.get("HUM_OFFLOAD_ARCH", "gfx950")
 

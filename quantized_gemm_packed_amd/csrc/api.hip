@@ -182,11 +182,18 @@ static int key_stages(const hum_tile_config& c) {
 }
 
 static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
-  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16, key_stages(c)};
+  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16, key_stages(c),
+                   c.stream_k > 0 ? 1 : 0};
 }
+
+// Stream-K tile counters: the workspace header, one u32 per tile.
+constexpr int64_t kWsHeader = HUM_WS_HEADER_BYTES;
+constexpr int64_t kSkMaxTiles = kWsHeader / 4;
 
 static bool cfg_sane(const hum_tile_config& c) {
   if (c.split_k < 1 || c.split_k > 64 || c.wave_m < 1 || c.wave_n < 1) return false;
+  if (c.stream_k < 0 || c.stream_k > 65536) return false;
+  if (c.stream_k > 0 && (c.kind == HUM_KERNEL_STREAM || c.split_k != 1)) return false;
   if (c.kind == HUM_KERNEL_STREAM) return c.wave_m == 1 && c.waves_n == 1 && c.waves_k >= 1 && c.waves_k <= 15;
   if (c.kind == HUM_KERNEL_TILE) return c.waves_n == 4 && c.waves_k == 1 && (c.stages == 0 || c.stages == 2 || c.stages == 3);
   if (c.kind == HUM_KERNEL_TILE32)
@@ -317,6 +324,17 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       c.split_k = 1;
     }
   }
+  if (c.kind == HUM_KERNEL_TILE && c.split_k > 1) {
+    // Stream-K in place of split-K: 512 workgroups share the tiles'
+    // K-blocks evenly and the last to finish a shared tile sums it, so no
+    // reduce launch follows (measured on MI355X, W4A16 at N = K = 8192: M =
+    // 32 / 64 / 128 in 20 / 24 / 32 us against 26 / 27 / 37 with split-K)
+    hum_tile_config sk = c;
+    sk.split_k = 1;
+    sk.stream_k = 512;
+    const int64_t tiles = cdiv(m, tile_rows(sk)) * cdiv(nt, tile_subtiles(sk));
+    if (tiles <= kSkMaxTiles && gemm_instance_exists(dense_key(d, sk))) c = sk;
+  }
   c.block_m = (int32_t)tile_rows(c);
   return c;
 }
@@ -434,9 +452,11 @@ struct DenseWs {
 static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_config& c, bool quant_a) {
   DenseWs w;
   const int64_t nt = cdiv(d->n, kNSub);
-  int64_t off = 0;
+  int64_t off = kWsHeader;  // Stream-K tile counters
   w.partials = off;
   if (c.split_k > 1) off = align256(off + (int64_t)c.split_k * m * nt * 16 * 4);
+  // Stream-K: two partial-tile slots per workgroup
+  if (c.stream_k > 0) off = align256(off + 2 * (int64_t)c.stream_k * tile_rows(c) * tile_subtiles(c) * 16 * 4);
   w.aq = off;
   if (quant_a) {
     off = align256(off + (d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 2) : m * d->k));
@@ -447,7 +467,8 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
   }
   w.rowsum = off;
   if (fmt_int(fmt_of(d)) && c.kind != HUM_KERNEL_STREAM) off = align256(off + cdiv(m, 16) * cdiv(d->k / kKBlk, 32) * 2048);
-  w.total = off;
+  // a call that uses no scratch at all needs no workspace
+  w.total = off == kWsHeader && c.stream_k == 0 ? 0 : off;
   return w;
 }
 
@@ -533,6 +554,7 @@ static hum_tile_config select_dense_invariant(const hum_weight_desc* d, int64_t 
   // one block shape for every m
   if (c.kind == HUM_KERNEL_TILE32) c.kind = HUM_KERNEL_TILE;
   c.split_k = 1;
+  c.stream_k = 0;  // (its segments follow the tile count, hence m)
   c.block_m = (int32_t)tile_rows(c);
   return c;
 }
@@ -650,6 +672,19 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.split_k = c.split_k;
   p.kb_per_split = kb_per_split(L.kb, c);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
+  if (c.stream_k > 0) {
+    const int64_t tiles = m_tiles * p.n_tiles;
+    if (tiles > kSkMaxTiles) return set_error(HUM_ERR_UNSUPPORTED, "Stream-K takes at most %lld tiles", (long long)kSkMaxTiles);
+    p.sk_tiles = (int)tiles;
+    p.sk_m_tiles = (int)m_tiles;
+    p.sk_len = cdiv(tiles * L.kb, c.stream_k);
+    // workgroups that get iterations (the rest would have none)
+    p.sk_groups = (int)cdiv(tiles * L.kb, p.sk_len);
+    p.sk_count = reinterpret_cast<uint32_t*>(ws);
+    p.sk_part = reinterpret_cast<float*>(ws + w.partials);
+    p.sk_part_bytes = 2 * (int64_t)p.sk_groups * tile_rows(c) * tile_subtiles(c) * 16 * 4;
+    if (p.sk_part_bytes >= ((int64_t)1 << 31)) return set_error(HUM_ERR_UNSUPPORTED, "Stream-K partial slots above 2 GiB");
+  }
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
                                             : m * desc->k * (fmt_bf16_act(fmt_of(desc)) ? 2 : 1);
@@ -749,6 +784,15 @@ static void dense_candidates(const hum_weight_desc* d, int64_t m, uint32_t flags
               // every split must own at least one K-block
               if (split > 1 && (int64_t)kb_per_split(kb, c) * (split - 1) >= kb) continue;
               if (cfg_sane(c) && gemm_instance_exists(dense_key(d, c))) out.push_back(c);
+              // Stream-K over 256 / 512 / 1024 workgroups
+              if (split == 1 && tile && !inv)
+                for (int g = 256; g <= 1024; g *= 2) {
+                  hum_tile_config k = c;
+                  k.stream_k = g;
+                  if (cdiv(m, tile_rows(k)) * cdiv(cdiv(d->n, kNSub), tile_subtiles(k)) <= kSkMaxTiles &&
+                      cfg_sane(k) && gemm_instance_exists(dense_key(d, k)))
+                    out.push_back(k);
+                }
             }
     }
   }
@@ -862,7 +906,7 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   w.cap = masked ? t : t * topk + E * (bm - 1);
   w.nblocks = cdiv(w.cap, bm);
   const int64_t pcols = (2 * inter > cdiv(h, kNSub) * kNSub) ? 2 * inter : cdiv(h, kNSub) * kNSub;
-  int64_t off = 0;
+  int64_t off = kWsHeader;  // (the Stream-K counters of dense calls sharing the workspace)
   w.partials = off;
   if (split > 1) off = align256(off + (int64_t)split * w.cap * pcols * 4);
   w.sorted = off;
@@ -1020,7 +1064,7 @@ static hum_status stage_setup(const hum_weight_desc* w, int32_t a_mode, int32_t 
     const MoeCfg mc = select_moe_shape(w, t < 1 ? 1 : t, topk);
     S.c = (tile_rows(mc.dn) == block_m) ? mc.dn : moe_tile_cfg(block_m / 16);
   }
-  if (!cfg_sane(S.c)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
+  if (!cfg_sane(S.c) || S.c.stream_k != 0) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   if (tile_rows(S.c) != block_m) return set_error(HUM_ERR_INVALID_ARG, "the configuration's block (%d rows) differs from block_m", (int)tile_rows(S.c));
   // sorted rows: the scatter epilogue's instances read them directly (that
   // epilogue implies grouped rows); the others take the grouped-row mode
@@ -1031,7 +1075,7 @@ static hum_status stage_setup(const hum_weight_desc* w, int32_t a_mode, int32_t 
   if (S.c.kind == HUM_KERNEL_STREAM && !moe_stream_fits(w, S.c, (int)(t * topk < 16 ? t * topk : 16)))
     return set_error(HUM_ERR_UNSUPPORTED, "decode kernel: K range per split too long for LDS (raise split_k)");
   S.nblocks = cdiv(sorted_len, block_m);
-  int64_t off = 0;
+  int64_t off = kWsHeader;  // (the Stream-K counters of dense calls sharing the workspace)
   S.bexp = off;
   off = align256(off + S.nblocks * 4);
   S.partials = off;
@@ -1115,7 +1159,7 @@ hum_status hum_moe_grouped_gemm(const hum_weight_desc* w, const void* packed, in
 static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelKey* kup, KernelKey* kdn) {
   const hum_tile_config& cu = mc.up;
   const hum_tile_config& cd = mc.dn;
-  if (!cfg_sane(cu) || !cfg_sane(cd) || tile_rows(cu) != tile_rows(cd))
+  if (!cfg_sane(cu) || !cfg_sane(cd) || cu.stream_k != 0 || cd.stream_k != 0 || tile_rows(cu) != tile_rows(cd))
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
   const int epi_up = moe_up_epi(f);

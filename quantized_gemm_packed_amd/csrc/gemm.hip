@@ -91,13 +91,13 @@ static const ReduceInstance kReduces[] = {
 
 static const Instance* find_instance(const KernelKey& k) {
   static const InstanceTable tables[] = {instances_dense_a(), instances_dense_b(), instances_dense_c(),
-                                         instances_dense_d(), instances_moe_a(), instances_moe_b(),
-                                         instances_moe_c()};
+                                         instances_dense_d(), instances_dense_sk(), instances_moe_a(),
+                                         instances_moe_b(), instances_moe_c()};
   for (const InstanceTable& t : tables)
     for (int i = 0; i < t.n; ++i) {
       const KernelKey& q = t.p[i].key;
       if (q.fmt == k.fmt && q.kind == k.kind && q.wm == k.wm && q.wn == k.wn && q.waves_n == k.waves_n &&
-          q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi && q.stages == k.stages)
+          q.waves_k == k.waves_k && q.amode == k.amode && q.epi == k.epi && q.stages == k.stages && q.sk == k.sk)
         return &t.p[i];
     }
   return nullptr;
@@ -124,7 +124,9 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
     return set_error(HUM_ERR_UNSUPPORTED,
                      "no GEMM instance fmt=%d kind=%d wm=%d wn=%d waves_n=%d waves_k=%d amode=%d epi=%d stages=%d",
                      key.fmt, key.kind, key.wm, key.wn, key.waves_n, key.waves_k, key.amode, key.epi, key.stages);
-  const int64_t grid = m_tiles * (int64_t)p.n_tiles * p.split_k;
+  const int64_t grid = p.sk_groups > 0 ? (int64_t)p.sk_groups : m_tiles * (int64_t)p.n_tiles * p.split_k;
+  if (p.sk_groups > 0 && (key.kind == KIND_STREAM || p.split_k != 1 || key.amode != A_DIRECT || key.epi != EPI_BF16))
+    return set_error(HUM_ERR_UNSUPPORTED, "Stream-K runs the dense tile kernels without split-K");
   if (grid <= 0) return HUM_OK;
   if (grid > 0x7FFFFFFF) return set_error(HUM_ERR_UNSUPPORTED, "grid too large");
   // buffer resources take 32-bit sizes and offsets

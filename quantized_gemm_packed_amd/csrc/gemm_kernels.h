@@ -1162,14 +1162,22 @@ struct TileLds {
 // swap's result R, dword s: the B operand of instruction (R, s).  The A
 // operand reads the same k from the LDS tile.  Dense layers, bf16
 // activations, INT and MXFP4 weights.
-template <int FMT, int WM, int WN, int AMODE, int EPI, int S, int MS = 16>
-__global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
+// Waves per SIMD a tile instance is held to (its register budget): the FP8
+// 128 x 128 tile fits 128 VGPRs, which lets four workgroups share a CU (as
+// many as its LDS admits); the others take what they need.
+constexpr int tile_min_waves(int fmt, int wm, int wn, int amode, int epi, int s, int ms, bool sk) {
+  return (fmt == F_FP8 && wm == 8 && wn == 2 && amode == A_DIRECT && epi == EPI_BF16 && s == 2 && ms == 16 && !sk) ? 4 : 1;
+}
+
+template <int FMT, int WM, int WN, int AMODE, int EPI, int S, int MS = 16, bool SK = false>
+__global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS, SK)) void tile_kernel(const GemmParams p) {
   using C = TileCfg<FMT, WM, WN, AMODE, EPI, S>;
   using T = typename C::T;
   constexpr int kAE = T::kAElem;
   static_assert(MS == 16 || (MS == 32 && (fmt_int(FMT) || FMT == F_MXFP4_BF16) && WM % 2 == 0 && WN % 2 == 0 &&
                              AMODE == A_DIRECT && EPI == EPI_BF16),
                 "32x32 blocks: dense bf16-activation INT / MXFP4 tiles of even sub-tile counts");
+  static_assert(!SK || (AMODE == A_DIRECT && EPI == EPI_BF16), "Stream-K: dense tiles");
   constexpr int MP = MS == 32 ? WM / 2 : 1, NP = MS == 32 ? WN / 2 : 1;
 
   const int tid = threadIdx.x;
@@ -1185,20 +1193,22 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
   const uint32_t nwg = gridDim.x;
   uint32_t bid = blockIdx.x;
   if (nwg % 8 == 0) bid = (bid % 8) * (nwg / 8) + bid / 8;
-  const int split = (int)(bid % (uint32_t)p.split_k);
-  bid /= (uint32_t)p.split_k;
-  int tn;
-  int64_t tm;
-  {
-    const uint32_t m_tiles = nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
+  const uint32_t m_tiles = SK ? (uint32_t)p.sk_m_tiles : nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
+  // tile index -> (M-tile, N-tile)
+  auto tile_coords = [&](uint32_t t, int64_t& tm, int& tn) {
     const uint32_t per_group = (uint32_t)p.group_m * (uint32_t)p.n_tiles;
-    const uint32_t g = bid / per_group, r = bid % per_group;
+    const uint32_t g = t / per_group, r = t % per_group;
     const uint32_t m0 = g * (uint32_t)p.group_m;
     const uint32_t gm = m_tiles - m0 < (uint32_t)p.group_m ? m_tiles - m0 : (uint32_t)p.group_m;
     tm = m0 + r % gm;
     tn = (int)(r / gm);
-  }
+  };
+  __shared__ int s_sk_last;
 
+  // One tile's K-blocks [kb_begin, kb_end): the whole tile, a split-K share
+  // (fp32 partials for the reduce kernel), or a Stream-K segment of tile
+  // sk_tile (>= 0) taken by workgroup sk_g.
+  auto tile_work = [&](int64_t tm, int tn, int split, int kb_begin, int kb_end, int sk_tile, int64_t sk_g) -> void {
   int expert = 0;
   if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {  // grouped rows: the block's expert (-1: all padding)
     expert = p.block_expert[tm];
@@ -1226,9 +1236,6 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     }
   }
 
-  const int kb_begin = split * p.kb_per_split;
-  int kb_end = kb_begin + p.kb_per_split;
-  if (kb_end > p.kb_count) kb_end = p.kb_count;
   const int nkb = kb_end > kb_begin ? kb_end - kb_begin : 0;
 
   // --- DMA sources (every lane always gets a valid address: rows past the
@@ -1656,8 +1663,8 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
     // more small product, taken here on the MFMA: row sums (A) times the
     // weight's offset terms (B, stored negated) with K running over
     // K-blocks, each operand as a bf16 hi / lo pair (hi*hi + hi*lo + lo*hi).
-    // The first split adds the whole of it.
-    if (split == 0 && MS == 32) {
+    // The share that starts at K-block 0 adds the whole of it.
+    if (kb_begin == 0 && MS == 32) {
       // the same product on the 32x32x16 MFMA: row sums of a pair of 16-row
       // tiles and offset terms of a pair of sub-tiles, each swapped into the
       // 32-wide operand layout as the weight codes are (K-block slots
@@ -1717,7 +1724,7 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
           }
         }
       }
-    } else if (split == 0) {
+    } else if (kb_begin == 0) {
       const int64_t mt16 = (p.m + 15) / 16;
       const int64_t rs_half = mt16 * p.kbc * 1024;
       const int64_t co_half = (int64_t)p.nt_count * p.kbc * 1024;
@@ -1743,6 +1750,65 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
             acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rh, cl[ns], acc[ms][ns], 0, 0, 0);
             acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rl, ch[ns], acc[ms][ns], 0, 0, 0);
           }
+        }
+      }
+    }
+  }
+
+  if constexpr (SK) {
+    // Stream-K: workgroup g takes iterations [g L, (g + 1) L) of the tiles'
+    // K-blocks laid end to end, so a tile's K-blocks may be shared by the
+    // workgroups g_first .. g_last.  Each of them writes its partial sums
+    // (slot 2 g for the first tile of its range, 2 g + 1 for the last); the
+    // last to finish adds every segment's slot in segment order -- a fixed
+    // order, so the result does not depend on which one finishes last --
+    // and stores the tile.  The counter is left at zero for the next call.
+    const int64_t KB = p.kb_count, L = p.sk_len;
+    const int64_t g_first = ((int64_t)sk_tile * KB) / L;
+    const int64_t g_last = ((int64_t)sk_tile * KB + KB - 1) / L;
+    const int nseg = (int)(g_last - g_first + 1);
+    if (nseg > 1) {
+      constexpr int kV = WM * WN;  // f32x4 of accumulators per lane
+      // The slots are written and read with device-coherent accesses (the
+      // cache policy of a device-scope atomic access: through to memory,
+      // around the XCD's L2), so no fence has to write back or invalidate a
+      // whole L2 -- which would cost every workgroup on that XCD its cached
+      // operands.
+      constexpr int kDev = 16;  // sc1
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.sk_part, p.sk_part_bytes);
+      auto slot = [&](int64_t g) -> uint32_t {
+        const int64_t sl = 2 * g + (((g * L) / KB) == sk_tile ? 0 : 1);
+        return (uint32_t)((((sl * 4 + wn) * kV) * 64 + lane) * 16);
+      };
+      auto acc_at = [&](int v) -> f32x4_t& {
+        if constexpr (MS == 32) {
+          // (f32x16 accumulators as four f32x4 each)
+          return reinterpret_cast<f32x4_t*>(&acc32[v / (4 * NP)][(v / 4) % NP])[v % 4];
+        } else {
+          return acc[v / WN][v % WN];
+        }
+      };
+      const uint32_t mine = slot(sk_g);
+#pragma unroll
+      for (int v = 0; v < kV; ++v)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc_at(v)), rp, mine + v * 1024, 0, kDev);
+      // every wave's slot stores have completed before the count goes up
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(p.sk_count + sk_tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old + 1 == (uint32_t)nseg;
+        if (last) __hip_atomic_store(p.sk_count + sk_tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_sk_last = last;
+      }
+      __syncthreads();
+      if (!s_sk_last) return;
+      for (int i = 0; i < nseg; ++i) {
+        const uint32_t src = slot(g_first + i);
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+          const f32x4_t x = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rp, src + v * 1024, 0, kDev));
+          acc_at(v) = i == 0 ? x : acc_at(v) + x;
         }
       }
     }
@@ -1810,6 +1876,39 @@ __global__ __launch_bounds__(256) void tile_kernel(const GemmParams p) {
         store_swiglu_mxfp8<FMT>(p, wp.meta, gs, rb, (int64_t)nts[2 * jj] * 16 + c16, acc[ms][2 * jj], acc[ms][2 * jj + WN / 2],
                            acc[ms][2 * jj + 1], acc[ms][2 * jj + 1 + WN / 2], lg, c16);
     }
+  }
+  };
+
+  if constexpr (SK) {
+    // Stream-K (dense layers): this workgroup's iterations [bid L, (bid + 1)
+    // L) of the tiles' K-blocks laid end to end, one segment per tile they
+    // touch
+    const int64_t KB = p.kb_count, L = p.sk_len;
+    const int64_t it_all = (int64_t)p.sk_tiles * KB;
+    int64_t it = (int64_t)bid * L;
+    const int64_t it_end = it + L < it_all ? it + L : it_all;
+    bool first = true;
+    while (it < it_end) {
+      const int64_t t = it / KB;
+      const int k0 = (int)(it - t * KB);
+      const int k1 = (int)(it_end - it < KB - k0 ? k0 + (it_end - it) : KB);
+      if (!first) __syncthreads();  // the previous segment's LDS reads are done
+      int64_t tm;
+      int tn;
+      tile_coords((uint32_t)t, tm, tn);
+      tile_work(tm, tn, 0, k0, k1, (int)t, (int64_t)bid);
+      first = false;
+      it += k1 - k0;
+    }
+  } else {
+    const int split = (int)(bid % (uint32_t)p.split_k);
+    int64_t tm;
+    int tn;
+    tile_coords(bid / (uint32_t)p.split_k, tm, tn);
+    const int kb_begin = split * p.kb_per_split;
+    int kb_end = kb_begin + p.kb_per_split;
+    if (kb_end > p.kb_count) kb_end = p.kb_count;
+    tile_work(tm, tn, split, kb_begin, kb_end, -1, 0);
   }
 }
 
@@ -1937,6 +2036,7 @@ InstanceTable instances_dense_a();
 InstanceTable instances_dense_b();
 InstanceTable instances_dense_c();
 InstanceTable instances_dense_d();
+InstanceTable instances_dense_sk();
 InstanceTable instances_moe_a();
 InstanceTable instances_moe_b();
 InstanceTable instances_moe_c();
@@ -1949,6 +2049,10 @@ InstanceTable instances_moe_c();
 #define HUM_TILE_S(F, WM, WN, AM, EP, S) \
   {{F, KIND_TILE, WM, WN, 4, 1, AM, EP, S}, tile_kernel<F, WM, WN, AM, EP, S>, 256}
 #define HUM_TILE(F, WM, WN, AM, EP) HUM_TILE_S(F, WM, WN, AM, EP, 2)
+// Stream-K variants of dense tiles (MS: 16 or 32)
+#define HUM_TILE_SK(F, WM, WN, S, MS)                                                              \
+  {{F, (MS) == 32 ? KIND_TILE32 : KIND_TILE, WM, WN, 4, 1, A_DIRECT, EPI_BF16, S, 1},              \
+   tile_kernel<F, WM, WN, A_DIRECT, EPI_BF16, S, MS, true>, 256}
 #define HUM_TILE32_S(F, WM, WN, S) \
   {{F, KIND_TILE32, WM, WN, 4, 1, A_DIRECT, EPI_BF16, S}, tile_kernel<F, WM, WN, A_DIRECT, EPI_BF16, S, 32>, 256}
 // 32x32-block tiles (bf16 activations: INT and MXFP4 weights; INT's 128 x

@@ -195,6 +195,14 @@ struct GemmParams {
   float* partials;    // split-K partials, [split][m][columns] fp32
   int split_k;
   int kb_per_split;
+  // Stream-K (tile kernel, dense): sk_groups workgroups share the
+  // sk_tiles * kb_count K-block iterations, sk_len each; per-tile counters
+  // (zero between calls) and per-workgroup partial slots
+  int sk_groups, sk_tiles, sk_m_tiles;
+  int64_t sk_len;
+  uint32_t* sk_count;
+  float* sk_part;
+  int64_t sk_part_bytes;
   int n_tiles;
   int group_m;        // tile kernel: M-tiles walked together (M fastest) per N sweep
   int stream_rows;    // stream kernel: most valid rows of one 16-row tile
@@ -273,6 +281,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
 struct KernelKey {
   int fmt, kind, wm, wn, waves_n, waves_k, amode, epi;
   int stages;  // tile kernel: LDS pipeline stages (2 or 3); 0 for the stream kernel
+  int sk = 0;  // 1: the Stream-K variant of a dense tile kernel
 };
 
 // Launches the GEMM kernel instance matching `key` (HUM_ERR_UNSUPPORTED if

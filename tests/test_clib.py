@@ -109,7 +109,7 @@ def test_selector_is_deterministic_and_covers_m_range(lib):
         c1 = hum.select_config(d, m).as_tuple()
         c2 = hum.select_config(d, m).as_tuple()
         assert c1 == c2
-        kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m, stages = c1
+        kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m, stages, stream_k = c1
         assert split_k >= 1 and block_m == 16 * wave_m
         assert kind == (1 if m <= 16 else (2 if m >= 256 else 0))   # decode, 16x16 tiles, 32x32 tiles
         assert 16 * wave_m >= min(m, 32)
@@ -209,3 +209,40 @@ def test_group_index_by_fp32_reciprocal_is_exact():
         inv = np.float32(1.0) / np.float32(d)
         q = np.floor(kb * inv).astype(np.int64)   # fp32 product, rounded to nearest
         assert np.array_equal(q, kbi // d), d
+
+
+def _sk(kind, wm, wn, stages, split, groups):
+    c = hum.TileConfig()
+    c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k = kind, wm, wn, 1 if kind == 1 else 4, 8 if kind == 1 else 1
+    c.stages, c.split_k, c.block_m, c.stream_k = stages, split, 16 * wm, groups
+    return c
+
+
+@pytest.mark.parametrize("cfg,why", [
+    (dict(kind=0, wm=2, wn=2, stages=3, split=2, groups=64), "with split-K"),
+    (dict(kind=1, wm=1, wn=1, stages=0, split=1, groups=64), "on the decode kernel"),
+    (dict(kind=0, wm=2, wn=2, stages=3, split=1, groups=-1), "negative"),
+    (dict(kind=0, wm=1, wn=4, stages=2, split=1, groups=64), "no such instance"),
+])
+def test_stream_k_configs_refused_before_launch(lib, cfg, why):
+    """Stream-K configurations the library does not run are refused with
+    HUM_ERR_UNSUPPORTED before anything is enqueued (null device pointers
+    would fault if a kernel were launched)."""
+    d = hum.make_desc("uint4", "group", 128, "bf16", 512, 1024, has_zero=True)
+    c = _sk(**cfg)
+    st = lib.hum_linear_ex(ctypes.byref(d), ctypes.c_void_p(256), 64, ctypes.c_void_p(256), None, None,
+                           ctypes.c_void_p(256), ctypes.c_void_p(256), 1 << 30, ctypes.byref(c), None)
+    assert st == 2, why
+
+
+def test_stream_k_workspace_has_counter_header_and_slots(lib):
+    """The workspace of a Stream-K call: the 64 KiB counter header, then two
+    fp32 partial-tile slots per workgroup (after the INT row sums' offset
+    region is added, the size only grows)."""
+    d = hum.make_desc("uint4", "group", 128, "bf16", 512, 1024, has_zero=True)
+    base = _sk(0, 2, 2, 3, 1, 0)
+    sk = _sk(0, 2, 2, 3, 1, 64)
+    b0 = hum.linear_workspace_bytes(d, 64, cfg=base)
+    b1 = hum.linear_workspace_bytes(d, 64, cfg=sk)
+    assert b1 - b0 >= 2 * 64 * 32 * 128 * 4
+    assert b0 >= 64 << 10
