@@ -23,6 +23,11 @@ bit layouts.  The readings below are the OCP definitions:
   exponent field 0 is subnormal with quantum 2^-9; codes 0x7F/0xFF are NaN;
   no Inf; largest finite 448.
 * E8M0 (OCP MX v1.0): 2^(c-127); c = 255 is NaN.
+* FP6 E2M3 / E3M2 (OCP MX v1.0; the WnA16 section of the announcement runs
+  FP4 to FP8 weights): sign, 2 (3) exponent bits with bias 1 (3), 3 (2)
+  mantissa bits; exponent 0 is subnormal (quantum 2^-3 / 2^-4); no Inf/NaN;
+  max 7.5 / 28.  Canonical packing: the LSB-first 6-bit stream along K
+  (codes [E][N][K*6/8]), with an E8M0 scale per 32 along K (MXFP6).
 * BF16: the upper 16 bits of an IEEE float32.
 
 Encoders round to nearest, ties to even, and saturate (E4M3, E2M1) where
@@ -216,6 +221,25 @@ def unpack_nibbles(packed):
     return out
 
 
+def _decode_minifloat(c, ebits: int, mbits: int, bias: int):
+    """Sign / exponent / mantissa fields -> value; exponent 0 is subnormal."""
+    c = np.asarray(c, dtype=np.int64)
+    s = (c >> (ebits + mbits)) & 1
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    m = c & ((1 << mbits) - 1)
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), 1 - bias - mbits),
+                   np.ldexp(1.0 + np.ldexp(m.astype(np.float64), -mbits), e - bias))
+    return np.where(s == 1, -mag, mag).astype(np.float64)
+
+
+def decode_e2m3(c):
+    return _decode_minifloat(c, 2, 3, 1)
+
+
+def decode_e3m2(c):
+    return _decode_minifloat(c, 3, 2, 3)
+
+
 INT_BITS = {"int1": 1, "int2": 2, "int3": 3, "uint1": 1, "uint2": 2, "uint3": 3}
 
 
@@ -240,6 +264,9 @@ def decode_intb(c, bits: int):
 
 def decode_weight_codes(codes, weight_dtype: str):
     """Canonical code array -> float64 element values v(q)."""
+    if weight_dtype in ("e2m3", "e3m2"):
+        q = unpack_bits(codes, 6)
+        return decode_e2m3(q) if weight_dtype == "e2m3" else decode_e3m2(q)
     if weight_dtype in INT_BITS:
         b = INT_BITS[weight_dtype]
         q = unpack_bits(codes, b)

@@ -34,7 +34,7 @@ from .quant import dequant_fp8_group, dequant_fp8_per_token, dequant_mxfp4, dequ
 
 @dataclass
 class WeightDesc:
-    weight_dtype: str          # "int1".."int4" | "uint1".."uint4" | "int8" | "e2m1" | "e4m3"
+    weight_dtype: str          # "int1".."int4" | "uint1".."uint4" | "int8" | "e2m1" | "e2m3" | "e3m2" | "e4m3"
     scale_gran: str            # "tensor" | "channel" | "group"
     group_size: int            # along K (ignored unless scale_gran == "group")
     scale_dtype: str           # "bf16" | "f32" | "e8m0" | "e4m3" (NVFP4: E2M1 codes, G = 16)

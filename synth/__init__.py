@@ -156,6 +156,8 @@ def quant_weights(seed: int, weight_dtype: str, scale_gran: str, group: int,
     elif weight_dtype in INT_BITS:
         b = INT_BITS[weight_dtype]
         codes = pack_bits(g.integers(0, 1 << b, size=(e, n, k), dtype=np.uint8), b)
+    elif weight_dtype in ("e2m3", "e3m2"):
+        codes = pack_bits(g.integers(0, 64, size=(e, n, k), dtype=np.uint8), 6)
     else:
         codes = pack_nibbles(g.integers(0, 16, size=(e, n, k), dtype=np.uint8))
     if scale_dtype == "bf16":

@@ -29,6 +29,16 @@ def s_intb(c, b):
     return c - (1 << b) if c >= (1 << (b - 1)) else c
 
 
+def s_fp6(c, ebits):
+    """FP6 code -> exact rational from its bit fields (OCP MX: E2M3 bias 1,
+    E3M2 bias 3; exponent 0 subnormal)."""
+    mbits, bias = 5 - ebits, (1 if ebits == 2 else 3)
+    s, e, m = c >> 5, (c >> mbits) & ((1 << ebits) - 1), c & ((1 << mbits) - 1)
+    v = Fraction(m, 1 << mbits) * Fraction(2) ** (1 - bias) if e == 0 else \
+        (1 + Fraction(m, 1 << mbits)) * Fraction(2) ** (e - bias)
+    return -v if s else v
+
+
 def s_e2m1(c):
     v = E2M1[c & 7]
     return -v if c & 8 else v
@@ -56,7 +66,8 @@ def brute_linear(desc, a_vals, codes_unpacked, scales, zeros, gscale):
     """C[m][n] with exact rationals, one scalar at a time."""
     dec = {"int4": s_int4, "uint4": lambda c: c, "int8": s_int8, "e2m1": s_e2m1, "e4m3": s_e4m3,
            "int3": lambda c: s_intb(c, 3), "int2": lambda c: s_intb(c, 2), "int1": lambda c: s_intb(c, 1),
-           "uint3": lambda c: c, "uint2": lambda c: c, "uint1": lambda c: c}[desc.weight_dtype]
+           "uint3": lambda c: c, "uint2": lambda c: c, "uint1": lambda c: c,
+           "e2m3": lambda c: s_fp6(c, 2), "e3m2": lambda c: s_fp6(c, 3)}[desc.weight_dtype]
     m, k = len(a_vals), desc.k
     out = []
     for i in range(m):
@@ -103,8 +114,10 @@ CASES = [
     ("uint2", "group", 16, "f32", True, True),
     ("int1", "group", 32, "bf16", False, False),
     ("uint1", "tensor", 0, "f32", True, False),
+    ("e2m3", "group", 32, "e8m0", False, False),
+    ("e3m2", "group", 32, "e8m0", False, True),
 ]
-BITS = {"int3": 3, "uint3": 3, "int2": 2, "uint2": 2, "int1": 1, "uint1": 1}
+BITS = {"int3": 3, "uint3": 3, "int2": 2, "uint2": 2, "int1": 1, "uint1": 1, "e2m3": 6, "e3m2": 6}
 
 
 @pytest.mark.parametrize("wd,gran,gs,sd,zp,gl", CASES)
@@ -374,3 +387,25 @@ def test_low_bit_codes_equal_zero_point_give_zero(wd):
     a = decode_bf16(bf16_bits(g.standard_normal((3, k)).astype(np.float32)))
     d = G.WeightDesc(wd, "group", gs, "bf16", True, False, 1, n, k)
     assert np.all(G.linear(d, a, pack_bits(cu, b), sc, z) == 0)
+
+
+@pytest.mark.parametrize("wd", ["e2m3", "e3m2"])
+def test_fp6_values_match_ocp_table(wd):
+    """Every FP6 code against the OCP MX v1.0 value table (golden file), both
+    signs, through the canonical 6-bit stream."""
+    import os
+    from oracle.formats import decode_weight_codes
+    path = os.path.join(os.path.dirname(__file__), "golden", f"{wd}_values.txt")
+    table = {}
+    for ln in open(path):
+        if ln.startswith("#") or not ln.strip():
+            continue
+        c, v = ln.split()
+        table[int(c, 16)] = float(v)
+    assert len(table) == 32
+    codes = np.arange(64, dtype=np.uint8)[None, :]
+    got = decode_weight_codes(pack_bits(codes, 6), wd)[0]
+    for c in range(64):
+        want = table[c & 31] * (-1.0 if c & 32 else 1.0)
+        assert got[c] == want and np.signbit(got[c]) == bool(c & 32), (c, got[c], want)
+    assert got.max() == (7.5 if wd == "e2m3" else 28.0)
