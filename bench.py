@@ -46,7 +46,7 @@ FP8_PEAK = 5.0e15
 FP4_PEAK = 10.1e15
 
 SUITES = ("dense_w4a16", "tiny", "w8a8", "w8a8_block", "w8a16_fp8", "w8a16_int8", "w4a16_mxfp4",
-          "w4a16_nvfp4", "w4a16_mxint4", "w3a16", "w2a16", "w4a4", "moe_w4a16", "moe_w4a8", "moe_w4a4", "moe_masked",
+          "w4a16_nvfp4", "w4a16_mxint4", "w3a16", "w2a16", "w6a16", "w4a4", "moe_w4a16", "moe_w4a8", "moe_w4a4", "moe_masked",
           "moe_w8a8_block", "peaks")
 
 
@@ -260,6 +260,18 @@ def dense_lowbit(hum, timer, iters, wd):
     wbytes = n * k * bits // 8 + n * (k // 128) * 2
     return dense_sweep(hum, timer, iters, f"w{bits}a16_{wd}", desc, packed, wbytes, sizes(synth.DENSE_SWEEP_M), 64,
                        BF16_PEAK, synth.seed_for(12, 9))
+
+
+def dense_mxfp6(hum, timer, iters):
+    """MXFP6 E2M3 weights (E8M0 per 32) x bf16 at N = K = 8192."""
+    import synth
+    n = k = 8192
+    w = synth.quant_weights(synth.seed_for(13), "e2m3", "group", 32, "e8m0", 1, n, k)
+    desc = hum.make_desc("e2m3", "group", 32, "e8m0", n, k)
+    packed = hum.prepare_weight(desc, _dev(w["codes"]), _dev(w["scales"]))
+    wbytes = n * k * 6 // 8 + n * (k // 32)
+    return dense_sweep(hum, timer, iters, "w6a16_mxfp6", desc, packed, wbytes, sizes(synth.DENSE_SWEEP_M), 64,
+                       BF16_PEAK, synth.seed_for(13, 1))
 
 
 def dense_tiny(hum, timer, iters):
@@ -573,6 +585,7 @@ def run_suites(hum, timer, iters, want, peaks, d=None):
         ("w4a16_mxint4", "dense_w4a16_mxint4_n8192_k8192", lambda: dense_w4a16_fp4(hum, timer, iters, "mxint4")),
         ("w3a16", "dense_w3a16_int3_g128_n8192_k8192", lambda: dense_lowbit(hum, timer, iters, "int3")),
         ("w2a16", "dense_w2a16_int2_g128_n8192_k8192", lambda: dense_lowbit(hum, timer, iters, "int2")),
+        ("w6a16", "dense_w6a16_mxfp6_e2m3_n8192_k8192", lambda: dense_mxfp6(hum, timer, iters)),
         ("w4a4", "dense_w4a4_mxfp4_n7168_k2048", lambda: dense_w4a4(hum, timer, iters)),
         ("moe_w4a16", "moe_w4a16_mxfp4_e128_top8_h4096_i1024", lambda: moe(hum, timer, iters, "bf16", peaks)),
         ("moe_w4a8", "moe_w4a8_mxfp4_mxfp8_zipf1.1_e128_top8_h4096_i1024",

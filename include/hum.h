@@ -68,7 +68,13 @@ typedef enum hum_dtype {
   HUM_INT2 = 10,  /* -2..1 */
   HUM_UINT2 = 11, /* 0..3 */
   HUM_INT1 = 12,  /* -1..0 */
-  HUM_UINT1 = 13  /* 0..1 */
+  HUM_UINT1 = 13, /* 0..1 */
+  /* FP6 weights (OCP MX v1.0 element types; "WnA16" in the Humming
+     announcement runs FP4 to FP8 weights): codes packed as an LSB-first 6-bit
+     stream along K ([E][N][K*6/8]), an E8M0 scale per 32 along K (MXFP6),
+     bf16 activations. */
+  HUM_E2M3 = 14,  /* exponent bias 1, 3 mantissa bits, max 7.5 */
+  HUM_E3M2 = 15   /* exponent bias 3, 2 mantissa bits, max 28 */
 } hum_dtype;
 
 typedef enum hum_scale_gran {
@@ -140,7 +146,7 @@ size_t hum_packed_weight_bytes(const hum_weight_desc* desc);
 
 /* Canonical ("standard format") tensors -> packed kernel layout.
  *   codes  : u8 [E][N][K/2] (4-bit), [E][N][K] (INT8, E4M3) or
- *            [E][N][K*b/8] (b-bit integers, b = 1, 2, 3)
+ *            [E][N][K*b/8] (b-bit integers, b = 1, 2, 3; FP6: b = 6)
  *   scales : [E][N'][K/G'] in scale_dtype (N' = 1 for TENSOR, G' per gran)
  *   zeros  : u8 [E][N'][K/G'] or NULL when has_zero_point == 0
  *   global_scale : f32 [E] or NULL when has_global_scale == 0

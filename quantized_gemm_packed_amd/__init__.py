@@ -15,7 +15,7 @@ from dataclasses import dataclass
 __all__ = [
     "HumError", "WeightDesc", "TileConfig", "lib_path", "load_library",
     "BF16", "F32", "INT4", "UINT4", "E2M1", "E4M3", "E8M0", "INT8",
-    "INT3", "UINT3", "INT2", "UINT2", "INT1", "UINT1",
+    "INT3", "UINT3", "INT2", "UINT2", "INT1", "UINT1", "E2M3", "E3M2",
     "SCALE_TENSOR", "SCALE_CHANNEL", "SCALE_GROUP", "SCALE_BLOCK",
     "ACT_BF16", "ACT_FP8_TOKEN", "ACT_MXFP8", "ACT_MXFP4", "ACT_FP8_GROUP",
     "packed_weight_bytes", "prepare_weight", "dequant_weight", "quant_act",
@@ -23,9 +23,9 @@ __all__ = [
     "moe_gemm", "moe_align", "moe_reduce", "Workspace", "header_functions",
 ]
 
-BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0, INT8, INT3, UINT3, INT2, UINT2, INT1, UINT1 = range(14)
+BF16, F32, INT4, UINT4, E2M1, E4M3, E8M0, INT8, INT3, UINT3, INT2, UINT2, INT1, UINT1, E2M3, E3M2 = range(16)
 # bits per code of the packed-integer weight dtypes (LSB-first bit stream along K)
-_BITS = {INT4: 4, UINT4: 4, E2M1: 4, INT3: 3, UINT3: 3, INT2: 2, UINT2: 2, INT1: 1, UINT1: 1}
+_BITS = {INT4: 4, UINT4: 4, E2M1: 4, INT3: 3, UINT3: 3, INT2: 2, UINT2: 2, INT1: 1, UINT1: 1, E2M3: 6, E3M2: 6}
 KERNEL_TILE, KERNEL_STREAM, KERNEL_TILE32 = range(3)
 SCALE_TENSOR, SCALE_CHANNEL, SCALE_GROUP, SCALE_BLOCK = range(4)
 ACT_BF16, ACT_FP8_TOKEN, ACT_MXFP8, ACT_MXFP4, ACT_FP8_GROUP = range(5)
@@ -217,7 +217,7 @@ def _check_linear_args(desc, packed, a, a_scales, bias, out):
 
 
 _DT = {"int4": INT4, "uint4": UINT4, "e2m1": E2M1, "e4m3": E4M3, "int8": INT8, "int3": INT3, "uint3": UINT3,
-       "int2": INT2, "uint2": UINT2, "int1": INT1, "uint1": UINT1}
+       "int2": INT2, "uint2": UINT2, "int1": INT1, "uint1": UINT1, "e2m3": E2M3, "e3m2": E3M2}
 _GR = {"tensor": SCALE_TENSOR, "channel": SCALE_CHANNEL, "group": SCALE_GROUP, "block": SCALE_BLOCK}
 _SD = {"bf16": BF16, "f32": F32, "e8m0": E8M0, "e4m3": E4M3}
 _AF = {"bf16": ACT_BF16, "fp8_token": ACT_FP8_TOKEN, "mxfp8": ACT_MXFP8, "mxfp4": ACT_MXFP4,

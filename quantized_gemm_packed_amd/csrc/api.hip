@@ -89,6 +89,13 @@ hum_status check_desc(const hum_weight_desc* d) {
       if (d->act_fmt != HUM_ACT_BF16 && d->act_fmt != HUM_ACT_MXFP8 && d->act_fmt != HUM_ACT_MXFP4)
         return set_error(HUM_ERR_UNSUPPORTED, "MXFP4 runs with bf16, MXFP8 or MXFP4 activations");
       return HUM_OK;
+    case HUM_E2M3:
+    case HUM_E3M2:
+      if (d->scale_gran != HUM_SCALE_GROUP || d->group_size != 32 || d->scale_dtype != HUM_E8M0)
+        return set_error(HUM_ERR_UNSUPPORTED, "FP6 weights need E8M0 scales per 32 along K (MXFP6)");
+      if (d->has_zero_point) return set_error(HUM_ERR_UNSUPPORTED, "FP6 takes no zero point");
+      if (d->act_fmt != HUM_ACT_BF16) return set_error(HUM_ERR_UNSUPPORTED, "MXFP6 weights run with bf16 activations");
+      return HUM_OK;
     case HUM_INT8:
       if (d->scale_gran != HUM_SCALE_CHANNEL && d->scale_gran != HUM_SCALE_TENSOR)
         return set_error(HUM_ERR_UNSUPPORTED, "INT8 weights take per-channel or per-tensor scales");
@@ -118,6 +125,8 @@ int fmt_of(const hum_weight_desc* d) {
     default: break;
   }
   if (d->weight_dtype == HUM_INT8) return F_INT8_BF16;
+  if (d->weight_dtype == HUM_E2M3) return F_MXFP6_BF16;
+  if (d->weight_dtype == HUM_E3M2) return F_MXBF6_BF16;
   if (d->weight_dtype == HUM_E4M3)
     return d->scale_gran == HUM_SCALE_BLOCK ? F_FP8_BLOCK : (d->act_fmt == HUM_ACT_BF16 ? F_FP8_BF16 : F_FP8);
   if (d->scale_dtype == HUM_E4M3) return F_NVFP4_BF16;
@@ -133,7 +142,8 @@ hum_status compute_layout(const hum_weight_desc* d, Layout* L) {
   L->kb = d->k / kKBlk;
   L->kb4 = cdiv(L->kb, 4);
   const int f = fmt_of(d);
-  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || fmt_w8_bf16(f)) ? 32 : (fmt_int(f) ? 4 * fmt_int_bits(f) : 16);
+  L->code_bytes = (f == F_FP8 || f == F_FP8_BLOCK || fmt_w8_bf16(f)) ? 32
+                  : (fmt_int(f) ? 4 * fmt_int_bits(f) : (fmt_fp6(f) ? 24 : 16));
   L->codes_per_expert = L->nt * L->kb * 64 * L->code_bytes;
   if (fmt_int(f)) {
     const bool grp = d->scale_gran == HUM_SCALE_GROUP && d->group_size < d->k;
@@ -240,7 +250,8 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     const int64_t a_bytes = m * (bf16_act ? 2 : 1);            // per k
     const int64_t w_bytes16 = (fmt_of(d) == F_FP8 || fmt_w8_bf16(fmt_of(d)))
                                   ? 16
-                                  : (fmt_int(fmt_of(d)) ? 2 * fmt_int_bits(fmt_of(d)) : 8);  // per k of a 16-column sub-tile
+                                  : (fmt_int(fmt_of(d)) ? 2 * fmt_int_bits(fmt_of(d))
+                                                        : (fmt_fp6(fmt_of(d)) ? 12 : 8));  // per k of a 16-column sub-tile
     const int64_t need = cdiv(a_bytes, w_bytes16);
     c.wave_n = need <= 1 ? 1 : (need <= 2 ? 2 : 4);
     const int64_t wgs = cdiv(nt, c.wave_n);

@@ -65,6 +65,8 @@ static const ReduceInstance kReduces[] = {
     {F_INT3, EPI_BF16, splitk_reduce_kernel<F_INT3, EPI_BF16>},
     {F_INT2, EPI_BF16, splitk_reduce_kernel<F_INT2, EPI_BF16>},
     {F_INT1, EPI_BF16, splitk_reduce_kernel<F_INT1, EPI_BF16>},
+    {F_MXFP6_BF16, EPI_BF16, splitk_reduce_kernel<F_MXFP6_BF16, EPI_BF16>},
+    {F_MXBF6_BF16, EPI_BF16, splitk_reduce_kernel<F_MXBF6_BF16, EPI_BF16>},
     {F_FP8, EPI_BF16, splitk_reduce_kernel<F_FP8, EPI_BF16>},
     {F_MXFP4_BF16, EPI_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_BF16>},
     {F_MXFP4_BF16, EPI_SWIGLU_BF16, splitk_reduce_kernel<F_MXFP4_BF16, EPI_SWIGLU_BF16>},

@@ -44,6 +44,8 @@
 //                  through f32 (exact), the FP8 path's layout and epilogue.
 //   F_NVFP4_BF16   NVFP4: E2M1 -> f32, times its E4M3 scale per 16 (exact: at
 //                  most 6 significant bits) -> bf16.
+//   F_MXFP6_BF16 / F_MXBF6_BF16  MXFP6 (E2M3 / E3M2 with an E8M0 scale per
+//                  32): the 32-wide hardware FP6 -> bf16 conversion, bf16 MFMA.
 //   F_MXINT4_BF16  MXINT4: INT4 with an E8M0 scale per 32 -> f32 -> bf16
 //                  (exact), the MX path's scale staging.
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
@@ -76,7 +78,7 @@ struct Tr {
   // integer family: bits per code; code bytes per lane per K-block (b-bit
   // integers: 4b, else 16 per 16-byte word)
   static constexpr int kIntBits = fmt_int_bits(FMT);
-  static constexpr int kCodeB = fmt_int(FMT) ? 4 * kIntBits : 16 * kBWords;
+  static constexpr int kCodeB = fmt_int(FMT) ? 4 * kIntBits : (fmt_fp6(FMT) ? 24 : 16 * kBWords);
   // MX / NVFP4 weight scales: a metadata row (a dword per lane) covers
   // 1 << kMetaRowShift K-blocks (E8M0 per 32: 4; NVFP4's two E4M3 per 32: 2)
   static constexpr int kMetaRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
@@ -91,12 +93,13 @@ struct Tr {
 // (b < 4) b dwords.
 template <int B>
 struct CodeWord { using type = u32x4_t; };
+template <> struct CodeWord<24> { using type = u32x6_t; };
 template <> struct CodeWord<12> { using type = u32x3_t; };
 template <> struct CodeWord<8> { using type = u32x2_t; };
 template <> struct CodeWord<4> { using type = u32x1_t; };
 
 template <int FMT>
-using CodeW = typename CodeWord<Tr<FMT>::kCodeB < 16 ? Tr<FMT>::kCodeB : 16>::type;
+using CodeW = typename CodeWord<(Tr<FMT>::kCodeB < 16 || Tr<FMT>::kCodeB == 24) ? Tr<FMT>::kCodeB : 16>::type;
 
 // One buffer load of a lane's code word (16-byte words: one of them).
 template <int FMT>
@@ -110,6 +113,10 @@ __device__ __forceinline__ CodeW<FMT> load_code_word(__amdgpu_buffer_rsrc_t r, u
     return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   } else if constexpr (B == 12) {
     return __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+  } else if constexpr (B == 24) {
+    const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x2_t b = __builtin_amdgcn_raw_buffer_load_b64(r, off + 16, 0, 0);
+    return CodeW<FMT>{a[0], a[1], a[2], a[3], b[0], b[1]};
   } else {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   }
@@ -186,7 +193,7 @@ __device__ __forceinline__ WStripe make_stripe(const GemmParams& p, const WPtrs&
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
     const int64_t zb = (int64_t)p.ng * 8;
     s.zero = make_rsrc(w.zero + ntc * zb, (valid && p.has_zero) ? zb : 0);
-  } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
+  } else if (fmt_mx_meta(FMT)) {
     const int64_t sb = (int64_t)p.kb4 * 256;
     s.meta = make_rsrc(w.meta + ntc * sb, valid ? sb : 0);
   }
@@ -217,7 +224,7 @@ __device__ __forceinline__ BFrag<FMT> load_b(const GemmParams& p, const WStripe&
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, so, 0, 0);
     const uint32_t zo = ok ? (uint32_t)gi * 8 + ((c16 >> 3) << 2) : kOob;
     f.zero = __builtin_amdgcn_raw_buffer_load_b32(s.zero, zo, 0, 0);
-  } else if (META && (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16)) {
+  } else if (META && (fmt_mx_meta(FMT))) {
     const uint32_t mo = ok ? (uint32_t)((kb >> Tr<FMT>::kMetaRowShift) * 64 + lane) * 4 : kOob;
     f.meta = __builtin_amdgcn_raw_buffer_load_b32(s.meta, mo, 0, 0);
   }
@@ -359,6 +366,25 @@ __device__ __forceinline__ void dequant_b(const BFrag<FMT>& f, uint32_t meta, in
       o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
       d[s] = __builtin_bit_cast(bf16x8_t, o);
     }
+  } else if constexpr (fmt_fp6(FMT)) {
+    // MXFP6: the lane's 32 codes of the K-block (a 6-bit stream) through the
+    // hardware's 32-wide FP6 -> bf16 conversion with the E8M0 scale (exact:
+    // at most 4 significant bits); element j of k-step s is bf16 8 s + j.
+    // (The result is taken as a whole: per-element extraction from the
+    // 32-wide vector is avoided.)
+    typedef int i32x6_t __attribute__((ext_vector_type(6)));
+    typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+    const float fs = e8m0_to_f32(frag_mx_code(meta, kb));
+    const i32x6_t x = __builtin_bit_cast(i32x6_t, f.w[0]);
+    bf16x32_t r;
+    if constexpr (FMT == F_MXFP6_BF16)
+      r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(x, fs);
+    else
+      r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(x, fs);
+    struct Steps { bf16x8_t s[4]; };
+    const Steps st = __builtin_bit_cast(Steps, r);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) d[s] = st.s[s];
   } else if constexpr (FMT == F_MXINT4_BF16) {
     // MXINT4: the integer path's nibble order (k-step s in dword s, element
     // j at bit (j & 1) * 16 + (j >> 1) * 4) holding q + 8; (u - 8) * 2^E is
@@ -808,7 +834,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
           }
         }
       }
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nkb > 0) {
+    } else if ((fmt_mx_meta(FMT)) && nkb > 0) {
       const int n16 = (((kb_end + (1 << kRS) - 1) >> kRS) - r0) * 16;  // 16-byte slots of scale rows
 #pragma unroll
       for (int ns = 0; ns < WN; ++ns) {
@@ -867,7 +893,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     // weight metadata of the wave's K-blocks (INT: scales and zero points of
     // the groups they touch; MX: their 4-K-block E8M0 rows), up to kML KB
     constexpr int kML =
-        fmt_int(FMT) ? 1 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) ? 2 : 0);
+        fmt_int(FMT) ? 1 : ((fmt_mx_meta(FMT)) ? 2 : 0);
     u32x4_t mbuf[WN][kML > 0 ? kML : 1];
     uint32_t zbuf[WN];
     int mb0 = 0, mbytes = 0, zb0 = 0, zbytes = 0, mdst = 0, zdst = 0;
@@ -880,7 +906,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       zb0 = g0w * 8;
       zbytes = p.has_zero ? (g1w - g0w) * 8 : 0;  // <= 256 B
       zdst = p.lds_zero_off + (g0w - g0) * 8;
-    } else if ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) && nj > 0) {
+    } else if ((fmt_mx_meta(FMT)) && nj > 0) {
       const int rw0 = kw0 >> kRS, rw1 = (kw0 + nj + (1 << kRS) - 1) >> kRS;
       mb0 = rw0 * 256;
       mbytes = (rw1 - rw0) * 256;  // <= 2 KB
@@ -944,7 +970,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       m = *reinterpret_cast<const uint32_t*>(mb + ((gl * 16 + (c16 & (14 | sf))) << (1 + sf)));
       const uint32_t zr = *reinterpret_cast<const uint32_t*>(mb + p.lds_zero_off + gl * 8 + ((c16 >> 3) << 2));
       z = p.has_zero ? zr : 0u;
-    } else if (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_NVFP4_BF16) {
+    } else if (fmt_mx_meta(FMT)) {
       m = *reinterpret_cast<const uint32_t*>(mb + (((kb >> kRS) - r0) * 64 + lane) * 4);
     }
   };
@@ -1107,8 +1133,7 @@ struct TileCfg {
   static constexpr bool kTracked = (kS == 3);
   static constexpr int kMI = (fmt_int(FMT) || FMT == F_FP8_BLOCK)
                                  ? 1
-                                 : ((FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                                     FMT == F_NVFP4_BF16) ? WN : 0);
+                                 : ((fmt_mx_meta(FMT) || FMT == F_MXFP4_MXFP4) ? WN : 0);
   static constexpr int kM = 4 * kMI * 256;                       // metadata words (per wave: kMI x 256 B)
   static constexpr int kStage = kA + kXI * 256 + kB + kM;
   static constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
@@ -1305,8 +1330,7 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
     const uint32_t nt = ntv[sub] ? (uint32_t)nts[sub] : 0u;
     mi_off = nt * p.ng * 16 * (2 << sf) + d * 4;
     mi_gmul = 16u * (2u << sf);
-  } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                       FMT == F_NVFP4_BF16) {
+  } else if constexpr (fmt_mx_meta(FMT) || FMT == F_MXFP4_MXFP4) {
     rms = rsrc_words(wp.meta, p.scales_per_expert);
     rmsr = make_rsrc(wp.meta, p.scales_per_expert);
   } else if constexpr (FMT == F_FP8_BLOCK) {
@@ -1368,8 +1392,7 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
       dma4(rms, rmsr, mw, mi_off + (uint32_t)gi * mi_gmul);
     } else if constexpr (FMT == F_FP8_BLOCK) {
       dma4(rms, rmsr, mw, mi_off + (uint32_t)kb * 4u);
-    } else if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 ||
-                         FMT == F_NVFP4_BF16) {
+    } else if constexpr (fmt_mx_meta(FMT) || FMT == F_MXFP4_MXFP4) {
       // a metadata row covers 4 K-blocks (E8M0 per 32) or 2 (NVFP4: two
       // E4M3 per 32 of a lane)
       constexpr int kRowShift = FMT == F_NVFP4_BF16 ? 1 : 2;
@@ -1437,7 +1460,7 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
         bf[ns].w[h] = C::kBReg ? bsrc[ns].w[h]
                                : *reinterpret_cast<const CodeW<FMT>*>(bbase + ns * C::kCB + lane * T::kCodeB + h * 16);
       mw[ns] = 0;
-      if constexpr (FMT == F_MXFP4_BF16 || FMT == F_MXINT4_BF16 || FMT == F_MXFP4_MXFP8 || FMT == F_MXFP4_MXFP4 || FMT == F_NVFP4_BF16)
+      if constexpr (fmt_mx_meta(FMT) || FMT == F_MXFP4_MXFP4)
         mw[ns] = *reinterpret_cast<const uint32_t*>(mbase + ns * 256 + lane * 4);
     }
     if constexpr (FMT == F_FP8_BLOCK) {
@@ -2070,7 +2093,7 @@ InstanceTable instances_moe_c();
 
 // Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.
-#define HUM_PF(F, n) (((F) == F_FP8 || fmt_w8_bf16(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
+#define HUM_PF(F, n) (((F) == F_FP8 || fmt_w8_bf16(F) || fmt_fp6(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
 #define HUM_DENSE_SET(F)                                   \
   HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
   HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \

@@ -3,7 +3,9 @@
 // Packed weight layout (what hum_prepare_weight produces), per expert e:
 //
 //   codes : [NT][KB][64 lanes][B bytes]   NT = ceil(N/16), KB = K/128
-//           B = 16 for 4-bit formats, 32 for E4M3.  Lane l = c + 16*lg
+//           B = 16 for 4-bit formats, 32 for E4M3, 24 for FP6 (the
+//           canonical 6-bit stream of the lane's 32 codes, unchanged: the
+//           hardware's 32-wide FP6 conversion reads it in that order).  Lane l = c + 16*lg
 //           (c = column within the 16-column sub-tile, lg = 0..3) holds
 //             4-bit : k = 128*kb + 32*lg + (0..31)            (32 codes)
 //             E4M3  : k = 128*kb + 16*lg + (0..15) then
@@ -67,8 +69,17 @@ struct Layout {
 
 enum Fmt : int {
   F_INT = 0, F_MXFP4_BF16 = 1, F_FP8 = 2, F_MXFP4_MXFP8 = 3, F_MXFP4_MXFP4 = 4, F_FP8_BLOCK = 5, F_FP8_BF16 = 6,
-  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8, F_MXINT4_BF16 = 9, F_INT3 = 10, F_INT2 = 11, F_INT1 = 12
+  F_INT8_BF16 = 7, F_NVFP4_BF16 = 8, F_MXINT4_BF16 = 9, F_INT3 = 10, F_INT2 = 11, F_INT1 = 12,
+  F_MXFP6_BF16 = 13, F_MXBF6_BF16 = 14
 };
+
+// MXFP6 weights (E2M3 / E3M2 codes, E8M0 per 32) x bf16 activations.
+constexpr bool fmt_fp6(int f) { return f == F_MXFP6_BF16 || f == F_MXBF6_BF16; }
+// Formats whose weight metadata are per-lane rows of scale bytes (E8M0 per
+// 32: a dword per lane covers 4 K-blocks; NVFP4's E4M3 per 16: 2).
+constexpr bool fmt_mx_meta(int f) {
+  return f == F_MXFP4_BF16 || f == F_MXINT4_BF16 || f == F_MXFP4_MXFP8 || f == F_NVFP4_BF16 || fmt_fp6(f);
+}
 
 // The integer family (b-bit codes with bf16 / f32 group scales, optional
 // zero points, bf16 activations): one kernel path, b = 4, 3, 2, 1.
@@ -90,7 +101,7 @@ constexpr bool dtype_int_signed(int dt) {
 // Formats whose activations stay bf16 (bf16 MFMA on widened weights).
 constexpr bool fmt_bf16_act(int f) {
   return fmt_int(f) || f == F_MXFP4_BF16 || f == F_FP8_BF16 || f == F_INT8_BF16 || f == F_NVFP4_BF16 ||
-         f == F_MXINT4_BF16;
+         f == F_MXINT4_BF16 || fmt_fp6(f);
 }
 // 8-bit weight codes laid out for the bf16 MFMA: a lane's 32 codes of a
 // K-block contiguous (k = 32 * (lane / 16) + j), per-channel f32 scales.
@@ -251,7 +262,7 @@ constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, i
     const int64_t zr = ((groups * 8 + 255) / 256) * 256;
     L.zero_off = sc;
     L.meta_stride = sc + zr;
-  } else if (fmt == F_MXFP4_BF16 || fmt == F_MXINT4_BF16 || fmt == F_MXFP4_MXFP8 || fmt == F_NVFP4_BF16) {
+  } else if (fmt_mx_meta(fmt)) {
     // scale rows a range of kb blocks touches (a row: 4 K-blocks, NVFP4 2)
     int64_t r = (fmt == F_NVFP4_BF16 ? kb / 2 : kb / 4) + 2;
     if (r > kb4) r = kb4;
@@ -273,7 +284,7 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
     const int64_t groups = (per + kb_per_group - 1) / kb_per_group + 1;
     return groups * 16 * (scale_f32 ? 4 : 2) <= 1024 && groups * 8 <= 256;
   }
-  if (fmt == F_MXFP4_BF16 || fmt == F_MXINT4_BF16 || fmt == F_MXFP4_MXFP8) return (per / 4 + 2) * 256 <= 2048;
+  if (fmt_mx_meta(fmt) && fmt != F_NVFP4_BF16) return (per / 4 + 2) * 256 <= 2048;
   if (fmt == F_NVFP4_BF16) return (per / 2 + 2) * 256 <= 2048;
   return true;
 }

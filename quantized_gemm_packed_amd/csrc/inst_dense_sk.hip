@@ -29,6 +29,8 @@ static const Instance kDenseSk[] = {
     HUM_TILE_SK(F_INT3, 2, 2, 3, 16),
     HUM_TILE_SK(F_INT2, 2, 2, 3, 16),
     HUM_TILE_SK(F_INT1, 2, 2, 3, 16),
+    HUM_TILE_SK(F_MXFP6_BF16, 2, 2, 3, 16),
+    HUM_TILE_SK(F_MXBF6_BF16, 2, 2, 3, 16),
 };
 
 HUM_TABLE(instances_dense_sk, kDenseSk)

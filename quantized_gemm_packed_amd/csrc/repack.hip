@@ -113,6 +113,16 @@ __global__ void repack_codes_kernel(RepackArgs a) {
     u32x4_t* d = reinterpret_cast<u32x4_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 32);
     d[0] = lo;
     d[1] = hi;
+  } else if (a.wdt == HUM_E2M3 || a.wdt == HUM_E3M2) {
+    // FP6: the canonical 6-bit stream of the lane's 32 codes, as is (24
+    // dword-aligned bytes: K is a multiple of 128)
+    uint32_t v[6] = {0, 0, 0, 0, 0, 0};
+    if (n < a.n) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(a.codes + ((e * a.n + n) * a.k + kb * kKBlk + 32 * lg) * 6 / 8);
+      for (int i = 0; i < 6; ++i) v[i] = w[i];
+    }
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + ((nt * a.kb + kb) * 64 + lane) * 24);
+    for (int i = 0; i < 6; ++i) d[i] = v[i];
   } else if (dtype_int_bits(a.wdt) != 0 && dtype_int_bits(a.wdt) < 4) {
     const int bits = dtype_int_bits(a.wdt);
     uint32_t v[3];
@@ -340,7 +350,7 @@ hum_status launch_repack(const hum_weight_desc* d, const Layout& L, const void* 
     repack_int_co_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kbc * 64, B), B, 0, s>>>(a);
   } else if (f == F_NVFP4_BF16) {
     repack_nv_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
-  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4 || f == F_MXINT4_BF16) {
+  } else if (f == F_MXFP4_BF16 || f == F_MXFP4_MXFP8 || f == F_MXFP4_MXFP4 || f == F_MXINT4_BF16 || fmt_fp6(f)) {
     repack_mx_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb4 * 64, B), B, 0, s>>>(a);
   } else if (f == F_FP8_BLOCK) {
     repack_fp8_block_meta_kernel<<<grid_for((int64_t)d->num_experts * L.nt * L.kb, B), B, 0, s>>>(a);
@@ -406,6 +416,23 @@ __global__ void dequant_kernel(DequantArgs a) {
     for (int j = 0; j < 32; ++j) {
       const int kk = a.bf16_order ? (32 * lg + j) : ((j < 16) ? (16 * lg + j) : (64 + 16 * lg + j - 16));
       orow[kk] = (a.wdt == HUM_INT8 ? (float)(int8_t)src[j] : e4m3_value(src[j])) * s;
+    }
+    return;
+  }
+  if (a.wdt == HUM_E2M3 || a.wdt == HUM_E3M2) {
+    // FP6: sign, exponent (bias 1 / 3), mantissa; exponent 0 subnormal
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(base + ((nt * a.kb + kb) * 64 + lane) * 24);
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(
+        a.packed + a.scales_off + e * a.scales_pe + ((nt * a.kb4 + kb / 4) * 64 + lane) * 4);
+    const float s = e8m0_to_f32((word >> (8 * (kb % 4))) & 0xFF);
+    const int eb = a.wdt == HUM_E2M3 ? 2 : 3, mb = 5 - eb, bias = a.wdt == HUM_E2M3 ? 1 : 3;
+    for (int j = 0; j < 32; ++j) {
+      const int bit = 6 * j;
+      const uint64_t win = (uint64_t)w[bit / 32] | ((bit / 32 + 1 < 6) ? (uint64_t)w[bit / 32 + 1] << 32 : 0);
+      const uint32_t c = (uint32_t)(win >> (bit % 32)) & 63u;
+      const uint32_t ex = (c >> mb) & ((1u << eb) - 1), m = c & ((1u << mb) - 1);
+      const float mag = ex == 0 ? ldexpf((float)m, 1 - bias - mb) : ldexpf(1.0f + ldexpf((float)m, -mb), (int)ex - bias);
+      orow[32 * lg + j] = ((c & 32u) ? -mag : mag) * s;
     }
     return;
   }

@@ -138,6 +138,47 @@ def test_lowbit_random_vs_oracle(wd, gran, gs, sd, zero, m):
     assert_tol(out, ref, f"{wd} {gran} m={m}")
 
 
+@pytest.mark.parametrize("wd", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("tile", DENSE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_mxfp6_exact_every_tile(wd, tile):
+    """MXFP6 (E2M3 / E3M2 with E8M0 per 32) x integer activations: every FP6
+    code, scales 2^-1 .. 2^0, all sums exact in fp32 -- bit for bit on every
+    compiled tile, split 1 and 2."""
+    m, n, k = rows_for(tile, 19), 208, 1024
+    g = synth.rng(synth.seed_of("fp6x", wd))
+    xb = synth.bf16_bits(g.integers(-8, 9, size=(m, k)).astype(np.float32))
+    w = synth.quant_weights(synth.seed_of("fp6w", wd), wd, "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
+    hd, od = descs(wd, "group", 32, "e8m0", 1, n, k)
+    packed = prepare(hd, w, "e8m0")
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    for split in (1, 2):
+        print(f"case {wd} exact tile={tile} split={split}", flush=True)
+        if not stream_fits(tile, m, k, split):
+            continue
+        out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+        torch.cuda.synchronize()
+        assert_bf16_exact(out, ref, f"{wd} tile={tile} split={split}")
+
+
+@pytest.mark.parametrize("wd", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("m", [1, 9, 64, 300])
+def test_mxfp6_random_vs_oracle(wd, m):
+    """MXFP6 weights on random data at the selector's configuration, ragged N,
+    a bias and a global scale."""
+    n, k = 600, 2048
+    w = synth.quant_weights(synth.seed_of("fp6r", wd, m), wd, "group", 32, "e8m0", 1, n, k, global_scale=True)
+    hd, od = descs(wd, "group", 32, "e8m0", 1, n, k, glob=True)
+    xb = synth.bf16_normal(synth.rng(synth.seed_of("fp6rx", wd, m)), (m, k))
+    bias = synth.bf16_normal(synth.rng(synth.seed_of("fp6rb", wd)), (n,))
+    packed = prepare(hd, w, "e8m0")
+    print(f"case {wd} random m={m}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), bias=dev(bias))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"], None, w["global_scale"],
+                             bias_bits=bias)
+    assert_tol(out, ref, f"{wd} m={m}")
+
+
 @pytest.mark.parametrize("tile", DENSE_TILES + TILE32_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_mxfp4_bf16_exact_every_tile(tile):
     m, n, k = 9, 96, 1024

@@ -31,7 +31,7 @@ SK_TILES = [
     ("e2m1_mxfp4", 0, 2, 2, 3), ("e2m1_mxfp4", 0, 4, 4, 3),
     ("e4m3_block", 0, 2, 2, 3), ("e4m3_block", 0, 8, 2, 2),
     ("e4m3_bf16", 0, 2, 2, 3), ("int8", 0, 2, 2, 3), ("nvfp4", 0, 2, 2, 3), ("mxint4", 0, 2, 2, 3),
-    ("int3", 0, 2, 2, 3), ("uint2", 0, 2, 2, 3), ("int1", 0, 2, 2, 3),
+    ("int3", 0, 2, 2, 3), ("uint2", 0, 2, 2, 3), ("int1", 0, 2, 2, 3), ("e2m3", 0, 2, 2, 3), ("e3m2", 0, 2, 2, 3),
 ]
 
 
@@ -99,6 +99,12 @@ def _case(fmt, m, n, k, exact, seed):
         hd, od = descs(fmt, "group", 128, "bf16", 1, n, k, zero=zero)
         packed = prepare(hd, w, "bf16")
         return hd, packed, xb, oracle.gemm.linear(od, a, w["codes"], w["scales"], w.get("zeros"))
+    if fmt in ("e2m3", "e3m2"):
+        lo, hi = (126, 127) if exact else (119, 123)
+        w = synth.quant_weights(seed, fmt, "group", 32, "e8m0", 1, n, k, e8m0_lo=lo, e8m0_hi=hi)
+        hd, od = descs(fmt, "group", 32, "e8m0", 1, n, k)
+        packed = prepare(hd, w, "e8m0")
+        return hd, packed, xb, oracle.gemm.linear(od, a, w["codes"], w["scales"])
     if fmt == "nvfp4":
         lo, hi = (0x30, 0x38) if exact else (0x18, 0x38)
         w = synth.quant_weights(seed, "e2m1", "group", 16, "e4m3", 1, n, k, global_scale=not exact,

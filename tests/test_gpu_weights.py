@@ -31,6 +31,8 @@ FORMATS = [
     ("uint2", "group", 128, "bf16", True, False),
     ("int1", "tensor", 0, "bf16", False, False),
     ("uint1", "group", 128, "bf16", True, False),
+    ("e2m3", "group", 32, "e8m0", False, False),
+    ("e3m2", "group", 32, "e8m0", False, True),
 ]
 SHAPES = [(1, 40, 256), (3, 640, 1024), (2, 16, 128)]
 
