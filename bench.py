@@ -654,8 +654,12 @@ def main():
         "kernel": f"tile_kernel F_INT m={dom['m']} tile={dom['tile']} (+ rowsum_kernel)", "flops_per_launch": dom_flops,
         "us_per_launch": dom["us"],
     }
-    if "mfma_bf16_flops" in peaks:
-        roofline["frac_of_measured_peak"] = dom["tflops"] * 1e12 / peaks["mfma_bf16_flops"]
+    # the measured rate of the instruction shape the kernel issues (32x32x16
+    # for the 32x32-block tiles, 16x16x32 otherwise)
+    pk = "mfma32_bf16_flops" if dom["tile"][0] == 2 else "mfma_bf16_flops"
+    if pk in peaks:
+        roofline["frac_of_measured_peak"] = dom["tflops"] * 1e12 / peaks[pk]
+        roofline["measured_peak_key"] = pk
     del d["copies"]
     torch.cuda.empty_cache()
     sweep = run_suites(hum, timer, iters, want - {"dense_w4a16"}, peaks, d=d)

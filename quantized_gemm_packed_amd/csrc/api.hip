@@ -5,6 +5,7 @@
 // Humming: Fast, Flexible Kernels for Quantized Inference": the shape, the
 // format and the device's resources (here: 256 CUs, 160 KB LDS, wave64)
 // choose a tile and split per M range, at run time, with no compilation.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -1208,6 +1209,13 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const hum_tile_config& cu = mc.up;
   const hum_tile_config& cd = mc.dn;
   const int32_t bm = (int32_t)tile_rows(cu);
+  // Row tiles to launch.  Indexed layout: an expert with rows fills whole
+  // blocks from its (block-aligned) segment start, so the live blocks are a
+  // prefix of the padded block array, at most one per routed slot -- the
+  // blocks past t * topk are all padding and are not launched (at decode
+  // sizes most of the E * (block_m - 1) padding would be).  Masked layout:
+  // every expert buffer's blocks.
+  const int64_t m_tiles = r.counts ? w.nblocks : std::min<int64_t>(w.nblocks, t * (int64_t)r.topk);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + w.sorted);
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + w.bexp);
   const int act = w13->act_fmt;
@@ -1252,7 +1260,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const ActBytes xb = act_bytes(act, t, h);
   p.a_bytes = xb.codes;
   p.a_scale_bytes = xb.scales;
-  st = launch_gemm(kup, p, w.nblocks, bm, stream);
+  st = launch_gemm(kup, p, m_tiles, bm, stream);
   if (st != HUM_OK) return st;
   // FP8 per token / per group: quantize the live rows of the intermediate
   const void* a2 = ws + w.inter;
@@ -1291,7 +1299,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const ActBytes ab = act_bytes(act, w.cap, inter);
   q.a_bytes = ab.codes;
   q.a_scale_bytes = ab.scales;
-  return launch_gemm(kdn, q, w.nblocks, bm, stream);
+  return launch_gemm(kdn, q, m_tiles, bm, stream);
 }
 
 hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, const hum_weight_desc* w2,
