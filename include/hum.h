@@ -393,6 +393,17 @@ hum_status hum_moe_align(const int32_t* topk_ids, int64_t num_tokens, int32_t to
                          int32_t num_experts, int32_t block_m, int32_t* sorted,
                          int32_t* offsets, int32_t* counts, void* stream);
 
+/* The same sort with scratch for large routing tables, which many
+ * workgroups then share (the result is identical).  workspace: device
+ * buffer of hum_moe_align_workspace_bytes(num_tokens, topk, num_experts)
+ * bytes (0 when the table is small enough for one workgroup; NULL is then
+ * accepted); HUM_ERR_WORKSPACE if smaller. */
+size_t hum_moe_align_workspace_bytes(int64_t num_tokens, int32_t topk, int32_t num_experts);
+hum_status hum_moe_align_ex(const int32_t* topk_ids, int64_t num_tokens, int32_t topk,
+                            int32_t num_experts, int32_t block_m, int32_t* sorted,
+                            int32_t* offsets, int32_t* counts, void* workspace,
+                            size_t ws_bytes, void* stream);
+
 /* Stage export: out[t] = bf16(sum_j w[t][j] * y[t*topk + j]) with y bf16
  * [T*topk][h] indexed by flat slot, fp32 sum in fixed j order
  * ("moe_fused_mul_sum" in the SGLang PR #23754 summary). */

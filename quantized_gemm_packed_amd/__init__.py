@@ -106,6 +106,8 @@ _SIGS = {
     "hum_moe_gemm": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "hum_moe_gemm_ex": (_I32, [_DP, _P, _DP, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _CP, _P]),
     "hum_moe_align": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]),
+    "hum_moe_align_ex": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "hum_moe_align_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "hum_moe_reduce": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
     "hum_peak_probe": (_I32, [_I32, _I64, _P, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "hum_moe_grouped_gemm_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I64, _I32, _I64, _I32, _CP]),
@@ -567,8 +569,10 @@ def moe_gemm_masked(w13: WeightDesc, packed_w13, w2: WeightDesc, packed_w2, x, e
     return out
 
 
-def moe_align(topk_ids, num_experts: int, block_m: int):
-    """-> (sorted int32 [T*topk + E*(block_m-1)], offsets int32 [E+1], counts int32 [E])."""
+def moe_align(topk_ids, num_experts: int, block_m: int, multi_workgroup: bool = False):
+    """-> (sorted int32 [T*topk + E*(block_m-1)], offsets int32 [E+1], counts int32 [E]).
+    multi_workgroup: give the sort scratch so that large tables are shared by
+    many workgroups (the layer's own path); the result is the same."""
     import torch
     if topk_ids is None or topk_ids.dim() != 2:
         raise ValueError("topk_ids must be a 2-D tensor [T, topk]")
@@ -580,6 +584,13 @@ def moe_align(topk_ids, num_experts: int, block_m: int):
     srt = torch.empty(cap, dtype=torch.int32, device=dev)
     off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
     cnt = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    if multi_workgroup:
+        lib = load_library()
+        nb = lib.hum_moe_align_workspace_bytes(t, k, num_experts)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        _check(lib.hum_moe_align_ex(_ptr(topk_ids), t, k, num_experts, block_m, _ptr(srt), _ptr(off), _ptr(cnt),
+                                    _ptr(ws), nb, _stream(dev)))
+        return srt, off, cnt
     _check(load_library().hum_moe_align(_ptr(topk_ids), t, k, num_experts, block_m, _ptr(srt), _ptr(off), _ptr(cnt),
                                         _stream(dev)))
     return srt, off, cnt

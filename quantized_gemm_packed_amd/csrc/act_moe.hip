@@ -315,80 +315,22 @@ constexpr int kAlignWaves = kAlignThreads / 64;
 constexpr int kMaxExperts = 512;
 static_assert(kAlignThreads >= kMaxExperts, "one thread per expert in the offset scan");
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __restrict__ ids, int64_t n,
-                                                              int32_t num_experts, int32_t block_m,
-                                                              int32_t* __restrict__ sorted, int64_t cap,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ block_expert,
-                                                              int64_t nblocks) {
-  __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t off[kMaxExperts + 1];
-  __shared__ int32_t running[kMaxExperts];
-  __shared__ int32_t wcnt[kAlignWaves][kMaxExperts];  // per-wave counts of one chunk
+// Stable scatter of ids [i0, i1) (one workgroup, kAlignThreads lanes):
+// running[e] holds the next position of expert e's slots.  Sub-chunks of
+// kAlignThreads slots; lanes of a wave holding the same expert are found
+// with one ballot per id bit, per-wave counts go through an LDS table, so a
+// slot's position is running[e] + earlier waves + earlier lanes.
+__device__ void align_scatter_range(const int32_t* __restrict__ ids, int64_t i0, int64_t i1, int32_t E,
+                                    int32_t* running, int32_t (*wcnt)[kMaxExperts],
+                                    int32_t* __restrict__ sorted) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int32_t E = num_experts;
-  const int32_t sentinel = (int32_t)n;
-  for (int64_t i = tid; i < cap; i += kAlignThreads) sorted[i] = sentinel;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    cnt[e] = 0;
-    running[e] = 0;
-  }
-  __syncthreads();
-  for (int64_t i = tid; i < n; i += kAlignThreads) {
-    const int32_t e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  // padded segment sizes, exclusive scan over the experts: a shuffle scan
-  // inside each wave (64 experts), then the wave totals (at most 8 waves)
-  {
-    __shared__ int32_t wsum[kMaxExperts / 64];
-    const int e = tid;
-    int32_t v = 0;
-    if (e < E) v = (cnt[e] + block_m - 1) / block_m * block_m;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int32_t u = __shfl_up(v, d);
-      if (lane >= d) v += u;
-    }
-    if (e < kMaxExperts && lane == 63) wsum[wave] = v;
-    __syncthreads();
-    if (e < E) {
-      int32_t before = 0;
-      for (int w = 0; w < wave; ++w) before += wsum[w];
-      off[e + 1] = before + v;
-    }
-    if (tid == 0) off[0] = 0;
-  }
-  __syncthreads();
-  for (int e = tid; e <= E; e += kAlignThreads) offsets[e] = off[e];
-  for (int e = tid; e < E; e += kAlignThreads) counts[e] = cnt[e];
-  for (int64_t b = tid; b < nblocks; b += kAlignThreads) {
-    const int64_t pos = b * block_m;
-    int32_t ex = -1;
-    if (pos < off[E]) {
-      int lo = 0, hi = E - 1;  // largest e with off[e] <= pos
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= pos) lo = mid;
-        else hi = mid - 1;
-      }
-      ex = lo;
-    }
-    block_expert[b] = ex;
-  }
-  // Stable scatter, 1024 slots per chunk.  Lanes of a wave holding the same
-  // expert are found with one ballot per id bit; per-wave counts go through
-  // an LDS table so that a slot's position is
-  //   segment start + earlier chunks + earlier waves + earlier lanes.
   int nbits = 1;
   while ((1 << nbits) <= E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = 0; base < n; base += kAlignThreads) {
+  for (int64_t base = i0; base < i1; base += kAlignThreads) {
     const int64_t i = base + tid;
-    int32_t e = (i < n) ? ids[i] : -1;
+    int32_t e = (i < i1) ? ids[i] : -1;
     if (e < 0 || e >= E) e = -1;
     const uint32_t key = (uint32_t)(e + 1);
     uint64_t same = ~0ull;
@@ -406,7 +348,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __r
     if (e >= 0) {
       int32_t prefix = 0;
       for (int w = 0; w < wave; ++w) prefix += wcnt[w][e];
-      sorted[off[e] + running[e] + prefix + rank_w] = (int32_t)i;
+      sorted[running[e] + prefix + rank_w] = (int32_t)i;
     }
     __syncthreads();
     for (int ex = tid; ex < E; ex += kAlignThreads) {
@@ -418,14 +360,178 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __r
   }
 }
 
+// Padded segment offsets from per-expert counts (one workgroup): off[e+1] =
+// off[e] + ceil(cnt[e] / block_m) * block_m, a shuffle scan inside each wave
+// (64 experts), then the wave totals.
+__device__ void align_offsets(const int32_t* cnt, int32_t E, int32_t block_m, int32_t* off) {
+  __shared__ int32_t wsum[kMaxExperts / 64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int e = tid;
+  int32_t v = 0;
+  if (e < E) v = (cnt[e] + block_m - 1) / block_m * block_m;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  if (e < kMaxExperts && lane == 63) wsum[wave] = v;
+  __syncthreads();
+  if (e < E) {
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    off[e + 1] = before + v;
+  }
+  if (tid == 0) off[0] = 0;
+  __syncthreads();
+}
+
+// The block -> expert map (block b: rows b*block_m ..; -1 past off[E]).
+__device__ void align_block_experts(const int32_t* off, int32_t E, int32_t block_m, int32_t* __restrict__ block_expert,
+                                    int64_t nblocks) {
+  for (int64_t b = threadIdx.x; b < nblocks; b += kAlignThreads) {
+    const int64_t pos = b * block_m;
+    int32_t ex = -1;
+    if (pos < off[E]) {
+      int lo = 0, hi = E - 1;  // largest e with off[e] <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= pos) lo = mid;
+        else hi = mid - 1;
+      }
+      ex = lo;
+    }
+    block_expert[b] = ex;
+  }
+}
+
+// One workgroup for the whole sort (small routing tables).
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                              int32_t num_experts, int32_t block_m,
+                                                              int32_t* __restrict__ sorted, int64_t cap,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ block_expert,
+                                                              int64_t nblocks) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts + 1];
+  __shared__ int32_t running[kMaxExperts];
+  __shared__ int32_t wcnt[kAlignWaves][kMaxExperts];  // per-wave counts of one sub-chunk
+  const int tid = threadIdx.x;
+  const int32_t E = num_experts;
+  const int32_t sentinel = (int32_t)n;
+  for (int64_t i = tid; i < cap; i += kAlignThreads) sorted[i] = sentinel;
+  for (int e = tid; e < E; e += kAlignThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += kAlignThreads) {
+    const int32_t e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  align_offsets(cnt, E, block_m, off);
+  for (int e = tid; e <= E; e += kAlignThreads) offsets[e] = off[e];
+  for (int e = tid; e < E; e += kAlignThreads) {
+    counts[e] = cnt[e];
+    running[e] = off[e];
+  }
+  align_block_experts(off, E, block_m, block_expert, nblocks);
+  __syncthreads();
+  align_scatter_range(ids, 0, n, E, running, wcnt, sorted);
+}
+
+// Multi-workgroup sort (large routing tables), three launches:
+//   count   : workgroup g counts the experts of ids [g C, (g+1) C) -> part[g][e]
+//   scan    : one workgroup: totals, padded offsets, and part[g][e] becomes
+//             the position of chunk g's first slot of expert e (offset of e
+//             plus the counts of the chunks before g); sentinel fill, block map
+//   scatter : workgroup g places its chunk's slots from part[g][e] on
+// The result is the same stable order as the one-workgroup sort.
+constexpr int64_t kAlignChunk = 4096;
+
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                    int32_t E, int32_t* __restrict__ part) {
+  __shared__ int32_t cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t i1 = i0 + kAlignChunk < n ? i0 + kAlignChunk : n;
+  for (int e = tid; e < E; e += kAlignThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int64_t i = i0 + tid; i < i1; i += kAlignThreads) {
+    const int32_t e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) part[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(int32_t* __restrict__ part, int64_t chunks,
+                                                                   int64_t n, int32_t E, int32_t block_m,
+                                                                   int32_t* __restrict__ sorted, int64_t cap,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ block_expert,
+                                                                   int64_t nblocks) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int32_t sentinel = (int32_t)n;
+  for (int64_t i = tid; i < cap; i += kAlignThreads) sorted[i] = sentinel;
+  // per expert: running sums over the chunks (counts before chunk g)
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int32_t run = 0;
+    for (int64_t g = 0; g < chunks; ++g) {
+      const int32_t c = part[g * E + e];
+      part[g * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  align_offsets(cnt, E, block_m, off);
+  for (int e = tid; e <= E; e += kAlignThreads) offsets[e] = off[e];
+  for (int e = tid; e < E; e += kAlignThreads) {
+    counts[e] = cnt[e];
+    for (int64_t g = 0; g < chunks; ++g) part[g * E + e] += off[e];
+  }
+  align_block_experts(off, E, block_m, block_expert, nblocks);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                                      int32_t E, const int32_t* __restrict__ part,
+                                                                      int32_t* __restrict__ sorted) {
+  __shared__ int32_t running[kMaxExperts];
+  __shared__ int32_t wcnt[kAlignWaves][kMaxExperts];
+  const int64_t i0 = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t i1 = i0 + kAlignChunk < n ? i0 + kAlignChunk : n;
+  for (int e = threadIdx.x; e < E; e += kAlignThreads) running[e] = part[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  align_scatter_range(ids, i0, i1, E, running, wcnt, sorted);
+}
+
+int64_t align_workspace_bytes(int64_t t, int32_t topk, int32_t e) {
+  const int64_t n = t * topk;
+  return n > kAlignChunk ? ((n + kAlignChunk - 1) / kAlignChunk) * (int64_t)e * 4 : 0;
+}
+
 hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e, int32_t block_m,
                         int32_t* sorted, int32_t* offsets, int32_t* counts, int32_t* block_expert,
-                        int64_t nblocks, void* stream) {
+                        int64_t nblocks, void* stream, void* tmp, int64_t tmp_bytes) {
   if (e > kMaxExperts) return set_error(HUM_ERR_UNSUPPORTED, "align: at most %d experts", kMaxExperts);
   const int64_t n = t * topk;
   const int64_t cap = n + (int64_t)e * (block_m - 1);
-  align_kernel<<<1, kAlignThreads, 0, static_cast<hipStream_t>(stream)>>>(ids, n, e, block_m, sorted, cap,
-                                                                          offsets, counts, block_expert, nblocks);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t need = align_workspace_bytes(t, topk, e);
+  if (need > 0 && tmp && tmp_bytes >= need) {
+    const int64_t chunks = (n + kAlignChunk - 1) / kAlignChunk;
+    int32_t* part = static_cast<int32_t*>(tmp);
+    align_count_kernel<<<(unsigned)chunks, kAlignThreads, 0, s>>>(ids, n, e, part);
+    align_scan_kernel<<<1, kAlignThreads, 0, s>>>(part, chunks, n, e, block_m, sorted, cap, offsets, counts,
+                                                  block_expert, nblocks);
+    align_scatter_kernel<<<(unsigned)chunks, kAlignThreads, 0, s>>>(ids, n, e, part, sorted);
+  } else {
+    align_kernel<<<1, kAlignThreads, 0, s>>>(ids, n, e, block_m, sorted, cap, offsets, counts, block_expert,
+                                             nblocks);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "align launch: %s", hipGetErrorString(err));
   return HUM_OK;

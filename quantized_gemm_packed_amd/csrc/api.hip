@@ -899,7 +899,7 @@ static bool act_fused_requant(int fmt) { return fmt == HUM_ACT_MXFP8 || fmt == H
 static bool act_separate_quant(int fmt) { return fmt == HUM_ACT_FP8_TOKEN || fmt == HUM_ACT_FP8_GROUP; }
 
 struct MoeWs {
-  int64_t partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0;
+  int64_t partials = 0, sorted = 0, offsets = 0, counts = 0, bexp = 0, align_tmp = 0;
   int64_t xq = 0, xs = 0, inter = 0, inter_s = 0, interq = 0, interq_s = 0, y = 0, total = 0;
   int64_t cap = 0, nblocks = 0;
 };
@@ -929,6 +929,8 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   off = align256(off + E * 4);
   w.bexp = off;
   off = align256(off + w.nblocks * 4);
+  w.align_tmp = off;  // per-chunk expert counts of the multi-workgroup sort
+  if (!masked) off = align256(off + align_workspace_bytes(t, topk, (int32_t)E));
   w.xq = off;
   if (act != HUM_ACT_BF16) {
     const ActBytes ab = act_bytes(act, t, h);
@@ -1018,6 +1020,26 @@ hum_status hum_moe_align(const int32_t* topk_ids, int64_t t, int32_t topk, int32
   if (e > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
   // The block -> expert map the GEMMs use is internal; this export skips it.
   return launch_align(topk_ids, t, topk, e, block_m, sorted, offsets, counts, nullptr, 0, stream);
+}
+
+size_t hum_moe_align_workspace_bytes(int64_t t, int32_t topk, int32_t e) {
+  clear_error();
+  if (t < 0 || topk < 1 || e < 1) return 0;
+  return (size_t)align_workspace_bytes(t, topk, e);
+}
+
+hum_status hum_moe_align_ex(const int32_t* topk_ids, int64_t t, int32_t topk, int32_t e, int32_t block_m,
+                            int32_t* sorted, int32_t* offsets, int32_t* counts, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  clear_error();
+  if (t < 0 || topk < 1 || e < 1 || block_m < 1) return set_error(HUM_ERR_INVALID_ARG, "bad sizes");
+  if (!sorted || !offsets || !counts || (t > 0 && !topk_ids)) return set_error(HUM_ERR_INVALID_ARG, "NULL pointer");
+  if (e > 512) return set_error(HUM_ERR_UNSUPPORTED, "at most 512 experts");
+  const int64_t need = align_workspace_bytes(t, topk, e);
+  if (need > 0 && (!workspace || (int64_t)ws_bytes < need))
+    return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)need);
+  return launch_align(topk_ids, t, topk, e, block_m, sorted, offsets, counts, nullptr, 0, stream, workspace,
+                      (int64_t)ws_bytes);
 }
 
 hum_status hum_moe_reduce(const void* y_bf16, const float* topk_weights, int64_t t, int32_t topk, int64_t h,
@@ -1325,7 +1347,8 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   const int64_t E = w13->num_experts, h = w13->k;
   st = launch_align(topk_ids, t, topk, (int32_t)E, (int32_t)tile_rows(mc.up), reinterpret_cast<int32_t*>(ws + w.sorted),
                     reinterpret_cast<int32_t*>(ws + w.offsets), reinterpret_cast<int32_t*>(ws + w.counts),
-                    reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream);
+                    reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream, ws + w.align_tmp,
+                    align_workspace_bytes(t, topk, (int32_t)E));
   if (st != HUM_OK) return st;
   const int64_t slots = t * topk;
   const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16), nullptr, 0};

@@ -136,9 +136,13 @@ hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, 
 hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
                                   void* stream, const int32_t* sorted = nullptr, int32_t sentinel = 0);
 hum_status launch_zero(void* p, size_t bytes, void* stream);
+// tmp / tmp_bytes (optional, align_workspace_bytes(t, topk, e) of scratch):
+// large routing tables are sorted by many workgroups (else one).
 hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e,
                         int32_t block_m, int32_t* sorted, int32_t* offsets, int32_t* counts,
-                        int32_t* block_expert, int64_t nblocks, void* stream);
+                        int32_t* block_expert, int64_t nblocks, void* stream, void* tmp = nullptr,
+                        int64_t tmp_bytes = 0);
+int64_t align_workspace_bytes(int64_t t, int32_t topk, int32_t e);
 // block_expert[b] = the expert whose padded segment (align's offsets[E+1])
 // holds rows b*block_m.., or -1 past the last segment.
 hum_status launch_block_expert(const int32_t* offsets, int32_t e, int32_t block_m, int64_t nblocks,

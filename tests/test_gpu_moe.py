@@ -24,12 +24,17 @@ def cfg(t, split=1):
     return c
 
 
+@pytest.mark.parametrize("multi", [False, True], ids=["one-wg", "multi-wg"])
 @pytest.mark.parametrize("t,k,e,bm,zipf", [(1, 8, 128, 16, None), (37, 8, 16, 32, None), (300, 4, 64, 64, None),
-                                           (4096, 8, 128, 128, 1.1), (8192, 8, 128, 16, 1.1), (5, 3, 7, 1, None)])
-def test_align_bit_exact(t, k, e, bm, zipf):
+                                           (4096, 8, 128, 128, 1.1), (8192, 8, 128, 16, 1.1), (5, 3, 7, 1, None),
+                                           (1025, 8, 128, 64, None), (3000, 7, 512, 16, 1.1), (2049, 4, 3, 128, None)])
+def test_align_bit_exact(t, k, e, bm, zipf, multi):
+    """The stable sort bit for bit, by one workgroup and by the multi-
+    workgroup path (chunks of 4096 slots: ragged last chunk, 512 experts,
+    three experts)."""
     ids, _ = synth.routing(500 + t, t, e, k, zipf_s=zipf)
-    print(f"case align t={t} k={k} e={e} bm={bm}", flush=True)
-    srt, off, cnt = hum.moe_align(dev(ids), e, bm)
+    print(f"case align t={t} k={k} e={e} bm={bm} multi={multi}", flush=True)
+    srt, off, cnt = hum.moe_align(dev(ids), e, bm, multi_workgroup=multi)
     torch.cuda.synchronize()
     rs, ro, rc = oracle.moe.align(ids, e, bm)
     assert np.array_equal(cnt.cpu().numpy(), rc)
