@@ -1878,6 +1878,92 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
     }
     return;
   }
+  if constexpr (MS == 16 && EPI == EPI_SCATTER) {
+    // Scatter output through LDS: in the 16x16 C layout a lane holds four
+    // rows of one column, so direct stores are 2 bytes wide -- to rows
+    // scattered over the output.  Instead the tile goes out 8 rows at a
+    // time: each lane writes its bf16 values of those rows into a row-major
+    // staging area (the pipeline's first stage, free after the K loop), and
+    // every thread then stores 16 contiguous bytes of one row to its flat
+    // slot.  (Measured on the MoE down GEMM: the layer at T = 8192 took 1489
+    // us with 2-byte scatter stores, 1308 us this way.  Dense tiles, whose
+    // rows are contiguous, keep the direct stores: staging their 128-row
+    // tiles cost more in barriers than it saved.)
+    constexpr int kCols = C::kTNS * 16;           // columns of the workgroup tile
+    constexpr int kChunks = kCols / 8;            // 16-byte chunks per row
+    constexpr int kRowB = kCols * 2;
+    // rows per slice (8, or 4 where a stage is small) and the staged row
+    // pitch (padded by 16 bytes where room allows: rows 4 apart then fall
+    // on other banks)
+    constexpr int kSlice = (8 * kRowB <= C::kStage) ? 8 : 4;
+    constexpr int kPitch = kRowB + ((kSlice * (kRowB + 16) <= C::kStage) ? 16 : 0);
+    static_assert(kSlice * kPitch <= C::kStage, "staged output rows fit one pipeline stage");
+    uint8_t* ep = St::stage(0);
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const int64_t col_base = (int64_t)tn * kCols;
+    // 16-byte stores need 16-byte aligned rows; else 2-byte stores from LDS
+    const bool vec = (p.ldo % 8) == 0 && ((uintptr_t)p.out & 15) == 0;
+#pragma unroll
+    for (int pz = 0; pz < (16 / kSlice) * WM; ++pz) {
+      const int ms = pz / (16 / kSlice), h = pz % (16 / kSlice);
+      // every wave is past its reads of the stage (the last K-block's
+      // operands, or the previous slice)
+      __syncthreads();
+      if ((4 * lg) / kSlice == h) {
+        // (column scales and bias read here, after the K loop: loaded any
+        // earlier they would hold registers through it)
+        float cs[WN], bias[WN];
+#pragma unroll
+        for (int ns = 0; ns < WN; ++ns) {
+          const int64_t col = (int64_t)nts[ns] * 16 + c16;
+          const bool cv = col < p.n;
+          cs[ns] = cv ? col_scale<FMT>(wp.meta, col, gs) : 0.0f;
+          bias[ns] = (EPI == EPI_BF16 && p.bias && cv) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r8 = 4 * lg + i - kSlice * h;  // row within the slice
+          float rs = 1.0f;
+          if constexpr (FMT == F_FP8) {
+            const int64_t row = row0 + ms * 16 + 4 * lg + i;
+            rs = row < p.m ? row_act_scale<FMT, AMODE>(p, row) : 1.0f;
+          }
+#pragma unroll
+          for (int ns = 0; ns < WN; ++ns) {
+            const float x = acc[ms][ns][i] * cs[ns] * rs + bias[ns];
+            *reinterpret_cast<uint16_t*>(ep + r8 * kPitch + ((wn * WN + ns) * 16 + c16) * 2) =
+                (uint16_t)f32_to_bf16_bits(x);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int sidx = tid; sidx < kSlice * kChunks; sidx += 256) {
+        const int r8 = sidx / kChunks, ch = sidx % kChunks;
+        const int64_t row = row0 + ms * 16 + kSlice * h + r8;
+        if (row >= p.m) continue;
+        int64_t dst = row;
+        if constexpr (EPI == EPI_SCATTER) {
+          const int32_t f = p.sorted[row];
+          if (f >= p.sentinel) continue;
+          dst = f;
+        } else if constexpr (AMODE != A_DIRECT) {
+          if (p.sorted[row] >= p.sentinel) continue;  // grouped rows: padding slots are not stored
+        }
+        const int64_t col0 = col_base + ch * 8;
+        if (col0 >= p.n) continue;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r8 * kPitch + ch * 16);
+        if (vec && col0 + 8 <= p.n) {
+          *reinterpret_cast<u32x4_t*>(out + dst * p.ldo + col0) = v;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (col0 + j < p.n) out[dst * p.ldo + col0 + j] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ms = 0; ms < WM; ++ms) {
     const int64_t rb = row0 + ms * 16;
