@@ -254,7 +254,11 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
                                   : (fmt_int(fmt_of(d)) ? 2 * fmt_int_bits(fmt_of(d))
                                                         : (fmt_fp6(fmt_of(d)) ? 12 : 8));  // per k of a 16-column sub-tile
     const int64_t need = cdiv(a_bytes, w_bytes16);
-    c.wave_n = need <= 1 ? 1 : (need <= 2 ? 2 : 4);
+    // (weights of 4 bits and fewer: four sub-tiles as soon as one is not
+    // enough -- measured at M = 8, N = K = 8192: 16 us against 24 with two)
+    // At M <= 4 one sub-tile per wave keeps enough workgroups to go without
+    // split-K for every format (3- and 2-bit weights would otherwise take two)
+    c.wave_n = (need <= 1 || m <= 4) ? 1 : ((need <= 2 && w_bytes16 > 8) ? 2 : 4);
     const int64_t wgs = cdiv(nt, c.wave_n);
     Layout L;
     compute_layout(d, &L);
@@ -273,6 +277,22 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
       c = c4;
     } else {
       while (c.split_k < 64 && !fits(c)) c.split_k *= 2;
+    }
+    if (m > 8 && c.split_k > 1) {
+      // Where the decode kernel needs split-K (and its reduce launch), the
+      // 32 x 128 tile with Stream-K over 256 workgroups is faster despite
+      // its unused rows (measured at M = 16, N = K = 8192: UINT4 17.5 us
+      // against 24, MXFP4 14.3 against 22)
+      hum_tile_config t{};
+      t.kind = HUM_KERNEL_TILE;
+      t.wave_m = 2;
+      t.wave_n = 2;
+      t.waves_n = 4;
+      t.waves_k = 1;
+      t.split_k = 1;
+      t.stages = 3;
+      t.stream_k = 256;
+      if (gemm_instance_exists(dense_key(d, t))) c = t;
     }
   } else {
     c.kind = HUM_KERNEL_TILE;
@@ -340,10 +360,11 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     // Stream-K in place of split-K: 512 workgroups share the tiles'
     // K-blocks evenly and the last to finish a shared tile sums it, so no
     // reduce launch follows (measured on MI355X, W4A16 at N = K = 8192: M =
-    // 32 / 64 / 128 in 20 / 24 / 32 us against 26 / 27 / 37 with split-K)
+    // 32 / 64 / 128 in 20 / 24 / 32 us against 26 / 27 / 37 with split-K;
+    // 256 workgroups at M = 32, 512 above)
     hum_tile_config sk = c;
     sk.split_k = 1;
-    sk.stream_k = 512;
+    sk.stream_k = m <= 32 ? 256 : 512;
     const int64_t tiles = cdiv(m, tile_rows(sk)) * cdiv(nt, tile_subtiles(sk));
     if (tiles <= kSkMaxTiles && gemm_instance_exists(dense_key(d, sk))) c = sk;
   }

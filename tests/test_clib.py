@@ -111,7 +111,7 @@ def test_selector_is_deterministic_and_covers_m_range(lib):
         assert c1 == c2
         kind, wave_m, wave_n, waves_n, waves_k, split_k, block_m, stages, stream_k = c1
         assert split_k >= 1 and block_m == 16 * wave_m
-        assert kind == (1 if m <= 16 else (2 if m >= 256 else 0))   # decode, 16x16 tiles, 32x32 tiles
+        assert kind == (1 if m <= 4 else (2 if m >= 256 else 0))   # decode, 16x16 tiles, 32x32 tiles
         assert 16 * wave_m >= min(m, 32)
         seen.add(c1)
     assert len(seen) >= 3
