@@ -435,10 +435,16 @@ static void moe_fit(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   if (!fix(w13, mc.up, epi_up) || !fix(w2, mc.dn, EPI_SCATTER)) mc = MoeCfg{moe_tile_cfg(1), moe_tile_cfg(1)};
 }
 
-// Measured on MI355X (E = 128, top-8, H = 4096, I = 1024) over the mean
-// rows per expert: the decode kernel only while most experts see at most a
-// row or two (it reads each weight once, but its bf16 path is VALU heavy);
-// 16-row tiles up to ~100 rows, larger tiles beyond.
+// Measured on MI355X (E = 128, top-8, H = 4096, I = 1024, MXFP4 weights with
+// bf16 or MXFP8 activations). The tile kernels read each routed expert's
+// weights once per 16 or 32 rows on MFMA and win as soon as their grid
+// (routed experts times 256-column slabs of the gate/up GEMM) covers half the
+// CUs; below that (one token, eight experts) the decode kernel, which also
+// splits K across workgroups, is faster.  Then 16-row tiles below 8 mean rows
+// per expert, 32-row tiles to 256 and 64-row tiles beyond for bf16
+// activations over uniform routing; with FP8 activations, measured over
+// Zipf-skewed routing (the hot experts hold many times the mean), 16-row
+// tiles below 4, 32-row tiles to 96, 64-row tiles beyond.
 static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk);
 static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk, const hum_weight_desc* w2 = nullptr) {
   MoeCfg mc = select_moe_shape(w13, t, topk);
@@ -448,19 +454,18 @@ static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk, co
 
 static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   const double rows = (double)t * topk / w13->num_experts;
-  if (fmt_of(w13) == F_MXFP4_MXFP4 || fmt_of(w13) == F_FP8_BLOCK) {
-    // W4A4 and block-scaled FP8: tile kernels only (no decode-kernel path)
-    const int wm = rows <= 16 ? 1 : (rows <= 256 ? 2 : 4);
+  const int f = fmt_of(w13);
+  if (f == F_MXFP4_MXFP4 || f == F_FP8_BLOCK) {
+    // W4A4 and block-scaled FP8: tile kernels only (no decode-kernel path);
+    // measured over Zipf-skewed routing like the FP8-activation rule below,
+    // block-scaled FP8 taking 64-row tiles from 24 rows per expert
+    const int wm = rows < 4 ? 1 : (rows <= (f == F_FP8_BLOCK ? 24 : 96) ? 2 : 4);
     return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
   }
-  if (fmt_of(w13) != F_MXFP4_MXFP8 && fmt_of(w13) != F_FP8) {
-    if (rows < 0.5) return {moe_stream_cfg(), moe_stream_cfg()};
-    const int wm = rows <= 96 ? 1 : (rows <= 192 ? 2 : 4);
-    return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
-  }
-  if (rows <= 2) return {moe_stream_cfg(), moe_stream_cfg()};
-  if (rows <= 16) return {moe_stream_cfg(), moe_tile_cfg(1)};
-  const int wm = rows <= 256 ? 2 : 4;
+  const int64_t tile_wgs = std::min<int64_t>(t * topk, w13->num_experts) * cdiv(w13->n, 256);
+  if (tile_wgs < 128) return {moe_stream_cfg(), moe_stream_cfg()};
+  const bool fp8_act = f == F_MXFP4_MXFP8 || f == F_FP8;
+  const int wm = rows < (fp8_act ? 4 : 8) ? 1 : (rows <= (fp8_act ? 96 : 256) ? 2 : 4);
   return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
 }
 
@@ -693,6 +698,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   p.m = m;
   p.sorted = nullptr;
   p.block_expert = nullptr;
+  p.live_rows = nullptr;
   p.topk = 1;
   p.sentinel = 0;
   p.out = out;
@@ -1191,6 +1197,7 @@ hum_status hum_moe_grouped_gemm(const hum_weight_desc* w, const void* packed, in
   p.m = sorted_len;
   p.sorted = sorted;
   p.block_expert = bexp;
+  p.live_rows = offsets + w->num_experts;
   p.topk = topk;
   p.sentinel = (int)(num_tokens * topk);
   p.out = out;
@@ -1289,6 +1296,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   p.m = w.cap;
   p.sorted = sorted;
   p.block_expert = bexp;
+  p.live_rows = r.counts ? nullptr : reinterpret_cast<const int32_t*>(ws + w.offsets) + w13->num_experts;
   p.topk = r.topk;
   p.sentinel = r.sentinel;
   p.out = ws + w.inter;
@@ -1328,6 +1336,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   q.m = w.cap;
   q.sorted = sorted;
   q.block_expert = bexp;
+  q.live_rows = p.live_rows;
   q.topk = r.topk;
   q.sentinel = r.sentinel;
   q.out = y;

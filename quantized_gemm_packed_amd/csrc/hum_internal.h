@@ -198,6 +198,11 @@ struct GemmParams {
   // MoE
   const int32_t* sorted;
   const int32_t* block_expert;
+  // Grouped rows whose live blocks are a prefix of the block array: the
+  // padded live row count (align's offsets[E]), read by the tile kernel to
+  // spread the live tiles over all XCDs.  Null: any launched tile may be
+  // live (dense layers, the masked layout).
+  const int32_t* live_rows;
   int topk;
   int sentinel;
   int a_gather;       // rows gathered through sorted (set from the kernel key by launch_gemm)
