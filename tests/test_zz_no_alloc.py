@@ -27,9 +27,10 @@ def _noalloc(lib, d, packed, a, a_scales, out):
 
 
 CASES = [
-    # (name, weight desc args, n, k, (m1, m2)): decode kernel with split-K
-    # partials; per-token FP8 activations quantized into the scratch; INT
-    # prefill tiles with row sums (and split-K at the smaller m)
+    # (name, weight desc args, n, k, (m1, m2)): Stream-K tiles, whose tile
+    # counters live in the array's header, then the decode kernel with
+    # split-K partials; per-token FP8 activations quantized into the
+    # scratch; INT tiles with row sums, Stream-K at both sizes
     ("uint4_zp_g128_decode", ("uint4", "group", 128, "bf16"), dict(zero=True), 4096, 4096, (16, 5)),
     ("fp8_token", ("e4m3", "channel", 0, "f32"), dict(act="fp8_token"), 2048, 2048, (64, 3)),
     ("uint4_zp_g128_tile", ("uint4", "group", 128, "bf16"), dict(zero=True), 2048, 4096, (200, 33)),
