@@ -94,6 +94,26 @@ def test_moe_layer_every_tile(act, tile, t):
 
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("wm", [2, 4])
+@pytest.mark.parametrize("t,inter", [(9, 512), (300, 512), (40, 256)])
+def test_moe_layer_three_stages(act, wm, t, inter):
+    """The three-stage MoE tiles (gathered gate_up with the SwiGLU epilogue,
+    sorted down with the staged scatter), including a down GEMM of two
+    K-blocks, fewer than the stages."""
+    e, h, k = 8, 1024, 2
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(720, e, h, inter, act)
+    ids, wts = synth.routing(721 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(722 + t), (t, h))
+    c = cfg((0, wm, 4, 4, 1))
+    c.stages = 3
+    print(f"case moe three stages act={act} wm={wm} t={t} inter={inter}", flush=True)
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=c)
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, ref, f"three stages act={act} wm={wm} t={t}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("tile", [(1, 1, 4, 1, 8), (0, 2, 4, 4, 1)], ids=["stream", "tile"])
 def test_moe_split_k(act, tile):
     e, h, inter, k, t = 4, 2048, 256, 2, 3
