@@ -444,9 +444,9 @@ static void moe_fit(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
 // weights once per 16 or 32 rows on MFMA and win as soon as their grid
 // (routed experts times 256-column slabs of the gate/up GEMM) covers half the
 // CUs; below that (one token, eight experts) the decode kernel, which also
-// splits K across workgroups, is faster.  Then 16-row tiles below 8 mean rows
-// per expert, 32-row tiles to 256 and 64-row tiles beyond for bf16
-// activations over uniform routing; with FP8 activations, measured over
+// splits K across workgroups, is faster.  Then, for bf16 activations over
+// uniform routing, 16-row tiles below 8 mean rows per expert, 32 below 128,
+// 64 below 512 and 128 beyond; with FP8 activations, measured over
 // Zipf-skewed routing (the hot experts hold many times the mean), 16-row
 // tiles below 4, 32-row tiles to 96, 64-row tiles beyond.
 static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk);
@@ -469,7 +469,8 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
   const int64_t tile_wgs = std::min<int64_t>(t * topk, w13->num_experts) * cdiv(w13->n, 256);
   if (tile_wgs < 128) return {moe_stream_cfg(), moe_stream_cfg()};
   const bool fp8_act = f == F_MXFP4_MXFP8 || f == F_FP8;
-  const int wm = rows < (fp8_act ? 4 : 8) ? 1 : (rows <= (fp8_act ? 96 : 256) ? 2 : 4);
+  const int wm = fp8_act ? (rows < 4 ? 1 : (rows <= 96 ? 2 : 4))
+                         : (rows < 8 ? 1 : (rows < 128 ? 2 : (rows < 512 ? 4 : 8)));
   hum_tile_config c = moe_tile_cfg(wm);
   // W4A8 32- and 64-row tiles: three stages (the down GEMM has only 8
   // K-blocks, and a second block in flight hides more of each one's load

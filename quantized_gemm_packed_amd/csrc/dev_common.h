@@ -22,10 +22,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
 
 // float -> bf16 bits, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  // the gfx950 conversion instruction (v_cvt_pk_bf16_f32): round to nearest
+  // even, a NaN stays a (quiet) NaN
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats -> a packed bf16 pair (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float a, float b) {
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // E8M0 code -> float 2^(c-127); 255 -> NaN.  Branch free: code 0 is the

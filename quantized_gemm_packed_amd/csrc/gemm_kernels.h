@@ -1913,10 +1913,11 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
     constexpr int kCols = C::kTNS * 16;           // columns of the workgroup tile
     constexpr int kChunks = kCols / 8;            // 16-byte chunks per row
     constexpr int kRowB = kCols * 2;
-    // rows per slice (8, or 4 where a stage is small) and the staged row
-    // pitch (padded by 16 bytes where room allows: rows 4 apart then fall
-    // on other banks)
-    constexpr int kSlice = (8 * kRowB <= C::kStage) ? 8 : 4;
+    // rows per slice (a whole 16-row block where a stage holds it, so that
+    // every lane converts and writes in every slice; else 8 or 4) and the
+    // staged row pitch (padded by 16 bytes where room allows: rows 4 apart
+    // then fall on other banks)
+    constexpr int kSlice = (16 * kRowB <= C::kStage) ? 16 : ((8 * kRowB <= C::kStage) ? 8 : 4);
     constexpr int kPitch = kRowB + ((kSlice * (kRowB + 16) <= C::kStage) ? 16 : 0);
     static_assert(kSlice * kPitch <= C::kStage, "staged output rows fit one pipeline stage");
     uint8_t* ep = St::stage(0);
@@ -1924,53 +1925,81 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
     const int64_t col_base = (int64_t)tn * kCols;
     // 16-byte stores need 16-byte aligned rows; else 2-byte stores from LDS
     const bool vec = (p.ldo % 8) == 0 && ((uintptr_t)p.out & 15) == 0;
+    // The flat slots of the rows this thread stores, every slice's loaded at
+    // once and only compared at their use: one memory latency for the
+    // epilogue rather than one per slice (each slice ends in a barrier, so
+    // loads issued inside it would wait in turn).  Rows past m load row0's
+    // slot (the block is live, so row0 < m) and are skipped by `in`.
+    constexpr int kSlices = (16 / kSlice) * WM;
+    constexpr int kPer = (kSlice * kChunks + 255) / 256;
+    int32_t slot[kSlices][kPer];
+    bool in[kSlices][kPer];
 #pragma unroll
-    for (int pz = 0; pz < (16 / kSlice) * WM; ++pz) {
+    for (int pz = 0; pz < kSlices; ++pz) {
+      const int ms = pz / (16 / kSlice), h = pz % (16 / kSlice);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int sidx = tid + 256 * q;
+        const int64_t row = row0 + ms * 16 + kSlice * h + sidx / kChunks;
+        in[pz][q] = sidx < kSlice * kChunks && row < p.m;
+        slot[pz][q] = p.sorted[in[pz][q] ? row : row0];
+      }
+    }
+    // column scales (read after the K loop: loaded any earlier they would
+    // hold registers through it)
+    float cs[WN];
+#pragma unroll
+    for (int ns = 0; ns < WN; ++ns) {
+      const int64_t col = (int64_t)nts[ns] * 16 + c16;
+      cs[ns] = col < p.n ? col_scale<FMT>(wp.meta, col, gs) : 0.0f;
+    }
+    // a barrier for the staging area alone: this wave's LDS accesses done,
+    // its stores to the output left in flight
+    auto lds_barrier = [&]() -> void {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    };
+#pragma unroll
+    for (int pz = 0; pz < kSlices; ++pz) {
       const int ms = pz / (16 / kSlice), h = pz % (16 / kSlice);
       // every wave is past its reads of the stage (the last K-block's
-      // operands, or the previous slice)
-      __syncthreads();
+      // operands, or the previous slice).  The first time with a full wait:
+      // the pipeline's trailing copies (and the slot loads) land first.
+      if (pz == 0)
+        __syncthreads();
+      else
+        lds_barrier();
       if ((4 * lg) / kSlice == h) {
-        // (column scales and bias read here, after the K loop: loaded any
-        // earlier they would hold registers through it)
-        float cs[WN], bias[WN];
+        // rows in pairs: one conversion instruction per two values
 #pragma unroll
-        for (int ns = 0; ns < WN; ++ns) {
-          const int64_t col = (int64_t)nts[ns] * 16 + c16;
-          const bool cv = col < p.n;
-          cs[ns] = cv ? col_scale<FMT>(wp.meta, col, gs) : 0.0f;
-          bias[ns] = (EPI == EPI_BF16 && p.bias && cv) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; i += 2) {
           const int r8 = 4 * lg + i - kSlice * h;  // row within the slice
-          float rs = 1.0f;
+          float rs0 = 1.0f, rs1 = 1.0f;
           if constexpr (FMT == F_FP8) {
             const int64_t row = row0 + ms * 16 + 4 * lg + i;
-            rs = row < p.m ? row_act_scale<FMT, AMODE>(p, row) : 1.0f;
+            rs0 = row < p.m ? row_act_scale<FMT, AMODE>(p, row) : 1.0f;
+            rs1 = row + 1 < p.m ? row_act_scale<FMT, AMODE>(p, row + 1) : 1.0f;
           }
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
-            const float x = acc[ms][ns][i] * cs[ns] * rs + bias[ns];
-            *reinterpret_cast<uint16_t*>(ep + r8 * kPitch + ((wn * WN + ns) * 16 + c16) * 2) =
-                (uint16_t)f32_to_bf16_bits(x);
+            const uint32_t pr = f32x2_to_bf16x2_bits(acc[ms][ns][i] * cs[ns] * rs0, acc[ms][ns][i + 1] * cs[ns] * rs1);
+            uint8_t* e0 = ep + r8 * kPitch + ((wn * WN + ns) * 16 + c16) * 2;
+            *reinterpret_cast<uint16_t*>(e0) = (uint16_t)pr;
+            *reinterpret_cast<uint16_t*>(e0 + kPitch) = (uint16_t)(pr >> 16);
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
-      for (int sidx = tid; sidx < kSlice * kChunks; sidx += 256) {
+      for (int q = 0; q < kPer; ++q) {
+        const int sidx = tid + 256 * q;
+        if (!in[pz][q] || slot[pz][q] >= p.sentinel) continue;
         const int r8 = sidx / kChunks, ch = sidx % kChunks;
-        const int64_t row = row0 + ms * 16 + kSlice * h + r8;
-        if (row >= p.m) continue;
-        int64_t dst = row;
-        if constexpr (EPI == EPI_SCATTER) {
-          const int32_t f = p.sorted[row];
-          if (f >= p.sentinel) continue;
-          dst = f;
-        } else if constexpr (AMODE != A_DIRECT) {
-          if (p.sorted[row] >= p.sentinel) continue;  // grouped rows: padding slots are not stored
-        }
+        const int64_t dst = slot[pz][q];
         const int64_t col0 = col_base + ch * 8;
         if (col0 >= p.n) continue;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + r8 * kPitch + ch * 16);
