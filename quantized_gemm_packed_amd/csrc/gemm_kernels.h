@@ -460,7 +460,12 @@ __device__ __forceinline__ f32x4_t mfma_f8_kblock(const i32x8_t& a8, int sa, con
 // ---------------------------------------------------------------------------
 // Epilogue pieces
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) and the reciprocal on
+// the hardware's 2^x and 1/x instructions (about one ulp each; 1/1 is exact,
+// so silu(g) = g wherever e^-g is below half an ulp of 1, g > 16.7)
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
 
 // Per-token FP8 row scale of a gathered row (the scale of the token its
 // sorted slot reads; 1 for padding slots, which are never stored).
