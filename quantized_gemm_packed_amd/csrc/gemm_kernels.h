@@ -1911,17 +1911,18 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
     }
     return;
   }
-  if constexpr (MS == 16 && EPI == EPI_SCATTER) {
-    // Scatter output through LDS: in the 16x16 C layout a lane holds four
-    // rows of one column, so direct stores are 2 bytes wide -- to rows
-    // scattered over the output.  Instead the tile goes out 8 rows at a
-    // time: each lane writes its bf16 values of those rows into a row-major
-    // staging area (the pipeline's first stage, free after the K loop), and
-    // every thread then stores 16 contiguous bytes of one row to its flat
-    // slot.  (Measured on the MoE down GEMM: the layer at T = 8192 took 1489
-    // us with 2-byte scatter stores, 1308 us this way.  Dense tiles, whose
-    // rows are contiguous, keep the direct stores: staging their 128-row
-    // tiles cost more in barriers than it saved.)
+  if constexpr (MS == 16 && (EPI == EPI_SCATTER || (EPI == EPI_BF16 && AMODE == A_DIRECT))) {
+    // Output through LDS: in the 16x16 C layout a lane holds four rows of
+    // one column, so direct stores are 2 bytes wide (and, for the MoE down
+    // GEMM, to rows scattered over the output).  Instead the tile goes out
+    // in slices of rows: each lane writes its bf16 values of those rows into
+    // a row-major staging area (the pipeline's first stage, free after the K
+    // loop), and every thread then stores 16 contiguous bytes of one row to
+    // its output row (its flat slot for the scatter).  Measured on MI355X:
+    // the MoE W4A8 layer at T = 8192 went from 1489 to 1308 us with 8-row
+    // slices, then to about 1120 with the slots loaded up front, 16-row
+    // slices and LDS-only barriers; dense FP8 W8A8 at M = 4096, N = 7168, K =
+    // 2048 from 98 to 88 us.
     constexpr int kCols = C::kTNS * 16;           // columns of the workgroup tile
     constexpr int kChunks = kCols / 8;            // 16-byte chunks per row
     constexpr int kRowB = kCols * 2;
@@ -1954,16 +1955,21 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
         const int sidx = tid + 256 * q;
         const int64_t row = row0 + ms * 16 + kSlice * h + sidx / kChunks;
         in[pz][q] = sidx < kSlice * kChunks && row < p.m;
-        slot[pz][q] = p.sorted[in[pz][q] ? row : row0];
+        if constexpr (EPI == EPI_SCATTER)
+          slot[pz][q] = p.sorted[in[pz][q] ? row : row0];
+        else
+          slot[pz][q] = (int32_t)row;  // dense rows: the output row itself
       }
     }
     // column scales (read after the K loop: loaded any earlier they would
     // hold registers through it)
-    float cs[WN];
+    float cs[WN], bias[WN];
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns) {
       const int64_t col = (int64_t)nts[ns] * 16 + c16;
-      cs[ns] = col < p.n ? col_scale<FMT>(wp.meta, col, gs) : 0.0f;
+      const bool cv = col < p.n;
+      cs[ns] = cv ? col_scale<FMT>(wp.meta, col, gs) : 0.0f;
+      bias[ns] = (EPI == EPI_BF16 && p.bias && cv) ? bf16_bits_to_f32(p.bias[col]) : 0.0f;
     }
     // a barrier for the staging area alone: this wave's LDS accesses done,
     // its stores to the output left in flight
@@ -1998,7 +2004,8 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
           }
 #pragma unroll
           for (int ns = 0; ns < WN; ++ns) {
-            const uint32_t pr = f32x2_to_bf16x2_bits(acc[ms][ns][i] * cs[ns] * rs0, acc[ms][ns][i + 1] * cs[ns] * rs1);
+            const uint32_t pr = f32x2_to_bf16x2_bits(acc[ms][ns][i] * cs[ns] * rs0 + bias[ns],
+                                                     acc[ms][ns][i + 1] * cs[ns] * rs1 + bias[ns]);
             uint8_t* e0 = ep + r8 * kPitch + ((wn * WN + ns) * 16 + c16) * 2;
             *reinterpret_cast<uint16_t*>(e0) = (uint16_t)pr;
             *reinterpret_cast<uint16_t*>(e0 + kPitch) = (uint16_t)(pr >> 16);
@@ -2009,7 +2016,7 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int sidx = tid + 256 * q;
-        if (!in[pz][q] || slot[pz][q] >= p.sentinel) continue;
+        if (!in[pz][q] || (EPI == EPI_SCATTER && slot[pz][q] >= p.sentinel)) continue;
         const int r8 = sidx / kChunks, ch = sidx % kChunks;
         const int64_t dst = slot[pz][q];
         const int64_t col0 = col_base + ch * 8;
