@@ -1312,6 +1312,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   p.sorted = sorted;
   p.block_expert = bexp;
   p.live_rows = r.counts ? nullptr : reinterpret_cast<const int32_t*>(ws + w.offsets) + w13->num_experts;
+  p.group_m = 1;  // N fastest over each expert block (groups of 8 blocks, M fastest, measured 0-10% slower)
   p.topk = r.topk;
   p.sentinel = r.sentinel;
   p.out = ws + w.inter;
@@ -1352,6 +1353,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   q.sorted = sorted;
   q.block_expert = bexp;
   q.live_rows = p.live_rows;
+  q.group_m = p.group_m;
   q.topk = r.topk;
   q.sentinel = r.sentinel;
   q.out = y;

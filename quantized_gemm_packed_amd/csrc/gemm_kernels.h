@@ -1226,7 +1226,7 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
   // Within it, tiles go in groups of group_m M-tiles by all N-tiles, M
   // fastest: the workgroups one XCD runs at a time then share both their
   // activation rows and their weight columns through that XCD's L2.  (MoE
-  // M-tiles belong to different experts and take group_m = 1.)
+  // launches take group_m = 1: N fastest over each expert block.)
   // Grouped rows with a live prefix: only the first `live` work items hold
   // rows, and a plain contiguous split would leave them on the first XCDs
   // (at 29 live expert blocks of 128 launched, two XCDs of eight), so each
@@ -1237,21 +1237,23 @@ __global__ __launch_bounds__(256, tile_min_waves(FMT, WM, WN, AMODE, EPI, S, MS,
   // XCDs, each then fetching the block's rows, and ran 1.3-1.6x slower.)
   const uint32_t nwg = gridDim.x;
   uint32_t bid = blockIdx.x;
-  if (nwg % 8 == 0) {
-    uint32_t live = nwg;
-    if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {
-      if (p.live_rows) {
-        const int64_t rows = *p.live_rows;
-        const int64_t items = (rows > 0 ? (rows + C::kTM - 1) / C::kTM : 0) * p.n_tiles * p.split_k;
-        live = items < (int64_t)nwg ? (uint32_t)items : nwg;
-      }
+  uint32_t m_tiles = SK ? (uint32_t)p.sk_m_tiles : nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
+  uint32_t live = nwg;
+  if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {
+    if (p.live_rows) {
+      // the live M-tiles are the tile grid (groups of group_m over them)
+      const int64_t rows = *p.live_rows;
+      const int64_t lm = rows > 0 ? (rows + C::kTM - 1) / C::kTM : 0;
+      if (lm < (int64_t)m_tiles) m_tiles = (uint32_t)lm;
+      live = m_tiles * (uint32_t)p.n_tiles * (uint32_t)p.split_k;
     }
+  }
+  if (nwg % 8 == 0) {
     const uint32_t per = (live + 7) / 8, local = bid / 8;
     if (local >= per) return;
     bid = (bid % 8) * per + local;
-    if (bid >= live) return;
   }
-  const uint32_t m_tiles = SK ? (uint32_t)p.sk_m_tiles : nwg / ((uint32_t)p.split_k * (uint32_t)p.n_tiles);
+  if (bid >= live) return;
   // tile index -> (M-tile, N-tile)
   auto tile_coords = [&](uint32_t t, int64_t& tm, int& tn) {
     const uint32_t per_group = (uint32_t)p.group_m * (uint32_t)p.n_tiles;
