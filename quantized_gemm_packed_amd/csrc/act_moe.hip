@@ -439,6 +439,84 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const int32_t* __r
   align_scatter_range(ids, 0, n, E, running, wcnt, sorted);
 }
 
+// One wave for routing tables of at most 64 slots (decode batches): lane f
+// holds slot f.  The lanes of one expert find each other with one ballot per
+// id bit; a slot's place in its expert's segment is the number of earlier
+// lanes of that expert (the stable order), and the expert's first lane (its
+// leader) owns the rest of the segment: its padding and its blocks of the
+// block -> expert map.  Every sorted entry and map entry is written exactly
+// once, so no store needs ordering against another.
+constexpr int kAlignSmall = 64;
+
+__global__ __launch_bounds__(64) void align_small_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                         int32_t num_experts, int32_t block_m,
+                                                         int32_t* __restrict__ sorted, int64_t cap,
+                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ block_expert, int64_t nblocks) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int32_t E = num_experts;
+  const int32_t sentinel = (int32_t)n;
+  int32_t e = lane < n ? ids[lane] : -1;
+  if (e < 0 || e >= E) e = -1;
+  for (int x = lane; x < E; x += 64) cnt[x] = 0;
+  int nbits = 1;
+  while ((1 << nbits) <= E) ++nbits;
+  const uint32_t key = (uint32_t)(e + 1);
+  uint64_t same = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & lt_mask);
+  const int c = __popcll(same);
+  const bool leader = e >= 0 && rank == 0;
+  __syncthreads();
+  if (leader) cnt[e] = c;
+  __syncthreads();
+  // padded offsets: lane l scans experts [l * per, (l + 1) * per)
+  const int per = (E + 63) / 64;
+  int32_t s = 0;
+  for (int i = 0; i < per; ++i) {
+    const int x = lane * per + i;
+    if (x < E) s += (cnt[x] + block_m - 1) / block_m * block_m;
+  }
+  int32_t inc = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t u = __shfl_up(inc, d);
+    if (lane >= d) inc += u;
+  }
+  const int32_t total = __shfl(inc, 63);
+  int32_t run = inc - s;
+  for (int i = 0; i < per; ++i) {
+    const int x = lane * per + i;
+    if (x < E) {
+      off[x] = run;
+      offsets[x] = run;
+      counts[x] = cnt[x];
+      run += (cnt[x] + block_m - 1) / block_m * block_m;
+    }
+  }
+  if (lane == 0) offsets[E] = total;
+  __syncthreads();
+  if (e >= 0) sorted[off[e] + rank] = lane;
+  if (leader) {
+    const int32_t o = off[e];
+    const int32_t psz = (c + block_m - 1) / block_m * block_m;
+    for (int32_t r = c; r < psz; ++r) sorted[o + r] = sentinel;
+    if (block_expert)
+      for (int32_t q = 0; q < psz / block_m; ++q)
+        if (o / block_m + q < nblocks) block_expert[o / block_m + q] = e;
+  }
+  for (int64_t i = total + lane; i < cap; i += 64) sorted[i] = sentinel;
+  if (block_expert)
+    for (int64_t b = total / block_m + lane; b < nblocks; b += 64) block_expert[b] = -1;
+}
+
 // Multi-workgroup sort (large routing tables), three launches:
 //   count   : workgroup g counts the experts of ids [g C, (g+1) C) -> part[g][e]
 //   scan    : one workgroup: totals, padded offsets, and part[g][e] becomes
@@ -528,6 +606,8 @@ hum_status launch_align(const int32_t* ids, int64_t t, int32_t topk, int32_t e, 
     align_scan_kernel<<<1, kAlignThreads, 0, s>>>(part, chunks, n, e, block_m, sorted, cap, offsets, counts,
                                                   block_expert, nblocks);
     align_scatter_kernel<<<(unsigned)chunks, kAlignThreads, 0, s>>>(ids, n, e, part, sorted);
+  } else if (n <= kAlignSmall) {
+    align_small_kernel<<<1, 64, 0, s>>>(ids, n, e, block_m, sorted, cap, offsets, counts, block_expert, nblocks);
   } else {
     align_kernel<<<1, kAlignThreads, 0, s>>>(ids, n, e, block_m, sorted, cap, offsets, counts, block_expert,
                                              nblocks);
@@ -551,19 +631,31 @@ __global__ __launch_bounds__(256) void moe_reduce_kernel(const uint16_t* __restr
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < topk; ++j) {
-    // a slot routed outside [0, E) (an expert held elsewhere) was never
-    // computed: it contributes nothing
-    if (ids) {
-      const int32_t e = ids[t * topk + j];
-      if (e < 0 || e >= num_experts) continue;
-    }
-    const float wj = w[t * topk + j];
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + (t * topk + j) * h + c8 * 8);
+  // Slots in chunks of 8: every load of a chunk (ids, weights, y rows) is
+  // issued before any is used, so a chunk costs one memory latency, not one
+  // per slot.  The y row of every existing slot is in bounds; a slot routed
+  // outside [0, E) (an expert held elsewhere) was never computed and its
+  // stale row is skipped, not multiplied by zero.
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    int32_t e[8];
+    float wj[8];
+    u32x4_t v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += wj * bf16_bits_to_f32(v[i] & 0xFFFF);
-      acc[2 * i + 1] += wj * bf16_bits_to_f32(v[i] >> 16);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj < topk ? j0 + jj : topk - 1;
+      const int64_t f = t * topk + j;
+      e[jj] = ids ? ids[f] : 0;
+      wj[jj] = w[f];
+      v[jj] = *reinterpret_cast<const u32x4_t*>(y + f * h + c8 * 8);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj >= topk || (ids && (e[jj] < 0 || e[jj] >= num_experts))) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wj[jj] * bf16_bits_to_f32(v[jj][i] & 0xFFFF);
+        acc[2 * i + 1] += wj[jj] * bf16_bits_to_f32(v[jj][i] >> 16);
+      }
     }
   }
   u32x4_t o;

@@ -467,6 +467,17 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
     return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
   }
   const int64_t tile_wgs = std::min<int64_t>(t * topk, w13->num_experts) * cdiv(w13->n, 256);
+  // MXFP4 experts with bf16 activations at one token, or with MXFP8
+  // activations up to 64 routed slots (Zipf-skewed routing): gate_up on the
+  // decode kernel with four K-waves per workgroup (eight waves of one or two
+  // K-blocks each spent more time in their fixed costs than in their loads),
+  // down on the 16-row tile kernel.  Measured per GEMM at T = 1 (bf16):
+  // gate_up 15.2 -> 12.9 us, down 17.2 -> 10.3 us.
+  if ((f == F_MXFP4_BF16 && tile_wgs < 128) || (f == F_MXFP4_MXFP8 && t * topk <= 64)) {
+    hum_tile_config up = moe_stream_cfg();
+    up.waves_k = 4;
+    return {up, moe_tile_cfg(1)};
+  }
   if (tile_wgs < 128) return {moe_stream_cfg(), moe_stream_cfg()};
   const bool fp8_act = f == F_MXFP4_MXFP8 || f == F_FP8;
   const int wm = fp8_act ? (rows < 4 ? 1 : (rows <= 96 ? 2 : 4))

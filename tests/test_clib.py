@@ -176,10 +176,11 @@ def test_moe_batch_invariant_selection(lib):
     kinds = set()
     for t in (0, 1, 16, 64, 1024, 8192):
         kinds.add(hum.moe_select_config(w13, w2, t, 8).kind)
+        kinds.add(hum.moe_select_config(w13, w2, t, 8, gate_up=True).kind)
         c = hum.moe_select_config(w13, w2, t, 8, batch_invariant=True)
         assert c.kind == hum.KERNEL_TILE and c.split_k == 1, (t, c)
         assert hum.moe_workspace_bytes(w13, w2, max(t, 1), 8, c) > 0
-    assert hum.KERNEL_STREAM in kinds    # the default does use the decode kernel
+    assert hum.KERNEL_STREAM in kinds    # the default does use the decode kernel (gate_up at decode sizes)
 
 
 def test_workspace_sizes(lib):

@@ -27,11 +27,15 @@ def cfg(t, split=1):
 @pytest.mark.parametrize("multi", [False, True], ids=["one-wg", "multi-wg"])
 @pytest.mark.parametrize("t,k,e,bm,zipf", [(1, 8, 128, 16, None), (37, 8, 16, 32, None), (300, 4, 64, 64, None),
                                            (4096, 8, 128, 128, 1.1), (8192, 8, 128, 16, 1.1), (5, 3, 7, 1, None),
-                                           (1025, 8, 128, 64, None), (3000, 7, 512, 16, 1.1), (2049, 4, 3, 128, None)])
+                                           (1025, 8, 128, 64, None), (3000, 7, 512, 16, 1.1), (2049, 4, 3, 128, None),
+                                           (8, 8, 128, 16, None), (21, 3, 512, 128, None), (2, 8, 3, 32, None),
+                                           (13, 5, 16, 16, None)])
 def test_align_bit_exact(t, k, e, bm, zipf, multi):
     """The stable sort bit for bit, by one workgroup and by the multi-
     workgroup path (chunks of 4096 slots: ragged last chunk, 512 experts,
-    three experts)."""
+    three experts); tables of at most 64 slots take the one-wave sort (64
+    slots exactly, 512 experts with 128-row blocks, three experts; 65 slots
+    is the first table past it)."""
     ids, _ = synth.routing(500 + t, t, e, k, zipf_s=zipf)
     print(f"case align t={t} k={k} e={e} bm={bm} multi={multi}", flush=True)
     srt, off, cnt = hum.moe_align(dev(ids), e, bm, multi_workgroup=multi)
@@ -303,10 +307,12 @@ def test_moe_masked_edges():
 
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
-def test_moe_invalid_expert_ids_contribute_nothing(act):
+@pytest.mark.parametrize("t", [40, 13])
+def test_moe_invalid_expert_ids_contribute_nothing(act, t):
     """Slots routed to an id outside [0, E) (-1: an expert held elsewhere, or
-    E itself) add nothing: the same as a valid id with weight 0."""
-    e, h, inter, k, t = 8, 256, 128, 3, 40
+    E itself) add nothing: the same as a valid id with weight 0 (13 tokens x
+    top-3: the one-wave sort)."""
+    e, h, inter, k = 8, 256, 128, 3
     w13, w2, d13, o13, d2, o2, p13, p2 = _layer(760, e, h, inter, act)
     ids, wts = synth.routing(761, t, e, k)
     bad = np.zeros_like(ids, dtype=bool)
