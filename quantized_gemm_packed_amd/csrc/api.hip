@@ -1267,6 +1267,10 @@ struct MoeRows {
   int32_t stream_rows;    // upper bound of the valid rows of one expert block
   const int32_t* counts;  // grouped_masked: live rows per expert buffer (else NULL)
   int64_t max_m;          // grouped_masked: rows per expert buffer
+  // indexed layout at decode sizes: the gate_up decode kernel routes the
+  // slots itself (no align launch) and writes the arrays the down GEMM reads
+  const int32_t* route_ids = nullptr;
+  int32_t route_e = 0;
 };
 
 // gate_up (+ SwiGLU, + requantization) into the workspace, then down with
@@ -1338,6 +1342,14 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const ActBytes xb = act_bytes(act, t, h);
   p.a_bytes = xb.codes;
   p.a_scale_bytes = xb.scales;
+  if (r.route_ids) {
+    p.route_ids = r.route_ids;
+    p.route_n = r.sentinel;
+    p.route_e = r.route_e;
+    p.route_sorted = sorted;
+    p.route_bexp = bexp;
+    p.route_live = reinterpret_cast<int32_t*>(ws + w.offsets) + w13->num_experts;
+  }
   st = launch_gemm(kup, p, m_tiles, bm, stream);
   if (st != HUM_OK) return st;
   // FP8 per token / per group: quantize the live rows of the intermediate
@@ -1403,13 +1415,26 @@ hum_status hum_moe_gemm_ex(const hum_weight_desc* w13, const void* packed_w13, c
   log_cfg("moe down", mc.dn, t);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t E = w13->num_experts, h = w13->k;
-  st = launch_align(topk_ids, t, topk, (int32_t)E, (int32_t)tile_rows(mc.up), reinterpret_cast<int32_t*>(ws + w.sorted),
-                    reinterpret_cast<int32_t*>(ws + w.offsets), reinterpret_cast<int32_t*>(ws + w.counts),
-                    reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream, ws + w.align_tmp,
-                    align_workspace_bytes(t, topk, (int32_t)E));
-  if (st != HUM_OK) return st;
   const int64_t slots = t * topk;
-  const MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16), nullptr, 0};
+  // At most 64 routed slots with a single-pass gate_up decode kernel (16-row
+  // blocks, no split-K on either GEMM, no separate requantization of the
+  // intermediate): the gate_up kernel routes them itself, in the align's
+  // order, and leaves the rows of every launched block for the down GEMM,
+  // which saves the align launch.
+  const bool route = slots <= 64 && mc.up.kind == HUM_KERNEL_STREAM && tile_rows(mc.up) == 16 &&
+                     mc.up.split_k == 1 && mc.dn.split_k == 1 && !act_separate_quant(w13->act_fmt);
+  if (!route) {
+    st = launch_align(topk_ids, t, topk, (int32_t)E, (int32_t)tile_rows(mc.up), reinterpret_cast<int32_t*>(ws + w.sorted),
+                      reinterpret_cast<int32_t*>(ws + w.offsets), reinterpret_cast<int32_t*>(ws + w.counts),
+                      reinterpret_cast<int32_t*>(ws + w.bexp), w.nblocks, stream, ws + w.align_tmp,
+                      align_workspace_bytes(t, topk, (int32_t)E));
+    if (st != HUM_OK) return st;
+  }
+  MoeRows rows{t, topk, (int32_t)slots, (int32_t)(slots < 16 ? slots : 16), nullptr, 0};
+  if (route) {
+    rows.route_ids = topk_ids;
+    rows.route_e = (int32_t)E;
+  }
   st = moe_gemms(w13, packed_w13, w2, packed_w2, mc, kup, kdn, w, ws, rows, x_bf16, ws + w.y, stream);
   if (st != HUM_OK) return st;
   return launch_moe_reduce(ws + w.y, topk_weights, t, topk, h, out_bf16, stream, topk_ids, (int32_t)E);

@@ -667,6 +667,52 @@ constexpr int stream_waves(int fmt, int kw, int amode, int epi) {
   return kw + (stream_self_staged(fmt, amode, epi) ? 0 : 1);
 }
 
+// Decode-size routing of one 16-row expert block, run by each wave on its
+// own (no barrier, no LDS): lane f holds flat slot f < route_n <= 64.  The
+// lanes of one expert find each other with one ballot per id bit; a slot's
+// position is its expert's padded segment start (the padded sizes of the
+// smaller experts present) plus the number of earlier lanes of that expert,
+// which is the align's stable order.  Returns the block's expert (-1: past
+// the live blocks); lane r < 16 gets the slot of block row r (-1: padding);
+// total = the padded live row count.  Slots routed outside [0, route_e) take
+// no row, as in the align.
+__device__ __forceinline__ int route_block(const GemmParams& p, int tm, int lane, int& slot, int& total) {
+  const int n = p.route_n;
+  int e = lane < n ? p.route_ids[lane] : -1;
+  if (e < 0 || e >= p.route_e) e = -1;
+  int nbits = 1;
+  while ((1 << nbits) <= p.route_e) ++nbits;
+  const uint32_t key = (uint32_t)(e + 1);
+  uint64_t same = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(same & lt_mask);
+  const int psz = e >= 0 ? (__popcll(same) + 15) / 16 * 16 : 0;
+  const int lead = (e >= 0 && rank == 0) ? psz : 0;  // an expert's padded size, on its first lane
+  int off = 0, tot = 0;
+  for (int j = 0; j < n; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    const int pj = __builtin_amdgcn_readlane(lead, j);
+    off += ej < e ? pj : 0;
+    tot += pj;
+  }
+  total = tot;
+  const int base = tm * 16;
+  const int pos = off + rank;
+  const uint64_t own = __ballot(e >= 0 && off <= base && base < off + psz);
+  const int expert = own ? __builtin_amdgcn_readlane(e, (int)__builtin_ctzll(own)) : -1;
+  slot = -1;
+  for (int r = 0; r < 16; ++r) {
+    const uint64_t hit = __ballot(e >= 0 && pos == base + r);
+    if (lane == r && hit) slot = (int)__builtin_ctzll(hit);
+  }
+  return expert;
+}
+
 template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
 __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
   using T = Tr<FMT>;
@@ -689,8 +735,21 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   const int split = (int)blockIdx.z;
 
   int expert = 0;
+  int route_slot = -1;  // routing inside the kernel: the slot of tile row `lane` (lanes < 16)
   if constexpr (AMODE != A_DIRECT || EPI == EPI_SCATTER) {  // grouped rows: the block's expert (-1: all padding)
-    expert = p.block_expert[tm];
+    if (AMODE == A_GATHER && p.route_ids) {
+      int total = 0;
+      expert = route_block(p, tm, lane, route_slot, total);
+      // the routing of every launched block, for the GEMM after this one
+      if (tn == 0 && split == 0 && wave == 0) {
+        if (lane < 16 && (int64_t)tm * 16 + lane < p.m)
+          p.route_sorted[tm * 16 + lane] = route_slot >= 0 ? route_slot : p.sentinel;
+        if (lane == 0) p.route_bexp[tm] = expert;
+        if (lane == 0 && tm == 0) *p.route_live = total;
+      }
+    } else {
+      expert = p.block_expert[tm];
+    }
     if (expert < 0) return;
   }
   const int64_t row0 = tm * 16;
@@ -754,8 +813,12 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     if (lane < 16) {
       const int64_t row = row0 + lane;
       if (AMODE == A_GATHER) {
-        const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
-        if (f < p.sentinel) src = f / p.topk;
+        if (p.route_ids) {
+          if (route_slot >= 0) src = route_slot / p.topk;
+        } else {
+          const int32_t f = row < p.m ? p.sorted[row] : p.sentinel;
+          if (f < p.sentinel) src = f / p.topk;
+        }
       } else if (row < p.m) {
         // grouped rows in sorted order: padding slots (sentinel) are skipped
         src = (p.sorted && p.sorted[row] >= p.sentinel) ? -1 : (int)row;

@@ -206,6 +206,17 @@ struct GemmParams {
   int topk;
   int sentinel;
   int a_gather;       // rows gathered through sorted (set from the kernel key by launch_gemm)
+  // Decode-size routing inside the gathered decode kernel (no align launch):
+  // route_n <= 64 flat slots of route_ids over route_e experts; each
+  // workgroup finds its 16-row block's expert and rows itself, in align's
+  // order, and the workgroups of the first N-tile write the blocks' sorted
+  // rows (sentinel padding), block -> expert entries and the padded live
+  // row count for the GEMM after it.  Null route_ids: the align's arrays.
+  const int32_t* route_ids;
+  int route_n, route_e;
+  int32_t* route_sorted;
+  int32_t* route_bexp;
+  int32_t* route_live;
   // outputs
   void* out;
   int64_t ldo;        // elements

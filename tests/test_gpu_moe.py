@@ -348,3 +348,37 @@ def test_moe_wide_hidden_decode(act, t):
     torch.cuda.synchronize()
     ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
     assert_tol(out, ref, f"wide act={act} t={t}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("t,k,e", [(1, 8, 128), (7, 8, 128), (4, 16, 40), (5, 3, 7), (21, 3, 16), (2, 8, 512)])
+def test_moe_decode_routing_matches_align(act, t, k, e):
+    """At most 64 routed slots: the gate_up decode kernel routes the slots
+    itself (no align launch) and leaves the sorted rows, block map and live
+    row count for the down GEMM.  The layer must equal, bit for bit, the same
+    kernels run stage by stage after the align."""
+    h, inter = 512, 256
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(780 + t, e, h, inter, act)
+    ids, wts = synth.routing(781 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(782 + t), (t, h))
+    up = hum.moe_select_config(d13, d2, t, k, gate_up=True)
+    dn = hum.moe_select_config(d13, d2, t, k)
+    assert up.kind == hum.KERNEL_STREAM and up.block_m == 16 and dn.block_m == 16, (up, dn)
+    print(f"case moe routing act={act} t={t} k={k} e={e}", flush=True)
+    x, di, dw = dev(xb), dev(ids), dev(wts)
+    out = hum.moe_gemm(d13, p13, d2, p2, x, di, dw)
+    srt, off, _ = hum.moe_align(di, e, 16)
+    if act == "bf16":
+        a, a_s, epi = x, None, "swiglu_bf16"
+    else:
+        a, a_s = hum.quant_act("mxfp8", x)
+        epi = "swiglu_mxfp8"
+    mid = hum.moe_grouped_gemm(d13, p13, a, srt, off, 16, t, k, a_mode="gather", epilogue=epi, a_scales=a_s, cfg=up)
+    ia, ia_s = (mid, None) if act == "bf16" else mid
+    y = hum.moe_grouped_gemm(d2, p2, ia, srt, off, 16, t, k, a_mode="sorted", epilogue="scatter", a_scales=ia_s,
+                             cfg=dn)
+    ref = hum.moe_reduce(y, dw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    o = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
+    assert_tol(out, o, f"routing act={act} t={t}")
