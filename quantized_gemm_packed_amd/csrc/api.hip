@@ -278,14 +278,16 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
     } else {
       while (c.split_k < 64 && !fits(c)) c.split_k *= 2;
     }
-    if (m > 8 && c.split_k > 1) {
+    if (m > 4 && c.split_k > 1) {
       // Where the decode kernel needs split-K (and its reduce launch), the
       // 32 x 128 tile with Stream-K over 256 workgroups is faster despite
       // its unused rows (measured at M = 16, N = K = 8192: UINT4 17.5 us
-      // against 24, MXFP4 14.3 against 22)
+      // against 24, MXFP4 14.3 against 22; at M = 5..8: UINT4 18.0 against
+      // 23.3, MXFP4 13.5 against 21.4); MXFP4 takes the 16 x 128 tile
+      // (13.5 us against 14.4 for 32 x 128)
       hum_tile_config t{};
       t.kind = HUM_KERNEL_TILE;
-      t.wave_m = 2;
+      t.wave_m = fmt_of(d) == F_MXFP4_BF16 ? 1 : 2;
       t.wave_n = 2;
       t.waves_n = 4;
       t.waves_k = 1;
@@ -698,7 +700,13 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const void* a_use = a;
   const void* as_use = a_scales;
-  if (quant_a) {
+  // Per-token FP8 activations on the dense decode kernel without split-K:
+  // the kernel quantizes the bf16 rows itself (same codes and scales as the
+  // quantizer launch, which it saves)
+  const bool fuse_q = quant_a && desc->act_fmt == HUM_ACT_FP8_TOKEN && fmt_of(desc) == F_FP8 &&
+                      c.kind == HUM_KERNEL_STREAM && c.split_k == 1 &&
+                      stream_fp8_fuse_fits((int)m, kb_per_split(L.kb, c), c.waves_k);
+  if (quant_a && !fuse_q) {
     st = hum_quant_act(desc->act_fmt, m, desc->k, a, desc->k, ws + w.aq, ws + w.as, stream);
     if (st != HUM_OK) return st;
     a_use = ws + w.aq;
@@ -747,7 +755,8 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   }
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
-                                            : m * desc->k * (fmt_bf16_act(fmt_of(desc)) ? 2 : 1);
+                                            : m * desc->k * ((fmt_bf16_act(fmt_of(desc)) || fuse_q) ? 2 : 1);
+  p.a_fp8_fuse = fuse_q ? 1 : 0;
   p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32)
                     : (desc->act_fmt == HUM_ACT_FP8_GROUP ? m * (desc->k / 128) * 4 : 0);
   return launch_gemm(dense_key(desc, c), p, m_tiles, (int)tile_rows(c), stream);

@@ -495,10 +495,12 @@ __device__ __forceinline__ float col_scale(const uint8_t* wmeta, int64_t col, fl
 }
 
 // Stores of one 16x16 accumulator tile held in the MFMA C layout (lane holds
-// rows 4*lg + i of column c16) for the plain and scatter epilogues.
+// rows 4*lg + i of column c16) for the plain and scatter epilogues.  lrs:
+// the tile's per-token FP8 row scales where the kernel computed them itself
+// (row_base + r at lrs[r]), else null.
 template <int FMT, int EPI, int AMODE>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* wmeta, float gs, int64_t row_base,
-                                           int64_t col, const f32x4_t& v, int lg) {
+                                           int64_t col, const f32x4_t& v, int lg, const float* lrs = nullptr) {
   if (col >= p.n) return;
   uint16_t* out = static_cast<uint16_t*>(p.out);
   const float cs = col_scale<FMT>(wmeta, col, gs);
@@ -508,7 +510,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const uint8_t* w
     const int64_t row = row_base + 4 * lg + i;
     if (row >= p.m) continue;
     float x = v[i] * cs;
-    if (FMT == F_FP8) x *= row_act_scale<FMT, AMODE>(p, row);
+    if (FMT == F_FP8) x *= lrs ? lrs[4 * lg + i] : row_act_scale<FMT, AMODE>(p, row);
     x += bias;
     if (EPI == EPI_SCATTER) {
       const int32_t f = p.sorted[row];
@@ -1005,6 +1007,94 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     }
   };
 
+  // Per-token FP8 activations quantized here (dense decode, p.a_fp8_fuse: p.a
+  // holds the bf16 rows).  The rule is the activation quantizer's: s = amax /
+  // 448 over the whole row (1 for an all-zero row), codes E4M3 round to
+  // nearest even of x / s, saturated.  Each wave loads the bf16 values of its
+  // own K-blocks (the chunks its code slots hold), issues its ring, and posts
+  // each row's maximum over them (a max over the 8 lanes of a chunk row, then
+  // an LDS max, order free); after one LDS-only barrier every wave takes the
+  // row maxima of all waves, divides, converts and writes its code slots.
+  // The codes and scales are the quantizer's bit for bit, so the result is
+  // that of the two-launch path.
+  constexpr bool kFuse = FMT == F_FP8 && kSelf;
+  constexpr int kFuseCh = 4;  // code chunks per lane (a wave's K range holds at most 256)
+  __shared__ uint32_t s_amax[kFuse ? KW * 16 : 1];
+  __shared__ float s_rsc[kFuse ? 16 : 1];
+  auto fuse_stage = [&](int nr) {
+    const int nch = nj * nr * kCPR;                  // 16-byte code chunks (<= 256)
+    const int slot0 = (kw0 - kb_begin) * nr * kCPR;
+    const uint32_t mnr = ((1u << 20) + nr - 1) / nr;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+    u32x4_t xb[2 * kFuseCh];
+    int rw[kFuseCh];
+#pragma unroll
+    for (int i = 0; i < kFuseCh; ++i) {
+      const int c = i * 64 + lane;
+      const uint32_t rowkb = (uint32_t)c / kCPR;
+      const int kbl = (int)((rowkb * mnr) >> 20);
+      const int r = (int)rowkb - kbl * nr;
+      const int lc = (c & (kCPR - 1)) ^ ((r >> 1) & 7);
+      rw[i] = r < 16 ? r : 0;
+      const uint32_t off = (uint32_t)(((row0 + r) * p.lda + (int64_t)(kw0 + kbl) * 128 + lc * 16) * 2);
+      xb[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off : kOob, 0, 0);
+      xb[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off + 16 : kOob, 0, 0);
+    }
+    issue_ring();
+    uint32_t* am = s_amax + wave * 16;
+    if (lane < 16) am[lane] = 0u;  // (a wave's LDS accesses complete in order)
+#pragma unroll
+    for (int i = 0; i < kFuseCh; ++i) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(bf16_bits_to_f32(xb[2 * i + h][d] & 0xFFFF)));
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(bf16_bits_to_f32(xb[2 * i + h][d] >> 16)));
+        }
+      // the 8 lanes of one chunk row (c / 8) share its row
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4));
+      if ((lane & 7) == 0 && i * 64 + lane < nch) atomicMax(&am[rw[i]], __float_as_uint(mx));
+    }
+    // every wave's maxima posted (LDS only: the ring stays in flight)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    auto row_scale = [&](int r) -> float {
+      uint32_t u = 0;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) u = u > s_amax[w * 16 + r] ? u : s_amax[w * 16 + r];
+      const float amax = __uint_as_float(u);
+      return amax > 0.0f ? amax / 448.0f : 1.0f;  // IEEE f32 division
+    };
+    if (wave == 0 && lane < 16) s_rsc[lane] = row_scale(lane);
+#pragma unroll
+    for (int i = 0; i < kFuseCh; ++i) {
+      // (one chunk at a time: the divisions of all chunks at once would hold
+      // far more registers than the decode loop)
+      __builtin_amdgcn_sched_barrier(0);
+      const int c = i * 64 + lane;
+      if (c >= nch) continue;
+      const float sc = row_scale(rw[i]);
+      u32x4_t q;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t w0 = xb[2 * i + h][2 * d], w1 = xb[2 * i + h][2 * d + 1];
+          q[2 * h + d] = f32x2_to_e4m3x2(bf16_bits_to_f32(w0 & 0xFFFF) / sc, bf16_bits_to_f32(w0 >> 16) / sc) |
+                         (f32x2_to_e4m3x2(bf16_bits_to_f32(w1 & 0xFFFF) / sc, bf16_bits_to_f32(w1 >> 16) / sc) << 16);
+        }
+      *reinterpret_cast<u32x4_t*>(dsm + (slot0 + c) * 16) = q;
+    }
+  };
+
   int nrows = 0;
   if constexpr (kSelf) {
     // Each wave copies the activation rows and weight metadata of its own
@@ -1013,7 +1103,14 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     // order, so the copy waits for them alone), then reads only what it
     // wrote: no barrier, no loader.  Rows < m of the tile are a prefix.
     nrows = p.m - row0 < 16 ? (int)(p.m - row0) : 16;
-    self_stage(nrows);
+    if constexpr (kFuse) {
+      if (p.a_fp8_fuse)
+        fuse_stage(nrows);
+      else
+        self_stage(nrows);
+    } else {
+      self_stage(nrows);
+    }
   } else {
     stage_via_loader();
     nrows = s_nrows;
@@ -1140,7 +1237,9 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   }
   if constexpr (EPI == EPI_BF16 || EPI == EPI_SCATTER) {
 #pragma unroll
-    for (int ns = 0; ns < WN; ++ns) store_tile<FMT, EPI, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg);
+    for (int ns = 0; ns < WN; ++ns)
+      store_tile<FMT, EPI, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg,
+                                  (kFuse && p.a_fp8_fuse) ? s_rsc : nullptr);
   } else if constexpr (EPI == EPI_SWIGLU_BF16) {
 #pragma unroll
     for (int j = 0; j < WN / 2; ++j)

@@ -183,6 +183,9 @@ struct GemmParams {
   int64_t lda;        // elements (bytes for fp8)
   const void* a_scale;
   int64_t a_scale_ld; // MXFP8: scale bytes per row
+  // Dense decode kernel with per-token FP8 activations: a holds the bf16 rows
+  // (lda elements apart) and the kernel quantizes them itself (no a_scale)
+  int a_fp8_fuse;
   // INT tile kernel: activation sums per (row, K-block) as bf16 hi / lo
   // pairs, [ceil(m/16)][kbc][64 lanes][8] hi then lo (lane l = r + 16*lg
   // holds K-blocks 32*kbc + 8*lg + (0..7) of row r: the A operand of a
@@ -307,6 +310,12 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
   if (fmt_mx_meta(fmt) && fmt != F_NVFP4_BF16) return (per / 4 + 2) * 256 <= 2048;
   if (fmt == F_NVFP4_BF16) return (per / 2 + 2) * 256 <= 2048;
   return true;
+}
+
+// The dense FP8 decode kernel quantizes per-token activations itself when
+// each wave's K range holds at most 4 16-byte code chunks per lane.
+constexpr bool stream_fp8_fuse_fits(int rows, int64_t kb, int kw) {
+  return rows * ((kb + kw - 1) / kw) * 8 <= 256;
 }
 
 struct KernelKey {

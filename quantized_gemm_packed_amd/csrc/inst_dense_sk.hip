@@ -14,6 +14,7 @@ static const Instance kDenseSk[] = {
     HUM_TILE_SK(F_FP8, 2, 2, 3, 16),
     HUM_TILE_SK(F_FP8, 4, 4, 2, 16),
     HUM_TILE_SK(F_FP8, 8, 2, 2, 16),
+    HUM_TILE_SK(F_MXFP4_BF16, 1, 2, 3, 16),
     HUM_TILE_SK(F_MXFP4_BF16, 2, 2, 3, 16),
     HUM_TILE_SK(F_MXFP4_BF16, 4, 4, 3, 32),
     HUM_TILE_SK(F_MXFP4_MXFP8, 2, 2, 3, 16),

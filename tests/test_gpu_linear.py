@@ -521,6 +521,40 @@ def test_fp8_w8a8_selector_vs_oracle(m):
     assert_tol(out, ref, f"m={m}")
 
 
+@pytest.mark.parametrize("tile", STREAM_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+@pytest.mark.parametrize("m,k", [(1, 1024), (3, 1024), (8, 1024), (16, 1024), (2, 7168), (5, 384), (1, 8192)])
+def test_fp8_w8a8_decode_quantizes_in_kernel(tile, m, k):
+    """Per-token FP8 activations on the decode kernel without split-K are
+    quantized inside the kernel: the output equals the quantizer launch
+    followed by the same kernel bit for bit (same codes and scales), and
+    meets the oracle's tolerance.  Rows: an all-zero row (scale 1), a row of
+    large values and N(0,1) rows; K ranges that leave waves without
+    K-blocks."""
+    n = 320
+    if not stream_fits(tile, m, k, 1, 8):
+        pytest.skip("K range per wave too long for this tile at split 1")
+    kb, kw = k // 128, tile[4]
+    fused = m * -(-kb // kw) * 8 <= 256   # else the quantizer launch runs (same result)
+    case = synth.dense_w8a8(synth.seed_for(3, 40 + m), m, n, k)
+    xb = case["x"].copy()
+    if m >= 3:
+        xb[0] = 0
+        big = oracle.formats.decode_bf16(xb[1]) * 3e3
+        xb[1] = torch.from_numpy(big.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    hd, od = descs("e4m3", "channel", 0, "f32", 1, n, k, act="fp8_token")
+    packed = prepare(hd, case, "f32")
+    x = dev(xb)
+    print(f"case fp8 in-kernel quant tile={tile} m={m} k={k} fused={fused}", flush=True)
+    o_fused = hum.linear(hd, packed, x, cfg=cfg(tile, 1))
+    q, s = hum.quant_act("fp8_token", x)
+    o_two = hum.linear(hd, packed, q, a_scales=s, cfg=cfg(tile, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(o_fused.view(torch.int16), o_two.view(torch.int16)), f"tile={tile} m={m} k={k}"
+    qo, so = oracle.quant.quant_fp8_per_token(oracle.formats.decode_bf16(xb).astype(np.float32))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_fp8_per_token(qo, so), case["codes"], case["scales"])
+    assert_tol(o_fused, ref, f"tile={tile} m={m} k={k}")
+
+
 def test_fp8_prequantized_activations_match_internal_quant():
     m, n, k = 33, 256, 1024
     case = synth.dense_w8a8(91, m, n, k)

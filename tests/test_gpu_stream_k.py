@@ -32,6 +32,7 @@ SK_TILES = [
     ("e4m3_block", 0, 2, 2, 3), ("e4m3_block", 0, 8, 2, 2),
     ("e4m3_bf16", 0, 2, 2, 3), ("int8", 0, 2, 2, 3), ("nvfp4", 0, 2, 2, 3), ("mxint4", 0, 2, 2, 3),
     ("int3", 0, 2, 2, 3), ("uint2", 0, 2, 2, 3), ("int1", 0, 2, 2, 3), ("e2m3", 0, 2, 2, 3), ("e3m2", 0, 2, 2, 3),
+    ("e2m1", 0, 1, 2, 3),
 ]
 
 
