@@ -213,6 +213,10 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
 // One 8-element chunk (row, c8) of the MXFP4 quantizer; every lane of a
 // wave calls it together (the DPP quad reduction reads the quad's four
 // lanes), with valid = false for lanes that have no chunk.
+// WIDE: each E2M1 code is written as the E4M3 byte of the same value (one
+// byte per element, k bytes per row), for the E4M3 x E2M1 decode kernel: an
+// MXFP4 activation block is then an MXFP8 block with the same E8M0 scale.
+template <bool WIDE = false>
 __device__ __forceinline__ void mxfp4_chunk(const uint16_t* __restrict__ x, int64_t ldx, int64_t k, int64_t row,
                                               int64_t c8, bool valid, uint8_t* __restrict__ q,
                                               uint8_t* __restrict__ s) {
@@ -231,20 +235,34 @@ __device__ __forceinline__ void mxfp4_chunk(const uint16_t* __restrict__ x, int6
   const int e = mx_scale_code_emax(amax, 2);
   const float inv = mx_inv_scale(e);
   if (!valid) return;
-  uint32_t o = 0;
+  if constexpr (WIDE) {
+    // E2M1 magnitude code -> E4M3 byte: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+    constexpr uint64_t kE4m3Of = 0x4C4844403C383000ull;
+    uint32_t o[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o |= f32_to_e2m1(f[i] * inv) << (4 * i);
-  *reinterpret_cast<uint32_t*>(q + row * (k / 2) + c8 * 4) = o;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c = f32_to_e2m1(f[i] * inv);
+      const uint32_t b = (uint32_t)((kE4m3Of >> (8 * (c & 7))) & 0xFF) | ((c & 8) << 4);
+      o[i >> 2] |= b << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(q + row * k + c8 * 8) = make_uint2(o[0], o[1]);
+  } else {
+    uint32_t o = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o |= f32_to_e2m1(f[i] * inv) << (4 * i);
+    *reinterpret_cast<uint32_t*>(q + row * (k / 2) + c8 * 4) = o;
+  }
   if ((c8 & 3) == 0) s[row * (k / 32) + c8 / 4] = (uint8_t)e;
 }
 
+template <bool WIDE>
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                           int64_t m, int64_t k, uint8_t* __restrict__ q,
                                                           uint8_t* __restrict__ s) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t cpr = k / 8;  // chunks per row
   const bool valid = id < m * cpr;
-  mxfp4_chunk(x, ldx, k, valid ? id / cpr : 0, valid ? id % cpr : 0, valid, q, s);
+  mxfp4_chunk<WIDE>(x, ldx, k, valid ? id / cpr : 0, valid ? id % cpr : 0, valid, q, s);
 }
 
 // grouped_masked buffers: workgroup (e, slice) walks rows slice, slice +
@@ -278,11 +296,22 @@ hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, 
         static_cast<const uint16_t*>(x), ldx, k, counts, max_m, slices, static_cast<uint8_t*>(q), s);
   } else {
     const int64_t chunks = m * (k / 8);
-    quant_mxfp4_kernel<<<cdiv_u(chunks, 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), ldx, m, k,
-                                                              static_cast<uint8_t*>(q), s);
+    quant_mxfp4_kernel<false><<<cdiv_u(chunks, 256), 256, 0, st>>>(static_cast<const uint16_t*>(x), ldx, m, k,
+                                                                     static_cast<uint8_t*>(q), s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp4 launch: %s", hipGetErrorString(err));
+  return HUM_OK;
+}
+
+hum_status launch_quant_mxfp4_wide(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, uint8_t* s,
+                                   void* stream) {
+  if (m == 0) return HUM_OK;
+  const int64_t chunks = m * (k / 8);
+  quant_mxfp4_kernel<true><<<cdiv_u(chunks, 256), 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint16_t*>(x), ldx, m, k, static_cast<uint8_t*>(q), s);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return set_error(HUM_ERR_HIP, "quant_mxfp4 (E4M3 bytes) launch: %s", hipGetErrorString(err));
   return HUM_OK;
 }
 

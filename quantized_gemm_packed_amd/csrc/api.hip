@@ -411,6 +411,11 @@ static int moe_up_epi(int f) {
   return f == F_MXFP4_MXFP8 ? EPI_SWIGLU_MXFP8 : (f == F_MXFP4_MXFP4 ? EPI_SWIGLU_MXFP4 : EPI_SWIGLU_BF16);
 }
 
+// The format a MoE GEMM of format f runs on the decode kernel: W4A4 gate_up
+// runs there as E4M3 x E2M1 (its MXFP4 activations handed over as the E4M3
+// bytes of the same values, requantized to MXFP4 in the SwiGLU epilogue).
+static int moe_stream_fmt(int f) { return f == F_MXFP4_MXFP4 ? F_MXFP4_MXFP8 : f; }
+
 // A gathered decode-kernel configuration stages the activation rows of its
 // whole K range (and the weight metadata) in LDS: it fits when that plan and
 // the in-workgroup reduction stay within kStreamLdsMax.
@@ -418,8 +423,8 @@ static bool moe_stream_fits(const hum_weight_desc* w, const hum_tile_config& c, 
   if (c.kind != HUM_KERNEL_STREAM) return true;
   Layout L;
   if (compute_layout(w, &L) != HUM_OK) return false;
-  const StreamLdsPlan P =
-      stream_lds_plan(fmt_of(w), rows, kb_per_split(L.kb, c), c.wave_n, L.kb_per_group, L.scale_f32, L.ng, L.kb4);
+  const StreamLdsPlan P = stream_lds_plan(moe_stream_fmt(fmt_of(w)), rows, kb_per_split(L.kb, c), c.wave_n,
+                                         L.kb_per_group, L.scale_f32, L.ng, L.kb4);
   const int64_t red = (int64_t)(c.waves_k - 1) * c.wave_n * 64 * 16;
   return P.total <= kStreamLdsMax && red <= kStreamLdsMax;
 }
@@ -461,8 +466,16 @@ static MoeCfg select_moe(const hum_weight_desc* w13, int64_t t, int32_t topk, co
 static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t topk) {
   const double rows = (double)t * topk / w13->num_experts;
   const int f = fmt_of(w13);
+  if (f == F_MXFP4_MXFP4 && t * topk <= 64) {
+    // W4A4 up to 64 routed slots: gate_up on the E4M3 x E2M1 decode kernel
+    // with four K-waves (as W4A8), down on the 16-row W4A4 tile
+    hum_tile_config up = moe_stream_cfg();
+    up.waves_k = 4;
+    return {up, moe_tile_cfg(1)};
+  }
   if (f == F_MXFP4_MXFP4 || f == F_FP8_BLOCK) {
-    // W4A4 and block-scaled FP8: tile kernels only (no decode-kernel path);
+    // W4A4 and block-scaled FP8: tile kernels (block-scaled FP8 has no
+    // decode-kernel path);
     // measured over Zipf-skewed routing like the FP8-activation rule below,
     // block-scaled FP8 taking 64-row tiles from 24 rows per expert
     const int wm = rows < 4 ? 1 : (rows <= (f == F_FP8_BLOCK ? 24 : 96) ? 2 : 4);
@@ -990,7 +1003,9 @@ static MoeWs moe_ws(const hum_weight_desc* w13, const hum_weight_desc* w2, int64
   if (!masked) off = align256(off + align_workspace_bytes(t, topk, (int32_t)E));
   w.xq = off;
   if (act != HUM_ACT_BF16) {
-    const ActBytes ab = act_bytes(act, t, h);
+    // (W4A4 gate_up on the decode kernel reads the codes as E4M3 bytes)
+    const bool wide = act == HUM_ACT_MXFP4 && mc.up.kind == HUM_KERNEL_STREAM;
+    const ActBytes ab = act_bytes(wide ? HUM_ACT_MXFP8 : act, t, h);
     off = align256(off + ab.codes);
     w.xs = off;
     off = align256(off + ab.scales);
@@ -1260,7 +1275,8 @@ static hum_status moe_keys(const hum_weight_desc* w13, const MoeCfg& mc, KernelK
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   const int f = fmt_of(w13);
   const int epi_up = moe_up_epi(f);
-  *kup = KernelKey{f, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
+  const int fu = cu.kind == HUM_KERNEL_STREAM ? moe_stream_fmt(f) : f;
+  *kup = KernelKey{fu, cu.kind, cu.wave_m, cu.wave_n, cu.waves_n, cu.waves_k, A_GATHER, epi_up, key_stages(cu)};
   *kdn = KernelKey{f, cd.kind, cd.wave_m, cd.wave_n, cd.waves_n, cd.waves_k, A_DIRECT, EPI_SCATTER, key_stages(cd)};
   if (!gemm_instance_exists(*kup) || !gemm_instance_exists(*kdn)) return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   if ((cu.split_k > 1 && !reduce_instance_exists(f, epi_up)) || (cd.split_k > 1 && !reduce_instance_exists(f, EPI_SCATTER)))
@@ -1312,7 +1328,11 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   const bool sep_q = act_separate_quant(act);
   const void* x_use = x_bf16;
   hum_status st = HUM_OK;
-  if (act == HUM_ACT_MXFP4) {
+  // W4A4 gate_up on the decode kernel: MXFP4 codes as E4M3 bytes
+  const bool wide_a = act == HUM_ACT_MXFP4 && kup.kind == KIND_STREAM;
+  if (wide_a) {
+    st = launch_quant_mxfp4_wide(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream);
+  } else if (act == HUM_ACT_MXFP4) {
     st = launch_quant_mxfp4(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
   } else if (act == HUM_ACT_MXFP8) {
     st = launch_quant_mxfp8(t, h, x_bf16, h, ws + w.xq, ws + w.xs, stream, r.counts, r.max_m);
@@ -1348,7 +1368,7 @@ static hum_status moe_gemms(const hum_weight_desc* w13, const void* packed_w13, 
   p.kb_per_split = kb_per_split(L13.kb, cu);
   p.partials = reinterpret_cast<float*>(ws + w.partials);
   p.stream_rows = r.stream_rows;
-  const ActBytes xb = act_bytes(act, t, h);
+  const ActBytes xb = act_bytes(wide_a ? HUM_ACT_MXFP8 : act, t, h);
   p.a_bytes = xb.codes;
   p.a_scale_bytes = xb.scales;
   if (r.route_ids) {

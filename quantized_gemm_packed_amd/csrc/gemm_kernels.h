@@ -719,7 +719,11 @@ template <int FMT, int WN, int KW, int PF, int AMODE, int EPI>
 __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream_kernel(const GemmParams p) {
   using T = Tr<FMT>;
   constexpr bool kSwiglu = (EPI == EPI_SWIGLU_BF16 || EPI == EPI_SWIGLU_MXFP8 || EPI == EPI_SWIGLU_MXFP4);
-  static_assert(EPI != EPI_SWIGLU_MXFP4 && FMT != F_MXFP4_MXFP4, "W4A4 runs on the tile kernel only");
+  // (W4A4 at decode sizes runs here as E4M3 x E2M1: its MXFP4 activations are
+  // handed over as the E4M3 bytes of the same values, and the SwiGLU output
+  // is requantized to MXFP4 for the W4A4 down GEMM)
+  static_assert(FMT != F_MXFP4_MXFP4 && (EPI != EPI_SWIGLU_MXFP4 || FMT == F_MXFP4_MXFP8),
+                "W4A4 decode: E4M3 x E2M1 with the MXFP4 SwiGLU epilogue");
   static_assert(!kSwiglu || WN % 2 == 0, "gate/up pairs");
   static_assert((EPI != EPI_SWIGLU_MXFP8 && EPI != EPI_SWIGLU_MXFP4) || WN % 4 == 0, "32-column MX blocks");
   constexpr int kRowB = StreamLds<FMT>::kRowB;
@@ -1244,6 +1248,11 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
 #pragma unroll
     for (int j = 0; j < WN / 2; ++j)
       store_swiglu_bf16<FMT, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[j] * 16 + c16, acc[j], acc[j + WN / 2], lg);
+  } else if constexpr (EPI == EPI_SWIGLU_MXFP4) {
+#pragma unroll
+    for (int jj = 0; jj < WN / 4; ++jj)
+      store_swiglu_mxfp4<FMT>(p, wp.meta, gs, row0, (int64_t)nts[2 * jj] * 16 + c16, acc[2 * jj], acc[2 * jj + WN / 2],
+                              acc[2 * jj + 1], acc[2 * jj + 1 + WN / 2], lg, c16);
   } else {
 #pragma unroll
     for (int jj = 0; jj < WN / 4; ++jj)

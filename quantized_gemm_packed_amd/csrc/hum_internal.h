@@ -133,6 +133,11 @@ hum_status launch_quant_mxfp8(int64_t m, int64_t k, const void* x, int64_t ldx, 
                               uint8_t* s, void* stream, const int32_t* counts = nullptr, int64_t max_m = 0);
 hum_status launch_quant_mxfp4(int64_t m, int64_t k, const void* x, int64_t ldx, void* q,
                               uint8_t* s, void* stream, const int32_t* counts = nullptr, int64_t max_m = 0);
+// The MXFP4 rule with each code written as the E4M3 byte of its value (k
+// bytes per row; scales as launch_quant_mxfp4): input of the E4M3 x E2M1
+// decode kernel that serves W4A4 layers at decode sizes.
+hum_status launch_quant_mxfp4_wide(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, uint8_t* s,
+                                   void* stream);
 hum_status launch_quant_fp8_group(int64_t m, int64_t k, const void* x, int64_t ldx, void* q, float* s,
                                   void* stream, const int32_t* sorted = nullptr, int32_t sentinel = 0);
 hum_status launch_zero(void* p, size_t bytes, void* stream);

@@ -382,3 +382,24 @@ def test_moe_decode_routing_matches_align(act, t, k, e):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     o = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act)
     assert_tol(out, o, f"routing act={act} t={t}")
+
+
+@pytest.mark.parametrize("t", [1, 3, 8])
+def test_w4a4_decode_gate_up_matches_tiles_and_oracle(t):
+    """W4A4 layers of up to 64 routed slots run gate_up on the E4M3 x E2M1
+    decode kernel (the MXFP4 activations handed over as the E4M3 bytes of the
+    same values, the SwiGLU output requantized to MXFP4) and down on the
+    16-row W4A4 tile: the layer matches the all-tile path (the same products,
+    summed by another matrix instruction) and the oracle."""
+    e, h, inter, k = 16, 1024, 512, 4
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(770, e, h, inter, "mxfp4")
+    assert hum.moe_select_config(d13, d2, t, k, gate_up=True).kind == hum.KERNEL_STREAM
+    ids, wts = synth.routing(771 + t, t, e, k)
+    xb = synth.bf16_normal(synth.rng(772 + t), (t, h))
+    print(f"case w4a4 decode gate_up t={t}", flush=True)
+    out = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    out_tiles = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts), cfg=cfg((0, 1, 4, 4, 1)))
+    torch.cuda.synchronize()
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, "mxfp4")
+    assert_tol(out, ref, f"decode gate_up t={t}")
+    assert_tol(out, out_tiles.float().cpu().numpy().astype(np.float64), f"decode vs tiles t={t}")
