@@ -192,9 +192,15 @@ static int key_stages(const hum_tile_config& c) {
   return c.kind != HUM_KERNEL_STREAM ? (c.stages == 0 ? 2 : c.stages) : 0;
 }
 
+// W4A4 on the decode kernel runs as E4M3 x E2M1: its MXFP4 activations are
+// quantized as the E4M3 bytes of the same values.
+static bool w4a4_on_stream(const hum_weight_desc* d, const hum_tile_config& c) {
+  return fmt_of(d) == F_MXFP4_MXFP4 && c.kind == HUM_KERNEL_STREAM;
+}
+
 static KernelKey dense_key(const hum_weight_desc* d, const hum_tile_config& c) {
-  return KernelKey{fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n, c.waves_k, A_DIRECT, EPI_BF16, key_stages(c),
-                   c.stream_k > 0 ? 1 : 0};
+  return KernelKey{w4a4_on_stream(d, c) ? (int)F_MXFP4_MXFP8 : fmt_of(d), c.kind, c.wave_m, c.wave_n, c.waves_n,
+                   c.waves_k, A_DIRECT, EPI_BF16, key_stages(c), c.stream_k > 0 ? 1 : 0};
 }
 
 // Stream-K tile counters: the workspace header, one u32 per tile.
@@ -234,7 +240,27 @@ static int kb_per_split(int64_t kb, const hum_tile_config& c) {
   return (int)(cdiv(cdiv(kb, c.split_k), unit) * unit);
 }
 
-static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m) {
+static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool w4a4_decode = true) {
+  if (w4a4_decode && fmt_of(d) == F_MXFP4_MXFP4 && m <= 16) {
+    // W4A4 at decode sizes: the E4M3 x E2M1 decode kernel, one sub-tile and
+    // four K-waves per workgroup while the activation rows fit its LDS
+    // (measured at N = 7168, K = 2048: M = 1 8.1 us, M = 16 10.6 us against
+    // 11.5 and 11.9 on the 32 x 128 tile; two or four sub-tiles with eight
+    // K-waves 10-20% slower)
+    hum_tile_config c{};
+    c.kind = HUM_KERNEL_STREAM;
+    c.wave_m = 1;
+    c.wave_n = 1;
+    c.waves_n = 1;
+    c.waves_k = 4;
+    c.split_k = 1;
+    c.block_m = 16;
+    Layout L;
+    compute_layout(d, &L);
+    if (stream_lds_plan(F_MXFP4_MXFP8, (int)m, kb_per_split(L.kb, c), 1, L.kb_per_group, L.scale_f32, L.ng, L.kb4)
+            .total <= kStreamLdsDense)
+      return c;
+  }
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
@@ -533,7 +559,7 @@ static DenseWs dense_ws(const hum_weight_desc* d, int64_t m, const hum_tile_conf
   if (c.stream_k > 0) off = align256(off + 2 * (int64_t)c.stream_k * tile_rows(c) * tile_subtiles(c) * 16 * 4);
   w.aq = off;
   if (quant_a) {
-    off = align256(off + (d->act_fmt == HUM_ACT_MXFP4 ? m * (d->k / 2) : m * d->k));
+    off = align256(off + (d->act_fmt == HUM_ACT_MXFP4 && !w4a4_on_stream(d, c) ? m * (d->k / 2) : m * d->k));
     w.as = off;
     off = align256(off + (d->act_fmt == HUM_ACT_MXFP8 || d->act_fmt == HUM_ACT_MXFP4
                               ? m * (d->k / 32)
@@ -700,12 +726,15 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   if (m < 0) return set_error(HUM_ERR_INVALID_ARG, "m < 0");
   if (m == 0) return HUM_OK;
   if (!packed || !a || !out) return set_error(HUM_ERR_INVALID_ARG, "packed, a and out must be non-NULL");
-  hum_tile_config c = cfg ? *cfg : select_dense(desc, m);
+  const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  // (pre-quantized W4A4 activations are E2M1 codes: the tile kernels take them)
+  hum_tile_config c = cfg ? *cfg : select_dense(desc, m, quant_a);
   if (!cfg_sane(c) || !gemm_instance_exists(dense_key(desc, c)) ||
       (c.split_k > 1 && !reduce_instance_exists(fmt_of(desc), EPI_BF16)))
     return set_error(HUM_ERR_UNSUPPORTED, "tile config not available");
   if (c.kind == HUM_KERNEL_STREAM && m > 16) return set_error(HUM_ERR_UNSUPPORTED, "the stream kernel takes m <= 16");
-  const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  if (w4a4_on_stream(desc, c) && !quant_a)
+    return set_error(HUM_ERR_UNSUPPORTED, "W4A4 on the decode kernel quantizes its activations itself");
   const DenseWs w = dense_ws(desc, m, c, quant_a);
   if (w.total > 0 && (!workspace || ws_bytes < (size_t)w.total))
     return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
@@ -719,7 +748,12 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   const bool fuse_q = quant_a && desc->act_fmt == HUM_ACT_FP8_TOKEN && fmt_of(desc) == F_FP8 &&
                       c.kind == HUM_KERNEL_STREAM && c.split_k == 1 &&
                       stream_fp8_fuse_fits((int)m, kb_per_split(L.kb, c), c.waves_k);
-  if (quant_a && !fuse_q) {
+  if (w4a4_on_stream(desc, c)) {
+    st = launch_quant_mxfp4_wide(m, desc->k, a, desc->k, ws + w.aq, reinterpret_cast<uint8_t*>(ws + w.as), stream);
+    if (st != HUM_OK) return st;
+    a_use = ws + w.aq;
+    as_use = ws + w.as;
+  } else if (quant_a && !fuse_q) {
     st = hum_quant_act(desc->act_fmt, m, desc->k, a, desc->k, ws + w.aq, ws + w.as, stream);
     if (st != HUM_OK) return st;
     a_use = ws + w.aq;
@@ -767,7 +801,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
     if (p.sk_part_bytes >= ((int64_t)1 << 31)) return set_error(HUM_ERR_UNSUPPORTED, "Stream-K partial slots above 2 GiB");
   }
   p.stream_rows = (int)(m < 16 ? m : 16);
-  p.a_bytes = fmt_of(desc) == F_MXFP4_MXFP4 ? m * (desc->k / 2)
+  p.a_bytes = (fmt_of(desc) == F_MXFP4_MXFP4 && !w4a4_on_stream(desc, c)) ? m * (desc->k / 2)
                                             : m * desc->k * ((fmt_bf16_act(fmt_of(desc)) || fuse_q) ? 2 : 1);
   p.a_fp8_fuse = fuse_q ? 1 : 0;
   p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32)
@@ -823,8 +857,8 @@ hum_status hum_linear_noalloc(const hum_weight_desc* desc, const void* packed, i
   if (st != HUM_OK) return st;
   if (m < 0) return set_error(HUM_ERR_INVALID_ARG, "m < 0");
   if (m == 0) return HUM_OK;
-  const hum_tile_config c = select_dense(desc, m);
   const bool quant_a = desc->act_fmt != HUM_ACT_BF16 && a_scales == nullptr;
+  const hum_tile_config c = select_dense(desc, m, quant_a);
   const int64_t need = dense_ws(desc, m, c, quant_a).total;
   if (need > (int64_t)HUM_NOALLOC_SCRATCH_BYTES)
     return set_error(HUM_ERR_WORKSPACE,

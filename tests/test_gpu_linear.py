@@ -239,6 +239,33 @@ def test_mxfp4_mxfp4_exact_every_tile(tile, split):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("tile", STREAM_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_w4a4_decode_kernel_exact(tile, split):
+    """Dense W4A4 on the decode kernel (E4M3 x E2M1: the MXFP4 activations
+    handed over as the E4M3 bytes of the same values): the exact case of
+    the tile test above, bitwise equal to the oracle, on every decode
+    configuration."""
+    m, n, k = 13, 96, 1024
+    g = synth.rng(37)
+    w = synth.quant_weights(37, "e2m1", "group", 32, "e8m0", 1, n, k, e8m0_lo=126, e8m0_hi=127)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    x = grid[g.integers(0, 8, size=(m, k))] * np.where(g.integers(0, 2, size=(m, k)) == 1, -1.0, 1.0)
+    x[:, ::32] = np.where(g.integers(0, 2, size=(m, k // 32)) == 1, 4.0, -6.0)
+    xb = oracle.formats.encode_bf16(x)
+    hd, od = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp4")
+    packed = prepare(hd, w, "e8m0")
+    print(f"case w4a4 decode exact tile={tile} split={split}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+    torch.cuda.synchronize()
+    ref = oracle.gemm.linear(od, oracle.formats.decode_bf16(xb), w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile} split={split}")
+    # pre-quantized W4A4 activations (E2M1 codes) are refused on the decode kernel
+    q, s = hum.quant_act("mxfp4", dev(xb))
+    with pytest.raises(hum.HumError, match="quantizes its activations itself"):
+        hum.linear(hd, packed, q, a_scales=s, cfg=cfg(tile, split))
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_w4a4_dense_random_vs_oracle(m):
     """Dense W4A4 (MXFP4 weights x MXFP4 activations) at the selector's config."""
