@@ -403,3 +403,36 @@ def test_w4a4_decode_gate_up_matches_tiles_and_oracle(t):
     ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, "mxfp4")
     assert_tol(out, ref, f"decode gate_up t={t}")
     assert_tol(out, out_tiles.float().cpu().numpy().astype(np.float64), f"decode vs tiles t={t}")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("t", [1, 5])
+def test_moe_decode_tokens_without_routed_slots(act, t):
+    """Decode sizes (in-kernel routing, no align launch): a token none of
+    whose slots is routed here (every id outside [0, E)) gets a zero row,
+    whatever `out` held; partly routed tokens sum their routed slots only;
+    the next call on the same workspace is unaffected."""
+    e, h, inter, k = 8, 512, 256, 4
+    w13, w2, d13, o13, d2, o2, p13, p2 = _layer(790, e, h, inter, act)
+    ids, wts = synth.routing(791 + t, t, e, k)
+    bad = np.zeros_like(ids, dtype=bool)
+    bad[0, :] = True
+    if t > 2:
+        bad[2, 1] = True
+    ids_bad = np.where(bad, -1, ids).astype(np.int32)
+    if t > 2:
+        ids_bad[2, 1] = e
+    xb = synth.bf16_normal(synth.rng(792 + t), (t, h))
+    out = torch.full((t, h), 7.0, dtype=torch.bfloat16, device="cuda")
+    print(f"case moe unrouted tokens act={act} t={t}", flush=True)
+    hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids_bad), dev(wts), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0].view(torch.int16), torch.zeros(h, dtype=torch.int16, device="cuda"))
+    ids_ref = np.where(bad, 0, ids).astype(np.int32)
+    wts_ref = np.where(bad, 0.0, wts).astype(np.float32)
+    ref = oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids_ref, wts_ref, act)
+    if t > 1:
+        assert_tol(out[1:], ref[1:], f"partly routed act={act} t={t}")
+    out2 = hum.moe_gemm(d13, p13, d2, p2, dev(xb), dev(ids), dev(wts))
+    torch.cuda.synchronize()
+    assert_tol(out2, oracle.moe.moe_forward(o13, w13, o2, w2, xb, ids, wts, act), f"next call act={act} t={t}")
