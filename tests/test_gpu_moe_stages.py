@@ -75,7 +75,7 @@ def stage_inputs(bits, q, s, act):
 @pytest.mark.parametrize("tile", MOE_TILES, ids=lambda t: "t" + "".join(map(str, t)))
 def test_gate_up_and_down_exact_integer_every_tile(act, tile):
     if act == "mxfp4" and tile[0] == 1:
-        pytest.skip("W4A4 runs on the tile kernel only")
+        pytest.skip("W4A4's decode kernel has the MXFP4 SwiGLU epilogue only")
     e, h, inter, k, t = 8, 1024, 512, 2, 40
     bm = 16 * tile[1]
     w13 = exact_weights(900, e, 2 * inter, h)
@@ -193,3 +193,40 @@ def test_stage_argument_errors():
         hum.moe_grouped_gemm(d13, pk, q, dev(srt), dev(off), 16, 3, 1, epilogue="swiglu_bf16", a_scales=s)
     with pytest.raises(hum.HumError, match="block_m"):
         hum.moe_grouped_gemm(d13, pk, q, dev(srt), dev(off), 24, 3, 1, epilogue="none", a_scales=s)
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
+def test_decode_down_tile_exact_integer(act):
+    """The down GEMM of decode-size layers (16-row tiles of 128 columns, three
+    stages): exact-integer rows in sorted order scattered to their flat
+    slots, bit for bit against the oracle per expert."""
+    e, h, inter, k, t = 8, 1024, 512, 2, 40
+    tile = hum.moe_select_config(*_decode_descs(act), 1, 8)
+    assert (tile.kind, tile.wave_m, tile.wave_n, tile.stages) == (hum.KERNEL_TILE, 1, 2, 3), tile
+    w2 = exact_weights(911, e, h, inter)
+    d2, o2 = descs("e2m1", "group", 32, "e8m0", e, h, inter, act=act)
+    p2 = prepare(d2, w2, "e8m0")
+    ids, _ = synth.routing(912, t, e, k, zipf_s=1.3)
+    srt, off, cnt = oracle.moe.align(ids, e, 16)
+    ibits, iq, isc, iv = exact_acts(914, len(srt), inter, act)
+    a2, a2_s = stage_inputs(ibits, iq, isc, act)
+    print(f"case decode down exact act={act}", flush=True)
+    y_flat = hum.moe_grouped_gemm(d2, p2, a2, dev(srt), dev(off), 16, t, k, a_mode="sorted", epilogue="scatter",
+                                  a_scales=a2_s, cfg=tile)
+    torch.cuda.synchronize()
+    yfb = bf16_bits_of(y_flat)
+    for ex in range(e):
+        seg = srt[off[ex]:off[ex] + cnt[ex]]
+        if len(seg) == 0:
+            continue
+        rows = np.arange(off[ex], off[ex] + cnt[ex])
+        yref = oracle.gemm.linear(o2, iv[rows], w2["codes"], w2["scales"], expert=ex)
+        assert np.array_equal(yfb[seg], oracle.formats.encode_bf16(yref)), f"down scatter expert {ex}"
+
+
+def _decode_descs(act):
+    """Descriptions of the E = 128, top-8, H = 4096, I = 1024 layer, whose
+    selector takes the decode configuration at one token."""
+    d13, _ = descs("e2m1", "group", 32, "e8m0", 128, 2048, 4096, act=act)
+    d2, _ = descs("e2m1", "group", 32, "e8m0", 128, 4096, 1024, act=act)
+    return d13, d2
