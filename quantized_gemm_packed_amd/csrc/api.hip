@@ -426,12 +426,14 @@ static hum_tile_config moe_tile_cfg(int wm) {
   return c;
 }
 
-// The down GEMM of decode-size layers: 16-row tiles of 128 columns with
-// three stages (twice the workgroups of the 256-column tile over its 8
-// K-blocks, two in flight; measured at T = 1, E = 128, top-8, H = 4096, I =
-// 1024: layer W4A16 23.0 -> 21.0 us, W4A8 24.5 -> 22.0, W4A4 26.2 -> 24.0;
-// 64-column tiles no better)
-static hum_tile_config moe_decode_down_cfg() {
+// 16-row tiles of 128 columns with three stages: twice the workgroups of
+// the 256-column tile, two K-blocks in flight.  The down GEMM of decode-size
+// layers (measured at T = 1, E = 128, top-8, H = 4096, I = 1024: layer W4A16
+// 23.0 -> 21.0 us, W4A8 24.5 -> 22.0, W4A4 26.2 -> 24.0; 64-column tiles no
+// better), and both GEMMs wherever MXFP4 x bf16 and block-scaled FP8 layers
+// take 16-row tiles (W4A16 T = 2 / 4 / 16 / 64: 45.5 -> 31.7, 54.8 -> 46.5,
+// 115 -> 110, 164 -> 159 us; block FP8 T = 1: 47.5 -> 33.3 us)
+static hum_tile_config moe_tile16_cfg() {
   hum_tile_config c = moe_tile_cfg(1);
   c.wave_n = 2;
   c.stages = 3;
@@ -509,7 +511,7 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
     // with four K-waves (as W4A8), down on the 16-row W4A4 tile
     hum_tile_config up = moe_stream_cfg();
     up.waves_k = 4;
-    return {up, moe_decode_down_cfg()};
+    return {up, moe_tile16_cfg()};
   }
   if (f == F_MXFP4_MXFP4 || f == F_FP8_BLOCK) {
     // W4A4 and block-scaled FP8: tile kernels (block-scaled FP8 has no
@@ -517,6 +519,7 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
     // measured over Zipf-skewed routing like the FP8-activation rule below,
     // block-scaled FP8 taking 64-row tiles from 24 rows per expert
     const int wm = rows < 4 ? 1 : (rows <= (f == F_FP8_BLOCK ? 24 : 96) ? 2 : 4);
+    if (f == F_FP8_BLOCK && wm == 1) return {moe_tile16_cfg(), moe_tile16_cfg()};
     return {moe_tile_cfg(wm), moe_tile_cfg(wm)};
   }
   const int64_t tile_wgs = std::min<int64_t>(t * topk, w13->num_experts) * cdiv(w13->n, 256);
@@ -529,13 +532,13 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
   if ((f == F_MXFP4_BF16 && tile_wgs < 128) || (f == F_MXFP4_MXFP8 && t * topk <= 64)) {
     hum_tile_config up = moe_stream_cfg();
     up.waves_k = 4;
-    return {up, moe_decode_down_cfg()};
+    return {up, moe_tile16_cfg()};
   }
   if (tile_wgs < 128) return {moe_stream_cfg(), moe_stream_cfg()};
   const bool fp8_act = f == F_MXFP4_MXFP8 || f == F_FP8;
   const int wm = fp8_act ? (rows < 4 ? 1 : (rows <= 96 ? 2 : 4))
                          : (rows < 8 ? 1 : (rows < 128 ? 2 : (rows < 512 ? 4 : 8)));
-  hum_tile_config c = moe_tile_cfg(wm);
+  hum_tile_config c = (f == F_MXFP4_BF16 && wm == 1) ? moe_tile16_cfg() : moe_tile_cfg(wm);
   // W4A8 32- and 64-row tiles: three stages (the down GEMM has only 8
   // K-blocks, and a second block in flight hides more of each one's load
   // latency; about 4% on the layer from T = 256 to 8192)

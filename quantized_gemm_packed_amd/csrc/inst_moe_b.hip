@@ -10,6 +10,10 @@ namespace hum {
 static const Instance kMoeB[] = {
     HUM_MOE_SET(F_FP8, EPI_SWIGLU_BF16),
     HUM_MOE_TILE_SET(F_FP8_BLOCK, EPI_SWIGLU_BF16),
+    HUM_TILE_S(F_FP8_BLOCK, 1, 2, A_GATHER, EPI_SWIGLU_BF16, 3),
+    HUM_TILE_S(F_FP8_BLOCK, 1, 2, A_DIRECT, EPI_SCATTER, 3),
+    HUM_TILE_S(F_FP8_BLOCK, 1, 4, A_GATHER, EPI_SWIGLU_BF16, 3),
+    HUM_TILE_S(F_FP8_BLOCK, 1, 4, A_DIRECT, EPI_SCATTER, 3),
     HUM_MOE_SET(F_FP8_BF16, EPI_SWIGLU_BF16),
     HUM_MOE_SET(F_INT8_BF16, EPI_SWIGLU_BF16),
 };
