@@ -240,8 +240,10 @@ static int kb_per_split(int64_t kb, const hum_tile_config& c) {
   return (int)(cdiv(cdiv(kb, c.split_k), unit) * unit);
 }
 
-static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool w4a4_decode = true) {
-  if (w4a4_decode && fmt_of(d) == F_MXFP4_MXFP4 && m <= 16) {
+// fused_decode: the activations are bf16 (not pre-quantized), so W4A4 and
+// block-scaled FP8 may take the decode kernel, which quantizes them itself.
+static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool fused_decode = true) {
+  if (fused_decode && fmt_of(d) == F_MXFP4_MXFP4 && m <= 16) {
     // W4A4 at decode sizes: the E4M3 x E2M1 decode kernel, one sub-tile and
     // four K-waves per workgroup while the activation rows fit its LDS
     // (measured at N = 7168, K = 2048: M = 1 8.1 us, M = 16 10.6 us against
@@ -264,6 +266,17 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool w4
   hum_tile_config c{};
   const int64_t nt = cdiv(d->n, kNSub);
   const int64_t kb = d->k / kKBlk;
+  if (fused_decode && fmt_of(d) == F_FP8_BLOCK && m <= 16) {
+    // block-scaled FP8 at decode sizes: the decode kernel, which quantizes
+    // each row's K-blocks itself, wherever the per-token FP8 layer of the
+    // same shape takes it and the rows fit four code chunks per lane
+    hum_weight_desc dt = *d;
+    dt.scale_gran = HUM_SCALE_CHANNEL;
+    dt.group_size = 0;
+    dt.act_fmt = HUM_ACT_FP8_TOKEN;
+    const hum_tile_config ct = select_dense(&dt, m);
+    if (ct.kind == HUM_KERNEL_STREAM && stream_fp8_fuse_fits((int)m, kb_per_split(kb, ct), ct.waves_k)) return ct;
+  }
   if (m <= 16 && fmt_of(d) != F_MXFP4_MXFP4 && fmt_of(d) != F_FP8_BLOCK) {
     // decode: one 16-row tile streamed by waves splitting K.  Sub-tiles per
     // wave: the fewest that keep the activation bytes each workgroup reads
@@ -750,6 +763,10 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   if (c.kind == HUM_KERNEL_STREAM && m > 16) return set_error(HUM_ERR_UNSUPPORTED, "the stream kernel takes m <= 16");
   if (w4a4_on_stream(desc, c) && !quant_a)
     return set_error(HUM_ERR_UNSUPPORTED, "W4A4 on the decode kernel quantizes its activations itself");
+  // block-scaled FP8 on the decode kernel: the kernel quantizes the bf16 rows
+  const bool blk_stream = fmt_of(desc) == F_FP8_BLOCK && c.kind == HUM_KERNEL_STREAM;
+  if (blk_stream && !quant_a)
+    return set_error(HUM_ERR_UNSUPPORTED, "block-scaled FP8 on the decode kernel quantizes its activations itself");
   const DenseWs w = dense_ws(desc, m, c, quant_a);
   if (w.total > 0 && (!workspace || ws_bytes < (size_t)w.total))
     return set_error(HUM_ERR_WORKSPACE, "workspace too small (%zu < %lld)", ws_bytes, (long long)w.total);
@@ -768,7 +785,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
     if (st != HUM_OK) return st;
     a_use = ws + w.aq;
     as_use = ws + w.as;
-  } else if (quant_a && !fuse_q) {
+  } else if (quant_a && !fuse_q && !blk_stream) {
     st = hum_quant_act(desc->act_fmt, m, desc->k, a, desc->k, ws + w.aq, ws + w.as, stream);
     if (st != HUM_OK) return st;
     a_use = ws + w.aq;
@@ -817,7 +834,7 @@ hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_
   }
   p.stream_rows = (int)(m < 16 ? m : 16);
   p.a_bytes = (fmt_of(desc) == F_MXFP4_MXFP4 && !w4a4_on_stream(desc, c)) ? m * (desc->k / 2)
-                                            : m * desc->k * ((fmt_bf16_act(fmt_of(desc)) || fuse_q) ? 2 : 1);
+                                            : m * desc->k * ((fmt_bf16_act(fmt_of(desc)) || fuse_q || blk_stream) ? 2 : 1);
   p.a_fp8_fuse = fuse_q ? 1 : 0;
   p.a_scale_bytes = (desc->act_fmt == HUM_ACT_MXFP8 || desc->act_fmt == HUM_ACT_MXFP4) ? m * (desc->k / 32)
                     : (desc->act_fmt == HUM_ACT_FP8_GROUP ? m * (desc->k / 128) * 4 : 0);

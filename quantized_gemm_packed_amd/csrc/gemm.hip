@@ -154,6 +154,9 @@ hum_status launch_gemm(const KernelKey& key, const GemmParams& p_in, int64_t m_t
     if (stream_self_staged(key.fmt, key.amode, key.epi) &&
         !stream_self_stage_fits(key.fmt, p.stream_rows, p.kb_per_split, key.waves_k, p.kb_per_group, p.scale_f32))
       return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per wave too long (raise split_k)");
+    // (block-scaled FP8 rows are quantized in the kernel, four code chunks per lane)
+    if (key.fmt == F_FP8_BLOCK && !stream_fp8_fuse_fits(p.stream_rows, p.kb_per_split, key.waves_k))
+      return set_error(HUM_ERR_UNSUPPORTED, "stream kernel: K range per wave too long (raise split_k)");
     p.lds_meta_off = (int)L.meta_off;
     p.lds_meta_stride = (int)L.meta_stride;
     p.lds_zero_off = (int)L.zero_off;

@@ -1021,10 +1021,11 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
   // row maxima of all waves, divides, converts and writes its code slots.
   // The codes and scales are the quantizer's bit for bit, so the result is
   // that of the two-launch path.
-  constexpr bool kFuse = FMT == F_FP8 && kSelf;
+  constexpr bool kFuse = (FMT == F_FP8 || FMT == F_FP8_BLOCK) && kSelf;
+  constexpr bool kBlk = FMT == F_FP8_BLOCK && kSelf;
   constexpr int kFuseCh = 4;  // code chunks per lane (a wave's K range holds at most 256)
-  __shared__ uint32_t s_amax[kFuse ? KW * 16 : 1];
-  __shared__ float s_rsc[kFuse ? 16 : 1];
+  __shared__ uint32_t s_amax[FMT == F_FP8 && kSelf ? KW * 16 : 1];
+  __shared__ float s_rsc[FMT == F_FP8 && kSelf ? 16 : 1];
   auto fuse_stage = [&](int nr) {
     const int nch = nj * nr * kCPR;                  // 16-byte code chunks (<= 256)
     const int slot0 = (kw0 - kb_begin) * nr * kCPR;
@@ -1043,6 +1044,58 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       const uint32_t off = (uint32_t)(((row0 + r) * p.lda + (int64_t)(kw0 + kbl) * 128 + lc * 16) * 2);
       xb[2 * i] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off : kOob, 0, 0);
       xb[2 * i + 1] = __builtin_amdgcn_raw_buffer_load_b128(ra, c < nch ? off + 16 : kOob, 0, 0);
+    }
+    if constexpr (kBlk) {
+      // block-scaled FP8: the scale group of a chunk is its row's K-block,
+      // whose 8 chunks are the 8 lanes of a chunk row: the group's maximum
+      // is a reduction over them, no other wave is involved.  The group
+      // scales go to [K-block][16 rows] after the code slots, the sub-tiles'
+      // block scales of the wave's K-blocks to [K-block][WN] after them.
+      const int sa_off = ((nr * kCPR * nkb + 63) & ~63) * 16;
+      const int sw_off = sa_off + nkb * 64;
+      const int nsw = nj * WN;
+      float swv = 0.0f;
+      if (lane < nsw) {
+        const int ns = lane % WN, j = lane / WN;
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(wp.meta, p.scales_per_expert);
+        const uint32_t mo = ntv[ns] ? (uint32_t)((nts[ns] * (int64_t)p.kb_count + kw0 + j) * 4) : kOob;
+        swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, mo, 0, 0));
+      }
+      issue_ring();
+      if (lane < nsw) *reinterpret_cast<float*>(dsm + sw_off + ((kw0 - kb_begin + lane / WN) * WN + lane % WN) * 4) = swv;
+#pragma unroll
+      for (int i = 0; i < kFuseCh; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int c = i * 64 + lane;
+        float mx = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(bf16_bits_to_f32(xb[2 * i + h][d] & 0xFFFF)));
+            mx = __builtin_fmaxf(mx, __builtin_fabsf(bf16_bits_to_f32(xb[2 * i + h][d] >> 16)));
+          }
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 1));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 2));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 4));
+        if (c >= nch) continue;
+        const float sc = mx > 0.0f ? mx / 448.0f : 1.0f;  // IEEE f32 division
+        const uint32_t rowkb = (uint32_t)c / kCPR;
+        const int kbl = (int)((rowkb * mnr) >> 20);
+        if ((lane & 7) == 0)
+          *reinterpret_cast<float*>(dsm + sa_off + ((kw0 - kb_begin + kbl) * 16 + rw[i]) * 4) = sc;
+        u32x4_t q;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const uint32_t w0 = xb[2 * i + h][2 * d], w1 = xb[2 * i + h][2 * d + 1];
+            q[2 * h + d] = f32x2_to_e4m3x2(bf16_bits_to_f32(w0 & 0xFFFF) / sc, bf16_bits_to_f32(w0 >> 16) / sc) |
+                           (f32x2_to_e4m3x2(bf16_bits_to_f32(w1 & 0xFFFF) / sc, bf16_bits_to_f32(w1 >> 16) / sc) << 16);
+          }
+        *reinterpret_cast<u32x4_t*>(dsm + (slot0 + c) * 16) = q;
+      }
+      return;
     }
     issue_ring();
     uint32_t* am = s_amax + wave * 16;
@@ -1107,7 +1160,9 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
     // order, so the copy waits for them alone), then reads only what it
     // wrote: no barrier, no loader.  Rows < m of the tile are a prefix.
     nrows = p.m - row0 < 16 ? (int)(p.m - row0) : 16;
-    if constexpr (kFuse) {
+    if constexpr (kBlk) {
+      fuse_stage(nrows);  // (block-scaled FP8 rows are always quantized here)
+    } else if constexpr (kFuse) {
       if (p.a_fp8_fuse)
         fuse_stage(nrows);
       else
@@ -1194,11 +1249,24 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
           i32x8_t a8;
           a8[0] = lo[0]; a8[1] = lo[1]; a8[2] = lo[2]; a8[3] = lo[3];
           a8[4] = hi[0]; a8[5] = hi[1]; a8[6] = hi[2]; a8[7] = hi[3];
+          if constexpr (kBlk) {
+            // acc += (row group scale x sub-tile block scale) x this K-block's sum
+            const int sa_off = ((nrows * kCPR * nkb + 63) & ~63) * 16;
+            const f32x4_t sg = *reinterpret_cast<const f32x4_t*>(dsm + sa_off + ((kb - kb_begin) * 16 + 4 * lg) * 4);
 #pragma unroll
-          for (int ns = 0; ns < WN; ++ns) {
-            uint32_t mw, zw;
-            lds_meta(ns, kb, mw, zw);
-            acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], mw, kb, acc[ns]);
+            for (int ns = 0; ns < WN; ++ns) {
+              const float sw = *reinterpret_cast<const float*>(dsm + sa_off + nkb * 64 + ((kb - kb_begin) * WN + ns) * 4);
+              const f32x4_t t = mfma_f8_kblock<FMT>(a8, 127, ring[q][ns], 0u, kb, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[ns][i] = __builtin_fmaf(sg[i] * sw, t[i], acc[ns][i]);
+            }
+          } else {
+#pragma unroll
+            for (int ns = 0; ns < WN; ++ns) {
+              uint32_t mw, zw;
+              lds_meta(ns, kb, mw, zw);
+              acc[ns] = mfma_f8_kblock<FMT>(a8, sa, ring[q][ns], mw, kb, acc[ns]);
+            }
           }
         }
       }
@@ -1243,7 +1311,7 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
 #pragma unroll
     for (int ns = 0; ns < WN; ++ns)
       store_tile<FMT, EPI, AMODE>(p, wp.meta, gs, row0, (int64_t)nts[ns] * 16 + c16, acc[ns], lg,
-                                  (kFuse && p.a_fp8_fuse) ? s_rsc : nullptr);
+                                  (FMT == F_FP8 && kSelf && p.a_fp8_fuse) ? s_rsc : nullptr);
   } else if constexpr (EPI == EPI_SWIGLU_BF16) {
 #pragma unroll
     for (int j = 0; j < WN / 2; ++j)
@@ -2421,7 +2489,7 @@ InstanceTable instances_moe_c();
 
 // Ring depth in 1-KB weight fragments per sub-tile (8-bit fragments are 2 KB:
 // half as many).  A CU keeps about 64-128 KB of weights in flight.
-#define HUM_PF(F, n) (((F) == F_FP8 || fmt_w8_bf16(F) || fmt_fp6(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
+#define HUM_PF(F, n) (((F) == F_FP8 || (F) == F_FP8_BLOCK || fmt_w8_bf16(F) || fmt_fp6(F)) ? ((n) > 1 ? (n) / 2 : 1) : (n))
 #define HUM_DENSE_SET(F)                                   \
   HUM_STREAM(F, 1, 8, HUM_PF(F, 8), A_DIRECT, EPI_BF16),   \
   HUM_STREAM(F, 1, 15, HUM_PF(F, 8), A_DIRECT, EPI_BF16),  \

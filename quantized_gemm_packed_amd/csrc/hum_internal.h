@@ -283,6 +283,12 @@ struct StreamLdsPlan {
 constexpr StreamLdsPlan stream_lds_plan(int fmt, int rows, int64_t kb, int wn, int64_t kb_per_group, int scale_f32,
                                         int64_t ng, int64_t kb4) {
   StreamLdsPlan L{stream_lds_footprint(fmt, rows, kb), 0, 0, 0};
+  if (fmt == F_FP8_BLOCK) {
+    // the group scales of the 16 tile rows per K-block, then the block
+    // scales of the sub-tiles per K-block (the kernel quantizes the rows)
+    L.total = L.meta_off + kb * 64 + ((kb * wn * 4 + 15) / 16) * 16;
+    return L;
+  }
   if (fmt_int(fmt)) {
     int64_t groups = (kb + kb_per_group - 1) / kb_per_group + 1;  // groups a range of kb blocks touches
     if (groups > ng) groups = ng;
@@ -319,6 +325,8 @@ constexpr bool stream_self_stage_fits(int fmt, int rows, int64_t kb, int kw, int
 
 // The dense FP8 decode kernel quantizes per-token activations itself when
 // each wave's K range holds at most 4 16-byte code chunks per lane.
+// (Block-scaled FP8 activations are always quantized in the decode kernel,
+// per row and K-block, under the same limit.)
 constexpr bool stream_fp8_fuse_fits(int rows, int64_t kb, int kw) {
   return rows * ((kb + kw - 1) / kw) * 8 <= 256;
 }

@@ -11,7 +11,7 @@ static const Instance kDenseA[] = {
     HUM_DENSE_SET(F_MXFP4_BF16),
     HUM_DENSE_SET(F_MXFP4_MXFP8),
     HUM_DENSE_TILE_SET(F_MXFP4_MXFP4),
-    HUM_DENSE_TILE_SET(F_FP8_BLOCK),
+    HUM_DENSE_SET(F_FP8_BLOCK),
     HUM_DENSE_TILE32_SET(F_INT),
     HUM_DENSE_TILE32_SET(F_MXFP4_BF16),
     HUM_TILE32_S(F_MXFP4_BF16, 8, 4, 2),

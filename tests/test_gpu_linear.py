@@ -312,6 +312,39 @@ def test_fp8_block_exact_every_tile(tile, split):
     assert_bf16_exact(out, ref, f"tile={tile}")
 
 
+@pytest.mark.parametrize("split", [1, 2])
+@pytest.mark.parametrize("tile", STREAM_TILES, ids=lambda t: "t" + "".join(map(str, t)))
+def test_fp8_block_decode_kernel_exact(tile, split):
+    """Block-scaled FP8 on the decode kernel, which quantizes each row's
+    K-blocks itself (the group rule: s = amax / 448 per row and 128 along K):
+    the exact case of the tile test above, bitwise equal to the oracle, on
+    every decode configuration; pre-quantized activations are refused
+    there."""
+    m, n, k = 13, 272, 1024
+    g = synth.rng(40)
+    ints = g.integers(-8, 9, size=(m, k)).astype(np.float64)
+    ints[:, ::128] = np.where(g.integers(0, 2, size=(m, k // 128)) == 1, 448.0, -448.0)
+    ints[3, 128:256] = 0.0                               # an all-zero group: scale 1
+    x = ints * np.ldexp(1.0, g.integers(-6, -3, size=(m, k // 128))).repeat(128, axis=1)
+    xb = oracle.formats.encode_bf16(x)
+    codes = oracle.formats.encode_e4m3(g.integers(-8, 9, size=(1, n, k)).astype(np.float64))
+    scales = np.ldexp(1.0, g.integers(-9, -7, size=(1, -(-n // 128), k // 128))).astype(np.float32)
+    w = {"codes": codes, "scales": scales}
+    hd, od = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
+    packed = prepare(hd, w, "f32")
+    print(f"case fp8 block decode exact tile={tile} split={split}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, split))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_group(oracle.formats.decode_bf16(xb).astype(np.float32))
+    a = oracle.quant.dequant_fp8_group(q, s)
+    assert np.array_equal(a, oracle.formats.decode_bf16(xb))
+    ref = oracle.gemm.linear(od, a, w["codes"], w["scales"])
+    assert_bf16_exact(out, ref, f"tile={tile} split={split}")
+    qa, sa = hum.quant_act("fp8_group", dev(xb))
+    with pytest.raises(hum.HumError, match="quantizes its activations itself"):
+        hum.linear(hd, packed, qa, a_scales=sa, cfg=cfg(tile, split))
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_fp8_block_dense_random_vs_oracle(m):
     """Block-scaled FP8 W8A8 at the selector's config (ragged N)."""
