@@ -226,12 +226,13 @@ hum_status hum_linear_noalloc(const hum_weight_desc* desc, const void* packed, i
                               const void* a, const void* a_scales, const void* bias,
                               void* out, void* stream);
 
-/* hum_linear with an explicit tile configuration (NULL = selector).  A W4A4
- * description on the decode kernel (kind HUM_KERNEL_STREAM) runs as E4M3 x
+/* hum_linear with an explicit tile configuration (NULL = selector).  On the
+ * decode kernel (kind HUM_KERNEL_STREAM) a W4A4 description runs as E4M3 x
  * E2M1 and quantizes its bf16 activations itself (each MXFP4 code as the
- * E4M3 byte of its value); pre-quantized E2M1 activations with such a
- * configuration are refused (HUM_ERR_UNSUPPORTED), and the selector gives
- * them a tile configuration. */
+ * E4M3 byte of its value), and a block-scaled FP8 description quantizes its
+ * bf16 rows itself (per row and 128 along K); pre-quantized activations
+ * with such a configuration are refused (HUM_ERR_UNSUPPORTED), and the
+ * selector gives them a tile configuration. */
 hum_status hum_linear_ex(const hum_weight_desc* desc, const void* packed, int64_t m,
                          const void* a, const void* a_scales, const void* bias,
                          void* out, void* workspace, size_t ws_bytes,
