@@ -1053,16 +1053,23 @@ __global__ __launch_bounds__(64 * stream_waves(FMT, KW, AMODE, EPI)) void stream
       // block scales of the wave's K-blocks to [K-block][WN] after them.
       const int sa_off = ((nr * kCPR * nkb + 63) & ~63) * 16;
       const int sw_off = sa_off + nkb * 64;
+      // (at most 4 code chunks per lane: a wave's K range is at most 32
+      // K-blocks, so its WN <= 4 sub-tiles hold at most 128 block scales)
       const int nsw = nj * WN;
-      float swv = 0.0f;
-      if (lane < nsw) {
-        const int ns = lane % WN, j = lane / WN;
-        const __amdgpu_buffer_rsrc_t rm = make_rsrc(wp.meta, p.scales_per_expert);
-        const uint32_t mo = ntv[ns] ? (uint32_t)((nts[ns] * (int64_t)p.kb_count + kw0 + j) * 4) : kOob;
-        swv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, mo, 0, 0));
+      const __amdgpu_buffer_rsrc_t rm = make_rsrc(wp.meta, p.scales_per_expert);
+      float swv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = h * 64 + lane, ns = e % WN, j = e / WN;
+        const uint32_t mo = (e < nsw && ntv[ns]) ? (uint32_t)((nts[ns] * (int64_t)p.kb_count + kw0 + j) * 4) : kOob;
+        swv[h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, mo, 0, 0));
       }
       issue_ring();
-      if (lane < nsw) *reinterpret_cast<float*>(dsm + sw_off + ((kw0 - kb_begin + lane / WN) * WN + lane % WN) * 4) = swv;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = h * 64 + lane;
+        if (e < nsw) *reinterpret_cast<float*>(dsm + sw_off + ((kw0 - kb_begin + e / WN) * WN + e % WN) * 4) = swv[h];
+      }
 #pragma unroll
       for (int i = 0; i < kFuseCh; ++i) {
         __builtin_amdgcn_sched_barrier(0);

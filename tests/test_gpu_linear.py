@@ -345,6 +345,26 @@ def test_fp8_block_decode_kernel_exact(tile, split):
         hum.linear(hd, packed, qa, a_scales=sa, cfg=cfg(tile, split))
 
 
+@pytest.mark.parametrize("tile,m,k", [((1, 1, 4, 1, 8), 1, 32768), ((1, 1, 2, 1, 8), 2, 8192), ((1, 1, 1, 1, 4), 2, 8192)],
+                         ids=lambda v: "-".join(map(str, v)) if isinstance(v, tuple) else str(v))
+def test_fp8_block_decode_kernel_long_k(tile, m, k):
+    """Block-scaled FP8 on the decode kernel with long K ranges per wave (32
+    K-blocks of four sub-tiles at K = 32768: 128 block scales staged per
+    wave) against the oracle, ragged N."""
+    n = 328
+    w = synth.quant_weights(synth.seed_for(7, 50 + m), "e4m3", "block", 128, "f32", 1, n, k,
+                            scale_lo=0.0005, scale_hi=0.002)
+    xb = synth.bf16_normal(synth.rng(synth.seed_for(7, 150 + m)), (m, k))
+    hd, od = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
+    packed = prepare(hd, w, "f32")
+    print(f"case fp8 block decode long k tile={tile} m={m}", flush=True)
+    out = hum.linear(hd, packed, dev(xb), cfg=cfg(tile, 1))
+    torch.cuda.synchronize()
+    q, s = oracle.quant.quant_fp8_group(oracle.formats.decode_bf16(xb).astype(np.float32))
+    ref = oracle.gemm.linear(od, oracle.quant.dequant_fp8_group(q, s), w["codes"], w["scales"])
+    assert_tol(out, ref, f"fp8 block long k m={m} tile={tile}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16, 100, 300])
 def test_fp8_block_dense_random_vs_oracle(m):
     """Block-scaled FP8 W8A8 at the selector's config (ragged N)."""
