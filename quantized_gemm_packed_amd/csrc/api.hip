@@ -342,8 +342,8 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool fu
     // Measured on MI355X (dense N = K = 8192 and N = 7168, K = 2048): small
     // tiles with split-K while the tile count is low; 64 x 256 tiles for
     // bf16 activations from M = 512 (fewer LDS activation reads per MFMA);
-    // 128 x 128 for FP8 activations.  W4A4 (no decode kernel) takes the
-    // small tiles from M = 1.
+    // 128 x 128 for FP8 activations.  W4A4 and block-scaled FP8 come here
+    // from M = 1 where their decode-kernel paths do not apply.
     const bool bf16_act = fmt_bf16_act(fmt_of(d));
     int64_t target = 3 * kCUs;
     if (m <= 256) {
@@ -368,7 +368,7 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool fu
     // measured 1.6-2.4x faster than split-K for M = 64..256 on MI355X)
     c.split_k = pick_split(wgs, 4, kb, 1, fmt_w8_bf16(fmt_of(d)) ? 16 : 4, target);
     if (fmt_of(d) == F_FP8_BLOCK) {
-      // block-scaled FP8 (no decode kernel): small tiles with three stages
+      // block-scaled FP8 above decode sizes: small tiles with three stages
       // to M = 256, then the FP8 128 x 128 tiles
       if (m <= 256) {
         c.wave_m = 2;

@@ -36,7 +36,9 @@
 //   F_MXFP4_MXFP8  E4M3 activations x E2M1 weights on the block-scaled
 //                  16x16x128 MFMA, both E8M0 scales as operands.
 //   F_MXFP4_MXFP4  E2M1 activations x E2M1 weights (W4A4) on the same
-//                  MFMA; prefill-tile kernel only.
+//                  MFMA; tile kernels (at decode sizes W4A4 runs on the
+//                  F_MXFP4_MXFP8 decode kernel, its MXFP4 activations handed
+//                  over as the E4M3 bytes of the same values).
 //   F_FP8_BF16     E4M3 weights x bf16 activations (W8A16): the hardware
 //                  FP8 -> bf16 conversion (exact), bf16 MFMA, per-channel
 //                  scales in the epilogue.
@@ -51,7 +53,8 @@
 //   F_FP8_BLOCK    block-scaled FP8: E4M3 x E4M3 on the same MFMA one
 //                  K-block (128) at a time, each K-block's result scaled by
 //                  the row's group scale times the 128 x 128 weight-block
-//                  scale (acc += sa * sw * P); prefill-tile kernel only.
+//                  scale (acc += sa * sw * P); tile kernels, and the dense
+//                  decode kernel, which quantizes each row's K-blocks itself.
 //
 // Split-K across workgroups writes fp32 partials; a separate reduce kernel
 // sums them in split order (deterministic) and applies the epilogue.
