@@ -65,7 +65,32 @@ def test_linear_fp8_graph_replay(m):
                    lambda: hum.linear(hd, packed, x[:1].contiguous()))
 
 
-@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["w4a4", "fp8_block"])
+@pytest.mark.parametrize("m", [1, 5])
+def test_linear_decode_quantizing_formats_graph_replay(fmt, m):
+    """The decode kernels that quantize their activations themselves (W4A4 as
+    E4M3 x E2M1, block-scaled FP8) and the quantizer launch they need, from
+    a captured graph."""
+    n, k = 512, 1024
+    if fmt == "w4a4":
+        w = synth.moe_weights_mxfp4(synth.seed_for(9, 200 + m), 1, n, k)
+        hd, _ = descs("e2m1", "group", 32, "e8m0", 1, n, k, act="mxfp4")
+        packed = prepare(hd, w, "e8m0")
+    else:
+        w = synth.quant_weights(synth.seed_for(9, 300 + m), "e4m3", "block", 128, "f32", 1, n, k,
+                                scale_lo=0.0005, scale_hi=0.002)
+        hd, _ = descs("e4m3", "block", 128, "f32", 1, n, k, act="fp8_group")
+        packed = prepare(hd, w, "f32")
+    assert hum.select_config(hd, m).kind == hum.KERNEL_STREAM
+    x = dev(synth.bf16_normal(synth.rng(synth.seed_for(9, 400 + m)), (m, k)))
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ws = hum.Workspace("cuda").get(hum.linear_workspace_bytes(hd, m))
+    print(f"case graph linear {fmt} m={m}", flush=True)
+    _replays_match([lambda: hum.linear(hd, packed, x, out=out, workspace=ws)], [out],
+                   lambda: hum.linear(hd, packed, x[:1].contiguous()))
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("t", [1, 40])
 def test_moe_graph_replay(act, t):
     e, h, inter, topk = 8, 256, 128, 2
