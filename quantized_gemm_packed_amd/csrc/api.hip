@@ -526,6 +526,18 @@ static MoeCfg select_moe_shape(const hum_weight_desc* w13, int64_t t, int32_t to
     up.waves_k = 4;
     return {up, moe_tile16_cfg()};
   }
+  if ((f == F_MXFP4_MXFP4 || (f == F_MXFP4_MXFP8 && t * topk > 64)) && rows < 4) {
+    // MX-activation layers below 4 mean rows per expert (past the decode
+    // path of W4A8 and W4A4): 16-row tiles with three stages, gate_up 256
+    // columns wide (its MX requantization takes 32-column blocks), down 128
+    // (measured with Zipf-skewed routing, E = 128, top-8, H = 4096, I =
+    // 1024: W4A8 T = 16 59.2 -> 52.0 us, W4A4 61.1 -> 53.9; at 4 mean rows
+    // the hot experts' many 16-row blocks lost to 32-row tiles on one
+    // routing, 83.7 -> 89.1 us, and won on another, 81.2 -> 77.7)
+    hum_tile_config up = moe_tile_cfg(1);
+    up.stages = 3;
+    return {up, moe_tile16_cfg()};
+  }
   if (f == F_MXFP4_MXFP4 || f == F_FP8_BLOCK) {
     // W4A4 and block-scaled FP8: tile kernels (block-scaled FP8 has no
     // decode-kernel path);

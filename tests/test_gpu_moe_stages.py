@@ -141,12 +141,12 @@ def swiglu_exact_case(seed, e, h, inter, t, k, act):
 
 @pytest.mark.parametrize("act", ["bf16", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("tile", [(1, 1, 4, 1, 8), (1, 1, 4, 1, 4), (0, 1, 4, 4, 1), (0, 2, 4, 4, 1), (0, 8, 4, 4, 1),
-                                  (0, 1, 2, 4, 1, 3)],
+                                  (0, 1, 2, 4, 1, 3), (0, 1, 4, 4, 1, 3)],
                          ids=lambda t: "t" + "".join(map(str, t)))
 def test_swiglu_epilogue_codes_bit_exact(act, tile):
     """SwiGLU (and its MXFP8 / MXFP4 requantization) bit for bit on every
-    gate_up kernel shape, the four-K-wave decode kernel and the 16-row,
-    128-column three-stage tile included."""
+    gate_up kernel shape, the four-K-wave decode kernel and the 16-row
+    three-stage tiles included."""
     if act == "mxfp4" and tile[0] == 1:
         pytest.skip("the stage export hands W4A4 activations over as E2M1 codes, which the decode kernel does not read")
     if act != "bf16" and tile[2] == 2:
