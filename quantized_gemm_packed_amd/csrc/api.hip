@@ -357,9 +357,10 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool fu
       c.wave_m = 4;
       c.wave_n = (m >= 512 && !fmt_w8_bf16(fmt_of(d))) ? 4 : 2;
     } else {
-      // per-channel FP8: 64 x 128 to M = 1024 (34.5 us against 38.2 for
-      // 128 x 128 at N = 7168, K = 2048), 128 x 128 above
-      c.wave_m = (fmt_of(d) == F_FP8 && m <= 1024) ? 4 : 8;
+      // per-channel FP8: 64 x 128 below M = 1024, 128 x 128 from there
+      // (measured at N = 7168, K = 2048: M = 512 22.4 us against 24.4, M =
+      // 768 even, M = 1024 29.9 against 32.4)
+      c.wave_m = (fmt_of(d) == F_FP8 && m < 1024) ? 4 : 8;
       c.wave_n = 2;
     }
     const int64_t wgs = cdiv(m, tile_rows(c)) * cdiv(nt, tile_subtiles(c));
