@@ -402,6 +402,38 @@ static hum_tile_config select_dense(const hum_weight_desc* d, int64_t m, bool fu
       c.split_k = 1;
     }
   }
+  if (c.kind == HUM_KERNEL_TILE && m > 128) {
+    // bf16-activation formats whose dequantization is heavier (NVFP4, MXINT4,
+    // INT8) on 16x16 blocks: more rows per tile, measured on MI355X at N = K
+    // = 8192 (INT8: N = 7168, K = 2048).  NVFP4 / MXINT4: 64 x 128 with three
+    // stages at M = 256 (70.5 -> 66.4 / 78.5 -> 69.1 us), 128 x 128 to M =
+    // 1024 (1024: 152 -> 134 / 177 -> 139), 128 x 256 from M = 2048 (4096:
+    // 538 -> 425 / 586 -> 442); INT8 128 x 128 above M = 256 (1024: 43.5 ->
+    // 39.3, 4096: 130 -> 126).  (MXFP6 measured slower on 64 x 128 at M =
+    // 256 and keeps its tiles.)
+    // Only where the larger tiles still number at least 3/4 of the compute
+    // units (a narrow layer keeps its smaller or split tiles).
+    const int f = fmt_of(d);
+    const bool nv_mxi = f == F_NVFP4_BF16 || f == F_MXINT4_BF16;
+    hum_tile_config b = c;
+    b.split_k = 1;
+    if (nv_mxi && m <= 256) {
+      b.wave_m = 4;
+      b.wave_n = 2;
+      b.stages = 3;
+    } else if (nv_mxi && m > 256) {
+      b.wave_m = 8;
+      b.wave_n = m >= 2048 ? 4 : 2;
+      b.stages = 0;
+    } else if (f == F_INT8_BF16 && m > 256) {
+      b.wave_m = 8;
+      b.wave_n = 2;
+      b.stages = 0;
+    }
+    if (cdiv(m, tile_rows(b)) * cdiv(nt, tile_subtiles(b)) >= kCUs * 3 / 4 &&
+        gemm_instance_exists(dense_key(d, b)))
+      c = b;
+  }
   if (c.kind == HUM_KERNEL_TILE && c.split_k > 1) {
     // Stream-K in place of split-K: 512 workgroups share the tiles'
     // K-blocks evenly and the last to finish a shared tile sums it, so no
